@@ -1,0 +1,424 @@
+"""Pins of the fp64 oracle against facts fixed by the definitions and by mathematics.
+
+Each test checks the oracle against something other than itself: a hand-written fixture, a
+closed form, an invariant, a library routine the case reduces to, or exact brute force on a
+tiny input. No GPU.
+"""
+import itertools
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+from oracle.numpy_ref import NumpyModel, dequant as np_dequant
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- number formats
+
+def test_f16_decode_every_pattern_matches_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.fixture(autouse=True)
+def _quiet_overflow():
+    with np.errstate(over="ignore"):
+        yield
+
+
+def _f16_test_values(rng):
+    # log-uniform magnitudes from deep subnormal to overflow, both signs, plus exact ties
+    mags = np.exp(rng.uniform(np.log(1e-9), np.log(7e4), 20000))
+    vals = mags * rng.choice([-1.0, 1.0], mags.size)
+    h = np.arange(0, 0x7BFF, 7, dtype=np.uint16).view(np.float16).astype(np.float64)
+    ties = (h[:-1] + h[1:]) / 2  # midpoints between neighbours (exact in fp64)
+    return np.concatenate([vals, ties, -ties, [0.0, -0.0, 65504.0, 65519.99, 65520.0, 2.0**-25, 2.0**-24 * 1.5]])
+
+
+def test_f16_encode_round_to_nearest_even_matches_numpy():
+    rng = np.random.default_rng(1)
+    vals = _f16_test_values(rng)
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f64_to_f16(v) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_generator_f16_encoder_matches_numpy():
+    rng = np.random.default_rng(2)
+    vals = _f16_test_values(rng)
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([synth.f16_bits(v) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_decode_every_pattern_matches_torch():
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    ref = bits.to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_f64(b) for b in range(65536)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_bf16_encode_round_to_nearest_even_matches_torch():
+    rng = np.random.default_rng(3)
+    f32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    # exact ties: fp32 patterns whose low 16 bits are 0x8000
+    tie_bits = (rng.integers(0, 2**15, 4000, dtype=np.uint32) << 16) | 0x8000
+    ties = tie_bits.view(np.float32)
+    vals = np.concatenate([f32, ties, np.float32([1e-40, -3e-39, 3.3895e38])])
+    vals = vals[np.isfinite(vals)]
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f64_to_bf16(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+    assert np.isnan(oracle.bf16_to_f64(oracle.f64_to_bf16(float("nan"))))
+
+
+# ---------------------------------------------------------------- int4 blocks
+
+def _golden_blocks():
+    with open(os.path.join(GOLDEN, "int4_blocks.json")) as f:
+        g = json.load(f)
+    codes = np.frombuffer(bytes.fromhex("".join(g["codes_hex"])), dtype=np.uint8).reshape(1, -1)
+    scales = np.array([int(s, 16) for s in g["scales_f16_hex"]], dtype=np.uint16).reshape(1, -1)
+    return g, codes, scales
+
+
+def test_dequant_matches_hand_written_fixture():
+    g, codes, scales = _golden_blocks()
+    W = oracle.dequant(codes, scales)
+    assert W.shape == (1, g["K"])
+    assert W[0].tolist() == g["expected_weights"]
+
+
+def test_numpy_twin_dequant_matches_fixture():
+    g, codes, scales = _golden_blocks()
+    assert np_dequant(codes, scales)[0].tolist() == g["expected_weights"]
+
+
+def test_dequant_exhaustive_codes_and_finite_scales_exact_in_fp32():
+    # every finite fp16 scale (both signs) x every code: oracle weight == numpy's fp16 value * (q-8),
+    # and the product is exact in fp32 (the bit-exact dequant contract)
+    sb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    sval = sb.view(np.float16)
+    sb = sb[np.isfinite(sval)]
+    n = sb.size
+    K = 32
+    for q in range(16):
+        codes = np.full((n, K // 2), q | (q << 4), dtype=np.uint8)
+        scales = sb.reshape(n, 1)
+        W = oracle.dequant(codes, scales)
+        ref = sb.view(np.float16).astype(np.float64) * (q - 8)
+        assert np.array_equal(W[:, 0], ref)
+        assert np.array_equal(W[:, 31], ref)
+        f32 = sb.view(np.float16).astype(np.float32) * np.float32(q - 8)
+        assert np.array_equal(f32.astype(np.float64), ref)
+
+
+def test_quant_round_trip():
+    rng = np.random.default_rng(4)
+    N, K = 16, 256
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = np.abs(rng.standard_normal((N, K // 32)) * 0.02).astype(np.float16).view(np.uint16)
+    W = oracle.dequant(codes, scales)
+    assert np.array_equal(oracle.quantize(W, scales), codes)
+    # within range, dequant(quantize(w)) is within half a step of w
+    s = scales.view(np.float16).astype(np.float64).repeat(32, axis=1)
+    w = rng.uniform(-7.5, 6.5, (N, K)) * s
+    back = oracle.dequant(oracle.quantize(w, scales), scales)
+    assert np.all(np.abs(back - w) <= s / 2 + 1e-18)
+
+
+def test_gemv_exact_rationals_tiny():
+    rng = np.random.default_rng(5)
+    N, K = 3, 64
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    # power-of-two scales and small integer x: every product and partial sum is exact in fp64
+    exps = rng.integers(-6, 2, (N, K // 32))
+    scales = (2.0 ** exps).astype(np.float16).view(np.uint16)
+    x = rng.integers(-9, 10, K).astype(np.float64)
+    y = oracle.gemv(codes, scales, x)
+    for n in range(N):
+        acc = Fraction(0)
+        for k in range(K):
+            b, i = divmod(k, 32)
+            byte = int(codes[n, 16 * b + (i % 16)])
+            q = (byte & 15) if i < 16 else (byte >> 4)
+            acc += Fraction(2) ** int(exps[n, b]) * (q - 8) * Fraction(int(x[k]))
+        assert Fraction(y[n]) == acc
+
+
+def test_gemv_matches_library_matmul():
+    rng = np.random.default_rng(6)
+    codes, scales = synth.int4_matrix(77, synth.QKV, 0, 0, 96, 512)
+    x = rng.standard_normal(512)
+    ref = np_dequant(codes, scales) @ x
+    got = oracle.gemv(codes, scales, x)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_gemv_f16_matches_library_matmul():
+    rng = np.random.default_rng(7)
+    W = synth.router(9, 0, 64, 256)
+    x = rng.standard_normal(256)
+    ref = W.view(np.float16).astype(np.float64) @ x
+    assert np.allclose(oracle.gemv_f16(W, x), ref, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- RMSNorm, RoPE, SiLU
+
+def test_rmsnorm_closed_forms():
+    one = np.full(8, np.float16(1.0).view(np.uint16), dtype=np.uint16)
+    # [3, 4] -> x / sqrt(12.5 + eps)
+    out = oracle.rmsnorm([3.0, 4.0], one[:2], 1e-6)
+    assert np.allclose(out, np.array([3.0, 4.0]) / np.sqrt(12.5 + 1e-6), rtol=1e-15)
+    # constant vector c: out = gamma * c / sqrt(c^2 + eps)
+    g = np.array([0.5, 1.0, 1.5, 2.0], dtype=np.float16)
+    out = oracle.rmsnorm([-3.0] * 4, g.view(np.uint16), 1e-6)
+    assert np.allclose(out, g.astype(np.float64) * -3.0 / np.sqrt(9.0 + 1e-6), rtol=1e-15)
+    # scale invariance when eps is negligible
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal(64) * 100
+    gb = np.full(64, np.float16(1.25).view(np.uint16), dtype=np.uint16)
+    assert np.allclose(oracle.rmsnorm(x, gb, 1e-6), oracle.rmsnorm(7.0 * x, gb, 1e-6), rtol=1e-9)
+
+
+def test_rope_hand_example_and_invariants():
+    # D = 2: one pair, angle = pos * base^0 = pos
+    out = oracle.rope([1.0, 0.0], 1, 1e6)
+    assert np.allclose(out, [np.cos(1.0), np.sin(1.0)], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(9)
+    D = 128
+    v = rng.standard_normal(D)
+    assert np.array_equal(oracle.rope(v, 0, 1e6), v)  # position 0 is the identity
+    r = oracle.rope(v, 12345, 1e6)
+    half = D // 2
+    assert np.allclose(r[:half] ** 2 + r[half:] ** 2, v[:half] ** 2 + v[half:] ** 2, rtol=1e-12)
+    # relative position: <R_m q, R_n k> depends only on m - n
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    a = oracle.rope(q, 40, 1e6) @ oracle.rope(k, 17, 1e6)
+    b = oracle.rope(q, 40 + 999, 1e6) @ oracle.rope(k, 17 + 999, 1e6)
+    assert abs(a - b) <= 1e-10 * (np.abs(q).sum() * np.abs(k).sum())
+    # the first pair rotates by exactly pos radians; the last pair by pos * base^(-(D-2)/D)
+    e = np.zeros(D)
+    e[0] = 1.0
+    r = oracle.rope(e, 3, 1e6)
+    assert np.isclose(r[0], np.cos(3.0)) and np.isclose(r[half], np.sin(3.0))
+    e = np.zeros(D)
+    e[half - 1] = 1.0
+    th = 3 * 1e6 ** (-(D - 2) / D)
+    r = oracle.rope(e, 3, 1e6)
+    assert np.isclose(r[half - 1], np.cos(th)) and np.isclose(r[D - 1], np.sin(th))
+
+
+def test_silu_closed_form():
+    assert oracle.silu(0.0) == 0.0
+    z = np.linspace(-30, 30, 601)
+    assert np.allclose([oracle.silu(v) for v in z], z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+
+
+# ---------------------------------------------------------------- softmax, argmax, top-k
+
+def test_softmax_rows_sum_to_one_and_match_library():
+    rng = np.random.default_rng(10)
+    for n in (1, 2, 17, 1000):
+        s = rng.standard_normal(n) * 30
+        p = oracle.softmax(s)
+        assert abs(p.sum() - 1.0) < 1e-13
+        assert np.allclose(p, scipy.special.softmax(s), rtol=1e-12, atol=1e-300)
+        assert np.allclose(oracle.softmax(s + 123.0), p, rtol=1e-12, atol=1e-300)
+
+
+def test_argmax_and_topk_brute_force_with_ties():
+    v = np.array([1.0, 5.0, 3.0, 5.0, -2.0, 5.0])
+    assert oracle.argmax(v) == 1 == int(np.argmax(v))
+    assert oracle.topk(v, 4).tolist() == [1, 3, 5, 2]
+    rng = np.random.default_rng(11)
+    for _ in range(50):
+        x = rng.integers(-5, 5, 64).astype(np.float64)  # many exact ties
+        k = int(rng.integers(1, 64))
+        ref = np.argsort(-x, kind="stable")[:k]
+        assert oracle.topk(x, k).tolist() == ref.tolist()
+        assert oracle.argmax(x) == int(np.argmax(x))
+
+
+# ---------------------------------------------------------------- attention
+
+def _online_softmax_attention(q, K, V, chunk):
+    """Split-K attention with running max / sum merge (a different algorithm)."""
+    D = q.size
+    m, l, acc = -np.inf, 0.0, np.zeros(D)
+    for j0 in range(0, K.shape[0], chunk):
+        s = K[j0:j0 + chunk] @ q / np.sqrt(D)
+        mj = s.max()
+        m_new = max(m, mj)
+        acc = acc * np.exp(m - m_new) + np.exp(s - m_new) @ V[j0:j0 + chunk]
+        l = l * np.exp(m - m_new) + np.exp(s - m_new).sum()
+        m = m_new
+    return acc / l
+
+
+def test_attention_naive_equals_online_softmax_split():
+    rng = np.random.default_rng(12)
+    D = 128
+    for n in (1, 15, 16, 17, 300):
+        q = rng.standard_normal(D) * 3
+        K = rng.standard_normal((n, D))
+        V = rng.standard_normal((n, D))
+        out, p = oracle.attention(q, K, V, with_probs=True)
+        assert abs(p.sum() - 1.0) < 1e-13
+        for chunk in (1, 7, 64):
+            assert np.allclose(out, _online_softmax_attention(q, K, V, chunk), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(13)
+    D, n = 64, 40
+    q = rng.standard_normal(D)
+    K = rng.standard_normal((n, D))
+    assert np.allclose(oracle.attention(q, K, np.ones((n, D))), 1.0, rtol=1e-14)  # V = 1 -> 1
+    V = rng.standard_normal((n, D))
+    assert np.array_equal(oracle.attention(q, K[:1], V[:1]), V[0])  # one key -> v0
+    Kid = np.tile(K[:1], (n, 1))  # identical keys -> mean of V
+    assert np.allclose(oracle.attention(q, Kid, V), V.mean(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_attention_invariant_to_page_pool_permutation():
+    rng = np.random.default_rng(14)
+    D, P, n, pt = 32, 9, 100, 16
+    q = rng.standard_normal(D)
+    Kp = rng.standard_normal((P * pt, D))
+    Vp = rng.standard_normal((P * pt, D))
+    table = rng.permutation(P)[: (n + pt - 1) // pt].astype(np.int32)
+    out = oracle.attention_paged(q, Kp, Vp, table, pt, n)
+    # logical contiguous view gives the same result
+    idx = np.concatenate([np.arange(p * pt, p * pt + pt) for p in table])[:n]
+    assert np.array_equal(out, oracle.attention(q, Kp[idx], Vp[idx]))
+    # permute the physical pool and remap the table: bitwise identical
+    perm = rng.permutation(P)  # new page id of old page p is perm[p]
+    Kq = np.empty_like(Kp)
+    Vq = np.empty_like(Vp)
+    for p in range(P):
+        Kq[perm[p] * pt:(perm[p] + 1) * pt] = Kp[p * pt:(p + 1) * pt]
+        Vq[perm[p] * pt:(perm[p] + 1) * pt] = Vp[p * pt:(p + 1) * pt]
+    assert np.array_equal(oracle.attention_paged(q, Kq, Vq, perm[table].astype(np.int32), pt, n), out)
+    # unmapped / stale slots beyond n do not matter
+    Kq2, Vq2 = Kq.copy(), Vq.copy()
+    last = perm[table[-1]]
+    used = n - (len(table) - 1) * pt
+    Kq2[last * pt + used:(last + 1) * pt] = np.nan
+    Vq2[last * pt + used:(last + 1) * pt] = np.nan
+    assert np.array_equal(oracle.attention_paged(q, Kq2, Vq2, perm[table].astype(np.int32), pt, n), out)
+
+
+# ---------------------------------------------------------------- generator
+
+def test_generator_counter_based_and_distributions():
+    c_full, s_full = synth.int4_matrix(5, synth.GATE, 3, 0, 64, 256)
+    # any row range regenerates the same rows
+    lib = synth.lib()
+    part_c = np.empty((10, 128), dtype=np.uint8)
+    part_s = np.empty((10, 8), dtype=np.uint16)
+    lib.bws_int4_matrix(5, synth.GATE, 3, 0, 64, 256, 17, 10, part_c.ctypes.data, part_s.ctypes.data)
+    assert np.array_equal(part_c, c_full[17:27]) and np.array_equal(part_s, s_full[17:27])
+    # codes uniform on 0..15
+    c, s = synth.int4_matrix(6, synth.DOWN, 0, 0, 512, 4096)
+    q = np.concatenate([c & 15, c >> 4]).ravel()
+    counts = np.bincount(q, minlength=16)
+    assert np.all(np.abs(counts / q.size - 1 / 16) < 0.002)
+    # scales |N(0, 0.02)|: mean 0.02*sqrt(2/pi), second moment 4e-4; subnormals kept
+    sv = s.view(np.float16).astype(np.float64).ravel()
+    assert np.all(sv >= 0)
+    assert abs(sv.mean() - 0.02 * np.sqrt(2 / np.pi)) < 3e-4
+    assert abs((sv ** 2).mean() - 4e-4) < 1e-5
+    assert np.any((sv > 0) & (sv < 2 ** -14))
+    # gains fp16(1 + 0.1 z)
+    g = synth.norm_gain(7, synth.ATTN_NORM, 0, 100000).view(np.float16).astype(np.float64)
+    assert abs(g.mean() - 1.0) < 2e-3 and abs(g.std() - 0.1) < 2e-3
+    # synthetic KV: ((h & 0xFF) - 128) / 64, exact in both cache dtypes
+    kv = synth.kv_fill(8, 1, 2, 100, 16, 4, 32, synth.KV_BF16)
+    vals = torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.all(vals * 64 == np.round(vals * 64)) and vals.min() >= -2 and vals.max() < 2
+    assert vals[3, 1, 2, 5] == synth.kv_value(8, 1, 2, 103, 1, 2, 5, 4, 32)
+    kvh = synth.kv_fill(8, 1, 2, 100, 16, 4, 32, synth.KV_F16).view(np.float16).astype(np.float64)
+    assert np.array_equal(kvh, vals)
+
+
+# ---------------------------------------------------------------- whole model
+
+TINY = dict(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=1024,
+            vocab=1024, rms_eps=1e-6, rope_base=1e6, kv_dtype="f16")
+TINY_MOE = dict(n_layers=2, d_model=128, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn_dim=0,
+                vocab=512, rms_eps=1e-6, rope_base=1e6, kv_dtype="bf16", n_experts=8, top_k=3,
+                expert_ffn=64, n_shared=1, shared_ffn=96)
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_MOE], ids=["dense", "moe"])
+def test_c_oracle_equals_numpy_twin(cfg):
+    seed = 1234
+    m = oracle.Model(cfg, seed)
+    kv = oracle.KV(m, 1, 64)
+    twin = NumpyModel(cfg, seed)
+    rng = np.random.default_rng(15)
+    toks = rng.integers(0, cfg["vocab"], 12)
+    for p, t in enumerate(toks):
+        a = oracle.forward(m, kv, 0, [t], p)["logits"][0]
+        b = twin.step(int(t))
+        assert np.max(np.abs(a - b)) <= 1e-9 * np.max(np.abs(b)), p
+
+
+def test_multi_token_step_equals_sequential_steps():
+    """Four tokens in one call (causal over the new positions) equal four single-token calls."""
+    m = oracle.Model(TINY, 99)
+    rng = np.random.default_rng(16)
+    prompt = rng.integers(0, 1024, 5)
+    toks = rng.integers(0, 1024, 4)
+    kv1, kv2 = oracle.KV(m, 1, 32), oracle.KV(m, 1, 32)
+    oracle.forward(m, kv1, 0, prompt, 0)
+    oracle.forward(m, kv2, 0, prompt, 0)
+    multi = oracle.forward(m, kv1, 0, toks, 5)["logits"]
+    seq = np.stack([oracle.forward(m, kv2, 0, [t], 5 + i)["logits"][0] for i, t in enumerate(toks)])
+    assert np.allclose(multi, seq, rtol=0, atol=1e-10 * np.abs(seq).max())
+
+
+def test_moe_full_topk_is_softmax_mixture_and_single_expert_is_dense():
+    m = oracle.Model(dict(TINY_MOE, top_k=8, n_shared=0), 5)
+    rng = np.random.default_rng(17)
+    h = rng.standard_normal(128)
+    out, sel = m.moe_ffn(0, h)
+    assert sorted(sel.tolist()) == list(range(8))
+    r = m.router_logits(0, h)
+    assert np.allclose(r, synth.router(5, 0, 8, 128).view(np.float16).astype(np.float64) @ h, rtol=1e-13)
+    P = scipy.special.softmax(r)
+    ref = sum(P[e] * m.ffn(0, h, expert=e) for e in range(8))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # one expert, top-1, no shared expert: the gate is 1 and the layer is that expert's FFN
+    m1 = oracle.Model(dict(TINY_MOE, n_experts=1, top_k=1, n_shared=0), 5)
+    out1, sel1 = m1.moe_ffn(1, h)
+    assert sel1.tolist() == [0]
+    assert np.array_equal(out1, m1.ffn(1, h, expert=0))
+    # top-k selection equals a stable descending sort of the router logits
+    m8 = oracle.Model(TINY_MOE, 6)
+    _, sel3 = m8.moe_ffn(0, h)
+    r8 = m8.router_logits(0, h)
+    assert sel3.tolist() == np.argsort(-r8, kind="stable")[:3].tolist()
+
+
+def test_oracle_reads_synthetic_context():
+    m = oracle.Model(TINY, 3)
+    kv = oracle.KV(m, 2, 8)
+    kv.set_synth(1, 4242, 7, 40)
+    for (l, pos, w, g, d) in itertools.product([0, 1], [0, 15, 39], [0, 1], [0, 1], [0, 63]):
+        assert kv.read(1, l, pos, w, g, d) == synth.kv_value(4242, l, 7, pos, w, g, d, 2, 64)
