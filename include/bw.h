@@ -1,0 +1,192 @@
+/*
+ * bw.h - C-ABI of the MI355X (gfx950) decode-step library libbw.so.
+ *
+ * The library runs one autoregressive decode step of a dense or MoE transformer whose linear
+ * layers are int4 block-quantised (32 weights per block, one fp16 scale, w = scale * (q - 8)),
+ * with grouped-query attention over a paged KV cache. Sources for the operation: the bw24
+ * deep-dive page (10100.com) - section 2 (engine core: paged KV manager, dense/MoE model and
+ * standard/MTP decoder strategies), section 4 (the Engine facade: callers only prefill and
+ * decode; a session shares the weights and owns its KV cache), section 5 stage 4 (the verify
+ * kernel unrolls K draft tokens along the sequence dimension over one shared KV cache) and
+ * section 6 item 2 (logical sequence positions map to fixed physical pages through a page
+ * table) - and the bw24 vs llama.cpp page (devpress.csdn.net) section 2.1 (each new token
+ * reads the whole KV cache) and section 2.2 (linear layer and activation fused in one kernel).
+ *
+ * Conventions for every entry point:
+ *  - Return value: BW_OK (0) or a negative BW_E* code. The text of the last error on the
+ *    calling thread is returned by bw_last_error(). No C++ exception crosses this boundary.
+ *  - Pointers named *_dev are device pointers (hipMalloc'd or from torch); pointers named
+ *    *_host are host pointers. `stream` is a hipStream_t (NULL = the default stream).
+ *  - Device work is enqueued asynchronously on `stream`; nothing here synchronises the stream
+ *    except the calls documented as synchronous (model load, pool create/synthesise/read,
+ *    bw_check_device_error, the debug readers).
+ *  - Ownership: handles are owned by the caller until the matching *_free. The library owns
+ *    all weight, KV-pool and workspace device memory behind a handle; it allocates at create
+ *    time only and allocates nothing in bw_decode_step. Caller buffers are borrowed for the
+ *    duration of the enqueued work.
+ *  - Errors detected on the device (a page id or token id out of range) never fault: the
+ *    offending read or write is skipped and a bit is set in the model's device error word,
+ *    returned by bw_check_device_error.
+ */
+#ifndef BW_H
+#define BW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define BW_OK 0
+#define BW_EINVAL (-1)  /* bad argument (null pointer, size out of range, inconsistent shape) */
+#define BW_ENOMEM (-2)  /* device or host allocation failed */
+#define BW_EHIP (-3)    /* a HIP runtime call failed */
+#define BW_ERANGE (-4)  /* a size exceeds what the handle was created for */
+#define BW_ESTATE (-5)  /* handle used in the wrong state (e.g. pool of another model) */
+
+/* KV cache element types */
+#define BW_KV_F16 1
+#define BW_KV_BF16 2
+
+/* device error bits (bw_check_device_error) */
+#define BW_DERR_PAGE 1   /* a page-table entry was outside [0, n_pages) */
+#define BW_DERR_TOKEN 2  /* a token id was outside [0, vocab) */
+
+typedef struct bw_model bw_model;
+typedef struct bw_kv_pool bw_kv_pool;
+
+/* Model shape. Dense models set n_experts = 0; MoE models set ffn_dim = 0 and the expert
+ * fields. All layers share one shape. */
+typedef struct {
+  int32_t n_layers;
+  int32_t d_model;      /* multiple of 32 */
+  int32_t n_q_heads;    /* multiple of n_kv_heads */
+  int32_t n_kv_heads;
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t ffn_dim;      /* dense SwiGLU width (multiple of 32) */
+  int32_t vocab;
+  float rms_eps;        /* RMSNorm epsilon (1e-6) */
+  double rope_base;     /* RoPE base (1e6) */
+  int32_t n_experts;    /* routed experts (MoE), 0 for dense */
+  int32_t top_k;        /* experts per token (MoE) */
+  int32_t expert_ffn;   /* SwiGLU width of a routed expert */
+  int32_t n_shared;     /* ungated shared experts (MoE) */
+  int32_t shared_ffn;   /* SwiGLU width of a shared expert */
+  int32_t kv_dtype;     /* BW_KV_F16 or BW_KV_BF16 */
+  int32_t page_tokens;  /* tokens per KV page; must be 16 */
+  int32_t max_positions;/* largest position + 1 any step may use (RoPE table length) */
+  int32_t max_tokens;   /* largest batch * t of one step (workspace size) */
+} bw_model_config;
+
+/* Create a model whose weights are generated from `seed` by the seeded input generator:
+ * int4 codes uniform on 0..15, block scales fp16(|0.02 z|), embeddings fp16(z), norm gains
+ * fp16(1 + 0.1 z), router fp16(0.02 z) (z standard normal). Generation runs on host threads;
+ * the weights are then copied to the current HIP device. Synchronous.
+ * Errors: BW_EINVAL for an unsupported shape, BW_ENOMEM, BW_EHIP. */
+int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed, bw_model** out);
+
+/* Release a model and all device memory it owns. NULL is accepted. */
+int bw_model_free(bw_model* model);
+
+/* Create a physical KV page pool of n_pages pages for `model`. One page holds page_tokens
+ * positions of every layer; its device layout is
+ *   pool[layer][page][kv_head][0 = K, 1 = V][slot 0..page_tokens-1][head_dim]
+ * in the model's kv_dtype (one page-layer is 64 KiB at 8 KV heads x 128 dims x bf16).
+ * The pool is zero-filled. Synchronous. Errors: BW_EINVAL, BW_ENOMEM, BW_EHIP. */
+int bw_kv_pool_create(const bw_model* model, int32_t n_pages, bw_kv_pool** out);
+
+/* Release a pool. NULL is accepted. */
+int bw_kv_pool_free(bw_kv_pool* pool);
+
+/* Fill every element of the pool with the 16-bit pattern `bits` (e.g. a NaN, to show that a
+ * step never reads a slot it should not). Asynchronous on stream. */
+int bw_kv_pool_fill(bw_kv_pool* pool, uint16_t bits, void* stream);
+
+/* Write synthetic cached context: for sequence b (0 <= b < batch) and every layer, positions
+ * [0, seq_lens_host[b]) receive the generator's synthetic K/V for (seed, layer, seq_ids_host[b])
+ * (values ((h & 0xFF) - 128) / 64, exact in the cache dtype), stored at page
+ * page_table_host[b * max_pages + pos / page_tokens], slot pos % page_tokens.
+ * Host pointers; synchronous. Errors: BW_EINVAL (a needed page id out of range). */
+int bw_kv_pool_synthesize(bw_kv_pool* pool, uint64_t seed, const int32_t* seq_ids_host,
+                          const int32_t* seq_lens_host, const int32_t* page_table_host,
+                          int32_t batch, int32_t max_pages);
+
+/* Copy one page-layer (n_kv_heads * 2 * page_tokens * head_dim elements, 2 bytes each, in the
+ * pool layout above) to host memory. Synchronous. Errors: BW_EINVAL, BW_ERANGE. */
+int bw_kv_pool_read(const bw_kv_pool* pool, int32_t layer, int32_t page, void* host_dst,
+                    size_t bytes);
+
+/* One decode step for `batch` sequences of `t` new tokens each (t = 1: plain decode; t > 1:
+ * the verify step of speculative decoding, the t tokens laid out along the sequence).
+ *   tokens_dev     int32 [batch * t]   token ids, row b*t + i is token i of sequence b
+ *   seq_lens_dev   int32 [batch]       positions already cached BEFORE this call; token i of
+ *                                      sequence b is at position seq_lens[b] + i
+ *   page_table_dev int32 [batch * max_pages]  physical page of logical page j of sequence b;
+ *                                      pages 0 .. (seq_lens[b] + t - 1) / page_tokens must be
+ *                                      mapped (entries beyond may hold anything)
+ *   logits_dev     float [batch * t * vocab] output logits, or NULL
+ *   argmax_dev     int32 [batch * t]   greedy token per row (lowest index on ties), or NULL
+ * The keys and values of all new tokens are written into the pool first; token i then attends
+ * causally to positions 0 .. seq_lens[b] + i. The caller advances seq_lens afterwards.
+ * Nothing is allocated and the stream is not synchronised.
+ * Errors: BW_EINVAL (null handle or buffer, t < 1, batch < 1, pool of another model),
+ * BW_ERANGE (batch * t > max_tokens). Page or token ids out of range are device errors. */
+int bw_decode_step(bw_model* model, bw_kv_pool* pool, const int32_t* tokens_dev,
+                   const int32_t* seq_lens_dev, const int32_t* page_table_dev, int32_t batch,
+                   int32_t t, int32_t max_pages, float* logits_dev, int32_t* argmax_dev,
+                   void* stream);
+
+/* Text of the last error on this thread ("" if none). */
+const char* bw_last_error(void);
+
+/* Synchronise `stream`, copy the model's device error word to *flags_host (BW_DERR_* bits)
+ * and clear it. */
+int bw_check_device_error(bw_model* model, void* stream, int32_t* flags_host);
+
+/* ---- parity-test entry points (same kernels as the step, exposed one at a time) ---------- */
+
+/* Matrix selectors */
+#define BW_MAT_QKV 0      /* [(Hq + 2 Hkv) * D][d_model]: q rows, then k rows, then v rows */
+#define BW_MAT_O 1        /* [d_model][Hq * D]                                            */
+#define BW_MAT_GATE 2     /* [ffn][d_model]  (MoE: routed expert `expert`)                 */
+#define BW_MAT_UP 3       /* [ffn][d_model]                                                 */
+#define BW_MAT_DOWN 4     /* [d_model][ffn]                                                 */
+#define BW_MAT_LM_HEAD 5  /* [vocab][d_model]                                               */
+#define BW_MAT_SGATE 6    /* shared expert `expert`                                         */
+#define BW_MAT_SUP 7
+#define BW_MAT_SDOWN 8
+
+/* Dequantise one int4 matrix on the device with the step's in-register dequantisation and
+ * write it as fp32 [N][K] in canonical row and column order (dst_dev must hold N*K floats).
+ * Asynchronous. Errors: BW_EINVAL. */
+int bw_debug_dequant(const bw_model* model, int32_t which, int32_t layer, int32_t expert,
+                     float* dst_dev, void* stream);
+
+/* y[m][n] = sum_k W[n][k] x[m][k] for m < n_vec with the step's GEMV (n_vec = 1) or the
+ * batched MFMA path (n_vec > 1), canonical row order. x_dev float [n_vec][K], y_dev float
+ * [n_vec][N]. Asynchronous. Errors: BW_EINVAL, BW_ERANGE (n_vec > max_tokens). */
+int bw_debug_matvec(bw_model* model, int32_t which, int32_t layer, int32_t expert,
+                    const float* x_dev, int32_t n_vec, float* y_dev, void* stream);
+
+/* Attention alone over the pool for layer `layer`: q_dev float [batch * t][Hq][D] (already
+ * rotated), causal as in bw_decode_step over positions 0 .. seq_lens[b] + i (the pool must
+ * already hold them); out_dev float [batch * t][Hq][D]. Asynchronous. */
+int bw_debug_attention(bw_model* model, bw_kv_pool* pool, int32_t layer, const float* q_dev,
+                       const int32_t* seq_lens_dev, const int32_t* page_table_dev,
+                       int32_t batch, int32_t t, int32_t max_pages, float* out_dev, void* stream);
+
+/* Experts chosen by the last bw_decode_step (MoE): int32 [n_layers][batch * t][top_k],
+ * copied to host. Synchronises `stream`. Errors: BW_ESTATE for a dense model. */
+int bw_debug_read_experts(bw_model* model, int32_t n_rows, int32_t* host_dst, void* stream);
+
+/* Residual stream after the last layer of the last bw_decode_step: float [batch * t][d_model],
+ * copied to host. Synchronises `stream`. */
+int bw_debug_read_hidden(bw_model* model, int32_t n_rows, float* host_dst, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BW_H */

@@ -1,0 +1,192 @@
+"""Python binding of libbw.so, the MI355X (gfx950) int4 paged-KV decode-step library.
+
+The functions here carry the C-ABI's names (include/bw.h) and only marshal arguments: torch
+tensors become device pointers, the current torch stream becomes the hipStream_t. Every step
+of the decode path runs in the library's HIP kernels. PyTorch provides device memory and
+streams only. If libbw.so is missing, the first call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import configs  # noqa: F401  (workload shapes)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbw.so")
+
+BW_OK, BW_EINVAL, BW_ENOMEM, BW_EHIP, BW_ERANGE, BW_ESTATE = 0, -1, -2, -3, -4, -5
+BW_KV_F16, BW_KV_BF16 = 1, 2
+BW_DERR_PAGE, BW_DERR_TOKEN = 1, 2
+MAT = {"qkv": 0, "o": 1, "gate": 2, "up": 3, "down": 4, "lm_head": 5,
+       "shared_gate": 6, "shared_up": 7, "shared_down": 8}
+
+EXPORTS = (
+    "bw_model_load_synthetic", "bw_model_free", "bw_kv_pool_create", "bw_kv_pool_free",
+    "bw_kv_pool_fill", "bw_kv_pool_synthesize", "bw_kv_pool_read", "bw_decode_step",
+    "bw_last_error", "bw_check_device_error", "bw_debug_dequant", "bw_debug_matvec",
+    "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden",
+)
+
+
+class BWError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where} failed with {code}: {msg}")
+        self.code = code
+
+
+class bw_model_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn_dim", ctypes.c_int32),
+        ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_double),
+        ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
+        ("n_shared", ctypes.c_int32), ("shared_ffn", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("page_tokens", ctypes.c_int32), ("max_positions", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbw.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+        for name in EXPORTS:
+            getattr(L, name).restype = i32
+        L.bw_last_error.restype = ctypes.c_char_p
+        L.bw_last_error.argtypes = []
+        L.bw_model_load_synthetic.argtypes = [ctypes.POINTER(bw_model_config), u64, ctypes.POINTER(vp)]
+        L.bw_model_free.argtypes = [vp]
+        L.bw_kv_pool_create.argtypes = [vp, i32, ctypes.POINTER(vp)]
+        L.bw_kv_pool_free.argtypes = [vp]
+        L.bw_kv_pool_fill.argtypes = [vp, ctypes.c_uint16, vp]
+        L.bw_kv_pool_synthesize.argtypes = [vp, u64, vp, vp, vp, i32, i32]
+        L.bw_kv_pool_read.argtypes = [vp, i32, i32, vp, sz]
+        L.bw_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+        L.bw_check_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
+        L.bw_debug_dequant.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.bw_debug_matvec.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp]
+        L.bw_debug_attention.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
+        L.bw_debug_read_experts.argtypes = [vp, i32, vp, vp]
+        L.bw_debug_read_hidden.argtypes = [vp, i32, vp, vp]
+        _lib = L
+    return _lib
+
+
+def bw_last_error() -> str:
+    return lib().bw_last_error().decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != BW_OK:
+        raise BWError(rc, where, bw_last_error())
+
+
+def _ptr(t) -> int | None:
+    """Device (or host) pointer of a tensor / numpy array, or None."""
+    if t is None:
+        return None
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_config(cfg: dict, max_positions: int, max_tokens: int) -> bw_model_config:
+    kv = cfg.get("kv_dtype", "bf16")
+    return bw_model_config(
+        cfg["n_layers"], cfg["d_model"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"],
+        cfg.get("ffn_dim", 0), cfg["vocab"], cfg.get("rms_eps", 1e-6), cfg.get("rope_base", 1e6),
+        cfg.get("n_experts", 0), cfg.get("top_k", 0), cfg.get("expert_ffn", 0),
+        cfg.get("n_shared", 0), cfg.get("shared_ffn", 0),
+        BW_KV_F16 if kv == "f16" else BW_KV_BF16, cfg.get("page_tokens", 16), max_positions,
+        max_tokens,
+    )
+
+
+# ---- the C-ABI, one Python function per entry point ---------------------------------------------
+
+def bw_model_load_synthetic(cfg: bw_model_config, seed: int) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().bw_model_load_synthetic(ctypes.byref(cfg), seed, ctypes.byref(h)), "bw_model_load_synthetic")
+    return h.value
+
+
+def bw_model_free(model: int) -> None:
+    _check(lib().bw_model_free(model), "bw_model_free")
+
+
+def bw_kv_pool_create(model: int, n_pages: int) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().bw_kv_pool_create(model, n_pages, ctypes.byref(h)), "bw_kv_pool_create")
+    return h.value
+
+
+def bw_kv_pool_free(pool: int) -> None:
+    _check(lib().bw_kv_pool_free(pool), "bw_kv_pool_free")
+
+
+def bw_kv_pool_fill(pool: int, bits: int, stream=None) -> None:
+    _check(lib().bw_kv_pool_fill(pool, bits, _stream(stream)), "bw_kv_pool_fill")
+
+
+def bw_kv_pool_synthesize(pool: int, seed: int, seq_ids, seq_lens, page_table, batch: int, max_pages: int) -> None:
+    """Host int32 numpy arrays."""
+    _check(lib().bw_kv_pool_synthesize(pool, seed, _ptr(seq_ids), _ptr(seq_lens), _ptr(page_table), batch, max_pages),
+           "bw_kv_pool_synthesize")
+
+
+def bw_kv_pool_read(pool: int, layer: int, page: int, out) -> None:
+    """out: host numpy uint16 array of one page-layer."""
+    _check(lib().bw_kv_pool_read(pool, layer, page, _ptr(out), out.nbytes), "bw_kv_pool_read")
+
+
+def bw_decode_step(model: int, pool: int, tokens, seq_lens, page_table, batch: int, t: int,
+                   max_pages: int, logits=None, argmax=None, stream=None) -> None:
+    """tokens/seq_lens/page_table/argmax: int32 device tensors; logits: float32 device tensor."""
+    _check(lib().bw_decode_step(model, pool, _ptr(tokens), _ptr(seq_lens), _ptr(page_table), batch, t,
+                                max_pages, _ptr(logits), _ptr(argmax), _stream(stream)), "bw_decode_step")
+
+
+def bw_check_device_error(model: int, stream=None) -> int:
+    flags = ctypes.c_int32(0)
+    _check(lib().bw_check_device_error(model, _stream(stream), ctypes.byref(flags)), "bw_check_device_error")
+    return flags.value
+
+
+def bw_debug_dequant(model: int, which: str, layer: int, expert: int, out, stream=None) -> None:
+    _check(lib().bw_debug_dequant(model, MAT[which], layer, expert, _ptr(out), _stream(stream)), "bw_debug_dequant")
+
+
+def bw_debug_matvec(model: int, which: str, layer: int, expert: int, x, y, stream=None) -> None:
+    _check(lib().bw_debug_matvec(model, MAT[which], layer, expert, _ptr(x), x.shape[0], _ptr(y), _stream(stream)),
+           "bw_debug_matvec")
+
+
+def bw_debug_attention(model: int, pool: int, layer: int, q, seq_lens, page_table, batch: int, t: int,
+                       max_pages: int, out, stream=None) -> None:
+    _check(lib().bw_debug_attention(model, pool, layer, _ptr(q), _ptr(seq_lens), _ptr(page_table), batch, t,
+                                    max_pages, _ptr(out), _stream(stream)), "bw_debug_attention")
+
+
+def bw_debug_read_experts(model: int, n_rows: int, out, stream=None) -> None:
+    _check(lib().bw_debug_read_experts(model, n_rows, _ptr(out), _stream(stream)), "bw_debug_read_experts")
+
+
+def bw_debug_read_hidden(model: int, n_rows: int, out, stream=None) -> None:
+    _check(lib().bw_debug_read_hidden(model, n_rows, _ptr(out), _stream(stream)), "bw_debug_read_hidden")

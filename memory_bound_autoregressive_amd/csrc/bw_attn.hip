@@ -1,0 +1,286 @@
+// bw_attn.hip - grouped-query decode attention over a paged KV cache, split along the context
+// with an online-softmax merge (gfx950).
+//
+// Operation: for each new token i of sequence b at position p = seq_lens[b] + i and each query
+// head h (KV head g = h / (Hq/Hkv)), o = softmax(q . K^T / sqrt(D)) V over positions 0..p. Keys
+// and values are read through the page table: logical position j is slot j % 16 of physical
+// page page_table[b][j / 16] (bw24 deep-dive page, section 6 item 2: logical positions map to
+// fixed physical pages; section 5 stage 4: the t new tokens of a verify step are unrolled along
+// the sequence and share one cache, with causal masking among them). Every new token reads the
+// whole cache of its sequence (bw24 vs llama.cpp page, section 2.1).
+//
+// Split: workgroup (split s, KV head g, sequence b) covers logical pages [s*PPS, (s+1)*PPS) and
+// all t * (Hq/Hkv) query rows that use KV head g, so each K/V page is read once per step for all
+// heads of its group. Each of the 4 waves takes every 4th page and keeps a running
+// (max, sum, acc) per query row; the waves merge in LDS and write one partial per split. The merge
+// kernel combines the splits in split order, so the result depends only on logical page order and
+// contents: permuting the physical pool changes nothing, bit for bit.
+//
+// Lane layout per page (D = 128): scores use 8 tokens x 8 lanes per pass (each lane a 16-dim
+// slice, 2 x 16-byte loads, 2 passes); values use 4 token groups x 16 lanes (each lane an 8-dim
+// slice of 4 tokens, 16-byte loads). Slots past the sequence end are masked by selection, so stale
+// or NaN contents there never reach the result.
+#include "bw_common.h"
+#include "bw_internal.h"
+
+namespace bw {
+
+template <int KVDT>
+__device__ __forceinline__ void unpack8(u32x4 v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = kv_to_f32<KVDT>((uint16_t)(v[i] & 0xFFFFu));
+    out[2 * i + 1] = kv_to_f32<KVDT>((uint16_t)(v[i] >> 16));
+  }
+}
+
+template <int KVDT, int D, int QR>
+__global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
+  constexpr int DL = D / 8;            // score dims per lane (8 lanes per token)
+  constexpr int NV = D / 8;            // lanes per token row for values (8 dims each)
+  constexpr int TG = kWave / NV;       // token groups for values
+  constexpr int TPL = kPageTokens / TG;// tokens per lane for values
+  constexpr bool QREG = (QR * DL <= 96);
+  constexpr int NCH = DL / 8;          // 16-byte chunks per lane per token for scores
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int rep = p.H / p.G;
+  const int base_pos = p.seq_lens[b];
+  const int kv_len = base_pos + p.t;
+  int n_pg = (kv_len + kPageTokens - 1) / kPageTokens;
+  if (n_pg > p.max_pages || n_pg > p.max_splits * p.pages_per_split) {
+    if (threadIdx.x == 0 && s == 0) atomicOr(p.err, 1);
+    n_pg = min(p.max_pages, p.max_splits * p.pages_per_split);
+  }
+  const int pg0 = s * p.pages_per_split;
+  if (pg0 >= n_pg) return;
+  const int pg1 = min(n_pg, pg0 + p.pages_per_split);
+
+  __shared__ float q_lds[QR * D];
+  __shared__ float p_lds[4][QR][kPageTokens];
+  __shared__ float m_lds[4][QR], l_lds[4][QR];
+  __shared__ float acc_lds[4][QR * D];
+
+  // query rows: qr = ti * rep + r  ->  token ti, head g * rep + r
+  for (int e = threadIdx.x; e < QR * D; e += kBlock) {
+    const int qr = e / D, d = e - qr * D;
+    const int ti = qr / rep, r = qr - ti * rep;
+    float v = 0.f;
+    if (ti < p.t) v = p.q[((int64_t)(b * p.t + ti) * p.H + g * rep + r) * D + d] * p.scale;
+    q_lds[e] = v;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sc_tok = lane >> 3, sc_c = lane & 7;     // scores: token within pass, dim slice
+  const int v_c = lane % NV, v_tg = lane / NV;       // values: dim chunk, token group
+
+  float qreg[QREG ? QR : 1][QREG ? DL : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int qr = 0; qr < QR; ++qr)
+#pragma unroll
+      for (int e = 0; e < DL; ++e) qreg[qr][e] = q_lds[qr * D + sc_c * DL + e];
+  }
+  int qpos[QR];
+#pragma unroll
+  for (int qr = 0; qr < QR; ++qr) qpos[qr] = (qr / rep < p.t) ? base_pos + qr / rep : -1;
+
+  float mrun[QR], lrun[QR], acc[QR][8];
+#pragma unroll
+  for (int qr = 0; qr < QR; ++qr) {
+    mrun[qr] = -INFINITY;
+    lrun[qr] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[qr][e] = 0.f;
+  }
+
+  for (int pg = pg0 + wave; pg < pg1; pg += 4) {
+    const int page = p.page_table[(int64_t)b * p.max_pages + pg];
+    if (page < 0 || page >= p.n_pages) {
+      if (lane == 0) atomicOr(p.err, 1);
+      continue;
+    }
+    const uint16_t* kbase = p.pool + (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D;
+    const uint16_t* vbase = kbase + kPageTokens * D;
+    // ---- scores for the 16 tokens (2 passes of 8)
+    float sc[2][QR];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int tok = pass * 8 + sc_tok;
+      const int j = pg * kPageTokens + tok;
+      float kf[DL];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        u32x4 raw = *(const u32x4*)(kbase + tok * D + sc_c * DL + ch * 8);
+        unpack8<KVDT>(raw, kf + ch * 8);
+      }
+#pragma unroll
+      for (int qr = 0; qr < QR; ++qr) {
+        float dot = 0.f;
+        if constexpr (QREG) {
+#pragma unroll
+          for (int e = 0; e < DL; ++e) dot = fmaf(qreg[qr][e], kf[e], dot);
+        } else {
+#pragma unroll
+          for (int e = 0; e < DL; ++e) dot = fmaf(q_lds[qr * D + sc_c * DL + e], kf[e], dot);
+        }
+        dot += __shfl_xor(dot, 1);
+        dot += __shfl_xor(dot, 2);
+        dot += __shfl_xor(dot, 4);
+        sc[pass][qr] = (j < kv_len && j <= qpos[qr]) ? dot : -INFINITY;
+      }
+    }
+    // ---- online softmax update per query row
+#pragma unroll
+    for (int qr = 0; qr < QR; ++qr) {
+      float pm = fmaxf(sc[0][qr], sc[1][qr]);
+      pm = fmaxf(pm, __shfl_xor(pm, 8));
+      pm = fmaxf(pm, __shfl_xor(pm, 16));
+      pm = fmaxf(pm, __shfl_xor(pm, 32));
+      const float mnew = fmaxf(mrun[qr], pm);
+      float p0 = 0.f, p1 = 0.f, alpha = 1.f;
+      if (mnew != -INFINITY) {
+        p0 = __expf(sc[0][qr] - mnew);
+        p1 = __expf(sc[1][qr] - mnew);
+        alpha = __expf(mrun[qr] - mnew);
+      }
+      float ps = p0 + p1;
+      ps += __shfl_xor(ps, 8);
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      lrun[qr] = lrun[qr] * alpha + ps;
+      mrun[qr] = mnew;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[qr][e] *= alpha;
+      if (sc_c == 0) {
+        p_lds[wave][qr][sc_tok] = p0;
+        p_lds[wave][qr][8 + sc_tok] = p1;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- values: lane covers 8 dims of TPL tokens
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const int tok = v_tg + u * TG;
+      const int j = pg * kPageTokens + tok;
+      u32x4 raw = *(const u32x4*)(vbase + tok * D + v_c * 8);
+      float vf[8];
+      unpack8<KVDT>(raw, vf);
+      const bool live = j < kv_len;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] = live ? vf[e] : 0.f;
+#pragma unroll
+      for (int qr = 0; qr < QR; ++qr) {
+        const float pw = p_lds[wave][qr][tok];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[qr][e] = fmaf(pw, vf[e], acc[qr][e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // ---- reduce the value partials over the token groups of the wave
+#pragma unroll
+  for (int qr = 0; qr < QR; ++qr)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int o = NV; o < kWave; o <<= 1) acc[qr][e] += __shfl_xor(acc[qr][e], o);
+  if (v_tg == 0) {
+#pragma unroll
+    for (int qr = 0; qr < QR; ++qr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc_lds[wave][qr * D + v_c * 8 + e] = acc[qr][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int qr = 0; qr < QR; ++qr) {
+      m_lds[wave][qr] = mrun[qr];
+      l_lds[wave][qr] = lrun[qr];
+    }
+  }
+  __syncthreads();
+  // ---- merge the 4 waves and write this split's partial
+  const int n_out = p.t * rep * (D + 2);
+  for (int e = threadIdx.x; e < QR * D; e += kBlock) {
+    const int qr = e / D, d = e - qr * D;
+    if (qr / rep >= p.t) continue;
+    float M = fmaxf(fmaxf(m_lds[0][qr], m_lds[1][qr]), fmaxf(m_lds[2][qr], m_lds[3][qr]));
+    float a = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __expf(m_lds[w][qr] - M);
+        a = fmaf(acc_lds[w][e], f, a);
+        l = fmaf(l_lds[w][qr], f, l);
+      }
+    }
+    const int ti = qr / rep, r = qr - ti * rep;
+    float* dst = p.part + (((int64_t)(b * p.t + ti) * p.H + g * rep + r) * p.max_splits + s) * (D + 2);
+    dst[d] = a;
+    if (d == 0) {
+      dst[D] = M;
+      dst[D + 1] = l;
+    }
+  }
+  (void)n_out;
+}
+
+// o[row][h][:] = sum_s acc_s exp(m_s - M) / sum_s l_s exp(m_s - M), splits in order
+template <int D>
+__global__ __launch_bounds__(D) void k_attn_merge(AttnParams p) {
+  const int h = blockIdx.x, row = blockIdx.y;
+  const int b = row / p.t;
+  const int kv_len = p.seq_lens[b] + p.t;
+  const int n_pg = min((kv_len + kPageTokens - 1) / kPageTokens, min(p.max_pages, p.max_splits * p.pages_per_split));
+  const int n_split = (n_pg + p.pages_per_split - 1) / p.pages_per_split;
+  const float* part = p.part + ((int64_t)row * p.H + h) * p.max_splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  float a = 0.f, l = 0.f;
+  const int d = threadIdx.x;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float* ps = part + s * (D + 2);
+      const float f = __expf(ps[D] - M);
+      a = fmaf(ps[d], f, a);
+      l = fmaf(ps[D + 1], f, l);
+    }
+  }
+  p.out[((int64_t)row * p.H + h) * D + d] = l > 0.f ? a / l : 0.f;
+}
+
+template <int KVDT, int D, int QR>
+static int launch_split(const AttnParams& p, int batch, hipStream_t s) {
+  hipLaunchKernelGGL((k_attn_split<KVDT, D, QR>), dim3(p.max_splits, p.G, batch), dim3(kBlock), 0, s, p);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int KVDT, int D>
+static int dispatch_qr(const AttnParams& p, int batch, hipStream_t s) {
+  const int qr = p.t * (p.H / p.G);
+  switch (qr) {
+    case 1: return launch_split<KVDT, D, 1>(p, batch, s);
+    case 2: return launch_split<KVDT, D, 2>(p, batch, s);
+    case 4: return launch_split<KVDT, D, 4>(p, batch, s);
+    case 5: return launch_split<KVDT, D, 5>(p, batch, s);
+    case 8: return launch_split<KVDT, D, 8>(p, batch, s);
+    case 16: return launch_split<KVDT, D, 16>(p, batch, s);
+    default: return -2;
+  }
+}
+
+int launch_attention(const AttnParams& p, int kv_dtype, int batch, hipStream_t s) {
+  int rc;
+  if (p.D == 128) rc = kv_dtype == 1 ? dispatch_qr<1, 128>(p, batch, s) : dispatch_qr<2, 128>(p, batch, s);
+  else if (p.D == 64) rc = kv_dtype == 1 ? dispatch_qr<1, 64>(p, batch, s) : dispatch_qr<2, 64>(p, batch, s);
+  else return -2;
+  if (rc) return rc;
+  if (p.D == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(p.H, batch * p.t), dim3(128), 0, s, p);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(p.H, batch * p.t), dim3(64), 0, s, p);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace bw

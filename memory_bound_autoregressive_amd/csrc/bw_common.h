@@ -1,0 +1,88 @@
+// bw_common.h - device helpers and shared parameter structs of libbw (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bw {
+
+constexpr int kWave = 64;   // CDNA wavefront
+constexpr int kBlock = 256; // threads per workgroup of the streaming kernels (4 waves)
+constexpr int kPageTokens = 16;
+
+// ---- number formats -------------------------------------------------------------------------
+
+// fp16 bits -> fp32 (v_cvt_f32_f16: exact, subnormal inputs kept)
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// fp32 -> fp16 bits, round to nearest even (hardware conversion in the default mode)
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+template <int KVDT>
+__device__ __forceinline__ float kv_to_f32(uint16_t v) {
+  if constexpr (KVDT == 1) return f16_to_f32(v);
+  else return bf16_to_f32(v);
+}
+template <int KVDT>
+__device__ __forceinline__ uint16_t f32_to_kv(float f) {
+  if constexpr (KVDT == 1) return f32_to_f16(f);
+  else return f32_to_bf16(f);
+}
+
+// ---- loads ------------------------------------------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load that does not displace cached data (weights are read once per step)
+__device__ __forceinline__ u32x4 load_stream16(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+// ---- LDS layout of the input vector ---------------------------------------------------------
+// Element e (0..31) of 32-element block b is stored at float index b*32 + ((e + 4*(b&7)) & 31):
+// the 16-byte chunk c of block b lands in slot (c + b) & 7 of the block's 128-byte row, so eight
+// lanes reading chunk c of eight consecutive blocks touch eight different slots (all banks).
+__device__ __forceinline__ int xs_index(int b, int e) { return b * 32 + ((e + 4 * (b & 7)) & 31); }
+__device__ __forceinline__ const float4* xs_chunk(const float* xs, int b, int c) {
+  return reinterpret_cast<const float4*>(xs + b * 32 + (((c + b) & 7) << 2));
+}
+
+// ---- reductions -------------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Sum over a 256-thread block; every thread gets the result. `red` holds >= 4 floats.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace bw

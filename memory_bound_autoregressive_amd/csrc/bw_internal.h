@@ -1,0 +1,114 @@
+// bw_internal.h - structures shared by the runtime and the kernel launchers of libbw.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bw {
+
+// One int4 matrix on the device.
+//  codes : [N][K/2] bytes. Row order is the device order (see the runtime: QKV rows are
+//          interleaved in RoPE pairs, gate/up rows are interleaved as (gate_i, up_i)); within a
+//          row the canonical block layout is kept: block b is bytes 16b..16b+15, byte i holds
+//          element i (low nibble) and element i+16 (high nibble).
+//  scales: fp16 [N][lpr][nb] with scales[n][j][c] = scale of block j + lpr*c of row n, so the
+//          scales one lane needs for a row are contiguous. lpr = gcd(K/32, 64), nb = K/32/lpr.
+struct Mat {
+  const uint8_t* codes = nullptr;
+  const uint16_t* scales = nullptr;
+  int32_t N = 0, K = 0;
+  int32_t lpr = 0, nb = 0;
+};
+
+// Per-layer expert tables (MoE): device arrays of pointers, routed experts first, then shared.
+struct ExpertTab {
+  const uint8_t* const* gu_codes = nullptr;   // [E + S] interleaved gate/up [2F][d]
+  const uint16_t* const* gu_scales = nullptr;
+  const uint8_t* const* dn_codes = nullptr;   // [E + S] down [d][F]
+  const uint16_t* const* dn_scales = nullptr;
+};
+
+enum InMode { IN_PLAIN = 0, IN_RMSNORM = 1, IN_MOE_DOWN = 2 };
+enum EpiMode {
+  EPI_STORE = 0,      // y[m][row] = v (device row order)
+  EPI_STORE_CANON = 1,// y[m][canonical row] = v (parity tests)
+  EPI_RESID = 2,      // y[m][row] += v
+  EPI_QKV = 3,        // RoPE pairs, q to qout, k/v rounded into the KV pool
+  EPI_SWIGLU = 4,     // rows (2i, 2i+1) = (gate_i, up_i): y[m][i] = silu(g) * u
+  EPI_LOGITS = 5,     // y[m][row] = v and per-workgroup argmax partial
+  EPI_MOE_SWIGLU = 6  // virtual rows over the selected experts, SwiGLU into y[m][slot*F + i]
+};
+
+struct GemvParams {
+  Mat w;
+  int32_t n_rows;          // rows to compute (== w.N except for MoE virtual rows)
+  // input rows: x[m * x_stride + k]
+  const float* x = nullptr;
+  int64_t x_stride = 0;
+  const uint16_t* gamma = nullptr;  // RMSNorm gain (IN_RMSNORM)
+  float eps = 1e-6f;
+  // output
+  float* y = nullptr;
+  int64_t y_stride = 0;
+  // EPI_STORE_CANON: canonical row of each device row; rows whose canonical index falls outside
+  // [map_lo, map_lo + map_n) are skipped, the others stored at index - map_lo
+  const int32_t* row_map = nullptr;
+  int32_t map_lo = 0, map_n = 0x7fffffff;
+  // EPI_QKV
+  int32_t H = 0, G = 0, D = 0;
+  const float2* rope = nullptr;     // [max_pos][D/2] (cos, sin)
+  int32_t max_pos = 0;
+  const int32_t* seq_lens = nullptr;
+  int32_t t = 1;                    // tokens per sequence in this step (row m = b*t + i)
+  const int32_t* page_table = nullptr;
+  int32_t max_pages = 0;
+  uint16_t* pool = nullptr;         // this layer's slice of the pool: [n_pages][G][2][16][D]
+  int64_t pool_page_stride = 0;     // elements per page in the layer slice
+  int32_t n_pages = 0;
+  int32_t kv_dtype = 2;             // 1 = fp16, 2 = bf16
+  float* qout = nullptr;            // [M][H][D]
+  int32_t* err = nullptr;
+  // EPI_LOGITS: per-workgroup argmax partials [M][gridDim.x]
+  float* amax_val = nullptr;
+  int32_t* amax_idx = nullptr;
+  // MoE
+  const int32_t* sel = nullptr;     // [M][top_k] selected experts
+  const float* gates = nullptr;     // [M][top_k] renormalised gates
+  int32_t n_experts = 0, top_k = 0, n_shared = 0, Fe = 0, Fs = 0;
+  ExpertTab ex;
+  int32_t ex_lpr = 0, ex_nb = 0;    // lane split of the MoE virtual down K
+};
+
+struct AttnParams {
+  const uint16_t* pool = nullptr;   // layer slice [n_pages][G][2][16][D]
+  int64_t pool_page_stride = 0;
+  int32_t n_pages = 0;
+  const float* q = nullptr;         // [M][H][D] rotated queries
+  const int32_t* seq_lens = nullptr;
+  const int32_t* page_table = nullptr;
+  int32_t max_pages = 0;
+  int32_t t = 1, H = 0, G = 0, D = 0;
+  int32_t pages_per_split = 4;
+  int32_t max_splits = 0;
+  float scale = 0.f;                // 1/sqrt(D)
+  float* part = nullptr;            // [M][H][max_splits][D + 2] (acc, m, l)
+  float* out = nullptr;             // [M][H][D]
+  int32_t* err = nullptr;
+};
+
+// launchers (bw_gemv.hip, bw_attn.hip, bw_misc.hip)
+int launch_gemv(int in_mode, int epi, const GemvParams& p, int M, hipStream_t s, int* grid_out = nullptr);
+int gemv_lane_split(int K, int* lpr, int* nb);
+int launch_attention(const AttnParams& p, int kv_dtype, int batch, hipStream_t s);
+int launch_embed(const uint16_t* embed, int32_t vocab, int32_t d, const int32_t* tokens, int M,
+                 float* x, int32_t* err, hipStream_t s);
+int launch_argmax_final(const float* val, const int32_t* idx, int parts, int M, int32_t* out,
+                        hipStream_t s);
+int launch_router(const uint16_t* wr, int E, int d, const float* x, const uint16_t* gamma,
+                  float eps, int M, float* logits, hipStream_t s);
+int launch_topk(const float* logits, int E, int k, int M, int32_t* sel, float* gates,
+                hipStream_t s);
+int launch_dequant(const Mat& w, const int32_t* row_map, int map_lo, int map_n, float* dst, hipStream_t s);
+int launch_fill16(uint16_t* dst, size_t n, uint16_t bits, hipStream_t s);
+
+}  // namespace bw

@@ -1,0 +1,213 @@
+// bw_misc.hip - the small kernels of the decode step (gfx950): embedding gather, final argmax,
+// MoE router GEMV and top-k, plus the dequantisation and fill kernels used by the parity tests.
+#include "bw_common.h"
+#include "bw_internal.h"
+
+namespace bw {
+
+// x[m][:] = fp32(E[token[m]][:]); out-of-range ids set the error word and read row 0
+__global__ __launch_bounds__(kBlock) void k_embed(const uint16_t* __restrict__ E, int32_t vocab,
+                                                  int32_t d, const int32_t* __restrict__ tokens,
+                                                  float* __restrict__ x, int32_t* err) {
+  const int m = blockIdx.x;
+  int tok = tokens[m];
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0) atomicOr(err, 2);
+    tok = 0;
+  }
+  const uint16_t* row = E + (int64_t)tok * d;
+  for (int i = threadIdx.x; i < d; i += kBlock) x[(int64_t)m * d + i] = f16_to_f32(row[i]);
+}
+
+int launch_embed(const uint16_t* embed, int32_t vocab, int32_t d, const int32_t* tokens, int M,
+                 float* x, int32_t* err, hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(kBlock), 0, s, embed, vocab, d, tokens, x, err);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// out[m] = index of the largest of the per-workgroup partials (lowest index on ties)
+__global__ __launch_bounds__(kBlock) void k_argmax_final(const float* __restrict__ val,
+                                                         const int32_t* __restrict__ idx, int parts,
+                                                         int32_t* __restrict__ out) {
+  const int m = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < parts; i += kBlock) {
+    float v = val[(int64_t)m * parts + i];
+    int k = idx[(int64_t)m * parts + i];
+    if (v > bv || (v == bv && k < bi)) { bv = v; bi = k; }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    float ov = __shfl_xor(bv, o);
+    int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+  __shared__ float wv[4];
+  __shared__ int wi[4];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { wv[w] = bv; wi[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; ++k)
+      if (wv[k] > wv[0] || (wv[k] == wv[0] && wi[k] < wi[0])) { wv[0] = wv[k]; wi[0] = wi[k]; }
+    out[m] = wi[0] == 0x7fffffff ? 0 : wi[0];
+  }
+}
+
+int launch_argmax_final(const float* val, const int32_t* idx, int parts, int M, int32_t* out,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_final, dim3(M), dim3(kBlock), 0, s, val, idx, parts, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Router logits r = W_r h with h = RMSNorm(x) * gamma, W_r fp16 [E][d]. Each wave takes rows; the
+// 64 lanes split d, 8 fp16 weights (one 16-byte load) per step.
+__global__ __launch_bounds__(kBlock) void k_router(const uint16_t* __restrict__ wr, int E, int d,
+                                                   const float* __restrict__ x,
+                                                   const uint16_t* __restrict__ gamma, float eps,
+                                                   float* __restrict__ logits, int rows_per_block) {
+  extern __shared__ float h[];
+  __shared__ float red[16];
+  const int m = blockIdx.y;
+  const float* xr = x + (int64_t)m * d;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += kBlock) ss = fmaf(xr[k], xr[k], ss);
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int k = threadIdx.x; k < d; k += kBlock) h[k] = xr[k] * r * f16_to_f32(gamma[k]);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * rows_per_block;
+  for (int e = row0 + wave; e < min(E, row0 + rows_per_block); e += 4) {
+    const uint16_t* wrow = wr + (int64_t)e * d;
+    float acc = 0.f;
+    for (int k = lane * 8; k < d; k += kWave * 8) {
+      u32x4 raw = load_stream16(wrow + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(f16_to_f32((uint16_t)(raw[i] & 0xFFFFu)), h[k + 2 * i], acc);
+        acc = fmaf(f16_to_f32((uint16_t)(raw[i] >> 16)), h[k + 2 * i + 1], acc);
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) logits[(int64_t)m * E + e] = acc;
+  }
+}
+
+int launch_router(const uint16_t* wr, int E, int d, const float* x, const uint16_t* gamma,
+                  float eps, int M, float* logits, hipStream_t s) {
+  const int rpb = 8;
+  hipLaunchKernelGGL(k_router, dim3((E + rpb - 1) / rpb, M), dim3(kBlock), sizeof(float) * d, s, wr, E,
+                     d, x, gamma, eps, logits, rpb);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// top-k of the router logits (descending, ties to the lower expert index) and the renormalised
+// gates softmax(r)_e / sum_{e' in top-k} softmax(r)_e' = exp(r_e - r_max) / sum_sel exp(r - r_max)
+__global__ __launch_bounds__(kBlock) void k_topk(const float* __restrict__ logits, int E, int k,
+                                                 int32_t* __restrict__ sel, float* __restrict__ gates) {
+  extern __shared__ float r[];
+  __shared__ float wv[4];
+  __shared__ int wi[4];
+  __shared__ int chosen[64];
+  const int m = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kBlock) r[e] = logits[(int64_t)m * E + e];
+  __syncthreads();
+  for (int round = 0; round < k; ++round) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int e = threadIdx.x; e < E; e += kBlock) {
+      bool taken = false;
+      for (int q = 0; q < round; ++q) taken |= (chosen[q] == e);
+      float v = r[e];
+      if (!taken && (v > bv || (v == bv && e < bi) || bi == 0x7fffffff)) { bv = v; bi = e; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float ov = __shfl_xor(bv, o);
+      int oi = __shfl_xor(bi, o);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { wv[w] = bv; wi[w] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float b0 = wv[0];
+      int i0 = wi[0];
+      for (int q = 1; q < 4; ++q)
+        if (wi[q] != 0x7fffffff && (i0 == 0x7fffffff || wv[q] > b0 || (wv[q] == b0 && wi[q] < i0))) { b0 = wv[q]; i0 = wi[q]; }
+      if (i0 == 0x7fffffff) {
+        // no comparable logit left (NaN): take the lowest index not chosen yet
+        for (int e = 0; e < E && i0 == 0x7fffffff; ++e) {
+          bool taken = false;
+          for (int q = 0; q < round; ++q) taken |= (chosen[q] == e);
+          if (!taken) i0 = e;
+        }
+      }
+      chosen[round] = i0;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float mx = r[chosen[0]];
+    float z = 0.f;
+    for (int q = 0; q < k; ++q) z += __expf(r[chosen[q]] - mx);
+    for (int q = 0; q < k; ++q) {
+      sel[(int64_t)m * k + q] = chosen[q];
+      gates[(int64_t)m * k + q] = __expf(r[chosen[q]] - mx) / z;
+    }
+  }
+}
+
+int launch_topk(const float* logits, int E, int k, int M, int32_t* sel, float* gates,
+                hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3(M), dim3(kBlock), sizeof(float) * E, s, logits, E, k, sel, gates);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Dequantise with the step's nibble extraction: element i < 16 of a block is the low nibble of
+// byte i, element 16 + i the high nibble; w = fp32(scale) * (q - 8), written in canonical order.
+__global__ __launch_bounds__(kBlock) void k_dequant(Mat w, const int32_t* __restrict__ row_map,
+                                                    int map_lo, int map_n, float* __restrict__ dst) {
+  const int nblk = w.K >> 5;
+  const int64_t total = (int64_t)w.N * nblk;
+  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < total; t += (int64_t)gridDim.x * kBlock) {
+    const int row = (int)(t / nblk), b = (int)(t - (int64_t)row * nblk);
+    const int cr = (row_map ? row_map[row] : row) - map_lo;
+    if (cr < 0 || cr >= map_n) continue;
+    const int j = b % w.lpr, c = b / w.lpr;
+    const float s = f16_to_f32(w.scales[(int64_t)row * nblk + j * w.nb + c]);
+    const u32x4 q = *(const u32x4*)(w.codes + (int64_t)row * (w.K >> 1) + b * 16);
+    float* out = dst + (int64_t)cr * w.K + b * 32;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = q[d] & 0x0F0F0F0Fu, hi = (q[d] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[4 * d + i] = s * ((float)((lo >> (8 * i)) & 0xFFu) - 8.0f);
+        out[16 + 4 * d + i] = s * ((float)((hi >> (8 * i)) & 0xFFu) - 8.0f);
+      }
+    }
+  }
+}
+
+int launch_dequant(const Mat& w, const int32_t* row_map, int map_lo, int map_n, float* dst, hipStream_t s) {
+  const int64_t total = (int64_t)w.N * (w.K >> 5);
+  int grid = (int)((total + kBlock - 1) / kBlock);
+  if (grid > 65535) grid = 65535;
+  hipLaunchKernelGGL(k_dequant, dim3(grid), dim3(kBlock), 0, s, w, row_map, map_lo, map_n, dst);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+__global__ void k_fill16(uint16_t* __restrict__ dst, size_t n, uint16_t bits) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = bits;
+}
+
+int launch_fill16(uint16_t* dst, size_t n, uint16_t bits, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill16, dim3(4096), dim3(kBlock), 0, s, dst, n, bits);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace bw

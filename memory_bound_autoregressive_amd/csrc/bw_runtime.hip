@@ -1,0 +1,896 @@
+// bw_runtime.hip - host side of libbw: model and pool objects, weight generation and layout, the
+// decode-step launch sequence and the C-ABI entry points declared in include/bw.h.
+//
+// The step (bw24 deep-dive page, section 4: callers only prefill and decode; section 2: dense and
+// MoE model strategies, standard and verify decoders) for M = batch * t token rows:
+//   embed -> per layer [RMSNorm + QKV GEMV + RoPE + KV append] -> [split attention + merge]
+//   -> [O GEMV + residual] -> dense: [RMSNorm + gate/up GEMV + SwiGLU] -> [down GEMV + residual]
+//                             MoE:   [RMSNorm + router] -> [top-k] -> [RMSNorm + expert gate/up +
+//                                    SwiGLU] -> [gated expert down + shared + residual]
+//   -> [final RMSNorm + lm_head GEMV + argmax partials] -> [argmax].
+// Every launch is enqueued on the caller's stream; nothing is allocated and nothing synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "bw.h"
+#include "bw_common.h"
+#include "bw_internal.h"
+#include "bw_synth.h"
+
+using namespace bw;
+
+// ---------------------------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------------------------
+
+static thread_local std::string g_err;
+
+static int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_OK(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(BW_EHIP, "%s: %s", #expr, hipGetErrorString(e_));    \
+  } while (0)
+
+// ---------------------------------------------------------------------------------------------
+// host threads
+// ---------------------------------------------------------------------------------------------
+
+static int host_threads() {
+  unsigned n = std::thread::hardware_concurrency();
+  if (n == 0) n = 4;
+  return (int)std::min(n, 16u);
+}
+
+template <class F>
+static void parallel_for(int64_t n, F fn) {
+  const int T = (int)std::min<int64_t>(host_threads(), std::max<int64_t>(n, 1));
+  std::vector<std::thread> th;
+  for (int t = 0; t < T; ++t)
+    th.emplace_back([=] {
+      for (int64_t i = t; i < n; i += T) fn(i);
+    });
+  for (auto& x : th) x.join();
+}
+
+// ---------------------------------------------------------------------------------------------
+// device arena: weights live in a few large allocations
+// ---------------------------------------------------------------------------------------------
+
+struct Arena {
+  std::vector<void*> blocks;
+  char* cur = nullptr;
+  size_t left = 0;
+  int alloc(size_t bytes, void** out) {
+    bytes = (bytes + 255) & ~(size_t)255;
+    if (bytes > left) {
+      size_t sz = std::max<size_t>(bytes, (size_t)1 << 30);
+      void* p = nullptr;
+      if (hipMalloc(&p, sz) != hipSuccess) return fail(BW_ENOMEM, "hipMalloc(%zu) failed", sz);
+      blocks.push_back(p);
+      cur = (char*)p;
+      left = sz;
+    }
+    *out = cur;
+    cur += bytes;
+    left -= bytes;
+    return 0;
+  }
+  void release() {
+    for (void* p : blocks) (void)hipFree(p);
+    blocks.clear();
+    cur = nullptr;
+    left = 0;
+  }
+};
+
+// ---------------------------------------------------------------------------------------------
+// objects
+// ---------------------------------------------------------------------------------------------
+
+struct LayerDev {
+  uint16_t* attn_norm = nullptr;
+  uint16_t* ffn_norm = nullptr;
+  Mat qkv, o, gu, dn;            // dense gate/up interleaved, down
+  uint16_t* router = nullptr;    // MoE [E][d]
+  ExpertTab ex;                  // MoE device pointer tables
+  std::vector<Mat> ex_gu, ex_dn; // MoE descriptors (routed then shared)
+};
+
+struct bw_model {
+  bw_model_config c{};
+  uint64_t seed = 0;
+  Arena arena;
+  std::vector<void*> ws;         // workspace allocations
+  uint16_t* embed = nullptr;
+  uint16_t* final_norm = nullptr;
+  Mat lm;
+  std::vector<LayerDev> L;
+  float2* rope = nullptr;
+  int32_t* qkv_map = nullptr;    // device row -> canonical row
+  std::map<int, int32_t*> gu_map;// F -> [2F] device row -> (gate i -> i, up i -> F + i)
+  // workspace
+  float* x = nullptr;            // [T][d] residual stream
+  float* q = nullptr;            // [T][H][D]
+  float* attn_part = nullptr;    // [T][H][max_splits][D+2]
+  float* attn_out = nullptr;     // [T][H*D]
+  float* act = nullptr;          // [T][act_width]
+  int64_t act_width = 0;
+  float* logits = nullptr;       // [T][V]
+  float* amax_val = nullptr;     // [T][lm_parts]
+  int32_t* amax_idx = nullptr;
+  int lm_parts = 0;
+  float* router_logits = nullptr;// [T][E]
+  int32_t* sel = nullptr;        // [L][T][k]
+  float* gates = nullptr;        // [L][T][k]
+  int32_t* err = nullptr;
+  int pages_per_split = 4;
+  int max_splits = 0;
+};
+
+struct bw_kv_pool {
+  const bw_model* m = nullptr;
+  int32_t n_pages = 0;
+  uint16_t* data = nullptr;
+  int64_t page_elems = 0;        // elements of one page-layer
+  int64_t layer_elems = 0;       // n_pages * page_elems
+};
+
+static bool is_moe(const bw_model_config& c) { return c.n_experts > 0; }
+
+// ---------------------------------------------------------------------------------------------
+// weight layout
+// ---------------------------------------------------------------------------------------------
+
+// Retile fp16 scales [N][K/32] -> [N][lpr][nb] (scale of block j + lpr*c at [n][j][c]).
+static void retile_scales(const uint16_t* src, int64_t N, int K, int lpr, int nb, uint16_t* dst) {
+  const int nblk = K / 32;
+  for (int64_t n = 0; n < N; ++n)
+    for (int j = 0; j < lpr; ++j)
+      for (int c = 0; c < nb; ++c) dst[n * nblk + j * nb + c] = src[n * nblk + j + lpr * c];
+}
+
+// Generate a matrix into host buffers, reorder its rows with dev_of_canon (nullptr = identity),
+// retile the scales and upload it.
+struct HostMat {
+  std::vector<uint8_t> codes;
+  std::vector<uint16_t> scales;
+};
+
+static void gen_canonical(uint64_t seed, uint32_t kind, uint32_t layer, uint32_t expert, int64_t N,
+                          int K, HostMat& h) {
+  h.codes.resize((size_t)N * K / 2);
+  h.scales.resize((size_t)N * K / 32);
+  const int64_t chunk = 512;
+  const int64_t nchunks = (N + chunk - 1) / chunk;
+  parallel_for(nchunks, [&](int64_t ci) {
+    int64_t r0 = ci * chunk, nr = std::min(chunk, N - r0);
+    bws_int4_matrix(seed, kind, layer, expert, N, K, r0, nr, h.codes.data() + r0 * (K / 2),
+                    h.scales.data() + r0 * (K / 32));
+  });
+}
+
+static int upload_mat(bw_model* m, const HostMat& h, int64_t N, int K,
+                      const std::vector<int64_t>* canon_of_dev, Mat* out) {
+  int lpr, nb;
+  gemv_lane_split(K, &lpr, &nb);
+  std::vector<uint8_t> codes((size_t)N * K / 2);
+  std::vector<uint16_t> sc_perm((size_t)N * K / 32), sc((size_t)N * K / 32);
+  const int64_t rb = K / 2, sb = K / 32;
+  parallel_for(N, [&](int64_t d) {
+    int64_t cr = canon_of_dev ? (*canon_of_dev)[d] : d;
+    memcpy(&codes[d * rb], &h.codes[cr * rb], rb);
+    memcpy(&sc_perm[d * sb], &h.scales[cr * sb], sb * 2);
+  });
+  retile_scales(sc_perm.data(), N, K, lpr, nb, sc.data());
+  void *pc, *ps;
+  if (int rc = m->arena.alloc(codes.size(), &pc)) return rc;
+  if (int rc = m->arena.alloc(sc.size() * 2, &ps)) return rc;
+  HIP_OK(hipMemcpy(pc, codes.data(), codes.size(), hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(ps, sc.data(), sc.size() * 2, hipMemcpyHostToDevice));
+  out->codes = (const uint8_t*)pc;
+  out->scales = (const uint16_t*)ps;
+  out->N = (int32_t)N;
+  out->K = K;
+  out->lpr = lpr;
+  out->nb = nb;
+  return 0;
+}
+
+// QKV device order: within the q block and the k block, the rows of each head are reordered to
+// (0, D/2, 1, D/2 + 1, ...) so that the two rows of every RoPE pair are adjacent; v is unchanged.
+static std::vector<int64_t> qkv_canon_of_dev(int H, int G, int D) {
+  std::vector<int64_t> v((size_t)(H + 2 * G) * D);
+  const int64_t nqk = (int64_t)(H + G) * D;
+  for (int64_t dr = 0; dr < (int64_t)v.size(); ++dr) {
+    if (dr < nqk) {
+      int64_t head = dr / D, loc = dr % D;
+      int64_t i = loc / 2, odd = loc % 2;
+      v[dr] = head * D + i + odd * (D / 2);
+    } else {
+      v[dr] = dr;
+    }
+  }
+  return v;
+}
+
+// gate/up interleave: device row 2i = gate row i, 2i + 1 = up row i
+static int upload_gate_up(bw_model* m, uint64_t seed, uint32_t layer, uint32_t expert, int F, int d,
+                          Mat* out) {
+  HostMat g, u, gu;
+  gen_canonical(seed, BWS_GATE, layer, expert, F, d, g);
+  gen_canonical(seed, BWS_UP, layer, expert, F, d, u);
+  gu.codes.resize((size_t)2 * F * d / 2);
+  gu.scales.resize((size_t)2 * F * d / 32);
+  const int64_t rb = d / 2, sb = d / 32;
+  for (int64_t i = 0; i < F; ++i) {
+    memcpy(&gu.codes[(2 * i) * rb], &g.codes[i * rb], rb);
+    memcpy(&gu.codes[(2 * i + 1) * rb], &u.codes[i * rb], rb);
+    memcpy(&gu.scales[(2 * i) * sb], &g.scales[i * sb], sb * 2);
+    memcpy(&gu.scales[(2 * i + 1) * sb], &u.scales[i * sb], sb * 2);
+  }
+  return upload_mat(m, gu, 2 * (int64_t)F, d, nullptr, out);
+}
+
+static int upload_plain(bw_model* m, uint64_t seed, uint32_t kind, uint32_t layer, uint32_t expert,
+                        int64_t N, int K, const std::vector<int64_t>* perm, Mat* out) {
+  HostMat h;
+  gen_canonical(seed, kind, layer, expert, N, K, h);
+  return upload_mat(m, h, N, K, perm, out);
+}
+
+static int upload_f16(bw_model* m, const std::vector<uint16_t>& v, uint16_t** out) {
+  void* p;
+  if (int rc = m->arena.alloc(v.size() * 2, &p)) return rc;
+  HIP_OK(hipMemcpy(p, v.data(), v.size() * 2, hipMemcpyHostToDevice));
+  *out = (uint16_t*)p;
+  return 0;
+}
+
+static int ws_alloc(bw_model* m, size_t bytes, void** out) {
+  void* p = nullptr;
+  if (bytes == 0) bytes = 256;
+  if (hipMalloc(&p, bytes) != hipSuccess) return fail(BW_ENOMEM, "hipMalloc(%zu) failed", bytes);
+  m->ws.push_back(p);
+  *out = p;
+  return 0;
+}
+
+static int make_gu_map(bw_model* m, int F) {
+  if (m->gu_map.count(F)) return 0;
+  std::vector<int32_t> v((size_t)2 * F);
+  for (int i = 0; i < F; ++i) {
+    v[2 * i] = i;
+    v[2 * i + 1] = F + i;
+  }
+  void* p;
+  if (int rc = ws_alloc(m, v.size() * 4, &p)) return rc;
+  HIP_OK(hipMemcpy(p, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+  m->gu_map[F] = (int32_t*)p;
+  return 0;
+}
+
+static int check_shape(const bw_model_config& c) {
+  if (c.n_layers < 1 || c.d_model < 32 || c.d_model % 32) return fail(BW_EINVAL, "d_model must be a positive multiple of 32");
+  if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads) return fail(BW_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(BW_EINVAL, "head_dim must be 64 or 128");
+  if (c.vocab < 1) return fail(BW_EINVAL, "vocab must be positive");
+  if (c.page_tokens != kPageTokens) return fail(BW_EINVAL, "page_tokens must be 16");
+  if (c.kv_dtype != BW_KV_F16 && c.kv_dtype != BW_KV_BF16) return fail(BW_EINVAL, "kv_dtype must be BW_KV_F16 or BW_KV_BF16");
+  if (c.max_positions < 1 || c.max_tokens < 1) return fail(BW_EINVAL, "max_positions and max_tokens must be positive");
+  int qr = c.n_q_heads / c.n_kv_heads;
+  (void)qr;
+  if (is_moe(c)) {
+    if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > 64) return fail(BW_EINVAL, "top_k must be in [1, min(64, n_experts)]");
+    if (c.expert_ffn < 32 || c.expert_ffn % 32 || c.expert_ffn > 2048) return fail(BW_EINVAL, "expert_ffn must be a multiple of 32 up to 2048");
+    if (c.n_shared < 0 || (c.n_shared > 0 && (c.shared_ffn < 32 || c.shared_ffn % 32 || c.shared_ffn > 2048))) return fail(BW_EINVAL, "shared_ffn must be a multiple of 32 up to 2048");
+    if (c.n_experts > 1024) return fail(BW_EINVAL, "n_experts must be <= 1024");
+  } else {
+    if (c.ffn_dim < 32 || c.ffn_dim % 32) return fail(BW_EINVAL, "ffn_dim must be a positive multiple of 32");
+  }
+  return 0;
+}
+
+extern "C" int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed, bw_model** out) {
+  if (!cfg || !out) return fail(BW_EINVAL, "null argument");
+  *out = nullptr;
+  if (int rc = check_shape(*cfg)) return rc;
+  bw_model* m = new bw_model();
+  m->c = *cfg;
+  m->seed = seed;
+  const bw_model_config& c = m->c;
+  const int d = c.d_model, H = c.n_q_heads, G = c.n_kv_heads, D = c.head_dim, Lc = c.n_layers;
+  auto bail = [&](int rc) {
+    bw_model_free(m);
+    return rc;
+  };
+  int rc = 0;
+  // embeddings, norms
+  {
+    std::vector<uint16_t> e((size_t)c.vocab * d);
+    const int64_t chunk = 256;
+    parallel_for((c.vocab + chunk - 1) / chunk, [&](int64_t ci) {
+      int64_t r0 = ci * chunk, nr = std::min<int64_t>(chunk, c.vocab - r0);
+      bws_embed_rows(seed, d, r0, nr, e.data() + r0 * d);
+    });
+    if ((rc = upload_f16(m, e, &m->embed))) return bail(rc);
+    std::vector<uint16_t> g(d);
+    bws_norm_gain(seed, BWS_FINAL_NORM, 0, d, g.data());
+    if ((rc = upload_f16(m, g, &m->final_norm))) return bail(rc);
+  }
+  const auto qkv_perm = qkv_canon_of_dev(H, G, D);
+  m->L.resize(Lc);
+  for (int l = 0; l < Lc; ++l) {
+    LayerDev& Ld = m->L[l];
+    std::vector<uint16_t> g(d);
+    bws_norm_gain(seed, BWS_ATTN_NORM, l, d, g.data());
+    if ((rc = upload_f16(m, g, &Ld.attn_norm))) return bail(rc);
+    bws_norm_gain(seed, BWS_FFN_NORM, l, d, g.data());
+    if ((rc = upload_f16(m, g, &Ld.ffn_norm))) return bail(rc);
+    if ((rc = upload_plain(m, seed, BWS_QKV, l, 0, (int64_t)(H + 2 * G) * D, d, &qkv_perm, &Ld.qkv))) return bail(rc);
+    if ((rc = upload_plain(m, seed, BWS_O, l, 0, d, H * D, nullptr, &Ld.o))) return bail(rc);
+    if (!is_moe(c)) {
+      if ((rc = upload_gate_up(m, seed, l, 0, c.ffn_dim, d, &Ld.gu))) return bail(rc);
+      if ((rc = upload_plain(m, seed, BWS_DOWN, l, 0, d, c.ffn_dim, nullptr, &Ld.dn))) return bail(rc);
+    } else {
+      const int E = c.n_experts, S = c.n_shared;
+      std::vector<uint16_t> r((size_t)E * d);
+      bws_router(seed, l, E, d, r.data());
+      if ((rc = upload_f16(m, r, &Ld.router))) return bail(rc);
+      Ld.ex_gu.resize(E + S);
+      Ld.ex_dn.resize(E + S);
+      for (int e = 0; e < E + S; ++e) {
+        const uint32_t ex = e < E ? 1u + (uint32_t)e : BWS_SHARED_EXPERT + (uint32_t)(e - E);
+        const int F = e < E ? c.expert_ffn : c.shared_ffn;
+        if ((rc = upload_gate_up(m, seed, l, ex, F, d, &Ld.ex_gu[e]))) return bail(rc);
+        if ((rc = upload_plain(m, seed, BWS_DOWN, l, ex, d, F, nullptr, &Ld.ex_dn[e]))) return bail(rc);
+      }
+      std::vector<const void*> t0(E + S), t1(E + S), t2(E + S), t3(E + S);
+      for (int e = 0; e < E + S; ++e) {
+        t0[e] = Ld.ex_gu[e].codes;
+        t1[e] = Ld.ex_gu[e].scales;
+        t2[e] = Ld.ex_dn[e].codes;
+        t3[e] = Ld.ex_dn[e].scales;
+      }
+      void* p;
+      const size_t tb = sizeof(void*) * (E + S);
+      if ((rc = m->arena.alloc(4 * tb, &p))) return bail(rc);
+      if (hipMemcpy(p, t0.data(), tb, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy((char*)p + tb, t1.data(), tb, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy((char*)p + 2 * tb, t2.data(), tb, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy((char*)p + 3 * tb, t3.data(), tb, hipMemcpyHostToDevice) != hipSuccess)
+        return bail(fail(BW_EHIP, "expert table upload failed"));
+      Ld.ex.gu_codes = (const uint8_t* const*)p;
+      Ld.ex.gu_scales = (const uint16_t* const*)((char*)p + tb);
+      Ld.ex.dn_codes = (const uint8_t* const*)((char*)p + 2 * tb);
+      Ld.ex.dn_scales = (const uint16_t* const*)((char*)p + 3 * tb);
+    }
+  }
+  if ((rc = upload_plain(m, seed, BWS_LM_HEAD, 0, 0, c.vocab, d, nullptr, &m->lm))) return bail(rc);
+  // RoPE table: angle pos * base^(-2i/D), evaluated in fp64, stored as fp32 (cos, sin)
+  {
+    std::vector<float2> t((size_t)c.max_positions * (D / 2));
+    parallel_for(c.max_positions, [&](int64_t pos) {
+      for (int i = 0; i < D / 2; ++i) {
+        double th = (double)pos * std::pow(c.rope_base, -2.0 * i / D);
+        t[pos * (D / 2) + i] = make_float2((float)std::cos(th), (float)std::sin(th));
+      }
+    });
+    void* p;
+    if ((rc = ws_alloc(m, t.size() * sizeof(float2), &p))) return bail(rc);
+    if (hipMemcpy(p, t.data(), t.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess)
+      return bail(fail(BW_EHIP, "rope upload failed"));
+    m->rope = (float2*)p;
+  }
+  // row maps for the parity entry points
+  {
+    std::vector<int32_t> v(qkv_perm.begin(), qkv_perm.end());
+    void* p;
+    if ((rc = ws_alloc(m, v.size() * 4, &p))) return bail(rc);
+    if (hipMemcpy(p, v.data(), v.size() * 4, hipMemcpyHostToDevice) != hipSuccess) return bail(fail(BW_EHIP, "map upload"));
+    m->qkv_map = (int32_t*)p;
+    if (!is_moe(c)) {
+      if ((rc = make_gu_map(m, c.ffn_dim))) return bail(rc);
+    } else {
+      if ((rc = make_gu_map(m, c.expert_ffn))) return bail(rc);
+      if (c.n_shared && (rc = make_gu_map(m, c.shared_ffn))) return bail(rc);
+    }
+  }
+  // workspace
+  {
+    const int64_t T = c.max_tokens;
+    m->max_splits = ((c.max_positions + kPageTokens - 1) / kPageTokens + m->pages_per_split - 1) / m->pages_per_split;
+    int64_t aw = is_moe(c) ? (int64_t)c.top_k * c.expert_ffn + (int64_t)c.n_shared * c.shared_ffn : c.ffn_dim;
+    aw = std::max<int64_t>(aw, 2 * (int64_t)std::max({c.ffn_dim, c.expert_ffn, c.shared_ffn}));
+    aw = std::max<int64_t>(aw, (int64_t)(H + 2 * G) * D);
+    aw = std::max<int64_t>(aw, d);
+    m->act_width = aw;
+    m->lm_parts = 4096;  // the GEMV launcher caps its grid at 4096 workgroups
+    void* p;
+    if ((rc = ws_alloc(m, sizeof(float) * T * d, &p))) return bail(rc);
+    m->x = (float*)p;
+    if ((rc = ws_alloc(m, sizeof(float) * T * H * D, &p))) return bail(rc);
+    m->q = (float*)p;
+    if ((rc = ws_alloc(m, sizeof(float) * T * H * m->max_splits * (D + 2), &p))) return bail(rc);
+    m->attn_part = (float*)p;
+    if ((rc = ws_alloc(m, sizeof(float) * T * H * D, &p))) return bail(rc);
+    m->attn_out = (float*)p;
+    if ((rc = ws_alloc(m, sizeof(float) * T * aw, &p))) return bail(rc);
+    m->act = (float*)p;
+    if ((rc = ws_alloc(m, sizeof(float) * T * c.vocab, &p))) return bail(rc);
+    m->logits = (float*)p;
+    if ((rc = ws_alloc(m, sizeof(float) * T * m->lm_parts, &p))) return bail(rc);
+    m->amax_val = (float*)p;
+    if ((rc = ws_alloc(m, sizeof(int32_t) * T * m->lm_parts, &p))) return bail(rc);
+    m->amax_idx = (int32_t*)p;
+    if ((rc = ws_alloc(m, 256, &p))) return bail(rc);
+    m->err = (int32_t*)p;
+    HIP_OK(hipMemset(m->err, 0, 256));
+    if (is_moe(c)) {
+      if ((rc = ws_alloc(m, sizeof(float) * T * c.n_experts, &p))) return bail(rc);
+      m->router_logits = (float*)p;
+      if ((rc = ws_alloc(m, sizeof(int32_t) * Lc * T * c.top_k, &p))) return bail(rc);
+      m->sel = (int32_t*)p;
+      if ((rc = ws_alloc(m, sizeof(float) * Lc * T * c.top_k, &p))) return bail(rc);
+      m->gates = (float*)p;
+    }
+  }
+  HIP_OK(hipDeviceSynchronize());
+  *out = m;
+  return BW_OK;
+}
+
+extern "C" int bw_model_free(bw_model* m) {
+  if (!m) return BW_OK;
+  (void)hipDeviceSynchronize();
+  m->arena.release();
+  for (void* p : m->ws) (void)hipFree(p);
+  delete m;
+  return BW_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// pool
+// ---------------------------------------------------------------------------------------------
+
+extern "C" int bw_kv_pool_create(const bw_model* m, int32_t n_pages, bw_kv_pool** out) {
+  if (!m || !out) return fail(BW_EINVAL, "null argument");
+  *out = nullptr;
+  if (n_pages < 1) return fail(BW_EINVAL, "n_pages must be positive");
+  const auto& c = m->c;
+  bw_kv_pool* p = new bw_kv_pool();
+  p->m = m;
+  p->n_pages = n_pages;
+  p->page_elems = (int64_t)c.n_kv_heads * 2 * kPageTokens * c.head_dim;
+  p->layer_elems = p->page_elems * n_pages;
+  const size_t bytes = (size_t)p->layer_elems * c.n_layers * 2;
+  void* d = nullptr;
+  if (hipMalloc(&d, bytes) != hipSuccess) {
+    delete p;
+    return fail(BW_ENOMEM, "hipMalloc(%zu) for the KV pool failed", bytes);
+  }
+  if (hipMemset(d, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(d);
+    delete p;
+    return fail(BW_EHIP, "pool clear failed");
+  }
+  p->data = (uint16_t*)d;
+  *out = p;
+  return BW_OK;
+}
+
+extern "C" int bw_kv_pool_free(bw_kv_pool* p) {
+  if (!p) return BW_OK;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(p->data);
+  delete p;
+  return BW_OK;
+}
+
+extern "C" int bw_kv_pool_fill(bw_kv_pool* p, uint16_t bits, void* stream) {
+  if (!p) return fail(BW_EINVAL, "null pool");
+  if (launch_fill16(p->data, (size_t)p->layer_elems * p->m->c.n_layers, bits, (hipStream_t)stream))
+    return fail(BW_EHIP, "fill launch failed");
+  return BW_OK;
+}
+
+// scatter staged page-layers to their physical pages, copying only the first nslot slots of
+// each (kv, head) row so that unused slots keep their contents
+__global__ void k_scatter_pages(const uint16_t* __restrict__ staged, const int32_t* __restrict__ dst_page,
+                                const int32_t* __restrict__ nslot, uint16_t* __restrict__ layer_base,
+                                int64_t page_elems, int D) {
+  const int i = blockIdx.x;
+  const int64_t dst = (int64_t)dst_page[i] * page_elems;
+  const int ns = nslot[i];
+  for (int64_t e = threadIdx.x; e < page_elems; e += blockDim.x) {
+    const int slot = (int)((e / D) % kPageTokens);
+    if (slot < ns) layer_base[dst + e] = staged[(int64_t)i * page_elems + e];
+  }
+}
+
+extern "C" int bw_kv_pool_synthesize(bw_kv_pool* p, uint64_t seed, const int32_t* seq_ids,
+                                     const int32_t* seq_lens, const int32_t* page_table,
+                                     int32_t batch, int32_t max_pages) {
+  if (!p || !seq_ids || !seq_lens || !page_table) return fail(BW_EINVAL, "null argument");
+  if (batch < 1 || max_pages < 1) return fail(BW_EINVAL, "batch and max_pages must be positive");
+  const auto& c = p->m->c;
+  const int G = c.n_kv_heads, D = c.head_dim;
+  const int dtype = c.kv_dtype == BW_KV_F16 ? BWS_KV_F16 : BWS_KV_BF16;
+  // list of (sequence, logical page) to write
+  struct Job { int b, lp, page, nslot; };
+  std::vector<Job> jobs;
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 0) return fail(BW_EINVAL, "negative seq_len");
+    const int np = (seq_lens[b] + kPageTokens - 1) / kPageTokens;
+    if (np > max_pages) return fail(BW_EINVAL, "seq_len %d needs more than max_pages pages", seq_lens[b]);
+    for (int lp = 0; lp < np; ++lp) {
+      const int page = page_table[(int64_t)b * max_pages + lp];
+      if (page < 0 || page >= p->n_pages) return fail(BW_EINVAL, "page id %d out of range", page);
+      jobs.push_back({b, lp, page, std::min(kPageTokens, seq_lens[b] - lp * kPageTokens)});
+    }
+  }
+  if (jobs.empty()) return BW_OK;
+  const int64_t pe = p->page_elems;
+  const int64_t chunk = std::min<int64_t>((int64_t)jobs.size(), std::max<int64_t>(1, (256ll << 20) / (pe * 2)));
+  std::vector<uint16_t> host((size_t)chunk * pe);
+  std::vector<int32_t> pid(chunk), ns(chunk);
+  void *dstage = nullptr, *dpid = nullptr, *dns = nullptr;
+  if (hipMalloc(&dstage, (size_t)chunk * pe * 2) != hipSuccess || hipMalloc(&dpid, chunk * 4) != hipSuccess ||
+      hipMalloc(&dns, chunk * 4) != hipSuccess) {
+    if (dstage) (void)hipFree(dstage);
+    if (dpid) (void)hipFree(dpid);
+    return fail(BW_ENOMEM, "staging allocation failed");
+  }
+  int rc = BW_OK;
+  for (int l = 0; l < c.n_layers && rc == BW_OK; ++l) {
+    for (int64_t j0 = 0; j0 < (int64_t)jobs.size() && rc == BW_OK; j0 += chunk) {
+      const int64_t nj = std::min<int64_t>(chunk, (int64_t)jobs.size() - j0);
+      parallel_for(nj, [&](int64_t i) {
+        const Job& jb = jobs[j0 + i];
+        std::vector<uint16_t> tmp((size_t)kPageTokens * 2 * G * D);
+        bws_kv_fill(seed, l, (uint32_t)seq_ids[jb.b], (int64_t)jb.lp * kPageTokens, jb.nslot, G, D, dtype, tmp.data());
+        uint16_t* dst = host.data() + i * pe;
+        // [tok][kv][g][d] -> [g][kv][slot][d]
+        for (int t = 0; t < jb.nslot; ++t)
+          for (int kv = 0; kv < 2; ++kv)
+            for (int g = 0; g < G; ++g)
+              memcpy(dst + (((int64_t)g * 2 + kv) * kPageTokens + t) * D, tmp.data() + (((int64_t)t * 2 + kv) * G + g) * D, D * 2);
+        pid[i] = jb.page;
+        ns[i] = jb.nslot;
+      });
+      if (hipMemcpy(dstage, host.data(), (size_t)nj * pe * 2, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy(dpid, pid.data(), nj * 4, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy(dns, ns.data(), nj * 4, hipMemcpyHostToDevice) != hipSuccess) {
+        rc = fail(BW_EHIP, "staging copy failed");
+        break;
+      }
+      hipLaunchKernelGGL(k_scatter_pages, dim3((unsigned)nj), dim3(256), 0, 0, (const uint16_t*)dstage,
+                         (const int32_t*)dpid, (const int32_t*)dns, p->data + (int64_t)l * p->layer_elems, pe, D);
+      if (hipDeviceSynchronize() != hipSuccess) rc = fail(BW_EHIP, "scatter failed");
+    }
+  }
+  (void)hipFree(dstage);
+  (void)hipFree(dpid);
+  (void)hipFree(dns);
+  return rc;
+}
+
+extern "C" int bw_kv_pool_read(const bw_kv_pool* p, int32_t layer, int32_t page, void* host_dst,
+                               size_t bytes) {
+  if (!p || !host_dst) return fail(BW_EINVAL, "null argument");
+  if (layer < 0 || layer >= p->m->c.n_layers || page < 0 || page >= p->n_pages)
+    return fail(BW_EINVAL, "layer or page out of range");
+  if (bytes < (size_t)p->page_elems * 2) return fail(BW_ERANGE, "destination too small");
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(host_dst, p->data + (int64_t)layer * p->layer_elems + (int64_t)page * p->page_elems,
+                   (size_t)p->page_elems * 2, hipMemcpyDeviceToHost));
+  return BW_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// the step
+// ---------------------------------------------------------------------------------------------
+
+static AttnParams attn_params(bw_model* m, const bw_kv_pool* pool, int l, const float* q,
+                              const int32_t* seq_lens, const int32_t* page_table, int t,
+                              int max_pages, float* out) {
+  const auto& c = m->c;
+  AttnParams a;
+  a.pool = pool->data + (int64_t)l * pool->layer_elems;
+  a.pool_page_stride = pool->page_elems;
+  a.n_pages = pool->n_pages;
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.t = t;
+  a.H = c.n_q_heads;
+  a.G = c.n_kv_heads;
+  a.D = c.head_dim;
+  a.pages_per_split = m->pages_per_split;
+  a.max_splits = m->max_splits;
+  a.scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+  a.part = m->attn_part;
+  a.out = out;
+  a.err = m->err;
+  return a;
+}
+
+extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens,
+                              const int32_t* seq_lens, const int32_t* page_table, int32_t batch,
+                              int32_t t, int32_t max_pages, float* logits_out, int32_t* argmax_out,
+                              void* stream) {
+  if (!m || !pool || !tokens || !seq_lens || !page_table) return fail(BW_EINVAL, "null argument");
+  if (pool->m != m) return fail(BW_ESTATE, "pool belongs to another model");
+  if (batch < 1 || t < 1 || max_pages < 1) return fail(BW_EINVAL, "batch, t and max_pages must be positive");
+  const int M = batch * t;
+  if (M > m->c.max_tokens) return fail(BW_ERANGE, "batch * t = %d exceeds max_tokens %d", M, m->c.max_tokens);
+  if ((int64_t)max_pages * kPageTokens > (int64_t)m->max_splits * m->pages_per_split * kPageTokens &&
+      (int64_t)max_pages > ((int64_t)m->c.max_positions + kPageTokens - 1) / kPageTokens + 1)
+    ;  // a wide page table is fine; positions are bounded by max_positions on the device
+  const auto& c = m->c;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = c.d_model, H = c.n_q_heads, G = c.n_kv_heads, D = c.head_dim;
+  if (launch_embed(m->embed, c.vocab, d, tokens, M, m->x, m->err, s)) return fail(BW_EHIP, "embed launch failed");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerDev& Ld = m->L[l];
+    // RMSNorm + QKV + RoPE + KV append
+    GemvParams g;
+    g.w = Ld.qkv;
+    g.n_rows = Ld.qkv.N;
+    g.x = m->x;
+    g.x_stride = d;
+    g.gamma = Ld.attn_norm;
+    g.eps = c.rms_eps;
+    g.H = H;
+    g.G = G;
+    g.D = D;
+    g.rope = m->rope;
+    g.max_pos = c.max_positions;
+    g.seq_lens = seq_lens;
+    g.t = t;
+    g.page_table = page_table;
+    g.max_pages = max_pages;
+    g.pool = pool->data + (int64_t)l * pool->layer_elems;
+    g.pool_page_stride = pool->page_elems;
+    g.n_pages = pool->n_pages;
+    g.kv_dtype = c.kv_dtype;
+    g.qout = m->q;
+    g.err = m->err;
+    if (launch_gemv(IN_RMSNORM, EPI_QKV, g, M, s)) return fail(BW_EHIP, "qkv launch failed (layer %d)", l);
+    // attention
+    AttnParams a = attn_params(m, pool, l, m->q, seq_lens, page_table, t, max_pages, m->attn_out);
+    if (launch_attention(a, c.kv_dtype, batch, s)) return fail(BW_EHIP, "attention launch failed (layer %d)", l);
+    // O + residual
+    GemvParams o;
+    o.w = Ld.o;
+    o.n_rows = Ld.o.N;
+    o.x = m->attn_out;
+    o.x_stride = (int64_t)H * D;
+    o.y = m->x;
+    o.y_stride = d;
+    if (launch_gemv(IN_PLAIN, EPI_RESID, o, M, s)) return fail(BW_EHIP, "o launch failed (layer %d)", l);
+    if (!is_moe(c)) {
+      GemvParams gu;
+      gu.w = Ld.gu;
+      gu.n_rows = Ld.gu.N;
+      gu.x = m->x;
+      gu.x_stride = d;
+      gu.gamma = Ld.ffn_norm;
+      gu.eps = c.rms_eps;
+      gu.y = m->act;
+      gu.y_stride = m->act_width;
+      if (launch_gemv(IN_RMSNORM, EPI_SWIGLU, gu, M, s)) return fail(BW_EHIP, "gate/up launch failed (layer %d)", l);
+      GemvParams dn;
+      dn.w = Ld.dn;
+      dn.n_rows = Ld.dn.N;
+      dn.x = m->act;
+      dn.x_stride = m->act_width;
+      dn.y = m->x;
+      dn.y_stride = d;
+      if (launch_gemv(IN_PLAIN, EPI_RESID, dn, M, s)) return fail(BW_EHIP, "down launch failed (layer %d)", l);
+    } else {
+      int32_t* sel = m->sel + (int64_t)l * c.max_tokens * c.top_k;
+      float* gates = m->gates + (int64_t)l * c.max_tokens * c.top_k;
+      if (launch_router(Ld.router, c.n_experts, d, m->x, Ld.ffn_norm, c.rms_eps, M, m->router_logits, s))
+        return fail(BW_EHIP, "router launch failed (layer %d)", l);
+      if (launch_topk(m->router_logits, c.n_experts, c.top_k, M, sel, gates, s))
+        return fail(BW_EHIP, "top-k launch failed (layer %d)", l);
+      GemvParams gu;
+      gu.w.K = d;
+      gu.n_rows = c.top_k * 2 * c.expert_ffn + c.n_shared * 2 * c.shared_ffn;
+      gu.x = m->x;
+      gu.x_stride = d;
+      gu.gamma = Ld.ffn_norm;
+      gu.eps = c.rms_eps;
+      gu.y = m->act;
+      gu.y_stride = m->act_width;
+      gu.sel = sel;
+      gu.gates = gates;
+      gu.n_experts = c.n_experts;
+      gu.top_k = c.top_k;
+      gu.n_shared = c.n_shared;
+      gu.Fe = c.expert_ffn;
+      gu.Fs = c.shared_ffn;
+      gu.ex = Ld.ex;
+      if (launch_gemv(IN_RMSNORM, EPI_MOE_SWIGLU, gu, M, s)) return fail(BW_EHIP, "expert gate/up launch failed (layer %d)", l);
+      GemvParams dn = gu;
+      dn.n_rows = d;
+      dn.x = m->act;
+      dn.x_stride = m->act_width;
+      dn.gamma = nullptr;
+      dn.y = m->x;
+      dn.y_stride = d;
+      if (int e = launch_gemv(IN_MOE_DOWN, EPI_RESID, dn, M, s))
+        return fail(BW_EHIP, "expert down launch failed (layer %d, code %d: -2 = unsupported K %d)", l, e,
+                    c.top_k * c.expert_ffn + c.n_shared * c.shared_ffn);
+    }
+  }
+  // final RMSNorm + lm_head + argmax
+  GemvParams lm;
+  lm.w = m->lm;
+  lm.n_rows = m->lm.N;
+  lm.x = m->x;
+  lm.x_stride = d;
+  lm.gamma = m->final_norm;
+  lm.eps = c.rms_eps;
+  lm.y = logits_out ? logits_out : m->logits;
+  lm.y_stride = c.vocab;
+  lm.amax_val = m->amax_val;
+  lm.amax_idx = m->amax_idx;
+  int lm_grid = 0;
+  if (launch_gemv(IN_RMSNORM, EPI_LOGITS, lm, M, s, &lm_grid)) return fail(BW_EHIP, "lm_head launch failed");
+  if (lm_grid > m->lm_parts) return fail(BW_EHIP, "lm_head grid exceeds the argmax workspace");
+  if (argmax_out && launch_argmax_final(m->amax_val, m->amax_idx, lm_grid, M, argmax_out, s))
+    return fail(BW_EHIP, "argmax launch failed");
+  return BW_OK;
+}
+
+extern "C" const char* bw_last_error(void) { return g_err.c_str(); }
+
+extern "C" int bw_check_device_error(bw_model* m, void* stream, int32_t* flags) {
+  if (!m || !flags) return fail(BW_EINVAL, "null argument");
+  HIP_OK(hipStreamSynchronize((hipStream_t)stream));
+  HIP_OK(hipMemcpy(flags, m->err, 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemset(m->err, 0, 4));
+  HIP_OK(hipDeviceSynchronize());
+  return BW_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// parity-test entry points
+// ---------------------------------------------------------------------------------------------
+
+// matrix descriptor, its device->canonical row map and the canonical row count
+static int find_mat(const bw_model* m, int which, int layer, int expert, Mat* w, const int32_t** map,
+                    int* n_canon, int* half) {
+  const auto& c = m->c;
+  *map = nullptr;
+  *half = -1;  // for interleaved gate/up: 0 = gate half, 1 = up half
+  if (which == BW_MAT_LM_HEAD) {
+    *w = m->lm;
+    *n_canon = m->lm.N;
+    return 0;
+  }
+  if (layer < 0 || layer >= c.n_layers) return fail(BW_EINVAL, "layer out of range");
+  const LayerDev& Ld = m->L[layer];
+  switch (which) {
+    case BW_MAT_QKV: *w = Ld.qkv; *map = m->qkv_map; *n_canon = Ld.qkv.N; return 0;
+    case BW_MAT_O: *w = Ld.o; *n_canon = Ld.o.N; return 0;
+    case BW_MAT_DOWN:
+      if (!is_moe(c)) { *w = Ld.dn; *n_canon = Ld.dn.N; return 0; }
+      if (expert < 0 || expert >= c.n_experts) return fail(BW_EINVAL, "expert out of range");
+      *w = Ld.ex_dn[expert]; *n_canon = w->N; return 0;
+    case BW_MAT_SDOWN:
+      if (!is_moe(c) || expert < 0 || expert >= c.n_shared) return fail(BW_EINVAL, "shared expert out of range");
+      *w = Ld.ex_dn[c.n_experts + expert]; *n_canon = w->N; return 0;
+    case BW_MAT_GATE:
+    case BW_MAT_UP:
+    case BW_MAT_SGATE:
+    case BW_MAT_SUP: {
+      const bool shared = which == BW_MAT_SGATE || which == BW_MAT_SUP;
+      if (!is_moe(c)) {
+        if (shared) return fail(BW_EINVAL, "dense model has no shared expert");
+        *w = Ld.gu;
+      } else if (shared) {
+        if (expert < 0 || expert >= c.n_shared) return fail(BW_EINVAL, "shared expert out of range");
+        *w = Ld.ex_gu[c.n_experts + expert];
+      } else {
+        if (expert < 0 || expert >= c.n_experts) return fail(BW_EINVAL, "expert out of range");
+        *w = Ld.ex_gu[expert];
+      }
+      const int F = w->N / 2;
+      *map = m->gu_map.at(F);
+      *n_canon = F;
+      *half = (which == BW_MAT_GATE || which == BW_MAT_SGATE) ? 0 : 1;
+      return 0;
+    }
+    default: return fail(BW_EINVAL, "unknown matrix selector %d", which);
+  }
+}
+
+extern "C" int bw_debug_dequant(const bw_model* m, int32_t which, int32_t layer, int32_t expert,
+                                float* dst, void* stream) {
+  if (!m || !dst) return fail(BW_EINVAL, "null argument");
+  Mat w;
+  const int32_t* map;
+  int n, half;
+  if (int rc = find_mat(m, which, layer, expert, &w, &map, &n, &half)) return rc;
+  // interleaved gate/up: keep only the requested half (canonical rows [half*F, half*F + F))
+  const int lo = half < 0 ? 0 : half * n;
+  if (launch_dequant(w, map, lo, n, dst, (hipStream_t)stream)) return fail(BW_EHIP, "dequant launch failed");
+  return BW_OK;
+}
+
+extern "C" int bw_debug_matvec(bw_model* m, int32_t which, int32_t layer, int32_t expert,
+                               const float* x, int32_t n_vec, float* y, void* stream) {
+  if (!m || !x || !y) return fail(BW_EINVAL, "null argument");
+  if (n_vec < 1) return fail(BW_EINVAL, "n_vec must be positive");
+  if (n_vec > m->c.max_tokens) return fail(BW_ERANGE, "n_vec exceeds max_tokens");
+  Mat w;
+  const int32_t* map;
+  int n, half;
+  if (int rc = find_mat(m, which, layer, expert, &w, &map, &n, &half)) return rc;
+  GemvParams g;
+  g.w = w;
+  g.n_rows = w.N;
+  g.x = x;
+  g.x_stride = w.K;
+  g.row_map = map;
+  g.map_lo = half < 0 ? 0 : half * n;
+  g.map_n = n;
+  g.y = y;
+  g.y_stride = n;
+  if (launch_gemv(IN_PLAIN, EPI_STORE_CANON, g, n_vec, (hipStream_t)stream)) return fail(BW_EHIP, "gemv launch failed");
+  return BW_OK;
+}
+
+extern "C" int bw_debug_attention(bw_model* m, bw_kv_pool* pool, int32_t layer, const float* q,
+                                  const int32_t* seq_lens, const int32_t* page_table, int32_t batch,
+                                  int32_t t, int32_t max_pages, float* out, void* stream) {
+  if (!m || !pool || !q || !seq_lens || !page_table || !out) return fail(BW_EINVAL, "null argument");
+  if (pool->m != m) return fail(BW_ESTATE, "pool belongs to another model");
+  if (layer < 0 || layer >= m->c.n_layers) return fail(BW_EINVAL, "layer out of range");
+  if (batch < 1 || t < 1 || batch * t > m->c.max_tokens) return fail(BW_ERANGE, "batch * t out of range");
+  AttnParams a = attn_params(m, pool, layer, q, seq_lens, page_table, t, max_pages, out);
+  if (launch_attention(a, m->c.kv_dtype, batch, (hipStream_t)stream)) return fail(BW_EHIP, "attention launch failed");
+  return BW_OK;
+}
+
+extern "C" int bw_debug_read_experts(bw_model* m, int32_t n_rows, int32_t* host_dst, void* stream) {
+  if (!m || !host_dst) return fail(BW_EINVAL, "null argument");
+  if (!is_moe(m->c)) return fail(BW_ESTATE, "dense model");
+  if (n_rows < 1 || n_rows > m->c.max_tokens) return fail(BW_ERANGE, "n_rows out of range");
+  HIP_OK(hipStreamSynchronize((hipStream_t)stream));
+  const auto& c = m->c;
+  for (int l = 0; l < c.n_layers; ++l)
+    HIP_OK(hipMemcpy(host_dst + (size_t)l * n_rows * c.top_k, m->sel + (size_t)l * c.max_tokens * c.top_k,
+                     sizeof(int32_t) * n_rows * c.top_k, hipMemcpyDeviceToHost));
+  return BW_OK;
+}
+
+extern "C" int bw_debug_read_hidden(bw_model* m, int32_t n_rows, float* host_dst, void* stream) {
+  if (!m || !host_dst) return fail(BW_EINVAL, "null argument");
+  if (n_rows < 1 || n_rows > m->c.max_tokens) return fail(BW_ERANGE, "n_rows out of range");
+  HIP_OK(hipStreamSynchronize((hipStream_t)stream));
+  HIP_OK(hipMemcpy(host_dst, m->x, sizeof(float) * n_rows * m->c.d_model, hipMemcpyDeviceToHost));
+  return BW_OK;
+}

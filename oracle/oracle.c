@@ -156,19 +156,26 @@ void or_quantize(const double* W, const uint16_t* scales, int64_t N, int64_t K, 
     }
 }
 
-/* y[n] = sum_k W[n][k] x[k], k ascending, W[n][k] formed exactly in fp64 */
+/* y[n] = sum_k W[n][k] x[k], k ascending, W[n][k] formed exactly in fp64. The block scales of
+ * a row are decoded once per row (the same values the per-weight formula uses). */
 void or_gemv(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, const double* x,
              double* y) {
-#pragma omp parallel for schedule(static)
-  for (int64_t n = 0; n < N; ++n) {
-    const uint8_t* rc = codes + n * (K / 2);
-    const uint16_t* rs = scales + n * (K / 32);
-    double acc = 0.0;
-    for (int64_t k = 0; k < K; ++k) {
-      double w = or_f16_to_f64(rs[k / 32]) * (double)(or_code(rc, k) - 8);
-      acc += w * x[k];
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(K / 32));
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+      const uint8_t* rc = codes + n * (K / 2);
+      const uint16_t* rs = scales + n * (K / 32);
+      for (int64_t b = 0; b < K / 32; ++b) s[b] = or_f16_to_f64(rs[b]);
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double w = s[k / 32] * (double)(or_code(rc, k) - 8);
+        acc += w * x[k];
+      }
+      y[n] = acc;
     }
-    y[n] = acc;
+    free(s);
   }
 }
 

@@ -1,0 +1,144 @@
+"""End-to-end parity of the decode step against the fp64 oracle (GPU).
+
+Both sides are teacher-forced on the oracle's greedy tokens, so every step is compared on the
+same inputs: logits within 2e-2 max-abs, and the GPU's greedy token equal to the oracle's wherever
+the oracle's top-2 margin exceeds 1e-2. For MoE, a router selection that differs from the
+oracle's only by experts within 1e-4 of the top-k boundary is a valid near tie: the oracle checks
+it and follows it (any other difference fails).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import memory_bound_autoregressive_amd as bw
+from memory_bound_autoregressive_amd import configs
+from memory_bound_autoregressive_amd.session import Session
+
+from helpers import LOGITS_MAX_ABS, TOKEN_MARGIN, oracle_cfg, top2_margin
+
+pytestmark = pytest.mark.gpu
+
+MOE_SMALL = dict(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=0, vocab=512,
+                 rms_eps=1e-6, rope_base=1e6, kv_dtype="bf16", page_tokens=16, n_experts=16, top_k=3,
+                 expert_ffn=128, n_shared=1, shared_ffn=128, name="moe-small")
+ROUTER_TAU = 1e-4
+
+
+def _cuda_i32(v):
+    return torch.tensor(v, dtype=torch.int32, device="cuda")
+
+
+class Pair:
+    """GPU session + oracle for one sequence, stepping both on the same tokens."""
+
+    def __init__(self, cfg, seed, max_len, ctx0=0, synth_seed=None):
+        self.cfg = cfg
+        self.s = Session(cfg, seed=seed, max_len=[max_len], max_tokens=4, pool_seed=seed + 100)
+        self.om = oracle.Model(oracle_cfg(cfg), seed)
+        self.okv = oracle.KV(self.om, 1, max_len - ctx0 + 1)
+        if ctx0:
+            self.s.synthesize(synth_seed, [ctx0])
+            self.okv.set_synth(0, synth_seed, 0, ctx0)
+        self.pos = ctx0
+        self.moe = cfg.get("n_experts", 0) > 0
+        self.adopted = 0
+
+    def step(self, tokens):
+        t = len(tokens)
+        logits, am = self.s.step(_cuda_i32(list(tokens)), _cuda_i32([self.pos]), t=t)
+        g = logits.cpu().numpy().astype(np.float64)
+        gam = am.cpu().numpy()
+        sel_in = None
+        if self.moe:
+            L, k = self.cfg["n_layers"], self.cfg["top_k"]
+            ex = np.empty((L, t, k), dtype=np.int32)
+            bw.bw_debug_read_experts(self.s.model, t, ex)
+            sel_in = np.ascontiguousarray(ex.transpose(1, 0, 2))
+        r = oracle.forward(self.om, self.okv, 0, list(tokens), self.pos, sel_in=sel_in, tau=ROUTER_TAU)
+        assert r["rc"] == 0, "GPU expert selection is not a near tie of the oracle's"
+        self.adopted += r["adopted"]
+        self.pos += t
+        return g, gam, r["logits"]
+
+    def close(self):
+        self.s.close()
+
+
+def _compare(g, gam, o, where):
+    err = float(np.max(np.abs(g - o)))
+    assert err <= LOGITS_MAX_ABS, (where, err)
+    for i in range(o.shape[0]):
+        ot = int(np.argmax(o[i]))
+        if top2_margin(o[i]) > TOKEN_MARGIN:
+            assert int(gam[i]) == ot, (where, i, int(gam[i]), ot)
+    return err
+
+
+@pytest.mark.parametrize("cfg,seed", [(configs.TINY, 1001), (MOE_SMALL, 1011)], ids=["tiny", "moe-small"])
+def test_prompt_then_greedy_decode(cfg, seed):
+    prompt_len, steps = cfg.get("prompt", 16), cfg.get("steps", 32)
+    rng = np.random.default_rng(seed)
+    prompt = rng.integers(0, cfg["vocab"], prompt_len)
+    p = Pair(cfg, seed, prompt_len + steps + 1)
+    worst = 0.0
+    try:
+        for i, tok in enumerate(prompt):
+            g, gam, o = p.step([int(tok)])
+            worst = max(worst, _compare(g, gam, o, f"prompt {i}"))
+        nxt = int(np.argmax(o[0]))
+        for i in range(steps):
+            g, gam, o = p.step([nxt])
+            worst = max(worst, _compare(g, gam, o, f"decode {i}"))
+            nxt = int(np.argmax(o[0]))  # teacher forcing on the oracle's token
+        print(f"[result] {cfg['name']} max |logit diff| = {worst:.3e}, near-tie router sets adopted = {p.adopted}")
+    finally:
+        p.close()
+
+
+def test_verify_step_equals_sequential_greedy():
+    """Four tokens verified in one call (the accepted token plus three drafts equal to the greedy
+    continuation) give the same per-position argmax as four single-token steps."""
+    cfg, seed = configs.TINY, 1021
+    rng = np.random.default_rng(seed)
+    prompt = rng.integers(0, cfg["vocab"], 12)
+    seq = Pair(cfg, seed, 40)
+    ver = Pair(cfg, seed, 40)
+    try:
+        for tok in prompt[:-1]:
+            seq.step([int(tok)])
+            ver.step([int(tok)])
+        cur = int(prompt[-1])
+        toks, am_seq, lg_seq = [], [], []
+        for i in range(4):
+            g, gam, o = seq.step([cur])
+            toks.append(cur)
+            am_seq.append(int(gam[0]))
+            lg_seq.append(g[0])
+            cur = int(np.argmax(o[0]))
+        g4, gam4, o4 = ver.step(toks)
+        _compare(g4, gam4, o4, "verify")
+        for i in range(4):
+            if top2_margin(o4[i]) > TOKEN_MARGIN:
+                assert int(gam4[i]) == am_seq[i], i
+        assert np.max(np.abs(g4 - np.stack(lg_seq))) <= LOGITS_MAX_ABS
+    finally:
+        seq.close()
+        ver.close()
+
+
+@pytest.mark.timeout(900)
+def test_dense_9b_synthesized_context():
+    cfg = configs.DENSE_9B
+    ctx, steps, seed = 2048, 3, cfg["seed"]
+    p = Pair(cfg, seed, ctx + steps + 1, ctx0=ctx, synth_seed=seed + 7)
+    try:
+        nxt = int(np.random.default_rng(seed).integers(0, cfg["vocab"]))
+        worst = 0.0
+        for i in range(steps):
+            g, gam, o = p.step([nxt])
+            worst = max(worst, _compare(g, gam, o, f"9b step {i}"))
+            nxt = int(np.argmax(o[0]))
+        print(f"[result] dense-9b max |logit diff| = {worst:.3e}")
+    finally:
+        p.close()

@@ -1,0 +1,217 @@
+"""Kernel-level parity of the HIP decode-step kernels against the fp64 oracle (GPU).
+
+Each kernel runs alone through the C-ABI's parity entry points on seeded inputs; the oracle gets
+the same inputs. Dequantisation and page indexing must match bit for bit; every other kernel
+output must be within 1e-3 relative L2 of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import memory_bound_autoregressive_amd as bw
+from memory_bound_autoregressive_amd import configs
+from memory_bound_autoregressive_amd.session import Session
+
+from helpers import KERNEL_REL_L2, kv_values, oracle_cfg, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TINY = configs.TINY
+# one layer of the 9B shape (every matrix at its real size), small vocabulary
+LAYER9B = dict(configs.DENSE_9B, n_layers=1, vocab=4096)
+# one layer of the 27B shape
+LAYER27B = dict(configs.DENSE_27B, n_layers=1, vocab=2048)
+# a small MoE with the 35B-A3B layer structure (router, top-k, shared expert)
+MOE_SMALL = dict(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=0, vocab=512,
+                 rms_eps=1e-6, rope_base=1e6, kv_dtype="bf16", page_tokens=16, n_experts=16, top_k=3,
+                 expert_ffn=128, n_shared=1, shared_ffn=128)
+
+
+def _model(cfg, seed, max_positions=512, max_tokens=8):
+    print(f"[case] load model {cfg.get('name', 'custom')} seed={seed}", flush=True)
+    return bw.bw_model_load_synthetic(bw.make_config(cfg, max_positions, max_tokens), seed)
+
+
+def _matrices(cfg):
+    names = ["qkv", "o", "lm_head"]
+    if cfg.get("n_experts", 0):
+        names += ["gate", "up", "down", "shared_gate", "shared_up", "shared_down"]
+    else:
+        names += ["gate", "up", "down"]
+    return names
+
+
+def _canonical(om: oracle.Model, name: str, expert: int = 0):
+    which = {"shared_gate": "shared_gate", "shared_up": "shared_up", "shared_down": "shared_down"}.get(name, name)
+    return om.matrix(which, 0, expert)
+
+
+@pytest.mark.parametrize("cfg,seed", [(TINY, 11), (LAYER9B, 12), (MOE_SMALL, 13)], ids=["tiny", "9b-layer", "moe"])
+def test_dequant_bit_exact(cfg, seed):
+    m = _model(cfg, seed)
+    om = oracle.Model(oracle_cfg(cfg), seed)
+    try:
+        for name in _matrices(cfg):
+            for expert in ([0, 5] if cfg.get("n_experts", 0) and name in ("gate", "up", "down") else [0]):
+                codes, scales = _canonical(om, name, expert)
+                N, K = codes.shape[0], codes.shape[1] * 2
+                print(f"[case] dequant {name} expert={expert} [{N}x{K}]", flush=True)
+                out = torch.empty((N, K), dtype=torch.float32, device="cuda")
+                bw.bw_debug_dequant(m, name, 0, expert, out)
+                torch.cuda.synchronize()
+                ref = oracle.dequant(codes, scales).astype(np.float32)
+                got = out.cpu().numpy()
+                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), name
+    finally:
+        bw.bw_model_free(m)
+
+
+@pytest.mark.parametrize("cfg,seed", [(TINY, 21), (LAYER9B, 22), (LAYER27B, 24), (MOE_SMALL, 23)],
+                         ids=["tiny", "9b-layer", "27b-layer", "moe"])
+def test_gemv_matches_oracle(cfg, seed):
+    m = _model(cfg, seed)
+    om = oracle.Model(oracle_cfg(cfg), seed)
+    rng = np.random.default_rng(seed)
+    try:
+        for name in _matrices(cfg):
+            codes, scales = _canonical(om, name, 3 if (cfg.get("n_experts", 0) and name in ("gate", "up", "down")) else 0)
+            expert = 3 if (cfg.get("n_experts", 0) and name in ("gate", "up", "down")) else 0
+            N, K = codes.shape[0], codes.shape[1] * 2
+            print(f"[case] gemv {name} [{N}x{K}]", flush=True)
+            x = rng.standard_normal(K).astype(np.float32)
+            xd = torch.from_numpy(x).cuda().reshape(1, K)
+            y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+            bw.bw_debug_matvec(m, name, 0, expert, xd, y)
+            torch.cuda.synchronize()
+            ref = oracle.gemv(codes, scales, x.astype(np.float64))
+            err = rel_l2(y.cpu().numpy()[0], ref)
+            assert err <= KERNEL_REL_L2, (name, err)
+            assert err <= 1e-5, (name, err)  # fp32 accumulation is far inside the bound
+    finally:
+        bw.bw_model_free(m)
+
+
+def _attention_case(cfg, seed, lens, t, pool_seed, poison=False):
+    """Synthesised contexts, random rotated queries; returns (gpu out, session)."""
+    H, G, D = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    B = len(lens)
+    s = Session(cfg, seed=seed, max_len=[n + t for n in lens], max_tokens=B * t, pool_seed=pool_seed)
+    if poison:
+        s.poison(0x7E00 if cfg["kv_dtype"] == "f16" else 0x7FC0)
+    s.synthesize(seed + 1, [n + t for n in lens])
+    rng = np.random.default_rng(seed + 2)
+    q = (rng.standard_normal((B * t, H, D)) * 2).astype(np.float32)
+    qd = torch.from_numpy(q).cuda()
+    out = torch.empty_like(qd)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    bw.bw_debug_attention(s.model, s.pool, 0, qd, sl, s.page_table, B, t, s.max_pages, out)
+    torch.cuda.synchronize()
+    return q, out.cpu().numpy(), s
+
+
+@pytest.mark.parametrize("cfg,lens,t", [
+    (TINY, [1, 37, 300], 1), (TINY, [5, 64, 200], 4),
+    (LAYER9B, [2048], 1), (LAYER9B, [1, 17, 999], 4), (LAYER27B, [700], 1),
+], ids=["tiny-t1", "tiny-t4", "9b-2048", "9b-t4-ragged", "27b-t1"])
+def test_attention_matches_oracle(cfg, lens, t):
+    seed = 31
+    H, G, D = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    rep = H // G
+    dtype = synth.KV_F16 if cfg["kv_dtype"] == "f16" else synth.KV_BF16
+    print(f"[case] attention {cfg.get('name')} lens={lens} t={t}", flush=True)
+    q, got, s = _attention_case(cfg, seed, lens, t, pool_seed=5)
+    try:
+        for b, n0 in enumerate(lens):
+            kv = kv_values(synth, seed + 1, 0, b, n0 + t, G, D, dtype)
+            for ti in range(t):
+                n = n0 + ti + 1
+                ref = np.stack([oracle.attention(q[b * t + ti, h].astype(np.float64), kv[:n, 0, h // rep], kv[:n, 1, h // rep])
+                                for h in range(H)])
+                err = rel_l2(got[b * t + ti], ref)
+                assert err <= KERNEL_REL_L2, (b, ti, err)
+                assert err <= 1e-5, (b, ti, err)
+    finally:
+        s.close()
+
+
+def test_attention_invariant_to_pool_permutation_and_poison():
+    cfg = LAYER9B
+    lens, t = [3, 290, 1000], 4
+    _, a, s1 = _attention_case(cfg, 41, lens, t, pool_seed=1)
+    s1.close()
+    _, b, s2 = _attention_case(cfg, 41, lens, t, pool_seed=2)
+    s2.close()
+    _, c, s3 = _attention_case(cfg, 41, lens, t, pool_seed=3, poison=True)
+    s3.close()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+    assert np.isfinite(c).all()
+
+
+def test_kv_append_lands_at_page_table_slot():
+    """One step at position p writes k, v (RoPE'd, rounded) to page table[p // 16], slot p % 16 and
+    nothing else; the values match the oracle's cached k, v to within one unit of the cache format."""
+    cfg = TINY
+    seed, ctx = 51, 37
+    G, D = cfg["n_kv_heads"], cfg["head_dim"]
+    s = Session(cfg, seed=seed, max_len=[ctx + 1], max_tokens=1, pool_seed=9)
+    try:
+        s.synthesize(seed + 1, [ctx])
+        before = {}
+        for l in range(cfg["n_layers"]):
+            for p in range(s.n_pages):
+                buf = np.empty(G * 2 * 16 * D, dtype=np.uint16)
+                bw.bw_kv_pool_read(s.pool, l, p, buf)
+                before[(l, p)] = buf
+        tok = 123
+        s.step(torch.tensor([tok], dtype=torch.int32, device="cuda"), torch.tensor([ctx], dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        om = oracle.Model(oracle_cfg(cfg), seed)
+        okv = oracle.KV(om, 1, 8)
+        okv.set_synth(0, seed + 1, 0, ctx)
+        oracle.forward(om, okv, 0, [tok], ctx, want_logits=False)
+        page = int(s.page_table_host[0, ctx // 16])
+        slot = ctx % 16
+        for l in range(cfg["n_layers"]):
+            for p in range(s.n_pages):
+                buf = np.empty(G * 2 * 16 * D, dtype=np.uint16)
+                bw.bw_kv_pool_read(s.pool, l, p, buf)
+                v = buf.reshape(G, 2, 16, D)
+                w = before[(l, p)].reshape(G, 2, 16, D)
+                if p != page:
+                    assert np.array_equal(v, w), (l, p)
+                    continue
+                mask = np.ones_like(v, dtype=bool)
+                mask[:, :, slot, :] = False
+                assert np.array_equal(v[mask], w[mask]), (l, p)
+                got = v[:, :, slot, :].view(np.float16).astype(np.float64)  # fp16 cache (tiny)
+                ref = np.array([[[okv.read(0, l, ctx, kv, g, d) for d in range(D)] for kv in range(2)] for g in range(G)])
+                ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+                assert np.all(np.abs(got - ref) <= ulp + 1e-12), (l, np.max(np.abs(got - ref)))
+    finally:
+        s.close()
+
+
+def test_device_errors_are_flagged_not_faults():
+    cfg = TINY
+    s = Session(cfg, seed=61, max_len=[40], max_tokens=2, pool_seed=3)
+    try:
+        bad = s.page_table.clone()
+        bad[0, 0] = s.n_pages + 5  # out of range page id
+        logits = torch.empty((1, cfg["vocab"]), dtype=torch.float32, device="cuda")
+        am = torch.empty(1, dtype=torch.int32, device="cuda")
+        bw.bw_decode_step(s.model, s.pool, torch.tensor([1], dtype=torch.int32, device="cuda"),
+                          torch.tensor([0], dtype=torch.int32, device="cuda"), bad, 1, 1, s.max_pages, logits, am)
+        assert bw.bw_check_device_error(s.model) & bw.BW_DERR_PAGE
+        bw.bw_decode_step(s.model, s.pool, torch.tensor([cfg["vocab"] + 3], dtype=torch.int32, device="cuda"),
+                          torch.tensor([0], dtype=torch.int32, device="cuda"), s.page_table, 1, 1, s.max_pages, logits, am)
+        assert bw.bw_check_device_error(s.model) & bw.BW_DERR_TOKEN
+        assert bw.bw_check_device_error(s.model) == 0
+        with pytest.raises(bw.BWError) as e:
+            bw.bw_decode_step(s.model, s.pool, torch.zeros(3, dtype=torch.int32, device="cuda"),
+                              torch.zeros(3, dtype=torch.int32, device="cuda"), s.page_table, 3, 1, s.max_pages, None, None)
+        assert e.value.code == bw.BW_ERANGE
+    finally:
+        s.close()
