@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of libbw on one MI355X.
+
+Workload (the measured configuration): 9B-shape dense decoder with int4 block weights (32 layers,
+d_model 4096, 32 query / 8 KV heads of 128, SwiGLU 12288, vocab 151936, bf16 KV in 16-token pages),
+batch 1, a 2048-token random prompt prefilled through the library, then `--steps` greedy decode
+steps timed. Each step's argmax is fed back as the next token on the device; nothing returns to
+the host inside the timed region.
+
+Output: one JSON line (metric, value = decode tok/s, ...) plus
+  - achieved step bandwidth: algorithmic bytes per step / step time, against 8 TB/s;
+  - "roofline" of the dominant kernel (RMSNorm + gate/up GEMV + SwiGLU): algorithmic bytes per
+    launch / its average launch time, timed with HIP events on the step's stream in a traced
+    pass right after the timed region;
+  - "cpu_baseline": the fp64 CPU oracle timed on this host on a bounded sample of the same
+    workload (decode steps at the same context, the context synthesised rather than prefilled).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s at batch 1 (9B-shape int4) + achieved HBM GB/s vs ~8 TB/s peak"
+HBM_PEAK_GBPS = 8000.0
+INT4_BYTES_PER_WEIGHT = 18.0 / 32.0  # 16 bytes of codes + one fp16 scale per 32 weights
+
+
+def algorithmic_bytes(cfg: dict, ctx_mean: float) -> dict:
+    """Bytes the step must move: active int4 weights, the KV read at the mean context, the new
+    K/V written, one embedding row (router matrices for MoE)."""
+    d, H, G, D, L = cfg["d_model"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["n_layers"]
+    w_attn = ((H + 2 * G) * D * d + d * H * D) * L
+    if cfg.get("n_experts", 0):
+        per = 3 * cfg["expert_ffn"] * d * cfg["top_k"] + 3 * cfg["shared_ffn"] * d * cfg["n_shared"]
+        w_ffn = per * L
+        router = cfg["n_experts"] * d * 2 * L
+    else:
+        w_ffn = 3 * cfg["ffn_dim"] * d * L
+        router = 0
+    w_lm = cfg["vocab"] * d
+    weights = (w_attn + w_ffn + w_lm) * INT4_BYTES_PER_WEIGHT
+    kv_read = ctx_mean * 2 * G * D * 2 * L
+    kv_write = 2 * G * D * 2 * L
+    embed = d * 2
+    return {"weights": weights, "kv_read": kv_read, "kv_write": kv_write, "router": router,
+            "embed": embed, "total": weights + kv_read + kv_write + router + embed}
+
+
+def cpu_baseline(cfg: dict, ctx: int, seconds: float) -> dict:
+    """The oracle as it stands: fp64 decode steps at context `ctx` (synthesised), timed."""
+    import numpy as np
+    import oracle
+
+    keys = ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab", "rms_eps",
+            "rope_base", "kv_dtype", "n_experts", "top_k", "expert_ffn", "n_shared", "shared_ffn")
+    om = oracle.Model({k: cfg[k] for k in keys if k in cfg}, cfg["seed"])
+    kv = oracle.KV(om, 1, 64)
+    kv.set_synth(0, cfg["seed"] + 7, 0, ctx)
+    tok = int(np.random.default_rng(cfg["seed"]).integers(0, cfg["vocab"]))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        r = oracle.forward(om, kv, 0, [tok], ctx + n)
+        tok = int(np.argmax(r["logits"][0]))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 60:
+            break
+    om.close()
+    return {"value": n / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} fp64 decode steps of the same model at context {ctx}..{ctx + n} "
+                      f"(context synthesised, not prefilled), {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--prompt", type=int, default=2048)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="launch the step's kernels directly instead of replaying a captured graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 4}))
+        return 0
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs the decode step on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import memory_bound_autoregressive_amd as bw
+    from memory_bound_autoregressive_amd import configs
+    from memory_bound_autoregressive_amd.session import Session
+
+    cfg = configs.DENSE_9B
+    P, W, K = args.prompt, args.warmup, args.steps
+    total = P + W + K + 1
+    torch.cuda.set_device(0)
+    t_load = time.perf_counter()
+    s = Session(cfg, seed=cfg["seed"], max_len=[total], max_tokens=1, pool_seed=cfg["seed"] + 1)
+    print(f"[bench] model + pool ready in {time.perf_counter() - t_load:.1f} s", file=sys.stderr, flush=True)
+    if args.no_graphs:
+        bw.bw_set_graphs(s.model, False)
+    dev = "cuda"
+    prompt = torch.from_numpy(np.random.default_rng(cfg["seed"]).integers(0, cfg["vocab"], P).astype(np.int32)).to(dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    sl = torch.zeros(1, dtype=torch.int32, device=dev)
+    am = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(feed_back: bool):
+        bw.bw_decode_step(s.model, s.pool, tok, sl, s.page_table, 1, 1, s.max_pages, None, tok if feed_back else am)
+        sl.add_(1)
+
+    # prefill: the prompt through the same decode step, one position at a time
+    t_pf = time.perf_counter()
+    for i in range(P):
+        tok.copy_(prompt[i:i + 1])
+        step(feed_back=(i == P - 1))
+    torch.cuda.synchronize()
+    print(f"[bench] prefill of {P} tokens in {time.perf_counter() - t_pf:.1f} s", file=sys.stderr, flush=True)
+    for _ in range(W):
+        step(feed_back=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        step(feed_back=True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    if bw.bw_check_device_error(s.model) != 0:
+        print("[bench] device error flag set", file=sys.stderr)
+        return 1
+    ms_per_step = ms / K
+    tok_s = 1000.0 / ms_per_step
+    ctx_mean = P + W + (K - 1) / 2.0
+    ab = algorithmic_bytes(cfg, ctx_mean)
+    step_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
+          f"{step_gbps:.0f} GB/s algorithmic ({step_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s)", file=sys.stderr, flush=True)
+
+    # traced pass: per-launch time of each kernel class, HIP events on the step's stream
+    kernel_us = {}
+    roofline = None
+    if not args.no_trace:
+        L = cfg["n_layers"]
+        classes = ["qkv", "attn", "o", "gate_up", "down", "lm_head"]
+        n_trace = 8
+        for cls in classes:
+            n_pairs = 1 if cls == "lm_head" else L
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_pairs)]
+            for e in evs:  # torch creates its events lazily, at the first record
+                e.record()
+            torch.cuda.synchronize()
+            arr = (ctypes.c_void_p * (2 * n_pairs))(*[ctypes.c_void_p(e.cuda_event) for e in evs])
+            bw.bw_set_trace(s.model, cls, arr, n_pairs)
+            tot, cnt = 0.0, 0
+            for _ in range(n_trace):
+                step(feed_back=True)
+                torch.cuda.synchronize()
+                for l in range(n_pairs):
+                    tot += evs[2 * l].elapsed_time(evs[2 * l + 1])
+                    cnt += 1
+            bw.bw_set_trace(s.model, cls, None, 0)
+            kernel_us[cls] = round(1000.0 * tot / cnt, 2)
+        d, F = cfg["d_model"], cfg["ffn_dim"]
+        gu_bytes = 2 * F * d * INT4_BYTES_PER_WEIGHT
+        gu_s = kernel_us["gate_up"] * 1e-6
+        achieved = gu_bytes / gu_s / 1e9
+        traffic = None
+        tr_path = os.path.join(ROOT, "profiles", "gate_up_dense9b_traffic.json")
+        if os.path.exists(tr_path):
+            with open(tr_path) as f:
+                tr = json.load(f)
+            from memory_bound_autoregressive_amd.build import source_digest
+            if tr.get("kernel_source_digest") == source_digest():
+                traffic = tr.get("hbm_bytes_per_launch")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                    "kernel": "RMSNorm + gate/up int4 GEMV + SwiGLU (24576 x 4096)",
+                    "bytes_per_launch": gu_bytes, "avg_launch_us": kernel_us["gate_up"]}
+        print(f"[bench] per-launch kernel time (us): {kernel_us}", file=sys.stderr, flush=True)
+    s.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, P + W, args.cpu_seconds)
+        print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "dense-9b int4 decode: batch 1, 2048-token random prompt prefilled, greedy steps",
+                   "batch": 1, "prompt": P, "context_range": [P + W, P + W + K], "weights": "int4 blocks of 32, fp16 scales",
+                   "kv": "bf16, 16-token pages, permuted pool", "seed": cfg["seed"]},
+        "achieved_hbm_gbps": round(step_gbps, 1), "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": ab, "kernel_us": kernel_us, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

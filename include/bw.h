@@ -130,13 +130,21 @@ int bw_kv_pool_read(const bw_kv_pool* pool, int32_t layer, int32_t page, void* h
  *   argmax_dev     int32 [batch * t]   greedy token per row (lowest index on ties), or NULL
  * The keys and values of all new tokens are written into the pool first; token i then attends
  * causally to positions 0 .. seq_lens[b] + i. The caller advances seq_lens afterwards.
- * Nothing is allocated and the stream is not synchronised.
+ * The step's kernels are captured once per distinct argument set (pointers and sizes) into a
+ * hipGraph on an internal stream and replayed on `stream`; the device buffers are read at
+ * replay time, so a caller that keeps its buffers and updates their contents on the device
+ * (e.g. feeding argmax_dev back as tokens_dev) replays one graph. The first call with a new
+ * argument set pays the capture; no device memory is allocated by the library and the stream
+ * is not synchronised.
  * Errors: BW_EINVAL (null handle or buffer, t < 1, batch < 1, pool of another model),
  * BW_ERANGE (batch * t > max_tokens). Page or token ids out of range are device errors. */
 int bw_decode_step(bw_model* model, bw_kv_pool* pool, const int32_t* tokens_dev,
                    const int32_t* seq_lens_dev, const int32_t* page_table_dev, int32_t batch,
                    int32_t t, int32_t max_pages, float* logits_dev, int32_t* argmax_dev,
                    void* stream);
+
+/* Turn step capture on (default) or off (every call then launches its kernels directly). */
+int bw_set_graphs(bw_model* model, int32_t enable);
 
 /* Text of the last error on this thread ("" if none). */
 const char* bw_last_error(void);
@@ -184,6 +192,27 @@ int bw_debug_read_experts(bw_model* model, int32_t n_rows, int32_t* host_dst, vo
 /* Residual stream after the last layer of the last bw_decode_step: float [batch * t][d_model],
  * copied to host. Synchronises `stream`. */
 int bw_debug_read_hidden(bw_model* model, int32_t n_rows, float* host_dst, void* stream);
+
+/* ---- measurement hook ------------------------------------------------------------------- */
+
+/* Kernel classes of one step, for bw_set_trace */
+#define BW_K_QKV 0        /* RMSNorm + QKV GEMV + RoPE + KV append      */
+#define BW_K_ATTN 1       /* split attention + merge                     */
+#define BW_K_O 2          /* O GEMV + residual                           */
+#define BW_K_GATE_UP 3    /* RMSNorm + gate/up GEMV + SwiGLU (dense)     */
+#define BW_K_DOWN 4       /* down GEMV + residual (dense)                */
+#define BW_K_LM_HEAD 5    /* final RMSNorm + lm_head GEMV (layer 0 slot) */
+#define BW_K_ROUTER 6     /* RMSNorm + router GEMV + top-k (MoE)         */
+#define BW_K_MOE_GATE_UP 7/* RMSNorm + selected experts' gate/up + SwiGLU */
+#define BW_K_MOE_DOWN 8   /* gated experts' down + shared + residual     */
+
+/* Record hipEvents around one kernel class in later bw_decode_step calls: before and after the
+ * launch(es) of class `kernel_class` in layer l, events[2l] and events[2l+1] are recorded on the
+ * step's stream (n_layers pairs; BW_K_LM_HEAD uses pair 0). `events` (an array of hipEvent_t
+ * owned by the caller) is borrowed until the hook is cleared with events = NULL. For measuring
+ * per-launch kernel time in a benchmark; the records add two stream markers per traced launch.
+ * Errors: BW_EINVAL. */
+int bw_set_trace(bw_model* model, int32_t kernel_class, void* const* events, int32_t n_layers);
 
 #ifdef __cplusplus
 }

@@ -25,8 +25,10 @@ EXPORTS = (
     "bw_model_load_synthetic", "bw_model_free", "bw_kv_pool_create", "bw_kv_pool_free",
     "bw_kv_pool_fill", "bw_kv_pool_synthesize", "bw_kv_pool_read", "bw_decode_step",
     "bw_last_error", "bw_check_device_error", "bw_debug_dequant", "bw_debug_matvec",
-    "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden",
+    "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden", "bw_set_trace", "bw_set_graphs",
 )
+KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
+                "moe_gate_up": 7, "moe_down": 8}
 
 
 class BWError(RuntimeError):
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.bw_debug_attention.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
         L.bw_debug_read_experts.argtypes = [vp, i32, vp, vp]
         L.bw_debug_read_hidden.argtypes = [vp, i32, vp, vp]
+        L.bw_set_trace.argtypes = [vp, i32, vp, i32]
+        L.bw_set_graphs.argtypes = [vp, i32]
         _lib = L
     return _lib
 
@@ -190,3 +194,12 @@ def bw_debug_read_experts(model: int, n_rows: int, out, stream=None) -> None:
 
 def bw_debug_read_hidden(model: int, n_rows: int, out, stream=None) -> None:
     _check(lib().bw_debug_read_hidden(model, n_rows, _ptr(out), _stream(stream)), "bw_debug_read_hidden")
+
+
+def bw_set_trace(model: int, kernel_class: str, events, n_layers: int) -> None:
+    """events: a ctypes array of 2 * n_layers hipEvent_t handles (or None to clear)."""
+    _check(lib().bw_set_trace(model, KERNEL_CLASS[kernel_class], events, n_layers), "bw_set_trace")
+
+
+def bw_set_graphs(model: int, enable: bool) -> None:
+    _check(lib().bw_set_graphs(model, int(bool(enable))), "bw_set_graphs")

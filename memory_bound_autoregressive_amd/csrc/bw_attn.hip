@@ -11,10 +11,11 @@
 //
 // Split: workgroup (split s, KV head g, sequence b) covers logical pages [s*PPS, (s+1)*PPS) and
 // all t * (Hq/Hkv) query rows that use KV head g, so each K/V page is read once per step for all
-// heads of its group. Each of the 4 waves takes every 4th page and keeps a running
-// (max, sum, acc) per query row; the waves merge in LDS and write one partial per split. The merge
-// kernel combines the splits in split order, so the result depends only on logical page order and
-// contents: permuting the physical pool changes nothing, bit for bit.
+// heads of its group. Each of the 4 waves takes every 4th page (its K and V loaded together) and
+// keeps a running (max, sum, acc) per query row; the waves merge in LDS and write one partial per
+// split. A merge kernel combines the splits of each (row, KV group) in split order, so the result
+// depends only on logical page order and contents: permuting the physical pool changes nothing,
+// bit for bit.
 //
 // Lane layout per page (D = 128): scores use 8 tokens x 8 lanes per pass (each lane a 16-dim
 // slice, 2 x 16-byte loads, 2 passes); values use 4 token groups x 16 lanes (each lane an 8-dim
@@ -36,21 +37,22 @@ __device__ __forceinline__ void unpack8(u32x4 v, float* out) {
 
 template <int KVDT, int D, int QR>
 __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
-  constexpr int DL = D / 8;            // score dims per lane (8 lanes per token)
-  constexpr int NV = D / 8;            // lanes per token row for values (8 dims each)
-  constexpr int TG = kWave / NV;       // token groups for values
-  constexpr int TPL = kPageTokens / TG;// tokens per lane for values
+  constexpr int DL = D / 8;             // score dims per lane (8 lanes per token)
+  constexpr int NV = D / 8;             // lanes per token row for values (8 dims each)
+  constexpr int TG = kWave / NV;        // token groups for values
+  constexpr int TPL = kPageTokens / TG; // tokens per lane for values
   constexpr bool QREG = (QR * DL <= 96);
-  constexpr int NCH = DL / 8;          // 16-byte chunks per lane per token for scores
+  constexpr int NCH = DL / 8;           // 16-byte chunks per lane per token for scores
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int rep = p.H / p.G;
   const int base_pos = p.seq_lens[b];
   const int kv_len = base_pos + p.t;
   int n_pg = (kv_len + kPageTokens - 1) / kPageTokens;
-  if (n_pg > p.max_pages || n_pg > p.max_splits * p.pages_per_split) {
+  const int pg_cap = min(p.max_pages, p.max_splits * p.pages_per_split);
+  if (n_pg > pg_cap) {
     if (threadIdx.x == 0 && s == 0) atomicOr(p.err, 1);
-    n_pg = min(p.max_pages, p.max_splits * p.pages_per_split);
+    n_pg = pg_cap;
   }
   const int pg0 = s * p.pages_per_split;
   if (pg0 >= n_pg) return;
@@ -61,19 +63,21 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
   __shared__ float m_lds[4][QR], l_lds[4][QR];
   __shared__ float acc_lds[4][QR * D];
 
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sc_tok = lane >> 3, sc_c = lane & 7;     // scores: token within pass, dim slice
+  const int v_c = lane % NV, v_tg = lane / NV;       // values: dim chunk, token group
+
+  // this wave's first page id goes out before anything else
+  int pg = pg0 + wave;
+  int page = pg < pg1 ? p.page_table[(int64_t)b * p.max_pages + pg] : -1;
+
   // query rows: qr = ti * rep + r  ->  token ti, head g * rep + r
   for (int e = threadIdx.x; e < QR * D; e += kBlock) {
     const int qr = e / D, d = e - qr * D;
     const int ti = qr / rep, r = qr - ti * rep;
-    float v = 0.f;
-    if (ti < p.t) v = p.q[((int64_t)(b * p.t + ti) * p.H + g * rep + r) * D + d] * p.scale;
-    q_lds[e] = v;
+    q_lds[e] = p.q[((int64_t)(b * p.t + ti) * p.H + g * rep + r) * D + d] * p.scale;
   }
   __syncthreads();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sc_tok = lane >> 3, sc_c = lane & 7;     // scores: token within pass, dim slice
-  const int v_c = lane % NV, v_tg = lane / NV;       // values: dim chunk, token group
 
   float qreg[QREG ? QR : 1][QREG ? DL : 1];
   if constexpr (QREG) {
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
   }
   int qpos[QR];
 #pragma unroll
-  for (int qr = 0; qr < QR; ++qr) qpos[qr] = (qr / rep < p.t) ? base_pos + qr / rep : -1;
+  for (int qr = 0; qr < QR; ++qr) qpos[qr] = base_pos + qr / rep;
 
   float mrun[QR], lrun[QR], acc[QR][8];
 #pragma unroll
@@ -95,91 +99,100 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
     for (int e = 0; e < 8; ++e) acc[qr][e] = 0.f;
   }
 
-  for (int pg = pg0 + wave; pg < pg1; pg += 4) {
-    const int page = p.page_table[(int64_t)b * p.max_pages + pg];
-    if (page < 0 || page >= p.n_pages) {
-      if (lane == 0) atomicOr(p.err, 1);
-      continue;
+  for (; pg < pg1; pg += 4) {
+    const bool valid = page >= 0 && page < p.n_pages;
+    if (!valid && lane == 0) atomicOr(p.err, 1);
+    // K (for the scores) and V (for the values) of this page, loaded together
+    u32x4 kraw[2][NCH], vraw[TPL];
+    if (valid) {
+      const uint16_t* kbase = p.pool + (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D;
+      const uint16_t* vbase = kbase + kPageTokens * D;
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+          kraw[pass][ch] = *(const u32x4*)(kbase + (pass * 8 + sc_tok) * D + sc_c * DL + ch * 8);
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) vraw[u] = *(const u32x4*)(vbase + (v_tg + u * TG) * D + v_c * 8);
     }
-    const uint16_t* kbase = p.pool + (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D;
-    const uint16_t* vbase = kbase + kPageTokens * D;
-    // ---- scores for the 16 tokens (2 passes of 8)
-    float sc[2][QR];
+    // the next page's id
+    const int pgn = pg + 4;
+    const int page_n = pgn < pg1 ? p.page_table[(int64_t)b * p.max_pages + pgn] : -1;
+    if (valid) {
+      // ---- scores for the 16 tokens (2 passes of 8)
+      float sc[2][QR];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int tok = pass * 8 + sc_tok;
-      const int j = pg * kPageTokens + tok;
-      float kf[DL];
+      for (int pass = 0; pass < 2; ++pass) {
+        const int j = pg * kPageTokens + pass * 8 + sc_tok;
+        float kf[DL];
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        u32x4 raw = *(const u32x4*)(kbase + tok * D + sc_c * DL + ch * 8);
-        unpack8<KVDT>(raw, kf + ch * 8);
-      }
+        for (int ch = 0; ch < NCH; ++ch) unpack8<KVDT>(kraw[pass][ch], kf + ch * 8);
 #pragma unroll
-      for (int qr = 0; qr < QR; ++qr) {
-        float dot = 0.f;
-        if constexpr (QREG) {
+        for (int qr = 0; qr < QR; ++qr) {
+          float dot = 0.f;
+          if constexpr (QREG) {
 #pragma unroll
-          for (int e = 0; e < DL; ++e) dot = fmaf(qreg[qr][e], kf[e], dot);
-        } else {
+            for (int e = 0; e < DL; ++e) dot = fmaf(qreg[qr][e], kf[e], dot);
+          } else {
 #pragma unroll
-          for (int e = 0; e < DL; ++e) dot = fmaf(q_lds[qr * D + sc_c * DL + e], kf[e], dot);
+            for (int e = 0; e < DL; ++e) dot = fmaf(q_lds[qr * D + sc_c * DL + e], kf[e], dot);
+          }
+          dot += __shfl_xor(dot, 1);
+          dot += __shfl_xor(dot, 2);
+          dot += __shfl_xor(dot, 4);
+          sc[pass][qr] = (j < kv_len && j <= qpos[qr]) ? dot : -INFINITY;
         }
-        dot += __shfl_xor(dot, 1);
-        dot += __shfl_xor(dot, 2);
-        dot += __shfl_xor(dot, 4);
-        sc[pass][qr] = (j < kv_len && j <= qpos[qr]) ? dot : -INFINITY;
       }
-    }
-    // ---- online softmax update per query row
-#pragma unroll
-    for (int qr = 0; qr < QR; ++qr) {
-      float pm = fmaxf(sc[0][qr], sc[1][qr]);
-      pm = fmaxf(pm, __shfl_xor(pm, 8));
-      pm = fmaxf(pm, __shfl_xor(pm, 16));
-      pm = fmaxf(pm, __shfl_xor(pm, 32));
-      const float mnew = fmaxf(mrun[qr], pm);
-      float p0 = 0.f, p1 = 0.f, alpha = 1.f;
-      if (mnew != -INFINITY) {
-        p0 = __expf(sc[0][qr] - mnew);
-        p1 = __expf(sc[1][qr] - mnew);
-        alpha = __expf(mrun[qr] - mnew);
-      }
-      float ps = p0 + p1;
-      ps += __shfl_xor(ps, 8);
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      lrun[qr] = lrun[qr] * alpha + ps;
-      mrun[qr] = mnew;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[qr][e] *= alpha;
-      if (sc_c == 0) {
-        p_lds[wave][qr][sc_tok] = p0;
-        p_lds[wave][qr][8 + sc_tok] = p1;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- values: lane covers 8 dims of TPL tokens
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      const int tok = v_tg + u * TG;
-      const int j = pg * kPageTokens + tok;
-      u32x4 raw = *(const u32x4*)(vbase + tok * D + v_c * 8);
-      float vf[8];
-      unpack8<KVDT>(raw, vf);
-      const bool live = j < kv_len;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vf[e] = live ? vf[e] : 0.f;
+      // ---- online softmax update per query row
 #pragma unroll
       for (int qr = 0; qr < QR; ++qr) {
-        const float pw = p_lds[wave][qr][tok];
+        float pm = fmaxf(sc[0][qr], sc[1][qr]);
+        pm = fmaxf(pm, __shfl_xor(pm, 8));
+        pm = fmaxf(pm, __shfl_xor(pm, 16));
+        pm = fmaxf(pm, __shfl_xor(pm, 32));
+        const float mnew = fmaxf(mrun[qr], pm);
+        float p0 = 0.f, p1 = 0.f, alpha = 1.f;
+        if (mnew != -INFINITY) {
+          p0 = __expf(sc[0][qr] - mnew);
+          p1 = __expf(sc[1][qr] - mnew);
+          alpha = __expf(mrun[qr] - mnew);
+        }
+        float ps = p0 + p1;
+        ps += __shfl_xor(ps, 8);
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        lrun[qr] = lrun[qr] * alpha + ps;
+        mrun[qr] = mnew;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[qr][e] = fmaf(pw, vf[e], acc[qr][e]);
+        for (int e = 0; e < 8; ++e) acc[qr][e] *= alpha;
+        if (sc_c == 0) {
+          p_lds[wave][qr][sc_tok] = p0;
+          p_lds[wave][qr][8 + sc_tok] = p1;
+        }
       }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // ---- values: lane covers 8 dims of TPL tokens
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        const int tok = v_tg + u * TG;
+        const int j = pg * kPageTokens + tok;
+        float vf[8];
+        unpack8<KVDT>(vraw[u], vf);
+        const bool live = j < kv_len;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = live ? vf[e] : 0.f;
+#pragma unroll
+        for (int qr = 0; qr < QR; ++qr) {
+          const float pw = p_lds[wave][qr][tok];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[qr][e] = fmaf(pw, vf[e], acc[qr][e]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
+    page = page_n;
   }
   // ---- reduce the value partials over the token groups of the wave
 #pragma unroll
@@ -202,12 +215,10 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
     }
   }
   __syncthreads();
-  // ---- merge the 4 waves and write this split's partial
-  const int n_out = p.t * rep * (D + 2);
+  // ---- merge the 4 waves and write this split's partial (acc, m, l)
   for (int e = threadIdx.x; e < QR * D; e += kBlock) {
     const int qr = e / D, d = e - qr * D;
-    if (qr / rep >= p.t) continue;
-    float M = fmaxf(fmaxf(m_lds[0][qr], m_lds[1][qr]), fmaxf(m_lds[2][qr], m_lds[3][qr]));
+    const float M = fmaxf(fmaxf(m_lds[0][qr], m_lds[1][qr]), fmaxf(m_lds[2][qr], m_lds[3][qr]));
     float a = 0.f, l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
@@ -225,31 +236,54 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
       dst[D + 1] = l;
     }
   }
-  (void)n_out;
 }
 
-// o[row][h][:] = sum_s acc_s exp(m_s - M) / sum_s l_s exp(m_s - M), splits in order
+// Merge of the split partials of one (row, query head): o = sum_s acc_s exp(m_s - M) / sum_s l_s
+// exp(m_s - M), M = max_s m_s, in split order. The (m, l) of every split are loaded in parallel
+// (one split per thread) and the per-split factors staged in LDS, so only the value sums loop.
 template <int D>
-__global__ __launch_bounds__(D) void k_attn_merge(AttnParams p) {
+__global__ __launch_bounds__(kBlock) void k_attn_merge(AttnParams p) {
+  __shared__ float fac[1024];
+  __shared__ float red[16];
   const int h = blockIdx.x, row = blockIdx.y;
   const int b = row / p.t;
   const int kv_len = p.seq_lens[b] + p.t;
   const int n_pg = min((kv_len + kPageTokens - 1) / kPageTokens, min(p.max_pages, p.max_splits * p.pages_per_split));
-  const int n_split = (n_pg + p.pages_per_split - 1) / p.pages_per_split;
-  const float* part = p.part + ((int64_t)row * p.H + h) * p.max_splits * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
-  float a = 0.f, l = 0.f;
-  const int d = threadIdx.x;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float* ps = part + s * (D + 2);
-      const float f = __expf(ps[D] - M);
-      a = fmaf(ps[d], f, a);
-      l = fmaf(ps[D + 1], f, l);
+  const int n_split = min((n_pg + p.pages_per_split - 1) / p.pages_per_split, 1024);
+  {
+    const float* part = p.part + ((int64_t)row * p.H + h) * p.max_splits * (D + 2);
+    // 1. M = max over splits (parallel loads)
+    float mloc = -INFINITY;
+    for (int sp = threadIdx.x; sp < n_split; sp += kBlock) mloc = fmaxf(mloc, part[sp * (D + 2) + D]);
+    mloc = wave_max(mloc);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mloc;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    // 2. factors and the denominator
+    float lloc = 0.f;
+    for (int sp = threadIdx.x; sp < n_split; sp += kBlock) {
+      const float f = M == -INFINITY ? 0.f : __expf(part[sp * (D + 2) + D] - M);
+      fac[sp] = f;
+      lloc = fmaf(part[sp * (D + 2) + D + 1], f, lloc);
+    }
+    __syncthreads();
+    // denominator: fixed per-thread split sets and a fixed reduction tree (deterministic)
+    const float L = block_sum(lloc, red + 4);
+    // 3. values: thread (d, quarter) sums a quarter of the splits, quarters combined in order
+    const int d = threadIdx.x % D, qq = threadIdx.x / D;  // kBlock / D quarters
+    constexpr int NQ = kBlock / D;
+    float a = 0.f;
+    for (int sp = qq; sp < n_split; sp += NQ) a = fmaf(part[sp * (D + 2) + d], fac[sp], a);
+    __shared__ float asum[kBlock];
+    asum[threadIdx.x] = a;
+    __syncthreads();
+    if (qq == 0) {
+      float t = 0.f;
+      for (int k = 0; k < NQ; ++k) t += asum[k * D + d];
+      p.out[((int64_t)row * p.H + h) * D + d] = L > 0.f ? t / L : 0.f;
     }
   }
-  p.out[((int64_t)row * p.H + h) * D + d] = l > 0.f ? a / l : 0.f;
 }
 
 template <int KVDT, int D, int QR>
@@ -278,8 +312,8 @@ int launch_attention(const AttnParams& p, int kv_dtype, int batch, hipStream_t s
   else if (p.D == 64) rc = kv_dtype == 1 ? dispatch_qr<1, 64>(p, batch, s) : dispatch_qr<2, 64>(p, batch, s);
   else return -2;
   if (rc) return rc;
-  if (p.D == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(p.H, batch * p.t), dim3(128), 0, s, p);
-  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(p.H, batch * p.t), dim3(64), 0, s, p);
+  if (p.D == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(p.H, batch * p.t), dim3(kBlock), 0, s, p);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(p.H, batch * p.t), dim3(kBlock), 0, s, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -52,12 +52,14 @@ __device__ __forceinline__ u32x4 load_stream16(const void* p) {
 }
 
 // ---- LDS layout of the input vector ---------------------------------------------------------
-// Element e (0..31) of 32-element block b is stored at float index b*32 + ((e + 4*(b&7)) & 31):
-// the 16-byte chunk c of block b lands in slot (c + b) & 7 of the block's 128-byte row, so eight
-// lanes reading chunk c of eight consecutive blocks touch eight different slots (all banks).
-__device__ __forceinline__ int xs_index(int b, int e) { return b * 32 + ((e + 4 * (b & 7)) & 31); }
-__device__ __forceinline__ const float4* xs_chunk(const float* xs, int b, int c) {
-  return reinterpret_cast<const float4*>(xs + b * 32 + (((c + b) & 7) << 2));
+// Each 32-element block of the input occupies 128 bytes = eight 16-byte chunks. Chunk c of block b
+// is stored in slot (c + b) & 7 of the block's row, so eight lanes reading chunk c of eight
+// consecutive blocks touch eight different slots (all banks).
+__device__ __forceinline__ float* xs_chunk(float* xs, int b, int c) {
+  return xs + b * 32 + (((c + b) & 7) << 2);
+}
+__device__ __forceinline__ const float* xs_chunk(const float* xs, int b, int c) {
+  return xs + b * 32 + (((c + b) & 7) << 2);
 }
 
 // ---- reductions -------------------------------------------------------------------------------

@@ -16,6 +16,8 @@
 // Prologues: plain vector, RMSNorm of the residual row, or the gated concatenation of the
 // selected experts' SwiGLU outputs (MoE down projection). Epilogues: store, residual add, RoPE
 // + KV append, SwiGLU, logits with an argmax partial, MoE SwiGLU.
+#include <algorithm>
+
 #include "bw_common.h"
 #include "bw_internal.h"
 
@@ -24,43 +26,6 @@ namespace bw {
 // ---------------------------------------------------------------------------------------------
 // input staging
 // ---------------------------------------------------------------------------------------------
-
-template <int IN>
-__device__ __forceinline__ void stage_input(const GemvParams& p, int K, int m, float* xs, float* bs,
-                                            float* red) {
-  const float* xr = p.x + (int64_t)m * p.x_stride;
-  if constexpr (IN == IN_RMSNORM) {
-    float ss = 0.f;
-    for (int k = threadIdx.x; k < K; k += kBlock) {
-      float v = xr[k];
-      ss = fmaf(v, v, ss);
-    }
-    ss = block_sum(ss, red);
-    const float r = 1.0f / sqrtf(ss / (float)K + p.eps);
-    for (int k = threadIdx.x; k < K; k += kBlock)
-      xs[xs_index(k >> 5, k & 31)] = xr[k] * r * f16_to_f32(p.gamma[k]);
-  } else if constexpr (IN == IN_MOE_DOWN) {
-    const int routed = p.top_k * p.Fe;
-    for (int k = threadIdx.x; k < K; k += kBlock) {
-      float g = k < routed ? p.gates[m * p.top_k + k / p.Fe] : 1.0f;
-      xs[xs_index(k >> 5, k & 31)] = g * xr[k];
-    }
-  } else {
-    for (int k = threadIdx.x; k < K; k += kBlock) xs[xs_index(k >> 5, k & 31)] = xr[k];
-  }
-  __syncthreads();
-  const int nblk = K >> 5;
-  for (int b = threadIdx.x; b < nblk; b += kBlock) {
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float4 v = *xs_chunk(xs, b, c);
-      s += (v.x + v.y) + (v.z + v.w);
-    }
-    bs[b] = s;
-  }
-  __syncthreads();
-}
 
 // ---------------------------------------------------------------------------------------------
 // row addressing
@@ -126,167 +91,311 @@ __device__ __forceinline__ void moe_dn_block(const GemvParams& p, int m, int n, 
 }
 
 // ---------------------------------------------------------------------------------------------
-// dot product of one 32-element block: sum_i q_i x_i - 8 sum_i x_i
+// dot product of one 32-element block: sum_i (q_i - 8) x_i
 // ---------------------------------------------------------------------------------------------
+// Two codes (w >> s) & 0x000F000F read as two fp16 subnormals q * 2^-24 (exact), so one shift and
+// one and unpack two codes; each feeds an fp32 FMA directly from its half of the register
+// (v_fma_mix_f32 converts the fp16 operand exactly), so every product and sum is fp32. For code
+// dword k of a block (bytes 4k..4k+3: low nibbles are elements 4k..4k+3, high nibbles elements
+// 16+4k..16+4k+3) the x values come from chunks k and 4+k of the block. With D = sum q 2^-24 x
+// and S = sum x over the block: sum (q - 8) x = 2^24 D - 8 S.
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float block_dot(u32x4 q, const float4* xv, float minus8sx) {
-  float dot = minus8sx;
+__device__ __forceinline__ float mix2(uint32_t pair, float x_even, float x_odd, float acc) {
+  const h2_t h = __builtin_bit_cast(h2_t, pair);
+  acc = fmaf((float)h[0], x_even, acc);
+  return fmaf((float)h[1], x_odd, acc);
+}
+
+__device__ __forceinline__ float block_dot(u32x4 q, const float4* xv, float bsum) {
+  float d = 0.f;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t w = q[d];
-    const uint32_t lo = w & 0x0F0F0F0Fu;          // elements 4d .. 4d+3
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 16+4d .. 16+4d+3
-    const float4 a = xv[d];
-    const float4 b = xv[4 + d];
-    dot = fmaf((float)(lo & 0xFFu), a.x, dot);
-    dot = fmaf((float)((lo >> 8) & 0xFFu), a.y, dot);
-    dot = fmaf((float)((lo >> 16) & 0xFFu), a.z, dot);
-    dot = fmaf((float)(lo >> 24), a.w, dot);
-    dot = fmaf((float)(hi & 0xFFu), b.x, dot);
-    dot = fmaf((float)((hi >> 8) & 0xFFu), b.y, dot);
-    dot = fmaf((float)((hi >> 16) & 0xFFu), b.z, dot);
-    dot = fmaf((float)(hi >> 24), b.w, dot);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = q[k];
+    const float4 lo = xv[k], hi = xv[4 + k];
+    d = mix2(w & 0x000F000Fu, lo.x, lo.z, d);           // elements 4k, 4k+2
+    d = mix2((w >> 8) & 0x000F000Fu, lo.y, lo.w, d);    // elements 4k+1, 4k+3
+    d = mix2((w >> 4) & 0x000F000Fu, hi.x, hi.z, d);    // elements 16+4k, 16+4k+2
+    d = mix2((w >> 12) & 0x000F000Fu, hi.y, hi.w, d);   // elements 16+4k+1, 16+4k+3
   }
-  return dot;
+  return fmaf(16777216.0f, d, -8.0f * bsum);
 }
 
 // ---------------------------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------------------------
 
+// The codes and scales of one group of rows (RW row steps of RPW rows) for one lane.
+template <int LPR, int NB, int RW>
+struct Group {
+  u32x4 q[RW][NB];
+  uint16_t sc[RW][NB];
+  int row[RW];
+  int moe_off[RW], moe_lr[RW];
+  float2 cs[RW];  // RoPE (cos, sin) of each row's pair (QKV epilogue)
+};
+
+// RoPE factors of a group's q/k rows at position pos (issued right after the group's weights)
+template <int LPR, int NB, int RW>
+__device__ __forceinline__ void load_rope(const GemvParams& p, int pos, Group<LPR, NB, RW>& g) {
+  const int D = p.D, HD = p.H * p.D, GD = p.G * p.D;
+  const bool pos_ok = pos >= 0 && pos < p.max_pos;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int dr = g.row[r];
+    g.cs[r] = make_float2(1.f, 0.f);
+    if (pos_ok && dr < HD + GD) {
+      const int local = dr < HD ? dr : dr - HD;
+      const int i = (local % D) >> 1;
+      g.cs[r] = p.rope[(int64_t)pos * (D >> 1) + i];
+    }
+  }
+}
+
+template <int LPR, int NB, int RW, int IN, int EPI>
+__device__ __forceinline__ void load_group(const GemvParams& p, int m, int K, int gi, int j, int rsub,
+                                           Group<LPR, NB, RW>& g) {
+  constexpr int RPW = kWave / LPR;
+  constexpr int GROUP = RPW * RW;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    g.row[r] = gi * GROUP + r * RPW + rsub;
+    const bool ok = g.row[r] < p.n_rows;
+    if constexpr (IN == IN_MOE_DOWN) {
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        const uint8_t* cp;
+        const uint16_t* sp;
+        moe_dn_block(p, m, ok ? g.row[r] : 0, j + LPR * c, &cp, &sp);
+        g.q[r][c] = ok ? load_stream16(cp) : u32x4{0, 0, 0, 0};
+        g.sc[r][c] = ok ? *sp : (uint16_t)0;
+      }
+    } else {
+      RowPtr rp;
+      if constexpr (EPI == EPI_MOE_SWIGLU)
+        rp = moe_gu_row_ptr<LPR, NB>(p, m, ok ? g.row[r] : 0, j, K, &g.moe_off[r], &g.moe_lr[r]);
+      else
+        rp = row_ptr<LPR, NB>(p.w, ok ? g.row[r] : 0, j);
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        g.q[r][c] = ok ? load_stream16(rp.codes + (j + LPR * c) * 16) : u32x4{0, 0, 0, 0};
+        g.sc[r][c] = ok ? rp.scales[c] : (uint16_t)0;
+      }
+    }
+  }
+}
+
+// Work split: wave w of workgroup b takes groups b*4 + w, then every 4*gridDim.x-th group. The
+// launcher sizes the grid so that every workgroup is resident at once.
+// Latency plan: the input-vector loads are issued first, the first group's weight loads second
+// (so the input can be staged while the weights are in flight), the next group's weights are
+// loaded before the current group is computed, and the epilogue's own inputs (position, page id,
+// RoPE factors) are fetched before any of that completes.
 template <int LPR, int NB, int RW, int IN, int EPI>
 __global__ __launch_bounds__(kBlock) void k_gemv(GemvParams p) {
   extern __shared__ float lds[];
   constexpr int RPW = kWave / LPR;
   constexpr int GROUP = RPW * RW;
-  const int K = (IN == IN_MOE_DOWN) ? (p.top_k * p.Fe + p.n_shared * p.Fs) : p.w.K;
+  constexpr int KC = LPR * NB * 32;                   // K of this instantiation
+  constexpr int XV = (KC / 4 + kBlock - 1) / kBlock;  // float4 input loads per thread
+  const int K = KC;
   const int nblk = K >> 5;
   float* xs = lds;
   float* bs = lds + K;
   float* red = bs + nblk;  // 16 floats
+  float* csum = red + 16;  // nblk * 8 chunk sums
   const int m = blockIdx.y;
-  stage_input<IN>(p, K, m, xs, bs, red);
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane % LPR, rsub = lane / LPR;
   const int n_groups = (p.n_rows + GROUP - 1) / GROUP;
 
+  // ---- 1. input loads (global -> registers)
+  float4 xv[XV];
+  {
+    const bool emb = (IN == IN_RMSNORM) && p.embed != nullptr;
+    int tok = 0;
+    if (emb) {
+      tok = p.tokens[m];
+      if (tok < 0 || tok >= p.vocab) {
+        if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(p.err, 2);
+        tok = 0;
+      }
+    }
+    const float* xr = p.x + (int64_t)m * p.x_stride;
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+      const int k4 = threadIdx.x + i * kBlock;
+      xv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k4 < KC / 4) {
+        if (emb) {
+          const uint2 h = *(const uint2*)(p.embed + (int64_t)tok * K + 4 * k4);
+          xv[i] = make_float4(f16_to_f32((uint16_t)(h.x & 0xFFFFu)), f16_to_f32((uint16_t)(h.x >> 16)),
+                              f16_to_f32((uint16_t)(h.y & 0xFFFFu)), f16_to_f32((uint16_t)(h.y >> 16)));
+        } else {
+          xv[i] = *(const float4*)(xr + 4 * k4);
+        }
+      }
+    }
+  }
+
+  // ---- 2. first group's weights
+  int gi = blockIdx.x * 4 + wave;
+  Group<LPR, NB, RW> cur;
+  if (gi < n_groups) load_group<LPR, NB, RW, IN, EPI>(p, m, K, gi, j, rsub, cur);
+
+  // ---- 3. epilogue inputs of the QKV step (uniform per row m), after the weights are in flight
+  int pos = 0, page = -1;
+  if constexpr (EPI == EPI_QKV) {
+    const int b = m / p.t, ti = m - b * p.t;
+    pos = p.seq_lens[b] + ti;
+    if (pos >= 0 && pos < p.max_pos && pos / kPageTokens < p.max_pages)
+      page = p.page_table[(int64_t)b * p.max_pages + pos / kPageTokens];
+    if (gi < n_groups) load_rope<LPR, NB, RW>(p, pos, cur);
+  }
+
+  // ---- 4. stage the input vector (RMSNorm / gate scaling) into LDS, block sums
+  {
+    float scale = 1.0f;
+    if constexpr (IN == IN_RMSNORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < XV; ++i) ss += (xv[i].x * xv[i].x + xv[i].y * xv[i].y) + (xv[i].z * xv[i].z + xv[i].w * xv[i].w);
+      ss = block_sum(ss, red);
+      scale = 1.0f / sqrtf(ss / (float)K + p.eps);
+    }
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+      const int k4 = threadIdx.x + i * kBlock;
+      if (k4 >= KC / 4) continue;
+      const int k = 4 * k4;
+      float4 v = xv[i];
+      if constexpr (IN == IN_RMSNORM) {
+        if (p.embed != nullptr && blockIdx.x == 0) *(float4*)(p.x_out + (int64_t)m * p.x_stride + k) = v;
+        const uint2 gh = *(const uint2*)(p.gamma + k);
+        v.x *= scale * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
+        v.y *= scale * f16_to_f32((uint16_t)(gh.x >> 16));
+        v.z *= scale * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
+        v.w *= scale * f16_to_f32((uint16_t)(gh.y >> 16));
+      } else if constexpr (IN == IN_MOE_DOWN) {
+        const float g = k < p.top_k * p.Fe ? p.gates[m * p.top_k + k / p.Fe] : 1.0f;
+        v.x *= g; v.y *= g; v.z *= g; v.w *= g;
+      }
+      // 4 consecutive elements of a block form one 16-byte chunk of the swizzled layout
+      *(float4*)xs_chunk(xs, k >> 5, (k & 31) >> 2) = v;
+      csum[(k >> 5) * 8 + ((k & 31) >> 2)] = (v.x + v.y) + (v.z + v.w);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < nblk; b += kBlock) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sacc += csum[b * 8 + c];
+      bs[b] = sacc;
+    }
+    __syncthreads();
+  }
+
   float best_v = -INFINITY;
   int best_i = 0x7fffffff;
 
-  for (int gi = blockIdx.x * 4 + wave; gi < n_groups; gi += gridDim.x * 4) {
-    u32x4 q[RW][NB];
-    uint16_t sc[RW][NB];
-    int row[RW];
-    int moe_off[RW], moe_lr[RW];
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      row[r] = gi * GROUP + r * RPW + rsub;
-      const bool ok = row[r] < p.n_rows;
-      if constexpr (IN == IN_MOE_DOWN) {
-#pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          const uint8_t* cp;
-          const uint16_t* sp;
-          moe_dn_block(p, m, ok ? row[r] : 0, j + LPR * c, &cp, &sp);
-          q[r][c] = ok ? load_stream16(cp) : u32x4{0, 0, 0, 0};
-          sc[r][c] = ok ? *sp : (uint16_t)0;
-        }
-      } else {
-        RowPtr rp;
-        if constexpr (EPI == EPI_MOE_SWIGLU)
-          rp = moe_gu_row_ptr<LPR, NB>(p, m, ok ? row[r] : 0, j, K, &moe_off[r], &moe_lr[r]);
-        else
-          rp = row_ptr<LPR, NB>(p.w, ok ? row[r] : 0, j);
-#pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          q[r][c] = ok ? load_stream16(rp.codes + (j + LPR * c) * 16) : u32x4{0, 0, 0, 0};
-          sc[r][c] = ok ? rp.scales[c] : (uint16_t)0;
-        }
+  // ---- 5. groups, double-buffered (A/B alternate so that no registers are copied)
+  auto compute = [&](const Group<LPR, NB, RW>& g) {
+      float acc[RW];
+  #pragma unroll
+      for (int r = 0; r < RW; ++r) acc[r] = 0.f;
+  #pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        // keep one x block live at a time (the code loads above are already in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        const int b = j + LPR * c;
+        float4 xb[8];
+  #pragma unroll
+        for (int k = 0; k < 8; ++k) xb[k] = *(const float4*)xs_chunk(xs, b, k);
+        const float sb = bs[b];
+  #pragma unroll
+        for (int r = 0; r < RW; ++r) acc[r] = fmaf(f16_to_f32(g.sc[r][c]), block_dot(g.q[r][c], xb, sb), acc[r]);
       }
-    }
-    float acc[RW];
-#pragma unroll
-    for (int r = 0; r < RW; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NB; ++c) {
-      // keep one x block live at a time (the code loads above are already in flight)
-      __builtin_amdgcn_sched_barrier(0);
-      const int b = j + LPR * c;
-      float4 xv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) xv[k] = *xs_chunk(xs, b, k);
-      const float m8 = -8.0f * bs[b];
-#pragma unroll
-      for (int r = 0; r < RW; ++r) acc[r] = fmaf(f16_to_f32(sc[r][c]), block_dot(q[r][c], xv, m8), acc[r]);
-    }
-    // reduce over the LPR lanes of each row
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) acc[r] += __shfl_xor(acc[r], o);
-    }
-    // partner row (row ^ 1) for the paired epilogues
-    float pv[RW];
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      if constexpr (RPW >= 2) pv[r] = __shfl_xor(acc[r], LPR);
-      else pv[r] = acc[r ^ (RW > 1 ? 1 : 0)];
-    }
-    if (j != 0) continue;
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const int dr = row[r];
-      if (dr >= p.n_rows) continue;
-      const float v = acc[r];
-      float* yr = p.y + (int64_t)m * p.y_stride;
-      if constexpr (EPI == EPI_STORE) {
-        yr[dr] = v;
-      } else if constexpr (EPI == EPI_STORE_CANON) {
-        const int cr = (p.row_map ? p.row_map[dr] : dr) - p.map_lo;
-        if (cr >= 0 && cr < p.map_n) yr[cr] = v;
-      } else if constexpr (EPI == EPI_RESID) {
-        yr[dr] += v;
-      } else if constexpr (EPI == EPI_LOGITS) {
-        yr[dr] = v;
-        if (v > best_v) { best_v = v; best_i = dr; }
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        if ((dr & 1) == 0) yr[dr >> 1] = silu(v) * pv[r];
-      } else if constexpr (EPI == EPI_MOE_SWIGLU) {
-        if ((moe_lr[r] & 1) == 0) yr[moe_off[r] + (moe_lr[r] >> 1)] = silu(v) * pv[r];
-      } else if constexpr (EPI == EPI_QKV) {
-        const int D = p.D, HD = p.H * p.D, GD = p.G * p.D;
-        const int b = m / p.t, ti = m - b * p.t;
-        const int pos = p.seq_lens[b] + ti;
-        if (pos < 0 || pos >= p.max_pos) { atomicOr(p.err, 4); continue; }
-        float out;
-        int head, d;
-        if (dr < HD + GD) {
-          const int local = dr < HD ? dr : dr - HD;
-          head = local / D;
-          const int i = (local - head * D) >> 1;
-          const float2 cs = p.rope[(int64_t)pos * (D >> 1) + i];
-          if ((dr & 1) == 0) { out = v * cs.x - pv[r] * cs.y; d = i; }
-          else { out = pv[r] * cs.y + v * cs.x; d = i + (D >> 1); }
-          if (dr < HD) {
-            p.qout[((int64_t)m * p.H + head) * D + d] = out;
-            continue;
+      // reduce over the LPR lanes of each row
+  #pragma unroll
+      for (int r = 0; r < RW; ++r) {
+  #pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) acc[r] += __shfl_xor(acc[r], o);
+      }
+      // partner row (row ^ 1) for the paired epilogues
+      float pv[RW];
+  #pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        if constexpr (RPW >= 2) pv[r] = __shfl_xor(acc[r], LPR);
+        else pv[r] = acc[r ^ (RW > 1 ? 1 : 0)];
+      }
+      if (j == 0) {
+  #pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          const int dr = g.row[r];
+          if (dr >= p.n_rows) continue;
+          const float v = acc[r];
+          float* yr = p.y + (int64_t)m * p.y_stride;
+          if constexpr (EPI == EPI_STORE) {
+            yr[dr] = v;
+          } else if constexpr (EPI == EPI_STORE_CANON) {
+            const int cr = (p.row_map ? p.row_map[dr] : dr) - p.map_lo;
+            if (cr >= 0 && cr < p.map_n) yr[cr] = v;
+          } else if constexpr (EPI == EPI_RESID) {
+            yr[dr] += v;
+          } else if constexpr (EPI == EPI_LOGITS) {
+            yr[dr] = v;
+            if (v > best_v) { best_v = v; best_i = dr; }
+          } else if constexpr (EPI == EPI_SWIGLU) {
+            if ((dr & 1) == 0) yr[dr >> 1] = silu(v) * pv[r];
+          } else if constexpr (EPI == EPI_MOE_SWIGLU) {
+            if ((g.moe_lr[r] & 1) == 0) yr[g.moe_off[r] + (g.moe_lr[r] >> 1)] = silu(v) * pv[r];
+          } else if constexpr (EPI == EPI_QKV) {
+            const int D = p.D, HD = p.H * p.D, GD = p.G * p.D;
+            if (pos < 0 || pos >= p.max_pos) { atomicOr(p.err, 4); continue; }
+            float out;
+            int head, d;
+            if (dr < HD + GD) {
+              const int local = dr < HD ? dr : dr - HD;
+              head = local / D;
+              const int i = (local - head * D) >> 1;
+              const float2 cs = g.cs[r];
+              if ((dr & 1) == 0) { out = v * cs.x - pv[r] * cs.y; d = i; }
+              else { out = pv[r] * cs.y + v * cs.x; d = i + (D >> 1); }
+              if (dr < HD) {
+                p.qout[((int64_t)m * p.H + head) * D + d] = out;
+                continue;
+              }
+            } else {
+              const int local = dr - HD - GD;
+              head = local / D;
+              d = local - head * D;
+              out = v;
+            }
+            const int which = dr < HD + GD ? 0 : 1;
+            if (page < 0 || page >= p.n_pages) { atomicOr(p.err, 1); continue; }
+            uint16_t* dst = p.pool + (int64_t)page * p.pool_page_stride +
+                            ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D + d;
+            *dst = (p.kv_dtype == 1) ? f32_to_f16(out) : f32_to_bf16(out);
           }
-        } else {
-          const int local = dr - HD - GD;
-          head = local / D;
-          d = local - head * D;
-          out = v;
         }
-        const int which = dr < HD + GD ? 0 : 1;
-        if (pos / kPageTokens >= p.max_pages) { atomicOr(p.err, 1); continue; }
-        const int page = p.page_table[(int64_t)b * p.max_pages + pos / kPageTokens];
-        if (page < 0 || page >= p.n_pages) { atomicOr(p.err, 1); continue; }
-        uint16_t* dst = p.pool + (int64_t)page * p.pool_page_stride +
-                        ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D + d;
-        *dst = (p.kv_dtype == 1) ? f32_to_f16(out) : f32_to_bf16(out);
       }
+  };
+  Group<LPR, NB, RW> alt;
+  while (gi < n_groups) {
+    int gn = gi + gridDim.x * 4;
+    if (gn < n_groups) {
+      load_group<LPR, NB, RW, IN, EPI>(p, m, K, gn, j, rsub, alt);
+      if constexpr (EPI == EPI_QKV) load_rope<LPR, NB, RW>(p, pos, alt);
     }
+    compute(cur);
+    gi = gn;
+    if (gi >= n_groups) break;
+    gn = gi + gridDim.x * 4;
+    if (gn < n_groups) {
+      load_group<LPR, NB, RW, IN, EPI>(p, m, K, gn, j, rsub, cur);
+      if constexpr (EPI == EPI_QKV) load_rope<LPR, NB, RW>(p, pos, cur);
+    }
+    compute(alt);
+    gi = gn;
   }
   if constexpr (EPI == EPI_LOGITS) {
     // workgroup argmax partial (ties -> lowest index)
@@ -324,17 +433,29 @@ static int gcd_pow2_64(int nblk) {
 template <int LPR, int NB, int RW, int IN, int EPI>
 static int launch_one(const GemvParams& p, int K, int M, hipStream_t s, int* grid_out) {
   constexpr int GROUP = (kWave / LPR) * RW;
+  auto kern = k_gemv<LPR, NB, RW, IN, EPI>;
+  const size_t lds = sizeof(float) * ((size_t)K + (size_t)(K >> 5) * 9 + 16);
+  // resident workgroups of this instantiation (queried once)
+  static int resident = 0;
+  if (resident == 0) {
+    if (lds > 65536 &&
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return -1;
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    resident = per_cu * cus;
+  }
   const int n_groups = (p.n_rows + GROUP - 1) / GROUP;
-  int grid = (n_groups + 3) / 4;
+  // fewest groups per wave that keeps every workgroup resident (M rows share the grid)
+  const int cap = std::max(1, resident / std::max(1, M));
+  const int waves_needed = (n_groups + 3) / 4;
+  const int per_wave = std::max(1, (waves_needed + cap - 1) / cap);
+  int grid = (n_groups + 4 * per_wave - 1) / (4 * per_wave);
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
   if (grid_out) *grid_out = grid;
-  const size_t lds = sizeof(float) * ((size_t)K + (size_t)(K >> 5) + 16);
-  auto kern = k_gemv<LPR, NB, RW, IN, EPI>;
-  if (lds > 65536) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return -1;
-  }
   hipLaunchKernelGGL(kern, dim3(grid, M), dim3(kBlock), lds, s, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -47,6 +47,12 @@ struct GemvParams {
   int64_t x_stride = 0;
   const uint16_t* gamma = nullptr;  // RMSNorm gain (IN_RMSNORM)
   float eps = 1e-6f;
+  // IN_RMSNORM of layer 0: the input row is the fp16 embedding of tokens[m] (rows >= vocab set
+  // the error word and read row 0); workgroup 0 also stores it to x_out (the residual stream)
+  const uint16_t* embed = nullptr;
+  const int32_t* tokens = nullptr;
+  int32_t vocab = 0;
+  float* x_out = nullptr;
   // output
   float* y = nullptr;
   int64_t y_stride = 0;
@@ -94,6 +100,7 @@ struct AttnParams {
   float* part = nullptr;            // [M][H][max_splits][D + 2] (acc, m, l)
   float* out = nullptr;             // [M][H][D]
   int32_t* err = nullptr;
+  int32_t* counters = nullptr;      // [batch][G] split arrival counters, zero between launches
 };
 
 // launchers (bw_gemv.hip, bw_attn.hip, bw_misc.hip)

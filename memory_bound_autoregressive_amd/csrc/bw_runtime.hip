@@ -132,6 +132,7 @@ struct bw_model {
   float* q = nullptr;            // [T][H][D]
   float* attn_part = nullptr;    // [T][H][max_splits][D+2]
   float* attn_out = nullptr;     // [T][H*D]
+  int32_t* attn_cnt = nullptr;   // [T][G] split counters (zero between launches)
   float* act = nullptr;          // [T][act_width]
   int64_t act_width = 0;
   float* logits = nullptr;       // [T][V]
@@ -144,6 +145,20 @@ struct bw_model {
   int32_t* err = nullptr;
   int pages_per_split = 4;
   int max_splits = 0;
+  // measurement hook
+  int trace_class = -1;
+  std::vector<hipEvent_t> trace_ev;
+  // captured steps: one hipGraph per distinct argument set, replayed on the caller's stream
+  hipStream_t cap_stream = nullptr;
+  struct GraphEntry {
+    std::vector<uintptr_t> key;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    uint64_t last_use = 0;
+  };
+  std::vector<GraphEntry> graphs;
+  uint64_t use_clock = 0;
+  bool use_graphs = true;
 };
 
 struct bw_kv_pool {
@@ -296,6 +311,7 @@ static int check_shape(const bw_model_config& c) {
   if (c.page_tokens != kPageTokens) return fail(BW_EINVAL, "page_tokens must be 16");
   if (c.kv_dtype != BW_KV_F16 && c.kv_dtype != BW_KV_BF16) return fail(BW_EINVAL, "kv_dtype must be BW_KV_F16 or BW_KV_BF16");
   if (c.max_positions < 1 || c.max_tokens < 1) return fail(BW_EINVAL, "max_positions and max_tokens must be positive");
+  if (c.max_positions > 65536) return fail(BW_EINVAL, "max_positions must be <= 65536");
   int qr = c.n_q_heads / c.n_kv_heads;
   (void)qr;
   if (is_moe(c)) {
@@ -433,6 +449,9 @@ extern "C" int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed
     m->attn_part = (float*)p;
     if ((rc = ws_alloc(m, sizeof(float) * T * H * D, &p))) return bail(rc);
     m->attn_out = (float*)p;
+    if ((rc = ws_alloc(m, sizeof(int32_t) * T * G, &p))) return bail(rc);
+    m->attn_cnt = (int32_t*)p;
+    HIP_OK(hipMemset(m->attn_cnt, 0, sizeof(int32_t) * T * G));
     if ((rc = ws_alloc(m, sizeof(float) * T * aw, &p))) return bail(rc);
     m->act = (float*)p;
     if ((rc = ws_alloc(m, sizeof(float) * T * c.vocab, &p))) return bail(rc);
@@ -453,7 +472,9 @@ extern "C" int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed
       m->gates = (float*)p;
     }
   }
-  HIP_OK(hipDeviceSynchronize());
+  if (hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess)
+    return bail(fail(BW_EHIP, "stream creation failed"));
+  if (hipDeviceSynchronize() != hipSuccess) return bail(fail(BW_EHIP, "device synchronisation failed"));
   *out = m;
   return BW_OK;
 }
@@ -461,6 +482,11 @@ extern "C" int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed
 extern "C" int bw_model_free(bw_model* m) {
   if (!m) return BW_OK;
   (void)hipDeviceSynchronize();
+  for (auto& g : m->graphs) {
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    if (g.graph) (void)hipGraphDestroy(g.graph);
+  }
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   m->arena.release();
   for (void* p : m->ws) (void)hipFree(p);
   delete m;
@@ -631,25 +657,35 @@ static AttnParams attn_params(bw_model* m, const bw_kv_pool* pool, int l, const 
   a.part = m->attn_part;
   a.out = out;
   a.err = m->err;
+  a.counters = m->attn_cnt;
   return a;
 }
 
-extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens,
-                              const int32_t* seq_lens, const int32_t* page_table, int32_t batch,
-                              int32_t t, int32_t max_pages, float* logits_out, int32_t* argmax_out,
-                              void* stream) {
-  if (!m || !pool || !tokens || !seq_lens || !page_table) return fail(BW_EINVAL, "null argument");
-  if (pool->m != m) return fail(BW_ESTATE, "pool belongs to another model");
-  if (batch < 1 || t < 1 || max_pages < 1) return fail(BW_EINVAL, "batch, t and max_pages must be positive");
+static inline void trace_mark(bw_model* m, int cls, int layer, int which, hipStream_t s) {
+  if (m->trace_class == cls && (size_t)(2 * layer + which) < m->trace_ev.size())
+    (void)hipEventRecord(m->trace_ev[2 * layer + which], s);
+}
+
+extern "C" int bw_set_trace(bw_model* m, int32_t kernel_class, void* const* events, int32_t n_layers) {
+  if (!m) return fail(BW_EINVAL, "null model");
+  if (!events) {
+    m->trace_class = -1;
+    m->trace_ev.clear();
+    return BW_OK;
+  }
+  if (kernel_class < 0 || kernel_class > BW_K_MOE_DOWN || n_layers < 1) return fail(BW_EINVAL, "bad trace request");
+  m->trace_ev.assign((hipEvent_t*)events, (hipEvent_t*)events + 2 * n_layers);
+  m->trace_class = kernel_class;
+  return BW_OK;
+}
+
+// enqueue every kernel of one step on stream s (arguments already validated)
+static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, const int32_t* seq_lens,
+                        const int32_t* page_table, int32_t batch, int32_t t, int32_t max_pages,
+                        float* logits_out, int32_t* argmax_out, hipStream_t s) {
   const int M = batch * t;
-  if (M > m->c.max_tokens) return fail(BW_ERANGE, "batch * t = %d exceeds max_tokens %d", M, m->c.max_tokens);
-  if ((int64_t)max_pages * kPageTokens > (int64_t)m->max_splits * m->pages_per_split * kPageTokens &&
-      (int64_t)max_pages > ((int64_t)m->c.max_positions + kPageTokens - 1) / kPageTokens + 1)
-    ;  // a wide page table is fine; positions are bounded by max_positions on the device
   const auto& c = m->c;
-  hipStream_t s = (hipStream_t)stream;
   const int d = c.d_model, H = c.n_q_heads, G = c.n_kv_heads, D = c.head_dim;
-  if (launch_embed(m->embed, c.vocab, d, tokens, M, m->x, m->err, s)) return fail(BW_EHIP, "embed launch failed");
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerDev& Ld = m->L[l];
     // RMSNorm + QKV + RoPE + KV append
@@ -675,10 +711,20 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
     g.kv_dtype = c.kv_dtype;
     g.qout = m->q;
     g.err = m->err;
+    if (l == 0) {  // the embedding gather runs in layer 0's input stage
+      g.embed = m->embed;
+      g.tokens = tokens;
+      g.vocab = c.vocab;
+      g.x_out = m->x;
+    }
+    trace_mark(m, BW_K_QKV, l, 0, s);
     if (launch_gemv(IN_RMSNORM, EPI_QKV, g, M, s)) return fail(BW_EHIP, "qkv launch failed (layer %d)", l);
+    trace_mark(m, BW_K_QKV, l, 1, s);
     // attention
     AttnParams a = attn_params(m, pool, l, m->q, seq_lens, page_table, t, max_pages, m->attn_out);
+    trace_mark(m, BW_K_ATTN, l, 0, s);
     if (launch_attention(a, c.kv_dtype, batch, s)) return fail(BW_EHIP, "attention launch failed (layer %d)", l);
+    trace_mark(m, BW_K_ATTN, l, 1, s);
     // O + residual
     GemvParams o;
     o.w = Ld.o;
@@ -687,7 +733,9 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
     o.x_stride = (int64_t)H * D;
     o.y = m->x;
     o.y_stride = d;
+    trace_mark(m, BW_K_O, l, 0, s);
     if (launch_gemv(IN_PLAIN, EPI_RESID, o, M, s)) return fail(BW_EHIP, "o launch failed (layer %d)", l);
+    trace_mark(m, BW_K_O, l, 1, s);
     if (!is_moe(c)) {
       GemvParams gu;
       gu.w = Ld.gu;
@@ -698,7 +746,9 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
       gu.eps = c.rms_eps;
       gu.y = m->act;
       gu.y_stride = m->act_width;
+      trace_mark(m, BW_K_GATE_UP, l, 0, s);
       if (launch_gemv(IN_RMSNORM, EPI_SWIGLU, gu, M, s)) return fail(BW_EHIP, "gate/up launch failed (layer %d)", l);
+      trace_mark(m, BW_K_GATE_UP, l, 1, s);
       GemvParams dn;
       dn.w = Ld.dn;
       dn.n_rows = Ld.dn.N;
@@ -706,14 +756,18 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
       dn.x_stride = m->act_width;
       dn.y = m->x;
       dn.y_stride = d;
+      trace_mark(m, BW_K_DOWN, l, 0, s);
       if (launch_gemv(IN_PLAIN, EPI_RESID, dn, M, s)) return fail(BW_EHIP, "down launch failed (layer %d)", l);
+      trace_mark(m, BW_K_DOWN, l, 1, s);
     } else {
       int32_t* sel = m->sel + (int64_t)l * c.max_tokens * c.top_k;
       float* gates = m->gates + (int64_t)l * c.max_tokens * c.top_k;
+      trace_mark(m, BW_K_ROUTER, l, 0, s);
       if (launch_router(Ld.router, c.n_experts, d, m->x, Ld.ffn_norm, c.rms_eps, M, m->router_logits, s))
         return fail(BW_EHIP, "router launch failed (layer %d)", l);
       if (launch_topk(m->router_logits, c.n_experts, c.top_k, M, sel, gates, s))
         return fail(BW_EHIP, "top-k launch failed (layer %d)", l);
+      trace_mark(m, BW_K_ROUTER, l, 1, s);
       GemvParams gu;
       gu.w.K = d;
       gu.n_rows = c.top_k * 2 * c.expert_ffn + c.n_shared * 2 * c.shared_ffn;
@@ -731,7 +785,9 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
       gu.Fe = c.expert_ffn;
       gu.Fs = c.shared_ffn;
       gu.ex = Ld.ex;
+      trace_mark(m, BW_K_MOE_GATE_UP, l, 0, s);
       if (launch_gemv(IN_RMSNORM, EPI_MOE_SWIGLU, gu, M, s)) return fail(BW_EHIP, "expert gate/up launch failed (layer %d)", l);
+      trace_mark(m, BW_K_MOE_GATE_UP, l, 1, s);
       GemvParams dn = gu;
       dn.n_rows = d;
       dn.x = m->act;
@@ -739,9 +795,11 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
       dn.gamma = nullptr;
       dn.y = m->x;
       dn.y_stride = d;
+      trace_mark(m, BW_K_MOE_DOWN, l, 0, s);
       if (int e = launch_gemv(IN_MOE_DOWN, EPI_RESID, dn, M, s))
         return fail(BW_EHIP, "expert down launch failed (layer %d, code %d: -2 = unsupported K %d)", l, e,
                     c.top_k * c.expert_ffn + c.n_shared * c.shared_ffn);
+      trace_mark(m, BW_K_MOE_DOWN, l, 1, s);
     }
   }
   // final RMSNorm + lm_head + argmax
@@ -757,10 +815,68 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
   lm.amax_val = m->amax_val;
   lm.amax_idx = m->amax_idx;
   int lm_grid = 0;
+  trace_mark(m, BW_K_LM_HEAD, 0, 0, s);
   if (launch_gemv(IN_RMSNORM, EPI_LOGITS, lm, M, s, &lm_grid)) return fail(BW_EHIP, "lm_head launch failed");
+  trace_mark(m, BW_K_LM_HEAD, 0, 1, s);
   if (lm_grid > m->lm_parts) return fail(BW_EHIP, "lm_head grid exceeds the argmax workspace");
   if (argmax_out && launch_argmax_final(m->amax_val, m->amax_idx, lm_grid, M, argmax_out, s))
     return fail(BW_EHIP, "argmax launch failed");
+  return BW_OK;
+}
+
+extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens,
+                              const int32_t* seq_lens, const int32_t* page_table, int32_t batch,
+                              int32_t t, int32_t max_pages, float* logits_out, int32_t* argmax_out,
+                              void* stream) {
+  if (!m || !pool || !tokens || !seq_lens || !page_table) return fail(BW_EINVAL, "null argument");
+  if (pool->m != m) return fail(BW_ESTATE, "pool belongs to another model");
+  if (batch < 1 || t < 1 || max_pages < 1) return fail(BW_EINVAL, "batch, t and max_pages must be positive");
+  if (batch * t > m->c.max_tokens) return fail(BW_ERANGE, "batch * t = %d exceeds max_tokens %d", batch * t, m->c.max_tokens);
+  hipStream_t s = (hipStream_t)stream;
+  if (!m->use_graphs || m->trace_class >= 0)
+    return enqueue_step(m, pool, tokens, seq_lens, page_table, batch, t, max_pages, logits_out, argmax_out, s);
+  // replay a captured step when the arguments match one, else capture one (a one-time cost)
+  const std::vector<uintptr_t> key = {(uintptr_t)pool, (uintptr_t)tokens, (uintptr_t)seq_lens, (uintptr_t)page_table,
+                                      (uintptr_t)batch, (uintptr_t)t, (uintptr_t)max_pages, (uintptr_t)logits_out,
+                                      (uintptr_t)argmax_out};
+  ++m->use_clock;
+  for (auto& g : m->graphs)
+    if (g.key == key) {
+      g.last_use = m->use_clock;
+      HIP_OK(hipGraphLaunch(g.exec, s));
+      return BW_OK;
+    }
+  bw_model::GraphEntry e;
+  e.key = key;
+  e.last_use = m->use_clock;
+  HIP_OK(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed));
+  int rc = enqueue_step(m, pool, tokens, seq_lens, page_table, batch, t, max_pages, logits_out, argmax_out, m->cap_stream);
+  hipError_t ce = hipStreamEndCapture(m->cap_stream, &e.graph);
+  if (rc) {
+    if (e.graph) (void)hipGraphDestroy(e.graph);
+    return rc;
+  }
+  if (ce != hipSuccess) return fail(BW_EHIP, "step capture failed: %s", hipGetErrorString(ce));
+  if (hipGraphInstantiate(&e.exec, e.graph, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(e.graph);
+    return fail(BW_EHIP, "graph instantiation failed");
+  }
+  if (m->graphs.size() >= 8) {  // evict the least recently used
+    size_t v = 0;
+    for (size_t i = 1; i < m->graphs.size(); ++i)
+      if (m->graphs[i].last_use < m->graphs[v].last_use) v = i;
+    (void)hipGraphExecDestroy(m->graphs[v].exec);
+    (void)hipGraphDestroy(m->graphs[v].graph);
+    m->graphs.erase(m->graphs.begin() + v);
+  }
+  m->graphs.push_back(e);
+  HIP_OK(hipGraphLaunch(e.exec, s));
+  return BW_OK;
+}
+
+extern "C" int bw_set_graphs(bw_model* m, int32_t enable) {
+  if (!m) return fail(BW_EINVAL, "null model");
+  m->use_graphs = enable != 0;
   return BW_OK;
 }
 
