@@ -146,6 +146,14 @@ int bw_decode_step(bw_model* model, bw_kv_pool* pool, const int32_t* tokens_dev,
 /* Turn step capture on (default) or off (every call then launches its kernels directly). */
 int bw_set_graphs(bw_model* model, int32_t enable);
 
+/* Row count from which a step (and bw_debug_matvec) runs its dense matrices -- QKV, O, gate/up,
+ * down, lm_head -- as one int4 GEMM on the matrix cores over all batch * t rows, reading each
+ * weight once (bw24 deep-dive page, section 5, stage 4: the drafted tokens of a verify step are
+ * extra rows of one pass over the weights). Below it each row takes its own GEMV pass. 0 turns
+ * the GEMM path off. Default 8. Routed experts always take the GEMV path.
+ * Errors: BW_EINVAL (null model, min_rows < 0). */
+int bw_set_gemm_min_rows(bw_model* model, int32_t min_rows);
+
 /* Text of the last error on this thread ("" if none). */
 const char* bw_last_error(void);
 

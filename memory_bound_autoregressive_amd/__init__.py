@@ -26,6 +26,7 @@ EXPORTS = (
     "bw_kv_pool_fill", "bw_kv_pool_synthesize", "bw_kv_pool_read", "bw_decode_step",
     "bw_last_error", "bw_check_device_error", "bw_debug_dequant", "bw_debug_matvec",
     "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden", "bw_set_trace", "bw_set_graphs",
+    "bw_set_gemm_min_rows",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.bw_debug_read_hidden.argtypes = [vp, i32, vp, vp]
         L.bw_set_trace.argtypes = [vp, i32, vp, i32]
         L.bw_set_graphs.argtypes = [vp, i32]
+        L.bw_set_gemm_min_rows.argtypes = [vp, i32]
         _lib = L
     return _lib
 
@@ -203,3 +205,7 @@ def bw_set_trace(model: int, kernel_class: str, events, n_layers: int) -> None:
 
 def bw_set_graphs(model: int, enable: bool) -> None:
     _check(lib().bw_set_graphs(model, int(bool(enable))), "bw_set_graphs")
+
+
+def bw_set_gemm_min_rows(model: int, min_rows: int) -> None:
+    _check(lib().bw_set_gemm_min_rows(model, int(min_rows)), "bw_set_gemm_min_rows")

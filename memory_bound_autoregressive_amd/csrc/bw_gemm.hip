@@ -1,0 +1,340 @@
+// bw_gemm.hip - int4 block-quantised GEMM on the matrix cores for the batched / verify step.
+//
+// Operation: Y[m][n] = sum_k W[n][k] X[m][k] for all M = batch * t rows of a step at once, W int4 in
+// blocks of 32 along K with one fp16 scale per block (w = scale * (q - 8)). With many rows every
+// weight is used by all of them, so the product is a dense contraction (bw24 deep-dive page,
+// section 5, stage 4: the verify kernel takes the drafted tokens as extra rows that share one pass
+// over the weights).
+//
+// Numerics, exact up to fp32 summation order:
+//  - a code q becomes the fp16 value (q - 8) exactly: the nibble goes into the mantissa of 1024
+//    (bits 0x6400 | q) and one packed subtract of 1032 follows;
+//  - X is staged as an fp16 pair x_hi = fp16(x), x_lo = fp16(x - x_hi), so a 32-wide block costs
+//    two v_mfma_f32_16x16x32_f16 whose products are exact and whose sums are fp32;
+//  - the fp16 block scale multiplies each block's 16x16 fp32 result, so no weight is rounded.
+//
+// MFMA operand layout (16x16x32 f16): lane l supplies row l % 16 of A and column l % 16 of B, eight
+// K slots each, lane group l / 16 taking slots 8 (l / 16) .. +7; the result lane l holds rows
+// 4 (l / 16) .. +3 of column l % 16. The sum over K does not depend on which element sits in which
+// slot as long as A and B agree, so lane group g takes bytes 4g..4g+3 of a block (elements 4g..4g+3
+// in the low nibbles, 16+4g..16+4g+3 in the high nibbles) with one 4-byte load, and X is staged in
+// the matching order.
+//
+// Work split: workgroup = (tile of 128 weight rows, k-split, group of up to 128 X rows); 4 waves,
+// wave w owns rows [32w, 32w + 32) of the tile as two 16-column B tiles and every m-tile. X is
+// staged through LDS 64 columns at a time. Each k-split writes fp32 partials; k_gemm_epilogue sums
+// them in split order and applies the step's epilogue (RoPE + KV append, residual, SwiGLU, logits).
+#include <algorithm>
+
+#include "bw_common.h"
+#include "bw_internal.h"
+
+namespace bw {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kNS = 2;              // 16-column B tiles per wave
+constexpr int kNT = 4 * 16 * kNS;   // weight rows per workgroup
+constexpr int kKC = 64;             // K columns staged per round (two blocks)
+constexpr int kXP = kKC + 8;        // staged row pitch in fp16 elements (16-byte aligned, skews banks)
+constexpr int kMaxRowsWG = 128;     // X rows per workgroup (8 m-tiles)
+
+// 1 / sqrt(mean(x^2) + eps) of each row of x (the RMSNorm factor of the batched path)
+__global__ __launch_bounds__(kBlock) void k_rowrms(const float* __restrict__ x, int64_t stride, int K,
+                                                   float eps, float* __restrict__ r) {
+  __shared__ float red[4];
+  const float* xr = x + (int64_t)blockIdx.x * stride;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < K; k += kBlock) ss = fmaf(xr[k], xr[k], ss);
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0) r[blockIdx.x] = 1.0f / sqrtf(ss / (float)K + eps);
+}
+
+// Bytes 4g..4g+3 of a block as eight fp16 (q - 8): low nibbles of the four bytes, then high nibbles.
+__device__ __forceinline__ h8_t codes_to_h8(uint32_t c) {
+  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+  u32x4 r;
+  r[0] = ((lo & 0xFFu) | ((lo & 0xFF00u) << 8)) | 0x64006400u;
+  r[1] = (((lo >> 16) & 0xFFu) | ((lo >> 8) & 0xFF0000u)) | 0x64006400u;
+  r[2] = ((hi & 0xFFu) | ((hi & 0xFF00u) << 8)) | 0x64006400u;
+  r[3] = (((hi >> 16) & 0xFFu) | ((hi >> 8) & 0xFF0000u)) | 0x64006400u;
+  const h8_t off = {(_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1032.0f,
+                    (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1032.0f};
+  return __builtin_bit_cast(h8_t, r) - off;  // (1024 + q) - 1032 = q - 8, exact
+}
+
+// Staged position of element kb (0..31, kb % 4 == 0) of a block: lane group (kb % 16) / 4, low half
+// for kb < 16, high half otherwise.
+__device__ __forceinline__ int staged_pos(int kb) { return 8 * ((kb & 15) >> 2) + 4 * (kb >> 4); }
+
+// element (m, n) of k-split ks goes to out[ks * ks_stride + m * ldo + n]
+template <int MT, int IN>
+__global__ __launch_bounds__(kBlock) void k_gemm(GemvParams p, int M, int ksplit, const float* __restrict__ rms,
+                                                float* __restrict__ out, int64_t ldo, int64_t ks_stride) {
+  __shared__ __attribute__((aligned(16))) _Float16 xh[MT * 16 * kXP];
+  __shared__ __attribute__((aligned(16))) _Float16 xl[MT * 16 * kXP];
+  const int K = p.w.K, N = p.w.N;
+  const int nblk = K >> 5;
+  const int n0 = blockIdx.x * kNT;
+  const int ks = blockIdx.y;
+  const int m0 = blockIdx.z * kMaxRowsWG;
+  const int kc = K / ksplit;
+  const int k_begin = ks * kc, k_end = k_begin + kc;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ln = lane & 15, g = lane >> 4;
+
+  int nrow[kNS];
+  bool nok[kNS];
+#pragma unroll
+  for (int s = 0; s < kNS; ++s) {
+    nrow[s] = n0 + wave * 16 * kNS + s * 16 + ln;
+    nok[s] = nrow[s] < N;
+  }
+
+  f4_t tot[kNS][MT];
+#pragma unroll
+  for (int s = 0; s < kNS; ++s)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) tot[s][t] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = k_begin; k0 < k_end; k0 += kKC) {
+    // this round's code slices and scales go out before the staging of X
+    uint32_t cw[kNS][kKC / 32];
+    float sc[kNS][kKC / 32];
+#pragma unroll
+    for (int s = 0; s < kNS; ++s)
+#pragma unroll
+      for (int bb = 0; bb < kKC / 32; ++bb) {
+        const int b = (k0 >> 5) + bb;
+        const int64_t n = nrow[s];
+        cw[s][bb] = nok[s] ? __builtin_nontemporal_load((const uint32_t*)(p.w.codes + n * (K >> 1) + b * 16 + 4 * g)) : 0u;
+        sc[s][bb] = nok[s] ? f16_to_f32(p.w.scales[n * nblk + (b % p.w.lpr) * p.w.nb + b / p.w.lpr]) : 0.f;
+      }
+    __syncthreads();  // the previous round's reads of xh / xl are done
+    for (int e = threadIdx.x; e < MT * 16 * (kKC / 4); e += kBlock) {
+      const int row = e / (kKC / 4), c4 = (e - row * (kKC / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m0 + row < M) {
+        v = *(const float4*)(p.x + (int64_t)(m0 + row) * p.x_stride + k0 + c4);
+        if constexpr (IN == IN_RMSNORM) {
+          const float r = rms[m0 + row];
+          const uint2 gh = *(const uint2*)(p.gamma + k0 + c4);
+          v.x *= r * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
+          v.y *= r * f16_to_f32((uint16_t)(gh.x >> 16));
+          v.z *= r * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
+          v.w *= r * f16_to_f32((uint16_t)(gh.y >> 16));
+        }
+      }
+      const int at = row * kXP + (c4 & ~31) + staged_pos(c4 & 31);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      uint16_t hh[4], ll[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 h = (_Float16)vv[i];
+        hh[i] = __builtin_bit_cast(uint16_t, h);
+        ll[i] = __builtin_bit_cast(uint16_t, (_Float16)(vv[i] - (float)h));
+      }
+      *(uint2*)(xh + at) = make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
+      *(uint2*)(xl + at) = make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bb = 0; bb < kKC / 32; ++bb) {
+      h8_t bf[kNS];
+#pragma unroll
+      for (int s = 0; s < kNS; ++s) bf[s] = codes_to_h8(cw[s][bb]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int at = (t * 16 + ln) * kXP + bb * 32 + 8 * g;
+        const h8_t ah = *(const h8_t*)(xh + at);
+        const h8_t al = *(const h8_t*)(xl + at);
+#pragma unroll
+        for (int s = 0; s < kNS; ++s) {
+          f4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bf[s], f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bf[s], acc, 0, 0, 0);
+          tot[s][t] += sc[s][bb] * acc;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kNS; ++s) {
+    if (!nok[s]) continue;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + t * 16 + 4 * g + v;
+        if (m < M) out[(int64_t)ks * ks_stride + (int64_t)m * ldo + nrow[s]] = tot[s][t][v];
+      }
+  }
+}
+
+// Sum of the k-split partials part[ks][m][n] (in split order) and the step's epilogue; one thread
+// per pair of device rows (2i, 2i + 1), which is a RoPE pair for q / k and a (gate, up) pair for
+// the SwiGLU matrix.
+template <int EPI>
+__global__ __launch_bounds__(kBlock) void k_gemm_epilogue(GemvParams p, int M, int ksplit,
+                                                         const float* __restrict__ part) {
+  const int N = p.w.N;
+  const int64_t pairs = (int64_t)M * (N >> 1);
+  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < pairs; t += (int64_t)gridDim.x * kBlock) {
+    const int m = (int)(t / (N >> 1));
+    const int dr = 2 * (int)(t - (int64_t)m * (N >> 1));
+    float v0 = 0.f, v1 = 0.f;
+    for (int s = 0; s < ksplit; ++s) {
+      const float2 pv = *(const float2*)(part + ((int64_t)s * M + m) * N + dr);
+      v0 += pv.x;
+      v1 += pv.y;
+    }
+    float* yr = p.y + (int64_t)m * p.y_stride;
+    if constexpr (EPI == EPI_STORE_CANON) {
+      const int c0 = (p.row_map ? p.row_map[dr] : dr) - p.map_lo;
+      const int c1 = (p.row_map ? p.row_map[dr + 1] : dr + 1) - p.map_lo;
+      if (c0 >= 0 && c0 < p.map_n) yr[c0] = v0;
+      if (c1 >= 0 && c1 < p.map_n) yr[c1] = v1;
+    } else if constexpr (EPI == EPI_RESID) {
+      yr[dr] += v0;
+      yr[dr + 1] += v1;
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      yr[dr >> 1] = silu(v0) * v1;
+    } else if constexpr (EPI == EPI_LOGITS) {
+      yr[dr] = v0;
+      yr[dr + 1] = v1;
+    } else if constexpr (EPI == EPI_QKV) {
+      const int D = p.D, HD = p.H * p.D, GD = p.G * p.D;
+      const int b = m / p.t, ti = m - b * p.t;
+      const int pos = p.seq_lens[b] + ti;
+      if (pos < 0 || pos >= p.max_pos) {
+        atomicOr(p.err, 4);
+        continue;
+      }
+      float o0 = v0, o1 = v1;
+      int head, d0, d1;
+      if (dr < HD + GD) {  // device rows (2i, 2i + 1) hold head dims (i, i + D/2)
+        const int local = dr < HD ? dr : dr - HD;
+        head = local / D;
+        const int i = (local - head * D) >> 1;
+        const float2 cs = p.rope[(int64_t)pos * (D >> 1) + i];
+        o0 = v0 * cs.x - v1 * cs.y;
+        o1 = v0 * cs.y + v1 * cs.x;
+        d0 = i;
+        d1 = i + (D >> 1);
+        if (dr < HD) {
+          p.qout[((int64_t)m * p.H + head) * D + d0] = o0;
+          p.qout[((int64_t)m * p.H + head) * D + d1] = o1;
+          continue;
+        }
+      } else {
+        const int local = dr - HD - GD;
+        head = local / D;
+        d0 = local - head * D;
+        d1 = d0 + 1;
+      }
+      const int which = dr < HD + GD ? 0 : 1;
+      const int page = pos / kPageTokens < p.max_pages ? p.page_table[(int64_t)b * p.max_pages + pos / kPageTokens] : -1;
+      if (page < 0 || page >= p.n_pages) {
+        atomicOr(p.err, 1);
+        continue;
+      }
+      uint16_t* base = p.pool + (int64_t)page * p.pool_page_stride +
+                       ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D;
+      base[d0] = (p.kv_dtype == 1) ? f32_to_f16(o0) : f32_to_bf16(o0);
+      base[d1] = (p.kv_dtype == 1) ? f32_to_f16(o1) : f32_to_bf16(o1);
+    }
+  }
+}
+
+// argmax of each row of logits [M][N] (lowest index on ties; NaN never wins)
+__global__ __launch_bounds__(kBlock) void k_argmax_rows(const float* __restrict__ logits, int64_t ld, int N,
+                                                       int32_t* __restrict__ out) {
+  const float* row = logits + (int64_t)blockIdx.x * ld;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < N; i += kBlock) {
+    const float v = row[i];
+    if (v > bv) { bv = v; bi = i; }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+  __shared__ float wv[4];
+  __shared__ int wi[4];
+  if ((threadIdx.x & 63) == 0) { wv[threadIdx.x >> 6] = bv; wi[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (wv[w] > wv[0] || (wv[w] == wv[0] && wi[w] < wi[0])) { wv[0] = wv[w]; wi[0] = wi[w]; }
+    out[blockIdx.x] = wi[0] == 0x7fffffff ? 0 : wi[0];
+  }
+}
+
+// ---- launch -----------------------------------------------------------------------------------
+
+int launch_rowrms(const float* x, int64_t stride, int K, float eps, int M, float* r, hipStream_t s) {
+  hipLaunchKernelGGL(k_rowrms, dim3(M), dim3(kBlock), 0, s, x, stride, K, eps, r);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// k-splits: enough workgroups for 256 CUs while each split keeps >= 4 rounds of 64 columns
+int gemm_ksplit(int N, int K, int M) {
+  const int tiles = (N + kNT - 1) / kNT;
+  const int mg = (M + kMaxRowsWG - 1) / kMaxRowsWG;
+  int ks = 1;
+  while (tiles * ks * mg < 256 && K % (ks * 2 * kKC) == 0 && K / (ks * 2) >= 4 * kKC) ks *= 2;
+  return ks;
+}
+
+int64_t gemm_part_elems(int N, int K, int M) { return (int64_t)gemm_ksplit(N, K, M) * M * N; }
+
+bool gemm_supported(int N, int K) { return K % kKC == 0 && N % 2 == 0 && K >= kKC; }
+
+int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* rms, float* part, hipStream_t s) {
+  if (M < 1 || !gemm_supported(p.w.N, p.w.K)) return -2;
+  if (in_mode != IN_PLAIN && in_mode != IN_RMSNORM) return -2;
+  if (in_mode == IN_RMSNORM && rms == nullptr) return -2;
+  const int ks = gemm_ksplit(p.w.N, p.w.K, M);
+  const int mg = (M + kMaxRowsWG - 1) / kMaxRowsWG;
+  const int mt = std::min(8, (M + 15) / 16);
+  // a single split of the logits goes straight to its destination
+  const bool direct = ks == 1 && epi == EPI_LOGITS;
+  float* out = direct ? p.y : part;
+  const int64_t ldo = direct ? p.y_stride : p.w.N;
+  const int64_t ks_stride = (int64_t)M * p.w.N;
+  if (out == nullptr) return -2;
+  const dim3 grid((p.w.N + kNT - 1) / kNT, ks, mg);
+#define BW_G(MT_)                                                                                                \
+  if (mt <= MT_) {                                                                                               \
+    if (in_mode == IN_RMSNORM)                                                                                   \
+      hipLaunchKernelGGL((k_gemm<MT_, IN_RMSNORM>), grid, dim3(kBlock), 0, s, p, M, ks, rms, out, ldo, ks_stride); \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_gemm<MT_, IN_PLAIN>), grid, dim3(kBlock), 0, s, p, M, ks, rms, out, ldo, ks_stride);   \
+  } else
+  BW_G(1) BW_G(2) BW_G(4) BW_G(8) {}
+#undef BW_G
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (direct) return 0;
+  const int64_t pairs = (int64_t)M * (p.w.N >> 1);
+  const int eg = (int)std::min<int64_t>(8192, (pairs + kBlock - 1) / kBlock);
+  const float* cpart = part;
+  switch (epi) {
+    case EPI_STORE_CANON: hipLaunchKernelGGL(k_gemm_epilogue<EPI_STORE_CANON>, dim3(eg), dim3(kBlock), 0, s, p, M, ks, cpart); break;
+    case EPI_RESID: hipLaunchKernelGGL(k_gemm_epilogue<EPI_RESID>, dim3(eg), dim3(kBlock), 0, s, p, M, ks, cpart); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_epilogue<EPI_SWIGLU>, dim3(eg), dim3(kBlock), 0, s, p, M, ks, cpart); break;
+    case EPI_LOGITS: hipLaunchKernelGGL(k_gemm_epilogue<EPI_LOGITS>, dim3(eg), dim3(kBlock), 0, s, p, M, ks, cpart); break;
+    case EPI_QKV: hipLaunchKernelGGL(k_gemm_epilogue<EPI_QKV>, dim3(eg), dim3(kBlock), 0, s, p, M, ks, cpart); break;
+    default: return -2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_rows, dim3(M), dim3(kBlock), 0, s, logits, ld, N, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace bw

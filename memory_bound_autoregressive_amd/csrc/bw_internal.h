@@ -118,4 +118,14 @@ int launch_topk(const float* logits, int E, int k, int M, int32_t* sel, float* g
 int launch_dequant(const Mat& w, const int32_t* row_map, int map_lo, int map_n, float* dst, hipStream_t s);
 int launch_fill16(uint16_t* dst, size_t n, uint16_t bits, hipStream_t s);
 
+// batched path (bw_gemm.hip): matrix-core GEMM over all rows of a step. IN_PLAIN / IN_RMSNORM
+// (rms = per-row RMSNorm factors from launch_rowrms); epilogues STORE_CANON, RESID, SWIGLU, LOGITS,
+// QKV. part: gemm_part_elems(N, K, M) floats of k-split partials.
+bool gemm_supported(int N, int K);
+int gemm_ksplit(int N, int K, int M);
+int64_t gemm_part_elems(int N, int K, int M);
+int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* rms, float* part, hipStream_t s);
+int launch_rowrms(const float* x, int64_t stride, int K, float eps, int M, float* r, hipStream_t s);
+int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, int32_t* out, hipStream_t s);
+
 }  // namespace bw

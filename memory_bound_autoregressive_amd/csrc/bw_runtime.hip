@@ -145,6 +145,10 @@ struct bw_model {
   int32_t* err = nullptr;
   int pages_per_split = 4;
   int max_splits = 0;
+  // batched path: steps with at least gemm_min_rows rows run the dense matrices as MFMA GEMMs
+  float* gemm_part = nullptr;    // k-split partials of the largest dense GEMM
+  float* rms = nullptr;          // [T] RMSNorm factors
+  int gemm_min_rows = 8;
   // measurement hook
   int trace_class = -1;
   std::vector<hipEvent_t> trace_ev;
@@ -460,6 +464,20 @@ extern "C" int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed
     m->amax_val = (float*)p;
     if ((rc = ws_alloc(m, sizeof(int32_t) * T * m->lm_parts, &p))) return bail(rc);
     m->amax_idx = (int32_t*)p;
+    {
+      int64_t part = 0;
+      const int64_t dims[9][2] = {{(int64_t)(H + 2 * G) * D, d}, {d, (int64_t)H * D}, {2 * (int64_t)c.ffn_dim, d},
+                                  {d, c.ffn_dim}, {c.vocab, d}, {2 * (int64_t)c.expert_ffn, d}, {d, c.expert_ffn},
+                                  {2 * (int64_t)c.shared_ffn, d}, {d, c.shared_ffn}};
+      for (int64_t M = 1; M <= T; ++M)
+        for (const auto& nk : dims)
+          if (nk[0] > 0 && nk[1] > 0 && gemm_supported((int)nk[0], (int)nk[1]))
+            part = std::max(part, gemm_part_elems((int)nk[0], (int)nk[1], (int)M));
+      if ((rc = ws_alloc(m, sizeof(float) * std::max<int64_t>(part, 64), &p))) return bail(rc);
+      m->gemm_part = (float*)p;
+      if ((rc = ws_alloc(m, sizeof(float) * T, &p))) return bail(rc);
+      m->rms = (float*)p;
+    }
     if ((rc = ws_alloc(m, 256, &p))) return bail(rc);
     m->err = (int32_t*)p;
     HIP_OK(hipMemset(m->err, 0, 256));
@@ -679,6 +697,26 @@ extern "C" int bw_set_trace(bw_model* m, int32_t kernel_class, void* const* even
   return BW_OK;
 }
 
+// One dense matrix product of a step: the MFMA GEMM when the step has gemm_min_rows rows or more
+// (weights read once for all rows), else the GEMV (one pass over the weights per row, each pass at
+// the HBM rate). The batched path computes the RMSNorm factors and the layer-0 embedding in their
+// own small kernels; its logits skip the per-workgroup argmax partials (argmax_rows follows).
+static bool batched(const bw_model* m, const Mat& w, int M) {
+  return m->gemm_min_rows > 0 && M >= m->gemm_min_rows && gemm_supported(w.N, w.K);
+}
+
+static int run_dense(bw_model* m, int in_mode, int epi, GemvParams p, int M, hipStream_t s, int* grid_out = nullptr) {
+  if (!batched(m, p.w, M)) return launch_gemv(in_mode, epi, p, M, s, grid_out);
+  if (in_mode == IN_RMSNORM) {
+    if (p.embed) {
+      if (launch_embed(p.embed, p.vocab, p.w.K, p.tokens, M, p.x_out, p.err, s)) return -1;
+      p.embed = nullptr;
+    }
+    if (launch_rowrms(p.x, p.x_stride, p.w.K, p.eps, M, m->rms, s)) return -1;
+  }
+  return launch_gemm(in_mode, epi, p, M, m->rms, m->gemm_part, s);
+}
+
 // enqueue every kernel of one step on stream s (arguments already validated)
 static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, const int32_t* seq_lens,
                         const int32_t* page_table, int32_t batch, int32_t t, int32_t max_pages,
@@ -718,7 +756,7 @@ static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, co
       g.x_out = m->x;
     }
     trace_mark(m, BW_K_QKV, l, 0, s);
-    if (launch_gemv(IN_RMSNORM, EPI_QKV, g, M, s)) return fail(BW_EHIP, "qkv launch failed (layer %d)", l);
+    if (run_dense(m, IN_RMSNORM, EPI_QKV, g, M, s)) return fail(BW_EHIP, "qkv launch failed (layer %d)", l);
     trace_mark(m, BW_K_QKV, l, 1, s);
     // attention
     AttnParams a = attn_params(m, pool, l, m->q, seq_lens, page_table, t, max_pages, m->attn_out);
@@ -734,7 +772,7 @@ static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, co
     o.y = m->x;
     o.y_stride = d;
     trace_mark(m, BW_K_O, l, 0, s);
-    if (launch_gemv(IN_PLAIN, EPI_RESID, o, M, s)) return fail(BW_EHIP, "o launch failed (layer %d)", l);
+    if (run_dense(m, IN_PLAIN, EPI_RESID, o, M, s)) return fail(BW_EHIP, "o launch failed (layer %d)", l);
     trace_mark(m, BW_K_O, l, 1, s);
     if (!is_moe(c)) {
       GemvParams gu;
@@ -747,7 +785,7 @@ static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, co
       gu.y = m->act;
       gu.y_stride = m->act_width;
       trace_mark(m, BW_K_GATE_UP, l, 0, s);
-      if (launch_gemv(IN_RMSNORM, EPI_SWIGLU, gu, M, s)) return fail(BW_EHIP, "gate/up launch failed (layer %d)", l);
+      if (run_dense(m, IN_RMSNORM, EPI_SWIGLU, gu, M, s)) return fail(BW_EHIP, "gate/up launch failed (layer %d)", l);
       trace_mark(m, BW_K_GATE_UP, l, 1, s);
       GemvParams dn;
       dn.w = Ld.dn;
@@ -757,7 +795,7 @@ static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, co
       dn.y = m->x;
       dn.y_stride = d;
       trace_mark(m, BW_K_DOWN, l, 0, s);
-      if (launch_gemv(IN_PLAIN, EPI_RESID, dn, M, s)) return fail(BW_EHIP, "down launch failed (layer %d)", l);
+      if (run_dense(m, IN_PLAIN, EPI_RESID, dn, M, s)) return fail(BW_EHIP, "down launch failed (layer %d)", l);
       trace_mark(m, BW_K_DOWN, l, 1, s);
     } else {
       int32_t* sel = m->sel + (int64_t)l * c.max_tokens * c.top_k;
@@ -816,8 +854,13 @@ static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, co
   lm.amax_idx = m->amax_idx;
   int lm_grid = 0;
   trace_mark(m, BW_K_LM_HEAD, 0, 0, s);
-  if (launch_gemv(IN_RMSNORM, EPI_LOGITS, lm, M, s, &lm_grid)) return fail(BW_EHIP, "lm_head launch failed");
+  if (run_dense(m, IN_RMSNORM, EPI_LOGITS, lm, M, s, &lm_grid)) return fail(BW_EHIP, "lm_head launch failed");
   trace_mark(m, BW_K_LM_HEAD, 0, 1, s);
+  if (batched(m, lm.w, M)) {
+    if (argmax_out && launch_argmax_rows(lm.y, lm.y_stride, c.vocab, M, argmax_out, s))
+      return fail(BW_EHIP, "argmax launch failed");
+    return BW_OK;
+  }
   if (lm_grid > m->lm_parts) return fail(BW_EHIP, "lm_head grid exceeds the argmax workspace");
   if (argmax_out && launch_argmax_final(m->amax_val, m->amax_idx, lm_grid, M, argmax_out, s))
     return fail(BW_EHIP, "argmax launch failed");
@@ -877,6 +920,13 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
 extern "C" int bw_set_graphs(bw_model* m, int32_t enable) {
   if (!m) return fail(BW_EINVAL, "null model");
   m->use_graphs = enable != 0;
+  return BW_OK;
+}
+
+extern "C" int bw_set_gemm_min_rows(bw_model* m, int32_t min_rows) {
+  if (!m) return fail(BW_EINVAL, "null model");
+  if (min_rows < 0) return fail(BW_EINVAL, "min_rows must be >= 0");
+  m->gemm_min_rows = min_rows;
   return BW_OK;
 }
 
@@ -975,7 +1025,7 @@ extern "C" int bw_debug_matvec(bw_model* m, int32_t which, int32_t layer, int32_
   g.map_n = n;
   g.y = y;
   g.y_stride = n;
-  if (launch_gemv(IN_PLAIN, EPI_STORE_CANON, g, n_vec, (hipStream_t)stream)) return fail(BW_EHIP, "gemv launch failed");
+  if (run_dense(m, IN_PLAIN, EPI_STORE_CANON, g, n_vec, (hipStream_t)stream)) return fail(BW_EHIP, "matrix product launch failed");
   return BW_OK;
 }
 

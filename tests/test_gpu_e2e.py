@@ -32,9 +32,11 @@ def _cuda_i32(v):
 class Pair:
     """GPU session + oracle for one sequence, stepping both on the same tokens."""
 
-    def __init__(self, cfg, seed, max_len, ctx0=0, synth_seed=None):
+    def __init__(self, cfg, seed, max_len, ctx0=0, synth_seed=None, gemm_min_rows=None):
         self.cfg = cfg
         self.s = Session(cfg, seed=seed, max_len=[max_len], max_tokens=4, pool_seed=seed + 100)
+        if gemm_min_rows is not None:
+            bw.bw_set_gemm_min_rows(self.s.model, gemm_min_rows)
         self.om = oracle.Model(oracle_cfg(cfg), seed)
         self.okv = oracle.KV(self.om, 1, max_len - ctx0 + 1)
         if ctx0:
@@ -75,12 +77,15 @@ def _compare(g, gam, o, where):
     return err
 
 
-@pytest.mark.parametrize("cfg,seed", [(configs.TINY, 1001), (MOE_SMALL, 1011)], ids=["tiny", "moe-small"])
-def test_prompt_then_greedy_decode(cfg, seed):
+@pytest.mark.parametrize("cfg,seed,gemm", [(configs.TINY, 1001, None), (MOE_SMALL, 1011, None), (configs.TINY, 1002, 1),
+                                           (MOE_SMALL, 1012, 1)],
+                         ids=["tiny", "moe-small", "tiny-gemm", "moe-small-gemm"])
+def test_prompt_then_greedy_decode(cfg, seed, gemm):
+    """gemm = 1 runs every dense matrix of every step on the matrix-core GEMM path."""
     prompt_len, steps = cfg.get("prompt", 16), cfg.get("steps", 32)
     rng = np.random.default_rng(seed)
     prompt = rng.integers(0, cfg["vocab"], prompt_len)
-    p = Pair(cfg, seed, prompt_len + steps + 1)
+    p = Pair(cfg, seed, prompt_len + steps + 1, gemm_min_rows=gemm)
     worst = 0.0
     try:
         for i, tok in enumerate(prompt):
@@ -96,14 +101,15 @@ def test_prompt_then_greedy_decode(cfg, seed):
         p.close()
 
 
-def test_verify_step_equals_sequential_greedy():
+@pytest.mark.parametrize("gemm", [None, 1], ids=["gemv", "gemm"])
+def test_verify_step_equals_sequential_greedy(gemm):
     """Four tokens verified in one call (the accepted token plus three drafts equal to the greedy
     continuation) give the same per-position argmax as four single-token steps."""
     cfg, seed = configs.TINY, 1021
     rng = np.random.default_rng(seed)
     prompt = rng.integers(0, cfg["vocab"], 12)
     seq = Pair(cfg, seed, 40)
-    ver = Pair(cfg, seed, 40)
+    ver = Pair(cfg, seed, 40, gemm_min_rows=gemm)
     try:
         for tok in prompt[:-1]:
             seq.step([int(tok)])
@@ -142,3 +148,42 @@ def test_dense_9b_synthesized_context():
         print(f"[result] dense-9b max |logit diff| = {worst:.3e}")
     finally:
         p.close()
+
+
+# the verify workload's layer shape (9B dimensions), two layers and a small vocabulary so that
+# the oracle checks every row of the batch
+VERIFY_SMALL = dict(configs.VERIFY_9B, n_layers=2, vocab=4096, name="verify-9b-2l")
+
+
+@pytest.mark.timeout(600)
+def test_batched_verify_ragged_contexts():
+    """Speculative verify over a ragged batch: 8 sequences with synthesised contexts of different
+    lengths (U[40, 1200], ragged final pages), 4 tokens each, one step (32 rows on the matrix-core
+    GEMM path). Every row against the oracle, which decodes each sequence on its own."""
+    cfg, seed = VERIFY_SMALL, 1031
+    B, t = 8, 4
+    rng = np.random.default_rng(seed)
+    lens = [int(v) for v in rng.integers(40, 1201, B)]
+    lens[0], lens[1] = 47, 1200  # a one-token-short page and a page-aligned context
+    s = Session(cfg, seed=seed, max_len=[n + t for n in lens], max_tokens=B * t, pool_seed=seed + 1)
+    om = oracle.Model(oracle_cfg(cfg), seed)
+    okv = oracle.KV(om, B, t + 1)
+    try:
+        s.poison()
+        s.synthesize(seed + 7, lens)
+        for b in range(B):
+            okv.set_synth(b, seed + 7, b, lens[b])
+        toks = rng.integers(0, cfg["vocab"], B * t).astype(np.int32)
+        print(f"[case] verify batch {B} x t {t}, contexts {lens}", flush=True)
+        logits, am = s.step(torch.from_numpy(toks).cuda(), _cuda_i32(lens), t=t)
+        g = logits.cpu().numpy().astype(np.float64)
+        gam = am.cpu().numpy()
+        worst = 0.0
+        for b in range(B):
+            r = oracle.forward(om, okv, b, [int(v) for v in toks[b * t:(b + 1) * t]], lens[b])
+            worst = max(worst, _compare(g[b * t:(b + 1) * t], gam[b * t:(b + 1) * t], r["logits"], f"seq {b}"))
+        print(f"[result] verify batch max |logit diff| = {worst:.3e}")
+    finally:
+        okv.close()
+        om.close()
+        s.close()

@@ -93,6 +93,61 @@ def test_gemv_matches_oracle(cfg, seed):
         bw.bw_model_free(m)
 
 
+@pytest.mark.parametrize("cfg,seed", [(TINY, 31), (LAYER9B, 32), (LAYER27B, 34), (MOE_SMALL, 33)],
+                         ids=["tiny", "9b-layer", "27b-layer", "moe"])
+def test_batched_gemm_matches_oracle(cfg, seed):
+    """The matrix-core GEMM of the batched step (forced for every row count) against the fp64
+    product of the oracle's dequantised matrix, at row counts that leave a ragged m-tile (5, 37),
+    fill one workgroup's 128 rows, and spill into a second row group (131)."""
+    m = _model(cfg, seed, max_tokens=136)
+    bw.bw_set_gemm_min_rows(m, 1)
+    om = oracle.Model(oracle_cfg(cfg), seed)
+    rng = np.random.default_rng(seed)
+    try:
+        for name in _matrices(cfg):
+            expert = 3 if (cfg.get("n_experts", 0) and name in ("gate", "up", "down")) else 0
+            codes, scales = _canonical(om, name, expert)
+            N, K = codes.shape[0], codes.shape[1] * 2
+            W = oracle.dequant(codes, scales)
+            for M in (1, 5, 37, 128, 131):
+                print(f"[case] gemm {name} [{N}x{K}] rows={M}", flush=True)
+                x = rng.standard_normal((M, K)).astype(np.float32)
+                y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+                bw.bw_debug_matvec(m, name, 0, expert, torch.from_numpy(x).cuda(), y)
+                torch.cuda.synchronize()
+                ref = x.astype(np.float64) @ W.T
+                got = y.cpu().numpy()
+                assert np.all(np.isfinite(got)), (name, M)
+                for r in range(M):
+                    err = rel_l2(got[r], ref[r])
+                    assert err <= 1e-5, (name, M, r, err)  # exact products, fp32 sums
+    finally:
+        bw.bw_model_free(m)
+
+
+def test_batched_gemm_threshold_and_gemv_agree():
+    """The same rows through the GEMV (threshold off) and the GEMM agree to fp32 summation order."""
+    cfg, seed = LAYER9B, 35
+    m = _model(cfg, seed, max_tokens=16)
+    rng = np.random.default_rng(seed)
+    try:
+        for name in ("qkv", "down"):
+            N = {"qkv": (cfg["n_q_heads"] + 2 * cfg["n_kv_heads"]) * cfg["head_dim"], "down": cfg["d_model"]}[name]
+            K = {"qkv": cfg["d_model"], "down": cfg["ffn_dim"]}[name]
+            x = torch.from_numpy(rng.standard_normal((16, K)).astype(np.float32)).cuda()
+            outs = []
+            for rows in (0, 1):
+                bw.bw_set_gemm_min_rows(m, rows)
+                y = torch.empty((16, N), dtype=torch.float32, device="cuda")
+                bw.bw_debug_matvec(m, name, 0, 0, x, y)
+                torch.cuda.synchronize()
+                outs.append(y.cpu().numpy().astype(np.float64))
+            for r in range(16):
+                assert rel_l2(outs[1][r], outs[0][r]) <= 1e-5, (name, r)
+    finally:
+        bw.bw_model_free(m)
+
+
 def _attention_case(cfg, seed, lens, t, pool_seed, poison=False):
     """Synthesised contexts, random rotated queries; returns (gpu out, session)."""
     H, G, D = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
