@@ -197,7 +197,7 @@ def main() -> int:
             with open(tr_path) as f:
                 tr = json.load(f)
             from memory_bound_autoregressive_amd.build import source_digest
-            if tr.get("kernel_source_digest") == source_digest():
+            if tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ()))):
                 traffic = tr.get("hbm_bytes_per_launch")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,

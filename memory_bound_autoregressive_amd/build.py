@@ -37,10 +37,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def source_digest() -> str:
-    """Digest of the HIP sources (a recorded counter profile is valid only for this digest)."""
+def source_digest(files: tuple[str, ...] | None = None) -> str:
+    """Digest of HIP sources (a recorded counter profile is valid only for this digest): the named
+    files of csrc/ (a kernel's own source and the headers it includes), else all of them."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+    paths = [os.path.join(CSRC, f) for f in files] if files else \
+        glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
+    for f in sorted(paths):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())

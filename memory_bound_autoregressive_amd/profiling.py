@@ -1,0 +1,126 @@
+"""Summaries of rocprofv3 CSV output for the decode-step kernels.
+
+  python -m memory_bound_autoregressive_amd.profiling stats    <kernel_stats.csv> <out.md> --command "..."
+  python -m memory_bound_autoregressive_amd.profiling counters <counter_collection.csv> <out.md> --command "..."
+  python -m memory_bound_autoregressive_amd.profiling traffic  --fetch F.csv --write W.csv \
+        --cal-fetch CF.csv --cal-write CW.csv --copy-bytes B --kernel SUBSTR --out traffic.json
+
+`traffic` turns the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of one kernel into HBM
+bytes per launch. Each counter is scaled by the factor that makes it read right on a plain device
+copy of known size (the copy reads B bytes and writes B bytes), measured in the same way on the
+same machine. The result records the digest of the kernel sources it was measured on, so a
+later change to the kernels invalidates it.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import json
+import sys
+
+
+def _rows(path: str):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def stats_table(path: str, top: int = 16) -> str:
+    rows = _rows(path)
+    out = ["| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} % |")
+    return "\n".join(out)
+
+
+def counter_means(path: str) -> dict:
+    """{kernel name: {counter: (dispatches, mean value per dispatch)}}"""
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _rows(path):
+        agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: (len(v), sum(v) / len(v)) for c, v in d.items()} for k, d in agg.items()}
+
+
+def counters_table(path: str) -> str:
+    out = ["| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+    for k, d in sorted(counter_means(path).items(), key=lambda kv: kv[0]):
+        for c, (n, mean) in d.items():
+            out.append(f"| `{k[:90]}` | {c} | {n} | {mean:.1f} |")
+    return "\n".join(out)
+
+
+def _one(path: str, kernel: str, counter: str) -> float:
+    hits = [(n, m) for k, d in counter_means(path).items() if kernel in k for c, (n, m) in d.items() if c == counter]
+    if not hits:
+        raise SystemExit(f"no {counter} rows for a kernel matching {kernel!r} in {path}")
+    tot = sum(n for n, _ in hits)
+    return sum(n * m for n, m in hits) / tot
+
+
+# sources of the GEMV kernels (the dominant kernel of the batch-1 step)
+GEMV_SOURCES = ("bw_gemv.hip", "bw_common.h", "bw_internal.h")
+
+
+def _copy(path: str, kernel: str, counter: str) -> float:
+    """Mean counter value of the large dispatches of the copy kernel (other, small uses of the
+    same kernel in the calibration run, such as argument uploads, are left out)."""
+    vals = [float(r["Counter_Value"]) for r in _rows(path) if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel!r} in {path}")
+    big = [v for v in vals if v >= 0.5 * max(vals)]
+    return sum(big) / len(big)
+
+
+def traffic(fetch: str, write: str, cal_fetch: str, cal_write: str, copy_bytes: int, kernel: str,
+            copy_kernel: str = "copyBuffer", sources: tuple[str, ...] = GEMV_SOURCES) -> dict:
+    from .build import source_digest
+    kib = 1024.0
+    cf = _copy(cal_fetch, copy_kernel, "FETCH_SIZE") * kib
+    cw = _copy(cal_write, copy_kernel, "WRITE_SIZE") * kib
+    f_scale, w_scale = copy_bytes / cf, copy_bytes / cw
+    kf = _one(fetch, kernel, "FETCH_SIZE") * kib
+    kw = _one(write, kernel, "WRITE_SIZE") * kib
+    return {"kernel": kernel, "fetch_kib_per_dispatch": kf / kib, "write_kib_per_dispatch": kw / kib,
+            "copy_bytes": copy_bytes, "copy_fetch_kib": cf / kib, "copy_write_kib": cw / kib,
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "hbm_bytes_per_launch": kf * f_scale + kw * w_scale, "kernel_sources": list(sources),
+            "kernel_source_digest": source_digest(sources)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="rocprofv3 kernel statistics")
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("out")
+    c.add_argument("--command", required=True)
+    c.add_argument("--title", default="rocprofv3 counters")
+    t = sub.add_parser("traffic")
+    for a in ("--fetch", "--write", "--cal-fetch", "--cal-write", "--kernel", "--out"):
+        t.add_argument(a, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        text = f"# {a.title}\n\nCommand:\n\n```\n{a.command}\n```\n\n{stats_table(a.csv)}\n"
+    elif a.cmd == "counters":
+        text = f"# {a.title}\n\nCommand:\n\n```\n{a.command}\n```\n\n{counters_table(a.csv)}\n"
+    else:
+        res = traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.copy_bytes, a.kernel)
+        with open(a.out, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return 0
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
