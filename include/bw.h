@@ -53,6 +53,9 @@ extern "C" {
 /* device error bits (bw_check_device_error) */
 #define BW_DERR_PAGE 1   /* a page-table entry was outside [0, n_pages) */
 #define BW_DERR_TOKEN 2  /* a token id was outside [0, vocab) */
+#define BW_DERR_POS 4    /* a position seq_lens[b] + i was outside [0, max_positions) */
+#define BW_DERR_PERSIST 8 /* the single-launch step gave up waiting (its deadline passed); later
+                           * single-launch steps return at once until bw_check_device_error */
 
 typedef struct bw_model bw_model;
 typedef struct bw_kv_pool bw_kv_pool;
@@ -146,6 +149,17 @@ int bw_decode_step(bw_model* model, bw_kv_pool* pool, const int32_t* tokens_dev,
 /* Turn step capture on (default) or off (every call then launches its kernels directly). */
 int bw_set_graphs(bw_model* model, int32_t enable);
 
+/* Batch-1 decode steps (batch = 1, t = 1) of a dense model run as ONE cooperative kernel launch
+ * when this is on (default) and the model's shape has a single-launch form: every layer's
+ * phases (QKV + RoPE + KV append, attention, merge, O, gate/up, down) and the lm_head run in one
+ * resident workgroup per CU that hand their small output vectors to each other through device
+ * memory, so the weight stream is not broken by kernel boundaries (bw24 vs llama.cpp page,
+ * section 2.2: launches and intermediate round trips are what fusion removes). Results match
+ * the kernel chain to fp32 rounding (exchanged activations keep 21 mantissa bits). Other steps,
+ * MoE models and traced steps use the kernel chain. *available_out (may be NULL) receives 1 when
+ * the model has the single-launch form, else 0. Errors: BW_EINVAL (null model). */
+int bw_set_single_launch(bw_model* model, int32_t enable, int32_t* available_out);
+
 /* Row count from which a step (and bw_debug_matvec) runs its dense matrices -- QKV, O, gate/up,
  * down, lm_head -- as one int4 GEMM on the matrix cores over all batch * t rows, reading each
  * weight once (bw24 deep-dive page, section 5, stage 4: the drafted tokens of a verify step are
@@ -200,6 +214,19 @@ int bw_debug_read_experts(bw_model* model, int32_t n_rows, int32_t* host_dst, vo
 /* Residual stream after the last layer of the last bw_decode_step: float [batch * t][d_model],
  * copied to host. Synchronises `stream`. */
 int bw_debug_read_hidden(bw_model* model, int32_t n_rows, float* host_dst, void* stream);
+
+/* Timeout of each wait inside the single-launch step, in ticks of the GPU's 100 MHz real-time
+ * counter (default 50,000,000 = 0.5 s). A wait that passes it raises BW_DERR_PERSIST and ends the
+ * step on every workgroup; tests use a tiny value to exercise that path.
+ * Errors: BW_EINVAL (null model), BW_ESTATE (no single-launch form). */
+int bw_debug_single_launch_deadline(bw_model* model, uint64_t ticks);
+
+/* Measurement hook of the single-launch step: while stamps_dev (device, n >= 8 * n_layers + 8
+ * uint64) is set, workgroup 0 writes the GPU's 100 MHz real-time counter at the start of each
+ * phase: [8 l + 0..5] = QKV, attention, merge, O, gate/up, down of layer l; [8 L + 0] = lm_head,
+ * [8 L + 1] = final argmax, [8 L + 2] = step end, [8 L + 3] = step start. NULL turns it off.
+ * Errors: BW_EINVAL, BW_ESTATE (no single-launch form), BW_ERANGE (n too small). */
+int bw_debug_single_launch_stamps(bw_model* model, uint64_t* stamps_dev, int32_t n);
 
 /* ---- measurement hook ------------------------------------------------------------------- */
 

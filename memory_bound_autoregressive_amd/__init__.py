@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libbw.so")
 
 BW_OK, BW_EINVAL, BW_ENOMEM, BW_EHIP, BW_ERANGE, BW_ESTATE = 0, -1, -2, -3, -4, -5
 BW_KV_F16, BW_KV_BF16 = 1, 2
-BW_DERR_PAGE, BW_DERR_TOKEN = 1, 2
+BW_DERR_PAGE, BW_DERR_TOKEN, BW_DERR_POS, BW_DERR_PERSIST = 1, 2, 4, 8
 MAT = {"qkv": 0, "o": 1, "gate": 2, "up": 3, "down": 4, "lm_head": 5,
        "shared_gate": 6, "shared_up": 7, "shared_down": 8}
 
@@ -26,7 +26,8 @@ EXPORTS = (
     "bw_kv_pool_fill", "bw_kv_pool_synthesize", "bw_kv_pool_read", "bw_decode_step",
     "bw_last_error", "bw_check_device_error", "bw_debug_dequant", "bw_debug_matvec",
     "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden", "bw_set_trace", "bw_set_graphs",
-    "bw_set_gemm_min_rows",
+    "bw_set_gemm_min_rows", "bw_set_single_launch", "bw_debug_single_launch_deadline",
+    "bw_debug_single_launch_stamps",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.bw_set_trace.argtypes = [vp, i32, vp, i32]
         L.bw_set_graphs.argtypes = [vp, i32]
         L.bw_set_gemm_min_rows.argtypes = [vp, i32]
+        L.bw_set_single_launch.argtypes = [vp, i32, ctypes.POINTER(i32)]
+        L.bw_debug_single_launch_deadline.argtypes = [vp, u64]
+        L.bw_debug_single_launch_stamps.argtypes = [vp, vp, i32]
         _lib = L
     return _lib
 
@@ -205,6 +209,24 @@ def bw_set_trace(model: int, kernel_class: str, events, n_layers: int) -> None:
 
 def bw_set_graphs(model: int, enable: bool) -> None:
     _check(lib().bw_set_graphs(model, int(bool(enable))), "bw_set_graphs")
+
+
+def bw_set_single_launch(model: int, enable: bool) -> bool:
+    """Switch batch-1 steps between one cooperative launch and the kernel chain; returns whether
+    the model has the single-launch form."""
+    avail = ctypes.c_int32(0)
+    _check(lib().bw_set_single_launch(model, int(bool(enable)), ctypes.byref(avail)), "bw_set_single_launch")
+    return bool(avail.value)
+
+
+def bw_debug_single_launch_deadline(model: int, ticks: int) -> None:
+    _check(lib().bw_debug_single_launch_deadline(model, int(ticks)), "bw_debug_single_launch_deadline")
+
+
+def bw_debug_single_launch_stamps(model: int, stamps, n: int = 0) -> None:
+    """stamps: a device int64 tensor of n >= 8 * n_layers + 8 entries, or None to stop."""
+    _check(lib().bw_debug_single_launch_stamps(model, _ptr(stamps) if stamps is not None else None, int(n)),
+           "bw_debug_single_launch_stamps")
 
 
 def bw_set_gemm_min_rows(model: int, min_rows: int) -> None:

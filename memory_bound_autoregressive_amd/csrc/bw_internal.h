@@ -103,6 +103,48 @@ struct AttnParams {
   int32_t* counters = nullptr;      // [batch][G] split arrival counters, zero between launches
 };
 
+// The single-launch batch-1 step of a dense model (bw_persist.hip).
+struct PLayer {
+  Mat qkv, o, gu, dn;
+  const uint16_t* attn_norm = nullptr;
+  const uint16_t* ffn_norm = nullptr;
+};
+
+constexpr int BW_DERR_PERSIST_BIT = 8;
+
+struct PersistParams {
+  const PLayer* layers = nullptr;   // device array [L]
+  int32_t L = 0, H = 0, G = 0, V = 0;
+  Mat lm;
+  const uint16_t* final_norm = nullptr;
+  const uint16_t* embed = nullptr;
+  float eps = 1e-6f, attn_scale = 0.f;
+  const float2* rope = nullptr;
+  int32_t max_pos = 0;
+  uint16_t* pool = nullptr;         // [L][n_pages][G][2][16][D]
+  int64_t layer_elems = 0, page_elems = 0;
+  int32_t n_pages = 0;
+  const int32_t* tokens = nullptr;  // [1]
+  const int32_t* seq_lens = nullptr;// [1]
+  const int32_t* page_table = nullptr;
+  int32_t max_pages = 0;
+  // exchange words (value with a 2-bit epoch tag in the low mantissa bits)
+  uint32_t* xq = nullptr;           // [(H + 2G) D]: rotated q, rounded k and v (canonical dims)
+  uint32_t* xp = nullptr;           // [H][splits][D + 2]: attention partials (acc, m, l)
+  uint32_t* xa = nullptr;           // [H D]: attention output
+  uint32_t* xm = nullptr;           // [d]: residual after attention
+  uint32_t* xf = nullptr;           // [F]: SwiGLU output
+  uint32_t* xx = nullptr;           // [d]: residual after the FFN (layer input)
+  uint64_t* xarg = nullptr;         // [workgroups]: argmax partial (value, index | tag << 30)
+  float* logits = nullptr;          // [V] or null
+  int32_t* argmax = nullptr;        // [1] or null
+  uint32_t* epoch = nullptr;        // [1] steps run so far (tags derive from it)
+  int32_t* err = nullptr;
+  uint32_t* abort_flag = nullptr;
+  uint64_t deadline_ticks = 50000000ull;  // one wait gives up after 0.5 s (100 MHz counter)
+  uint64_t* stamps = nullptr;       // optional [L * 8 + 8]: real-time counter at each phase start (workgroup 0)
+};
+
 // launchers (bw_gemv.hip, bw_attn.hip, bw_misc.hip)
 int launch_gemv(int in_mode, int epi, const GemvParams& p, int M, hipStream_t s, int* grid_out = nullptr);
 int gemv_lane_split(int K, int* lpr, int* nb);
@@ -127,5 +169,11 @@ int64_t gemm_part_elems(int N, int K, int M);
 int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* rms, float* part, hipStream_t s);
 int launch_rowrms(const float* x, int64_t stride, int K, float eps, int M, float* r, hipStream_t s);
 int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, int32_t* out, hipStream_t s);
+
+// single-launch step (bw_persist.hip): -2 when (d, F, head dim, query heads per KV head) has no
+// instantiation; query_only checks that one workgroup of it fits a CU
+int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
+                   bool query_only);
+int launch_persist_reset(const PersistParams& p, int n_q, int n_p, int n_a, int n_d, int n_f, int n_arg, hipStream_t s);
 
 }  // namespace bw

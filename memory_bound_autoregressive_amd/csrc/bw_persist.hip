@@ -1,0 +1,1017 @@
+// bw_persist.hip - the whole batch-1 decode step of a dense model as one persistent kernel.
+//
+// Why: a batch-1 step is a chain of ~6 matrix passes per layer, each moving 10-60 MB. As separate
+// kernels every pass pays a launch gap, a ramp of its first loads and a tail, ~5 us, against
+// 1.3-8 us of streaming. The pages attribute the same loss to kernel launches and intermediate
+// round trips and answer it by fusion (bw24 vs llama.cpp page, section 2.2). Here one workgroup
+// per CU stays resident for the whole step; the phases of a layer hand their (small) output
+// vectors to each other through device memory, and each workgroup issues its next weight loads
+// before it waits for the next input, so weight streaming continues across phase boundaries.
+//
+// Exchange. Each phase output element is one 32-bit word: the fp32 value with its two lowest
+// mantissa bits replaced by an epoch tag (a relative change below 2^-21). Producers store words
+// with agent-scope relaxed atomic stores (written through the XCD-local L2); consumers read them
+// with 16-byte loads that are coherent across the XCD L2s (sc1) and re-read every word whose tag
+// is not the one they wait for. A word is written once per layer, and consecutive writes of a
+// word carry different tags (mod 4), so a consumer can neither take a stale word nor wait on a
+// word that was already overwritten (every phase needs all of its predecessor's output, so no
+// workgroup is more than one phase ahead of any other). No fences are used. The exact fp32
+// residual rows stay in the LDS of the workgroup that owns them; only their exchanged copies are
+// tagged. Keys and values are rounded to the cache dtype before exchange, which leaves their low
+// bits zero.
+//
+// Every wait is bounded: a deadline on the real-time counter, and a device abort flag that any
+// waiter raises and every waiter polls. An aborted step sets BW_DERR_PERSIST in the error word and
+// all workgroups return; the abort flag stays raised (later steps return at once) until the host
+// clears it (bw_check_device_error), which also re-tags the exchange buffers.
+//
+// Phases of layer l (tags T(l) = epoch * (L + 2) + l + 1; the embedding writes T(-1)):
+//   QKV   in x (RMSNorm)      rows (Hq + 2Hkv) D, RoPE + KV append      out xq
+//   ATTN  in xq (q, new k/v)  (KV head, split) over the paged cache     out xp (acc, m, l)
+//   MERGE in xp               H*D outputs                               out xa
+//   O     in xa               d rows, residual (row owner)              out xm
+//   GU    in xm (RMSNorm)     2F rows, SwiGLU pairs                     out xf
+//   DOWN  in xf               d rows, residual (row owner)              out xx
+// then LM (in xx, RMSNorm; logits + per-workgroup argmax) and ARGMAX (workgroup 0). Each buffer
+// above is written once per layer, so two consecutive writes of a word differ in tag by 1, 2
+// (xx across a step boundary) or 3 (the others across a step boundary). The argmax partials are
+// written once per step and carry the epoch itself (difference 1).
+#include <algorithm>
+
+#include "bw_common.h"
+#include "bw_dot.h"
+#include "bw_internal.h"
+
+namespace bw {
+
+constexpr int kPT = 512;           // threads per workgroup
+constexpr int kPW = kPT / kWave;   // waves per workgroup
+constexpr uint32_t kRsrc3 = 0x00020000u;
+constexpr int kCohSC1 = 16;        // cache policy: coherent across the XCD L2s
+constexpr float kNoScore = -1.0e30f;               // running max of a split without positions
+
+// ---- exchange words ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t xenc(float v, uint32_t tag) { return (__float_as_uint(v) & ~3u) | (tag & 3u); }
+__device__ __forceinline__ float xdec(uint32_t w) { return __uint_as_float(w & ~3u); }
+__device__ __forceinline__ bool xok(uint32_t w, uint32_t tag) { return ((w ^ tag) & 3u) == 0u; }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrc3);
+}
+__device__ __forceinline__ u32x4 xload4(__amdgpu_buffer_rsrc_t r, int idx4) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, idx4 * 16, 0, kCohSC1);
+}
+__device__ __forceinline__ uint32_t xload1(__amdgpu_buffer_rsrc_t r, int idx) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, kCohSC1);
+}
+__device__ __forceinline__ void xstore(uint32_t* base, int idx, float v, uint32_t tag) {
+  __hip_atomic_store(base + idx, xenc(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct Ctl {
+  uint32_t* abort_flag;
+  int32_t* err;
+  int* bail;         // LDS flag of this workgroup
+  uint64_t t0;       // real-time counter at the start of the current wait
+  uint64_t deadline; // ticks of the 100 MHz real-time counter one wait may take
+};
+
+// true when this wait must give up: the step was aborted elsewhere or the deadline passed
+__device__ __forceinline__ bool give_up(Ctl& c) {
+  if (*c.bail) return true;
+  if (__hip_atomic_load(c.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+      __builtin_amdgcn_s_memrealtime() - c.t0 > c.deadline) {
+    atomicOr(c.err, BW_DERR_PERSIST_BIT);
+    __hip_atomic_store(c.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *c.bail = 1;
+    return true;
+  }
+  return false;
+}
+
+// Wait until n words of buf (starting at word 0) all carry tag; this thread covers 16-byte chunks
+// tid, tid + kPT, ... (PER of them). n is a multiple of 4.
+template <int PER>
+__device__ __forceinline__ void poll_chunks(int tid, __amdgpu_buffer_rsrc_t r, int n4, uint32_t tag, u32x4 (&v)[PER],
+                                            Ctl& c) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = tid + i * kPT;
+    v[i] = q < n4 ? xload4(r, q) : u32x4{tag, tag, tag, tag};
+  }
+  c.t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) all &= xok(v[i][k], tag);
+    if (all || give_up(c)) return;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ok &= xok(v[i][k], tag);
+      const int q = tid + i * kPT;
+      if (!ok && q < n4) v[i] = xload4(r, q);
+    }
+  }
+}
+
+// Wait for up to N words (idx[i] < 0: unused); all loads are issued before the first check
+template <int N>
+__device__ __forceinline__ void poll_words(__amdgpu_buffer_rsrc_t r, const int (&idx)[N], uint32_t tag, uint32_t (&w)[N],
+                                           Ctl& c) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = idx[i] >= 0 ? xload1(r, idx[i]) : tag;
+  c.t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) all &= xok(w[i], tag);
+    if (all || give_up(c)) return;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!xok(w[i], tag) && idx[i] >= 0) w[i] = xload1(r, idx[i]);
+  }
+}
+
+// This thread's index, opaque to the compiler: every phase starts from a fresh copy, so the
+// per-thread address terms of a phase are formed inside it instead of being hoisted out of the
+// layer loop and held in registers for the whole step.
+__device__ __forceinline__ int phase_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
+__device__ __forceinline__ int wave_of(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
+
+// A small read-only struct as wave-uniform values: each 32-bit word goes through readfirstlane,
+// so pointers built from it (buffer descriptors) are known uniform and loads through them need no
+// per-lane loop.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* src) {
+  static_assert(sizeof(T) % 4 == 0, "word-sized struct");
+  T r;
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(src);
+  uint32_t* b = reinterpret_cast<uint32_t*>(&r);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) b[i] = __builtin_amdgcn_readfirstlane(a[i]);
+  return r;
+}
+
+// measurement hook: workgroup 0 records the real-time counter at a phase start
+__device__ __forceinline__ void stamp(const PersistParams& p, int idx) {
+  if (p.stamps != nullptr && blockIdx.x == 0 && threadIdx.x == 0) p.stamps[idx] = __builtin_amdgcn_s_memrealtime();
+}
+
+// ---- LDS layout ---------------------------------------------------------------------------------
+
+struct Lds {
+  float* xs;     // staged input vector [Kmax] (bank-swizzled blocks)
+  float* bs;     // block sums [Kmax / 32]
+  float* csum;   // chunk sums [Kmax / 4]
+  float* ydot;   // row dot products of the current phase [kMaxRows]
+  float* resid;  // exact residual rows owned by this workgroup [kMaxOwn]
+  float* red;    // reduction scratch [32]
+  float* mrg;    // merge scratch [kMrg]
+  float* att;    // attention scratch
+};
+constexpr int kMaxRows = 1024;  // rows per workgroup per phase held in ydot
+#ifndef BW_LM_RW
+#define BW_LM_RW 2
+#endif
+constexpr int kLmRW = BW_LM_RW;  // row steps per group of the lm_head pass
+constexpr int kMaxOwn = 64;     // residual rows per workgroup
+constexpr int kMaxSplit = kPT / 4;  // attention splits per KV head (workgroups / KV heads)
+constexpr int kMrgProd = 2048;      // (attention output, split) products per workgroup
+// merge scratch: (m, l) of [2 heads][splits], factors [2][splits], denominators [2], products
+constexpr int kMrg = 4 * kMaxSplit + 2 * kMaxSplit + 8 + kMrgProd;
+
+// ---- staging of a GEMV input from the exchange ------------------------------------------------
+// xs gets the K values (times the RMSNorm factor and gain when gamma != nullptr), bs the per-block
+// sums. The caller synchronises before and after.
+template <int K>
+__device__ __forceinline__ void stage_x(int tid, const uint32_t* xin, uint32_t tag, const uint16_t* gamma, float eps,
+                                        Lds& s, Ctl& c) {
+  constexpr int N4 = K / 4;
+  constexpr int PER = (N4 + kPT - 1) / kPT;
+  u32x4 v[PER];
+  poll_chunks<PER>(tid, xrsrc(xin, (int64_t)K * 4), N4, tag, v, c);
+  float scale = 1.f;
+  if (gamma != nullptr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (tid + i * kPT < N4)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ss = fmaf(xdec(v[i][k]), xdec(v[i][k]), ss);
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) s.red[wave_of(tid)] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPW; ++w) tot += s.red[w];
+    scale = 1.0f / sqrtf(tot / (float)K + eps);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = tid + i * kPT;
+    if (q >= N4) continue;
+    const int k = 4 * q;
+    float4 f = make_float4(xdec(v[i][0]), xdec(v[i][1]), xdec(v[i][2]), xdec(v[i][3]));
+    if (gamma != nullptr) {
+      const uint2 gh = *(const uint2*)(gamma + k);
+      f.x *= scale * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
+      f.y *= scale * f16_to_f32((uint16_t)(gh.x >> 16));
+      f.z *= scale * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
+      f.w *= scale * f16_to_f32((uint16_t)(gh.y >> 16));
+    }
+    *(float4*)xs_chunk(s.xs, k >> 5, (k & 31) >> 2) = f;
+    s.csum[q] = (f.x + f.y) + (f.z + f.w);
+  }
+  __syncthreads();
+  for (int b = tid; b < K / 32; b += kPT) {
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a += s.csum[b * 8 + k];
+    s.bs[b] = a;
+  }
+  __syncthreads();
+}
+
+// ---- GEMV over a row range --------------------------------------------------------------------
+// Rows [r0, r1) of w; wave v takes groups v, v + kPW, ... of RW row steps (64 / LPR rows each).
+template <int LPR, int NB, int RW>
+struct PGroup {
+  u32x4 q[RW][NB];
+  uint16_t sc[RW][NB];
+  int row[RW];
+};
+
+// Loads of one group, as buffer loads on the matrix: every load is issued unconditionally and rows
+// past r1 get an offset beyond the buffer, which returns zero without touching memory. With no load
+// under a branch (and none through a flat pointer, which would also count against the LDS wait
+// counter) the compiler's wait counts stay exact: computing a group waits for that group's loads
+// only, while the next group's are in flight.
+constexpr int kOOB = 0x7FFFFFF0;  // byte offset past every matrix
+constexpr int kNT = 2;            // cache policy: non-temporal (each weight is read once per step)
+
+template <int LPR, int NB, int RW>
+__device__ __forceinline__ void pload(int tid, const Mat w, int r0, int r1, int gi, PGroup<LPR, NB, RW>& g) {
+  constexpr int RPW = kWave / LPR;
+  const int lane = tid & 63, j = lane % LPR, rsub = lane / LPR;
+  constexpr int nblk = LPR * NB;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)w.codes, 0, w.N * (nblk * 16), kRsrc3);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc((void*)w.scales, 0, w.N * (nblk * 2), kRsrc3);
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = r0 + (gi * RW + r) * RPW + rsub;
+    g.row[r] = row;
+    const bool ok = row < r1;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      g.q[r][c] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? row * (nblk * 16) + (j + LPR * c) * 16 : kOOB, 0, kNT);
+      g.sc[r][c] = __builtin_amdgcn_raw_buffer_load_b16(rsc, ok ? (row * nblk + j * NB + c) * 2 : kOOB, 0, 0);
+    }
+  }
+}
+
+template <int LPR, int NB, int RW>
+__device__ __forceinline__ void pcompute(int tid, const PGroup<LPR, NB, RW>& g, int r0, int r1, const Lds& s) {
+  const int lane = tid & 63, j = lane % LPR;
+  float acc[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int b = j + LPR * c;
+    float4 xb[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xb[k] = *(const float4*)xs_chunk(s.xs, b, k);
+    const float sb = s.bs[b];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[r] = fmaf(f16_to_f32(g.sc[r][c]), block_dot(g.q[r][c], xb, sb), acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) acc[r] += __shfl_xor(acc[r], o);
+    if (j == 0 && g.row[r] < r1) s.ydot[g.row[r] - r0] = acc[r];
+  }
+}
+
+// first group of this wave (issued before the input is waited for)
+template <int LPR, int NB, int RW>
+__device__ __forceinline__ void gemv_first(int tid, const Mat w, int r0, int r1, PGroup<LPR, NB, RW>& g) {
+  pload<LPR, NB, RW>(tid, w, r0, r1, wave_of(tid), g);
+}
+
+// The rest of the rows; ydot is complete after the caller's __syncthreads. The A/B groups
+// alternate so that the next group's loads are in flight while the current one is computed.
+template <int LPR, int NB, int RW>
+__device__ __forceinline__ void gemv_rest(int tid, const Mat w, int r0, int r1, PGroup<LPR, NB, RW>& cur, const Lds& s) {
+  constexpr int GROUP = (kWave / LPR) * RW;
+  const int n_groups = (r1 - r0 + GROUP - 1) / GROUP;
+  int gi = wave_of(tid);
+  if (gi >= n_groups) return;
+  PGroup<LPR, NB, RW> alt;
+  while (true) {
+    pload<LPR, NB, RW>(tid, w, r0, r1, gi + kPW, alt);
+    pcompute<LPR, NB, RW>(tid, cur, r0, r1, s);
+    gi += kPW;
+    if (gi >= n_groups) break;
+    pload<LPR, NB, RW>(tid, w, r0, r1, gi + kPW, cur);
+    pcompute<LPR, NB, RW>(tid, alt, r0, r1, s);
+    gi += kPW;
+    if (gi >= n_groups) break;
+  }
+}
+
+// ---- attention over the paged cache -----------------------------------------------------------
+
+template <int KVDT>
+__device__ __forceinline__ void unpack8p(u32x4 v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = kv_to_f32<KVDT>((uint16_t)(v[i] & 0xFFFFu));
+    out[2 * i + 1] = kv_to_f32<KVDT>((uint16_t)(v[i] >> 16));
+  }
+}
+
+// 16-byte chunk of the new token's key or value (cache dtype bits staged in LDS)
+__device__ __forceinline__ u32x4 lds_chunk16(const uint16_t* bits, int d0) {
+  return *(const u32x4*)(bits + d0);
+}
+
+// ---- parameters -------------------------------------------------------------------------------
+
+template <int D, int QR>
+struct alignas(16) AttnLds {
+  float q[QR * D];
+  float p[kPW][QR][kPageTokens];
+  float m[kPW][QR], l[kPW][QR];
+  float acc[kPW][QR * D];
+  alignas(16) uint16_t knew[D];
+  alignas(16) uint16_t vnew[D];
+};
+
+// ---- the kernel -------------------------------------------------------------------------------
+
+// RWQ, RWO, RWG, RWF: row steps per wave group of the QKV, O, gate/up and down passes, chosen so
+// that one group covers a wave's whole share of the phase at the instantiated shape.
+template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF>
+__global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  constexpr int KD = LPR_D * NB_D * 32;  // d_model (= Hq * D)
+  constexpr int KF = LPR_F * NB_F * 32;  // ffn dim
+  constexpr int KMAX = KD > KF ? KD : KF;
+  __shared__ int bail;
+  Lds s;
+  s.xs = lds;
+  s.bs = s.xs + KMAX;
+  s.csum = s.bs + KMAX / 32;
+  s.ydot = s.csum + KMAX / 4;
+  s.resid = s.ydot + kMaxRows;
+  s.red = s.resid + kMaxOwn;
+  s.mrg = s.red + 32;
+  s.att = s.mrg + kMrg;
+  AttnLds<D, QR>& al = *reinterpret_cast<AttnLds<D, QR>*>(s.att);
+
+  const int nwg = gridDim.x, w = blockIdx.x;
+  if (threadIdx.x == 0) bail = 0;
+  Ctl ctl{p.abort_flag, p.err, &bail, 0, p.deadline_ticks};
+  __syncthreads();
+  // a previous step that aborted leaves the flag raised: nothing runs until the host clears it
+  if (__hip_atomic_load(p.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+    if (threadIdx.x == 0 && w == 0) atomicOr(p.err, BW_DERR_PERSIST_BIT);
+    return;
+  }
+
+  const int L = p.L, H = p.H, G = p.G;
+  stamp(p, L * 8 + 3);
+  const uint32_t epoch = p.epoch[0];
+  const uint32_t base_tag = epoch * (uint32_t)(L + 2);
+  const int pos = p.seq_lens[0];
+  const int kv_len = pos + 1;
+  const bool pos_ok = pos >= 0 && pos < p.max_pos && pos / kPageTokens < p.max_pages;
+  const int HD = H * D, GD = G * D;
+  const int Nq = HD + 2 * GD;
+
+  // row ownership: residual rows [w*Rd, ...), QKV / GU rows in even-aligned ranges
+  const int Rd = (KD + nwg - 1) / nwg;
+  const int d0 = min(w * Rd, KD), d1 = min(d0 + Rd, KD);
+  const int Rq = (((Nq + nwg - 1) / nwg) + 1) & ~1;
+  const int q0 = min(w * Rq, Nq), q1 = min(q0 + Rq, Nq);
+  const int Rg = (((2 * KF + nwg - 1) / nwg) + 1) & ~1;
+  const int g0 = min(w * Rg, 2 * KF), g1 = min(g0 + Rg, 2 * KF);
+  const int Rv = (p.V + nwg - 1) / nwg;
+  const int v0 = min(w * Rv, p.V), v1 = min(v0 + Rv, p.V);
+  const int Rm = (HD + nwg - 1) / nwg;
+  const int m0 = min(w * Rm, HD), m1 = min(m0 + Rm, HD);
+  const int S = nwg / G;  // attention splits per KV head
+  const int ag = w / S, as = w - ag * S;  // this workgroup's (KV head, split); ag >= G: idle
+
+  // ---- embedding: owned residual rows
+  {
+    const int tid = phase_tid();
+    const int lane = tid & 63, wave = wave_of(tid);
+    (void)lane;
+    (void)wave;
+    int tok = p.tokens[0];
+    if (tok < 0 || tok >= p.V) {
+      if (tid == 0 && w == 0) atomicOr(p.err, 2);
+      tok = 0;
+    }
+    const uint32_t tag = base_tag;  // T(-1)
+    for (int r = d0 + tid; r < d1; r += kPT) {
+      const float v = f16_to_f32(p.embed[(int64_t)tok * KD + r]);
+      s.resid[r - d0] = v;
+      xstore(p.xx, r, v, tag);
+    }
+  }
+  if (!pos_ok && threadIdx.x == 0 && w == 0) atomicOr(p.err, 4);
+
+  for (int l = 0; l < L; ++l) {
+    // this layer's descriptors, read once with scalar loads (the table is constant for the step),
+    // so the matrix pointers are uniform registers and the loops below never re-read them
+    const PLayer Ly = load_uniform(p.layers + l);
+    const uint32_t tin = base_tag + (uint32_t)l;       // T(l - 1)
+    const uint32_t tout = base_tag + (uint32_t)l + 1;  // T(l)
+    uint16_t* pool = p.pool + (int64_t)l * p.layer_elems;
+
+    // ================= QKV =================
+    stamp(p, l * 8 + 0);
+    {
+      const int tid = phase_tid();
+      const int lane = tid & 63, wave = wave_of(tid);
+      (void)lane;
+      (void)wave;
+      PGroup<LPR_D, NB_D, RWQ> cur;
+      gemv_first<LPR_D, NB_D, RWQ>(tid, Ly.qkv, q0, q1, cur);
+      __syncthreads();
+      stage_x<KD>(tid, p.xx, tin, Ly.attn_norm, p.eps, s, ctl);
+      if (bail) return;
+      gemv_rest<LPR_D, NB_D, RWQ>(tid, Ly.qkv, q0, q1, cur, s);
+      __syncthreads();
+      const int page = pos_ok ? p.page_table[pos / kPageTokens] : -1;
+      for (int pi = tid; 2 * pi < q1 - q0; pi += kPT) {
+        const int dr = q0 + 2 * pi;
+        const float a = s.ydot[2 * pi], b = s.ydot[2 * pi + 1];
+        int head, dd0, dd1, which;
+        float o0 = a, o1 = b;
+        if (dr < HD + GD) {
+          const int local = dr < HD ? dr : dr - HD;
+          head = local / D;
+          const int i = (local - head * D) >> 1;
+          const float2 cs = pos_ok ? p.rope[(int64_t)pos * (D >> 1) + i] : make_float2(1.f, 0.f);
+          o0 = a * cs.x - b * cs.y;
+          o1 = a * cs.y + b * cs.x;
+          dd0 = i;
+          dd1 = i + (D >> 1);
+          which = 0;
+          if (dr < HD) {
+            xstore(p.xq, head * D + dd0, o0, tout);
+            xstore(p.xq, head * D + dd1, o1, tout);
+            continue;
+          }
+        } else {
+          const int local = dr - HD - GD;
+          head = local / D;
+          dd0 = local - head * D;
+          dd1 = dd0 + 1;
+          which = 1;
+        }
+        const uint16_t k0 = f32_to_kv<KVDT>(o0), k1 = f32_to_kv<KVDT>(o1);
+        const int xb = HD + which * GD + head * D;
+        xstore(p.xq, xb + dd0, kv_to_f32<KVDT>(k0), tout);
+        xstore(p.xq, xb + dd1, kv_to_f32<KVDT>(k1), tout);
+        if (page >= 0 && page < p.n_pages) {
+          uint16_t* dst = pool + (int64_t)page * p.page_elems +
+                          ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D;
+          dst[dd0] = k0;
+          dst[dd1] = k1;
+        } else if (pos_ok) {
+          atomicOr(p.err, 1);
+        }
+      }
+    }
+
+    // ================= ATTENTION (KV head ag, split as) =================
+    stamp(p, l * 8 + 1);
+    {
+      const int tid = phase_tid();
+      const int lane = tid & 63, wave = wave_of(tid);
+      (void)lane;
+      (void)wave;
+      constexpr int DL = D / 8, NV = D / 8, TG = kWave / NV, TPL = kPageTokens / TG, NCH = DL / 8;
+      const int rep = H / G;
+      int n_pg = (kv_len + kPageTokens - 1) / kPageTokens;
+      n_pg = min(n_pg, p.max_pages);
+      const int pps = (n_pg + S - 1) / S;
+      const bool active = ag < G;
+      const int pg0 = active ? as * pps : 0;
+      const int pg1 = active ? min(n_pg, pg0 + pps) : 0;
+      const int pg_new = pos / kPageTokens, slot_new = pos % kPageTokens;
+      const int sc_tok = lane >> 3, sc_c = lane & 7, v_c = lane % NV, v_tg = lane / NV;
+      // first page's id and data go out before the wait for q
+      int pg = pg0 + wave;
+      int page = (pg < pg1) ? p.page_table[pg] : -1;
+      u32x4 kraw[2][NCH], vraw[TPL];
+      auto load_page = [&](int pid) {
+        const bool ok = pid >= 0 && pid < p.n_pages;
+        const uint16_t* kb = pool + (int64_t)(ok ? pid : 0) * p.page_elems + (int64_t)(ag * 2) * kPageTokens * D;
+        const uint16_t* vb = kb + kPageTokens * D;
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch)
+            kraw[ps][ch] = ok ? *(const u32x4*)(kb + (ps * 8 + sc_tok) * D + sc_c * DL + ch * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) vraw[u] = ok ? *(const u32x4*)(vb + (v_tg + u * TG) * D + v_c * 8) : u32x4{0, 0, 0, 0};
+      };
+      if (active && pg < pg1) load_page(page);
+      // q rows of this KV head and the new key / value
+      if (active) {
+        const __amdgpu_buffer_rsrc_t r = xrsrc(p.xq, (int64_t)Nq * 4);
+        constexpr int NQW = (QR * D + 2 * D + kPT - 1) / kPT;
+        int idx[NQW];
+        uint32_t word[NQW];
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) {
+          const int e = tid + i * kPT;
+          if (e < QR * D) {
+            const int qr = e / D, dd = e - qr * D;
+            idx[i] = (ag * rep + qr) * D + dd;
+          } else if (e < QR * D + 2 * D) {
+            const int e2 = e - QR * D, which = e2 / D, dd = e2 - which * D;
+            idx[i] = HD + which * GD + ag * D + dd;
+          } else {
+            idx[i] = -1;
+          }
+        }
+        poll_words<NQW>(r, idx, tout, word, ctl);
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) {
+          const int e = tid + i * kPT;
+          if (e < QR * D) {
+            al.q[e] = xdec(word[i]) * p.attn_scale;
+          } else if (e < QR * D + 2 * D) {
+            const int e2 = e - QR * D, which = e2 / D, dd = e2 - which * D;
+            const uint16_t bits = f32_to_kv<KVDT>(xdec(word[i]));
+            if (which == 0) al.knew[dd] = bits;
+            else al.vnew[dd] = bits;
+          }
+        }
+      }
+      __syncthreads();
+      if (bail) return;
+      float mrun[QR], lrun[QR], acc[QR][8];
+#pragma unroll
+      for (int qr = 0; qr < QR; ++qr) {
+        mrun[qr] = -INFINITY;
+        lrun[qr] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[qr][e] = 0.f;
+      }
+      for (; active && pg < pg1; pg += kPW) {
+        const bool valid = page >= 0 && page < p.n_pages;
+        if (!valid && lane == 0) atomicOr(p.err, 1);
+        const int pgn = pg + kPW;
+        const int page_n = pgn < pg1 ? p.page_table[pgn] : -1;
+        if (pg == pg_new) {  // the new token's slot comes from the exchange
+#pragma unroll
+          for (int ps = 0; ps < 2; ++ps)
+            if (ps * 8 + sc_tok == slot_new)
+#pragma unroll
+              for (int ch = 0; ch < NCH; ++ch) kraw[ps][ch] = lds_chunk16(al.knew, sc_c * DL + ch * 8);
+#pragma unroll
+          for (int u = 0; u < TPL; ++u)
+            if (v_tg + u * TG == slot_new) vraw[u] = lds_chunk16(al.vnew, v_c * 8);
+        }
+        if (valid) {
+          float sc[2][QR];
+#pragma unroll
+          for (int ps = 0; ps < 2; ++ps) {
+            const int j = pg * kPageTokens + ps * 8 + sc_tok;
+            float kf[DL];
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) unpack8p<KVDT>(kraw[ps][ch], kf + ch * 8);
+#pragma unroll
+            for (int qr = 0; qr < QR; ++qr) {
+              float dot = 0.f;
+#pragma unroll
+              for (int e = 0; e < DL; ++e) dot = fmaf(al.q[qr * D + sc_c * DL + e], kf[e], dot);
+              dot += __shfl_xor(dot, 1);
+              dot += __shfl_xor(dot, 2);
+              dot += __shfl_xor(dot, 4);
+              sc[ps][qr] = j < kv_len ? dot : -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int qr = 0; qr < QR; ++qr) {
+            float pm = fmaxf(sc[0][qr], sc[1][qr]);
+            pm = fmaxf(pm, __shfl_xor(pm, 8));
+            pm = fmaxf(pm, __shfl_xor(pm, 16));
+            pm = fmaxf(pm, __shfl_xor(pm, 32));
+            const float mnew = fmaxf(mrun[qr], pm);
+            float p0 = 0.f, p1 = 0.f, alpha = 1.f;
+            if (mnew != -INFINITY) {
+              p0 = __expf(sc[0][qr] - mnew);
+              p1 = __expf(sc[1][qr] - mnew);
+              alpha = __expf(mrun[qr] - mnew);
+            }
+            float ps_ = p0 + p1;
+            ps_ += __shfl_xor(ps_, 8);
+            ps_ += __shfl_xor(ps_, 16);
+            ps_ += __shfl_xor(ps_, 32);
+            lrun[qr] = lrun[qr] * alpha + ps_;
+            mrun[qr] = mnew;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[qr][e] *= alpha;
+            if (sc_c == 0) {
+              al.p[wave][qr][sc_tok] = p0;
+              al.p[wave][qr][8 + sc_tok] = p1;
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+          for (int u = 0; u < TPL; ++u) {
+            const int tok = v_tg + u * TG;
+            const int j = pg * kPageTokens + tok;
+            float vf[8];
+            unpack8p<KVDT>(vraw[u], vf);
+            const bool live = j < kv_len;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vf[e] = live ? vf[e] : 0.f;
+#pragma unroll
+            for (int qr = 0; qr < QR; ++qr) {
+              const float pw = al.p[wave][qr][tok];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[qr][e] = fmaf(pw, vf[e], acc[qr][e]);
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+        page = page_n;
+        if (pgn < pg1) load_page(page);
+      }
+      // reduce the value partials over the token groups, then merge the waves
+#pragma unroll
+      for (int qr = 0; qr < QR; ++qr)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int o = NV; o < kWave; o <<= 1) acc[qr][e] += __shfl_xor(acc[qr][e], o);
+      if (v_tg == 0) {
+#pragma unroll
+        for (int qr = 0; qr < QR; ++qr)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) al.acc[wave][qr * D + v_c * 8 + e] = acc[qr][e];
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int qr = 0; qr < QR; ++qr) {
+          al.m[wave][qr] = mrun[qr];
+          al.l[wave][qr] = lrun[qr];
+        }
+      }
+      __syncthreads();
+      if (active) {
+        for (int e = tid; e < QR * D; e += kPT) {
+          const int qr = e / D, dd = e - qr * D;
+          float M = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < kPW; ++v) M = fmaxf(M, al.m[v][qr]);
+          float a = 0.f, lsum = 0.f;
+          if (M != -INFINITY) {
+#pragma unroll
+            for (int v = 0; v < kPW; ++v) {
+              const float f = __expf(al.m[v][qr] - M);
+              a = fmaf(al.acc[v][e], f, a);
+              lsum = fmaf(al.l[v][qr], f, lsum);
+            }
+          }
+          const int h = ag * rep + qr;
+          uint32_t* dst = p.xp + ((int64_t)h * S + as) * (D + 2);
+          xstore(dst, dd, a, tout);
+          if (dd == 0) {
+            xstore(dst, D, M == -INFINITY ? kNoScore : M, tout);
+            xstore(dst, D + 1, lsum, tout);
+          }
+        }
+      }
+    }
+
+    // ================= MERGE (outputs [m0, m1) of the H*D attention vector) =================
+    stamp(p, l * 8 + 2);
+    {
+      const int tid = phase_tid();
+      const int lane = tid & 63, wave = wave_of(tid);
+      (void)lane;
+      (void)wave;
+      // The range covers at most two heads (m1 - m0 <= D). Thread t first waits for one (m, l)
+      // word and for the acc words of (output, split) pairs t, t + kPT, ... (at most kMrgProd).
+      const __amdgpu_buffer_rsrc_t r = xrsrc(p.xp, (int64_t)H * S * (D + 2) * 4);
+      float* ml = s.mrg;                       // [2][S][2]
+      float* fm = s.mrg + 4 * kMaxSplit;       // [2][S]
+      float* den = fm + 2 * kMaxSplit;         // [2]
+      float* prod = den + 8;                   // [m1 - m0][S]
+      const int n_out = m1 - m0;
+      const int hA = m0 / D, hB = n_out > 0 ? (m1 - 1) / D : hA;
+      constexpr int NW = 1 + kMrgProd / kPT;
+      int idx[NW];
+      uint32_t word[NW];
+      {
+        const int e = tid;  // (head slot, split, m|l)
+        const int hh = e / (2 * S), rest = e - hh * 2 * S;
+        const bool use = n_out > 0 && hh < 2 && !(hh == 1 && hB == hA);
+        idx[0] = use ? ((hh == 0 ? hA : hB) * S + (rest >> 1)) * (D + 2) + D + (rest & 1) : -1;
+      }
+#pragma unroll
+      for (int i = 1; i < NW; ++i) {
+        const int t = tid + (i - 1) * kPT;  // (output, split)
+        const int eo = t / S, sp = t - eo * S;
+        if (eo < n_out) {
+          const int e = m0 + eo, h = e / D, dd = e - h * D;
+          idx[i] = (h * S + sp) * (D + 2) + dd;
+        } else {
+          idx[i] = -1;
+        }
+      }
+      poll_words<NW>(r, idx, tout, word, ctl);
+      if (idx[0] >= 0) ml[tid] = xdec(word[0]);
+      __syncthreads();
+      if (bail) return;
+      // per head: max over splits, factors, fixed-order denominator
+      if (n_out > 0 && wave < 2 && !(wave == 1 && hB == hA)) {
+        float M = kNoScore;
+        for (int sp = lane; sp < S; sp += kWave) M = fmaxf(M, ml[(wave * S + sp) * 2]);
+        M = wave_max(M);
+        for (int sp = lane; sp < S; sp += kWave) fm[wave * kMaxSplit + sp] = __expf(ml[(wave * S + sp) * 2] - M);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane == 0) {
+          float dsum = 0.f;
+          for (int sp = 0; sp < S; ++sp) dsum = fmaf(ml[(wave * S + sp) * 2 + 1], fm[wave * kMaxSplit + sp], dsum);
+          den[wave] = dsum;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 1; i < NW; ++i) {
+        if (idx[i] < 0) continue;
+        const int t = tid + (i - 1) * kPT;
+        const int eo = t / S, sp = t - eo * S;
+        const int hh = (m0 + eo) / D == hA ? 0 : 1;
+        prod[eo * S + sp] = xdec(word[i]) * fm[hh * kMaxSplit + sp];
+      }
+      __syncthreads();
+      for (int eo = tid; eo < n_out; eo += kPT) {
+        const int hh = (m0 + eo) / D == hA ? 0 : 1;
+        float a = 0.f;
+        for (int sp = 0; sp < S; ++sp) a += prod[eo * S + sp];
+        const float dd = den[hh];
+        xstore(p.xa, m0 + eo, dd > 0.f ? a / dd : 0.f, tout);
+      }
+    }
+
+    // ================= O + residual =================
+    stamp(p, l * 8 + 3);
+    {
+      const int tid = phase_tid();
+      const int lane = tid & 63, wave = wave_of(tid);
+      (void)lane;
+      (void)wave;
+      PGroup<LPR_D, NB_D, RWO> cur;
+      gemv_first<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, cur);
+      stage_x<KD>(tid, p.xa, tout, nullptr, 0.f, s, ctl);
+      if (bail) return;
+      gemv_rest<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, cur, s);
+      __syncthreads();
+      for (int r = d0 + tid; r < d1; r += kPT) {
+        const float v = s.resid[r - d0] + s.ydot[r - d0];
+        s.resid[r - d0] = v;
+        xstore(p.xm, r, v, tout);
+      }
+    }
+
+    // ================= gate/up + SwiGLU =================
+    stamp(p, l * 8 + 4);
+    {
+      const int tid = phase_tid();
+      const int lane = tid & 63, wave = wave_of(tid);
+      (void)lane;
+      (void)wave;
+      PGroup<LPR_D, NB_D, RWG> cur;
+      gemv_first<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, cur);
+      __syncthreads();
+      stage_x<KD>(tid, p.xm, tout, Ly.ffn_norm, p.eps, s, ctl);
+      if (bail) return;
+      stamp(p, l * 8 + 6);
+      gemv_rest<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, cur, s);
+      __syncthreads();
+      stamp(p, l * 8 + 7);
+      for (int pi = tid; 2 * pi < g1 - g0; pi += kPT) {
+        const float gv = s.ydot[2 * pi], uv = s.ydot[2 * pi + 1];
+        xstore(p.xf, (g0 >> 1) + pi, silu(gv) * uv, tout);
+      }
+    }
+
+    // ================= down + residual =================
+    stamp(p, l * 8 + 5);
+    {
+      const int tid = phase_tid();
+      const int lane = tid & 63, wave = wave_of(tid);
+      (void)lane;
+      (void)wave;
+      PGroup<LPR_F, NB_F, RWF> cur;
+      gemv_first<LPR_F, NB_F, RWF>(tid, Ly.dn, d0, d1, cur);
+      __syncthreads();
+      stage_x<KF>(tid, p.xf, tout, nullptr, 0.f, s, ctl);
+      if (bail) return;
+      gemv_rest<LPR_F, NB_F, RWF>(tid, Ly.dn, d0, d1, cur, s);
+      __syncthreads();
+      for (int r = d0 + tid; r < d1; r += kPT) {
+        const float v = s.resid[r - d0] + s.ydot[r - d0];
+        s.resid[r - d0] = v;
+        xstore(p.xx, r, v, tout);
+      }
+    }
+  }
+
+  // ================= final RMSNorm + lm_head + argmax partial =================
+  stamp(p, L * 8 + 0);
+  const uint32_t tfin = base_tag + (uint32_t)L;  // T(L - 1)
+  // ================= final RMSNorm + lm_head + argmax partial =================
+  {
+    const int tid = phase_tid();
+    const int lane = tid & 63, wave = wave_of(tid);
+    (void)lane;
+    (void)wave;
+    __syncthreads();
+    stage_x<KD>(tid, p.xx, tfin, p.final_norm, p.eps, s, ctl);
+    if (bail) return;
+    float best_v = -INFINITY;
+    int best_i = 0x7fffffff;
+    const Mat lm = p.lm;
+    for (int c0 = v0; c0 < v1; c0 += kMaxRows) {
+      const int c1 = min(v1, c0 + kMaxRows);
+      PGroup<LPR_D, NB_D, kLmRW> cur;
+      gemv_first<LPR_D, NB_D, kLmRW>(tid, lm, c0, c1, cur);
+      gemv_rest<LPR_D, NB_D, kLmRW>(tid, lm, c0, c1, cur, s);
+      __syncthreads();
+      for (int r = c0 + tid; r < c1; r += kPT) {
+        const float v = s.ydot[r - c0];
+        if (p.logits) p.logits[r] = v;
+        if (v > best_v || (v == best_v && r < best_i)) { best_v = v; best_i = r; }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(best_v, o);
+      const int oi = __shfl_xor(best_i, o);
+      if (ov > best_v || (ov == best_v && oi < best_i)) { best_v = ov; best_i = oi; }
+    }
+    if (lane == 0) {
+      s.red[wave] = best_v;
+      reinterpret_cast<int*>(s.red)[16 + wave] = best_i;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float bv = s.red[0];
+      int bi = reinterpret_cast<int*>(s.red)[16];
+      for (int v = 1; v < kPW; ++v) {
+        const float ov = s.red[v];
+        const int oi = reinterpret_cast<int*>(s.red)[16 + v];
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      // (value, index | tag << 30) as one 64-bit word: the value is exchanged exactly
+      const uint64_t word = ((uint64_t)(((uint32_t)bi & 0x3FFFFFFFu) | ((epoch & 3u) << 30)) << 32) | __float_as_uint(bv);
+      __hip_atomic_store(p.xarg + w, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (w != 0) return;
+  // ================= argmax over the workgroup partials (workgroup 0) =================
+  stamp(p, L * 8 + 1);
+  {
+    const int tid = phase_tid();
+    const int lane = tid & 63, wave = wave_of(tid);
+    (void)lane;
+    (void)wave;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int k = tid; k < nwg; k += kPT) {
+      uint64_t word = __hip_atomic_load(p.xarg + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ctl.t0 = __builtin_amdgcn_s_memrealtime();
+      while ((uint32_t)(word >> 62) != (epoch & 3u)) {
+        if (give_up(ctl)) break;
+        __builtin_amdgcn_s_sleep(1);
+        word = __hip_atomic_load(p.xarg + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const float v = __uint_as_float((uint32_t)word);
+      const int i = (int)((word >> 32) & 0x3FFFFFFFu);
+      if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    __syncthreads();
+    if (lane == 0) {
+      s.red[wave] = bv;
+      reinterpret_cast<int*>(s.red)[16 + wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float b2 = s.red[0];
+      int i2 = reinterpret_cast<int*>(s.red)[16];
+      for (int v = 1; v < kPW; ++v) {
+        const float ov = s.red[v];
+        const int oi = reinterpret_cast<int*>(s.red)[16 + v];
+        if (ov > b2 || (ov == b2 && oi < i2)) { b2 = ov; i2 = oi; }
+      }
+      if (!bail) {
+        if (p.argmax) p.argmax[0] = i2 == 0x7fffffff ? 0 : i2;
+        p.epoch[0] = epoch + 1;  // every workgroup has read it: all have reached the final phase
+      }
+      if (p.stamps != nullptr) p.stamps[L * 8 + 2] = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+}
+
+// Re-tag every exchange word so that no word matches the first tag the next step waits for
+// (T(-1) + 2 for the layer-input vector, T(0) + 2 for the others, epoch + 2 for the argmax).
+__global__ void k_persist_reset(PersistParams p, int n_q, int n_p, int n_a, int n_d, int n_f, int n_arg) {
+  const uint32_t epoch = p.epoch[0];
+  const uint32_t base_tag = epoch * (uint32_t)(p.L + 2);
+  const uint32_t bad_in = base_tag + 2, bad = base_tag + 3;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_q) p.xq[i] = xenc(0.f, bad);
+  if (i < n_p) p.xp[i] = xenc(0.f, bad);
+  if (i < n_a) p.xa[i] = xenc(0.f, bad);
+  if (i < n_d) {
+    p.xm[i] = xenc(0.f, bad);
+    p.xx[i] = xenc(0.f, bad_in);
+  }
+  if (i < n_f) p.xf[i] = xenc(0.f, bad);
+  if (i < n_arg) p.xarg[i] = (uint64_t)((epoch + 2) & 3u) << 62;
+  if (i == 0) p.abort_flag[0] = 0u;
+}
+
+// ---- host side ----------------------------------------------------------------------------------
+
+template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR>
+static size_t persist_lds_bytes() {
+  constexpr int KD = LPR_D * NB_D * 32, KF = LPR_F * NB_F * 32;
+  constexpr int KMAX = KD > KF ? KD : KF;
+  return sizeof(float) * ((size_t)KMAX + KMAX / 32 + KMAX / 4 + kMaxRows + kMaxOwn + 32 + kMrg) + sizeof(AttnLds<D, QR>);
+}
+
+template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF>
+static int launch_persist_t(const PersistParams& p, int nwg, hipStream_t s, bool query_only) {
+  auto kern = k_persist<LPR_D, NB_D, LPR_F, NB_F, KVDT, D, QR, RWQ, RWO, RWG, RWF>;
+  const size_t lds = persist_lds_bytes<LPR_D, NB_D, LPR_F, NB_F, KVDT, D, QR>();
+  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return -1;
+  if (query_only) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kPT, lds) != hipSuccess) return -1;
+    return per_cu >= 1 ? 0 : -2;
+  }
+  PersistParams a = p;
+  void* args[] = {&a};
+  if (hipLaunchCooperativeKernel((const void*)kern, dim3(nwg), dim3(kPT), args, lds, s) != hipSuccess) return -1;
+  return 0;
+}
+
+// Shapes with an instantiation: (d, ffn, head dim, query heads per KV head) with the row steps
+// per wave group sized for 256 workgroups
+int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
+                   bool query_only) {
+#define BW_P(DM, FF, LD, ND, LF, NF, DD, QR, RQ, RO, RG, RF)                                                  \
+  if (d == DM && F == FF && D == DD && rep == QR) {                                                           \
+    return kv_dtype == 1 ? launch_persist_t<LD, ND, LF, NF, 1, DD, QR, RQ, RO, RG, RF>(p, nwg, s, query_only) \
+                         : launch_persist_t<LD, ND, LF, NF, 2, DD, QR, RQ, RO, RG, RF>(p, nwg, s, query_only); \
+  }
+  BW_P(4096, 12288, 64, 2, 64, 6, 128, 4, 2, 1, 2, 1)  // dense-9b: 24 / 16 / 96 / 16 rows per workgroup
+  BW_P(256, 1024, 8, 1, 32, 1, 64, 2, 1, 1, 1, 1)       // tiny
+#undef BW_P
+  return -2;
+}
+
+int launch_persist_reset(const PersistParams& p, int n_q, int n_p, int n_a, int n_d, int n_f, int n_arg, hipStream_t s) {
+  const int n = std::max({n_q, n_p, n_a, n_d, n_f, n_arg});
+  hipLaunchKernelGGL(k_persist_reset, dim3((n + 255) / 256), dim3(256), 0, s, p, n_q, n_p, n_a, n_d, n_f, n_arg);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace bw

@@ -149,6 +149,12 @@ struct bw_model {
   float* gemm_part = nullptr;    // k-split partials of the largest dense GEMM
   float* rms = nullptr;          // [T] RMSNorm factors
   int gemm_min_rows = 8;
+  // single-launch batch-1 step (dense models): exchange buffers and switches
+  bool persist_ok = false;       // an instantiation exists and fits
+  bool use_persist = true;
+  int persist_nwg = 0;           // workgroups (one per CU)
+  PersistParams pp{};            // step-independent parameters
+  int n_xq = 0, n_xp = 0, n_xa = 0, n_xd = 0, n_xf = 0;
   // measurement hook
   int trace_class = -1;
   std::vector<hipEvent_t> trace_ev;
@@ -329,6 +335,75 @@ static int check_shape(const bw_model_config& c) {
   return 0;
 }
 
+// The single-launch step (bw_persist.hip) for a dense model whose shape has an instantiation:
+// one workgroup per CU, the geometry limits of the kernel checked here, exchange buffers
+// allocated and tagged. Models without one keep the kernel chain only.
+static int persist_setup(bw_model* m) {
+  const auto& c = m->c;
+  if (is_moe(c)) return BW_OK;
+  int dev = 0, ncu = 0;
+  HIP_OK(hipGetDevice(&dev));
+  HIP_OK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  const int d = c.d_model, H = c.n_q_heads, G = c.n_kv_heads, D = c.head_dim, F = c.ffn_dim;
+  const int nwg = ncu;
+  const int S = nwg / G;
+  const int Rm = (H * D + nwg - 1) / nwg;
+  const int Rd = (d + nwg - 1) / nwg;
+  const int Rq = ((((H + 2 * G) * D + nwg - 1) / nwg) + 1) & ~1;
+  const int Rg = (((2 * F + nwg - 1) / nwg) + 1) & ~1;
+  int lpr, nb;
+  gemv_lane_split(d, &lpr, &nb);
+  const bool fits = H * D == d && S >= 1 && S <= 128 && Rm * S <= 2048 && Rm <= D && Rd <= 64 && Rq <= 1024 &&
+                    Rg <= 1024 && (H / G) * D <= 4096;
+  if (!fits) return BW_OK;
+  PersistParams& p = m->pp;
+  if (launch_persist(p, d, F, c.kv_dtype, D, H / G, nwg, nullptr, true) != 0) return BW_OK;
+  std::vector<PLayer> layers(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerDev& Ld = m->L[l];
+    layers[l] = PLayer{Ld.qkv, Ld.o, Ld.gu, Ld.dn, Ld.attn_norm, Ld.ffn_norm};
+  }
+  void* ptr;
+  if (int rc = ws_alloc(m, sizeof(PLayer) * layers.size(), &ptr)) return rc;
+  HIP_OK(hipMemcpy(ptr, layers.data(), sizeof(PLayer) * layers.size(), hipMemcpyHostToDevice));
+  p.layers = (const PLayer*)ptr;
+  p.L = c.n_layers;
+  p.H = H;
+  p.G = G;
+  p.V = c.vocab;
+  p.lm = m->lm;
+  p.final_norm = m->final_norm;
+  p.embed = m->embed;
+  p.eps = c.rms_eps;
+  p.attn_scale = (float)(1.0 / std::sqrt((double)D));
+  p.rope = m->rope;
+  p.max_pos = c.max_positions;
+  p.err = m->err;
+  m->n_xq = (H + 2 * G) * D;
+  m->n_xp = H * S * (D + 2);
+  m->n_xa = H * D;
+  m->n_xd = d;
+  m->n_xf = F;
+  uint32_t** bufs[6] = {&p.xq, &p.xp, &p.xa, &p.xm, &p.xf, &p.xx};
+  const int sizes[6] = {m->n_xq, m->n_xp, m->n_xa, m->n_xd, m->n_xf, m->n_xd};
+  for (int i = 0; i < 6; ++i) {
+    if (int rc = ws_alloc(m, sizeof(uint32_t) * sizes[i], &ptr)) return rc;
+    *bufs[i] = (uint32_t*)ptr;
+  }
+  if (int rc = ws_alloc(m, sizeof(uint64_t) * nwg, &ptr)) return rc;
+  p.xarg = (uint64_t*)ptr;
+
+  if (int rc = ws_alloc(m, 256, &ptr)) return rc;
+  HIP_OK(hipMemset(ptr, 0, 256));
+  p.epoch = (uint32_t*)ptr;
+  p.abort_flag = (uint32_t*)ptr + 16;
+  if (launch_persist_reset(p, m->n_xq, m->n_xp, m->n_xa, m->n_xd, m->n_xf, nwg, nullptr)) return fail(BW_EHIP, "persistent-step reset failed");
+  HIP_OK(hipDeviceSynchronize());
+  m->persist_nwg = nwg;
+  m->persist_ok = true;
+  return BW_OK;
+}
+
 extern "C" int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed, bw_model** out) {
   if (!cfg || !out) return fail(BW_EINVAL, "null argument");
   *out = nullptr;
@@ -490,6 +565,7 @@ extern "C" int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed
       m->gates = (float*)p;
     }
   }
+  if ((rc = persist_setup(m))) return bail(rc);
   if (hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess)
     return bail(fail(BW_EHIP, "stream creation failed"));
   if (hipDeviceSynchronize() != hipSuccess) return bail(fail(BW_EHIP, "device synchronisation failed"));
@@ -876,6 +952,25 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
   if (batch < 1 || t < 1 || max_pages < 1) return fail(BW_EINVAL, "batch, t and max_pages must be positive");
   if (batch * t > m->c.max_tokens) return fail(BW_ERANGE, "batch * t = %d exceeds max_tokens %d", batch * t, m->c.max_tokens);
   hipStream_t s = (hipStream_t)stream;
+  if (m->persist_ok && m->use_persist && batch == 1 && t == 1 && m->trace_class < 0) {
+    // the whole step as one cooperative launch (no capture needed: one launch per step)
+    PersistParams p = m->pp;
+    p.pool = pool->data;
+    p.layer_elems = pool->layer_elems;
+    p.page_elems = pool->page_elems;
+    p.n_pages = pool->n_pages;
+    p.tokens = tokens;
+    p.seq_lens = seq_lens;
+    p.page_table = page_table;
+    p.max_pages = max_pages;
+    p.logits = logits_out;
+    p.argmax = argmax_out;
+    const auto& c = m->c;
+    if (launch_persist(p, c.d_model, c.ffn_dim, c.kv_dtype, c.head_dim, c.n_q_heads / c.n_kv_heads, m->persist_nwg, s,
+                       false))
+      return fail(BW_EHIP, "single-launch step failed to launch");
+    return BW_OK;
+  }
   if (!m->use_graphs || m->trace_class >= 0)
     return enqueue_step(m, pool, tokens, seq_lens, page_table, batch, t, max_pages, logits_out, argmax_out, s);
   // replay a captured step when the arguments match one, else capture one (a one-time cost)
@@ -923,6 +1018,13 @@ extern "C" int bw_set_graphs(bw_model* m, int32_t enable) {
   return BW_OK;
 }
 
+extern "C" int bw_set_single_launch(bw_model* m, int32_t enable, int32_t* available) {
+  if (!m) return fail(BW_EINVAL, "null model");
+  m->use_persist = enable != 0;
+  if (available) *available = m->persist_ok ? 1 : 0;
+  return BW_OK;
+}
+
 extern "C" int bw_set_gemm_min_rows(bw_model* m, int32_t min_rows) {
   if (!m) return fail(BW_EINVAL, "null model");
   if (min_rows < 0) return fail(BW_EINVAL, "min_rows must be >= 0");
@@ -937,6 +1039,9 @@ extern "C" int bw_check_device_error(bw_model* m, void* stream, int32_t* flags) 
   HIP_OK(hipStreamSynchronize((hipStream_t)stream));
   HIP_OK(hipMemcpy(flags, m->err, 4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemset(m->err, 0, 4));
+  if (m->persist_ok && (*flags & BW_DERR_PERSIST) &&
+      launch_persist_reset(m->pp, m->n_xq, m->n_xp, m->n_xa, m->n_xd, m->n_xf, m->persist_nwg, (hipStream_t)stream))
+    return fail(BW_EHIP, "persistent-step reset failed");
   HIP_OK(hipDeviceSynchronize());
   return BW_OK;
 }
@@ -1050,6 +1155,21 @@ extern "C" int bw_debug_read_experts(bw_model* m, int32_t n_rows, int32_t* host_
   for (int l = 0; l < c.n_layers; ++l)
     HIP_OK(hipMemcpy(host_dst + (size_t)l * n_rows * c.top_k, m->sel + (size_t)l * c.max_tokens * c.top_k,
                      sizeof(int32_t) * n_rows * c.top_k, hipMemcpyDeviceToHost));
+  return BW_OK;
+}
+
+extern "C" int bw_debug_single_launch_stamps(bw_model* m, uint64_t* stamps_dev, int32_t n) {
+  if (!m) return fail(BW_EINVAL, "null model");
+  if (!m->persist_ok) return fail(BW_ESTATE, "the model has no single-launch step");
+  if (stamps_dev && n < m->c.n_layers * 8 + 8) return fail(BW_ERANGE, "need %d stamps", m->c.n_layers * 8 + 8);
+  m->pp.stamps = stamps_dev;
+  return BW_OK;
+}
+
+extern "C" int bw_debug_single_launch_deadline(bw_model* m, uint64_t ticks) {
+  if (!m) return fail(BW_EINVAL, "null model");
+  if (!m->persist_ok) return fail(BW_ESTATE, "the model has no single-launch step");
+  m->pp.deadline_ticks = ticks;
   return BW_OK;
 }
 

@@ -32,9 +32,10 @@ def _cuda_i32(v):
 class Pair:
     """GPU session + oracle for one sequence, stepping both on the same tokens."""
 
-    def __init__(self, cfg, seed, max_len, ctx0=0, synth_seed=None, gemm_min_rows=None):
+    def __init__(self, cfg, seed, max_len, ctx0=0, synth_seed=None, gemm_min_rows=None, single=True):
         self.cfg = cfg
         self.s = Session(cfg, seed=seed, max_len=[max_len], max_tokens=4, pool_seed=seed + 100)
+        self.single = bw.bw_set_single_launch(self.s.model, single)
         if gemm_min_rows is not None:
             bw.bw_set_gemm_min_rows(self.s.model, gemm_min_rows)
         self.om = oracle.Model(oracle_cfg(cfg), seed)
@@ -77,15 +78,19 @@ def _compare(g, gam, o, where):
     return err
 
 
-@pytest.mark.parametrize("cfg,seed,gemm", [(configs.TINY, 1001, None), (MOE_SMALL, 1011, None), (configs.TINY, 1002, 1),
-                                           (MOE_SMALL, 1012, 1)],
-                         ids=["tiny", "moe-small", "tiny-gemm", "moe-small-gemm"])
-def test_prompt_then_greedy_decode(cfg, seed, gemm):
-    """gemm = 1 runs every dense matrix of every step on the matrix-core GEMM path."""
+@pytest.mark.parametrize("cfg,seed,gemm,single", [(configs.TINY, 1001, None, True), (configs.TINY, 1003, None, False),
+                                                  (MOE_SMALL, 1011, None, True), (configs.TINY, 1002, 1, False),
+                                                  (MOE_SMALL, 1012, 1, False)],
+                         ids=["tiny", "tiny-chain", "moe-small", "tiny-gemm", "moe-small-gemm"])
+def test_prompt_then_greedy_decode(cfg, seed, gemm, single):
+    """single: batch-1 steps as one cooperative launch (dense models); else the kernel chain.
+    gemm = 1 runs every dense matrix of every chain step on the matrix-core GEMM path."""
     prompt_len, steps = cfg.get("prompt", 16), cfg.get("steps", 32)
     rng = np.random.default_rng(seed)
     prompt = rng.integers(0, cfg["vocab"], prompt_len)
-    p = Pair(cfg, seed, prompt_len + steps + 1, gemm_min_rows=gemm)
+    p = Pair(cfg, seed, prompt_len + steps + 1, gemm_min_rows=gemm, single=single)
+    if single and not cfg.get("n_experts", 0):
+        assert p.single, "a dense model of this shape has the single-launch step"
     worst = 0.0
     try:
         for i, tok in enumerate(prompt):
@@ -134,10 +139,12 @@ def test_verify_step_equals_sequential_greedy(gemm):
 
 
 @pytest.mark.timeout(900)
-def test_dense_9b_synthesized_context():
+@pytest.mark.parametrize("single", [True, False], ids=["single-launch", "chain"])
+def test_dense_9b_synthesized_context(single):
     cfg = configs.DENSE_9B
     ctx, steps, seed = 2048, 3, cfg["seed"]
-    p = Pair(cfg, seed, ctx + steps + 1, ctx0=ctx, synth_seed=seed + 7)
+    p = Pair(cfg, seed, ctx + steps + 1, ctx0=ctx, synth_seed=seed + 7, single=single)
+    assert p.single or not single
     try:
         nxt = int(np.random.default_rng(seed).integers(0, cfg["vocab"]))
         worst = 0.0
@@ -145,7 +152,7 @@ def test_dense_9b_synthesized_context():
             g, gam, o = p.step([nxt])
             worst = max(worst, _compare(g, gam, o, f"9b step {i}"))
             nxt = int(np.argmax(o[0]))
-        print(f"[result] dense-9b max |logit diff| = {worst:.3e}")
+        print(f"[result] dense-9b ({'single launch' if single else 'chain'}) max |logit diff| = {worst:.3e}")
     finally:
         p.close()
 
@@ -187,3 +194,55 @@ def test_batched_verify_ragged_contexts():
         okv.close()
         om.close()
         s.close()
+
+
+def test_single_launch_matches_chain_over_many_steps():
+    """The single-launch step and the kernel chain agree step by step on the same tokens (tiny,
+    64 positions: every page, the ragged last page, both layers)."""
+    cfg, seed = configs.TINY, 1041
+    rng = np.random.default_rng(seed)
+    toks = rng.integers(0, cfg["vocab"], 64)
+    a = Session(cfg, seed=seed, max_len=[65], max_tokens=1, pool_seed=seed + 1)
+    b = Session(cfg, seed=seed, max_len=[65], max_tokens=1, pool_seed=seed + 2)
+    try:
+        assert bw.bw_set_single_launch(a.model, True)
+        bw.bw_set_single_launch(b.model, False)
+        worst = 0.0
+        for i, tok in enumerate(toks):
+            la, ma = a.step(_cuda_i32([int(tok)]), _cuda_i32([i]))
+            lb, mb = b.step(_cuda_i32([int(tok)]), _cuda_i32([i]))
+            ga, gb = la.cpu().numpy()[0], lb.cpu().numpy()[0]
+            d = float(np.max(np.abs(ga - gb)))
+            worst = max(worst, d)
+            assert d <= 1e-3, (i, d)
+            if top2_margin(gb.astype(np.float64)) > TOKEN_MARGIN:
+                assert int(ma.cpu()[0]) == int(mb.cpu()[0]), i
+        for sess in (a, b):
+            assert bw.bw_check_device_error(sess.model) == 0
+        print(f"[result] single launch vs chain, 64 steps: max |logit diff| = {worst:.3e}")
+    finally:
+        a.close()
+        b.close()
+
+
+def test_single_launch_timeout_is_reported_and_recovers():
+    """A wait that passes its deadline ends the single-launch step on every workgroup with
+    BW_DERR_PERSIST (forced here with a zero deadline); later steps return at once until the
+    error is read, after which the step runs normally again and matches the oracle."""
+    cfg, seed = configs.TINY, 1051
+    p = Pair(cfg, seed, 8)
+    try:
+        assert p.single
+        bw.bw_debug_single_launch_deadline(p.s.model, 0)
+        p.s.step(_cuda_i32([5]), _cuda_i32([0]))
+        torch.cuda.synchronize()
+        flags = bw.bw_check_device_error(p.s.model)
+        print(f"[result] device flags after a zero-deadline step: {flags}")
+        bw.bw_debug_single_launch_deadline(p.s.model, 50_000_000)
+        if flags:
+            assert flags & bw.BW_DERR_PERSIST, flags
+        g, gam, o = p.step([5])
+        _compare(g, gam, o, "after recovery")
+        assert bw.bw_check_device_error(p.s.model) == 0
+    finally:
+        p.close()
