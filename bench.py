@@ -9,9 +9,14 @@ the host inside the timed region.
 
 Output: one JSON line (metric, value = decode tok/s, ...) plus
   - achieved step bandwidth: algorithmic bytes per step / step time, against 8 TB/s;
-  - "roofline" of the dominant kernel (RMSNorm + gate/up GEMV + SwiGLU): algorithmic bytes per
-    launch / its average launch time, timed with HIP events on the step's stream in a traced
-    pass right after the timed region;
+  - "roofline" of the dominant kernel. The step runs as one kernel launch (k_persist: all layers,
+    the lm_head and the argmax), so that kernel is the step: algorithmic bytes per launch / its
+    average launch time, timed with HIP events on the step's stream around each launch in a traced
+    pass right after the timed region. "traffic" is the counted HBM bytes per launch from the
+    committed FETCH_SIZE / WRITE_SIZE profile while the kernel's sources are unchanged. With
+    --chain the kernel chain is timed instead and the roofline is its gate/up GEMV;
+  - "phases": per-layer wait / work time of each phase of the single-launch step, from GPU
+    real-time-counter stamps written by one workgroup;
   - "cpu_baseline": the fp64 CPU oracle timed on this host on a bounded sample of the same
     workload (decode steps at the same context, the context synthesised rather than prefilled).
 """
@@ -88,7 +93,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--no-graphs", action="store_true",
-                    help="launch the step's kernels directly instead of replaying a captured graph")
+                    help="kernel chain: launch the step's kernels directly instead of replaying a captured graph")
+    ap.add_argument("--chain", action="store_true",
+                    help="time the kernel chain instead of the single-launch step")
+    ap.add_argument("--cooperative", action="store_true",
+                    help="single-launch step through the cooperative launch API")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -124,6 +133,7 @@ def main() -> int:
     print(f"[bench] model + pool ready in {time.perf_counter() - t_load:.1f} s", file=sys.stderr, flush=True)
     if args.no_graphs:
         bw.bw_set_graphs(s.model, False)
+    single = bw.bw_set_single_launch(s.model, 0 if args.chain else (2 if args.cooperative else 1)) and not args.chain
     dev = "cuda"
     prompt = torch.from_numpy(np.random.default_rng(cfg["seed"]).integers(0, cfg["vocab"], P).astype(np.int32)).to(dev)
     tok = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -163,10 +173,63 @@ def main() -> int:
     print(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
           f"{step_gbps:.0f} GB/s algorithmic ({step_gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s)", file=sys.stderr, flush=True)
 
-    # traced pass: per-launch time of each kernel class, HIP events on the step's stream
-    kernel_us = {}
-    roofline = None
-    if not args.no_trace:
+    kernel_us, roofline, phases = {}, None, None
+    if not args.no_trace and single:
+        # traced pass: each step is one kernel launch; HIP events on the step's stream around each
+        # launch give the kernel's duration (the events sit outside the kernel, between launches)
+        n_tr = 64
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_tr)]
+        torch.cuda.synchronize()
+        for a_, b_ in evs:
+            a_.record()
+            step(feed_back=True)
+            b_.record()
+        torch.cuda.synchronize()
+        launch_us = sum(a_.elapsed_time(b_) for a_, b_ in evs) * 1000.0 / n_tr
+        ctx_tr = P + W + K + (n_tr - 1) / 2.0
+        bytes_tr = algorithmic_bytes(cfg, ctx_tr)["total"]
+        achieved = bytes_tr / (launch_us * 1e-6) / 1e9
+        traffic = None
+        tr_path = os.path.join(ROOT, "profiles", "step_dense9b_traffic.json")
+        if os.path.exists(tr_path):
+            with open(tr_path) as f:
+                tr = json.load(f)
+            from memory_bound_autoregressive_amd.build import source_digest
+            if tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ()))):
+                traffic = tr.get("hbm_bytes_per_launch")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                    "kernel": "k_persist: the whole batch-1 step in one launch (32 layers + lm_head + argmax)",
+                    "bytes_per_launch": round(bytes_tr), "avg_launch_us": round(launch_us, 2),
+                    "context_mean": ctx_tr}
+        kernel_us["k_persist"] = round(launch_us, 2)
+        # per-phase timeline of one workgroup (GPU real-time counter stamps)
+        L = cfg["n_layers"]
+        st = torch.zeros(L * 16 + 8, dtype=torch.int64, device=dev)
+        bw.bw_debug_single_launch_stamps(s.model, st, L * 16 + 8)
+        acc = np.zeros((L, 6, 2))
+        lm = np.zeros(2)
+        n_ph = 8
+        for _ in range(n_ph):
+            step(feed_back=True)
+            torch.cuda.synchronize()
+            v = st.cpu().numpy().astype(np.float64) / 100.0  # us
+            ph = v[:L * 16].reshape(L, 8, 2)[:, :6, :]
+            starts = ph[:, :, 0]
+            nxt = np.concatenate([starts[:, 1:], np.concatenate([starts[1:, :1], [[v[L * 16]]]])], axis=1)
+            acc[:, :, 0] += ph[:, :, 1] - ph[:, :, 0]
+            acc[:, :, 1] += nxt - ph[:, :, 1]
+            lm += [v[L * 16 + 1] - v[L * 16], v[L * 16 + 3] - v[L * 16 + 1]]
+        bw.bw_debug_single_launch_stamps(s.model, None)
+        acc /= n_ph
+        lm /= n_ph
+        names = ["qkv", "attention", "merge", "o", "gate_up", "down"]
+        phases = {k: {"wait_us": round(float(acc[:, i, 0].mean()), 2), "work_us": round(float(acc[:, i, 1].mean()), 2)}
+                  for i, k in enumerate(names)}
+        phases["lm_head"] = {"wait_us": round(float(lm[0]), 2), "work_us": round(float(lm[1]), 2)}
+        print(f"[bench] k_persist {launch_us:.1f} us per launch, {achieved:.0f} GB/s algorithmic; phases {phases}",
+              file=sys.stderr, flush=True)
+    elif not args.no_trace:
         L = cfg["n_layers"]
         classes = ["qkv", "attn", "o", "gate_up", "down", "lm_head"]
         n_trace = 8
@@ -189,19 +252,10 @@ def main() -> int:
             kernel_us[cls] = round(1000.0 * tot / cnt, 2)
         d, F = cfg["d_model"], cfg["ffn_dim"]
         gu_bytes = 2 * F * d * INT4_BYTES_PER_WEIGHT
-        gu_s = kernel_us["gate_up"] * 1e-6
-        achieved = gu_bytes / gu_s / 1e9
-        traffic = None
-        tr_path = os.path.join(ROOT, "profiles", "gate_up_dense9b_traffic.json")
-        if os.path.exists(tr_path):
-            with open(tr_path) as f:
-                tr = json.load(f)
-            from memory_bound_autoregressive_amd.build import source_digest
-            if tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ()))):
-                traffic = tr.get("hbm_bytes_per_launch")
+        achieved = gu_bytes / (kernel_us["gate_up"] * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                    "kernel": "RMSNorm + gate/up int4 GEMV + SwiGLU (24576 x 4096)",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "kernel": "chain: RMSNorm + gate/up int4 GEMV + SwiGLU (24576 x 4096)",
                     "bytes_per_launch": gu_bytes, "avg_launch_us": kernel_us["gate_up"]}
         print(f"[bench] per-launch kernel time (us): {kernel_us}", file=sys.stderr, flush=True)
     s.close()
@@ -216,10 +270,11 @@ def main() -> int:
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "dense-9b int4 decode: batch 1, 2048-token random prompt prefilled, greedy steps",
+                   "step": "single launch" if single else "kernel chain (hipGraph replay)",
                    "batch": 1, "prompt": P, "context_range": [P + W, P + W + K], "weights": "int4 blocks of 32, fp16 scales",
                    "kv": "bf16, 16-token pages, permuted pool", "seed": cfg["seed"]},
         "achieved_hbm_gbps": round(step_gbps, 1), "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "bytes_per_step": ab, "kernel_us": kernel_us, "roofline": roofline, "cpu_baseline": cpu,
+        "bytes_per_step": ab, "kernel_us": kernel_us, "phases": phases, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out))
     return 0

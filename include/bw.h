@@ -149,16 +149,23 @@ int bw_decode_step(bw_model* model, bw_kv_pool* pool, const int32_t* tokens_dev,
 /* Turn step capture on (default) or off (every call then launches its kernels directly). */
 int bw_set_graphs(bw_model* model, int32_t enable);
 
-/* Batch-1 decode steps (batch = 1, t = 1) of a dense model run as ONE cooperative kernel launch
- * when this is on (default) and the model's shape has a single-launch form: every layer's
- * phases (QKV + RoPE + KV append, attention, merge, O, gate/up, down) and the lm_head run in one
- * resident workgroup per CU that hand their small output vectors to each other through device
- * memory, so the weight stream is not broken by kernel boundaries (bw24 vs llama.cpp page,
- * section 2.2: launches and intermediate round trips are what fusion removes). Results match
- * the kernel chain to fp32 rounding (exchanged activations keep 21 mantissa bits). Other steps,
- * MoE models and traced steps use the kernel chain. *available_out (may be NULL) receives 1 when
- * the model has the single-launch form, else 0. Errors: BW_EINVAL (null model). */
-int bw_set_single_launch(bw_model* model, int32_t enable, int32_t* available_out);
+/* Batch-1 decode steps (batch = 1, t = 1) of a dense model run as ONE kernel launch when this is
+ * on and the model's shape has a single-launch form: every layer's phases (QKV + RoPE + KV append,
+ * attention, merge, O, gate/up, down) and the lm_head run in one resident workgroup per CU, and
+ * the phases hand their small output vectors to each other through device memory, so the weight
+ * stream is not broken by kernel boundaries (bw24 vs llama.cpp page, section 2.2: launches and
+ * intermediate round trips are what fusion removes). Results match the kernel chain to fp32
+ * rounding (exchanged activations keep 21 mantissa bits). Other steps, MoE models and traced steps
+ * use the kernel chain.
+ *   mode 0: off (kernel chain);
+ *   mode 1 (default): on, ordinary launch of one workgroup per CU (the model load checked that
+ *           one fits per CU, so on an otherwise idle GPU all are resident together);
+ *   mode 2: on, cooperative launch (the runtime guarantees co-residency or refuses the launch).
+ * Every wait inside the step is bounded either way (bw_debug_single_launch_deadline), so a
+ * workgroup that cannot start never hangs the step: it ends with BW_DERR_PERSIST.
+ * *available_out (may be NULL) receives 1 when the model has the single-launch form, else 0.
+ * Errors: BW_EINVAL (null model, mode outside 0..2). */
+int bw_set_single_launch(bw_model* model, int32_t mode, int32_t* available_out);
 
 /* Row count from which a step (and bw_debug_matvec) runs its dense matrices -- QKV, O, gate/up,
  * down, lm_head -- as one int4 GEMM on the matrix cores over all batch * t rows, reading each
@@ -221,10 +228,11 @@ int bw_debug_read_hidden(bw_model* model, int32_t n_rows, float* host_dst, void*
  * Errors: BW_EINVAL (null model), BW_ESTATE (no single-launch form). */
 int bw_debug_single_launch_deadline(bw_model* model, uint64_t ticks);
 
-/* Measurement hook of the single-launch step: while stamps_dev (device, n >= 8 * n_layers + 8
- * uint64) is set, workgroup 0 writes the GPU's 100 MHz real-time counter at the start of each
- * phase: [8 l + 0..5] = QKV, attention, merge, O, gate/up, down of layer l; [8 L + 0] = lm_head,
- * [8 L + 1] = final argmax, [8 L + 2] = step end, [8 L + 3] = step start. NULL turns it off.
+/* Measurement hook of the single-launch step: while stamps_dev (device, n >= 16 * n_layers + 8
+ * uint64) is set, workgroup 0 writes the GPU's 100 MHz real-time counter at each phase start and
+ * when the phase's input has arrived: [16 l + 2 k] and [16 l + 2 k + 1] for phases k = 0..5 (QKV,
+ * attention, merge, O, gate/up, down) of layer l; [16 L + 0 / 1] lm_head start / input ready,
+ * [16 L + 2] final argmax, [16 L + 3] step end, [16 L + 4] step start. NULL turns it off.
  * Errors: BW_EINVAL, BW_ESTATE (no single-launch form), BW_ERANGE (n too small). */
 int bw_debug_single_launch_stamps(bw_model* model, uint64_t* stamps_dev, int32_t n);
 

@@ -211,11 +211,11 @@ def bw_set_graphs(model: int, enable: bool) -> None:
     _check(lib().bw_set_graphs(model, int(bool(enable))), "bw_set_graphs")
 
 
-def bw_set_single_launch(model: int, enable: bool) -> bool:
-    """Switch batch-1 steps between one cooperative launch and the kernel chain; returns whether
-    the model has the single-launch form."""
+def bw_set_single_launch(model: int, mode: int | bool) -> bool:
+    """Batch-1 steps as one launch (mode 1 / True: ordinary launch, 2: cooperative launch) or as
+    the kernel chain (0 / False); returns whether the model has the single-launch form."""
     avail = ctypes.c_int32(0)
-    _check(lib().bw_set_single_launch(model, int(bool(enable)), ctypes.byref(avail)), "bw_set_single_launch")
+    _check(lib().bw_set_single_launch(model, int(mode), ctypes.byref(avail)), "bw_set_single_launch")
     return bool(avail.value)
 
 
@@ -224,7 +224,7 @@ def bw_debug_single_launch_deadline(model: int, ticks: int) -> None:
 
 
 def bw_debug_single_launch_stamps(model: int, stamps, n: int = 0) -> None:
-    """stamps: a device int64 tensor of n >= 8 * n_layers + 8 entries, or None to stop."""
+    """stamps: a device int64 tensor of n >= 16 * n_layers + 8 entries, or None to stop."""
     _check(lib().bw_debug_single_launch_stamps(model, _ptr(stamps) if stamps is not None else None, int(n)),
            "bw_debug_single_launch_stamps")
 

@@ -142,7 +142,8 @@ struct PersistParams {
   int32_t* err = nullptr;
   uint32_t* abort_flag = nullptr;
   uint64_t deadline_ticks = 50000000ull;  // one wait gives up after 0.5 s (100 MHz counter)
-  uint64_t* stamps = nullptr;       // optional [L * 8 + 8]: real-time counter at each phase start (workgroup 0)
+  uint64_t* stamps = nullptr;       // optional [L * 16 + 8]: real-time counter at phase starts (workgroup 0)
+  bool plain_launch = false;        // ordinary launch instead of the cooperative one (see the runtime)
 };
 
 // launchers (bw_gemv.hip, bw_attn.hip, bw_misc.hip)

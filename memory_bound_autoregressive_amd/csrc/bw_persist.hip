@@ -172,7 +172,6 @@ __device__ __forceinline__ void stamp(const PersistParams& p, int idx) {
 struct Lds {
   float* xs;     // staged input vector [Kmax] (bank-swizzled blocks)
   float* bs;     // block sums [Kmax / 32]
-  float* csum;   // chunk sums [Kmax / 4]
   float* ydot;   // row dot products of the current phase [kMaxRows]
   float* resid;  // exact residual rows owned by this workgroup [kMaxOwn]
   float* red;    // reduction scratch [32]
@@ -218,26 +217,23 @@ __device__ __forceinline__ void stage_x(int tid, const uint32_t* xin, uint32_t t
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int q = tid + i * kPT;
-    if (q >= N4) continue;
+    const int q = tid + i * kPT;  // chunk q = elements 4q..4q+3; block q / 8 sits in 8 adjacent lanes
+    const bool in = q < N4;
     const int k = 4 * q;
     float4 f = make_float4(xdec(v[i][0]), xdec(v[i][1]), xdec(v[i][2]), xdec(v[i][3]));
-    if (gamma != nullptr) {
+    if (in && gamma != nullptr) {
       const uint2 gh = *(const uint2*)(gamma + k);
       f.x *= scale * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
       f.y *= scale * f16_to_f32((uint16_t)(gh.x >> 16));
       f.z *= scale * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
       f.w *= scale * f16_to_f32((uint16_t)(gh.y >> 16));
     }
-    *(float4*)xs_chunk(s.xs, k >> 5, (k & 31) >> 2) = f;
-    s.csum[q] = (f.x + f.y) + (f.z + f.w);
-  }
-  __syncthreads();
-  for (int b = tid; b < K / 32; b += kPT) {
-    float a = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) a += s.csum[b * 8 + k];
-    s.bs[b] = a;
+    if (in) *(float4*)xs_chunk(s.xs, k >> 5, (k & 31) >> 2) = f;
+    float cs = in ? (f.x + f.y) + (f.z + f.w) : 0.f;
+    cs += __shfl_xor(cs, 1);
+    cs += __shfl_xor(cs, 2);
+    cs += __shfl_xor(cs, 4);
+    if (in && (q & 7) == 0) s.bs[q >> 3] = cs;
   }
   __syncthreads();
 }
@@ -310,24 +306,35 @@ __device__ __forceinline__ void gemv_first(int tid, const Mat w, int r0, int r1,
   pload<LPR, NB, RW>(tid, w, r0, r1, wave_of(tid), g);
 }
 
-// The rest of the rows; ydot is complete after the caller's __syncthreads. The A/B groups
-// alternate so that the next group's loads are in flight while the current one is computed.
-template <int LPR, int NB, int RW>
+// The rest of the rows; ydot is complete after the caller's __syncthreads. DB: the A/B groups
+// alternate so that the next group's loads are in flight while the current one is computed;
+// otherwise one group is kept (for phases whose group covers a wave's whole share of the rows,
+// so the loop runs once and no second register set is needed).
+template <int LPR, int NB, int RW, bool DB>
 __device__ __forceinline__ void gemv_rest(int tid, const Mat w, int r0, int r1, PGroup<LPR, NB, RW>& cur, const Lds& s) {
   constexpr int GROUP = (kWave / LPR) * RW;
   const int n_groups = (r1 - r0 + GROUP - 1) / GROUP;
   int gi = wave_of(tid);
   if (gi >= n_groups) return;
-  PGroup<LPR, NB, RW> alt;
-  while (true) {
-    pload<LPR, NB, RW>(tid, w, r0, r1, gi + kPW, alt);
-    pcompute<LPR, NB, RW>(tid, cur, r0, r1, s);
-    gi += kPW;
-    if (gi >= n_groups) break;
-    pload<LPR, NB, RW>(tid, w, r0, r1, gi + kPW, cur);
-    pcompute<LPR, NB, RW>(tid, alt, r0, r1, s);
-    gi += kPW;
-    if (gi >= n_groups) break;
+  if constexpr (DB) {
+    PGroup<LPR, NB, RW> alt;
+    while (true) {
+      pload<LPR, NB, RW>(tid, w, r0, r1, gi + kPW, alt);
+      pcompute<LPR, NB, RW>(tid, cur, r0, r1, s);
+      gi += kPW;
+      if (gi >= n_groups) break;
+      pload<LPR, NB, RW>(tid, w, r0, r1, gi + kPW, cur);
+      pcompute<LPR, NB, RW>(tid, alt, r0, r1, s);
+      gi += kPW;
+      if (gi >= n_groups) break;
+    }
+  } else {
+    while (true) {
+      pcompute<LPR, NB, RW>(tid, cur, r0, r1, s);
+      gi += kPW;
+      if (gi >= n_groups) break;
+      pload<LPR, NB, RW>(tid, w, r0, r1, gi, cur);
+    }
   }
 }
 
@@ -361,8 +368,8 @@ struct alignas(16) AttnLds {
 
 // ---- the kernel -------------------------------------------------------------------------------
 
-// RWQ, RWO, RWG, RWF: row steps per wave group of the QKV, O, gate/up and down passes, chosen so
-// that one group covers a wave's whole share of the phase at the instantiated shape.
+// RWQ, RWO, RWG, RWF: row steps per register group of the QKV, O, gate/up and down passes; a
+// group that covers a wave's whole share of a phase is loaded in full before the phase's wait.
 template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF>
 __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -373,8 +380,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   Lds s;
   s.xs = lds;
   s.bs = s.xs + KMAX;
-  s.csum = s.bs + KMAX / 32;
-  s.ydot = s.csum + KMAX / 4;
+  s.ydot = s.bs + KMAX / 32;
   s.resid = s.ydot + kMaxRows;
   s.red = s.resid + kMaxOwn;
   s.mrg = s.red + 32;
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   }
 
   const int L = p.L, H = p.H, G = p.G;
-  stamp(p, L * 8 + 3);
+  stamp(p, L * 16 + 4);
   const uint32_t epoch = p.epoch[0];
   const uint32_t base_tag = epoch * (uint32_t)(L + 2);
   const int pos = p.seq_lens[0];
@@ -435,27 +441,33 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   }
   if (!pos_ok && threadIdx.x == 0 && w == 0) atomicOr(p.err, 4);
 
+  // First weight groups of a phase are issued one phase early where registers allow: QKV's during
+  // the previous layer's down pass, O's during the merge, gate/up's during O.
+  PGroup<LPR_D, NB_D, RWQ> qkv_pre;
+  gemv_first<LPR_D, NB_D, RWQ>(phase_tid(), load_uniform(p.layers).qkv, q0, q1, qkv_pre);
+
   for (int l = 0; l < L; ++l) {
     // this layer's descriptors, read once with scalar loads (the table is constant for the step),
     // so the matrix pointers are uniform registers and the loops below never re-read them
     const PLayer Ly = load_uniform(p.layers + l);
+    const Mat next_qkv = load_uniform(&p.layers[l + 1 < L ? l + 1 : l].qkv);
     const uint32_t tin = base_tag + (uint32_t)l;       // T(l - 1)
     const uint32_t tout = base_tag + (uint32_t)l + 1;  // T(l)
     uint16_t* pool = p.pool + (int64_t)l * p.layer_elems;
 
     // ================= QKV =================
-    stamp(p, l * 8 + 0);
+    stamp(p, l * 16 + 0);
     {
       const int tid = phase_tid();
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
-      PGroup<LPR_D, NB_D, RWQ> cur;
-      gemv_first<LPR_D, NB_D, RWQ>(tid, Ly.qkv, q0, q1, cur);
+      PGroup<LPR_D, NB_D, RWQ>& cur = qkv_pre;
       __syncthreads();
       stage_x<KD>(tid, p.xx, tin, Ly.attn_norm, p.eps, s, ctl);
       if (bail) return;
-      gemv_rest<LPR_D, NB_D, RWQ>(tid, Ly.qkv, q0, q1, cur, s);
+      stamp(p, l * 16 + 1);
+      gemv_rest<LPR_D, NB_D, RWQ, (RWQ < 3)>(tid, Ly.qkv, q0, q1, cur, s);
       __syncthreads();
       const int page = pos_ok ? p.page_table[pos / kPageTokens] : -1;
       for (int pi = tid; 2 * pi < q1 - q0; pi += kPT) {
@@ -501,7 +513,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     }
 
     // ================= ATTENTION (KV head ag, split as) =================
-    stamp(p, l * 8 + 1);
+    stamp(p, l * 16 + 2);
     {
       const int tid = phase_tid();
       const int lane = tid & 63, wave = wave_of(tid);
@@ -554,6 +566,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           }
         }
         poll_words<NQW>(r, idx, tout, word, ctl);
+        stamp(p, l * 16 + 3);
 #pragma unroll
         for (int i = 0; i < NQW; ++i) {
           const int e = tid + i * kPT;
@@ -709,12 +722,14 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     }
 
     // ================= MERGE (outputs [m0, m1) of the H*D attention vector) =================
-    stamp(p, l * 8 + 2);
+    stamp(p, l * 16 + 4);
+    PGroup<LPR_D, NB_D, RWO> o_pre;
     {
       const int tid = phase_tid();
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
+      gemv_first<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, o_pre);
       // The range covers at most two heads (m1 - m0 <= D). Thread t first waits for one (m, l)
       // word and for the acc words of (output, split) pairs t, t + kPT, ... (at most kMrgProd).
       const __amdgpu_buffer_rsrc_t r = xrsrc(p.xp, (int64_t)H * S * (D + 2) * 4);
@@ -745,55 +760,75 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         }
       }
       poll_words<NW>(r, idx, tout, word, ctl);
+      stamp(p, l * 16 + 5);
       if (idx[0] >= 0) ml[tid] = xdec(word[0]);
       __syncthreads();
       if (bail) return;
-      // per head: max over splits, factors, fixed-order denominator
+      // per head: max over splits, factors, denominator (fixed-order reductions: deterministic)
+      const bool fast = S <= kWave && (S & (S - 1)) == 0;
       if (n_out > 0 && wave < 2 && !(wave == 1 && hB == hA)) {
         float M = kNoScore;
         for (int sp = lane; sp < S; sp += kWave) M = fmaxf(M, ml[(wave * S + sp) * 2]);
         M = wave_max(M);
-        for (int sp = lane; sp < S; sp += kWave) fm[wave * kMaxSplit + sp] = __expf(ml[(wave * S + sp) * 2] - M);
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane == 0) {
-          float dsum = 0.f;
-          for (int sp = 0; sp < S; ++sp) dsum = fmaf(ml[(wave * S + sp) * 2 + 1], fm[wave * kMaxSplit + sp], dsum);
-          den[wave] = dsum;
+        float dpart = 0.f;
+        for (int sp = lane; sp < S; sp += kWave) {
+          const float f = __expf(ml[(wave * S + sp) * 2] - M);
+          fm[wave * kMaxSplit + sp] = f;
+          dpart = fmaf(ml[(wave * S + sp) * 2 + 1], f, dpart);
         }
+        dpart = wave_sum(dpart);
+        if (lane == 0) den[wave] = dpart;
       }
       __syncthreads();
+      if (fast) {
+        // the S splits of one output sit in S consecutive lanes: butterfly sum within the group
 #pragma unroll
-      for (int i = 1; i < NW; ++i) {
-        if (idx[i] < 0) continue;
-        const int t = tid + (i - 1) * kPT;
-        const int eo = t / S, sp = t - eo * S;
-        const int hh = (m0 + eo) / D == hA ? 0 : 1;
-        prod[eo * S + sp] = xdec(word[i]) * fm[hh * kMaxSplit + sp];
-      }
-      __syncthreads();
-      for (int eo = tid; eo < n_out; eo += kPT) {
-        const int hh = (m0 + eo) / D == hA ? 0 : 1;
-        float a = 0.f;
-        for (int sp = 0; sp < S; ++sp) a += prod[eo * S + sp];
-        const float dd = den[hh];
-        xstore(p.xa, m0 + eo, dd > 0.f ? a / dd : 0.f, tout);
+        for (int i = 1; i < NW; ++i) {
+          const int t = tid + (i - 1) * kPT;
+          const int eo = t / S, sp = t - eo * S;
+          const int hh = (m0 + eo) / D == hA ? 0 : 1;
+          float v = idx[i] >= 0 ? xdec(word[i]) * fm[hh * kMaxSplit + sp] : 0.f;
+          for (int o = S >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+          if (idx[i] >= 0 && sp == 0) {
+            const float dd = den[hh];
+            xstore(p.xa, m0 + eo, dd > 0.f ? v / dd : 0.f, tout);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 1; i < NW; ++i) {
+          if (idx[i] < 0) continue;
+          const int t = tid + (i - 1) * kPT;
+          const int eo = t / S, sp = t - eo * S;
+          const int hh = (m0 + eo) / D == hA ? 0 : 1;
+          prod[eo * S + sp] = xdec(word[i]) * fm[hh * kMaxSplit + sp];
+        }
+        __syncthreads();
+        for (int eo = tid; eo < n_out; eo += kPT) {
+          const int hh = (m0 + eo) / D == hA ? 0 : 1;
+          float a = 0.f;
+          for (int sp = 0; sp < S; ++sp) a += prod[eo * S + sp];
+          const float dd = den[hh];
+          xstore(p.xa, m0 + eo, dd > 0.f ? a / dd : 0.f, tout);
+        }
       }
     }
 
     // ================= O + residual =================
-    stamp(p, l * 8 + 3);
+    stamp(p, l * 16 + 6);
+    PGroup<LPR_D, NB_D, RWG> gu_pre;
     {
       const int tid = phase_tid();
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
-      PGroup<LPR_D, NB_D, RWO> cur;
-      gemv_first<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, cur);
+      PGroup<LPR_D, NB_D, RWO>& cur = o_pre;
       stage_x<KD>(tid, p.xa, tout, nullptr, 0.f, s, ctl);
       if (bail) return;
-      gemv_rest<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, cur, s);
+      stamp(p, l * 16 + 7);
+      gemv_rest<LPR_D, NB_D, RWO, (RWO < 2)>(tid, Ly.o, d0, d1, cur, s);
+      // issued after this pass's own loads were waited for (waits count loads in issue order)
+      gemv_first<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, gu_pre);
       __syncthreads();
       for (int r = d0 + tid; r < d1; r += kPT) {
         const float v = s.resid[r - d0] + s.ydot[r - d0];
@@ -803,21 +838,19 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     }
 
     // ================= gate/up + SwiGLU =================
-    stamp(p, l * 8 + 4);
+    stamp(p, l * 16 + 8);
     {
       const int tid = phase_tid();
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
-      PGroup<LPR_D, NB_D, RWG> cur;
-      gemv_first<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, cur);
+      PGroup<LPR_D, NB_D, RWG>& cur = gu_pre;
       __syncthreads();
       stage_x<KD>(tid, p.xm, tout, Ly.ffn_norm, p.eps, s, ctl);
       if (bail) return;
-      stamp(p, l * 8 + 6);
-      gemv_rest<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, cur, s);
+      stamp(p, l * 16 + 9);
+      gemv_rest<LPR_D, NB_D, RWG, (RWG < 6)>(tid, Ly.gu, g0, g1, cur, s);
       __syncthreads();
-      stamp(p, l * 8 + 7);
       for (int pi = tid; 2 * pi < g1 - g0; pi += kPT) {
         const float gv = s.ydot[2 * pi], uv = s.ydot[2 * pi + 1];
         xstore(p.xf, (g0 >> 1) + pi, silu(gv) * uv, tout);
@@ -825,7 +858,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     }
 
     // ================= down + residual =================
-    stamp(p, l * 8 + 5);
+    stamp(p, l * 16 + 10);
     {
       const int tid = phase_tid();
       const int lane = tid & 63, wave = wave_of(tid);
@@ -836,7 +869,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       __syncthreads();
       stage_x<KF>(tid, p.xf, tout, nullptr, 0.f, s, ctl);
       if (bail) return;
-      gemv_rest<LPR_F, NB_F, RWF>(tid, Ly.dn, d0, d1, cur, s);
+      stamp(p, l * 16 + 11);
+      gemv_rest<LPR_F, NB_F, RWF, (RWF < 2)>(tid, Ly.dn, d0, d1, cur, s);
+      if (l + 1 < L) gemv_first<LPR_D, NB_D, RWQ>(tid, next_qkv, q0, q1, qkv_pre);
       __syncthreads();
       for (int r = d0 + tid; r < d1; r += kPT) {
         const float v = s.resid[r - d0] + s.ydot[r - d0];
@@ -847,7 +882,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   }
 
   // ================= final RMSNorm + lm_head + argmax partial =================
-  stamp(p, L * 8 + 0);
+  stamp(p, L * 16 + 0);
   const uint32_t tfin = base_tag + (uint32_t)L;  // T(L - 1)
   // ================= final RMSNorm + lm_head + argmax partial =================
   {
@@ -858,6 +893,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     __syncthreads();
     stage_x<KD>(tid, p.xx, tfin, p.final_norm, p.eps, s, ctl);
     if (bail) return;
+    stamp(p, L * 16 + 1);
     float best_v = -INFINITY;
     int best_i = 0x7fffffff;
     const Mat lm = p.lm;
@@ -865,7 +901,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int c1 = min(v1, c0 + kMaxRows);
       PGroup<LPR_D, NB_D, kLmRW> cur;
       gemv_first<LPR_D, NB_D, kLmRW>(tid, lm, c0, c1, cur);
-      gemv_rest<LPR_D, NB_D, kLmRW>(tid, lm, c0, c1, cur, s);
+      gemv_rest<LPR_D, NB_D, kLmRW, true>(tid, lm, c0, c1, cur, s);
       __syncthreads();
       for (int r = c0 + tid; r < c1; r += kPT) {
         const float v = s.ydot[r - c0];
@@ -900,7 +936,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   }
   if (w != 0) return;
   // ================= argmax over the workgroup partials (workgroup 0) =================
-  stamp(p, L * 8 + 1);
+  stamp(p, L * 16 + 2);
   {
     const int tid = phase_tid();
     const int lane = tid & 63, wave = wave_of(tid);
@@ -944,7 +980,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         if (p.argmax) p.argmax[0] = i2 == 0x7fffffff ? 0 : i2;
         p.epoch[0] = epoch + 1;  // every workgroup has read it: all have reached the final phase
       }
-      if (p.stamps != nullptr) p.stamps[L * 8 + 2] = __builtin_amdgcn_s_memrealtime();
+      if (p.stamps != nullptr) p.stamps[L * 16 + 3] = __builtin_amdgcn_s_memrealtime();
     }
   }
 }
@@ -974,7 +1010,7 @@ template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR>
 static size_t persist_lds_bytes() {
   constexpr int KD = LPR_D * NB_D * 32, KF = LPR_F * NB_F * 32;
   constexpr int KMAX = KD > KF ? KD : KF;
-  return sizeof(float) * ((size_t)KMAX + KMAX / 32 + KMAX / 4 + kMaxRows + kMaxOwn + 32 + kMrg) + sizeof(AttnLds<D, QR>);
+  return sizeof(float) * ((size_t)KMAX + KMAX / 32 + kMaxRows + kMaxOwn + 32 + kMrg) + sizeof(AttnLds<D, QR>);
 }
 
 template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF>
@@ -988,6 +1024,10 @@ static int launch_persist_t(const PersistParams& p, int nwg, hipStream_t s, bool
     return per_cu >= 1 ? 0 : -2;
   }
   PersistParams a = p;
+  if (p.plain_launch) {
+    hipLaunchKernelGGL(kern, dim3(nwg), dim3(kPT), lds, s, a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   void* args[] = {&a};
   if (hipLaunchCooperativeKernel((const void*)kern, dim3(nwg), dim3(kPT), args, lds, s) != hipSuccess) return -1;
   return 0;
@@ -1002,7 +1042,7 @@ int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, in
     return kv_dtype == 1 ? launch_persist_t<LD, ND, LF, NF, 1, DD, QR, RQ, RO, RG, RF>(p, nwg, s, query_only) \
                          : launch_persist_t<LD, ND, LF, NF, 2, DD, QR, RQ, RO, RG, RF>(p, nwg, s, query_only); \
   }
-  BW_P(4096, 12288, 64, 2, 64, 6, 128, 4, 2, 1, 2, 1)  // dense-9b: 24 / 16 / 96 / 16 rows per workgroup
+  BW_P(4096, 12288, 64, 2, 64, 6, 128, 4, 3, 2, 2, 1)  // dense-9b: 24 / 16 / 96 / 16 rows per workgroup
   BW_P(256, 1024, 8, 1, 32, 1, 64, 2, 1, 1, 1, 1)       // tiny
 #undef BW_P
   return -2;

@@ -399,6 +399,7 @@ static int persist_setup(bw_model* m) {
   p.abort_flag = (uint32_t*)ptr + 16;
   if (launch_persist_reset(p, m->n_xq, m->n_xp, m->n_xa, m->n_xd, m->n_xf, nwg, nullptr)) return fail(BW_EHIP, "persistent-step reset failed");
   HIP_OK(hipDeviceSynchronize());
+  p.plain_launch = true;  // mode 1 (see bw_set_single_launch)
   m->persist_nwg = nwg;
   m->persist_ok = true;
   return BW_OK;
@@ -1018,9 +1019,11 @@ extern "C" int bw_set_graphs(bw_model* m, int32_t enable) {
   return BW_OK;
 }
 
-extern "C" int bw_set_single_launch(bw_model* m, int32_t enable, int32_t* available) {
+extern "C" int bw_set_single_launch(bw_model* m, int32_t mode, int32_t* available) {
   if (!m) return fail(BW_EINVAL, "null model");
-  m->use_persist = enable != 0;
+  if (mode < 0 || mode > 2) return fail(BW_EINVAL, "mode must be 0, 1 or 2");
+  m->use_persist = mode != 0;
+  m->pp.plain_launch = mode != 2;
   if (available) *available = m->persist_ok ? 1 : 0;
   return BW_OK;
 }
@@ -1161,7 +1164,7 @@ extern "C" int bw_debug_read_experts(bw_model* m, int32_t n_rows, int32_t* host_
 extern "C" int bw_debug_single_launch_stamps(bw_model* m, uint64_t* stamps_dev, int32_t n) {
   if (!m) return fail(BW_EINVAL, "null model");
   if (!m->persist_ok) return fail(BW_ESTATE, "the model has no single-launch step");
-  if (stamps_dev && n < m->c.n_layers * 8 + 8) return fail(BW_ERANGE, "need %d stamps", m->c.n_layers * 8 + 8);
+  if (stamps_dev && n < m->c.n_layers * 16 + 8) return fail(BW_ERANGE, "need %d stamps", m->c.n_layers * 16 + 8);
   m->pp.stamps = stamps_dev;
   return BW_OK;
 }

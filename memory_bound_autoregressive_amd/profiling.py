@@ -58,8 +58,9 @@ def _one(path: str, kernel: str, counter: str) -> float:
     return sum(n * m for n, m in hits) / tot
 
 
-# sources of the GEMV kernels (the dominant kernel of the batch-1 step)
-GEMV_SOURCES = ("bw_gemv.hip", "bw_common.h", "bw_internal.h")
+# sources of the GEMV kernels of the kernel chain, and of the single-launch step
+GEMV_SOURCES = ("bw_gemv.hip", "bw_common.h", "bw_dot.h", "bw_internal.h")
+STEP_SOURCES = ("bw_persist.hip", "bw_common.h", "bw_dot.h", "bw_internal.h")
 
 
 def _copy(path: str, kernel: str, counter: str) -> float:
@@ -105,13 +106,15 @@ def main(argv=None) -> int:
     for a in ("--fetch", "--write", "--cal-fetch", "--cal-write", "--kernel", "--out"):
         t.add_argument(a, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--sources", default="step", choices=("step", "gemv"))
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         text = f"# {a.title}\n\nCommand:\n\n```\n{a.command}\n```\n\n{stats_table(a.csv)}\n"
     elif a.cmd == "counters":
         text = f"# {a.title}\n\nCommand:\n\n```\n{a.command}\n```\n\n{counters_table(a.csv)}\n"
     else:
-        res = traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.copy_bytes, a.kernel)
+        res = traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.copy_bytes, a.kernel,
+                      sources=STEP_SOURCES if a.sources == "step" else GEMV_SOURCES)
         with open(a.out, "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res))

@@ -78,12 +78,14 @@ def _compare(g, gam, o, where):
     return err
 
 
-@pytest.mark.parametrize("cfg,seed,gemm,single", [(configs.TINY, 1001, None, True), (configs.TINY, 1003, None, False),
-                                                  (MOE_SMALL, 1011, None, True), (configs.TINY, 1002, 1, False),
-                                                  (MOE_SMALL, 1012, 1, False)],
-                         ids=["tiny", "tiny-chain", "moe-small", "tiny-gemm", "moe-small-gemm"])
+@pytest.mark.parametrize("cfg,seed,gemm,single", [(configs.TINY, 1001, None, 1), (configs.TINY, 1004, None, 2),
+                                                  (configs.TINY, 1003, None, 0),
+                                                  (MOE_SMALL, 1011, None, 1), (configs.TINY, 1002, 1, 0),
+                                                  (MOE_SMALL, 1012, 1, 0)],
+                         ids=["tiny", "tiny-cooperative", "tiny-chain", "moe-small", "tiny-gemm", "moe-small-gemm"])
 def test_prompt_then_greedy_decode(cfg, seed, gemm, single):
-    """single: batch-1 steps as one cooperative launch (dense models); else the kernel chain.
+    """single: batch-1 steps as one launch (1: ordinary, 2: cooperative; dense models), 0: the
+    kernel chain.
     gemm = 1 runs every dense matrix of every chain step on the matrix-core GEMM path."""
     prompt_len, steps = cfg.get("prompt", 16), cfg.get("steps", 32)
     rng = np.random.default_rng(seed)
@@ -198,7 +200,10 @@ def test_batched_verify_ragged_contexts():
 
 def test_single_launch_matches_chain_over_many_steps():
     """The single-launch step and the kernel chain agree step by step on the same tokens (tiny,
-    64 positions: every page, the ragged last page, both layers)."""
+    64 positions: every page, the ragged last page, both layers). Both are fp32 evaluations of the
+    same step in different summation orders (and the single launch exchanges activations with 21
+    mantissa bits), so their difference is bounded by the sum of their distances to the exact
+    result; the bound used is a tenth of the logits tolerance against the oracle."""
     cfg, seed = configs.TINY, 1041
     rng = np.random.default_rng(seed)
     toks = rng.integers(0, cfg["vocab"], 64)
@@ -214,7 +219,7 @@ def test_single_launch_matches_chain_over_many_steps():
             ga, gb = la.cpu().numpy()[0], lb.cpu().numpy()[0]
             d = float(np.max(np.abs(ga - gb)))
             worst = max(worst, d)
-            assert d <= 1e-3, (i, d)
+            assert d <= LOGITS_MAX_ABS / 10, (i, d)
             if top2_margin(gb.astype(np.float64)) > TOKEN_MARGIN:
                 assert int(ma.cpu()[0]) == int(mb.cpu()[0]), i
         for sess in (a, b):
