@@ -143,6 +143,7 @@ struct PersistParams {
   uint32_t* abort_flag = nullptr;
   uint64_t deadline_ticks = 50000000ull;  // one wait gives up after 0.5 s (100 MHz counter)
   uint64_t* stamps = nullptr;       // optional [L * 16 + 8]: real-time counter at phase starts (workgroup 0)
+  int32_t stamp_stride = 0;         // > 0: every workgroup w writes its own record at w * stamp_stride
   bool plain_launch = false;        // ordinary launch instead of the cooperative one (see the runtime)
 };
 

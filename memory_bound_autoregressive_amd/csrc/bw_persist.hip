@@ -49,6 +49,7 @@ constexpr int kPW = kPT / kWave;   // waves per workgroup
 constexpr uint32_t kRsrc3 = 0x00020000u;
 constexpr int kCohSC1 = 16;        // cache policy: coherent across the XCD L2s
 constexpr float kNoScore = -1.0e30f;               // running max of a split without positions
+constexpr int kOOB = 0x7FFFFFF0;  // buffer offset past every buffer: the load returns zero, touches nothing
 
 // ---- exchange words ---------------------------------------------------------------------------
 
@@ -76,11 +77,18 @@ struct Ctl {
   uint64_t deadline; // ticks of the 100 MHz real-time counter one wait may take
 };
 
-// true when this wait must give up: the step was aborted elsewhere or the deadline passed
-__device__ __forceinline__ bool give_up(Ctl& c) {
+// The abort flag as a coherent buffer load, issued in the same batch as a wait's reloads so that
+// one memory round trip serves both.
+__device__ __forceinline__ uint32_t load_abort(const Ctl& c) {
+  return __builtin_amdgcn_raw_buffer_load_b32(__builtin_amdgcn_make_buffer_rsrc(c.abort_flag, 0, 4, kRsrc3), 0, 0,
+                                              kCohSC1);
+}
+
+// true when this wait must give up: the step was aborted elsewhere (flag: the abort flag as last
+// loaded) or the deadline passed
+__device__ __forceinline__ bool give_up(Ctl& c, uint32_t flag) {
   if (*c.bail) return true;
-  if (__hip_atomic_load(c.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-      __builtin_amdgcn_s_memrealtime() - c.t0 > c.deadline) {
+  if (flag != 0u || __builtin_amdgcn_s_memrealtime() - c.t0 > c.deadline) {
     atomicOr(c.err, BW_DERR_PERSIST_BIT);
     __hip_atomic_store(c.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *c.bail = 1;
@@ -89,52 +97,37 @@ __device__ __forceinline__ bool give_up(Ctl& c) {
   return false;
 }
 
-// Wait until n words of buf (starting at word 0) all carry tag; this thread covers 16-byte chunks
-// tid, tid + kPT, ... (PER of them). n is a multiple of 4.
-template <int PER>
-__device__ __forceinline__ void poll_chunks(int tid, __amdgpu_buffer_rsrc_t r, int n4, uint32_t tag, u32x4 (&v)[PER],
-                                            Ctl& c) {
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int q = tid + i * kPT;
-    v[i] = q < n4 ? xload4(r, q) : u32x4{tag, tag, tag, tag};
-  }
-  c.t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
-    bool all = true;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) all &= xok(v[i][k], tag);
-    if (all || give_up(c)) return;
-    __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      bool ok = true;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) ok &= xok(v[i][k], tag);
-      const int q = tid + i * kPT;
-      if (!ok && q < n4) v[i] = xload4(r, q);
-    }
-  }
-}
-
-// Wait for up to N words (idx[i] < 0: unused); all loads are issued before the first check
+// Waits on up to N words (idx[i] < 0: unused) in two parts: poll_words_issue loads every word
+// once (unconditionally; an unused slot reads zero past the buffer), the caller may then issue its
+// weight loads, and poll_words_wait checks the first results outside the retry loop, so that
+// check waits for the word loads only, not for weight loads issued after them.
 template <int N>
-__device__ __forceinline__ void poll_words(__amdgpu_buffer_rsrc_t r, const int (&idx)[N], uint32_t tag, uint32_t (&w)[N],
-                                           Ctl& c) {
+__device__ __forceinline__ void poll_words_issue(__amdgpu_buffer_rsrc_t r, const int (&idx)[N], uint32_t (&w)[N]) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) w[i] = idx[i] >= 0 ? xload1(r, idx[i]) : tag;
+  for (int i = 0; i < N; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, idx[i] >= 0 ? idx[i] * 4 : kOOB, 0, kCohSC1);
+}
+template <int N>
+__device__ __forceinline__ void poll_words_wait(__amdgpu_buffer_rsrc_t r, const int (&idx)[N], uint32_t tag, uint32_t (&w)[N],
+                                                Ctl& c) {
   c.t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
-    bool all = true;
+  bool all = true;
 #pragma unroll
-    for (int i = 0; i < N; ++i) all &= xok(w[i], tag);
-    if (all || give_up(c)) return;
+  for (int i = 0; i < N; ++i) all &= idx[i] < 0 || xok(w[i], tag);
+  uint32_t flag = 0u;
+  while (!all && !give_up(c, flag)) {
     __builtin_amdgcn_s_sleep(1);
+    flag = load_abort(c);
+    // branch-free reloads (a word already seen reads past the buffer), so they all go out
+    // before the one wait below
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-      if (!xok(w[i], tag) && idx[i] >= 0) w[i] = xload1(r, idx[i]);
+    for (int i = 0; i < N; ++i) {
+      const bool need = idx[i] >= 0 && !xok(w[i], tag);
+      const uint32_t nw = __builtin_amdgcn_raw_buffer_load_b32(r, need ? idx[i] * 4 : kOOB, 0, kCohSC1);
+      w[i] = need ? nw : w[i];
+    }
+    all = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) all &= idx[i] < 0 || xok(w[i], tag);
   }
 }
 
@@ -162,9 +155,11 @@ __device__ __forceinline__ T load_uniform(const T* src) {
   return r;
 }
 
-// measurement hook: workgroup 0 records the real-time counter at a phase start
+// measurement hook: workgroup 0 (or every workgroup, at its own record) stores the real-time
+// counter at a phase start
 __device__ __forceinline__ void stamp(const PersistParams& p, int idx) {
-  if (p.stamps != nullptr && blockIdx.x == 0 && threadIdx.x == 0) p.stamps[idx] = __builtin_amdgcn_s_memrealtime();
+  if (p.stamps != nullptr && threadIdx.x == 0 && (p.stamp_stride > 0 || blockIdx.x == 0))
+    p.stamps[(int64_t)blockIdx.x * p.stamp_stride + idx] = __builtin_amdgcn_s_memrealtime();
 }
 
 // ---- LDS layout ---------------------------------------------------------------------------------
@@ -176,31 +171,88 @@ struct Lds {
   float* resid;  // exact residual rows owned by this workgroup [kMaxOwn]
   float* red;    // reduction scratch [32]
   float* mrg;    // merge scratch [kMrg]
+  int* pgid;     // page ids of this workgroup's attention split [kMaxSplitPages]
   float* att;    // attention scratch
 };
 constexpr int kMaxRows = 1024;  // rows per workgroup per phase held in ydot
 #ifndef BW_LM_RW
-#define BW_LM_RW 2
+#define BW_LM_RW 4
 #endif
 constexpr int kLmRW = BW_LM_RW;  // row steps per group of the lm_head pass
 constexpr int kMaxOwn = 64;     // residual rows per workgroup
+constexpr int kMaxSplitPages = 256;  // pages of one attention split (workgroup)
 constexpr int kMaxSplit = kPT / 4;  // attention splits per KV head (workgroups / KV heads)
 constexpr int kMrgProd = 2048;      // (attention output, split) products per workgroup
 // merge scratch: (m, l) of [2 heads][splits], factors [2][splits], denominators [2], products
 constexpr int kMrg = 4 * kMaxSplit + 2 * kMaxSplit + 8 + kMrgProd;
 
 // ---- staging of a GEMV input from the exchange ------------------------------------------------
-// xs gets the K values (times the RMSNorm factor and gain when gamma != nullptr), bs the per-block
-// sums. The caller synchronises before and after.
+// xs gets the K values (times the RMSNorm factor and gain when NORM), bs the per-block sums.
+// stage_issue loads every chunk once (and the gain), the caller then issues the phase's first
+// weight loads, and stage_finish waits (its first check needs only the chunk loads: waits count
+// loads in issue order), normalises and stores. The caller synchronises before stage_issue's
+// data is used by other threads' previous phase; stage_finish ends with a barrier.
 template <int K>
-__device__ __forceinline__ void stage_x(int tid, const uint32_t* xin, uint32_t tag, const uint16_t* gamma, float eps,
-                                        Lds& s, Ctl& c) {
-  constexpr int N4 = K / 4;
-  constexpr int PER = (N4 + kPT - 1) / kPT;
+struct XStage {
+  static constexpr int N4 = K / 4, PER = (N4 + kPT - 1) / kPT;
   u32x4 v[PER];
-  poll_chunks<PER>(tid, xrsrc(xin, (int64_t)K * 4), N4, tag, v, c);
+  uint32_t g[PER][2];
+};
+
+template <int K, bool NORM>
+__device__ __forceinline__ void stage_issue(int tid, const uint32_t* xin, const uint16_t* gamma, XStage<K>& x) {
+  using X = XStage<K>;
+  const __amdgpu_buffer_rsrc_t r = xrsrc(xin, (int64_t)K * 4);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc((void*)gamma, 0, K * 2, kRsrc3);
+#pragma unroll
+  for (int i = 0; i < X::PER; ++i) {
+    const int q = tid + i * kPT;
+    if constexpr (NORM) {
+      const auto gv = __builtin_amdgcn_raw_buffer_load_b64(rg, q < X::N4 ? q * 8 : kOOB, 0, 0);
+      x.g[i][0] = gv[0];
+      x.g[i][1] = gv[1];
+    }
+    x.v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, q < X::N4 ? q * 16 : kOOB, 0, kCohSC1);
+  }
+}
+
+template <int K, bool NORM>
+__device__ __forceinline__ void stage_finish(int tid, const uint32_t* xin, uint32_t tag, float eps, XStage<K>& x, Lds& s,
+                                             Ctl& c) {
+  using X = XStage<K>;
+  constexpr int N4 = X::N4, PER = X::PER;
+  auto& v = x.v;
+  {
+    const __amdgpu_buffer_rsrc_t r = xrsrc(xin, (int64_t)K * 4);
+    c.t0 = __builtin_amdgcn_s_memrealtime();
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) all &= tid + i * kPT >= N4 || xok(v[i][k], tag);
+    uint32_t flag = 0u;
+    while (!all && !give_up(c, flag)) {
+      __builtin_amdgcn_s_sleep(1);
+      flag = load_abort(c);
+      all = true;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {  // branch-free, as in poll_words_wait
+        const int q = tid + i * kPT;
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ok &= xok(v[i][k], tag);
+        ok = ok || q >= N4;
+        const u32x4 nv = __builtin_amdgcn_raw_buffer_load_b128(r, ok ? kOOB : q * 16, 0, kCohSC1);
+        v[i] = ok ? v[i] : nv;
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) all &= tid + i * kPT >= N4 || xok(v[i][k], tag);
+    }
+  }
   float scale = 1.f;
-  if (gamma != nullptr) {
+  if constexpr (NORM) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
@@ -221,21 +273,41 @@ __device__ __forceinline__ void stage_x(int tid, const uint32_t* xin, uint32_t t
     const bool in = q < N4;
     const int k = 4 * q;
     float4 f = make_float4(xdec(v[i][0]), xdec(v[i][1]), xdec(v[i][2]), xdec(v[i][3]));
-    if (in && gamma != nullptr) {
-      const uint2 gh = *(const uint2*)(gamma + k);
-      f.x *= scale * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
-      f.y *= scale * f16_to_f32((uint16_t)(gh.x >> 16));
-      f.z *= scale * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
-      f.w *= scale * f16_to_f32((uint16_t)(gh.y >> 16));
+    if constexpr (NORM) {
+      f.x *= scale * f16_to_f32((uint16_t)(x.g[i][0] & 0xFFFFu));
+      f.y *= scale * f16_to_f32((uint16_t)(x.g[i][0] >> 16));
+      f.z *= scale * f16_to_f32((uint16_t)(x.g[i][1] & 0xFFFFu));
+      f.w *= scale * f16_to_f32((uint16_t)(x.g[i][1] >> 16));
     }
-    if (in) *(float4*)xs_chunk(s.xs, k >> 5, (k & 31) >> 2) = f;
     float cs = in ? (f.x + f.y) + (f.z + f.w) : 0.f;
+    // elements 16..31 of a block pair with the high nibbles, which block_dot_hs reads 16x too large
+    if ((k & 31) >= 16) f = make_float4(f.x * 0.0625f, f.y * 0.0625f, f.z * 0.0625f, f.w * 0.0625f);
+    if (in) *(float4*)xs_chunk(s.xs, k >> 5, (k & 31) >> 2) = f;
     cs += __shfl_xor(cs, 1);
     cs += __shfl_xor(cs, 2);
     cs += __shfl_xor(cs, 4);
     if (in && (q & 7) == 0) s.bs[q >> 3] = cs;
   }
   __syncthreads();
+}
+
+// ---- block dot product on high-nibble-scaled x ------------------------------------------------
+// As block_dot (bw_dot.h), with one AND fewer per code pair: the high nibbles are masked in place
+// ((w >> s) & 0x00F000F0 reads as two fp16 subnormals 16 q 2^-24, exact), and the x values they
+// pair with (elements 16..31 of the block) were staged divided by 16 (exact), so every product is
+// still q x 2^-24. Per code dword: one shift and four ANDs for eight codes.
+__device__ __forceinline__ float block_dot_hs(u32x4 q, const float4* xv, float bsum) {
+  float d = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w = q[k], w8 = q[k] >> 8;
+    const float4 lo = xv[k], hi = xv[4 + k];
+    d = mix2(w & 0x000F000Fu, lo.x, lo.z, d);    // elements 4k, 4k+2
+    d = mix2(w & 0x00F000F0u, hi.x, hi.z, d);    // elements 16+4k, 16+4k+2 (x / 16)
+    d = mix2(w8 & 0x000F000Fu, lo.y, lo.w, d);   // elements 4k+1, 4k+3
+    d = mix2(w8 & 0x00F000F0u, hi.y, hi.w, d);   // elements 16+4k+1, 16+4k+3 (x / 16)
+  }
+  return fmaf(16777216.0f, d, -8.0f * bsum);
 }
 
 // ---- GEMV over a row range --------------------------------------------------------------------
@@ -252,7 +324,6 @@ struct PGroup {
 // under a branch (and none through a flat pointer, which would also count against the LDS wait
 // counter) the compiler's wait counts stay exact: computing a group waits for that group's loads
 // only, while the next group's are in flight.
-constexpr int kOOB = 0x7FFFFFF0;  // byte offset past every matrix
 constexpr int kNT = 2;            // cache policy: non-temporal (each weight is read once per step)
 
 template <int LPR, int NB, int RW>
@@ -290,7 +361,7 @@ __device__ __forceinline__ void pcompute(int tid, const PGroup<LPR, NB, RW>& g, 
     for (int k = 0; k < 8; ++k) xb[k] = *(const float4*)xs_chunk(s.xs, b, k);
     const float sb = s.bs[b];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) acc[r] = fmaf(f16_to_f32(g.sc[r][c]), block_dot(g.q[r][c], xb, sb), acc[r]);
+    for (int r = 0; r < RW; ++r) acc[r] = fmaf(f16_to_f32(g.sc[r][c]), block_dot_hs(g.q[r][c], xb, sb), acc[r]);
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
@@ -349,6 +420,34 @@ __device__ __forceinline__ void unpack8p(u32x4 v, float* out) {
   }
 }
 
+// K and V of one page for KV head g, as buffer loads on the layer's pool slice (an invalid page id
+// reads zeros without touching memory). Lane layout as in the chain's attention kernel: scores use
+// 8 tokens x 8 lanes per pass (2 passes), values 4 token groups x 16 lanes.
+template <int D>
+struct PageRegs {
+  static constexpr int DL = D / 8, NV = D / 8, TG = kWave / NV, TPL = kPageTokens / TG, NCH = DL / 8;
+  u32x4 k[2][NCH];
+  u32x4 v[TPL];
+};
+
+template <int D>
+__device__ __forceinline__ void load_page(int lane, __amdgpu_buffer_rsrc_t pool, int64_t page_elems, int n_pages,
+                                          int page, int g, PageRegs<D>& pr) {
+  using PR = PageRegs<D>;
+  const int sc_tok = lane >> 3, sc_c = lane & 7, v_c = lane % PR::NV, v_tg = lane / PR::NV;
+  const bool ok = page >= 0 && page < n_pages;
+  const int kb = ok ? (int)(((int64_t)page * page_elems + (int64_t)(g * 2) * kPageTokens * D) * 2) : kOOB;
+  const int vb = ok ? kb + kPageTokens * D * 2 : kOOB;
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+    for (int ch = 0; ch < PR::NCH; ++ch)
+      pr.k[ps][ch] = __builtin_amdgcn_raw_buffer_load_b128(pool, ok ? kb + ((ps * 8 + sc_tok) * D + sc_c * PR::DL + ch * 8) * 2 : kOOB, 0, 0);
+#pragma unroll
+  for (int u = 0; u < PR::TPL; ++u)
+    pr.v[u] = __builtin_amdgcn_raw_buffer_load_b128(pool, ok ? vb + ((v_tg + u * PR::TG) * D + v_c * 8) * 2 : kOOB, 0, 0);
+}
+
 // 16-byte chunk of the new token's key or value (cache dtype bits staged in LDS)
 __device__ __forceinline__ u32x4 lds_chunk16(const uint16_t* bits, int d0) {
   return *(const u32x4*)(bits + d0);
@@ -384,7 +483,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   s.resid = s.ydot + kMaxRows;
   s.red = s.resid + kMaxOwn;
   s.mrg = s.red + 32;
-  s.att = s.mrg + kMrg;
+  s.pgid = reinterpret_cast<int*>(s.mrg + kMrg);
+  s.att = s.mrg + kMrg + kMaxSplitPages;
   AttnLds<D, QR>& al = *reinterpret_cast<AttnLds<D, QR>*>(s.att);
 
   const int nwg = gridDim.x, w = blockIdx.x;
@@ -441,19 +541,49 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   }
   if (!pos_ok && threadIdx.x == 0 && w == 0) atomicOr(p.err, 4);
 
-  // First weight groups of a phase are issued one phase early where registers allow: QKV's during
-  // the previous layer's down pass, O's during the merge, gate/up's during O.
-  PGroup<LPR_D, NB_D, RWQ> qkv_pre;
-  gemv_first<LPR_D, NB_D, RWQ>(phase_tid(), load_uniform(p.layers).qkv, q0, q1, qkv_pre);
+  // This workgroup's attention split: pages [apg0, apg1) of KV head ag (the same for every layer).
+  // Each wave's first page id is read once per step; its K/V are loaded during each layer's QKV pass.
+  int apg0, apg1, first_page;
+  {
+    int n_pg = (kv_len + kPageTokens - 1) / kPageTokens;
+    n_pg = max(0, min(n_pg, p.max_pages));
+    const int pps = (n_pg + S - 1) / S;
+    apg0 = ag < G ? as * pps : 0;
+    apg1 = ag < G ? min(n_pg, apg0 + pps) : 0;
+    const int tid = phase_tid();
+    for (int i = tid; i < apg1 - apg0 && i < kMaxSplitPages; i += kPT) s.pgid[i] = p.page_table[apg0 + i];
+    __syncthreads();
+    const int pg = apg0 + wave_of(tid);
+    first_page = pg < apg1 ? s.pgid[pg - apg0] : -1;
+  }
+
+  // Per-step constants of the QKV epilogue, read before any weight is in flight: the new token's
+  // page and the RoPE factors of this thread's row pair (at most one pair per thread).
+  const int page_new = pos_ok ? __builtin_amdgcn_readfirstlane(p.page_table[pos / kPageTokens]) : -1;
+  float2 rope_cs = make_float2(1.f, 0.f);
+  {
+    const int tid = phase_tid();
+    const int dr = q0 + 2 * tid;
+    if (pos_ok && dr < q1 && dr < HD + GD) {
+      const int local = dr < HD ? dr : dr - HD;
+      const int i = (local % D) >> 1;
+      rope_cs = p.rope[(int64_t)pos * (D >> 1) + i];
+    }
+  }
+
+  // Each phase issues its input loads first, then its first weight group, then waits for the
+  // input (O's weights go out during the merge, whose input loads precede them the same way).
 
   for (int l = 0; l < L; ++l) {
     // this layer's descriptors, read once with scalar loads (the table is constant for the step),
     // so the matrix pointers are uniform registers and the loops below never re-read them
     const PLayer Ly = load_uniform(p.layers + l);
-    const Mat next_qkv = load_uniform(&p.layers[l + 1 < L ? l + 1 : l].qkv);
     const uint32_t tin = base_tag + (uint32_t)l;       // T(l - 1)
     const uint32_t tout = base_tag + (uint32_t)l + 1;  // T(l)
     uint16_t* pool = p.pool + (int64_t)l * p.layer_elems;
+    const __amdgpu_buffer_rsrc_t pool_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)pool, 0, (int)min<int64_t>(p.layer_elems * 2, 0x7FFFFFF0), kRsrc3);
+    PageRegs<D> kv_first;
 
     // ================= QKV =================
     stamp(p, l * 16 + 0);
@@ -462,52 +592,57 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
-      PGroup<LPR_D, NB_D, RWQ>& cur = qkv_pre;
+      XStage<KD> xin;
+      stage_issue<KD, true>(tid, p.xx, Ly.attn_norm, xin);
+      PGroup<LPR_D, NB_D, RWQ> cur;
+      gemv_first<LPR_D, NB_D, RWQ>(tid, Ly.qkv, q0, q1, cur);
       __syncthreads();
-      stage_x<KD>(tid, p.xx, tin, Ly.attn_norm, p.eps, s, ctl);
+      stage_finish<KD, true>(tid, p.xx, tin, p.eps, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 1);
+      // this layer's first attention page, after the input wait (waits count loads in issue
+      // order): its id is known, only the new token's slot changes in this step, and that slot
+      // is taken from the exchange
+      load_page<D>(lane, pool_rs, p.page_elems, p.n_pages, first_page, ag, kv_first);
       gemv_rest<LPR_D, NB_D, RWQ, (RWQ < 3)>(tid, Ly.qkv, q0, q1, cur, s);
       __syncthreads();
-      const int page = pos_ok ? p.page_table[pos / kPageTokens] : -1;
-      for (int pi = tid; 2 * pi < q1 - q0; pi += kPT) {
-        const int dr = q0 + 2 * pi;
+      if (2 * tid < q1 - q0) {
+        // one RoPE pair (q, k) or two adjacent value dims per thread; k and v are rounded to the
+        // cache dtype, stored in the pool and exchanged as the rounded values
+        const int pi = tid, dr = q0 + 2 * pi;
         const float a = s.ydot[2 * pi], b = s.ydot[2 * pi + 1];
-        int head, dd0, dd1, which;
+        const bool is_v = dr >= HD + GD;
+        const int local = dr < HD ? dr : (is_v ? dr - HD - GD : dr - HD);
+        const int head = local / D;
+        int dd0, dd1;
         float o0 = a, o1 = b;
-        if (dr < HD + GD) {
-          const int local = dr < HD ? dr : dr - HD;
-          head = local / D;
+        if (!is_v) {
           const int i = (local - head * D) >> 1;
-          const float2 cs = pos_ok ? p.rope[(int64_t)pos * (D >> 1) + i] : make_float2(1.f, 0.f);
-          o0 = a * cs.x - b * cs.y;
-          o1 = a * cs.y + b * cs.x;
+          o0 = a * rope_cs.x - b * rope_cs.y;
+          o1 = a * rope_cs.y + b * rope_cs.x;
           dd0 = i;
           dd1 = i + (D >> 1);
-          which = 0;
-          if (dr < HD) {
-            xstore(p.xq, head * D + dd0, o0, tout);
-            xstore(p.xq, head * D + dd1, o1, tout);
-            continue;
-          }
         } else {
-          const int local = dr - HD - GD;
-          head = local / D;
           dd0 = local - head * D;
           dd1 = dd0 + 1;
-          which = 1;
         }
-        const uint16_t k0 = f32_to_kv<KVDT>(o0), k1 = f32_to_kv<KVDT>(o1);
-        const int xb = HD + which * GD + head * D;
-        xstore(p.xq, xb + dd0, kv_to_f32<KVDT>(k0), tout);
-        xstore(p.xq, xb + dd1, kv_to_f32<KVDT>(k1), tout);
-        if (page >= 0 && page < p.n_pages) {
-          uint16_t* dst = pool + (int64_t)page * p.page_elems +
-                          ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D;
-          dst[dd0] = k0;
-          dst[dd1] = k1;
-        } else if (pos_ok) {
-          atomicOr(p.err, 1);
+        if (dr < HD) {
+          xstore(p.xq, head * D + dd0, o0, tout);
+          xstore(p.xq, head * D + dd1, o1, tout);
+        } else {
+          const int which = is_v ? 1 : 0;
+          const uint16_t k0 = f32_to_kv<KVDT>(o0), k1 = f32_to_kv<KVDT>(o1);
+          const int xb = HD + which * GD + head * D;
+          xstore(p.xq, xb + dd0, kv_to_f32<KVDT>(k0), tout);
+          xstore(p.xq, xb + dd1, kv_to_f32<KVDT>(k1), tout);
+          if (page_new >= 0 && page_new < p.n_pages) {
+            uint16_t* dst = pool + (int64_t)page_new * p.page_elems +
+                            ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D;
+            dst[dd0] = k0;
+            dst[dd1] = k1;
+          } else if (pos_ok) {
+            atomicOr(p.err, 1);
+          }
         }
       }
     }
@@ -521,31 +656,14 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       (void)wave;
       constexpr int DL = D / 8, NV = D / 8, TG = kWave / NV, TPL = kPageTokens / TG, NCH = DL / 8;
       const int rep = H / G;
-      int n_pg = (kv_len + kPageTokens - 1) / kPageTokens;
-      n_pg = min(n_pg, p.max_pages);
-      const int pps = (n_pg + S - 1) / S;
       const bool active = ag < G;
-      const int pg0 = active ? as * pps : 0;
-      const int pg1 = active ? min(n_pg, pg0 + pps) : 0;
+      const int pg0 = apg0, pg1 = apg1;
       const int pg_new = pos / kPageTokens, slot_new = pos % kPageTokens;
       const int sc_tok = lane >> 3, sc_c = lane & 7, v_c = lane % NV, v_tg = lane / NV;
-      // first page's id and data go out before the wait for q
       int pg = pg0 + wave;
-      int page = (pg < pg1) ? p.page_table[pg] : -1;
-      u32x4 kraw[2][NCH], vraw[TPL];
-      auto load_page = [&](int pid) {
-        const bool ok = pid >= 0 && pid < p.n_pages;
-        const uint16_t* kb = pool + (int64_t)(ok ? pid : 0) * p.page_elems + (int64_t)(ag * 2) * kPageTokens * D;
-        const uint16_t* vb = kb + kPageTokens * D;
-#pragma unroll
-        for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch)
-            kraw[ps][ch] = ok ? *(const u32x4*)(kb + (ps * 8 + sc_tok) * D + sc_c * DL + ch * 8) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < TPL; ++u) vraw[u] = ok ? *(const u32x4*)(vb + (v_tg + u * TG) * D + v_c * 8) : u32x4{0, 0, 0, 0};
-      };
-      if (active && pg < pg1) load_page(page);
+      int page = first_page;
+      u32x4 (&kraw)[2][NCH] = kv_first.k;
+      u32x4 (&vraw)[TPL] = kv_first.v;
       // q rows of this KV head and the new key / value
       if (active) {
         const __amdgpu_buffer_rsrc_t r = xrsrc(p.xq, (int64_t)Nq * 4);
@@ -565,8 +683,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
             idx[i] = -1;
           }
         }
-        poll_words<NQW>(r, idx, tout, word, ctl);
-        stamp(p, l * 16 + 3);
+        poll_words_issue<NQW>(r, idx, word);
+        poll_words_wait<NQW>(r, idx, tout, word, ctl);
 #pragma unroll
         for (int i = 0; i < NQW; ++i) {
           const int e = tid + i * kPT;
@@ -581,6 +699,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         }
       }
       __syncthreads();
+      stamp(p, l * 16 + 3);
       if (bail) return;
       float mrun[QR], lrun[QR], acc[QR][8];
 #pragma unroll
@@ -594,7 +713,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         const bool valid = page >= 0 && page < p.n_pages;
         if (!valid && lane == 0) atomicOr(p.err, 1);
         const int pgn = pg + kPW;
-        const int page_n = pgn < pg1 ? p.page_table[pgn] : -1;
+        const int page_n = pgn < pg1 ? s.pgid[pgn - pg0] : -1;
         if (pg == pg_new) {  // the new token's slot comes from the exchange
 #pragma unroll
           for (int ps = 0; ps < 2; ++ps)
@@ -672,8 +791,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           __builtin_amdgcn_wave_barrier();
         }
         page = page_n;
-        if (pgn < pg1) load_page(page);
+        load_page<D>(lane, pool_rs, p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
       }
+      stamp(p, l * 16 + 12);
       // reduce the value partials over the token groups, then merge the waves
 #pragma unroll
       for (int qr = 0; qr < QR; ++qr)
@@ -695,6 +815,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         }
       }
       __syncthreads();
+      stamp(p, l * 16 + 13);
       if (active) {
         for (int e = tid; e < QR * D; e += kPT) {
           const int qr = e / D, dd = e - qr * D;
@@ -729,7 +850,6 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
-      gemv_first<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, o_pre);
       // The range covers at most two heads (m1 - m0 <= D). Thread t first waits for one (m, l)
       // word and for the acc words of (output, split) pairs t, t + kPT, ... (at most kMrgProd).
       const __amdgpu_buffer_rsrc_t r = xrsrc(p.xp, (int64_t)H * S * (D + 2) * 4);
@@ -759,10 +879,12 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           idx[i] = -1;
         }
       }
-      poll_words<NW>(r, idx, tout, word, ctl);
-      stamp(p, l * 16 + 5);
+      poll_words_issue<NW>(r, idx, word);
+      gemv_first<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, o_pre);
+      poll_words_wait<NW>(r, idx, tout, word, ctl);
       if (idx[0] >= 0) ml[tid] = xdec(word[0]);
       __syncthreads();
+      stamp(p, l * 16 + 5);
       if (bail) return;
       // per head: max over splits, factors, denominator (fixed-order reductions: deterministic)
       const bool fast = S <= kWave && (S & (S - 1)) == 0;
@@ -816,19 +938,18 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
 
     // ================= O + residual =================
     stamp(p, l * 16 + 6);
-    PGroup<LPR_D, NB_D, RWG> gu_pre;
     {
       const int tid = phase_tid();
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
       PGroup<LPR_D, NB_D, RWO>& cur = o_pre;
-      stage_x<KD>(tid, p.xa, tout, nullptr, 0.f, s, ctl);
+      XStage<KD> xin;
+      stage_issue<KD, false>(tid, p.xa, nullptr, xin);
+      stage_finish<KD, false>(tid, p.xa, tout, 0.f, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 7);
       gemv_rest<LPR_D, NB_D, RWO, (RWO < 2)>(tid, Ly.o, d0, d1, cur, s);
-      // issued after this pass's own loads were waited for (waits count loads in issue order)
-      gemv_first<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, gu_pre);
       __syncthreads();
       for (int r = d0 + tid; r < d1; r += kPT) {
         const float v = s.resid[r - d0] + s.ydot[r - d0];
@@ -844,9 +965,12 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
-      PGroup<LPR_D, NB_D, RWG>& cur = gu_pre;
+      XStage<KD> xin;
+      stage_issue<KD, true>(tid, p.xm, Ly.ffn_norm, xin);
+      PGroup<LPR_D, NB_D, RWG> cur;
+      gemv_first<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, cur);
       __syncthreads();
-      stage_x<KD>(tid, p.xm, tout, Ly.ffn_norm, p.eps, s, ctl);
+      stage_finish<KD, true>(tid, p.xm, tout, p.eps, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 9);
       gemv_rest<LPR_D, NB_D, RWG, (RWG < 6)>(tid, Ly.gu, g0, g1, cur, s);
@@ -864,14 +988,15 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
+      XStage<KF> xin;
+      stage_issue<KF, false>(tid, p.xf, nullptr, xin);
       PGroup<LPR_F, NB_F, RWF> cur;
       gemv_first<LPR_F, NB_F, RWF>(tid, Ly.dn, d0, d1, cur);
       __syncthreads();
-      stage_x<KF>(tid, p.xf, tout, nullptr, 0.f, s, ctl);
+      stage_finish<KF, false>(tid, p.xf, tout, 0.f, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 11);
       gemv_rest<LPR_F, NB_F, RWF, (RWF < 2)>(tid, Ly.dn, d0, d1, cur, s);
-      if (l + 1 < L) gemv_first<LPR_D, NB_D, RWQ>(tid, next_qkv, q0, q1, qkv_pre);
       __syncthreads();
       for (int r = d0 + tid; r < d1; r += kPT) {
         const float v = s.resid[r - d0] + s.ydot[r - d0];
@@ -890,8 +1015,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     const int lane = tid & 63, wave = wave_of(tid);
     (void)lane;
     (void)wave;
+    XStage<KD> xin;
+    stage_issue<KD, true>(tid, p.xx, p.final_norm, xin);
     __syncthreads();
-    stage_x<KD>(tid, p.xx, tfin, p.final_norm, p.eps, s, ctl);
+    stage_finish<KD, true>(tid, p.xx, tfin, p.eps, xin, s, ctl);
     if (bail) return;
     stamp(p, L * 16 + 1);
     float best_v = -INFINITY;
@@ -948,7 +1075,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       uint64_t word = __hip_atomic_load(p.xarg + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ctl.t0 = __builtin_amdgcn_s_memrealtime();
       while ((uint32_t)(word >> 62) != (epoch & 3u)) {
-        if (give_up(ctl)) break;
+        if (give_up(ctl, __hip_atomic_load(ctl.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) break;
         __builtin_amdgcn_s_sleep(1);
         word = __hip_atomic_load(p.xarg + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -1010,7 +1137,8 @@ template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR>
 static size_t persist_lds_bytes() {
   constexpr int KD = LPR_D * NB_D * 32, KF = LPR_F * NB_F * 32;
   constexpr int KMAX = KD > KF ? KD : KF;
-  return sizeof(float) * ((size_t)KMAX + KMAX / 32 + kMaxRows + kMaxOwn + 32 + kMrg) + sizeof(AttnLds<D, QR>);
+  return sizeof(float) * ((size_t)KMAX + KMAX / 32 + kMaxRows + kMaxOwn + 32 + kMrg + kMaxSplitPages) +
+         sizeof(AttnLds<D, QR>);
 }
 
 template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF>

@@ -967,6 +967,10 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
     p.logits = logits_out;
     p.argmax = argmax_out;
     const auto& c = m->c;
+    // one attention split's pages are held in LDS (256 ids)
+    const int splits = m->persist_nwg / c.n_kv_heads;
+    if ((max_pages + splits - 1) / splits > 256)
+      return fail(BW_ERANGE, "max_pages %d is beyond the single-launch step (at most %d)", max_pages, 256 * splits);
     if (launch_persist(p, c.d_model, c.ffn_dim, c.kv_dtype, c.head_dim, c.n_q_heads / c.n_kv_heads, m->persist_nwg, s,
                        false))
       return fail(BW_EHIP, "single-launch step failed to launch");
@@ -1164,8 +1168,10 @@ extern "C" int bw_debug_read_experts(bw_model* m, int32_t n_rows, int32_t* host_
 extern "C" int bw_debug_single_launch_stamps(bw_model* m, uint64_t* stamps_dev, int32_t n) {
   if (!m) return fail(BW_EINVAL, "null model");
   if (!m->persist_ok) return fail(BW_ESTATE, "the model has no single-launch step");
-  if (stamps_dev && n < m->c.n_layers * 16 + 8) return fail(BW_ERANGE, "need %d stamps", m->c.n_layers * 16 + 8);
+  const int rec = m->c.n_layers * 16 + 8;
+  if (stamps_dev && n < rec) return fail(BW_ERANGE, "need %d stamps", rec);
   m->pp.stamps = stamps_dev;
+  m->pp.stamp_stride = stamps_dev && (int64_t)n >= (int64_t)rec * m->persist_nwg ? rec : 0;
   return BW_OK;
 }
 
