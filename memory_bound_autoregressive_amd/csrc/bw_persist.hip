@@ -69,6 +69,59 @@ __device__ __forceinline__ void xstore(uint32_t* base, int idx, float v, uint32_
   __hip_atomic_store(base + idx, xenc(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- cross-lane steps without the LDS crossbar -------------------------------------------------
+// DPP moves within a row of 16 lanes and the row / half-wave swaps of gfx950. Each reduction
+// combines (lane, partner) in the same order on both lanes, so all lanes of a group agree.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over each aligned group of 8 lanes (xor 1, xor 2, then the mirror within the half row)
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  return v + dpp_mov<0x141>(v);  // row_half_mirror
+}
+// the value of lane ^ 8 (rotation by 8 within the row of 16)
+__device__ __forceinline__ float xor8(float v) { return dpp_mov<0x128>(v); }
+// (v of the even row, v of the odd row) of each pair of 16-lane rows (0, 1), (2, 3)
+__device__ __forceinline__ float2 pair16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// (v of lanes 0..31, v of lanes 32..63), paired lane by lane
+__device__ __forceinline__ float2 pair32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) { const float2 t = pair16(v); return t.x + t.y; }
+__device__ __forceinline__ float sum_xor32(float v) { const float2 t = pair32(v); return t.x + t.y; }
+__device__ __forceinline__ float max_xor16(float v) { const float2 t = pair16(v); return fmaxf(t.x, t.y); }
+__device__ __forceinline__ float max_xor32(float v) { const float2 t = pair32(v); return fmaxf(t.x, t.y); }
+// whole-wave sum / max (every lane active)
+__device__ __forceinline__ float wsum(float v) {
+  v = sum8(v);
+  v += xor8(v);
+  return sum_xor32(sum_xor16(v));
+}
+__device__ __forceinline__ float wmax(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, xor8(v));
+  return max_xor32(max_xor16(v));
+}
+// sum over aligned groups of n lanes, n a power of two up to 64 (wave-uniform)
+__device__ __forceinline__ float sum_lanes(float v, int n) {
+  if (n >= 2) v += dpp_mov<0xB1>(v);
+  if (n >= 4) v += dpp_mov<0x4E>(v);
+  if (n >= 8) v += dpp_mov<0x141>(v);
+  if (n >= 16) v += xor8(v);
+  if (n >= 32) v = sum_xor16(v);
+  if (n >= 64) v = sum_xor32(v);
+  return v;
+}
+
 struct Ctl {
   uint32_t* abort_flag;
   int32_t* err;
@@ -259,7 +312,7 @@ __device__ __forceinline__ void stage_finish(int tid, const uint32_t* xin, uint3
       if (tid + i * kPT < N4)
 #pragma unroll
         for (int k = 0; k < 4; ++k) ss = fmaf(xdec(v[i][k]), xdec(v[i][k]), ss);
-    ss = wave_sum(ss);
+    ss = wsum(ss);
     if ((tid & 63) == 0) s.red[wave_of(tid)] = ss;
     __syncthreads();
     float tot = 0.f;
@@ -283,9 +336,7 @@ __device__ __forceinline__ void stage_finish(int tid, const uint32_t* xin, uint3
     // elements 16..31 of a block pair with the high nibbles, which block_dot_hs reads 16x too large
     if ((k & 31) >= 16) f = make_float4(f.x * 0.0625f, f.y * 0.0625f, f.z * 0.0625f, f.w * 0.0625f);
     if (in) *(float4*)xs_chunk(s.xs, k >> 5, (k & 31) >> 2) = f;
-    cs += __shfl_xor(cs, 1);
-    cs += __shfl_xor(cs, 2);
-    cs += __shfl_xor(cs, 4);
+    cs = sum8(cs);
     if (in && (q & 7) == 0) s.bs[q >> 3] = cs;
   }
   __syncthreads();
@@ -365,8 +416,7 @@ __device__ __forceinline__ void pcompute(int tid, const PGroup<LPR, NB, RW>& g, 
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) acc[r] += __shfl_xor(acc[r], o);
+    acc[r] = sum_lanes(acc[r], LPR);
     if (j == 0 && g.row[r] < r1) s.ydot[g.row[r] - r0] = acc[r];
   }
 }
@@ -737,18 +787,16 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
               float dot = 0.f;
 #pragma unroll
               for (int e = 0; e < DL; ++e) dot = fmaf(al.q[qr * D + sc_c * DL + e], kf[e], dot);
-              dot += __shfl_xor(dot, 1);
-              dot += __shfl_xor(dot, 2);
-              dot += __shfl_xor(dot, 4);
+              dot = sum8(dot);  // the 8 lanes of token sc_tok
               sc[ps][qr] = j < kv_len ? dot : -INFINITY;
             }
           }
 #pragma unroll
           for (int qr = 0; qr < QR; ++qr) {
             float pm = fmaxf(sc[0][qr], sc[1][qr]);
-            pm = fmaxf(pm, __shfl_xor(pm, 8));
-            pm = fmaxf(pm, __shfl_xor(pm, 16));
-            pm = fmaxf(pm, __shfl_xor(pm, 32));
+            pm = fmaxf(pm, xor8(pm));
+            pm = max_xor16(pm);
+            pm = max_xor32(pm);
             const float mnew = fmaxf(mrun[qr], pm);
             float p0 = 0.f, p1 = 0.f, alpha = 1.f;
             if (mnew != -INFINITY) {
@@ -757,9 +805,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
               alpha = __expf(mrun[qr] - mnew);
             }
             float ps_ = p0 + p1;
-            ps_ += __shfl_xor(ps_, 8);
-            ps_ += __shfl_xor(ps_, 16);
-            ps_ += __shfl_xor(ps_, 32);
+            ps_ += xor8(ps_);
+            ps_ = sum_xor16(ps_);
+            ps_ = sum_xor32(ps_);
             lrun[qr] = lrun[qr] * alpha + ps_;
             mrun[qr] = mnew;
 #pragma unroll
@@ -795,12 +843,15 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       }
       stamp(p, l * 16 + 12);
       // reduce the value partials over the token groups, then merge the waves
+      static_assert(NV == 8 || NV == 16, "value lanes per token group: 8 or 16");
 #pragma unroll
       for (int qr = 0; qr < QR; ++qr)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-          for (int o = NV; o < kWave; o <<= 1) acc[qr][e] += __shfl_xor(acc[qr][e], o);
+        for (int e = 0; e < 8; ++e) {
+          float a = acc[qr][e];
+          if constexpr (NV == 8) a += xor8(a);
+          acc[qr][e] = sum_xor32(sum_xor16(a));
+        }
       if (v_tg == 0) {
 #pragma unroll
         for (int qr = 0; qr < QR; ++qr)
@@ -891,14 +942,14 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       if (n_out > 0 && wave < 2 && !(wave == 1 && hB == hA)) {
         float M = kNoScore;
         for (int sp = lane; sp < S; sp += kWave) M = fmaxf(M, ml[(wave * S + sp) * 2]);
-        M = wave_max(M);
+        M = wmax(M);
         float dpart = 0.f;
         for (int sp = lane; sp < S; sp += kWave) {
           const float f = __expf(ml[(wave * S + sp) * 2] - M);
           fm[wave * kMaxSplit + sp] = f;
           dpart = fmaf(ml[(wave * S + sp) * 2 + 1], f, dpart);
         }
-        dpart = wave_sum(dpart);
+        dpart = wsum(dpart);
         if (lane == 0) den[wave] = dpart;
       }
       __syncthreads();
@@ -910,7 +961,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           const int eo = t / S, sp = t - eo * S;
           const int hh = (m0 + eo) / D == hA ? 0 : 1;
           float v = idx[i] >= 0 ? xdec(word[i]) * fm[hh * kMaxSplit + sp] : 0.f;
-          for (int o = S >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+          v = sum_lanes(v, S);
           if (idx[i] >= 0 && sp == 0) {
             const float dd = den[hh];
             xstore(p.xa, m0 + eo, dd > 0.f ? v / dd : 0.f, tout);
