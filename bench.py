@@ -13,7 +13,8 @@ Output: one JSON line (metric, value = decode tok/s, ...) plus
     the lm_head and the argmax), so that kernel is the step: algorithmic bytes per launch / its
     average launch time, timed with HIP events on the step's stream around each launch in a traced
     pass right after the timed region. "traffic" is the counted HBM bytes per launch from the
-    committed FETCH_SIZE / WRITE_SIZE profile while the kernel's sources are unchanged. With
+    committed FETCH_SIZE / WRITE_SIZE profile while the kernel's sources are unchanged and the
+    profile's contexts lie within 64 positions of the traced pass's. With
     --chain the kernel chain is timed instead and the roofline is its gate/up GEMV;
   - "phases": per-layer wait / work time of each phase of the single-launch step, from GPU
     real-time-counter stamps written by one workgroup;
@@ -91,6 +92,9 @@ def main() -> int:
     ap.add_argument("--prompt", type=int, default=2048)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--synth-context", action="store_true",
+                    help="profiling aid: synthesise the --prompt positions of KV in the pool instead of "
+                         "prefilling them (same bytes per step, far fewer launches under a counter profiler)")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--no-graphs", action="store_true",
                     help="kernel chain: launch the step's kernels directly instead of replaying a captured graph")
@@ -144,13 +148,22 @@ def main() -> int:
         bw.bw_decode_step(s.model, s.pool, tok, sl, s.page_table, 1, 1, s.max_pages, None, tok if feed_back else am)
         sl.add_(1)
 
-    # prefill: the prompt through the same decode step, one position at a time
     t_pf = time.perf_counter()
-    for i in range(P):
-        tok.copy_(prompt[i:i + 1])
-        step(feed_back=(i == P - 1))
-    torch.cuda.synchronize()
-    print(f"[bench] prefill of {P} tokens in {time.perf_counter() - t_pf:.1f} s", file=sys.stderr, flush=True)
+    if args.synth_context:
+        # the pool holds P synthesised positions; decoding starts at position P from a seeded token
+        s.synthesize(cfg["seed"] + 7, [P])
+        tok.copy_(prompt[P - 1:P])
+        sl.fill_(P)
+        torch.cuda.synchronize()
+        print(f"[bench] context of {P} positions synthesised in {time.perf_counter() - t_pf:.1f} s", file=sys.stderr,
+              flush=True)
+    else:
+        # prefill: the prompt through the same decode step, one position at a time
+        for i in range(P):
+            tok.copy_(prompt[i:i + 1])
+            step(feed_back=(i == P - 1))
+        torch.cuda.synchronize()
+        print(f"[bench] prefill of {P} tokens in {time.perf_counter() - t_pf:.1f} s", file=sys.stderr, flush=True)
     for _ in range(W):
         step(feed_back=True)
     torch.cuda.synchronize()
@@ -195,8 +208,11 @@ def main() -> int:
             with open(tr_path) as f:
                 tr = json.load(f)
             from memory_bound_autoregressive_amd.build import source_digest
-            if tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ()))):
-                traffic = tr.get("hbm_bytes_per_launch")
+            # counted bytes per launch, measured at (about) this pass's context with unchanged sources
+            lo, hi = tr.get("contexts", (0, -1))
+            if (lo - 64 <= ctx_tr <= hi + 64 and
+                    tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ())))):
+                traffic = round(tr["hbm_bytes_per_launch"])
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                     "kernel": "k_persist: the whole batch-1 step in one launch (32 layers + lm_head + argmax)",

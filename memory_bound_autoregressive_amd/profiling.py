@@ -10,6 +10,12 @@ bytes per launch. Each counter is scaled by the factor that makes it read right 
 copy of known size (the copy reads B bytes and writes B bytes), measured in the same way on the
 same machine. The result records the digest of the kernel sources it was measured on, so a
 later change to the kernels invalidates it.
+
+--context-start C records the contexts the dispatches ran at: the kernel's i-th dispatch (in
+Dispatch_Id order) attended C + i + 1 positions, as in a bench.py --no-trace run where every launch
+is one token. With --fit-context the per-dispatch bytes are also fitted by least squares to
+a + b x context (b: KV traffic per cached token; a: the context-independent part); that needs the
+dispatches to span a wide range of contexts.
 """
 from __future__ import annotations
 
@@ -73,8 +79,31 @@ def _copy(path: str, kernel: str, counter: str) -> float:
     return sum(big) / len(big)
 
 
+def _per_dispatch(path: str, kernel: str, counter: str) -> list[float]:
+    rows = [r for r in _rows(path) if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not rows or "Dispatch_Id" not in rows[0]:
+        raise SystemExit(f"no per-dispatch {counter} rows (with Dispatch_Id) for {kernel!r} in {path}")
+    by_id = collections.defaultdict(float)
+    for r in rows:  # one row per dispatch (a counter summed over its instances)
+        by_id[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return [by_id[k] for k in sorted(by_id)]
+
+
+def _linfit(y: list[float], c0: int = 0) -> tuple[float, float, float]:
+    """least squares y[i] = a + b (c0 + i + 1); returns (a, b, rms residual)"""
+    n = len(y)
+    xs = [c0 + i + 1.0 for i in range(n)]
+    mx, my = sum(xs) / n, sum(y) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    b = sum((x - mx) * (v - my) for x, v in zip(xs, y)) / sxx
+    a = my - b * mx
+    rms = (sum((v - a - b * x) ** 2 for x, v in zip(xs, y)) / n) ** 0.5
+    return a, b, rms
+
+
 def traffic(fetch: str, write: str, cal_fetch: str, cal_write: str, copy_bytes: int, kernel: str,
-            copy_kernel: str = "copyBuffer", sources: tuple[str, ...] = GEMV_SOURCES) -> dict:
+            copy_kernel: str = "copyBuffer", sources: tuple[str, ...] = GEMV_SOURCES,
+            fit_context: bool = False, context_start: int | None = None) -> dict:
     from .build import source_digest
     kib = 1024.0
     cf = _copy(cal_fetch, copy_kernel, "FETCH_SIZE") * kib
@@ -82,11 +111,25 @@ def traffic(fetch: str, write: str, cal_fetch: str, cal_write: str, copy_bytes: 
     f_scale, w_scale = copy_bytes / cf, copy_bytes / cw
     kf = _one(fetch, kernel, "FETCH_SIZE") * kib
     kw = _one(write, kernel, "WRITE_SIZE") * kib
-    return {"kernel": kernel, "fetch_kib_per_dispatch": kf / kib, "write_kib_per_dispatch": kw / kib,
-            "copy_bytes": copy_bytes, "copy_fetch_kib": cf / kib, "copy_write_kib": cw / kib,
-            "fetch_scale": f_scale, "write_scale": w_scale,
-            "hbm_bytes_per_launch": kf * f_scale + kw * w_scale, "kernel_sources": list(sources),
-            "kernel_source_digest": source_digest(sources)}
+    res = {"kernel": kernel, "fetch_kib_per_dispatch": kf / kib, "write_kib_per_dispatch": kw / kib,
+           "copy_bytes": copy_bytes, "copy_fetch_kib": cf / kib, "copy_write_kib": cw / kib,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_bytes_per_launch": kf * f_scale + kw * w_scale, "kernel_sources": list(sources),
+           "kernel_source_digest": source_digest(sources)}
+    if context_start is not None:
+        n = len(_per_dispatch(fetch, kernel, "FETCH_SIZE"))
+        res["contexts"] = [context_start + 1, context_start + n]
+    if fit_context:
+        c0 = context_start or 0
+        fv = _per_dispatch(fetch, kernel, "FETCH_SIZE")
+        wv = _per_dispatch(write, kernel, "WRITE_SIZE")
+        n = min(len(fv), len(wv))
+        tot = [fv[i] * kib * f_scale + wv[i] * kib * w_scale for i in range(n)]
+        a, b, rms = _linfit(tot, c0)
+        res["fit"] = {"bytes_at_context_0": a, "bytes_per_context_token": b, "contexts": [c0 + 1, c0 + n],
+                      "rms_residual_bytes": rms,
+                      "model": "HBM bytes of one launch = bytes_at_context_0 + bytes_per_context_token x context"}
+    return res
 
 
 def main(argv=None) -> int:
@@ -107,6 +150,8 @@ def main(argv=None) -> int:
         t.add_argument(a, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--sources", default="step", choices=("step", "gemv"))
+    t.add_argument("--fit-context", action="store_true")
+    t.add_argument("--context-start", type=int, default=None)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         text = f"# {a.title}\n\nCommand:\n\n```\n{a.command}\n```\n\n{stats_table(a.csv)}\n"
@@ -114,7 +159,8 @@ def main(argv=None) -> int:
         text = f"# {a.title}\n\nCommand:\n\n```\n{a.command}\n```\n\n{counters_table(a.csv)}\n"
     else:
         res = traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.copy_bytes, a.kernel,
-                      sources=STEP_SOURCES if a.sources == "step" else GEMV_SOURCES)
+                      sources=STEP_SOURCES if a.sources == "step" else GEMV_SOURCES, fit_context=a.fit_context,
+                      context_start=a.context_start)
         with open(a.out, "w") as f:
             json.dump(res, f, indent=1)
         print(json.dumps(res))

@@ -1,0 +1,49 @@
+"""Host logic of the rocprofv3 summaries (CPU): the copy-calibrated HBM traffic figure and its
+per-launch context fit, on synthetic counter CSVs whose answer is known."""
+import csv
+import json
+
+from memory_bound_autoregressive_amd import profiling
+
+
+def _write(path, rows, fields):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_traffic_scales_by_the_copy_and_fits_context(tmp_path):
+    kib = 1024.0
+    copy_bytes = 1 << 28
+    # the copy's FETCH_SIZE reads half the true bytes (scale 2), WRITE_SIZE reads them right
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    _write(tmp_path / "cf.csv", [{"Dispatch_Id": 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "FETCH_SIZE",
+                                  "Counter_Value": copy_bytes / 2 / kib}], fields)
+    _write(tmp_path / "cw.csv", [{"Dispatch_Id": 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": "WRITE_SIZE",
+                                  "Counter_Value": copy_bytes / kib}], fields)
+    a, b, wr = 3.8e9, 131072.0, 4096.0  # true bytes of launch n: a + b (n + 1) read, wr written
+    n = 50
+    fetch = [{"Dispatch_Id": 10 + 2 * i, "Kernel_Name": "void bw::k_persist<...>", "Counter_Name": "FETCH_SIZE",
+              "Counter_Value": (a + b * (i + 1)) / 2 / kib} for i in range(n)]
+    fetch.append({"Dispatch_Id": 11, "Kernel_Name": "other", "Counter_Name": "FETCH_SIZE", "Counter_Value": 1e9})
+    # the reset kernel shares the name prefix; the template's "<" keeps it out of the figure
+    fetch.append({"Dispatch_Id": 3, "Kernel_Name": "bw::k_persist_reset(bw::PersistParams)", "Counter_Name": "FETCH_SIZE",
+                  "Counter_Value": 16.0})
+    write = [{"Dispatch_Id": 10 + 2 * i, "Kernel_Name": "void bw::k_persist<...>", "Counter_Name": "WRITE_SIZE",
+              "Counter_Value": wr / kib} for i in range(n)]
+    _write(tmp_path / "f.csv", fetch[::-1], fields)  # dispatch order comes from Dispatch_Id, not row order
+    _write(tmp_path / "w.csv", write, fields)
+    res = profiling.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                            str(tmp_path / "cw.csv"), copy_bytes, "k_persist<", sources=profiling.STEP_SOURCES,
+                            fit_context=True, context_start=0)
+    assert abs(res["fetch_scale"] - 2.0) < 1e-12 and abs(res["write_scale"] - 1.0) < 1e-12
+    mean_true = a + b * (n + 1) / 2 + wr
+    assert abs(res["hbm_bytes_per_launch"] - mean_true) / mean_true < 1e-9
+    fit = res["fit"]
+    assert abs(fit["bytes_at_context_0"] - (a + wr)) / a < 1e-9
+    assert abs(fit["bytes_per_context_token"] - b) / b < 1e-6
+    assert fit["contexts"] == [1, n] and fit["rms_residual_bytes"] < 1.0
+    assert res["contexts"] == [1, n]
+    json.dumps(res)
