@@ -178,6 +178,34 @@ int bw_set_gemm_min_rows(bw_model* model, int32_t min_rows);
 /* Text of the last error on this thread ("" if none). */
 const char* bw_last_error(void);
 
+/* Greedy acceptance after a verify step: the bookkeeping of speculative decoding, on the device.
+ * bw24 deep-dive page: section 1 (speculative output must equal plain token-by-token argmax
+ * decoding), section 2 (the engine's verify-accept logic with a ring buffer of drafts and
+ * logits), section 5 stage 4 (after the first mismatching draft the later positions' logits are
+ * forced to -inf).
+ * Row b*t + i of a bw_decode_step call with t tokens per sequence holds input x_i (x_0: the
+ * last committed token, not yet cached; x_1..x_{t-1}: drafts) and its greedy token a_i. Draft
+ * x_{j+1} is accepted while x_1..x_j were and x_{j+1} == a_j; with n accepted, a_0..a_n are
+ * this step's committed tokens.
+ *   tokens_dev   int32 [batch * t]  in: the step's inputs; out: tokens[b*t] = a_n, the next
+ *                                   step's x_0 (the caller writes the next drafts into the rest)
+ *   argmax_dev   int32 [batch * t]  the step's argmax output
+ *   logits_dev   float [batch * t * vocab] the step's logits, or NULL; rows i > n become -inf
+ *   seq_lens_dev int32 [batch]      in/out: advanced by n + 1 (keys and values of x_0..x_n stay;
+ *                                   those of rejected drafts lie beyond and are overwritten by the
+ *                                   next step before anything attends to them)
+ *   ring_dev     int32 [batch * ring_cap] or NULL: committed tokens, token k of sequence b at
+ *                                   ring[b * ring_cap + k % ring_cap]
+ *   count_dev    int32 [batch] or NULL (with ring_dev): in/out, tokens committed so far
+ *   accepted_dev int32 [batch] or NULL: n of this step
+ * With t = 1 this is the bookkeeping of plain greedy decoding. Asynchronous on `stream`;
+ * allocates nothing.
+ * Errors: BW_EINVAL (null model, tokens, argmax or seq_lens; batch or t < 1; ring without
+ * count or the reverse; ring_cap < t), BW_ERANGE (batch or t above 65535), BW_EHIP. */
+int bw_spec_accept(bw_model* model, int32_t* tokens_dev, const int32_t* argmax_dev, float* logits_dev,
+                   int32_t* seq_lens_dev, int32_t* ring_dev, int32_t* count_dev, int32_t ring_cap,
+                   int32_t* accepted_dev, int32_t batch, int32_t t, void* stream);
+
 /* Synchronise `stream`, copy the model's device error word to *flags_host (BW_DERR_* bits)
  * and clear it. */
 int bw_check_device_error(bw_model* model, void* stream, int32_t* flags_host);

@@ -27,7 +27,7 @@ EXPORTS = (
     "bw_last_error", "bw_check_device_error", "bw_debug_dequant", "bw_debug_matvec",
     "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden", "bw_set_trace", "bw_set_graphs",
     "bw_set_gemm_min_rows", "bw_set_single_launch", "bw_debug_single_launch_deadline",
-    "bw_debug_single_launch_stamps",
+    "bw_debug_single_launch_stamps", "bw_spec_accept",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
         L.bw_set_single_launch.argtypes = [vp, i32, ctypes.POINTER(i32)]
         L.bw_debug_single_launch_deadline.argtypes = [vp, u64]
         L.bw_debug_single_launch_stamps.argtypes = [vp, vp, i32]
+        L.bw_spec_accept.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -171,6 +172,15 @@ def bw_decode_step(model: int, pool: int, tokens, seq_lens, page_table, batch: i
     """tokens/seq_lens/page_table/argmax: int32 device tensors; logits: float32 device tensor."""
     _check(lib().bw_decode_step(model, pool, _ptr(tokens), _ptr(seq_lens), _ptr(page_table), batch, t,
                                 max_pages, _ptr(logits), _ptr(argmax), _stream(stream)), "bw_decode_step")
+
+
+def bw_spec_accept(model: int, tokens, argmax, logits, seq_lens, ring, count, ring_cap: int, accepted,
+                   batch: int, t: int, stream=None) -> None:
+    """Greedy acceptance after a verify step (device tensors; logits, ring/count and accepted may
+    be None). See include/bw.h."""
+    _check(lib().bw_spec_accept(model, _ptr(tokens), _ptr(argmax), _ptr(logits), _ptr(seq_lens), _ptr(ring),
+                                _ptr(count), int(ring_cap), _ptr(accepted), batch, t, _stream(stream)),
+           "bw_spec_accept")
 
 
 def bw_check_device_error(model: int, stream=None) -> int:

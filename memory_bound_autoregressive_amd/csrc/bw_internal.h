@@ -172,6 +172,10 @@ int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* r
 int launch_rowrms(const float* x, int64_t stride, int K, float eps, int M, float* r, hipStream_t s);
 int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, int32_t* out, hipStream_t s);
 
+// greedy acceptance after a verify step (bw_spec.hip)
+int launch_spec_accept(int32_t* tokens, const int32_t* argmax, float* logits, int64_t V, int32_t* seq_lens,
+                       int32_t* ring, int32_t* count, int cap, int32_t* accepted, int batch, int t, hipStream_t s);
+
 // single-launch step (bw_persist.hip): -2 when (d, F, head dim, query heads per KV head) has no
 // instantiation; query_only checks that one workgroup of it fits a CU
 int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,

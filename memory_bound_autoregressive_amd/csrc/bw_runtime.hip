@@ -953,8 +953,12 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
   if (batch < 1 || t < 1 || max_pages < 1) return fail(BW_EINVAL, "batch, t and max_pages must be positive");
   if (batch * t > m->c.max_tokens) return fail(BW_ERANGE, "batch * t = %d exceeds max_tokens %d", batch * t, m->c.max_tokens);
   hipStream_t s = (hipStream_t)stream;
-  if (m->persist_ok && m->use_persist && batch == 1 && t == 1 && m->trace_class < 0) {
-    // the whole step as one cooperative launch (no capture needed: one launch per step)
+  // the single launch holds one attention split's page ids in LDS (at most 256 per split);
+  // a longer page table takes the kernel chain
+  const bool persist_pages =
+      m->persist_ok && (max_pages + m->persist_nwg / m->c.n_kv_heads - 1) / (m->persist_nwg / m->c.n_kv_heads) <= 256;
+  if (m->persist_ok && m->use_persist && persist_pages && batch == 1 && t == 1 && m->trace_class < 0) {
+    // the whole step as one launch (no capture needed: one launch per step)
     PersistParams p = m->pp;
     p.pool = pool->data;
     p.layer_elems = pool->layer_elems;
@@ -967,10 +971,6 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
     p.logits = logits_out;
     p.argmax = argmax_out;
     const auto& c = m->c;
-    // one attention split's pages are held in LDS (256 ids)
-    const int splits = m->persist_nwg / c.n_kv_heads;
-    if ((max_pages + splits - 1) / splits > 256)
-      return fail(BW_ERANGE, "max_pages %d is beyond the single-launch step (at most %d)", max_pages, 256 * splits);
     if (launch_persist(p, c.d_model, c.ffn_dim, c.kv_dtype, c.head_dim, c.n_q_heads / c.n_kv_heads, m->persist_nwg, s,
                        false))
       return fail(BW_EHIP, "single-launch step failed to launch");
@@ -1040,6 +1040,20 @@ extern "C" int bw_set_gemm_min_rows(bw_model* m, int32_t min_rows) {
 }
 
 extern "C" const char* bw_last_error(void) { return g_err.c_str(); }
+
+extern "C" int bw_spec_accept(bw_model* m, int32_t* tokens, const int32_t* argmax, float* logits, int32_t* seq_lens,
+                              int32_t* ring, int32_t* count, int32_t ring_cap, int32_t* accepted, int32_t batch,
+                              int32_t t, void* stream) {
+  if (!m || !tokens || !argmax || !seq_lens) return fail(BW_EINVAL, "null argument");
+  if (batch < 1 || t < 1) return fail(BW_EINVAL, "batch and t must be positive");
+  if (t > 65535 || batch > 65535) return fail(BW_ERANGE, "batch and t are at most 65535");
+  if ((ring == nullptr) != (count == nullptr)) return fail(BW_EINVAL, "ring and count go together");
+  if (ring != nullptr && ring_cap < t) return fail(BW_EINVAL, "ring_cap %d is below t = %d", ring_cap, t);
+  if (launch_spec_accept(tokens, argmax, logits, m->c.vocab, seq_lens, ring, count, ring_cap, accepted, batch, t,
+                         (hipStream_t)stream))
+    return fail(BW_EHIP, "acceptance kernel failed to launch");
+  return BW_OK;
+}
 
 extern "C" int bw_check_device_error(bw_model* m, void* stream, int32_t* flags) {
   if (!m || !flags) return fail(BW_EINVAL, "null argument");

@@ -322,6 +322,23 @@ def forward(model: Model, kv: KV, seq: int, tokens, pos0: int, *, want_logits=Tr
     return {"logits": logits, "hidden": hidden, "sel": sel, "adopted": adopted.value, "rc": rc}
 
 
+def spec_accept(inputs, argmaxes):
+    """Greedy acceptance of one verify step of one sequence.
+
+    bw24 deep-dive page, section 1: speculative decoding must give exactly the tokens of plain
+    token-by-token argmax decoding; section 5 stage 4: after the first draft that does not match,
+    the later positions are masked.
+    inputs = [x_0, ..., x_{t-1}]: x_0 is the last committed token, x_1.. the drafts;
+    argmaxes[i] = the greedy token predicted after x_0..x_i.
+    Draft x_{j+1} stands if every earlier draft stood and x_{j+1} == argmaxes[j].
+    Returns (n drafts standing, committed tokens argmaxes[0..n], masked rows n+1..t-1).
+    """
+    n = 0
+    while n + 1 < len(inputs) and int(inputs[n + 1]) == int(argmaxes[n]):
+        n += 1
+    return n, [int(v) for v in argmaxes[:n + 1]], list(range(n + 1, len(inputs)))
+
+
 def num_threads() -> int:
     return int(lib().or_num_threads())
 

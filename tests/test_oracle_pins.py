@@ -422,3 +422,65 @@ def test_oracle_reads_synthetic_context():
     kv.set_synth(1, 4242, 7, 40)
     for (l, pos, w, g, d) in itertools.product([0, 1], [0, 15, 39], [0, 1], [0, 1], [0, 63]):
         assert kv.read(1, l, pos, w, g, d) == synth.kv_value(4242, l, 7, pos, w, g, d, 2, 64)
+
+
+# ---- speculative acceptance -------------------------------------------------------------------
+
+def test_spec_accept_hand_cases():
+    """Worked cases of the acceptance rule (inputs = [last token, drafts...], argmaxes per row)."""
+    # every draft matches the prediction before it: 3 stand, 4 tokens committed, nothing masked
+    assert oracle.spec_accept([5, 7, 9, 11], [7, 9, 11, 13]) == (3, [7, 9, 11, 13], [])
+    # the first draft misses: only the prediction after the last token is committed
+    assert oracle.spec_accept([5, 8, 9, 11], [7, 9, 11, 13]) == (0, [7], [1, 2, 3])
+    # the second draft misses; the third would match its row but comes after a miss
+    assert oracle.spec_accept([5, 7, 4, 11], [7, 9, 11, 13]) == (1, [7, 9], [2, 3])
+    # t = 1: plain greedy decoding
+    assert oracle.spec_accept([5], [6]) == (0, [6], [])
+
+
+def _toy_next(prefix):
+    """a deterministic 'model': the greedy token after a prefix (a hash of it, 16 symbols)"""
+    h = 1469598103934665603
+    for v in prefix:
+        h = ((h ^ (int(v) + 1)) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return (h >> 17) % 16
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 6])
+def test_spec_accept_reproduces_sequential_greedy(t):
+    """The defining property: a loop of verify steps with any drafts, committing by the rule,
+    yields exactly the tokens of one-token-at-a-time greedy decoding; with correct drafts it
+    commits t tokens per step, with wrong drafts one."""
+    rng = np.random.default_rng(t)
+    prompt = [int(v) for v in rng.integers(0, 16, 5)]
+    n_new = 60
+    seq = list(prompt)
+    for _ in range(n_new):
+        seq.append(_toy_next(seq))
+    greedy = seq[len(prompt):]
+    for policy in ("right", "wrong", "mixed"):
+        committed, cur = [], list(prompt)
+        steps = 0
+        while len(committed) < n_new:
+            # drafts: the true continuation, a wrong one, or right for a random prefix
+            truth = greedy[len(committed):len(committed) + t - 1]
+            truth += [0] * (t - 1 - len(truth))
+            keep = {"right": t - 1, "wrong": 0, "mixed": int(rng.integers(0, t))}[policy]
+            drafts = [truth[j] if j < keep else (truth[j] + 1) % 16 for j in range(t - 1)]
+            inputs = [cur[-1]] + drafts
+            # the verify step: row i predicts after cur + drafts[:i]
+            argm = [_toy_next(cur + drafts[:i]) for i in range(t)]
+            n, toks, masked = oracle.spec_accept(inputs, argm)
+            assert masked == list(range(n + 1, t))
+            if policy == "right" and len(committed) + t <= n_new:
+                assert n == t - 1
+            if policy == "wrong":
+                assert n == 0
+            committed += toks
+            cur += toks
+            steps += 1
+        assert committed[:n_new] == greedy
+        if policy == "right":
+            assert steps == -(-n_new // t)
+        if policy == "wrong":
+            assert steps == n_new
