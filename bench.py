@@ -84,6 +84,106 @@ def cpu_baseline(cfg: dict, ctx: int, seconds: float) -> dict:
                       f"(context synthesised, not prefilled), {el:.1f} s"}
 
 
+def run_workload(args) -> int:
+    """The other timed workloads (synthesised contexts, kernel chain): dense-27b and moe-35b-a3b
+    decode at batch 1, and verify-9b, a speculative loop over 32 sequences (t = 4: the last
+    committed token and three drafts drawn uniformly from the vocabulary, greedy acceptance on the
+    device). One JSON line, like the default run, with this workload's own metric."""
+    import numpy as np
+    import torch
+
+    import memory_bound_autoregressive_amd as bw
+    from memory_bound_autoregressive_amd import configs
+    from memory_bound_autoregressive_amd.session import Session
+
+    cfg = configs.ALL[args.workload]
+    seed, V = cfg["seed"], cfg["vocab"]
+    K = args.steps if args.steps_set else cfg["steps"]
+    W = args.warmup if args.warmup_set else 4
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    rng = np.random.default_rng(seed)
+    t_load = time.perf_counter()
+    if args.workload == "verify-9b":
+        B, t = cfg["batch"], cfg["t"]
+        lens = [int(v) for v in rng.integers(cfg["ctx_lo"], cfg["ctx_hi"] + 1, B)]
+        s = Session(cfg, seed=seed, max_len=[n + (W + K + 2) * t for n in lens], max_tokens=B * t,
+                    pool_seed=seed + 1)
+        s.synthesize(seed + 7, lens)
+    else:
+        B, t = 1, 1
+        lens = [cfg["context"]]
+        s = Session(cfg, seed=seed, max_len=[lens[0] + W + K + 2], max_tokens=1, pool_seed=seed + 1)
+        s.synthesize(seed + 7, lens)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: model + pool ({s.n_pages} pages) ready in {time.perf_counter() - t_load:.1f} s",
+          file=sys.stderr, flush=True)
+    tokens = torch.from_numpy(rng.integers(0, V, B * t).astype(np.int32)).to(dev)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+    argmax = torch.empty(B * t, dtype=torch.int32, device=dev)
+    logits = torch.empty((B * t, V), dtype=torch.float32, device=dev) if t > 1 else None
+    cap = 1024
+    ring = torch.zeros(B * cap, dtype=torch.int32, device=dev)
+    count = torch.zeros(B, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def step():
+        if t > 1:  # fresh drafts after each sequence's next input token
+            tokens.view(B, t)[:, 1:] = torch.randint(0, V, (B, t - 1), generator=gen, device=dev, dtype=torch.int32)
+        bw.bw_decode_step(s.model, s.pool, tokens, seq_lens, s.page_table, B, t, s.max_pages, logits, argmax)
+        bw.bw_spec_accept(s.model, tokens, argmax, logits, seq_lens, ring, count, cap, None, B, t)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    ctx0 = seq_lens.cpu().numpy().astype(np.float64)
+    c0 = int(count.sum().item())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    if bw.bw_check_device_error(s.model) != 0:
+        print("[bench] device error flag set", file=sys.stderr)
+        return 1
+    ms_per_step = e0.elapsed_time(e1) / K
+    committed = int(count.sum().item()) - c0
+    ctx1 = seq_lens.cpu().numpy().astype(np.float64)
+    s.close()
+    # algorithmic bytes per step: the weights once, each sequence's KV read at its mean context
+    # over the timed steps (t positions attend, the later ones to the earlier: counted once),
+    # the new K/V, and for verify the logits written
+    ab1 = algorithmic_bytes(cfg, 0.0)
+    # step k reads seq_lens_k + t positions; seq_lens grows by about one per step (drafts drawn at
+    # random are almost never accepted; at t = 1 exactly one)
+    ctx_mean = (ctx0 + ctx1) / 2.0 + t - 0.5
+    kv_per_pos = 2 * cfg["n_kv_heads"] * cfg["head_dim"] * 2 * cfg["n_layers"]
+    kv_read = float(ctx_mean.sum()) * kv_per_pos
+    per_step = ab1["weights"] + ab1["router"] + kv_read + B * t * (kv_per_pos + ab1["embed"]) + \
+        (B * t * V * 4 if t > 1 else 0)
+    gbps = per_step / (ms_per_step * 1e-3) / 1e9
+    if t > 1:
+        metric, value, unit = "verified positions/s (verify-9b, 32 x 4 per step)", B * t * 1000.0 / ms_per_step, "positions/s"
+    else:
+        metric, value, unit = f"decode tok/s at batch 1 ({args.workload} int4)", 1000.0 / ms_per_step, "tok/s"
+    print(f"[bench] {args.workload}: {K} steps, {ms_per_step * 1e3:.1f} us/step, {value:.1f} {unit}, "
+          f"{gbps:.0f} GB/s algorithmic ({gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s)", file=sys.stderr, flush=True)
+    out = {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "step": "kernel chain (hipGraph replay)", "batch": B, "t": t,
+                   "context": "synthesised", "context_range": [int(ctx0.min()), int(ctx1.max())],
+                   "context_sum_start": int(ctx0.sum()), "seed": seed},
+        "achieved_hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": round(per_step), "committed_tokens_per_s": round(committed * 1000.0 / (ms_per_step * K), 1),
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,9 +202,14 @@ def main() -> int:
                     help="time the kernel chain instead of the single-launch step")
     ap.add_argument("--cooperative", action="store_true",
                     help="single-launch step through the cooperative launch API")
+    ap.add_argument("--workload", default="dense-9b",
+                    choices=("dense-9b", "dense-27b", "moe-35b-a3b", "verify-9b"),
+                    help="dense-9b (default): the headline line; the others time their own workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
+    args.steps_set = "--steps" in sys.argv
+    args.warmup_set = "--warmup" in sys.argv
     if args.calibrate_copy:
         import torch
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
@@ -120,6 +225,8 @@ def main() -> int:
         print(f"bench.py: this build runs the decode step on one GPU; --gpus {args.gpus} "
               f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.workload != "dense-9b":
+        return run_workload(args)
 
     import numpy as np
     import torch

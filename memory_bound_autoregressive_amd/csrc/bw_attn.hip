@@ -23,6 +23,9 @@
 // or NaN contents there never reach the result.
 #include "bw_common.h"
 #include "bw_internal.h"
+#include "bw_lanes.h"
+
+#include <type_traits>
 
 namespace bw {
 
@@ -238,6 +241,263 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
   }
 }
 
+// ---- matrix-core split attention (verify steps: QR query rows per KV head, up to 16) ----------
+// The same split and partial format as k_attn_split, with both contractions on the matrix cores.
+// Per page (16 tokens) a wave computes
+//   scores^T [16 tokens][16 rows] = K [16][D] . Q^T   as D/32 steps of a 16x16x32 product, and
+//   O [16 rows][D] += P [16][16 tokens] . V [16][D]    as D/16 steps of a 16x16x16 product.
+// The first product's output layout (lane l: tokens 4(l/16)..+3 of row l%16) is the second one's
+// A-operand layout, so P never moves between lanes. K rows load directly as A operands (16-byte
+// loads, token l%16, dims 8(l/16)..+7 of each 32-dim chunk). V is staged in LDS and read back with
+// tokens along K: B[token 4(l/16)+i][dim l%16]. Q and P are split into sums of cache-dtype parts,
+// so each product term is exact in fp32 and only the summation order differs from the VALU
+// kernel: Q in three bf16 parts (residual below 2^-26 of |q|; a score scales q by up to a few
+// hundred) or two fp16 parts (2^-22), P in two parts (2^-17 for bf16). Rows past QR are padding.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int KVDT>
+struct MfmaT;
+template <>
+struct MfmaT<1> {  // fp16 cache
+  typedef _Float16 e8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 e4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4 mm32(e8 a, e8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mm16(e4 a, e4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct MfmaT<2> {  // bf16 cache
+  typedef __bf16 e8 __attribute__((ext_vector_type(8)));
+  typedef short e4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4 mm32(e8 a, e8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mm16(e4 a, e4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr int kVStride = 136;
+constexpr int kMfmaMaxPps = 32;  // most pages of one split of the matrix-core kernel  // LDS row of a staged V page, in 16-bit elements (272 B: conflict-free reads)
+
+template <int KVDT, int D>
+__global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR) {
+  using M = MfmaT<KVDT>;
+  typedef typename M::e8 e8;
+  typedef typename M::e4 e4;
+  constexpr int NC = D / 32;  // 32-dim chunks (scores)
+  constexpr int NV = D / 16;  // 16-dim chunks (values)
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int rep = p.H / p.G;
+  const int base_pos = p.seq_lens[b];
+  const int kv_len = base_pos + p.t;
+  int n_pg = (kv_len + kPageTokens - 1) / kPageTokens;
+  const int pg_cap = min(p.max_pages, p.max_splits * p.pages_per_split);
+  if (n_pg > pg_cap) {
+    if (threadIdx.x == 0 && s == 0) atomicOr(p.err, 1);
+    n_pg = pg_cap;
+  }
+  const int pg0 = s * p.pages_per_split;
+  if (pg0 >= n_pg) return;
+  const int pg1 = min(n_pg, pg0 + p.pages_per_split);
+
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[4][kPageTokens * kVStride];
+  __shared__ float acc_lds[4][16 * D];
+  __shared__ float m_lds[4][16], l_lds[4][16];
+  __shared__ int pid_lds[kMfmaMaxPps];  // this split's page ids (read once; LDS reads do not wait for memory loads)
+
+  // the wave index through readfirstlane: page ids and buffer descriptors derived from it are
+  // then known to be uniform, so no load needs a per-lane loop
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, grp = lane >> 4;  // column / row-block of the 16x16 tiles
+  // query row c16 (padding rows past QR: zero query, no causal limit, never written)
+  const int qr = c16;
+  const bool real = qr < QR;
+  const int ti = real ? qr / rep : 0, hr = real ? qr - ti * rep : 0;
+  const int qpos = real ? base_pos + ti : 0x7fffffff;
+  constexpr int NQ = KVDT == 2 ? 3 : 2;  // parts of the query
+  typedef typename std::remove_reference<decltype(e8{}[0])>::type el8;
+  typedef typename std::remove_reference<decltype(e4{}[0])>::type el4;
+  e8 qp[NQ][NC];
+  {
+    // unconditional 16-byte loads (a padding row reads row 0 and is zeroed), all issued first
+    const float4* qsrc = (const float4*)(p.q + ((int64_t)(b * p.t + ti) * p.H + g * rep + hr) * D);
+    float4 qv[NC][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) qv[c][h] = qsrc[(32 * c + 8 * grp) / 4 + h];
+    const float qs = real ? p.scale : 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 v4 = qv[c][e >> 2];
+        float x = ((e & 3) == 0 ? v4.x : (e & 3) == 1 ? v4.y : (e & 3) == 2 ? v4.z : v4.w) * qs;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+          const uint16_t bits = f32_to_kv<KVDT>(x);
+          qp[k][c][e] = __builtin_bit_cast(el8, bits);
+          x -= kv_to_f32<KVDT>(bits);
+        }
+      }
+  }
+  float mrun = -INFINITY, lrun = 0.f;  // of row c16
+  f32x4 o[NV];
+#pragma unroll
+  for (int c = 0; c < NV; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* vl = v_lds[wave];
+
+  // K and V of one page of this KV head as buffer loads on that page (an invalid page id reads
+  // zeros from past the buffer), issued one page ahead of the page being computed
+  {
+    const int32_t* ptab = p.page_table + (int64_t)b * p.max_pages;
+    if ((int)threadIdx.x < pg1 - pg0) pid_lds[threadIdx.x] = ptab[pg0 + threadIdx.x];
+    __syncthreads();
+  }
+  auto load_kv = [&](int page, u32x4 (&kr)[NC], u32x4 (&vr)[D / 32]) {
+    const bool ok = page >= 0 && page < p.n_pages;
+    const uint16_t* base = p.pool + (ok ? (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D : 0);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 2 * kPageTokens * D * 2, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kr[c] = __builtin_amdgcn_raw_buffer_load_b128(r, ok ? (c16 * D + 32 * c + 8 * grp) * 2 : 0x7FFFFFF0, 0, 0);
+#pragma unroll
+    for (int q4 = 0; q4 < D / 32; ++q4) {  // 16-byte chunk k = lane + 64 q4: token k / (D/8), dims 8 (k % (D/8))
+      const int k = lane + 64 * q4;
+      vr[q4] = __builtin_amdgcn_raw_buffer_load_b128(
+          r, ok ? (kPageTokens * D + (k / (D / 8)) * D + 8 * (k % (D / 8))) * 2 : 0x7FFFFFF0, 0, 0);
+    }
+  };
+  // one page: scores, online softmax, values (kr, vr hold its K and V)
+  auto compute = [&](int pg, int page, const u32x4 (&kraw)[NC], const u32x4 (&vraw)[D / 32]) {
+    if (page < 0 || page >= p.n_pages) {
+      if (lane == 0) atomicOr(p.err, 1);
+      return;
+    }
+    // stage V (this wave's buffer; LDS operations of one wave run in order)
+#pragma unroll
+    for (int q4 = 0; q4 < D / 32; ++q4) {
+      const int k = lane + 64 * q4;
+      *(u32x4*)(vl + (k / (D / 8)) * kVStride + 8 * (k % (D / 8))) = vraw[q4];
+    }
+    // scores^T: lane holds tokens 4 grp + i of row c16
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const e8 kop = __builtin_bit_cast(e8, kraw[c]);
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) sc = M::mm32(kop, qp[k][c], sc);
+    }
+    float sv[4];
+    float pm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = pg * kPageTokens + 4 * grp + i;
+      sv[i] = (j < kv_len && j <= qpos) ? sc[i] : -INFINITY;
+      pm = fmaxf(pm, sv[i]);
+    }
+    pm = max_xor32(max_xor16(pm));
+    const float mnew = fmaxf(mrun, pm);
+    float pv[4], alpha = 1.f, psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = mnew == -INFINITY ? 0.f : __expf(sv[i] - mnew);
+      psum += pv[i];
+    }
+    if (mnew != -INFINITY) alpha = __expf(mrun - mnew);
+    psum = sum_xor32(sum_xor16(psum));
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+    // P as the A operand (row c16, tokens 4 grp + i), hi + lo
+    e4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t hb = f32_to_kv<KVDT>(pv[i]);
+      const uint16_t lb = f32_to_kv<KVDT>(pv[i] - kv_to_f32<KVDT>(hb));
+      ph[i] = __builtin_bit_cast(el4, hb);
+      pl[i] = __builtin_bit_cast(el4, lb);
+    }
+    // rescale the accumulators: lane holds rows 4 grp + i, whose factors sit in lanes 4 grp + i
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
+    // values: B [token 4 grp + i][dim 16 c + c16] from the staged page; slots past the sequence
+    // end are zeroed (stale or NaN contents must not meet a zero probability)
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) live[i] = pg * kPageTokens + 4 * grp + i < kv_len;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      e4 vb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t bits = live[i] ? vl[(4 * grp + i) * kVStride + 16 * c + c16] : (uint16_t)0;
+        vb[i] = __builtin_bit_cast(el4, bits);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
+      o[c] = M::mm16(ph, vb, o[c]);
+      o[c] = M::mm16(pl, vb, o[c]);
+    }
+  };
+  // two register sets alternate: the next page's loads are in flight while a page is computed,
+  // and no register moves between them (a move would wait for the loads)
+  int pg = pg0 + wave;
+  int page = pg < pg1 ? __builtin_amdgcn_readfirstlane(pid_lds[pg - pg0]) : -1;
+  u32x4 ka[NC], va[D / 32], kb[NC], vb2[D / 32];
+  load_kv(page, ka, va);
+  while (pg < pg1) {
+    int pgn = pg + 4;
+    int page_n = pgn < pg1 ? __builtin_amdgcn_readfirstlane(pid_lds[pgn - pg0]) : -1;
+    load_kv(page_n, kb, vb2);
+    compute(pg, page, ka, va);
+    pg = pgn;
+    page = page_n;
+    if (pg >= pg1) break;
+    pgn = pg + 4;
+    page_n = pgn < pg1 ? __builtin_amdgcn_readfirstlane(pid_lds[pgn - pg0]) : -1;
+    load_kv(page_n, ka, va);
+    compute(pg, page, kb, vb2);
+    pg = pgn;
+    page = page_n;
+  }
+  // ---- merge the 4 waves (rows 4 grp + i, dims 16 c + c16) and write this split's partials
+#pragma unroll
+  for (int c = 0; c < NV; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc_lds[wave][(4 * grp + i) * D + 16 * c + c16] = o[c][i];
+  if (grp == 0) {
+    m_lds[wave][c16] = mrun;
+    l_lds[wave][c16] = lrun;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < QR * D; e += kBlock) {
+    const int r = e / D, d = e - r * D;
+    const float Mx = fmaxf(fmaxf(m_lds[0][r], m_lds[1][r]), fmaxf(m_lds[2][r], m_lds[3][r]));
+    float a = 0.f, l = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __expf(m_lds[w][r] - Mx);
+        a = fmaf(acc_lds[w][r * D + d], f, a);
+        l = fmaf(l_lds[w][r], f, l);
+      }
+    }
+    const int rt = r / rep, rh = r - rt * rep;
+    float* dst = p.part + (((int64_t)(b * p.t + rt) * p.H + g * rep + rh) * p.max_splits + s) * (D + 2);
+    dst[d] = a;
+    if (d == 0) {
+      dst[D] = Mx;
+      dst[D + 1] = l;
+    }
+  }
+}
+
 // Merge of the split partials of one (row, query head): o = sum_s acc_s exp(m_s - M) / sum_s l_s
 // exp(m_s - M), M = max_s m_s, in split order. The (m, l) of every split are loaded in parallel
 // (one split per thread) and the per-split factors staged in LDS, so only the value sums loop.
@@ -306,8 +566,30 @@ static int dispatch_qr(const AttnParams& p, int batch, hipStream_t s) {
   }
 }
 
+// pages per split of the matrix-core kernel: 8 pages per wave keep the partials (one per split,
+// row and head) small next to the KV read of verify steps over long contexts
+constexpr int kMfmaPagesPerSplit = kMfmaMaxPps;
+
+template <int D>
+static int launch_mfma(const AttnParams& p, int kv_dtype, int batch, int qr, hipStream_t s) {
+  AttnParams m = p;
+  m.pages_per_split = kMfmaPagesPerSplit;
+  m.max_splits = min((p.max_pages + kMfmaPagesPerSplit - 1) / kMfmaPagesPerSplit, p.max_splits);
+  if (kv_dtype == 1)
+    hipLaunchKernelGGL((k_attn_split_mfma<1, D>), dim3(m.max_splits, m.G, batch), dim3(kBlock), 0, s, m, qr);
+  else
+    hipLaunchKernelGGL((k_attn_split_mfma<2, D>), dim3(m.max_splits, m.G, batch), dim3(kBlock), 0, s, m, qr);
+  hipLaunchKernelGGL(k_attn_merge<D>, dim3(m.H, batch * m.t), dim3(kBlock), 0, s, m);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_attention(const AttnParams& p, int kv_dtype, int batch, hipStream_t s) {
   int rc;
+  const int qr = p.t * (p.H / p.G);
+  if (p.mfma && qr >= 8 && qr <= 16) {  // verify steps: both products on the matrix cores
+    if (p.D == 128) return launch_mfma<128>(p, kv_dtype, batch, qr, s);
+    if (p.D == 64) return launch_mfma<64>(p, kv_dtype, batch, qr, s);
+  }
   if (p.D == 128) rc = kv_dtype == 1 ? dispatch_qr<1, 128>(p, batch, s) : dispatch_qr<2, 128>(p, batch, s);
   else if (p.D == 64) rc = kv_dtype == 1 ? dispatch_qr<1, 64>(p, batch, s) : dispatch_qr<2, 64>(p, batch, s);
   else return -2;

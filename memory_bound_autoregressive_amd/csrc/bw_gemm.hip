@@ -69,11 +69,19 @@ __device__ __forceinline__ h8_t codes_to_h8(uint32_t c) {
 __device__ __forceinline__ int staged_pos(int kb) { return 8 * ((kb & 15) >> 2) + 4 * (kb >> 4); }
 
 // element (m, n) of k-split ks goes to out[ks * ks_stride + m * ldo + n]
+// Rounds of kKC columns are software-pipelined: round r + 1's codes, scales and X values are
+// loaded into registers before round r's products, and its X is converted and staged into the
+// other LDS buffer after them, so one barrier per round separates the buffers and the memory
+// latency of a round overlaps the previous round's matrix-core work. Every load is issued
+// unconditionally (rows past N or M are clamped and their values zeroed by selection), so the
+// compiler's wait counts are exact.
 template <int MT, int IN>
 __global__ __launch_bounds__(kBlock) void k_gemm(GemvParams p, int M, int ksplit, const float* __restrict__ rms,
                                                 float* __restrict__ out, int64_t ldo, int64_t ks_stride) {
-  __shared__ __attribute__((aligned(16))) _Float16 xh[MT * 16 * kXP];
-  __shared__ __attribute__((aligned(16))) _Float16 xl[MT * 16 * kXP];
+  constexpr int XB = MT * 16 * kXP;  // one staged buffer (fp16 elements)
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2][XB];
+  __shared__ __attribute__((aligned(16))) _Float16 xl[2][XB];
+  constexpr int NX = (MT * 16 * (kKC / 4) + kBlock - 1) / kBlock;  // float4 of X per thread per round
   const int K = p.w.K, N = p.w.N;
   const int nblk = K >> 5;
   const int n0 = blockIdx.x * kNT;
@@ -98,65 +106,113 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemvParams p, int M, int ksplit
 #pragma unroll
     for (int t = 0; t < MT; ++t) tot[s][t] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = k_begin; k0 < k_end; k0 += kKC) {
-    // this round's code slices and scales go out before the staging of X
+  struct Round {
     uint32_t cw[kNS][kKC / 32];
-    float sc[kNS][kKC / 32];
+    uint16_t sc[kNS][kKC / 32];
+    float4 xv[NX];
+    uint2 gm[IN == IN_RMSNORM ? NX : 1];  // RMSNorm gains of the staged columns
+  };
+  // the RMSNorm factor of each X row this thread stages (the same rows every round)
+  float rrow[IN == IN_RMSNORM ? NX : 1];
+  if constexpr (IN == IN_RMSNORM) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int row = (threadIdx.x + i * kBlock) / (kKC / 4);
+      rrow[i] = rms[min(m0 + row, M - 1)];
+    }
+  }
+  auto load_round = [&](int k0, Round& r) {
 #pragma unroll
     for (int s = 0; s < kNS; ++s)
 #pragma unroll
       for (int bb = 0; bb < kKC / 32; ++bb) {
         const int b = (k0 >> 5) + bb;
-        const int64_t n = nrow[s];
-        cw[s][bb] = nok[s] ? __builtin_nontemporal_load((const uint32_t*)(p.w.codes + n * (K >> 1) + b * 16 + 4 * g)) : 0u;
-        sc[s][bb] = nok[s] ? f16_to_f32(p.w.scales[n * nblk + (b % p.w.lpr) * p.w.nb + b / p.w.lpr]) : 0.f;
+        const int64_t n = min(nrow[s], N - 1);
+        r.cw[s][bb] = __builtin_nontemporal_load((const uint32_t*)(p.w.codes + n * (K >> 1) + b * 16 + 4 * g));
+        r.sc[s][bb] = p.w.scales[n * nblk + (b % p.w.lpr) * p.w.nb + b / p.w.lpr];
       }
-    __syncthreads();  // the previous round's reads of xh / xl are done
-    for (int e = threadIdx.x; e < MT * 16 * (kKC / 4); e += kBlock) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int e = threadIdx.x + i * kBlock;
       const int row = e / (kKC / 4), c4 = (e - row * (kKC / 4)) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (m0 + row < M) {
-        v = *(const float4*)(p.x + (int64_t)(m0 + row) * p.x_stride + k0 + c4);
-        if constexpr (IN == IN_RMSNORM) {
-          const float r = rms[m0 + row];
-          const uint2 gh = *(const uint2*)(p.gamma + k0 + c4);
-          v.x *= r * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
-          v.y *= r * f16_to_f32((uint16_t)(gh.x >> 16));
-          v.z *= r * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
-          v.w *= r * f16_to_f32((uint16_t)(gh.y >> 16));
-        }
+      const int mr = min(m0 + row, M - 1);
+      r.xv[i] = *(const float4*)(p.x + (int64_t)mr * p.x_stride + k0 + c4);
+      if constexpr (IN == IN_RMSNORM) r.gm[i] = *(const uint2*)(p.gamma + k0 + c4);
+    }
+  };
+  auto stage_round = [&](int k0, const Round& r, int buf) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int e = threadIdx.x + i * kBlock;
+      if (e >= MT * 16 * (kKC / 4)) continue;
+      const int row = e / (kKC / 4), c4 = (e - row * (kKC / 4)) * 4;
+      float4 v = m0 + row < M ? r.xv[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (IN == IN_RMSNORM) {
+        const float rr = rrow[i];
+        const uint2 gh = r.gm[i];
+        v.x *= rr * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
+        v.y *= rr * f16_to_f32((uint16_t)(gh.x >> 16));
+        v.z *= rr * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
+        v.w *= rr * f16_to_f32((uint16_t)(gh.y >> 16));
       }
       const int at = row * kXP + (c4 & ~31) + staged_pos(c4 & 31);
       const float vv[4] = {v.x, v.y, v.z, v.w};
       uint16_t hh[4], ll[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 h = (_Float16)vv[i];
-        hh[i] = __builtin_bit_cast(uint16_t, h);
-        ll[i] = __builtin_bit_cast(uint16_t, (_Float16)(vv[i] - (float)h));
+      for (int j = 0; j < 4; ++j) {
+        const _Float16 h = (_Float16)vv[j];
+        hh[j] = __builtin_bit_cast(uint16_t, h);
+        ll[j] = __builtin_bit_cast(uint16_t, (_Float16)(vv[j] - (float)h));
       }
-      *(uint2*)(xh + at) = make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
-      *(uint2*)(xl + at) = make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
+      *(uint2*)(xh[buf] + at) = make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
+      *(uint2*)(xl[buf] + at) = make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
     }
-    __syncthreads();
+  };
+  auto compute_round = [&](const Round& r, int buf) {
 #pragma unroll
     for (int bb = 0; bb < kKC / 32; ++bb) {
       h8_t bf[kNS];
+      float scf[kNS];
 #pragma unroll
-      for (int s = 0; s < kNS; ++s) bf[s] = codes_to_h8(cw[s][bb]);
+      for (int s = 0; s < kNS; ++s) {
+        bf[s] = codes_to_h8(nok[s] ? r.cw[s][bb] : 0x88888888u);  // rows past N: codes 8, value 0
+        scf[s] = nok[s] ? f16_to_f32(r.sc[s][bb]) : 0.f;
+      }
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const int at = (t * 16 + ln) * kXP + bb * 32 + 8 * g;
-        const h8_t ah = *(const h8_t*)(xh + at);
-        const h8_t al = *(const h8_t*)(xl + at);
+        const h8_t ah = *(const h8_t*)(xh[buf] + at);
+        const h8_t al = *(const h8_t*)(xl[buf] + at);
 #pragma unroll
         for (int s = 0; s < kNS; ++s) {
           f4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bf[s], f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bf[s], acc, 0, 0, 0);
-          tot[s][t] += sc[s][bb] * acc;
+          tot[s][t] += scf[s] * acc;
         }
       }
     }
+  };
+
+  Round ra, rb;
+  load_round(k_begin, ra);
+  stage_round(k_begin, ra, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = k_begin; k0 < k_end; k0 += 2 * kKC) {
+    const bool more1 = k0 + kKC < k_end;
+    if (more1) load_round(k0 + kKC, rb);
+    compute_round(ra, buf);
+    if (!more1) break;
+    stage_round(k0 + kKC, rb, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    const bool more2 = k0 + 2 * kKC < k_end;
+    if (more2) load_round(k0 + 2 * kKC, ra);
+    compute_round(rb, buf);
+    if (!more2) break;
+    stage_round(k0 + 2 * kKC, ra, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int s = 0; s < kNS; ++s) {

@@ -101,6 +101,7 @@ struct AttnParams {
   float* out = nullptr;             // [M][H][D]
   int32_t* err = nullptr;
   int32_t* counters = nullptr;      // [batch][G] split arrival counters, zero between launches
+  int32_t mfma = 1;                 // 8..16 query rows per KV head: the matrix-core kernel
 };
 
 // The single-launch batch-1 step of a dense model (bw_persist.hip).
