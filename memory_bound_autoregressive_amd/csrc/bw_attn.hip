@@ -280,8 +280,8 @@ struct MfmaT<2> {  // bf16 cache
   }
 };
 
-constexpr int kVStride = 136;
-constexpr int kMfmaMaxPps = 32;  // most pages of one split of the matrix-core kernel  // LDS row of a staged V page, in 16-bit elements (272 B: conflict-free reads)
+constexpr int kVStride = 136;  // LDS row of a staged V page, in 16-bit elements (272 B: conflict-free reads)
+constexpr int kMfmaMaxPps = 32;  // most pages of one split of the matrix-core kernel
 
 template <int KVDT, int D>
 __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR) {
@@ -379,11 +379,14 @@ __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR
       if (lane == 0) atomicOr(p.err, 1);
       return;
     }
-    // stage V (this wave's buffer; LDS operations of one wave run in order)
+    // stage V (this wave's buffer; the LDS operations of one wave run in order); slots past the
+    // sequence end are written as zeros, so stale or NaN contents never meet a zero probability
 #pragma unroll
     for (int q4 = 0; q4 < D / 32; ++q4) {
       const int k = lane + 64 * q4;
-      *(u32x4*)(vl + (k / (D / 8)) * kVStride + 8 * (k % (D / 8))) = vraw[q4];
+      const int tk = k / (D / 8);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *(u32x4*)(vl + tk * kVStride + 8 * (k % (D / 8))) = pg * kPageTokens + tk < kv_len ? vraw[q4] : z;
     }
     // scores^T: lane holds tokens 4 grp + i of row c16
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -422,25 +425,23 @@ __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR
       ph[i] = __builtin_bit_cast(el4, hb);
       pl[i] = __builtin_bit_cast(el4, lb);
     }
-    // rescale the accumulators: lane holds rows 4 grp + i, whose factors sit in lanes 4 grp + i
-    float al[4];
+    // rescale the accumulators (lane holds rows 4 grp + i, whose factors sit in lanes 4 grp + i),
+    // only when some row's running max moved (rare after the first pages)
+    if (__ballot(alpha != 1.f) != 0) {
+      float al[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
-    // values: B [token 4 grp + i][dim 16 c + c16] from the staged page; slots past the sequence
-    // end are zeroed (stale or NaN contents must not meet a zero probability)
-    bool live[4];
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) live[i] = pg * kPageTokens + 4 * grp + i < kv_len;
+      for (int c = 0; c < NV; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
+    }
+    // values: B [token 4 grp + i][dim 16 c + c16] from the staged page
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
       e4 vb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t bits = live[i] ? vl[(4 * grp + i) * kVStride + 16 * c + c16] : (uint16_t)0;
-        vb[i] = __builtin_bit_cast(el4, bits);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
+      for (int i = 0; i < 4; ++i) vb[i] = __builtin_bit_cast(el4, vl[(4 * grp + i) * kVStride + 16 * c + c16]);
       o[c] = M::mm16(ph, vb, o[c]);
       o[c] = M::mm16(pl, vb, o[c]);
     }

@@ -68,6 +68,39 @@ __device__ __forceinline__ h8_t codes_to_h8(uint32_t c) {
 // for kb < 16, high half otherwise.
 __device__ __forceinline__ int staged_pos(int kb) { return 8 * ((kb & 15) >> 2) + 4 * (kb >> 4); }
 
+// X as fp16 pairs once per product: xh = fp16(x), xl = fp16(x - xh), with x times the row's
+// RMSNorm factor and the gain for IN_RMSNORM, each 32-wide block in the staged order above.
+// Every workgroup of the product then copies 16-byte chunks into LDS with no conversion.
+template <int IN>
+__global__ __launch_bounds__(kBlock) void k_stage_x(const float* __restrict__ x, int64_t stride, int K, int M,
+                                                   const float* __restrict__ rms, const uint16_t* __restrict__ gamma,
+                                                   uint16_t* __restrict__ xh, uint16_t* __restrict__ xl) {
+  const int n4 = K >> 2;
+  const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (e >= (int64_t)M * n4) return;
+  const int m = (int)(e / n4), c4 = (int)(e - (int64_t)m * n4) * 4;
+  float4 v = *(const float4*)(x + (int64_t)m * stride + c4);
+  if constexpr (IN == IN_RMSNORM) {
+    const float r = rms[m];
+    const uint2 gh = *(const uint2*)(gamma + c4);
+    v.x *= r * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
+    v.y *= r * f16_to_f32((uint16_t)(gh.x >> 16));
+    v.z *= r * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
+    v.w *= r * f16_to_f32((uint16_t)(gh.y >> 16));
+  }
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+  uint16_t hh[4], ll[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 h = (_Float16)vv[j];
+    hh[j] = __builtin_bit_cast(uint16_t, h);
+    ll[j] = __builtin_bit_cast(uint16_t, (_Float16)(vv[j] - (float)h));
+  }
+  const int64_t at = (int64_t)m * K + (c4 & ~31) + staged_pos(c4 & 31);
+  *(uint2*)(xh + at) = make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
+  *(uint2*)(xl + at) = make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
+}
+
 // element (m, n) of k-split ks goes to out[ks * ks_stride + m * ldo + n]
 // Rounds of kKC columns are software-pipelined: round r + 1's codes, scales and X values are
 // loaded into registers before round r's products, and its X is converted and staged into the
@@ -75,13 +108,15 @@ __device__ __forceinline__ int staged_pos(int kb) { return 8 * ((kb & 15) >> 2) 
 // latency of a round overlaps the previous round's matrix-core work. Every load is issued
 // unconditionally (rows past N or M are clamped and their values zeroed by selection), so the
 // compiler's wait counts are exact.
-template <int MT, int IN>
-__global__ __launch_bounds__(kBlock) void k_gemm(GemvParams p, int M, int ksplit, const float* __restrict__ rms,
-                                                float* __restrict__ out, int64_t ldo, int64_t ks_stride) {
+template <int MT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemvParams p, int M, int ksplit, const uint16_t* __restrict__ gxh,
+                                                const uint16_t* __restrict__ gxl, float* __restrict__ out, int64_t ldo,
+                                                int64_t ks_stride) {
   constexpr int XB = MT * 16 * kXP;  // one staged buffer (fp16 elements)
   __shared__ __attribute__((aligned(16))) _Float16 xh[2][XB];
   __shared__ __attribute__((aligned(16))) _Float16 xl[2][XB];
-  constexpr int NX = (MT * 16 * (kKC / 4) + kBlock - 1) / kBlock;  // float4 of X per thread per round
+  constexpr int XCH = MT * 16 * (kKC / 8);            // 16-byte chunks of one round's X (each of hi, lo)
+  constexpr int NX = (XCH + kBlock - 1) / kBlock;     // per thread
   const int K = p.w.K, N = p.w.N;
   const int nblk = K >> 5;
   const int n0 = blockIdx.x * kNT;
@@ -109,18 +144,8 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemvParams p, int M, int ksplit
   struct Round {
     uint32_t cw[kNS][kKC / 32];
     uint16_t sc[kNS][kKC / 32];
-    float4 xv[NX];
-    uint2 gm[IN == IN_RMSNORM ? NX : 1];  // RMSNorm gains of the staged columns
+    u32x4 xv[NX][2];  // hi, lo chunks
   };
-  // the RMSNorm factor of each X row this thread stages (the same rows every round)
-  float rrow[IN == IN_RMSNORM ? NX : 1];
-  if constexpr (IN == IN_RMSNORM) {
-#pragma unroll
-    for (int i = 0; i < NX; ++i) {
-      const int row = (threadIdx.x + i * kBlock) / (kKC / 4);
-      rrow[i] = rms[min(m0 + row, M - 1)];
-    }
-  }
   auto load_round = [&](int k0, Round& r) {
 #pragma unroll
     for (int s = 0; s < kNS; ++s)
@@ -133,39 +158,23 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemvParams p, int M, int ksplit
       }
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
-      const int e = threadIdx.x + i * kBlock;
-      const int row = e / (kKC / 4), c4 = (e - row * (kKC / 4)) * 4;
-      const int mr = min(m0 + row, M - 1);
-      r.xv[i] = *(const float4*)(p.x + (int64_t)mr * p.x_stride + k0 + c4);
-      if constexpr (IN == IN_RMSNORM) r.gm[i] = *(const uint2*)(p.gamma + k0 + c4);
+      const int e = min((int)threadIdx.x + i * kBlock, XCH - 1);
+      const int row = e / (kKC / 8), ch = e - row * (kKC / 8);
+      const int64_t at = (int64_t)min(m0 + row, M - 1) * K + k0 + 8 * ch;
+      r.xv[i][0] = *(const u32x4*)(gxh + at);
+      r.xv[i][1] = *(const u32x4*)(gxl + at);
     }
   };
-  auto stage_round = [&](int k0, const Round& r, int buf) {
+  auto stage_round = [&](const Round& r, int buf) {
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int e = threadIdx.x + i * kBlock;
-      if (e >= MT * 16 * (kKC / 4)) continue;
-      const int row = e / (kKC / 4), c4 = (e - row * (kKC / 4)) * 4;
-      float4 v = m0 + row < M ? r.xv[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (IN == IN_RMSNORM) {
-        const float rr = rrow[i];
-        const uint2 gh = r.gm[i];
-        v.x *= rr * f16_to_f32((uint16_t)(gh.x & 0xFFFFu));
-        v.y *= rr * f16_to_f32((uint16_t)(gh.x >> 16));
-        v.z *= rr * f16_to_f32((uint16_t)(gh.y & 0xFFFFu));
-        v.w *= rr * f16_to_f32((uint16_t)(gh.y >> 16));
-      }
-      const int at = row * kXP + (c4 & ~31) + staged_pos(c4 & 31);
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-      uint16_t hh[4], ll[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const _Float16 h = (_Float16)vv[j];
-        hh[j] = __builtin_bit_cast(uint16_t, h);
-        ll[j] = __builtin_bit_cast(uint16_t, (_Float16)(vv[j] - (float)h));
-      }
-      *(uint2*)(xh[buf] + at) = make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
-      *(uint2*)(xl[buf] + at) = make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
+      if (e >= XCH) continue;
+      const int row = e / (kKC / 8), ch = e - row * (kKC / 8);
+      const bool in = m0 + row < M;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *(u32x4*)(xh[buf] + row * kXP + 8 * ch) = in ? r.xv[i][0] : z;
+      *(u32x4*)(xl[buf] + row * kXP + 8 * ch) = in ? r.xv[i][1] : z;
     }
   };
   auto compute_round = [&](const Round& r, int buf) {
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemvParams p, int M, int ksplit
 
   Round ra, rb;
   load_round(k_begin, ra);
-  stage_round(k_begin, ra, 0);
+  stage_round(ra, 0);
   __syncthreads();
   int buf = 0;
   for (int k0 = k_begin; k0 < k_end; k0 += 2 * kKC) {
@@ -203,14 +212,14 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemvParams p, int M, int ksplit
     if (more1) load_round(k0 + kKC, rb);
     compute_round(ra, buf);
     if (!more1) break;
-    stage_round(k0 + kKC, rb, buf ^ 1);
+    stage_round(rb, buf ^ 1);
     __syncthreads();
     buf ^= 1;
     const bool more2 = k0 + 2 * kKC < k_end;
     if (more2) load_round(k0 + 2 * kKC, ra);
     compute_round(rb, buf);
     if (!more2) break;
-    stage_round(k0 + 2 * kKC, ra, buf ^ 1);
+    stage_round(ra, buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
@@ -349,10 +358,22 @@ int64_t gemm_part_elems(int N, int K, int M) { return (int64_t)gemm_ksplit(N, K,
 
 bool gemm_supported(int N, int K) { return K % kKC == 0 && N % 2 == 0 && K >= kKC; }
 
-int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* rms, float* part, hipStream_t s) {
-  if (M < 1 || !gemm_supported(p.w.N, p.w.K)) return -2;
+int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* rms, float* part, uint16_t* xs,
+                hipStream_t s) {
+  if (M < 1 || !gemm_supported(p.w.N, p.w.K) || xs == nullptr) return -2;
   if (in_mode != IN_PLAIN && in_mode != IN_RMSNORM) return -2;
   if (in_mode == IN_RMSNORM && rms == nullptr) return -2;
+  // X once as staged fp16 pairs (xs: [2][M][K])
+  uint16_t* gxh = xs;
+  uint16_t* gxl = xs + (int64_t)M * p.w.K;
+  {
+    const int64_t n4 = (int64_t)M * (p.w.K >> 2);
+    const dim3 sg((unsigned)((n4 + kBlock - 1) / kBlock));
+    if (in_mode == IN_RMSNORM)
+      hipLaunchKernelGGL(k_stage_x<IN_RMSNORM>, sg, dim3(kBlock), 0, s, p.x, p.x_stride, p.w.K, M, rms, p.gamma, gxh, gxl);
+    else
+      hipLaunchKernelGGL(k_stage_x<IN_PLAIN>, sg, dim3(kBlock), 0, s, p.x, p.x_stride, p.w.K, M, rms, p.gamma, gxh, gxl);
+  }
   const int ks = gemm_ksplit(p.w.N, p.w.K, M);
   const int mg = (M + kMaxRowsWG - 1) / kMaxRowsWG;
   const int mt = std::min(8, (M + 15) / 16);
@@ -363,12 +384,9 @@ int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* r
   const int64_t ks_stride = (int64_t)M * p.w.N;
   if (out == nullptr) return -2;
   const dim3 grid((p.w.N + kNT - 1) / kNT, ks, mg);
-#define BW_G(MT_)                                                                                                \
-  if (mt <= MT_) {                                                                                               \
-    if (in_mode == IN_RMSNORM)                                                                                   \
-      hipLaunchKernelGGL((k_gemm<MT_, IN_RMSNORM>), grid, dim3(kBlock), 0, s, p, M, ks, rms, out, ldo, ks_stride); \
-    else                                                                                                         \
-      hipLaunchKernelGGL((k_gemm<MT_, IN_PLAIN>), grid, dim3(kBlock), 0, s, p, M, ks, rms, out, ldo, ks_stride);   \
+#define BW_G(MT_)                                                                                     \
+  if (mt <= MT_) {                                                                                    \
+    hipLaunchKernelGGL((k_gemm<MT_>), grid, dim3(kBlock), 0, s, p, M, ks, gxh, gxl, out, ldo, ks_stride); \
   } else
   BW_G(1) BW_G(2) BW_G(4) BW_G(8) {}
 #undef BW_G

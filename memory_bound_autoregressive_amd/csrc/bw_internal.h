@@ -169,7 +169,8 @@ int launch_fill16(uint16_t* dst, size_t n, uint16_t bits, hipStream_t s);
 bool gemm_supported(int N, int K);
 int gemm_ksplit(int N, int K, int M);
 int64_t gemm_part_elems(int N, int K, int M);
-int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* rms, float* part, hipStream_t s);
+int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* rms, float* part, uint16_t* xs,
+                hipStream_t s);  // xs: [2][M][K] fp16 staging of X
 int launch_rowrms(const float* x, int64_t stride, int K, float eps, int M, float* r, hipStream_t s);
 int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, int32_t* out, hipStream_t s);
 

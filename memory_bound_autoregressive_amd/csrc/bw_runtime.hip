@@ -147,6 +147,7 @@ struct bw_model {
   int max_splits = 0;
   // batched path: steps with at least gemm_min_rows rows run the dense matrices as MFMA GEMMs
   float* gemm_part = nullptr;    // k-split partials of the largest dense GEMM
+  uint16_t* gemm_x = nullptr;    // X of a GEMM as staged fp16 pairs [2][T][K max]
   float* rms = nullptr;          // [T] RMSNorm factors
   int gemm_min_rows = 8;
   // single-launch batch-1 step (dense models): exchange buffers and switches
@@ -553,6 +554,10 @@ extern "C" int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed
       m->gemm_part = (float*)p;
       if ((rc = ws_alloc(m, sizeof(float) * T, &p))) return bail(rc);
       m->rms = (float*)p;
+      int64_t kmax = 0;
+      for (const auto& nk : dims) kmax = std::max(kmax, nk[1]);
+      if ((rc = ws_alloc(m, sizeof(uint16_t) * 2 * T * kmax, &p))) return bail(rc);
+      m->gemm_x = (uint16_t*)p;
     }
     if ((rc = ws_alloc(m, 256, &p))) return bail(rc);
     m->err = (int32_t*)p;
@@ -791,7 +796,7 @@ static int run_dense(bw_model* m, int in_mode, int epi, GemvParams p, int M, hip
     }
     if (launch_rowrms(p.x, p.x_stride, p.w.K, p.eps, M, m->rms, s)) return -1;
   }
-  return launch_gemm(in_mode, epi, p, M, m->rms, m->gemm_part, s);
+  return launch_gemm(in_mode, epi, p, M, m->rms, m->gemm_part, m->gemm_x, s);
 }
 
 // enqueue every kernel of one step on stream s (arguments already validated)
