@@ -84,6 +84,74 @@ def cpu_baseline(cfg: dict, ctx: int, seconds: float) -> dict:
                       f"(context synthesised, not prefilled), {el:.1f} s"}
 
 
+def run_prefill(args) -> int:
+    """Chunked prefill of the dense-9b workload's 2048-token prompt (chunks of --chunk tokens, one
+    step each on the matrix-core path; logits for the last chunk only), timed over --steps runs
+    after --warmup runs, each into a fresh cache state (positions restart at 0)."""
+    import numpy as np
+    import torch
+
+    import memory_bound_autoregressive_amd as bw
+    from memory_bound_autoregressive_amd import configs
+    from memory_bound_autoregressive_amd.session import Session
+
+    cfg = configs.DENSE_9B
+    P, C = args.prompt, args.chunk
+    K = args.steps if args.steps_set else 5
+    W = args.warmup if args.warmup_set else 1
+    torch.cuda.set_device(0)
+    t_load = time.perf_counter()
+    s = Session(cfg, seed=cfg["seed"], max_len=[P + 1], max_tokens=C, pool_seed=cfg["seed"] + 1)
+    print(f"[bench] prefill-9b: model + pool ready in {time.perf_counter() - t_load:.1f} s", file=sys.stderr, flush=True)
+    prompt = np.random.default_rng(cfg["seed"]).integers(0, cfg["vocab"], P).astype(np.int32)
+    dev = "cuda"
+    chunks = []
+    for c0 in range(0, P, C):
+        c1 = min(P, c0 + C)
+        chunks.append((torch.from_numpy(prompt[c0:c1]).to(dev), torch.tensor([c0], dtype=torch.int32, device=dev), c1 - c0))
+    logits = torch.empty((chunks[-1][2], cfg["vocab"]), dtype=torch.float32, device=dev)
+    argmax = torch.empty(chunks[-1][2], dtype=torch.int32, device=dev)
+
+    def run():
+        for i, (tk, sl, t) in enumerate(chunks):
+            last = i == len(chunks) - 1
+            bw.bw_decode_step(s.model, s.pool, tk, sl, s.page_table, 1, t, s.max_pages,
+                              logits if last else None, argmax if last else None)
+
+    for _ in range(W):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    if bw.bw_check_device_error(s.model) != 0:
+        print("[bench] device error flag set", file=sys.stderr)
+        return 1
+    ms = e0.elapsed_time(e1) / K
+    s.close()
+    d, L = cfg["d_model"], cfg["n_layers"]
+    H, G, D, F = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn_dim"]
+    w_layers = ((H + 2 * G) * D * d + d * H * D + 3 * F * d) * L
+    flop = 2.0 * w_layers * P + 2.0 * cfg["vocab"] * d * chunks[-1][2]  # weights x tokens (lm_head: last chunk)
+    flop += 2.0 * 2 * H * D * L * P * (P + 1) / 2.0                     # causal attention (QK and PV)
+    tflops = flop / (ms * 1e-3) / 1e12
+    value = P * 1000.0 / ms
+    print(f"[bench] prefill-9b: {P} tokens in chunks of {C}: {ms:.2f} ms, {value:.0f} tok/s, "
+          f"{tflops:.1f} TFLOP/s of useful products", file=sys.stderr, flush=True)
+    out = {
+        "metric": "prefill tok/s (dense-9b, chunked)", "value": round(value, 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (fp16 hi/lo and bf16 parts on the matrix cores)", "data": "synthetic",
+        "config": {"workload": "prefill-9b", "prompt": P, "chunk": C, "chunks": len(chunks), "seed": cfg["seed"]},
+        "useful_tflops": round(tflops, 2),
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def run_workload(args) -> int:
     """The other timed workloads (synthesised contexts, kernel chain): dense-27b and moe-35b-a3b
     decode at batch 1, and verify-9b, a speculative loop over 32 sequences (t = 4: the last
@@ -203,8 +271,9 @@ def main() -> int:
     ap.add_argument("--cooperative", action="store_true",
                     help="single-launch step through the cooperative launch API")
     ap.add_argument("--workload", default="dense-9b",
-                    choices=("dense-9b", "dense-27b", "moe-35b-a3b", "verify-9b"),
+                    choices=("dense-9b", "dense-27b", "moe-35b-a3b", "verify-9b", "prefill-9b"),
                     help="dense-9b (default): the headline line; the others time their own workload")
+    ap.add_argument("--chunk", type=int, default=256, help="prefill-9b: tokens per prefill step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -225,6 +294,8 @@ def main() -> int:
         print(f"bench.py: this build runs the decode step on one GPU; --gpus {args.gpus} "
               f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.workload == "prefill-9b":
+        return run_prefill(args)
     if args.workload != "dense-9b":
         return run_workload(args)
 

@@ -283,6 +283,9 @@ struct MfmaT<2> {  // bf16 cache
 constexpr int kVStride = 136;  // LDS row of a staged V page, in 16-bit elements (272 B: conflict-free reads)
 constexpr int kMfmaMaxPps = 32;  // most pages of one split of the matrix-core kernel
 
+// Grid (split, KV head x row tile, sequence): a workgroup takes 16 of the QR query rows of its KV
+// head (a verify step has one tile; a prefill chunk of t tokens has ceil(QR / 16)), over the pages
+// of its split that the tile's last position reaches.
 template <int KVDT, int D>
 __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR) {
   using M = MfmaT<KVDT>;
@@ -291,10 +294,12 @@ __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR
   constexpr int NC = D / 32;  // 32-dim chunks (scores)
   constexpr int NV = D / 16;  // 16-dim chunks (values)
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int n_tiles = (QR + 15) >> 4;
+  const int s = blockIdx.x, g = blockIdx.y / n_tiles, tile = blockIdx.y - g * n_tiles, b = blockIdx.z;
   const int rep = p.H / p.G;
   const int base_pos = p.seq_lens[b];
-  const int kv_len = base_pos + p.t;
+  const int r_last = min(QR, 16 * tile + 16) - 1;   // last real row of the tile
+  const int kv_len = base_pos + r_last / rep + 1;   // positions the tile's rows reach
   int n_pg = (kv_len + kPageTokens - 1) / kPageTokens;
   const int pg_cap = min(p.max_pages, p.max_splits * p.pages_per_split);
   if (n_pg > pg_cap) {
@@ -314,8 +319,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR
   // then known to be uniform, so no load needs a per-lane loop
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, grp = lane >> 4;  // column / row-block of the 16x16 tiles
-  // query row c16 (padding rows past QR: zero query, no causal limit, never written)
-  const int qr = c16;
+  // query row 16 tile + c16 (padding rows past QR: zero query, no causal limit, never written)
+  const int qr = 16 * tile + c16;
   const bool real = qr < QR;
   const int ti = real ? qr / rep : 0, hr = real ? qr - ti * rep : 0;
   const int qpos = real ? base_pos + ti : 0x7fffffff;
@@ -477,16 +482,17 @@ __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR
     l_lds[wave][c16] = lrun;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < QR * D; e += kBlock) {
-    const int r = e / D, d = e - r * D;
-    const float Mx = fmaxf(fmaxf(m_lds[0][r], m_lds[1][r]), fmaxf(m_lds[2][r], m_lds[3][r]));
+  const int rows = min(16, QR - 16 * tile);
+  for (int e = threadIdx.x; e < rows * D; e += kBlock) {
+    const int rl = e / D, d = e - rl * D, r = 16 * tile + rl;
+    const float Mx = fmaxf(fmaxf(m_lds[0][rl], m_lds[1][rl]), fmaxf(m_lds[2][rl], m_lds[3][rl]));
     float a = 0.f, l = 0.f;
     if (Mx != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float f = __expf(m_lds[w][r] - Mx);
-        a = fmaf(acc_lds[w][r * D + d], f, a);
-        l = fmaf(l_lds[w][r], f, l);
+        const float f = __expf(m_lds[w][rl] - Mx);
+        a = fmaf(acc_lds[w][rl * D + d], f, a);
+        l = fmaf(l_lds[w][rl], f, l);
       }
     }
     const int rt = r / rep, rh = r - rt * rep;
@@ -508,7 +514,9 @@ __global__ __launch_bounds__(kBlock) void k_attn_merge(AttnParams p) {
   __shared__ float red[16];
   const int h = blockIdx.x, row = blockIdx.y;
   const int b = row / p.t;
-  const int kv_len = p.seq_lens[b] + p.t;
+  // the splits this row's own position reaches (later splits of a longer step were written fully
+  // masked for it, or, for a prefill tile that ends earlier, not at all)
+  const int kv_len = p.seq_lens[b] + (row - b * p.t) + 1;
   const int n_pg = min((kv_len + kPageTokens - 1) / kPageTokens, min(p.max_pages, p.max_splits * p.pages_per_split));
   const int n_split = min((n_pg + p.pages_per_split - 1) / p.pages_per_split, 1024);
   {
@@ -576,10 +584,12 @@ static int launch_mfma(const AttnParams& p, int kv_dtype, int batch, int qr, hip
   AttnParams m = p;
   m.pages_per_split = kMfmaPagesPerSplit;
   m.max_splits = min((p.max_pages + kMfmaPagesPerSplit - 1) / kMfmaPagesPerSplit, p.max_splits);
+  const int tiles = (qr + 15) / 16;
+  if ((int64_t)m.G * tiles > 65535) return -2;
   if (kv_dtype == 1)
-    hipLaunchKernelGGL((k_attn_split_mfma<1, D>), dim3(m.max_splits, m.G, batch), dim3(kBlock), 0, s, m, qr);
+    hipLaunchKernelGGL((k_attn_split_mfma<1, D>), dim3(m.max_splits, m.G * tiles, batch), dim3(kBlock), 0, s, m, qr);
   else
-    hipLaunchKernelGGL((k_attn_split_mfma<2, D>), dim3(m.max_splits, m.G, batch), dim3(kBlock), 0, s, m, qr);
+    hipLaunchKernelGGL((k_attn_split_mfma<2, D>), dim3(m.max_splits, m.G * tiles, batch), dim3(kBlock), 0, s, m, qr);
   hipLaunchKernelGGL(k_attn_merge<D>, dim3(m.H, batch * m.t), dim3(kBlock), 0, s, m);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -587,7 +597,7 @@ static int launch_mfma(const AttnParams& p, int kv_dtype, int batch, int qr, hip
 int launch_attention(const AttnParams& p, int kv_dtype, int batch, hipStream_t s) {
   int rc;
   const int qr = p.t * (p.H / p.G);
-  if (p.mfma && qr >= 8 && qr <= 16) {  // verify steps: both products on the matrix cores
+  if (p.mfma && qr >= 8) {  // verify steps and prefill chunks: both products on the matrix cores
     if (p.D == 128) return launch_mfma<128>(p, kv_dtype, batch, qr, s);
     if (p.D == 64) return launch_mfma<64>(p, kv_dtype, batch, qr, s);
   }

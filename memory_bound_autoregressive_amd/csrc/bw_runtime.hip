@@ -922,7 +922,9 @@ static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, co
       trace_mark(m, BW_K_MOE_DOWN, l, 1, s);
     }
   }
-  // final RMSNorm + lm_head + argmax
+  // final RMSNorm + lm_head + argmax; a step that asks for neither (a prefill chunk before the
+  // last) ends with the layers
+  if (!logits_out && !argmax_out) return BW_OK;
   GemvParams lm;
   lm.w = m->lm;
   lm.n_rows = m->lm.N;

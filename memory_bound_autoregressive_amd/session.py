@@ -81,6 +81,25 @@ class Session:
                        logits, argmax)
         return logits, argmax
 
+    def prefill_chunked(self, prompt: list[int] | np.ndarray, chunk: int) -> torch.Tensor:
+        """Prefill one sequence (batch 1) in chunks of up to `chunk` tokens, each one step with
+        t = chunk rows (matrix-core GEMMs and attention); the chunks before the last ask for no
+        logits, so they skip the lm_head (bw24 deep-dive page, section 5 stage 3: the prompt goes in
+        chunks, the cache grows with each, logits come back for the last). Returns the logits of
+        the prompt's last position. Needs max_tokens >= chunk."""
+        assert self.batch == 1
+        n = len(prompt)
+        out = None
+        for c0 in range(0, n, chunk):
+            c1 = min(n, c0 + chunk)
+            tk = torch.tensor([int(v) for v in prompt[c0:c1]], dtype=torch.int32, device=self.device)
+            sl = torch.tensor([c0], dtype=torch.int32, device=self.device)
+            if c1 == n:
+                out, _ = self.step(tk, sl, t=c1 - c0)
+            else:
+                bw_decode_step(self.model, self.pool, tk, sl, self.page_table, 1, c1 - c0, self.max_pages, None, None)
+        return out[-1]
+
     def prefill(self, prompt: list[int] | np.ndarray, b: int = 0) -> torch.Tensor:
         """Feed a prompt of one sequence (batch 1) token by token; returns the last logits."""
         assert self.batch == 1
