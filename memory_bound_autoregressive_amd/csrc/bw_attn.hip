@@ -542,8 +542,17 @@ __global__ __launch_bounds__(kBlock) void k_attn_merge(AttnParams p) {
     // 3. values: thread (d, quarter) sums a quarter of the splits, quarters combined in order
     const int d = threadIdx.x % D, qq = threadIdx.x / D;  // kBlock / D quarters
     constexpr int NQ = kBlock / D;
+    // loads in batches of 8 (one wait per batch), sums in the same split order
     float a = 0.f;
-    for (int sp = qq; sp < n_split; sp += NQ) a = fmaf(part[sp * (D + 2) + d], fac[sp], a);
+    int sp = qq;
+    for (; sp + 7 * NQ < n_split; sp += 8 * NQ) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(sp + u * NQ) * (D + 2) + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a = fmaf(v[u], fac[sp + u * NQ], a);
+    }
+    for (; sp < n_split; sp += NQ) a = fmaf(part[sp * (D + 2) + d], fac[sp], a);
     __shared__ float asum[kBlock];
     asum[threadIdx.x] = a;
     __syncthreads();

@@ -61,15 +61,28 @@ int launch_argmax_final(const float* val, const int32_t* idx, int parts, int M, 
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// Router logits r = W_r h with h = RMSNorm(x) * gamma, W_r fp16 [E][d]. Each wave takes rows; the
-// 64 lanes split d, 8 fp16 weights (one 16-byte load) per step.
+// Router logits r = W_r h with h = RMSNorm(x) * gamma, W_r fp16 [E][d]. One row per wave: its
+// 16-byte weight loads (8 fp16 per lane per step, at most 8 steps) go out first, as buffer loads
+// (past the row end they read zeros), so they are in flight during the RMSNorm reduction.
+constexpr int kRouterMaxSteps = 8;  // d <= 4096
 __global__ __launch_bounds__(kBlock) void k_router(const uint16_t* __restrict__ wr, int E, int d,
                                                    const float* __restrict__ x,
                                                    const uint16_t* __restrict__ gamma, float eps,
-                                                   float* __restrict__ logits, int rows_per_block) {
+                                                   float* __restrict__ logits) {
   extern __shared__ float h[];
   __shared__ float red[16];
   const int m = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+  const bool row_ok = e < E;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(wr + (int64_t)(row_ok ? e : 0) * d), 0, d * 2, 0x00020000);
+  u32x4 raw[kRouterMaxSteps];
+#pragma unroll
+  for (int st = 0; st < kRouterMaxSteps; ++st) {
+    const int k = lane * 8 + st * kWave * 8;
+    raw[st] = __builtin_amdgcn_raw_buffer_load_b128(rw, k < d ? k * 2 : 0x7FFFFFF0, 0, 2);
+  }
   const float* xr = x + (int64_t)m * d;
   float ss = 0.f;
   for (int k = threadIdx.x; k < d; k += kBlock) ss = fmaf(xr[k], xr[k], ss);
@@ -77,92 +90,74 @@ __global__ __launch_bounds__(kBlock) void k_router(const uint16_t* __restrict__ 
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
   for (int k = threadIdx.x; k < d; k += kBlock) h[k] = xr[k] * r * f16_to_f32(gamma[k]);
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row0 = blockIdx.x * rows_per_block;
-  for (int e = row0 + wave; e < min(E, row0 + rows_per_block); e += 4) {
-    const uint16_t* wrow = wr + (int64_t)e * d;
-    float acc = 0.f;
-    for (int k = lane * 8; k < d; k += kWave * 8) {
-      u32x4 raw = load_stream16(wrow + k);
+  float acc = 0.f;
+#pragma unroll
+  for (int st = 0; st < kRouterMaxSteps; ++st) {
+    const int k = lane * 8 + st * kWave * 8;
+    if (k < d) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc = fmaf(f16_to_f32((uint16_t)(raw[i] & 0xFFFFu)), h[k + 2 * i], acc);
-        acc = fmaf(f16_to_f32((uint16_t)(raw[i] >> 16)), h[k + 2 * i + 1], acc);
+        acc = fmaf(f16_to_f32((uint16_t)(raw[st][i] & 0xFFFFu)), h[k + 2 * i], acc);
+        acc = fmaf(f16_to_f32((uint16_t)(raw[st][i] >> 16)), h[k + 2 * i + 1], acc);
       }
     }
-    acc = wave_sum(acc);
-    if (lane == 0) logits[(int64_t)m * E + e] = acc;
   }
+  acc = wave_sum(acc);
+  if (lane == 0 && row_ok) logits[(int64_t)m * E + e] = acc;
 }
 
 int launch_router(const uint16_t* wr, int E, int d, const float* x, const uint16_t* gamma,
                   float eps, int M, float* logits, hipStream_t s) {
-  const int rpb = 8;
-  hipLaunchKernelGGL(k_router, dim3((E + rpb - 1) / rpb, M), dim3(kBlock), sizeof(float) * d, s, wr, E,
-                     d, x, gamma, eps, logits, rpb);
+  if (d > kRouterMaxSteps * kWave * 8 || d % 8 != 0) return -2;
+  hipLaunchKernelGGL(k_router, dim3((E + 3) / 4, M), dim3(kBlock), sizeof(float) * d, s, wr, E, d, x, gamma, eps,
+                     logits);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// top-k of the router logits (descending, ties to the lower expert index) and the renormalised
-// gates softmax(r)_e / sum_{e' in top-k} softmax(r)_e' = exp(r_e - r_max) / sum_sel exp(r - r_max)
+// top-k of the router logits (descending, ties to the lower expert index; a NaN logit ranks as
+// -inf) and the renormalised gates softmax(r)_e / sum_{e' in top-k} softmax(r)_e'
+// = exp(r_e - r_max) / sum_sel exp(r - r_max). One pass: the rank of logit e is the number of
+// logits ahead of it, and e is chosen when its rank is below k.
+// (The float4 reads cover indices below E rounded down to 4; the rest are read one by one.)
 __global__ __launch_bounds__(kBlock) void k_topk(const float* __restrict__ logits, int E, int k,
                                                  int32_t* __restrict__ sel, float* __restrict__ gates) {
   extern __shared__ float r[];
-  __shared__ float wv[4];
-  __shared__ int wi[4];
   __shared__ int chosen[64];
   const int m = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += kBlock) r[e] = logits[(int64_t)m * E + e];
-  __syncthreads();
-  for (int round = 0; round < k; ++round) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int e = threadIdx.x; e < E; e += kBlock) {
-      bool taken = false;
-      for (int q = 0; q < round; ++q) taken |= (chosen[q] == e);
-      float v = r[e];
-      if (!taken && (v > bv || (v == bv && e < bi) || bi == 0x7fffffff)) { bv = v; bi = e; }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o);
-      int oi = __shfl_xor(bi, o);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
-    }
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { wv[w] = bv; wi[w] = bi; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float b0 = wv[0];
-      int i0 = wi[0];
-      for (int q = 1; q < 4; ++q)
-        if (wi[q] != 0x7fffffff && (i0 == 0x7fffffff || wv[q] > b0 || (wv[q] == b0 && wi[q] < i0))) { b0 = wv[q]; i0 = wi[q]; }
-      if (i0 == 0x7fffffff) {
-        // no comparable logit left (NaN): take the lowest index not chosen yet
-        for (int e = 0; e < E && i0 == 0x7fffffff; ++e) {
-          bool taken = false;
-          for (int q = 0; q < round; ++q) taken |= (chosen[q] == e);
-          if (!taken) i0 = e;
-        }
-      }
-      chosen[round] = i0;
-    }
-    __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kBlock) {
+    const float v = logits[(int64_t)m * E + e];
+    r[e] = v != v ? -INFINITY : v;
   }
-  if (threadIdx.x == 0) {
-    float mx = r[chosen[0]];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kBlock) {
+    const float v = r[e];
+    int rank = 0;
+    int j = 0;
+    // 16-byte LDS reads, four in flight per step
+#pragma unroll 4
+    for (; j + 4 <= E; j += 4) {
+      const float4 u = *(const float4*)(r + j);
+      rank += (u.x > v || (u.x == v && j < e)) + (u.y > v || (u.y == v && j + 1 < e)) +
+              (u.z > v || (u.z == v && j + 2 < e)) + (u.w > v || (u.w == v && j + 3 < e));
+    }
+    for (; j < E; ++j) rank += (r[j] > v || (r[j] == v && j < e)) ? 1 : 0;
+    if (rank < k) chosen[rank] = e;
+  }
+  __syncthreads();
+  if (threadIdx.x < k) {
+    const float mx = r[chosen[0]];
     float z = 0.f;
     for (int q = 0; q < k; ++q) z += __expf(r[chosen[q]] - mx);
-    for (int q = 0; q < k; ++q) {
-      sel[(int64_t)m * k + q] = chosen[q];
-      gates[(int64_t)m * k + q] = __expf(r[chosen[q]] - mx) / z;
-    }
+    const int q = threadIdx.x;
+    sel[(int64_t)m * k + q] = chosen[q];
+    gates[(int64_t)m * k + q] = __expf(r[chosen[q]] - mx) / z;
   }
 }
 
 int launch_topk(const float* logits, int E, int k, int M, int32_t* sel, float* gates,
                 hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(M), dim3(kBlock), sizeof(float) * E, s, logits, E, k, sel, gates);
+  if (k > 64 || k > E) return -2;
+  hipLaunchKernelGGL(k_topk, dim3(M), dim3(kBlock), sizeof(float) * ((E + 3) & ~3), s, logits, E, k, sel, gates);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
