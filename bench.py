@@ -153,8 +153,8 @@ def run_prefill(args) -> int:
 
 
 def run_workload(args) -> int:
-    """The other timed workloads (synthesised contexts, kernel chain): dense-27b and moe-35b-a3b
-    decode at batch 1, and verify-9b, a speculative loop over 32 sequences (t = 4: the last
+    """The other timed workloads (synthesised contexts): dense-27b and moe-35b-a3b decode at batch 1
+    (as one launch per step where the shape has one, else the kernel chain), and verify-9b, a speculative loop over 32 sequences (t = 4: the last
     committed token and three drafts drawn uniformly from the vocabulary, greedy acceptance on the
     device). One JSON line, like the default run, with this workload's own metric."""
     import numpy as np
@@ -183,6 +183,7 @@ def run_workload(args) -> int:
         lens = [cfg["context"]]
         s = Session(cfg, seed=seed, max_len=[lens[0] + W + K + 2], max_tokens=1, pool_seed=seed + 1)
         s.synthesize(seed + 7, lens)
+    single = bool(bw.bw_set_single_launch(s.model, 0 if args.chain else 1)) and not args.chain and B * t == 1
     torch.cuda.synchronize()
     print(f"[bench] {args.workload}: model + pool ({s.n_pages} pages) ready in {time.perf_counter() - t_load:.1f} s",
           file=sys.stderr, flush=True)
@@ -242,7 +243,8 @@ def run_workload(args) -> int:
         "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": args.workload, "step": "kernel chain (hipGraph replay)", "batch": B, "t": t,
+        "config": {"workload": args.workload, "step": "single launch" if single else "kernel chain (hipGraph replay)",
+                   "batch": B, "t": t,
                    "context": "synthesised", "context_range": [int(ctx0.min()), int(ctx1.max())],
                    "context_sum_start": int(ctx0.sum()), "seed": seed},
         "achieved_hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),

@@ -259,7 +259,9 @@ int bw_debug_single_launch_deadline(bw_model* model, uint64_t ticks);
 /* Measurement hook of the single-launch step: while stamps_dev (device, n >= 16 * n_layers + 8
  * uint64) is set, workgroup 0 writes the GPU's 100 MHz real-time counter at each phase start and
  * when the phase's input has arrived: [16 l + 2 k] and [16 l + 2 k + 1] for phases k = 0..5 (QKV,
- * attention, merge, O, gate/up, down) of layer l; [16 L + 0 / 1] lm_head start / input ready,
+ * attention, merge, O, gate/up, down) of layer l (MoE models: k = 0..6, QKV, attention, merge, O,
+ * router, top-k + expert gate/up, expert down, with [16 l + 14] / [16 l + 15] the start / end of
+ * the expert gate/up matrix pass); [16 L + 0 / 1] lm_head start / input ready,
  * [16 L + 2] final argmax, [16 L + 3] step end, [16 L + 4] step start. NULL turns it off. With
  * n >= (16 n_layers + 8) x the step's workgroup count (one per CU), every workgroup w writes the
  * same record at w (16 n_layers + 8) (the final argmax and step end only in workgroup 0).

@@ -106,9 +106,11 @@ struct AttnParams {
 
 // The single-launch batch-1 step of a dense model (bw_persist.hip).
 struct PLayer {
-  Mat qkv, o, gu, dn;
+  Mat qkv, o, gu, dn;               // gu, dn: dense FFN (unused for MoE)
   const uint16_t* attn_norm = nullptr;
   const uint16_t* ffn_norm = nullptr;
+  const uint16_t* router = nullptr; // MoE: fp16 [E][d]
+  ExpertTab ex;                     // MoE: expert matrices (routed, then shared)
 };
 
 constexpr int BW_DERR_PERSIST_BIT = 8;
@@ -143,6 +145,11 @@ struct PersistParams {
   int32_t* err = nullptr;
   uint32_t* abort_flag = nullptr;
   uint64_t deadline_ticks = 50000000ull;  // one wait gives up after 0.5 s (100 MHz counter)
+  // MoE (moe != 0): E experts, top_k routed + n_shared shared, each FFN width Fe
+  int32_t moe = 0, E = 0, top_k = 0, n_shared = 0, Fe = 0;
+  uint32_t* xr = nullptr;           // [E]: router logits (exchange)
+  int32_t* sel_out = nullptr;       // optional: selected experts of layer l at sel_out[l * sel_stride + k]
+  int64_t sel_stride = 0;
   uint64_t* stamps = nullptr;       // optional [L * 16 + 8]: real-time counter at phase starts (workgroup 0)
   int32_t stamp_stride = 0;         // > 0: every workgroup w writes its own record at w * stamp_stride
   bool plain_launch = false;        // ordinary launch instead of the cooperative one (see the runtime)
@@ -183,5 +190,8 @@ int launch_spec_accept(int32_t* tokens, const int32_t* argmax, float* logits, in
 int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                    bool query_only);
 int launch_persist_reset(const PersistParams& p, int n_q, int n_p, int n_a, int n_d, int n_f, int n_arg, hipStream_t s);
+// MoE form (router, top-k and expert phases): -2 when the shape has no instantiation
+int launch_persist_moe(const PersistParams& p, int d, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
+                       bool query_only);
 
 }  // namespace bw

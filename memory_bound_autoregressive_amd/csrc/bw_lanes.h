@@ -47,6 +47,19 @@ __device__ __forceinline__ float wmax(float v) {
   v = fmaxf(v, xor8(v));
   return max_xor32(max_xor16(v));
 }
+// maximum of an unsigned 64-bit value over each aligned row of 16 lanes (every lane active)
+__device__ __forceinline__ uint64_t max16_u64(uint64_t v) {
+  auto step = [](uint64_t a, uint64_t o) { return o > a ? o : a; };
+#define BW_MAX16_STEP(CTRL)                                                                                       \
+  v = step(v, ((uint64_t)(uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false) << 32) | \
+                  (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false))
+  BW_MAX16_STEP(0xB1);   // quad_perm [1, 0, 3, 2]
+  BW_MAX16_STEP(0x4E);   // quad_perm [2, 3, 0, 1]
+  BW_MAX16_STEP(0x141);  // row_half_mirror
+  BW_MAX16_STEP(0x128);  // row_ror:8
+#undef BW_MAX16_STEP
+  return v;
+}
 // sum over aligned groups of n lanes, n a power of two up to 64 (wave-uniform)
 __device__ __forceinline__ float sum_lanes(float v, int n) {
   if (n >= 2) v += dpp_mov<0xB1>(v);

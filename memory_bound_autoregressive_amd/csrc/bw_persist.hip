@@ -185,7 +185,37 @@ constexpr int kMaxSplitPages = 256;  // pages of one attention split (workgroup)
 constexpr int kMaxSplit = kPT / 4;  // attention splits per KV head (workgroups / KV heads)
 constexpr int kMrgProd = 2048;      // (attention output, split) products per workgroup
 // merge scratch: (m, l) of [2 heads][splits], factors [2][splits], denominators [2], products
-constexpr int kMrg = 4 * kMaxSplit + 2 * kMaxSplit + 8 + kMrgProd;
+// MoE scratch inside mrg (free outside the merge phase), in floats: top-k candidates [kMoeMaxE]
+// (uint64 keys), maxima of 16-key rows [32] (uint64), the threshold (uint64) and candidate count,
+// chosen experts [64] and their keys [64] (uint64), slot gates, slot matrix pointers [slots][4],
+// and the gate/up matrix pointers of every expert [E + shared][2]
+constexpr int kMoeMaxE = 512, kMoeCand = 0, kMoeGmax = kMoeCand + 2 * kMoeMaxE, kMoeThr = kMoeGmax + 64;
+constexpr int kMoeCnt = kMoeThr + 2, kMoeChosen = kMoeThr + 8, kMoeChosenKey = kMoeChosen + 64;
+constexpr int kMoeGate = kMoeChosenKey + 128, kMoePtr = kMoeGate + 64;
+constexpr int kMoeMaxSlots = 32;
+constexpr int kMoeAll = kMoePtr + 2 * 4 * kMoeMaxSlots;
+constexpr int kMoeMaxEx = 480;  // routed + shared experts
+constexpr int kMrgMerge = 4 * kMaxSplit + 2 * kMaxSplit + 8 + kMrgProd;
+constexpr int kMrgMoe = kMoeAll + 2 * 2 * kMoeMaxEx;
+constexpr int kMrg = kMrgMerge > kMrgMoe ? kMrgMerge : kMrgMoe;
+static_assert(kMoeGmax % 4 == 0 && kMoeThr % 2 == 0 && kMoeChosenKey % 2 == 0 && kMoePtr % 4 == 0 && kMoeAll % 4 == 0,
+              "MoE tables aligned");
+
+// Router logit as a 64-bit key whose unsigned order is the top-k order: the float's bits mapped
+// to an order-preserving integer (NaN as -inf, -0 as +0) above the complemented expert index, so
+// that of equal logits the lower index ranks first and no two keys are equal. Zero is below every
+// key (padding).
+__device__ __forceinline__ uint64_t moe_key(float v, int e) {
+  if (v != v) v = -INFINITY;
+  if (v == 0.f) v = 0.f;
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ float moe_key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
 
 // ---- staging of a GEMV input from the exchange ------------------------------------------------
 // xs gets the K values (times the RMSNorm factor and gain when NORM), bs the per-block sums.
@@ -407,6 +437,98 @@ __device__ __forceinline__ void gemv_rest(int tid, const Mat w, int r0, int r1, 
   }
 }
 
+// As gemv_rest, with each group's loads done by load(gi, group): the MoE phases pick the matrix
+// of a row step or of a block column.
+template <int LPR, int NB, int RW, bool DB, typename LoadF>
+__device__ __forceinline__ void gemv_rest_f(int tid, int r0, int r1, PGroup<LPR, NB, RW>& cur, const Lds& s,
+                                            LoadF&& load) {
+  constexpr int GROUP = (kWave / LPR) * RW;
+  const int n_groups = (r1 - r0 + GROUP - 1) / GROUP;
+  int gi = wave_of(tid);
+  if (gi >= n_groups) return;
+  if constexpr (DB) {
+    PGroup<LPR, NB, RW> alt;
+    while (true) {
+      load(gi + kPW, alt);
+      pcompute<LPR, NB, RW>(tid, cur, r0, r1, s);
+      gi += kPW;
+      if (gi >= n_groups) break;
+      load(gi + kPW, cur);
+      pcompute<LPR, NB, RW>(tid, alt, r0, r1, s);
+      gi += kPW;
+      if (gi >= n_groups) break;
+    }
+  } else {
+    while (true) {
+      pcompute<LPR, NB, RW>(tid, cur, r0, r1, s);
+      gi += kPW;
+      if (gi >= n_groups) break;
+      load(gi, cur);
+    }
+  }
+}
+
+// ---- MoE expert matrices ----------------------------------------------------------------------
+// mp: per slot (top_k routed experts in rank order, then the shared ones) the device pointers of
+// its gate/up codes and scales and its down codes and scales, staged in LDS after the top-k.
+__device__ __forceinline__ const void* lds_ptr(const uint64_t* mp, int i) {
+  const uint64_t v = mp[i];
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Rows [r0, r1) of the concatenated gate/up matrices (slot k holds rows [2 Fe k, 2 Fe (k + 1)), its
+// expert's own rows 0 .. 2 Fe - 1, gate and up interleaved). One row per wave per row step
+// (LPR = 64), so the matrix of each row step is uniform.
+template <int LPR, int NB, int RW>
+__device__ __forceinline__ void pload_moe_gu(int tid, const uint64_t* mp, int Fe, int r0, int r1, int gi,
+                                             PGroup<LPR, NB, RW>& g) {
+  static_assert(LPR == kWave, "one row per wave per row step");
+  const int j = tid & 63;
+  constexpr int nblk = LPR * NB;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = r0 + gi * RW + r;
+    g.row[r] = row;
+    const bool ok = row < r1;
+    const int slot = ok ? row / (2 * Fe) : 0, lr = row - slot * 2 * Fe;
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)lds_ptr(mp, slot * 4 + 0), 0, 2 * Fe * (nblk * 16), kRsrc3);
+    const __amdgpu_buffer_rsrc_t rsc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)lds_ptr(mp, slot * 4 + 1), 0, 2 * Fe * (nblk * 2), kRsrc3);
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      g.q[r][c] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? lr * (nblk * 16) + (j + LPR * c) * 16 : kOOB, 0, kNT);
+      g.sc[r][c] = __builtin_amdgcn_raw_buffer_load_b16(rsc, ok ? (lr * nblk + j * NB + c) * 2 : kOOB, 0, 0);
+    }
+  }
+}
+
+// Rows [r0, r1) of the down projection over the concatenated expert outputs: a lane's block
+// column c is block j of slot c's matrix [d][Fe] (Fe = 32 LPR), so every load of column c reads
+// slot c's matrix.
+template <int LPR, int NB, int RW>
+__device__ __forceinline__ void pload_moe_dn(int tid, const uint64_t* mp, int d, int r0, int r1, int gi,
+                                             PGroup<LPR, NB, RW>& g) {
+  constexpr int RPW = kWave / LPR;
+  const int lane = tid & 63, j = lane % LPR, rsub = lane / LPR;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = r0 + (gi * RW + r) * RPW + rsub;
+    g.row[r] = row;
+    const bool ok = row < r1;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      const __amdgpu_buffer_rsrc_t rc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)lds_ptr(mp, c * 4 + 2), 0, d * (LPR * 16), kRsrc3);
+      const __amdgpu_buffer_rsrc_t rsc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)lds_ptr(mp, c * 4 + 3), 0, d * (LPR * 2), kRsrc3);
+      g.q[r][c] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? row * (LPR * 16) + j * 16 : kOOB, 0, kNT);
+      g.sc[r][c] = __builtin_amdgcn_raw_buffer_load_b16(rsc, ok ? (row * LPR + j) * 2 : kOOB, 0, 0);
+    }
+  }
+}
+
 // ---- attention over the paged cache -----------------------------------------------------------
 
 template <int KVDT>
@@ -467,7 +589,8 @@ struct alignas(16) AttnLds {
 
 // RWQ, RWO, RWG, RWF: row steps per register group of the QKV, O, gate/up and down passes; a
 // group that covers a wave's whole share of a phase is loaded in full before the phase's wait.
-template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF>
+template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF,
+          bool MOE>
 __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   constexpr int KD = LPR_D * NB_D * 32;  // d_model (= Hq * D)
@@ -789,7 +912,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         page = page_n;
         load_page<D>(lane, pool_rs, p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
       }
-      stamp(p, l * 16 + 12);
+      if constexpr (!MOE) stamp(p, l * 16 + 12);  // MoE: the down phase's slot
       // reduce the value partials over the token groups, then merge the waves
       static_assert(NV == 8 || NV == 16, "value lanes per token group: 8 or 16");
 #pragma unroll
@@ -814,7 +937,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         }
       }
       __syncthreads();
-      stamp(p, l * 16 + 13);
+      if constexpr (!MOE) stamp(p, l * 16 + 13);
       if (active) {
         for (int e = tid; e < QR * D; e += kPT) {
           const int qr = e / D, dd = e - qr * D;
@@ -957,6 +1080,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       }
     }
 
+    if constexpr (!MOE) {
     // ================= gate/up + SwiGLU =================
     stamp(p, l * 16 + 8);
     {
@@ -1002,6 +1126,201 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         s.resid[r - d0] = v;
         xstore(p.xx, r, v, tout);
       }
+    }
+    } else {
+    static_assert((KMAX + KMAX / 32 + kMaxRows + kMaxOwn + 32) % 4 == 0, "MoE scratch 16-byte aligned");
+    // ================= MoE router (one row of the router per workgroup) =================
+    stamp(p, l * 16 + 8);
+    {
+      const int tid = phase_tid();
+      const int wave = wave_of(tid);
+      XStage<KD> xin;
+      stage_issue<KD, true>(tid, p.xm, Ly.ffn_norm, xin);
+      // this workgroup's router row, 4 fp16 per thread, issued before the input wait
+      const bool has_row = w < p.E;
+      const bool mine = 4 * tid < KD;
+      const __amdgpu_buffer_rsrc_t rr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Ly.router + (int64_t)(has_row ? w : 0) * KD), 0, KD * 2, kRsrc3);
+      const auto wv = __builtin_amdgcn_raw_buffer_load_b64(rr, mine ? tid * 8 : kOOB, 0, kNT);
+      // the gate/up matrices' addresses of every expert, for the slots the top-k fills next
+      const int n_ex = p.E + p.n_shared;
+      const auto pgc = __builtin_amdgcn_raw_buffer_load_b64(xrsrc(Ly.ex.gu_codes, (int64_t)n_ex * 8),
+                                                            tid < n_ex ? tid * 8 : kOOB, 0, 0);
+      const auto pgs = __builtin_amdgcn_raw_buffer_load_b64(xrsrc(Ly.ex.gu_scales, (int64_t)n_ex * 8),
+                                                            tid < n_ex ? tid * 8 : kOOB, 0, 0);
+      __syncthreads();
+      stage_finish<KD, true>(tid, p.xm, tout, p.eps, xin, s, ctl);
+      if (bail) return;
+      stamp(p, l * 16 + 9);
+      // elements 4 tid .. +3 from the staged layout (the second half of a block is staged / 16);
+      // the staged input stays in LDS for the expert gate/up phase
+      float dot = 0.f;
+      if (mine) {
+        const float4 xv = *(const float4*)xs_chunk(s.xs, tid >> 3, tid & 7);
+        dot = fmaf(f16_to_f32((uint16_t)(wv[0] & 0xFFFFu)), xv.x, dot);
+        dot = fmaf(f16_to_f32((uint16_t)(wv[0] >> 16)), xv.y, dot);
+        dot = fmaf(f16_to_f32((uint16_t)(wv[1] & 0xFFFFu)), xv.z, dot);
+        dot = fmaf(f16_to_f32((uint16_t)(wv[1] >> 16)), xv.w, dot);
+        if ((tid & 7) >= 4) dot *= 16.f;
+      }
+      dot = wsum(dot);
+      if ((tid & 63) == 0) s.red[wave] = dot;
+      if (tid < n_ex) {
+        uint32_t* all = reinterpret_cast<uint32_t*>(s.mrg + kMoeAll) + 4 * tid;
+        all[0] = pgc[0];
+        all[1] = pgc[1];
+        all[2] = pgs[0];
+        all[3] = pgs[1];
+      }
+      __syncthreads();
+      if (tid == 0 && has_row) {
+        float tot = 0.f;
+#pragma unroll
+        for (int v = 0; v < kPW; ++v) tot += s.red[v];
+        xstore(p.xr, w, tot, tout);
+      }
+    }
+
+    // ================= MoE top-k + expert gate/up + SwiGLU =================
+    stamp(p, l * 16 + 10);
+    {
+      const int tid = phase_tid();
+      uint64_t* cand = reinterpret_cast<uint64_t*>(s.mrg + kMoeCand);  // [Ep] top-k candidates
+      uint64_t* gmax = reinterpret_cast<uint64_t*>(s.mrg + kMoeGmax);  // [Ep / 16] row maxima
+      uint64_t* thr = reinterpret_cast<uint64_t*>(s.mrg + kMoeThr);
+      int* cnt = reinterpret_cast<int*>(s.mrg + kMoeCnt);
+      int* chosen = reinterpret_cast<int*>(s.mrg + kMoeChosen);              // [top_k]
+      uint64_t* ckey = reinterpret_cast<uint64_t*>(s.mrg + kMoeChosenKey);   // [top_k]
+      float* gate = s.mrg + kMoeGate;                                        // [slots]
+      uint64_t* mp = reinterpret_cast<uint64_t*>(s.mrg + kMoePtr);           // [slots][4]
+      const uint64_t* all = reinterpret_cast<const uint64_t*>(s.mrg + kMoeAll);  // [E + shared][2]
+      const int Ep = (p.E + 31) & ~31;
+      const int nrows = Ep / 16;
+      // Top-k, descending, ties to the lower index, over keys whose unsigned order is that order.
+      // The maxima of the 16-key rows are distinct keys, so the k-th largest of them bounds the
+      // k-th largest key from below: only keys at or above it can be chosen, and a candidate's rank
+      // among all keys is its rank among the candidates.
+      uint64_t my = 0;
+      {
+        const __amdgpu_buffer_rsrc_t r = xrsrc(p.xr, (int64_t)p.E * 4);
+        int idx[1] = {tid < p.E ? tid : -1};
+        uint32_t word[1];
+        poll_words_issue<1>(r, idx, word);
+        poll_words_wait<1>(r, idx, tout, word, ctl);
+        if (tid < p.E) my = moe_key(xdec(word[0]), tid);
+        const uint64_t rmax = max16_u64(my);  // every lane, so no DPP source lane is inactive
+        if (tid < Ep) {
+          cand[tid] = 0ull;
+          if ((tid & 15) == 0) gmax[tid >> 4] = rmax;
+        }
+      }
+      __syncthreads();
+      if (bail) return;
+      stamp(p, l * 16 + 11);
+      if (tid < nrows && nrows >= p.top_k) {
+        const uint64_t g = gmax[tid];
+        int rank = 0;
+        for (int j = 0; j < nrows; ++j) {
+          const uint64_t o = gmax[j];
+          rank += (o > g || (o == g && j < tid)) ? 1 : 0;
+        }
+        if (rank == p.top_k - 1) thr[0] = g;
+      }
+      if (tid == 0) {
+        cnt[0] = 0;
+        if (nrows < p.top_k) thr[0] = 0ull;
+      }
+      __syncthreads();
+      const bool is_cand = tid < p.E && my >= thr[0];
+      if (is_cand) cand[atomicAdd(cnt, 1)] = my;
+      __syncthreads();
+      if (is_cand) {
+        const int nc = (cnt[0] + 15) & ~15;  // entries past the count hold zero keys
+        int rank = 0;
+        for (int j = 0; j < nc; j += 16) {
+          ulong2 u[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) u[q] = *(const ulong2*)(cand + j + 2 * q);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) rank += (u[q].x > my ? 1 : 0) + (u[q].y > my ? 1 : 0);
+        }
+        if (rank < p.top_k) {
+          chosen[rank] = tid;
+          ckey[rank] = my;
+        }
+      }
+      __syncthreads();
+      // slot k: the k-th routed expert (gate: its softmax weight renormalised over the top-k) or a
+      // shared expert (gate 1); its matrices' pointers go to LDS
+      // (the down matrices' addresses are loaded here and land in LDS after the gate/up pass)
+      const int e_slot = tid < NB_F ? (tid < p.top_k ? chosen[tid] : p.E + (tid - p.top_k)) : 0;
+      const int n_ex = p.E + p.n_shared;
+      const auto pdc = __builtin_amdgcn_raw_buffer_load_b64(xrsrc(Ly.ex.dn_codes, (int64_t)n_ex * 8),
+                                                            tid < NB_F ? e_slot * 8 : kOOB, 0, 0);
+      const auto pds = __builtin_amdgcn_raw_buffer_load_b64(xrsrc(Ly.ex.dn_scales, (int64_t)n_ex * 8),
+                                                            tid < NB_F ? e_slot * 8 : kOOB, 0, 0);
+      if (tid < NB_F) {
+        const int k = tid;
+        const int e = e_slot;
+        float g = 1.f;
+        if (k < p.top_k) {
+          const float mx = moe_key_value(ckey[0]);
+          float z = 0.f;
+          for (int q = 0; q < p.top_k; ++q) z += __expf(moe_key_value(ckey[q]) - mx);
+          g = __expf(moe_key_value(ckey[k]) - mx) / z;
+        }
+        gate[k] = g;
+        mp[k * 4 + 0] = all[e * 2 + 0];
+        mp[k * 4 + 1] = all[e * 2 + 1];
+        if (w == 0 && k < p.top_k && p.sel_out != nullptr) p.sel_out[(int64_t)l * p.sel_stride + k] = e;
+      }
+      __syncthreads();
+      stamp(p, l * 16 + 14);
+      PGroup<LPR_D, NB_D, RWG> cur;
+      pload_moe_gu<LPR_D, NB_D, RWG>(tid, mp, p.Fe, g0, g1, wave_of(tid), cur);
+      gemv_rest_f<LPR_D, NB_D, RWG, (RWG < 5)>(tid, g0, g1, cur, s, [&](int gi, PGroup<LPR_D, NB_D, RWG>& gg) {
+        pload_moe_gu<LPR_D, NB_D, RWG>(tid, mp, p.Fe, g0, g1, gi, gg);
+      });
+      if (tid < NB_F) {
+        uint32_t* dn = reinterpret_cast<uint32_t*>(mp + tid * 4 + 2);
+        dn[0] = pdc[0];
+        dn[1] = pdc[1];
+        dn[2] = pds[0];
+        dn[3] = pds[1];
+      }
+      __syncthreads();
+      stamp(p, l * 16 + 15);
+      for (int pi = tid; 2 * pi < g1 - g0; pi += kPT) {
+        const int r = g0 + 2 * pi;
+        const int slot = r / (2 * p.Fe), i = (r - slot * 2 * p.Fe) >> 1;
+        const float gv = s.ydot[2 * pi], uv = s.ydot[2 * pi + 1];
+        xstore(p.xf, slot * p.Fe + i, gate[slot] * (silu(gv) * uv), tout);
+      }
+    }
+
+    // ================= MoE down (over the concatenated gated expert outputs) + residual ========
+    stamp(p, l * 16 + 12);
+    {
+      const int tid = phase_tid();
+      const uint64_t* mp = reinterpret_cast<const uint64_t*>(s.mrg + kMoePtr);
+      XStage<KF> xin;
+      stage_issue<KF, false>(tid, p.xf, nullptr, xin);
+      PGroup<LPR_F, NB_F, RWF> cur;
+      pload_moe_dn<LPR_F, NB_F, RWF>(tid, mp, KD, d0, d1, wave_of(tid), cur);
+      __syncthreads();
+      stage_finish<KF, false>(tid, p.xf, tout, 0.f, xin, s, ctl);
+      if (bail) return;
+      stamp(p, l * 16 + 13);
+      gemv_rest_f<LPR_F, NB_F, RWF, (RWF < 2)>(tid, d0, d1, cur, s, [&](int gi, PGroup<LPR_F, NB_F, RWF>& gg) {
+        pload_moe_dn<LPR_F, NB_F, RWF>(tid, mp, KD, d0, d1, gi, gg);
+      });
+      __syncthreads();
+      for (int r = d0 + tid; r < d1; r += kPT) {
+        const float v = s.resid[r - d0] + s.ydot[r - d0];
+        s.resid[r - d0] = v;
+        xstore(p.xx, r, v, tout);
+      }
+    }
     }
   }
 
@@ -1126,6 +1445,7 @@ __global__ void k_persist_reset(PersistParams p, int n_q, int n_p, int n_a, int 
     p.xx[i] = xenc(0.f, bad_in);
   }
   if (i < n_f) p.xf[i] = xenc(0.f, bad);
+  if (p.xr != nullptr && i < p.E) p.xr[i] = xenc(0.f, bad);
   if (i < n_arg) p.xarg[i] = (uint64_t)((epoch + 2) & 3u) << 62;
   if (i == 0) p.abort_flag[0] = 0u;
 }
@@ -1140,9 +1460,10 @@ static size_t persist_lds_bytes() {
          sizeof(AttnLds<D, QR>);
 }
 
-template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF>
+template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF,
+          bool MOE = false>
 static int launch_persist_t(const PersistParams& p, int nwg, hipStream_t s, bool query_only) {
-  auto kern = k_persist<LPR_D, NB_D, LPR_F, NB_F, KVDT, D, QR, RWQ, RWO, RWG, RWF>;
+  auto kern = k_persist<LPR_D, NB_D, LPR_F, NB_F, KVDT, D, QR, RWQ, RWO, RWG, RWF, MOE>;
   const size_t lds = persist_lds_bytes<LPR_D, NB_D, LPR_F, NB_F, KVDT, D, QR>();
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return -1;
   if (query_only) {
@@ -1175,8 +1496,25 @@ int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, in
   return -2;
 }
 
+// MoE shapes: (d, slots x expert width, head dim, query heads per KV head). The gate/up pass reads
+// one row per wave per row step (LPR_D = 64), the down pass one slot's Fe / 32 blocks per lane
+// column (Fe = 32 LPR_F, NB_F = slots).
+int launch_persist_moe(const PersistParams& p, int d, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
+                       bool query_only) {
+  const int slots = p.top_k + p.n_shared;
+#define BW_PM(DM, FE, SL, LD, ND, LF, DD, QR, RQ, RO, RG, RF)                                                    \
+  if (d == DM && p.Fe == FE && slots == SL && D == DD && rep == QR) {                                           \
+    static_assert(DM == LD * ND * 32 && FE == LF * 32, "d and Fe match the lane split");                        \
+    return kv_dtype == 1 ? launch_persist_t<LD, ND, LF, SL, 1, DD, QR, RQ, RO, RG, RF, true>(p, nwg, s, query_only) \
+                         : launch_persist_t<LD, ND, LF, SL, 2, DD, QR, RQ, RO, RG, RF, true>(p, nwg, s, query_only); \
+  }
+  BW_PM(2048, 512, 9, 64, 1, 16, 128, 4, 2, 1, 5, 1)  // moe-35b-a3b: 12 / 8 / 36 / 8 rows per workgroup
+#undef BW_PM
+  return -2;
+}
+
 int launch_persist_reset(const PersistParams& p, int n_q, int n_p, int n_a, int n_d, int n_f, int n_arg, hipStream_t s) {
-  const int n = std::max({n_q, n_p, n_a, n_d, n_f, n_arg});
+  const int n = std::max({n_q, n_p, n_a, n_d, n_f, n_arg, p.xr != nullptr ? p.E : 0});
   hipLaunchKernelGGL(k_persist_reset, dim3((n + 255) / 256), dim3(256), 0, s, p, n_q, n_p, n_a, n_d, n_f, n_arg);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -336,17 +336,36 @@ static int check_shape(const bw_model_config& c) {
   return 0;
 }
 
-// The single-launch step (bw_persist.hip) for a dense model whose shape has an instantiation:
-// one workgroup per CU, the geometry limits of the kernel checked here, exchange buffers
-// allocated and tagged. Models without one keep the kernel chain only.
+// The single-launch step (bw_persist.hip) for a model whose shape has an instantiation: one
+// workgroup per CU, the geometry limits of the kernel checked here, exchange buffers allocated
+// and tagged. Models without one keep the kernel chain only.
+// MoE: every routed and shared expert has the same width Fe, and the F of the layout below is
+// the concatenation of the slots (top_k routed, then the shared ones), slots x Fe.
+static int launch_persist_any(const bw_model* m, const PersistParams& p, int nwg, hipStream_t s, bool query_only) {
+  const auto& c = m->c;
+  if (is_moe(c))
+    return launch_persist_moe(p, c.d_model, c.kv_dtype, c.head_dim, c.n_q_heads / c.n_kv_heads, nwg, s, query_only);
+  return launch_persist(p, c.d_model, c.ffn_dim, c.kv_dtype, c.head_dim, c.n_q_heads / c.n_kv_heads, nwg, s,
+                        query_only);
+}
+
 static int persist_setup(bw_model* m) {
   const auto& c = m->c;
-  if (is_moe(c)) return BW_OK;
+  const bool moe = is_moe(c);
   int dev = 0, ncu = 0;
   HIP_OK(hipGetDevice(&dev));
   HIP_OK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-  const int d = c.d_model, H = c.n_q_heads, G = c.n_kv_heads, D = c.head_dim, F = c.ffn_dim;
+  const int d = c.d_model, H = c.n_q_heads, G = c.n_kv_heads, D = c.head_dim;
+  const int slots = moe ? c.top_k + c.n_shared : 0;
+  const int F = moe ? slots * c.expert_ffn : c.ffn_dim;
   const int nwg = ncu;
+  if (moe) {
+    // the router phase gives each workgroup one expert's logit, and the top-k reads them with
+    // one thread each; the expert slots' pointers and gates sit in a fixed LDS table
+    const bool moe_fits = (c.n_shared == 0 || c.shared_ffn == c.expert_ffn) && c.n_experts <= nwg &&
+                          c.n_experts <= 512 && c.n_experts + c.n_shared <= 480 && slots <= 32 && c.top_k <= 64;
+    if (!moe_fits) return BW_OK;
+  }
   const int S = nwg / G;
   const int Rm = (H * D + nwg - 1) / nwg;
   const int Rd = (d + nwg - 1) / nwg;
@@ -358,11 +377,21 @@ static int persist_setup(bw_model* m) {
                     Rg <= 1024 && (H / G) * D <= 4096;
   if (!fits) return BW_OK;
   PersistParams& p = m->pp;
-  if (launch_persist(p, d, F, c.kv_dtype, D, H / G, nwg, nullptr, true) != 0) return BW_OK;
+  if (moe) {
+    p.moe = 1;
+    p.E = c.n_experts;
+    p.top_k = c.top_k;
+    p.n_shared = c.n_shared;
+    p.Fe = c.expert_ffn;
+  }
+  if (launch_persist_any(m, p, nwg, nullptr, true) != 0) {
+    p = PersistParams{};
+    return BW_OK;
+  }
   std::vector<PLayer> layers(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerDev& Ld = m->L[l];
-    layers[l] = PLayer{Ld.qkv, Ld.o, Ld.gu, Ld.dn, Ld.attn_norm, Ld.ffn_norm};
+    layers[l] = PLayer{Ld.qkv, Ld.o, Ld.gu, Ld.dn, Ld.attn_norm, Ld.ffn_norm, Ld.router, Ld.ex};
   }
   void* ptr;
   if (int rc = ws_alloc(m, sizeof(PLayer) * layers.size(), &ptr)) return rc;
@@ -393,6 +422,12 @@ static int persist_setup(bw_model* m) {
   }
   if (int rc = ws_alloc(m, sizeof(uint64_t) * nwg, &ptr)) return rc;
   p.xarg = (uint64_t*)ptr;
+  if (moe) {
+    if (int rc = ws_alloc(m, sizeof(uint32_t) * c.n_experts, &ptr)) return rc;
+    p.xr = (uint32_t*)ptr;
+    p.sel_out = m->sel;  // row 0 of each layer's selection table
+    p.sel_stride = (int64_t)c.max_tokens * c.top_k;
+  }
 
   if (int rc = ws_alloc(m, 256, &ptr)) return rc;
   HIP_OK(hipMemset(ptr, 0, 256));
@@ -977,9 +1012,7 @@ extern "C" int bw_decode_step(bw_model* m, bw_kv_pool* pool, const int32_t* toke
     p.max_pages = max_pages;
     p.logits = logits_out;
     p.argmax = argmax_out;
-    const auto& c = m->c;
-    if (launch_persist(p, c.d_model, c.ffn_dim, c.kv_dtype, c.head_dim, c.n_q_heads / c.n_kv_heads, m->persist_nwg, s,
-                       false))
+    if (launch_persist_any(m, p, m->persist_nwg, s, false))
       return fail(BW_EHIP, "single-launch step failed to launch");
     return BW_OK;
   }

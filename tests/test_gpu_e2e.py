@@ -22,6 +22,12 @@ pytestmark = pytest.mark.gpu
 MOE_SMALL = dict(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=0, vocab=512,
                  rms_eps=1e-6, rope_base=1e6, kv_dtype="bf16", page_tokens=16, n_experts=16, top_k=3,
                  expert_ffn=128, n_shared=1, shared_ffn=128, name="moe-small")
+# the MoE shape of the single-launch step (d 2048, nine slots of width 512, head dim 128, four query
+# heads per KV head) at two layers and a small vocabulary
+MOE_2K = dict(n_layers=2, d_model=2048, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn_dim=0, vocab=512,
+              rms_eps=1e-6, rope_base=1e6, kv_dtype="bf16", page_tokens=16, n_experts=32, top_k=8,
+              expert_ffn=512, n_shared=1, shared_ffn=512, name="moe-2k", prompt=12, steps=20)
+SINGLE_LAUNCH_SHAPES = ("tiny", "moe-2k")  # workloads whose shape has a single-launch instantiation
 ROUTER_TAU = 1e-4
 
 
@@ -81,18 +87,20 @@ def _compare(g, gam, o, where):
 @pytest.mark.parametrize("cfg,seed,gemm,single", [(configs.TINY, 1001, None, 1), (configs.TINY, 1004, None, 2),
                                                   (configs.TINY, 1003, None, 0),
                                                   (MOE_SMALL, 1011, None, 1), (configs.TINY, 1002, 1, 0),
-                                                  (MOE_SMALL, 1012, 1, 0)],
-                         ids=["tiny", "tiny-cooperative", "tiny-chain", "moe-small", "tiny-gemm", "moe-small-gemm"])
+                                                  (MOE_SMALL, 1012, 1, 0), (MOE_2K, 1013, None, 1),
+                                                  (MOE_2K, 1014, None, 2), (MOE_2K, 1015, None, 0)],
+                         ids=["tiny", "tiny-cooperative", "tiny-chain", "moe-small", "tiny-gemm", "moe-small-gemm",
+                              "moe-2k", "moe-2k-cooperative", "moe-2k-chain"])
 def test_prompt_then_greedy_decode(cfg, seed, gemm, single):
-    """single: batch-1 steps as one launch (1: ordinary, 2: cooperative; dense models), 0: the
+    """single: batch-1 steps as one launch (1: ordinary, 2: cooperative; shapes with an instantiation), 0: the
     kernel chain.
     gemm = 1 runs every dense matrix of every chain step on the matrix-core GEMM path."""
     prompt_len, steps = cfg.get("prompt", 16), cfg.get("steps", 32)
     rng = np.random.default_rng(seed)
     prompt = rng.integers(0, cfg["vocab"], prompt_len)
     p = Pair(cfg, seed, prompt_len + steps + 1, gemm_min_rows=gemm, single=single)
-    if single and not cfg.get("n_experts", 0):
-        assert p.single, "a dense model of this shape has the single-launch step"
+    if single and cfg["name"] in SINGLE_LAUNCH_SHAPES:
+        assert p.single, "a model of this shape has the single-launch step"
     worst = 0.0
     try:
         for i, tok in enumerate(prompt):
