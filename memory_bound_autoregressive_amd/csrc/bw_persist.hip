@@ -63,6 +63,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(const void* p, int64_t b
 __device__ __forceinline__ u32x4 xload4(__amdgpu_buffer_rsrc_t r, int idx4) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, idx4 * 16, 0, kCohSC1);
 }
+// A buffer descriptor whose words are provably uniform: a pointer kept across phases may sit in
+// vector registers, and a descriptor built from those would make every load through it a loop
+// over lanes; readfirstlane puts the words back in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, __builtin_amdgcn_readfirstlane(bytes),
+                                           kRsrc3);
+}
 __device__ __forceinline__ uint32_t xload1(__amdgpu_buffer_rsrc_t r, int idx) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, kCohSC1);
 }
@@ -702,8 +711,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     const uint32_t tin = base_tag + (uint32_t)l;       // T(l - 1)
     const uint32_t tout = base_tag + (uint32_t)l + 1;  // T(l)
     uint16_t* pool = p.pool + (int64_t)l * p.layer_elems;
-    const __amdgpu_buffer_rsrc_t pool_rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)pool, 0, (int)min<int64_t>(p.layer_elems * 2, 0x7FFFFFF0), kRsrc3);
+    const int pool_bytes = (int)min<int64_t>(p.layer_elems * 2, 0x7FFFFFF0);
     PageRegs<D> kv_first;
 
     // ================= QKV =================
@@ -724,7 +732,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       // this layer's first attention page, after the input wait (waits count loads in issue
       // order): its id is known, only the new token's slot changes in this step, and that slot
       // is taken from the exchange
-      load_page<D>(lane, pool_rs, p.page_elems, p.n_pages, first_page, ag, kv_first);
+      load_page<D>(lane, uniform_rsrc(pool, pool_bytes), p.page_elems, p.n_pages, first_page, ag, kv_first);
       gemv_rest<LPR_D, NB_D, RWQ, (RWQ < 3)>(tid, Ly.qkv, q0, q1, cur, s);
       __syncthreads();
       if (2 * tid < q1 - q0) {
@@ -910,7 +918,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           __builtin_amdgcn_wave_barrier();
         }
         page = page_n;
-        load_page<D>(lane, pool_rs, p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
+        load_page<D>(lane, uniform_rsrc(pool, pool_bytes), p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
       }
       if constexpr (!MOE) stamp(p, l * 16 + 12);  // MoE: the down phase's slot
       // reduce the value partials over the token groups, then merge the waves
