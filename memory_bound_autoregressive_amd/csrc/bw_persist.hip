@@ -393,7 +393,10 @@ __device__ __forceinline__ void pcompute(int tid, const PGroup<LPR, NB, RW>& g, 
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
     __builtin_amdgcn_sched_barrier(0);
-    const int b = j + LPR * c;
+    // with many blocks per lane, the block index goes through an opaque move, so the chunk
+    // addresses are formed per block instead of all NB x 8 of them being hoisted into registers
+    int b = j + LPR * c;
+    if constexpr (NB > 12) asm volatile("v_mov_b32 %0, %1" : "=v"(b) : "v"(j + LPR * c));
     float4 xb[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) xb[k] = *(const float4*)xs_chunk(s.xs, b, k);
@@ -605,6 +608,12 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   constexpr int KD = LPR_D * NB_D * 32;  // d_model (= Hq * D)
   constexpr int KF = LPR_F * NB_F * 32;  // ffn dim
   constexpr int KMAX = KD > KF ? KD : KF;
+  // A phase alternates two register groups (the next one's loads in flight while one is computed)
+  // only where a group is small: at most 12 blocks per lane (60 registers of codes and scales).
+  constexpr bool DBQ = RWQ < 3 && RWQ * NB_D <= 12, DBO = RWO < 2 && RWO * NB_D <= 12;
+  constexpr bool DBG = RWG < 6 && RWG * NB_D <= 12, DBF = RWF < 2 && RWF * NB_F <= 12;
+  // lm_head row steps per group: about eight blocks per lane
+  constexpr int LMRW = NB_D <= 2 ? kLmRW : (kLmRW * 2 >= NB_D ? kLmRW * 2 / NB_D : 1);
   __shared__ int bail;
   Lds s;
   s.xs = lds;
@@ -733,7 +742,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       // order): its id is known, only the new token's slot changes in this step, and that slot
       // is taken from the exchange
       load_page<D>(lane, uniform_rsrc(pool, pool_bytes), p.page_elems, p.n_pages, first_page, ag, kv_first);
-      gemv_rest<LPR_D, NB_D, RWQ, (RWQ < 3)>(tid, Ly.qkv, q0, q1, cur, s);
+      gemv_rest<LPR_D, NB_D, RWQ, DBQ>(tid, Ly.qkv, q0, q1, cur, s);
       __syncthreads();
       if (2 * tid < q1 - q0) {
         // one RoPE pair (q, k) or two adjacent value dims per thread; k and v are rounded to the
@@ -1079,7 +1088,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       stage_finish<KD, false>(tid, p.xa, tout, 0.f, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 7);
-      gemv_rest<LPR_D, NB_D, RWO, (RWO < 2)>(tid, Ly.o, d0, d1, cur, s);
+      gemv_rest<LPR_D, NB_D, RWO, DBO>(tid, Ly.o, d0, d1, cur, s);
       __syncthreads();
       for (int r = d0 + tid; r < d1; r += kPT) {
         const float v = s.resid[r - d0] + s.ydot[r - d0];
@@ -1104,7 +1113,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       stage_finish<KD, true>(tid, p.xm, tout, p.eps, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 9);
-      gemv_rest<LPR_D, NB_D, RWG, (RWG < 6)>(tid, Ly.gu, g0, g1, cur, s);
+      gemv_rest<LPR_D, NB_D, RWG, DBG>(tid, Ly.gu, g0, g1, cur, s);
       __syncthreads();
       for (int pi = tid; 2 * pi < g1 - g0; pi += kPT) {
         const float gv = s.ydot[2 * pi], uv = s.ydot[2 * pi + 1];
@@ -1127,7 +1136,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       stage_finish<KF, false>(tid, p.xf, tout, 0.f, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 11);
-      gemv_rest<LPR_F, NB_F, RWF, (RWF < 2)>(tid, Ly.dn, d0, d1, cur, s);
+      gemv_rest<LPR_F, NB_F, RWF, DBF>(tid, Ly.dn, d0, d1, cur, s);
       __syncthreads();
       for (int r = d0 + tid; r < d1; r += kPT) {
         const float v = s.resid[r - d0] + s.ydot[r - d0];
@@ -1319,7 +1328,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       stage_finish<KF, false>(tid, p.xf, tout, 0.f, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 13);
-      gemv_rest_f<LPR_F, NB_F, RWF, (RWF < 2)>(tid, d0, d1, cur, s, [&](int gi, PGroup<LPR_F, NB_F, RWF>& gg) {
+      gemv_rest_f<LPR_F, NB_F, RWF, DBF>(tid, d0, d1, cur, s, [&](int gi, PGroup<LPR_F, NB_F, RWF>& gg) {
         pload_moe_dn<LPR_F, NB_F, RWF>(tid, mp, KD, d0, d1, gi, gg);
       });
       __syncthreads();
@@ -1352,9 +1361,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     const Mat lm = p.lm;
     for (int c0 = v0; c0 < v1; c0 += kMaxRows) {
       const int c1 = min(v1, c0 + kMaxRows);
-      PGroup<LPR_D, NB_D, kLmRW> cur;
-      gemv_first<LPR_D, NB_D, kLmRW>(tid, lm, c0, c1, cur);
-      gemv_rest<LPR_D, NB_D, kLmRW, true>(tid, lm, c0, c1, cur, s);
+      PGroup<LPR_D, NB_D, LMRW> cur;
+      gemv_first<LPR_D, NB_D, LMRW>(tid, lm, c0, c1, cur);
+      gemv_rest<LPR_D, NB_D, LMRW, true>(tid, lm, c0, c1, cur, s);
       __syncthreads();
       for (int r = c0 + tid; r < c1; r += kPT) {
         const float v = s.ydot[r - c0];
@@ -1499,6 +1508,7 @@ int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, in
                          : launch_persist_t<LD, ND, LF, NF, 2, DD, QR, RQ, RO, RG, RF>(p, nwg, s, query_only); \
   }
   BW_P(4096, 12288, 64, 2, 64, 6, 128, 4, 3, 2, 2, 1)  // dense-9b: 24 / 16 / 96 / 16 rows per workgroup
+  BW_P(5120, 17408, 32, 5, 32, 17, 128, 5, 1, 1, 1, 1)  // dense-27b: 28 / 20 / 136 / 20 rows per workgroup
   BW_P(256, 1024, 8, 1, 32, 1, 64, 2, 1, 1, 1, 1)       // tiny
 #undef BW_P
   return -2;

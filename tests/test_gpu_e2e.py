@@ -27,7 +27,10 @@ MOE_SMALL = dict(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64
 MOE_2K = dict(n_layers=2, d_model=2048, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn_dim=0, vocab=512,
               rms_eps=1e-6, rope_base=1e6, kv_dtype="bf16", page_tokens=16, n_experts=32, top_k=8,
               expert_ffn=512, n_shared=1, shared_ffn=512, name="moe-2k", prompt=12, steps=20)
-SINGLE_LAUNCH_SHAPES = ("tiny", "moe-2k")  # workloads whose shape has a single-launch instantiation
+# the 27B shape (d 5120, F 17408, five query heads per KV head) at two layers and a small vocabulary
+DENSE_27B_2L = dict(configs.DENSE_27B, n_layers=2, vocab=512, name="dense-27b-2l", prompt=12, steps=20)
+DENSE_27B_2L.pop("context", None)
+SINGLE_LAUNCH_SHAPES = ("tiny", "moe-2k", "dense-27b-2l")  # shapes with a single-launch instantiation
 ROUTER_TAU = 1e-4
 
 
@@ -88,9 +91,10 @@ def _compare(g, gam, o, where):
                                                   (configs.TINY, 1003, None, 0),
                                                   (MOE_SMALL, 1011, None, 1), (configs.TINY, 1002, 1, 0),
                                                   (MOE_SMALL, 1012, 1, 0), (MOE_2K, 1013, None, 1),
-                                                  (MOE_2K, 1014, None, 2), (MOE_2K, 1015, None, 0)],
+                                                  (MOE_2K, 1014, None, 2), (MOE_2K, 1015, None, 0),
+                                                  (DENSE_27B_2L, 1016, None, 1)],
                          ids=["tiny", "tiny-cooperative", "tiny-chain", "moe-small", "tiny-gemm", "moe-small-gemm",
-                              "moe-2k", "moe-2k-cooperative", "moe-2k-chain"])
+                              "moe-2k", "moe-2k-cooperative", "moe-2k-chain", "dense-27b-2l"])
 def test_prompt_then_greedy_decode(cfg, seed, gemm, single):
     """single: batch-1 steps as one launch (1: ordinary, 2: cooperative; shapes with an instantiation), 0: the
     kernel chain.

@@ -34,6 +34,7 @@ def test_full_model_synthesized_context(name, ctx):
     seed, steps = cfg["seed"], 2
     print(f"[case] {name}: synthesised context {ctx}, {steps} steps", flush=True)
     p = Pair(cfg, seed, ctx + steps + 1, ctx0=ctx, synth_seed=seed + 7)
+    assert p.single, "both full-size shapes have a single-launch step"
     try:
         nxt = int(np.random.default_rng(seed).integers(0, cfg["vocab"]))
         worst = 0.0
