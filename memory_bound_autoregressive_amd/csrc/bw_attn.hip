@@ -280,14 +280,22 @@ struct MfmaT<2> {  // bf16 cache
   }
 };
 
+// Round to the cache dtype, nearest even, with the hardware conversion (v_cvt_pk_bf16_f32 for
+// bf16); used for the query and probability parts, which no stored value depends on.
+template <int KVDT>
+__device__ __forceinline__ uint16_t part_bits(float x) {
+  if constexpr (KVDT == 1) return f32_to_f16(x);
+  else return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
 constexpr int kVStride = 136;  // LDS row of a staged V page, in 16-bit elements (272 B: conflict-free reads)
-constexpr int kMfmaMaxPps = 32;  // most pages of one split of the matrix-core kernel
+constexpr int kMfmaMaxPps = 128;  // most pages of one split of the matrix-core kernel
 
 // Grid (split, KV head x row tile, sequence): a workgroup takes 16 of the QR query rows of its KV
 // head (a verify step has one tile; a prefill chunk of t tokens has ceil(QR / 16)), over the pages
 // of its split that the tile's last position reaches.
 template <int KVDT, int D>
-__global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_split_mfma(AttnParams p, int QR) {
   using M = MfmaT<KVDT>;
   typedef typename M::e8 e8;
   typedef typename M::e4 e4;
@@ -345,7 +353,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR
         float x = ((e & 3) == 0 ? v4.x : (e & 3) == 1 ? v4.y : (e & 3) == 2 ? v4.z : v4.w) * qs;
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
-          const uint16_t bits = f32_to_kv<KVDT>(x);
+          const uint16_t bits = part_bits<KVDT>(x);
           qp[k][c][e] = __builtin_bit_cast(el8, bits);
           x -= kv_to_f32<KVDT>(bits);
         }
@@ -425,8 +433,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR
     e4 ph, pl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint16_t hb = f32_to_kv<KVDT>(pv[i]);
-      const uint16_t lb = f32_to_kv<KVDT>(pv[i] - kv_to_f32<KVDT>(hb));
+      const uint16_t hb = part_bits<KVDT>(pv[i]);
+      const uint16_t lb = part_bits<KVDT>(pv[i] - kv_to_f32<KVDT>(hb));
       ph[i] = __builtin_bit_cast(el4, hb);
       pl[i] = __builtin_bit_cast(el4, lb);
     }
@@ -441,12 +449,15 @@ __global__ __launch_bounds__(kBlock) void k_attn_split_mfma(AttnParams p, int QR
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[c][i] *= al[i];
     }
-    // values: B [token 4 grp + i][dim 16 c + c16] from the staged page
+    // values: B [token 4 grp + i][dim 16 c + c16] from the staged page by one transpose read per
+    // 16-dim chunk: within each 16-lane group, lanes 4r..4r+3 read row r (token 4 grp + r, 16
+    // dims) and every lane receives its column, i.e. its four tokens of dim 16 c + c16
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const uint16_t* vrow = vl + (4 * grp + (c16 >> 2)) * kVStride + 4 * (c16 & 3);
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
-      e4 vb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vb[i] = __builtin_bit_cast(el4, vl[(4 * grp + i) * kVStride + 16 * c + c16]);
+      const s4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vrow + 16 * c));
+      const e4 vb = __builtin_bit_cast(e4, t);
       o[c] = M::mm16(ph, vb, o[c]);
       o[c] = M::mm16(pl, vb, o[c]);
     }
@@ -586,14 +597,23 @@ static int dispatch_qr(const AttnParams& p, int batch, hipStream_t s) {
 
 // pages per split of the matrix-core kernel: 8 pages per wave keep the partials (one per split,
 // row and head) small next to the KV read of verify steps over long contexts
-constexpr int kMfmaPagesPerSplit = kMfmaMaxPps;
+// Pages per split: long splits amortise a workgroup's fixed work (the query split, the page ids,
+// the wave merge, the partials) and leave fewer partials to merge, so the longest split that
+// still gives about four workgroups per CU slot (2048 at two per CU) is taken.
+static int mfma_pages_per_split(const AttnParams& p, int batch, int tiles) {
+  for (int pps = kMfmaMaxPps; pps > 32; pps /= 2) {
+    const int64_t wgs = (int64_t)batch * p.G * tiles * ((p.max_pages + pps - 1) / pps);
+    if (wgs >= 2048) return pps;
+  }
+  return 32;
+}
 
 template <int D>
 static int launch_mfma(const AttnParams& p, int kv_dtype, int batch, int qr, hipStream_t s) {
   AttnParams m = p;
-  m.pages_per_split = kMfmaPagesPerSplit;
-  m.max_splits = min((p.max_pages + kMfmaPagesPerSplit - 1) / kMfmaPagesPerSplit, p.max_splits);
   const int tiles = (qr + 15) / 16;
+  m.pages_per_split = mfma_pages_per_split(p, batch, tiles);
+  m.max_splits = min((p.max_pages + m.pages_per_split - 1) / m.pages_per_split, p.max_splits);
   if ((int64_t)m.G * tiles > 65535) return -2;
   if (kv_dtype == 1)
     hipLaunchKernelGGL((k_attn_split_mfma<1, D>), dim3(m.max_splits, m.G * tiles, batch), dim3(kBlock), 0, s, m, qr);
