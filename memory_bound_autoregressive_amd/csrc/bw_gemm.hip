@@ -24,6 +24,10 @@
 // wave w owns rows [32w, 32w + 32) of the tile as two 16-column B tiles and every m-tile. X is
 // staged through LDS 64 columns at a time. Each k-split writes fp32 partials; k_gemm_epilogue sums
 // them in split order and applies the step's epilogue (RoPE + KV append, residual, SwiGLU, logits).
+//
+// Products of more than 64 rows (verify steps, prefill chunks) take k_gemm_w32 instead: 32x32
+// tiles, 256 weight rows per workgroup, and the block scales folded into the weights as exact fp16
+// pairs (described at the kernel). The two forms write the same partials.
 #include <algorithm>
 
 #include "bw_common.h"
@@ -236,6 +240,191 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 }
 
+// ---- the wide form: 32x32 tiles with the scales folded into the weights --------------------------
+// For products of more than 64 rows. A workgroup of 8 waves covers 256 weight rows x 128 X rows:
+// wave w owns weight rows [32 w, +32) against all 128 X rows as 4 tiles of
+// v_mfma_f32_32x32x16_f16 (lane l gives A row / B column l % 32 with K slots 8 (l / 32) .. +7; the
+// result's slot r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32), so each
+// dequantised weight fragment feeds 12 matrix instructions.
+// Weights: lane l reads bytes 8h..8h+7 of a block (h = l / 32); its 4-byte group g = 2h + s feeds
+// K-step s of the block, in the staged X order. The block scale folds into the weight exactly as an
+// fp16 pair, w_hi = fp16(s (q - 8)) and w_lo = s (q - 8) - w_hi (a fused multiply-add whose exact
+// result is representable), so there is no per-block fp32 work and the accumulators run over the
+// whole K range: y += x_hi w_hi + x_hi w_lo + x_lo w_hi (the dropped x_lo w_lo is below 2^-22 of a
+// product). Rows past N or M read clamped addresses; their results are never stored.
+// Pipelining: a chunk's X (from L2) is loaded one chunk ahead and staged into the other LDS buffer
+// after the current chunk's products; its codes and scales (from HBM) are loaded two chunks ahead
+// into one of three register sets.
+constexpr int kW32Threads = 512;
+constexpr int kW32N = 256;          // weight rows per workgroup
+constexpr int kW32M = 128;          // X rows per workgroup
+constexpr int kW32KC = 64;          // K columns per chunk (two blocks)
+constexpr int kW32XP = kW32KC + 8;  // LDS row pitch in fp16 elements (16-byte aligned, skews banks)
+constexpr int kW32MinRows = 65;     // products with fewer rows use k_gemm
+
+typedef float f16x_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// codes_to_h8 with byte permutes: each half is byte 0x64 over a code nibble, 1024 + q
+__device__ __forceinline__ h8_t codes_to_h8_perm(uint32_t c) {
+  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);
+  r[1] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u);
+  r[2] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u);
+  r[3] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u);
+  const h8_t off = {(_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1032.0f,
+                    (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1032.0f};
+  return __builtin_bit_cast(h8_t, r) - off;  // (1024 + q) - 1032 = q - 8, exact
+}
+
+// (X without __restrict__: restrict-qualified loads could be moved across the compiler barriers)
+__global__ __launch_bounds__(kW32Threads, 2) void k_gemm_w32(GemvParams p, int M, int ksplit, const uint16_t* gxh,
+                                                             const uint16_t* gxl, float* __restrict__ out, int64_t ldo,
+                                                             int64_t ks_stride) {
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][2][kW32M * kW32XP];  // [buffer][hi, lo]
+  const int K = p.w.K, N = p.w.N, nblk = K >> 5;
+  // the scale of block b sits at (b % lpr) nb + b / lpr of its row (lpr a power of two)
+  const int lpr_mask = p.w.lpr - 1, lpr_log = __builtin_ctz(p.w.lpr), nb = p.w.nb;
+  const int n0 = blockIdx.x * kW32N, ks = blockIdx.y, m0 = blockIdx.z * kW32M;
+  const int kc = K / ksplit;
+  const int k_begin = ks * kc, k_end = k_begin + kc;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // this wave's first weight row and this lane's (both clamped): the descriptors start at the
+  // wave's row, so they are uniform, and the lane's row is an offset
+  const int wrow = min(n0 + 32 * wave, N - 1);
+  const int nrow = min(n0 + 32 * wave + l32, N - 1);
+  const int crow = (nrow - wrow) * (K >> 1) + 8 * h, srow = (nrow - wrow) * nblk * 2;
+  // this thread's two 16-byte X chunks per round: row e / 8, columns 8 (e % 8) .. +7
+  int xrow[2];
+  int64_t xat[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + i * kW32Threads;
+    xrow[i] = e >> 3;
+    xat[i] = (int64_t)min(m0 + xrow[i], M - 1) * K + 8 * (e & 7);
+  }
+
+  struct XChunk {
+    u32x4 v[2][2];  // [hi, lo][chunk]
+  };
+  struct WChunk {
+    u32x2_t cw[2];     // [block]
+    uint32_t sc[2];    // [block] fp16 bits (whole registers: no sub-word arrays to demote to memory)
+  };
+  auto next = [&](int k0) { return k0 < k_end ? k0 : k_begin; };  // loads past the split re-read its start
+  // buffer loads on this wave's weight rows (codes, scales); X through global pointers, whose loads
+  // the compiler memory barriers below keep in place
+  const __amdgpu_buffer_rsrc_t rcw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.w.codes + (int64_t)wrow * (K >> 1)), 0, 32 * (K >> 1), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.w.scales + (int64_t)wrow * nblk), 0, 32 * nblk * 2, 0x00020000);
+  auto load_x = [&](int k0, XChunk& c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      c.v[0][i] = *(const u32x4*)(gxh + xat[i] + k0);
+      c.v[1][i] = *(const u32x4*)(gxl + xat[i] + k0);
+    }
+  };
+  auto load_w = [&](int k0, WChunk& c) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = (k0 >> 5) + bb;
+      c.cw[bb] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rcw, crow + b * 16, 0, 2));
+      c.sc[bb] = __builtin_amdgcn_raw_buffer_load_b16(rsc, srow + ((b & lpr_mask) * nb + (b >> lpr_log)) * 2, 0, 0);
+    }
+  };
+  auto stage = [&](const XChunk& c, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int at = xrow[i] * kW32XP + 8 * ((tid + i * kW32Threads) & 7);
+      *(u32x4*)(xs[buf][0] + at) = c.v[0][i];
+      *(u32x4*)(xs[buf][1] + at) = c.v[1][i];
+    }
+  };
+  f16x_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  auto compute = [&](const WChunk& c, int buf) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)c.sc[bb]);
+      const h8_t s8 = {sv, sv, sv, sv, sv, sv, sv, sv};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const h8_t q = codes_to_h8_perm(c.cw[bb][st]);
+        const h8_t wh = q * s8;
+        const h8_t wl = __builtin_elementwise_fma(q, s8, -wh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int at = (32 * i + l32) * kW32XP + 32 * bb + 8 * (2 * h + st);
+          const h8_t ah = *(const h8_t*)(xs[buf][0] + at);
+          const h8_t al = *(const h8_t*)(xs[buf][1] + at);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, wh, acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, wl, acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, wh, acc[i], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // every load is issued unconditionally, so the wait counts stay exact
+  XChunk x;
+  WChunk w0, w1, w2;
+  load_x(k_begin, x);
+  load_w(k_begin, w0);
+  load_w(next(k_begin + kW32KC), w1);
+  stage(x, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = k_begin;; k0 += 3 * kW32KC) {
+    load_x(next(k0 + kW32KC), x);
+    load_w(next(k0 + 2 * kW32KC), w2);
+    // the loads stay ahead of the products: a compiler memory barrier keeps them from being sunk
+    // to their uses past the loop's exit test
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w0, buf);
+    if (k0 + kW32KC >= k_end) break;
+    stage(x, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    load_x(next(k0 + 2 * kW32KC), x);
+    load_w(next(k0 + 3 * kW32KC), w0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w1, buf);
+    if (k0 + 2 * kW32KC >= k_end) break;
+    stage(x, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    load_x(next(k0 + 3 * kW32KC), x);
+    load_w(next(k0 + 4 * kW32KC), w1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w2, buf);
+    if (k0 + 3 * kW32KC >= k_end) break;
+    stage(x, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  const int n = n0 + 32 * wave + l32;
+  if (n < N) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M) out[(int64_t)ks * ks_stride + (int64_t)m * ldo + n] = acc[i][r];
+      }
+  }
+}
+
 // Sum of the k-split partials part[ks][m][n] (in split order) and the step's epilogue; one thread
 // per pair of device rows (2i, 2i + 1), which is a RoPE pair for q / k and a (gate, up) pair for
 // the SwiGLU matrix.
@@ -347,7 +536,8 @@ int launch_rowrms(const float* x, int64_t stride, int K, float eps, int M, float
 
 // k-splits: enough workgroups for 256 CUs while each split keeps >= 4 rounds of 64 columns
 int gemm_ksplit(int N, int K, int M) {
-  const int tiles = (N + kNT - 1) / kNT;
+  const bool wide = M >= kW32MinRows;
+  const int tiles = (N + (wide ? kW32N : kNT) - 1) / (wide ? kW32N : kNT);
   const int mg = (M + kMaxRowsWG - 1) / kMaxRowsWG;
   int ks = 1;
   while (tiles * ks * mg < 256 && K % (ks * 2 * kKC) == 0 && K / (ks * 2) >= 4 * kKC) ks *= 2;
@@ -376,20 +566,26 @@ int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* r
   }
   const int ks = gemm_ksplit(p.w.N, p.w.K, M);
   const int mg = (M + kMaxRowsWG - 1) / kMaxRowsWG;
-  const int mt = std::min(8, (M + 15) / 16);
+  const int mt = std::min(4, (M + 15) / 16);
   // a single split of the logits goes straight to its destination
   const bool direct = ks == 1 && epi == EPI_LOGITS;
   float* out = direct ? p.y : part;
   const int64_t ldo = direct ? p.y_stride : p.w.N;
   const int64_t ks_stride = (int64_t)M * p.w.N;
   if (out == nullptr) return -2;
+  if (M >= kW32MinRows) {
+    static_assert(kW32M == kMaxRowsWG, "row groups of the two forms agree");
+    hipLaunchKernelGGL(k_gemm_w32, dim3((p.w.N + kW32N - 1) / kW32N, ks, mg), dim3(kW32Threads), 0, s, p, M, ks, gxh,
+                       gxl, out, ldo, ks_stride);
+  } else {
   const dim3 grid((p.w.N + kNT - 1) / kNT, ks, mg);
 #define BW_G(MT_)                                                                                     \
   if (mt <= MT_) {                                                                                    \
     hipLaunchKernelGGL((k_gemm<MT_>), grid, dim3(kBlock), 0, s, p, M, ks, gxh, gxl, out, ldo, ks_stride); \
   } else
-  BW_G(1) BW_G(2) BW_G(4) BW_G(8) {}
+  BW_G(1) BW_G(2) BW_G(4) {}  // fewer than kW32MinRows rows: at most 4 m-tiles
 #undef BW_G
+  }
   if (hipGetLastError() != hipSuccess) return -1;
   if (direct) return 0;
   const int64_t pairs = (int64_t)M * (p.w.N >> 1);
