@@ -372,18 +372,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     if ((int)threadIdx.x < pg1 - pg0) pid_lds[threadIdx.x] = ptab[pg0 + threadIdx.x];
     __syncthreads();
   }
+  // An invalid page id gives a descriptor of zero bytes, so every load through it reads zeros: the
+  // offsets need no selection, which the compiler would turn into a branch around each load
+  // (and then wait for all loads in flight at the join).
   auto load_kv = [&](int page, u32x4 (&kr)[NC], u32x4 (&vr)[D / 32]) {
     const bool ok = page >= 0 && page < p.n_pages;
     const uint16_t* base = p.pool + (ok ? (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D : 0);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 2 * kPageTokens * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, ok ? 2 * kPageTokens * D * 2 : 0, 0x00020000);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      kr[c] = __builtin_amdgcn_raw_buffer_load_b128(r, ok ? (c16 * D + 32 * c + 8 * grp) * 2 : 0x7FFFFFF0, 0, 0);
+      kr[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c16 * D + 32 * c + 8 * grp) * 2, 0, 0);
 #pragma unroll
     for (int q4 = 0; q4 < D / 32; ++q4) {  // 16-byte chunk k = lane + 64 q4: token k / (D/8), dims 8 (k % (D/8))
       const int k = lane + 64 * q4;
-      vr[q4] = __builtin_amdgcn_raw_buffer_load_b128(
-          r, ok ? (kPageTokens * D + (k / (D / 8)) * D + 8 * (k % (D / 8))) * 2 : 0x7FFFFFF0, 0, 0);
+      vr[q4] = __builtin_amdgcn_raw_buffer_load_b128(r, (kPageTokens * D + (k / (D / 8)) * D + 8 * (k % (D / 8))) * 2, 0, 0);
     }
   };
   // one page: scores, online softmax, values (kr, vr hold its K and V)

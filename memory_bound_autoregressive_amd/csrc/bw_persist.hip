@@ -563,21 +563,25 @@ struct PageRegs {
 };
 
 template <int D>
-__device__ __forceinline__ void load_page(int lane, __amdgpu_buffer_rsrc_t pool, int64_t page_elems, int n_pages,
+__device__ __forceinline__ void load_page(int lane, const uint16_t* pool, int64_t page_elems, int n_pages,
                                           int page, int g, PageRegs<D>& pr) {
   using PR = PageRegs<D>;
   const int sc_tok = lane >> 3, sc_c = lane & 7, v_c = lane % PR::NV, v_tg = lane / PR::NV;
+  // the descriptor covers this KV head's K and V of the page, or no bytes for an invalid page id
+  // (every load then reads zeros): the offsets need no selection, which the compiler would turn
+  // into a branch around each load and a wait for every load in flight at the join
   const bool ok = page >= 0 && page < n_pages;
-  const int kb = ok ? (int)(((int64_t)page * page_elems + (int64_t)(g * 2) * kPageTokens * D) * 2) : kOOB;
-  const int vb = ok ? kb + kPageTokens * D * 2 : kOOB;
+  const __amdgpu_buffer_rsrc_t r =
+      uniform_rsrc(pool + (ok ? (int64_t)page * page_elems + (int64_t)(g * 2) * kPageTokens * D : 0),
+                   ok ? 2 * kPageTokens * D * 2 : 0);
 #pragma unroll
   for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
     for (int ch = 0; ch < PR::NCH; ++ch)
-      pr.k[ps][ch] = __builtin_amdgcn_raw_buffer_load_b128(pool, ok ? kb + ((ps * 8 + sc_tok) * D + sc_c * PR::DL + ch * 8) * 2 : kOOB, 0, 0);
+      pr.k[ps][ch] = __builtin_amdgcn_raw_buffer_load_b128(r, ((ps * 8 + sc_tok) * D + sc_c * PR::DL + ch * 8) * 2, 0, 0);
 #pragma unroll
   for (int u = 0; u < PR::TPL; ++u)
-    pr.v[u] = __builtin_amdgcn_raw_buffer_load_b128(pool, ok ? vb + ((v_tg + u * PR::TG) * D + v_c * 8) * 2 : kOOB, 0, 0);
+    pr.v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (kPageTokens * D + (v_tg + u * PR::TG) * D + v_c * 8) * 2, 0, 0);
 }
 
 // 16-byte chunk of the new token's key or value (cache dtype bits staged in LDS)
@@ -720,7 +724,6 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     const uint32_t tin = base_tag + (uint32_t)l;       // T(l - 1)
     const uint32_t tout = base_tag + (uint32_t)l + 1;  // T(l)
     uint16_t* pool = p.pool + (int64_t)l * p.layer_elems;
-    const int pool_bytes = (int)min<int64_t>(p.layer_elems * 2, 0x7FFFFFF0);
     PageRegs<D> kv_first;
 
     // ================= QKV =================
@@ -741,7 +744,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       // this layer's first attention page, after the input wait (waits count loads in issue
       // order): its id is known, only the new token's slot changes in this step, and that slot
       // is taken from the exchange
-      load_page<D>(lane, uniform_rsrc(pool, pool_bytes), p.page_elems, p.n_pages, first_page, ag, kv_first);
+      load_page<D>(lane, pool, p.page_elems, p.n_pages, first_page, ag, kv_first);
       gemv_rest<LPR_D, NB_D, RWQ, DBQ>(tid, Ly.qkv, q0, q1, cur, s);
       __syncthreads();
       if (2 * tid < q1 - q0) {
@@ -927,7 +930,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           __builtin_amdgcn_wave_barrier();
         }
         page = page_n;
-        load_page<D>(lane, uniform_rsrc(pool, pool_bytes), p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
+        load_page<D>(lane, pool, p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
       }
       if constexpr (!MOE) stamp(p, l * 16 + 12);  // MoE: the down phase's slot
       // reduce the value partials over the token groups, then merge the waves
