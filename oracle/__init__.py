@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-KV_F16, KV_BF16 = 1, 2
+KV_F16, KV_BF16, KV_FP8 = 1, 2, 3
+KV_DTYPES = {"f16": KV_F16, "bf16": KV_BF16, "fp8": KV_FP8}
 
 
 def build() -> str:
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.or_f64_to_f16.argtypes = [dbl]
         L.or_f64_to_bf16.restype = ctypes.c_uint16
         L.or_f64_to_bf16.argtypes = [dbl]
+        L.or_fp8_to_f64.restype = dbl
+        L.or_fp8_to_f64.argtypes = [ctypes.c_uint8]
+        L.or_f64_to_fp8.restype = ctypes.c_uint8
+        L.or_f64_to_fp8.argtypes = [dbl]
         L.or_code.restype = i32
         L.or_code.argtypes = [vp, i64]
         L.or_dequant.argtypes = [vp, vp, i64, i64, vp]
@@ -124,6 +129,16 @@ def f64_to_f16(v: float) -> int:
 
 def f64_to_bf16(v: float) -> int:
     return int(lib().or_f64_to_bf16(float(v)))
+
+
+def fp8_to_f64(bits: int) -> float:
+    """OCP FP8 E4M3 bits -> value"""
+    return float(lib().or_fp8_to_f64(int(bits)))
+
+
+def f64_to_fp8(v: float) -> int:
+    """value -> OCP FP8 E4M3 bits (nearest, ties to even, saturating at +-448)"""
+    return int(lib().or_f64_to_fp8(float(v)))
 
 
 def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
@@ -223,7 +238,7 @@ class Model:
             cfg.get("ffn_dim", 0), cfg["vocab"], cfg.get("rms_eps", 1e-6), cfg.get("rope_base", 1e6),
             cfg.get("n_experts", 0), cfg.get("top_k", 0), cfg.get("expert_ffn", 0),
             cfg.get("n_shared", 0), cfg.get("shared_ffn", 0),
-            KV_F16 if cfg.get("kv_dtype", "bf16") == "f16" else KV_BF16,
+            KV_DTYPES[cfg.get("kv_dtype", "bf16")],
         )
         self._c = c
         self.h = lib().or_model_create(ctypes.byref(c), seed)

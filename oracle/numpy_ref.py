@@ -32,6 +32,8 @@ def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 def round_kv(v: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return v.astype(np.float16).astype(np.float64)
+    if dtype != "bf16":
+        raise NotImplementedError(f"the NumPy twin models fp16 and bf16 caches only, not {dtype}")
     # bf16 round-to-nearest-even via the binary32 pattern (v is fp64: go through fp32 exactly
     # only when representable; use integer rounding on the fp64 mantissa instead)
     m, e = np.frexp(v)  # v = m * 2^e, |m| in [0.5, 1)

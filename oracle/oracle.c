@@ -8,7 +8,8 @@
  *
  * Every quantity is computed in fp64 with plain loops in the order the definition states. The
  * only rounding the oracle applies is the one the method defines: new keys and values are
- * rounded to the cache dtype (bf16 or fp16, round-to-nearest-even) before they are stored.
+ * rounded to the cache dtype (bf16, fp16 or FP8 E4M3, round-to-nearest-even) before they are
+ * stored.
  *
  * Sources. The pages ("Deep dive: bw24, a Rust + hand-written CUDA engine for Blackwell RTX 50",
  * 10100.com) describe a decode engine whose KV cache maps logical sequence positions to fixed
@@ -38,6 +39,7 @@
 
 #define OR_KV_F16 1
 #define OR_KV_BF16 2
+#define OR_KV_FP8 3 /* OCP FP8 E4M3 */
 
 /* ------------------------------------------------------------------------------------------ */
 /* number formats                                                                              */
@@ -111,7 +113,40 @@ static uint16_t or_round_bits(double v, int p, int emin, int emax, int bias, int
 uint16_t or_f64_to_f16(double v) { return or_round_bits(v, 11, -14, 15, 15, 5); }
 uint16_t or_f64_to_bf16(double v) { return or_round_bits(v, 8, -126, 127, 127, 8); }
 
+/* OCP FP8 E4M3 (the "E4M3FN" of the OCP 8-bit floating point specification): 1 sign, 4 exponent
+ * bits (bias 7), 3 fraction bits; exponent field 0 is subnormal (f * 2^-9); there is no
+ * infinity, and only exponent field 15 with fraction 7 is NaN, so the largest finite value is
+ * 1.75 * 2^8 = 448. */
+double or_fp8_to_f64(uint8_t b) {
+  int sign = (b >> 7) & 1;
+  int e = (b >> 3) & 0xF;
+  int f = b & 7;
+  double v;
+  if (e == 15 && f == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)f, -9);
+  else
+    v = ldexp((double)(8 + f), e - 10);
+  return sign ? -v : v;
+}
+
+/* Round to E4M3, to nearest with ties to even, saturating: a magnitude whose rounding would
+ * exceed 448 (that is, |v| >= 464, the midpoint to the next binade step) becomes 448, infinities
+ * included. NaN becomes the NaN pattern. (The saturating reading of an FP8 cache: a stored key
+ * or value is always finite.) */
+uint8_t or_f64_to_fp8(double v) {
+  if (isnan(v)) return 0x7F;
+  uint8_t sign = signbit(v) ? 0x80 : 0;
+  double a = fabs(v);
+  if (a >= 464.0) return (uint8_t)(sign | 0x7E); /* 448 */
+  /* below 464 the IEEE-style rounding of p = 4 significant bits, emin = -6, never reaches the
+   * exponent field 15 with fraction 7 */
+  return (uint8_t)(sign | or_round_bits(a, 4, -6, 8, 7, 4));
+}
+
 static double or_kv_round(double v, int dtype) {
+  if (dtype == OR_KV_FP8) return or_fp8_to_f64(or_f64_to_fp8(v));
   return dtype == OR_KV_F16 ? or_f16_to_f64(or_f64_to_f16(v)) : or_bf16_to_f64(or_f64_to_bf16(v));
 }
 
@@ -301,7 +336,7 @@ typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   double rms_eps, rope_base;
   int32_t n_experts, top_k, expert_ffn, n_shared, shared_ffn;
-  int32_t kv_dtype; /* OR_KV_F16 or OR_KV_BF16 */
+  int32_t kv_dtype; /* OR_KV_F16, OR_KV_BF16 or OR_KV_FP8 */
 } or_config;
 
 typedef struct {
@@ -505,6 +540,7 @@ typedef struct {
 
 typedef struct {
   int L, G, D;
+  int dtype; /* cache dtype: selects the synthetic context's values */
   int n_seqs;
   or_seq* seqs;
 } or_kv;
@@ -514,6 +550,7 @@ or_kv* or_kv_create(const or_model* m, int n_seqs, int64_t cap) {
   kv->L = m->c.n_layers;
   kv->G = m->c.n_kv_heads;
   kv->D = m->c.head_dim;
+  kv->dtype = m->c.kv_dtype;
   kv->n_seqs = n_seqs;
   kv->seqs = (or_seq*)calloc((size_t)n_seqs, sizeof(or_seq));
   for (int s = 0; s < n_seqs; ++s) {
@@ -541,8 +578,8 @@ void or_kv_set_synth(or_kv* kv, int s, uint64_t synth_seed, uint32_t synth_seq, 
 static inline double or_kv_get(const or_kv* kv, const or_seq* sq, int l, int64_t pos, int which,
                                int g, int d) {
   if (pos < sq->ctx0)
-    return bws_kv_value(sq->synth_seed, (uint32_t)l, sq->synth_seq, pos, which, g, d, kv->G,
-                        kv->D);
+    return bws_kv_value_dt(sq->synth_seed, (uint32_t)l, sq->synth_seq, pos, which, g, d, kv->G,
+                           kv->D, kv->dtype);
   int64_t a = pos - sq->ctx0;
   return sq->app[((((int64_t)l * sq->cap + a) * 2 + which) * kv->G + g) * kv->D + d];
 }

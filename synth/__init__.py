@@ -23,7 +23,7 @@ EMBED, FINAL_NORM, LM_HEAD = 1, 2, 3
 ATTN_NORM, QKV, O, FFN_NORM, GATE, UP, DOWN, ROUTER = 10, 11, 12, 13, 14, 15, 16, 17
 KV = 20
 SHARED_EXPERT = 0x100000
-KV_F16, KV_BF16 = 1, 2
+KV_F16, KV_BF16, KV_FP8 = 1, 2, 3
 
 CFLAGS = ["-O2", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall"]
 
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.bws_router.argtypes = [u64, u32, i64, i64, vp]
         L.bws_kv_value.restype = ctypes.c_double
         L.bws_kv_value.argtypes = [u64, u32, u32, i64, i32, i32, i32, i32, i32]
+        L.bws_kv_value_dt.restype = ctypes.c_double
+        L.bws_kv_value_dt.argtypes = [u64, u32, u32, i64, i32, i32, i32, i32, i32, i32]
         L.bws_kv_bits.restype = ctypes.c_uint16
         L.bws_kv_bits.argtypes = [u64, u32, u32, i64, i32, i32, i32, i32, i32, i32]
         L.bws_kv_fill.argtypes = [u64, u32, u32, i64, i64, i32, i32, i32, vp]
@@ -115,8 +117,13 @@ def kv_value(seed: int, layer: int, seq: int, pos: int, kv: int, g: int, d: int,
     return float(lib().bws_kv_value(seed, layer, seq, pos, kv, g, d, G, D))
 
 
+def kv_value_dt(seed: int, layer: int, seq: int, pos: int, kv: int, g: int, d: int, G: int, D: int,
+                dtype: int) -> float:
+    return float(lib().bws_kv_value_dt(seed, layer, seq, pos, kv, g, d, G, D, dtype))
+
+
 def kv_fill(seed: int, layer: int, seq: int, pos0: int, ntok: int, G: int, D: int, dtype: int) -> np.ndarray:
-    """Synthetic K/V bits [ntok][2][G][D]."""
-    out = np.empty((ntok, 2, G, D), dtype=np.uint16)
+    """Synthetic K/V bits [ntok][2][G][D] (uint16; uint8 for an fp8 cache)."""
+    out = np.empty((ntok, 2, G, D), dtype=np.uint8 if dtype == KV_FP8 else np.uint16)
     lib().bws_kv_fill(seed, layer, seq, pos0, ntok, G, D, dtype, out.ctypes.data)
     return out

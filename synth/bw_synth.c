@@ -116,6 +116,19 @@ static inline int kv_code(uint64_t key, int64_t pos, int kv, int g, int d, int G
 }
 
 static inline uint16_t kv_code_bits(int c, int dtype) {
+  if (dtype == BWS_KV_FP8) {
+    /* (c >> 3) / 8 = m / 8 with |m| <= 16: at most 4 significant bits, exact in E4M3
+     * (1 sign, 4 exponent bits with bias 7, 3 fraction bits) */
+    int m = c >> 3;
+    uint16_t sign = m < 0 ? 0x80 : 0;
+    if (m < 0) m = -m;
+    if (m == 0) return sign;
+    int k = 0;
+    while ((m >> (k + 1)) != 0) ++k;         /* m in [2^k, 2^(k+1)) */
+    int field = k - 3 + 7;                   /* m / 8 = 2^(k-3) (1 + frac) */
+    int frac = (m - (1 << k)) << (3 - k);
+    return (uint16_t)(sign | (field << 3) | frac);
+  }
   /* c/64 with c in [-128, 127]: at most 8 significant bits, exact in bf16 and fp16 */
   double v = (double)c / 64.0;
   if (dtype == BWS_KV_F16) return bws_f16_bits(v);
@@ -132,6 +145,13 @@ double bws_kv_value(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos, in
   return (double)kv_code(key, pos, kv, g, d, G, D) / 64.0;
 }
 
+double bws_kv_value_dt(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos, int kv, int g,
+                       int d, int G, int D, int dtype) {
+  if (dtype != BWS_KV_FP8) return bws_kv_value(seed, layer, seq, pos, kv, g, d, G, D);
+  uint64_t key = bws_key(seed, BWS_KV, layer, seq, 0);
+  return (double)(kv_code(key, pos, kv, g, d, G, D) >> 3) / 8.0;
+}
+
 uint16_t bws_kv_bits(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos, int kv, int g,
                      int d, int G, int D, int dtype) {
   uint64_t key = bws_key(seed, BWS_KV, layer, seq, 0);
@@ -139,13 +159,21 @@ uint16_t bws_kv_bits(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos, i
 }
 
 void bws_kv_fill(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos0, int64_t ntok, int G,
-                 int D, int dtype, uint16_t* dst) {
+                 int D, int dtype, void* dst) {
   uint64_t key = bws_key(seed, BWS_KV, layer, seq, 0);
   uint16_t lut[256];
   for (int c = -128; c < 128; ++c) lut[c + 128] = kv_code_bits(c, dtype);
+  uint16_t* d16 = (uint16_t*)dst;
+  uint8_t* d8 = (uint8_t*)dst;
   size_t o = 0;
   for (int64_t t = 0; t < ntok; ++t)
     for (int kv = 0; kv < 2; ++kv)
       for (int g = 0; g < G; ++g)
-        for (int d = 0; d < D; ++d) dst[o++] = lut[kv_code(key, pos0 + t, kv, g, d, G, D) + 128];
+        for (int d = 0; d < D; ++d, ++o) {
+          uint16_t b = lut[kv_code(key, pos0 + t, kv, g, d, G, D) + 128];
+          if (dtype == BWS_KV_FP8)
+            d8[o] = (uint8_t)b;
+          else
+            d16[o] = b;
+        }
 }

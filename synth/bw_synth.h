@@ -21,7 +21,8 @@
  *   embeddings        : fp16(z)
  *   RMSNorm gains     : fp16(1 + 0.1 z)
  *   MoE router matrix : fp16(0.02 z)
- *   synthetic KV      : ((h & 0xFF) - 128) / 64, exact in bf16 and fp16
+ *   synthetic KV      : c / 64 with c = (h & 0xFF) - 128, exact in bf16 and fp16; for an fp8
+ *                       (OCP E4M3) cache (c >> 3) / 8, in [-2, 1.875], exact in E4M3
  */
 #ifndef BW_SYNTH_H
 #define BW_SYNTH_H
@@ -60,6 +61,7 @@ enum {
 /* KV element dtype codes */
 #define BWS_KV_F16 1
 #define BWS_KV_BF16 2
+#define BWS_KV_FP8 3 /* OCP FP8 E4M3 (one byte per element) */
 
 static inline uint64_t bws_mix(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
@@ -118,14 +120,19 @@ void bws_router(uint64_t seed, uint32_t layer, int64_t n_experts, int64_t d, uin
 double bws_kv_value(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos, int kv, int g,
                     int d, int G, int D);
 
-/* The same element as bf16 or fp16 bits (dtype BWS_KV_BF16 / BWS_KV_F16); exact. */
+/* The element of a cache of the given dtype: bws_kv_value for BWS_KV_F16 / BWS_KV_BF16, and
+ * (c >> 3) / 8 (arithmetic shift of the same code c) for BWS_KV_FP8. */
+double bws_kv_value_dt(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos, int kv, int g,
+                       int d, int G, int D, int dtype);
+
+/* The same element as bits of the dtype (bf16, fp16, or E4M3 in the low byte); exact. */
 uint16_t bws_kv_bits(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos, int kv, int g,
                      int d, int G, int D, int dtype);
 
 /* Fill the synthetic K and V of positions [pos0, pos0+ntok) of one (layer, seq) in the
- * order [tok][kv][g][d] (ntok*2*G*D values of the given dtype). */
+ * order [tok][kv][g][d] (ntok*2*G*D values of the given dtype: 2 bytes each, 1 byte for fp8). */
 void bws_kv_fill(uint64_t seed, uint32_t layer, uint32_t seq, int64_t pos0, int64_t ntok, int G,
-                 int D, int dtype, uint16_t* dst);
+                 int D, int dtype, void* dst);
 
 #ifdef __cplusplus
 }

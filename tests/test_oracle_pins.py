@@ -86,6 +86,46 @@ def test_bf16_encode_round_to_nearest_even_matches_torch():
     assert np.isnan(oracle.bf16_to_f64(oracle.f64_to_bf16(float("nan"))))
 
 
+def test_fp8_decode_every_pattern_matches_torch():
+    """OCP FP8 E4M3 decode of all 256 patterns against torch.float8_e4m3fn."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.fp8_to_f64(b) for b in range(256)])
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(got), nan)  # 0x7F and 0xFF only
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert oracle.fp8_to_f64(0x7E) == 448.0 and oracle.fp8_to_f64(0x01) == 2.0 ** -9
+
+
+def test_fp8_encode_round_to_nearest_even_matches_torch():
+    """Below the saturation point (|v| < 464) the encode is torch's round to nearest even."""
+    finite = np.array([oracle.fp8_to_f64(b) for b in range(128) if b != 0x7F])  # 0 .. 448
+    mids = (finite[:-1] + finite[1:]) / 2  # exact ties
+    rng = np.random.default_rng(5)
+    rand = rng.uniform(-1, 1, 20000) * np.exp(rng.uniform(-9, 6.1, 20000))
+    vals = np.concatenate([finite, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9), rand])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)  # all exact in fp32
+    vals = vals[np.abs(vals) < 464]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.f64_to_fp8(float(v)) for v in vals], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_fp8_encode_saturates_and_special_cases():
+    # ties to even at both ends of the subnormal range and at the top of the range
+    assert oracle.f64_to_fp8(2.0 ** -10) == 0x00 and oracle.f64_to_fp8(-(2.0 ** -10)) == 0x80
+    assert oracle.f64_to_fp8(3 * 2.0 ** -10) == 0x02
+    assert oracle.f64_to_fp8(463.99) == 0x7E
+    # saturating reading: beyond the midpoint above 448, infinities included, the result is +-448
+    for v in (464.0, 479.0, 480.0, 1e6, float("inf")):
+        assert oracle.f64_to_fp8(v) == 0x7E and oracle.f64_to_fp8(-v) == 0xFE
+    assert oracle.f64_to_fp8(float("nan")) == 0x7F
+    assert oracle.f64_to_fp8(0.0) == 0x00 and oracle.f64_to_fp8(-0.0) == 0x80
+    # every finite pattern round-trips
+    for b in range(256):
+        if b & 0x7F != 0x7F:
+            assert oracle.f64_to_fp8(oracle.fp8_to_f64(b)) == b
+
+
 # ---------------------------------------------------------------- int4 blocks
 
 def _golden_blocks():
@@ -354,6 +394,13 @@ def test_generator_counter_based_and_distributions():
     assert vals[3, 1, 2, 5] == synth.kv_value(8, 1, 2, 103, 1, 2, 5, 4, 32)
     kvh = synth.kv_fill(8, 1, 2, 100, 16, 4, 32, synth.KV_F16).view(np.float16).astype(np.float64)
     assert np.array_equal(kvh, vals)
+    # fp8 cache: (c >> 3) / 8 of the same codes c = 64 v, exact in E4M3
+    kv8 = synth.kv_fill(8, 1, 2, 100, 16, 4, 32, synth.KV_FP8)
+    assert kv8.dtype == np.uint8
+    v8 = torch.from_numpy(kv8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(v8, np.floor(vals * 8) / 8)
+    assert v8[3, 1, 2, 5] == synth.kv_value_dt(8, 1, 2, 103, 1, 2, 5, 4, 32, synth.KV_FP8)
+    assert synth.kv_value_dt(8, 1, 2, 103, 1, 2, 5, 4, 32, synth.KV_BF16) == vals[3, 1, 2, 5]
 
 
 # ---------------------------------------------------------------- whole model
@@ -422,6 +469,38 @@ def test_oracle_reads_synthetic_context():
     kv.set_synth(1, 4242, 7, 40)
     for (l, pos, w, g, d) in itertools.product([0, 1], [0, 15, 39], [0, 1], [0, 1], [0, 63]):
         assert kv.read(1, l, pos, w, g, d) == synth.kv_value(4242, l, 7, pos, w, g, d, 2, 64)
+    m8 = oracle.Model(dict(TINY, kv_dtype="fp8"), 3)
+    kv8 = oracle.KV(m8, 2, 8)
+    kv8.set_synth(1, 4242, 7, 40)
+    for (l, pos, w, g, d) in itertools.product([0, 1], [0, 39], [0, 1], [0, 1], [0, 63]):
+        v = synth.kv_value(4242, l, 7, pos, w, g, d, 2, 64)
+        assert kv8.read(1, l, pos, w, g, d) == np.floor(v * 8) / 8
+
+
+def test_fp8_cache_stores_e4m3_roundings():
+    """With an fp8 cache every appended key and value is the E4M3 rounding of the same token's
+    key and value in an fp16 cache model (the cache dtype changes nothing before the rounding at
+    layer 0), and the logits stay close to the fp16 cache's."""
+    m16 = oracle.Model(TINY, 11)
+    m8 = oracle.Model(dict(TINY, kv_dtype="fp8"), 11)
+    kv16, kv8 = oracle.KV(m16, 1, 16), oracle.KV(m8, 1, 16)
+    toks = [3, 77, 512, 9]
+    out16 = oracle.forward(m16, kv16, 0, toks, 0)["logits"]
+    out8 = oracle.forward(m8, kv8, 0, toks, 0)["logits"]
+    G, D = TINY["n_kv_heads"], TINY["head_dim"]
+    n_diff = 0
+    for pos, w, g, d in itertools.product(range(4), [0, 1], range(G), range(D)):
+        a16, a8 = kv16.read(0, 0, pos, w, g, d), kv8.read(0, 0, pos, w, g, d)
+        # layer 0's keys and values do not depend on the cache, so a16 = fp16(k) and a8 = E4M3(k)
+        # of the same k: E4M3(a16) equals a8 except where a16 fell exactly on the midpoint of two
+        # E4M3 neighbours (a double-rounding tie), and then a8 is one of those neighbours
+        assert oracle.fp8_to_f64(oracle.f64_to_fp8(a8)) == a8
+        r = oracle.fp8_to_f64(oracle.f64_to_fp8(a16))
+        if r != a8:
+            n_diff += 1
+            assert a16 == (r + a8) / 2
+    assert n_diff < 20
+    assert np.max(np.abs(out8 - out16)) < 0.05 * np.max(np.abs(out16))
 
 
 # ---- speculative acceptance -------------------------------------------------------------------
