@@ -49,6 +49,10 @@ extern "C" {
 /* KV cache element types */
 #define BW_KV_F16 1
 #define BW_KV_BF16 2
+/* OCP FP8 E4M3 (one byte per element; no scale): a key or value is rounded to nearest, ties to
+ * even, and saturates at +-448. The low-precision cache variant on CDNA4 of the pages' FP8 paths
+ * ("Deep dive: bw24", section 1 and the comparison table of section 7). Halves the KV bytes. */
+#define BW_KV_FP8 3
 
 /* device error bits (bw_check_device_error) */
 #define BW_DERR_PAGE 1   /* a page-table entry was outside [0, n_pages) */
@@ -77,7 +81,7 @@ typedef struct {
   int32_t expert_ffn;   /* SwiGLU width of a routed expert */
   int32_t n_shared;     /* ungated shared experts (MoE) */
   int32_t shared_ffn;   /* SwiGLU width of a shared expert */
-  int32_t kv_dtype;     /* BW_KV_F16 or BW_KV_BF16 */
+  int32_t kv_dtype;     /* BW_KV_F16, BW_KV_BF16 or BW_KV_FP8 */
   int32_t page_tokens;  /* tokens per KV page; must be 16 */
   int32_t max_positions;/* largest position + 1 any step may use (RoPE table length) */
   int32_t max_tokens;   /* largest batch * t of one step (workspace size) */
@@ -96,7 +100,8 @@ int bw_model_free(bw_model* model);
 /* Create a physical KV page pool of n_pages pages for `model`. One page holds page_tokens
  * positions of every layer; its device layout is
  *   pool[layer][page][kv_head][0 = K, 1 = V][slot 0..page_tokens-1][head_dim]
- * in the model's kv_dtype (one page-layer is 64 KiB at 8 KV heads x 128 dims x bf16).
+ * in the model's kv_dtype (one page-layer is 64 KiB at 8 KV heads x 128 dims x bf16, 32 KiB
+ * with an FP8 cache).
  * The pool is zero-filled. Synchronous. Errors: BW_EINVAL, BW_ENOMEM, BW_EHIP. */
 int bw_kv_pool_create(const bw_model* model, int32_t n_pages, bw_kv_pool** out);
 
@@ -104,20 +109,22 @@ int bw_kv_pool_create(const bw_model* model, int32_t n_pages, bw_kv_pool** out);
 int bw_kv_pool_free(bw_kv_pool* pool);
 
 /* Fill every element of the pool with the 16-bit pattern `bits` (e.g. a NaN, to show that a
- * step never reads a slot it should not). Asynchronous on stream. */
+ * step never reads a slot it should not); an FP8 pool takes the low byte of `bits`.
+ * Asynchronous on stream. */
 int bw_kv_pool_fill(bw_kv_pool* pool, uint16_t bits, void* stream);
 
 /* Write synthetic cached context: for sequence b (0 <= b < batch) and every layer, positions
  * [0, seq_lens_host[b]) receive the generator's synthetic K/V for (seed, layer, seq_ids_host[b])
- * (values ((h & 0xFF) - 128) / 64, exact in the cache dtype), stored at page
+ * (values c / 64 with c = (h & 0xFF) - 128, or (c >> 3) / 8 for an FP8 cache: exact in the
+ * cache dtype), stored at page
  * page_table_host[b * max_pages + pos / page_tokens], slot pos % page_tokens.
  * Host pointers; synchronous. Errors: BW_EINVAL (a needed page id out of range). */
 int bw_kv_pool_synthesize(bw_kv_pool* pool, uint64_t seed, const int32_t* seq_ids_host,
                           const int32_t* seq_lens_host, const int32_t* page_table_host,
                           int32_t batch, int32_t max_pages);
 
-/* Copy one page-layer (n_kv_heads * 2 * page_tokens * head_dim elements, 2 bytes each, in the
- * pool layout above) to host memory. Synchronous. Errors: BW_EINVAL, BW_ERANGE. */
+/* Copy one page-layer (n_kv_heads * 2 * page_tokens * head_dim elements, 2 bytes each or 1 for
+ * FP8, in the pool layout above) to host memory. Synchronous. Errors: BW_EINVAL, BW_ERANGE. */
 int bw_kv_pool_read(const bw_kv_pool* pool, int32_t layer, int32_t page, void* host_dst,
                     size_t bytes);
 
@@ -241,6 +248,12 @@ int bw_debug_matvec(bw_model* model, int32_t which, int32_t layer, int32_t exper
 int bw_debug_attention(bw_model* model, bw_kv_pool* pool, int32_t layer, const float* q_dev,
                        const int32_t* seq_lens_dev, const int32_t* page_table_dev,
                        int32_t batch, int32_t t, int32_t max_pages, float* out_dev, void* stream);
+
+/* Round n fp32 values x_dev to the cache dtype kv_dtype with the conversion every kernel uses to
+ * store a key or value: bits_dev[i] (uint16; an FP8 code in the low byte) and back_dev[i], the
+ * stored value read back as fp32 the way the attention reads it. Asynchronous. Errors: BW_EINVAL. */
+int bw_debug_kv_round(int32_t kv_dtype, const float* x_dev, int64_t n, uint16_t* bits_dev, float* back_dev,
+                      void* stream);
 
 /* Experts chosen by the last bw_decode_step (MoE): int32 [n_layers][batch * t][top_k],
  * copied to host. Synchronises `stream`. Errors: BW_ESTATE for a dense model. */

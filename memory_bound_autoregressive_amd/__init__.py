@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbw.so")
 
 BW_OK, BW_EINVAL, BW_ENOMEM, BW_EHIP, BW_ERANGE, BW_ESTATE = 0, -1, -2, -3, -4, -5
-BW_KV_F16, BW_KV_BF16 = 1, 2
+BW_KV_F16, BW_KV_BF16, BW_KV_FP8 = 1, 2, 3
+KV_DTYPES = {"f16": BW_KV_F16, "bf16": BW_KV_BF16, "fp8": BW_KV_FP8}
 BW_DERR_PAGE, BW_DERR_TOKEN, BW_DERR_POS, BW_DERR_PERSIST = 1, 2, 4, 8
 MAT = {"qkv": 0, "o": 1, "gate": 2, "up": 3, "down": 4, "lm_head": 5,
        "shared_gate": 6, "shared_up": 7, "shared_down": 8}
@@ -27,7 +28,7 @@ EXPORTS = (
     "bw_last_error", "bw_check_device_error", "bw_debug_dequant", "bw_debug_matvec",
     "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden", "bw_set_trace", "bw_set_graphs",
     "bw_set_gemm_min_rows", "bw_set_single_launch", "bw_debug_single_launch_deadline",
-    "bw_debug_single_launch_stamps", "bw_spec_accept",
+    "bw_debug_single_launch_stamps", "bw_spec_accept", "bw_debug_kv_round",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.bw_debug_dequant.argtypes = [vp, i32, i32, i32, vp, vp]
         L.bw_debug_matvec.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp]
         L.bw_debug_attention.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
+        L.bw_debug_kv_round.argtypes = [i32, vp, ctypes.c_int64, vp, vp, vp]
         L.bw_debug_read_experts.argtypes = [vp, i32, vp, vp]
         L.bw_debug_read_hidden.argtypes = [vp, i32, vp, vp]
         L.bw_set_trace.argtypes = [vp, i32, vp, i32]
@@ -125,7 +127,7 @@ def make_config(cfg: dict, max_positions: int, max_tokens: int) -> bw_model_conf
         cfg.get("ffn_dim", 0), cfg["vocab"], cfg.get("rms_eps", 1e-6), cfg.get("rope_base", 1e6),
         cfg.get("n_experts", 0), cfg.get("top_k", 0), cfg.get("expert_ffn", 0),
         cfg.get("n_shared", 0), cfg.get("shared_ffn", 0),
-        BW_KV_F16 if kv == "f16" else BW_KV_BF16, cfg.get("page_tokens", 16), max_positions,
+        KV_DTYPES[kv], cfg.get("page_tokens", 16), max_positions,
         max_tokens,
     )
 
@@ -163,7 +165,7 @@ def bw_kv_pool_synthesize(pool: int, seed: int, seq_ids, seq_lens, page_table, b
 
 
 def bw_kv_pool_read(pool: int, layer: int, page: int, out) -> None:
-    """out: host numpy uint16 array of one page-layer."""
+    """out: host numpy array of one page-layer (uint16; uint8 for an FP8 cache)."""
     _check(lib().bw_kv_pool_read(pool, layer, page, _ptr(out), out.nbytes), "bw_kv_pool_read")
 
 
@@ -202,6 +204,12 @@ def bw_debug_attention(model: int, pool: int, layer: int, q, seq_lens, page_tabl
                        max_pages: int, out, stream=None) -> None:
     _check(lib().bw_debug_attention(model, pool, layer, _ptr(q), _ptr(seq_lens), _ptr(page_table), batch, t,
                                     max_pages, _ptr(out), _stream(stream)), "bw_debug_attention")
+
+
+def bw_debug_kv_round(kv_dtype: int, x, bits, back, stream=None) -> None:
+    """x: device float32 [n]; bits: device int16/uint16 [n]; back: device float32 [n]."""
+    _check(lib().bw_debug_kv_round(kv_dtype, _ptr(x), x.numel(), _ptr(bits), _ptr(back), _stream(stream)),
+           "bw_debug_kv_round")
 
 
 def bw_debug_read_experts(model: int, n_rows: int, out, stream=None) -> None:

@@ -18,8 +18,9 @@
 // bit for bit.
 //
 // Lane layout per page (D = 128): scores use 8 tokens x 8 lanes per pass (each lane a 16-dim
-// slice, 2 x 16-byte loads, 2 passes); values use 4 token groups x 16 lanes (each lane an 8-dim
-// slice of 4 tokens, 16-byte loads). Slots past the sequence end are masked by selection, so stale
+// slice, 2 loads of 8 elements, 2 passes); values use 4 token groups x 16 lanes (each lane an
+// 8-dim slice of 4 tokens). A load of 8 elements is 16 bytes for the 16-bit caches and 8 bytes for
+// an FP8 E4M3 cache, which is widened to fp32 by the hardware conversion. Slots past the sequence end are masked by selection, so stale
 // or NaN contents there never reach the result.
 #include "bw_common.h"
 #include "bw_internal.h"
@@ -29,15 +30,6 @@
 
 namespace bw {
 
-template <int KVDT>
-__device__ __forceinline__ void unpack8(u32x4 v, float* out) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = kv_to_f32<KVDT>((uint16_t)(v[i] & 0xFFFFu));
-    out[2 * i + 1] = kv_to_f32<KVDT>((uint16_t)(v[i] >> 16));
-  }
-}
-
 template <int KVDT, int D, int QR>
 __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
   constexpr int DL = D / 8;             // score dims per lane (8 lanes per token)
@@ -45,7 +37,9 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
   constexpr int TG = kWave / NV;        // token groups for values
   constexpr int TPL = kPageTokens / TG; // tokens per lane for values
   constexpr bool QREG = (QR * DL <= 96);
-  constexpr int NCH = DL / 8;           // 16-byte chunks per lane per token for scores
+  constexpr int NCH = DL / 8;           // 8-element chunks per lane per token for scores
+  typedef typename KvT<KVDT>::E E;
+  typedef typename KvT<KVDT>::C8 C8;
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int rep = p.H / p.G;
@@ -106,17 +100,17 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
     const bool valid = page >= 0 && page < p.n_pages;
     if (!valid && lane == 0) atomicOr(p.err, 1);
     // K (for the scores) and V (for the values) of this page, loaded together
-    u32x4 kraw[2][NCH], vraw[TPL];
+    C8 kraw[2][NCH], vraw[TPL];
     if (valid) {
-      const uint16_t* kbase = p.pool + (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D;
-      const uint16_t* vbase = kbase + kPageTokens * D;
+      const E* kbase = (const E*)p.pool + (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D;
+      const E* vbase = kbase + kPageTokens * D;
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
-          kraw[pass][ch] = *(const u32x4*)(kbase + (pass * 8 + sc_tok) * D + sc_c * DL + ch * 8);
+          kraw[pass][ch] = *(const C8*)(kbase + (pass * 8 + sc_tok) * D + sc_c * DL + ch * 8);
 #pragma unroll
-      for (int u = 0; u < TPL; ++u) vraw[u] = *(const u32x4*)(vbase + (v_tg + u * TG) * D + v_c * 8);
+      for (int u = 0; u < TPL; ++u) vraw[u] = *(const C8*)(vbase + (v_tg + u * TG) * D + v_c * 8);
     }
     // the next page's id
     const int pgn = pg + 4;
@@ -129,7 +123,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
         const int j = pg * kPageTokens + pass * 8 + sc_tok;
         float kf[DL];
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) unpack8<KVDT>(kraw[pass][ch], kf + ch * 8);
+        for (int ch = 0; ch < NCH; ++ch) kv_unpack8<KVDT>(kraw[pass][ch], kf + ch * 8);
 #pragma unroll
         for (int qr = 0; qr < QR; ++qr) {
           float dot = 0.f;
@@ -182,7 +176,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
         const int tok = v_tg + u * TG;
         const int j = pg * kPageTokens + tok;
         float vf[8];
-        unpack8<KVDT>(vraw[u], vf);
+        kv_unpack8<KVDT>(vraw[u], vf);
         const bool live = j < kv_len;
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[e] = live ? vf[e] : 0.f;
@@ -296,7 +290,9 @@ constexpr int kMfmaMaxPps = 128;  // most pages of one split of the matrix-core 
 // of its split that the tile's last position reaches.
 template <int KVDT, int D>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_split_mfma(AttnParams p, int QR) {
-  using M = MfmaT<KVDT>;
+  // an FP8 cache is widened to bf16 on load (exact) and takes the bf16 products
+  constexpr int MT = KVDT == 3 ? 2 : KVDT;
+  using M = MfmaT<MT>;
   typedef typename M::e8 e8;
   typedef typename M::e4 e4;
   constexpr int NC = D / 32;  // 32-dim chunks (scores)
@@ -332,7 +328,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   const bool real = qr < QR;
   const int ti = real ? qr / rep : 0, hr = real ? qr - ti * rep : 0;
   const int qpos = real ? base_pos + ti : 0x7fffffff;
-  constexpr int NQ = KVDT == 2 ? 3 : 2;  // parts of the query
+  constexpr int NQ = MT == 2 ? 3 : 2;  // parts of the query
   typedef typename std::remove_reference<decltype(e8{}[0])>::type el8;
   typedef typename std::remove_reference<decltype(e4{}[0])>::type el4;
   e8 qp[NQ][NC];
@@ -353,9 +349,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         float x = ((e & 3) == 0 ? v4.x : (e & 3) == 1 ? v4.y : (e & 3) == 2 ? v4.z : v4.w) * qs;
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
-          const uint16_t bits = part_bits<KVDT>(x);
+          const uint16_t bits = part_bits<MT>(x);
           qp[k][c][e] = __builtin_bit_cast(el8, bits);
-          x -= kv_to_f32<KVDT>(bits);
+          x -= kv_to_f32<MT>(bits);
         }
       }
   }
@@ -376,24 +372,52 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   // offsets need no selection, which the compiler would turn into a branch around each load
   // (and then wait for all loads in flight at the join).
   auto load_kv = [&](int page, u32x4 (&kr)[NC], u32x4 (&vr)[D / 32]) {
+    constexpr int ES = KvT<KVDT>::ES;
     const bool ok = page >= 0 && page < p.n_pages;
-    const uint16_t* base = p.pool + (ok ? (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D : 0);
+    const typename KvT<KVDT>::E* base =
+        (const typename KvT<KVDT>::E*)p.pool +
+        (ok ? (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D : 0);
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, ok ? 2 * kPageTokens * D * 2 : 0, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, ok ? 2 * kPageTokens * D * ES : 0, 0x00020000);
+    if constexpr (KVDT == 3) {  // 8-byte loads, widened to bf16 when the page is used
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      kr[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c16 * D + 32 * c + 8 * grp) * 2, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, c16 * D + 32 * c + 8 * grp, 0, 0);
+        kr[c] = u32x4{w[0], w[1], 0u, 0u};
+      }
 #pragma unroll
-    for (int q4 = 0; q4 < D / 32; ++q4) {  // 16-byte chunk k = lane + 64 q4: token k / (D/8), dims 8 (k % (D/8))
-      const int k = lane + 64 * q4;
-      vr[q4] = __builtin_amdgcn_raw_buffer_load_b128(r, (kPageTokens * D + (k / (D / 8)) * D + 8 * (k % (D / 8))) * 2, 0, 0);
+      for (int q4 = 0; q4 < D / 32; ++q4) {
+        const int k = lane + 64 * q4;
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, kPageTokens * D + (k / (D / 8)) * D + 8 * (k % (D / 8)), 0, 0);
+        vr[q4] = u32x4{w[0], w[1], 0u, 0u};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kr[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c16 * D + 32 * c + 8 * grp) * 2, 0, 0);
+#pragma unroll
+      for (int q4 = 0; q4 < D / 32; ++q4) {  // 16-byte chunk k = lane + 64 q4: token k / (D/8), dims 8 (k % (D/8))
+        const int k = lane + 64 * q4;
+        vr[q4] = __builtin_amdgcn_raw_buffer_load_b128(r, (kPageTokens * D + (k / (D / 8)) * D + 8 * (k % (D / 8))) * 2, 0, 0);
+      }
     }
   };
   // one page: scores, online softmax, values (kr, vr hold its K and V)
-  auto compute = [&](int pg, int page, const u32x4 (&kraw)[NC], const u32x4 (&vraw)[D / 32]) {
+  auto compute = [&](int pg, int page, const u32x4 (&kin)[NC], const u32x4 (&vin)[D / 32]) {
     if (page < 0 || page >= p.n_pages) {
       if (lane == 0) atomicOr(p.err, 1);
       return;
+    }
+    u32x4 kraw[NC], vraw[D / 32];  // bf16 / fp16 operands
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (KVDT == 3) kraw[c] = fp8x8_to_bf16x8(u32x2{kin[c][0], kin[c][1]});
+      else kraw[c] = kin[c];
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < D / 32; ++q4) {
+      if constexpr (KVDT == 3) vraw[q4] = fp8x8_to_bf16x8(u32x2{vin[q4][0], vin[q4][1]});
+      else vraw[q4] = vin[q4];
     }
     // stage V (this wave's buffer; the LDS operations of one wave run in order); slots past the
     // sequence end are written as zeros, so stale or NaN contents never meet a zero probability
@@ -436,8 +460,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     e4 ph, pl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint16_t hb = part_bits<KVDT>(pv[i]);
-      const uint16_t lb = part_bits<KVDT>(pv[i] - kv_to_f32<KVDT>(hb));
+      const uint16_t hb = part_bits<MT>(pv[i]);
+      const uint16_t lb = part_bits<MT>(pv[i] - kv_to_f32<MT>(hb));
       ph[i] = __builtin_bit_cast(el4, hb);
       pl[i] = __builtin_bit_cast(el4, lb);
     }
@@ -620,6 +644,8 @@ static int launch_mfma(const AttnParams& p, int kv_dtype, int batch, int qr, hip
   if ((int64_t)m.G * tiles > 65535) return -2;
   if (kv_dtype == 1)
     hipLaunchKernelGGL((k_attn_split_mfma<1, D>), dim3(m.max_splits, m.G * tiles, batch), dim3(kBlock), 0, s, m, qr);
+  else if (kv_dtype == 3)
+    hipLaunchKernelGGL((k_attn_split_mfma<3, D>), dim3(m.max_splits, m.G * tiles, batch), dim3(kBlock), 0, s, m, qr);
   else
     hipLaunchKernelGGL((k_attn_split_mfma<2, D>), dim3(m.max_splits, m.G * tiles, batch), dim3(kBlock), 0, s, m, qr);
   hipLaunchKernelGGL(k_attn_merge<D>, dim3(m.H, batch * m.t), dim3(kBlock), 0, s, m);
@@ -633,9 +659,14 @@ int launch_attention(const AttnParams& p, int kv_dtype, int batch, hipStream_t s
     if (p.D == 128) return launch_mfma<128>(p, kv_dtype, batch, qr, s);
     if (p.D == 64) return launch_mfma<64>(p, kv_dtype, batch, qr, s);
   }
-  if (p.D == 128) rc = kv_dtype == 1 ? dispatch_qr<1, 128>(p, batch, s) : dispatch_qr<2, 128>(p, batch, s);
-  else if (p.D == 64) rc = kv_dtype == 1 ? dispatch_qr<1, 64>(p, batch, s) : dispatch_qr<2, 64>(p, batch, s);
-  else return -2;
+  if (p.D == 128)
+    rc = kv_dtype == 1 ? dispatch_qr<1, 128>(p, batch, s)
+                       : (kv_dtype == 3 ? dispatch_qr<3, 128>(p, batch, s) : dispatch_qr<2, 128>(p, batch, s));
+  else if (p.D == 64)
+    rc = kv_dtype == 1 ? dispatch_qr<1, 64>(p, batch, s)
+                       : (kv_dtype == 3 ? dispatch_qr<3, 64>(p, batch, s) : dispatch_qr<2, 64>(p, batch, s));
+  else
+    return -2;
   if (rc) return rc;
   if (p.D == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(p.H, batch * p.t), dim3(kBlock), 0, s, p);
   else hipLaunchKernelGGL(k_attn_merge<64>, dim3(p.H, batch * p.t), dim3(kBlock), 0, s, p);

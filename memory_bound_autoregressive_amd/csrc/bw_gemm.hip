@@ -492,10 +492,17 @@ __global__ __launch_bounds__(kBlock) void k_gemm_epilogue(GemvParams p, int M, i
         atomicOr(p.err, 1);
         continue;
       }
-      uint16_t* base = p.pool + (int64_t)page * p.pool_page_stride +
-                       ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D;
-      base[d0] = (p.kv_dtype == 1) ? f32_to_f16(o0) : f32_to_bf16(o0);
-      base[d1] = (p.kv_dtype == 1) ? f32_to_f16(o1) : f32_to_bf16(o1);
+      const int64_t e = (int64_t)page * p.pool_page_stride +
+                        ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D;
+      if (p.kv_dtype == 3) {
+        uint8_t* base = (uint8_t*)p.pool + e;
+        base[d0] = (uint8_t)f32_to_fp8(o0);
+        base[d1] = (uint8_t)f32_to_fp8(o1);
+      } else {
+        uint16_t* base = p.pool + e;
+        base[d0] = (p.kv_dtype == 1) ? f32_to_f16(o0) : f32_to_bf16(o0);
+        base[d1] = (p.kv_dtype == 1) ? f32_to_f16(o1) : f32_to_bf16(o1);
+      }
     }
   }
 }

@@ -342,9 +342,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvParams p) {
             }
             const int which = dr < HD + GD ? 0 : 1;
             if (page < 0 || page >= p.n_pages) { atomicOr(p.err, 1); continue; }
-            uint16_t* dst = p.pool + (int64_t)page * p.pool_page_stride +
-                            ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D + d;
-            *dst = (p.kv_dtype == 1) ? f32_to_f16(out) : f32_to_bf16(out);
+            const int64_t e = (int64_t)page * p.pool_page_stride +
+                              ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D + d;
+            if (p.kv_dtype == 3) ((uint8_t*)p.pool)[e] = (uint8_t)f32_to_fp8(out);
+            else p.pool[e] = (p.kv_dtype == 1) ? f32_to_f16(out) : f32_to_bf16(out);
           }
         }
       }

@@ -68,10 +68,11 @@ struct GemvParams {
   int32_t t = 1;                    // tokens per sequence in this step (row m = b*t + i)
   const int32_t* page_table = nullptr;
   int32_t max_pages = 0;
-  uint16_t* pool = nullptr;         // this layer's slice of the pool: [n_pages][G][2][16][D]
+  uint16_t* pool = nullptr;         // this layer's slice of the pool: [n_pages][G][2][16][D] elements
+                                    // of the cache dtype (bytes for FP8, cast on use)
   int64_t pool_page_stride = 0;     // elements per page in the layer slice
   int32_t n_pages = 0;
-  int32_t kv_dtype = 2;             // 1 = fp16, 2 = bf16
+  int32_t kv_dtype = 2;             // 1 = fp16, 2 = bf16, 3 = FP8 E4M3
   float* qout = nullptr;            // [M][H][D]
   int32_t* err = nullptr;
   // EPI_LOGITS: per-workgroup argmax partials [M][gridDim.x]
@@ -86,8 +87,8 @@ struct GemvParams {
 };
 
 struct AttnParams {
-  const uint16_t* pool = nullptr;   // layer slice [n_pages][G][2][16][D]
-  int64_t pool_page_stride = 0;
+  const uint16_t* pool = nullptr;   // layer slice [n_pages][G][2][16][D] of the cache dtype (cast on use)
+  int64_t pool_page_stride = 0;     // elements per page
   int32_t n_pages = 0;
   const float* q = nullptr;         // [M][H][D] rotated queries
   const int32_t* seq_lens = nullptr;
@@ -124,8 +125,8 @@ struct PersistParams {
   float eps = 1e-6f, attn_scale = 0.f;
   const float2* rope = nullptr;
   int32_t max_pos = 0;
-  uint16_t* pool = nullptr;         // [L][n_pages][G][2][16][D]
-  int64_t layer_elems = 0, page_elems = 0;
+  uint16_t* pool = nullptr;         // [L][n_pages][G][2][16][D] of the cache dtype (cast on use)
+  int64_t layer_elems = 0, page_elems = 0;  // in elements of the cache dtype
   int32_t n_pages = 0;
   const int32_t* tokens = nullptr;  // [1]
   const int32_t* seq_lens = nullptr;// [1]
@@ -169,6 +170,7 @@ int launch_topk(const float* logits, int E, int k, int M, int32_t* sel, float* g
                 hipStream_t s);
 int launch_dequant(const Mat& w, const int32_t* row_map, int map_lo, int map_n, float* dst, hipStream_t s);
 int launch_fill16(uint16_t* dst, size_t n, uint16_t bits, hipStream_t s);
+int launch_kv_round(int kv_dtype, const float* x, int64_t n, uint16_t* bits, float* back, hipStream_t s);
 
 // batched path (bw_gemm.hip): matrix-core GEMM over all rows of a step. IN_PLAIN / IN_RMSNORM
 // (rms = per-row RMSNorm factors from launch_rowrms); epilogues STORE_CANON, RESID, SWIGLU, LOGITS,

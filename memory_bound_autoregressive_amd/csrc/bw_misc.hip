@@ -205,4 +205,25 @@ int launch_fill16(uint16_t* dst, size_t n, uint16_t bits, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// cache-dtype rounding of n values with the device conversions the kernels use: bits (in the
+// low bits of a uint16) and the value read back
+template <int KVDT>
+__global__ void k_kv_round(const float* __restrict__ x, int64_t n, uint16_t* __restrict__ bits,
+                           float* __restrict__ back) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint16_t b = f32_to_kv<KVDT>(x[i]);
+  bits[i] = b;
+  back[i] = kv_to_f32<KVDT>(b);
+}
+
+int launch_kv_round(int kv_dtype, const float* x, int64_t n, uint16_t* bits, float* back, hipStream_t s) {
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (kv_dtype == 1) hipLaunchKernelGGL(k_kv_round<1>, dim3(blocks), dim3(256), 0, s, x, n, bits, back);
+  else if (kv_dtype == 2) hipLaunchKernelGGL(k_kv_round<2>, dim3(blocks), dim3(256), 0, s, x, n, bits, back);
+  else if (kv_dtype == 3) hipLaunchKernelGGL(k_kv_round<3>, dim3(blocks), dim3(256), 0, s, x, n, bits, back);
+  else return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace bw

@@ -543,29 +543,21 @@ __device__ __forceinline__ void pload_moe_dn(int tid, const uint64_t* mp, int d,
 
 // ---- attention over the paged cache -----------------------------------------------------------
 
-template <int KVDT>
-__device__ __forceinline__ void unpack8p(u32x4 v, float* out) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = kv_to_f32<KVDT>((uint16_t)(v[i] & 0xFFFFu));
-    out[2 * i + 1] = kv_to_f32<KVDT>((uint16_t)(v[i] >> 16));
-  }
-}
-
 // K and V of one page for KV head g, as buffer loads on the layer's pool slice (an invalid page id
 // reads zeros without touching memory). Lane layout as in the chain's attention kernel: scores use
 // 8 tokens x 8 lanes per pass (2 passes), values 4 token groups x 16 lanes.
-template <int D>
+template <int D, int KVDT>
 struct PageRegs {
   static constexpr int DL = D / 8, NV = D / 8, TG = kWave / NV, TPL = kPageTokens / TG, NCH = DL / 8;
-  u32x4 k[2][NCH];
-  u32x4 v[TPL];
+  typename KvT<KVDT>::C8 k[2][NCH];
+  typename KvT<KVDT>::C8 v[TPL];
 };
 
-template <int D>
-__device__ __forceinline__ void load_page(int lane, const uint16_t* pool, int64_t page_elems, int n_pages,
-                                          int page, int g, PageRegs<D>& pr) {
-  using PR = PageRegs<D>;
+template <int D, int KVDT>
+__device__ __forceinline__ void load_page(int lane, const typename KvT<KVDT>::E* pool, int64_t page_elems,
+                                          int n_pages, int page, int g, PageRegs<D, KVDT>& pr) {
+  using PR = PageRegs<D, KVDT>;
+  constexpr int ES = KvT<KVDT>::ES;
   const int sc_tok = lane >> 3, sc_c = lane & 7, v_c = lane % PR::NV, v_tg = lane / PR::NV;
   // the descriptor covers this KV head's K and V of the page, or no bytes for an invalid page id
   // (every load then reads zeros): the offsets need no selection, which the compiler would turn
@@ -573,20 +565,23 @@ __device__ __forceinline__ void load_page(int lane, const uint16_t* pool, int64_
   const bool ok = page >= 0 && page < n_pages;
   const __amdgpu_buffer_rsrc_t r =
       uniform_rsrc(pool + (ok ? (int64_t)page * page_elems + (int64_t)(g * 2) * kPageTokens * D : 0),
-                   ok ? 2 * kPageTokens * D * 2 : 0);
+                   ok ? 2 * kPageTokens * D * ES : 0);
+  auto ld = [&](int elem) {  // 8 elements: 16 bytes, or 8 for FP8
+    if constexpr (KVDT == 3) return __builtin_amdgcn_raw_buffer_load_b64(r, elem, 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b128(r, elem * 2, 0, 0);
+  };
 #pragma unroll
   for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-    for (int ch = 0; ch < PR::NCH; ++ch)
-      pr.k[ps][ch] = __builtin_amdgcn_raw_buffer_load_b128(r, ((ps * 8 + sc_tok) * D + sc_c * PR::DL + ch * 8) * 2, 0, 0);
+    for (int ch = 0; ch < PR::NCH; ++ch) pr.k[ps][ch] = ld((ps * 8 + sc_tok) * D + sc_c * PR::DL + ch * 8);
 #pragma unroll
-  for (int u = 0; u < PR::TPL; ++u)
-    pr.v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (kPageTokens * D + (v_tg + u * PR::TG) * D + v_c * 8) * 2, 0, 0);
+  for (int u = 0; u < PR::TPL; ++u) pr.v[u] = ld(kPageTokens * D + (v_tg + u * PR::TG) * D + v_c * 8);
 }
 
-// 16-byte chunk of the new token's key or value (cache dtype bits staged in LDS)
-__device__ __forceinline__ u32x4 lds_chunk16(const uint16_t* bits, int d0) {
-  return *(const u32x4*)(bits + d0);
+// 8 elements of the new token's key or value (cache dtype bits staged in LDS)
+template <int KVDT>
+__device__ __forceinline__ typename KvT<KVDT>::C8 lds_chunk8(const uint16_t* bits, int d0) {
+  return *(const typename KvT<KVDT>::C8*)((const typename KvT<KVDT>::E*)bits + d0);
 }
 
 // ---- parameters -------------------------------------------------------------------------------
@@ -597,7 +592,7 @@ struct alignas(16) AttnLds {
   float p[kPW][QR][kPageTokens];
   float m[kPW][QR], l[kPW][QR];
   float acc[kPW][QR * D];
-  alignas(16) uint16_t knew[D];
+  alignas(16) uint16_t knew[D];  // cache dtype bits (the first D bytes for FP8)
   alignas(16) uint16_t vnew[D];
 };
 
@@ -723,8 +718,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     const PLayer Ly = load_uniform(p.layers + l);
     const uint32_t tin = base_tag + (uint32_t)l;       // T(l - 1)
     const uint32_t tout = base_tag + (uint32_t)l + 1;  // T(l)
-    uint16_t* pool = p.pool + (int64_t)l * p.layer_elems;
-    PageRegs<D> kv_first;
+    typedef typename KvT<KVDT>::E KE;
+    KE* pool = (KE*)p.pool + (int64_t)l * p.layer_elems;
+    PageRegs<D, KVDT> kv_first;
 
     // ================= QKV =================
     stamp(p, l * 16 + 0);
@@ -744,7 +740,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       // this layer's first attention page, after the input wait (waits count loads in issue
       // order): its id is known, only the new token's slot changes in this step, and that slot
       // is taken from the exchange
-      load_page<D>(lane, pool, p.page_elems, p.n_pages, first_page, ag, kv_first);
+      load_page<D, KVDT>(lane, pool, p.page_elems, p.n_pages, first_page, ag, kv_first);
       gemv_rest<LPR_D, NB_D, RWQ, DBQ>(tid, Ly.qkv, q0, q1, cur, s);
       __syncthreads();
       if (2 * tid < q1 - q0) {
@@ -777,10 +773,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           xstore(p.xq, xb + dd0, kv_to_f32<KVDT>(k0), tout);
           xstore(p.xq, xb + dd1, kv_to_f32<KVDT>(k1), tout);
           if (page_new >= 0 && page_new < p.n_pages) {
-            uint16_t* dst = pool + (int64_t)page_new * p.page_elems +
-                            ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D;
-            dst[dd0] = k0;
-            dst[dd1] = k1;
+            KE* dst = pool + (int64_t)page_new * p.page_elems +
+                      ((int64_t)(head * 2 + which) * kPageTokens + (pos % kPageTokens)) * D;
+            dst[dd0] = (KE)k0;
+            dst[dd1] = (KE)k1;
           } else if (pos_ok) {
             atomicOr(p.err, 1);
           }
@@ -803,8 +799,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int sc_tok = lane >> 3, sc_c = lane & 7, v_c = lane % NV, v_tg = lane / NV;
       int pg = pg0 + wave;
       int page = first_page;
-      u32x4 (&kraw)[2][NCH] = kv_first.k;
-      u32x4 (&vraw)[TPL] = kv_first.v;
+      typename KvT<KVDT>::C8 (&kraw)[2][NCH] = kv_first.k;
+      typename KvT<KVDT>::C8 (&vraw)[TPL] = kv_first.v;
       // q rows of this KV head and the new key / value
       if (active) {
         const __amdgpu_buffer_rsrc_t r = xrsrc(p.xq, (int64_t)Nq * 4);
@@ -834,8 +830,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           } else if (e < QR * D + 2 * D) {
             const int e2 = e - QR * D, which = e2 / D, dd = e2 - which * D;
             const uint16_t bits = f32_to_kv<KVDT>(xdec(word[i]));
-            if (which == 0) al.knew[dd] = bits;
-            else al.vnew[dd] = bits;
+            if (which == 0) ((KE*)al.knew)[dd] = (KE)bits;
+            else ((KE*)al.vnew)[dd] = (KE)bits;
           }
         }
       }
@@ -860,10 +856,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           for (int ps = 0; ps < 2; ++ps)
             if (ps * 8 + sc_tok == slot_new)
 #pragma unroll
-              for (int ch = 0; ch < NCH; ++ch) kraw[ps][ch] = lds_chunk16(al.knew, sc_c * DL + ch * 8);
+              for (int ch = 0; ch < NCH; ++ch) kraw[ps][ch] = lds_chunk8<KVDT>(al.knew, sc_c * DL + ch * 8);
 #pragma unroll
           for (int u = 0; u < TPL; ++u)
-            if (v_tg + u * TG == slot_new) vraw[u] = lds_chunk16(al.vnew, v_c * 8);
+            if (v_tg + u * TG == slot_new) vraw[u] = lds_chunk8<KVDT>(al.vnew, v_c * 8);
         }
         if (valid) {
           float sc[2][QR];
@@ -872,7 +868,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
             const int j = pg * kPageTokens + ps * 8 + sc_tok;
             float kf[DL];
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) unpack8p<KVDT>(kraw[ps][ch], kf + ch * 8);
+            for (int ch = 0; ch < NCH; ++ch) kv_unpack8<KVDT>(kraw[ps][ch], kf + ch * 8);
 #pragma unroll
             for (int qr = 0; qr < QR; ++qr) {
               float dot = 0.f;
@@ -916,7 +912,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
             const int tok = v_tg + u * TG;
             const int j = pg * kPageTokens + tok;
             float vf[8];
-            unpack8p<KVDT>(vraw[u], vf);
+            kv_unpack8<KVDT>(vraw[u], vf);
             const bool live = j < kv_len;
 #pragma unroll
             for (int e = 0; e < 8; ++e) vf[e] = live ? vf[e] : 0.f;
@@ -930,7 +926,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           __builtin_amdgcn_wave_barrier();
         }
         page = page_n;
-        load_page<D>(lane, pool, p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
+        load_page<D, KVDT>(lane, pool, p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
       }
       if constexpr (!MOE) stamp(p, l * 16 + 12);  // MoE: the down phase's slot
       // reduce the value partials over the token groups, then merge the waves
@@ -1505,6 +1501,14 @@ static int launch_persist_t(const PersistParams& p, int nwg, hipStream_t s, bool
 // per wave group sized for 256 workgroups
 int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                    bool query_only) {
+  // FP8 E4M3 caches: the 9B and tiny shapes
+#define BW_P8(DM, FF, LD, ND, LF, NF, DD, QR, RQ, RO, RG, RF)                        \
+  if (kv_dtype == 3 && d == DM && F == FF && D == DD && rep == QR)                  \
+    return launch_persist_t<LD, ND, LF, NF, 3, DD, QR, RQ, RO, RG, RF>(p, nwg, s, query_only);
+  BW_P8(4096, 12288, 64, 2, 64, 6, 128, 4, 3, 2, 2, 1)
+  BW_P8(256, 1024, 8, 1, 32, 1, 64, 2, 1, 1, 1, 1)
+#undef BW_P8
+  if (kv_dtype == 3) return -2;
 #define BW_P(DM, FF, LD, ND, LF, NF, DD, QR, RQ, RO, RG, RF)                                                  \
   if (d == DM && F == FF && D == DD && rep == QR) {                                                           \
     return kv_dtype == 1 ? launch_persist_t<LD, ND, LF, NF, 1, DD, QR, RQ, RO, RG, RF>(p, nwg, s, query_only) \
@@ -1523,6 +1527,7 @@ int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, in
 int launch_persist_moe(const PersistParams& p, int d, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                        bool query_only) {
   const int slots = p.top_k + p.n_shared;
+  if (kv_dtype == 3) return -2;  // no FP8 form: the kernel chain runs the step
 #define BW_PM(DM, FE, SL, LD, ND, LF, DD, QR, RQ, RO, RG, RF)                                                    \
   if (d == DM && p.Fe == FE && slots == SL && D == DD && rep == QR) {                                           \
     static_assert(DM == LD * ND * 32 && FE == LF * 32, "d and Fe match the lane split");                        \

@@ -175,9 +175,12 @@ struct bw_model {
 struct bw_kv_pool {
   const bw_model* m = nullptr;
   int32_t n_pages = 0;
-  uint16_t* data = nullptr;
+  uint16_t* data = nullptr;      // elements of the cache dtype (bytes for FP8)
   int64_t page_elems = 0;        // elements of one page-layer
   int64_t layer_elems = 0;       // n_pages * page_elems
+  int es = 2;                    // bytes per element
+  // layer l's slice
+  uint16_t* layer(int l) const { return (uint16_t*)((uint8_t*)data + (int64_t)l * layer_elems * es); }
 };
 
 static bool is_moe(const bw_model_config& c) { return c.n_experts > 0; }
@@ -320,7 +323,8 @@ static int check_shape(const bw_model_config& c) {
   if (c.head_dim != 64 && c.head_dim != 128) return fail(BW_EINVAL, "head_dim must be 64 or 128");
   if (c.vocab < 1) return fail(BW_EINVAL, "vocab must be positive");
   if (c.page_tokens != kPageTokens) return fail(BW_EINVAL, "page_tokens must be 16");
-  if (c.kv_dtype != BW_KV_F16 && c.kv_dtype != BW_KV_BF16) return fail(BW_EINVAL, "kv_dtype must be BW_KV_F16 or BW_KV_BF16");
+  if (c.kv_dtype != BW_KV_F16 && c.kv_dtype != BW_KV_BF16 && c.kv_dtype != BW_KV_FP8)
+    return fail(BW_EINVAL, "kv_dtype must be BW_KV_F16, BW_KV_BF16 or BW_KV_FP8");
   if (c.max_positions < 1 || c.max_tokens < 1) return fail(BW_EINVAL, "max_positions and max_tokens must be positive");
   if (c.max_positions > 65536) return fail(BW_EINVAL, "max_positions must be <= 65536");
   int qr = c.n_q_heads / c.n_kv_heads;
@@ -642,7 +646,8 @@ extern "C" int bw_kv_pool_create(const bw_model* m, int32_t n_pages, bw_kv_pool*
   p->n_pages = n_pages;
   p->page_elems = (int64_t)c.n_kv_heads * 2 * kPageTokens * c.head_dim;
   p->layer_elems = p->page_elems * n_pages;
-  const size_t bytes = (size_t)p->layer_elems * c.n_layers * 2;
+  p->es = c.kv_dtype == BW_KV_FP8 ? 1 : 2;
+  const size_t bytes = (size_t)p->layer_elems * c.n_layers * p->es;
   void* d = nullptr;
   if (hipMalloc(&d, bytes) != hipSuccess) {
     delete p;
@@ -668,22 +673,25 @@ extern "C" int bw_kv_pool_free(bw_kv_pool* p) {
 
 extern "C" int bw_kv_pool_fill(bw_kv_pool* p, uint16_t bits, void* stream) {
   if (!p) return fail(BW_EINVAL, "null pool");
-  if (launch_fill16(p->data, (size_t)p->layer_elems * p->m->c.n_layers, bits, (hipStream_t)stream))
+  // an FP8 pool is filled with the low byte of bits (its element count is even)
+  const size_t n16 = (size_t)p->layer_elems * p->m->c.n_layers * p->es / 2;
+  if (p->es == 1) bits = (uint16_t)((bits & 0xFFu) | ((bits & 0xFFu) << 8));
+  if (launch_fill16(p->data, n16, bits, (hipStream_t)stream))
     return fail(BW_EHIP, "fill launch failed");
   return BW_OK;
 }
 
 // scatter staged page-layers to their physical pages, copying only the first nslot slots of
 // each (kv, head) row so that unused slots keep their contents
-__global__ void k_scatter_pages(const uint16_t* __restrict__ staged, const int32_t* __restrict__ dst_page,
-                                const int32_t* __restrict__ nslot, uint16_t* __restrict__ layer_base,
-                                int64_t page_elems, int D) {
+__global__ void k_scatter_pages(const uint8_t* __restrict__ staged, const int32_t* __restrict__ dst_page,
+                                const int32_t* __restrict__ nslot, uint8_t* __restrict__ layer_base,
+                                int64_t page_bytes, int row_bytes) {
   const int i = blockIdx.x;
-  const int64_t dst = (int64_t)dst_page[i] * page_elems;
+  const int64_t dst = (int64_t)dst_page[i] * page_bytes;
   const int ns = nslot[i];
-  for (int64_t e = threadIdx.x; e < page_elems; e += blockDim.x) {
-    const int slot = (int)((e / D) % kPageTokens);
-    if (slot < ns) layer_base[dst + e] = staged[(int64_t)i * page_elems + e];
+  for (int64_t e = threadIdx.x; e < page_bytes; e += blockDim.x) {
+    const int slot = (int)((e / row_bytes) % kPageTokens);
+    if (slot < ns) layer_base[dst + e] = staged[(int64_t)i * page_bytes + e];
   }
 }
 
@@ -694,7 +702,8 @@ extern "C" int bw_kv_pool_synthesize(bw_kv_pool* p, uint64_t seed, const int32_t
   if (batch < 1 || max_pages < 1) return fail(BW_EINVAL, "batch and max_pages must be positive");
   const auto& c = p->m->c;
   const int G = c.n_kv_heads, D = c.head_dim;
-  const int dtype = c.kv_dtype == BW_KV_F16 ? BWS_KV_F16 : BWS_KV_BF16;
+  const int dtype = c.kv_dtype == BW_KV_F16 ? BWS_KV_F16 : (c.kv_dtype == BW_KV_FP8 ? BWS_KV_FP8 : BWS_KV_BF16);
+  const int es = p->es;
   // list of (sequence, logical page) to write
   struct Job { int b, lp, page, nslot; };
   std::vector<Job> jobs;
@@ -709,12 +718,12 @@ extern "C" int bw_kv_pool_synthesize(bw_kv_pool* p, uint64_t seed, const int32_t
     }
   }
   if (jobs.empty()) return BW_OK;
-  const int64_t pe = p->page_elems;
-  const int64_t chunk = std::min<int64_t>((int64_t)jobs.size(), std::max<int64_t>(1, (256ll << 20) / (pe * 2)));
-  std::vector<uint16_t> host((size_t)chunk * pe);
+  const int64_t pb = p->page_elems * es;  // bytes of one page-layer
+  const int64_t chunk = std::min<int64_t>((int64_t)jobs.size(), std::max<int64_t>(1, (256ll << 20) / pb));
+  std::vector<uint8_t> host((size_t)(chunk * pb));
   std::vector<int32_t> pid(chunk), ns(chunk);
   void *dstage = nullptr, *dpid = nullptr, *dns = nullptr;
-  if (hipMalloc(&dstage, (size_t)chunk * pe * 2) != hipSuccess || hipMalloc(&dpid, chunk * 4) != hipSuccess ||
+  if (hipMalloc(&dstage, (size_t)(chunk * pb)) != hipSuccess || hipMalloc(&dpid, chunk * 4) != hipSuccess ||
       hipMalloc(&dns, chunk * 4) != hipSuccess) {
     if (dstage) (void)hipFree(dstage);
     if (dpid) (void)hipFree(dpid);
@@ -726,25 +735,26 @@ extern "C" int bw_kv_pool_synthesize(bw_kv_pool* p, uint64_t seed, const int32_t
       const int64_t nj = std::min<int64_t>(chunk, (int64_t)jobs.size() - j0);
       parallel_for(nj, [&](int64_t i) {
         const Job& jb = jobs[j0 + i];
-        std::vector<uint16_t> tmp((size_t)kPageTokens * 2 * G * D);
+        std::vector<uint8_t> tmp((size_t)kPageTokens * 2 * G * D * es);
         bws_kv_fill(seed, l, (uint32_t)seq_ids[jb.b], (int64_t)jb.lp * kPageTokens, jb.nslot, G, D, dtype, tmp.data());
-        uint16_t* dst = host.data() + i * pe;
+        uint8_t* dst = host.data() + i * pb;
         // [tok][kv][g][d] -> [g][kv][slot][d]
         for (int t = 0; t < jb.nslot; ++t)
           for (int kv = 0; kv < 2; ++kv)
             for (int g = 0; g < G; ++g)
-              memcpy(dst + (((int64_t)g * 2 + kv) * kPageTokens + t) * D, tmp.data() + (((int64_t)t * 2 + kv) * G + g) * D, D * 2);
+              memcpy(dst + ((((int64_t)g * 2 + kv) * kPageTokens + t) * D) * es,
+                     tmp.data() + ((((int64_t)t * 2 + kv) * G + g) * D) * es, (size_t)D * es);
         pid[i] = jb.page;
         ns[i] = jb.nslot;
       });
-      if (hipMemcpy(dstage, host.data(), (size_t)nj * pe * 2, hipMemcpyHostToDevice) != hipSuccess ||
+      if (hipMemcpy(dstage, host.data(), (size_t)(nj * pb), hipMemcpyHostToDevice) != hipSuccess ||
           hipMemcpy(dpid, pid.data(), nj * 4, hipMemcpyHostToDevice) != hipSuccess ||
           hipMemcpy(dns, ns.data(), nj * 4, hipMemcpyHostToDevice) != hipSuccess) {
         rc = fail(BW_EHIP, "staging copy failed");
         break;
       }
-      hipLaunchKernelGGL(k_scatter_pages, dim3((unsigned)nj), dim3(256), 0, 0, (const uint16_t*)dstage,
-                         (const int32_t*)dpid, (const int32_t*)dns, p->data + (int64_t)l * p->layer_elems, pe, D);
+      hipLaunchKernelGGL(k_scatter_pages, dim3((unsigned)nj), dim3(256), 0, 0, (const uint8_t*)dstage,
+                         (const int32_t*)dpid, (const int32_t*)dns, (uint8_t*)p->layer(l), pb, D * es);
       if (hipDeviceSynchronize() != hipSuccess) rc = fail(BW_EHIP, "scatter failed");
     }
   }
@@ -759,10 +769,10 @@ extern "C" int bw_kv_pool_read(const bw_kv_pool* p, int32_t layer, int32_t page,
   if (!p || !host_dst) return fail(BW_EINVAL, "null argument");
   if (layer < 0 || layer >= p->m->c.n_layers || page < 0 || page >= p->n_pages)
     return fail(BW_EINVAL, "layer or page out of range");
-  if (bytes < (size_t)p->page_elems * 2) return fail(BW_ERANGE, "destination too small");
+  const size_t pb = (size_t)p->page_elems * p->es;
+  if (bytes < pb) return fail(BW_ERANGE, "destination too small");
   HIP_OK(hipDeviceSynchronize());
-  HIP_OK(hipMemcpy(host_dst, p->data + (int64_t)layer * p->layer_elems + (int64_t)page * p->page_elems,
-                   (size_t)p->page_elems * 2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(host_dst, (const uint8_t*)p->layer(layer) + (int64_t)page * pb, pb, hipMemcpyDeviceToHost));
   return BW_OK;
 }
 
@@ -775,7 +785,7 @@ static AttnParams attn_params(bw_model* m, const bw_kv_pool* pool, int l, const 
                               int max_pages, float* out) {
   const auto& c = m->c;
   AttnParams a;
-  a.pool = pool->data + (int64_t)l * pool->layer_elems;
+  a.pool = pool->layer(l);
   a.pool_page_stride = pool->page_elems;
   a.n_pages = pool->n_pages;
   a.q = q;
@@ -860,7 +870,7 @@ static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, co
     g.t = t;
     g.page_table = page_table;
     g.max_pages = max_pages;
-    g.pool = pool->data + (int64_t)l * pool->layer_elems;
+    g.pool = pool->layer(l);
     g.pool_page_stride = pool->page_elems;
     g.n_pages = pool->n_pages;
     g.kv_dtype = c.kv_dtype;
@@ -1204,6 +1214,15 @@ extern "C" int bw_debug_attention(bw_model* m, bw_kv_pool* pool, int32_t layer, 
   if (batch < 1 || t < 1 || batch * t > m->c.max_tokens) return fail(BW_ERANGE, "batch * t out of range");
   AttnParams a = attn_params(m, pool, layer, q, seq_lens, page_table, t, max_pages, out);
   if (launch_attention(a, m->c.kv_dtype, batch, (hipStream_t)stream)) return fail(BW_EHIP, "attention launch failed");
+  return BW_OK;
+}
+
+extern "C" int bw_debug_kv_round(int32_t kv_dtype, const float* x, int64_t n, uint16_t* bits, float* back,
+                                 void* stream) {
+  if (!x || !bits || !back) return fail(BW_EINVAL, "null argument");
+  if (n < 1 || n > (int64_t)1 << 31) return fail(BW_EINVAL, "n out of range");
+  if (kv_dtype != BW_KV_F16 && kv_dtype != BW_KV_BF16 && kv_dtype != BW_KV_FP8) return fail(BW_EINVAL, "bad kv_dtype");
+  if (launch_kv_round(kv_dtype, x, n, bits, back, (hipStream_t)stream)) return fail(BW_EHIP, "launch failed");
   return BW_OK;
 }
 

@@ -58,8 +58,10 @@ class Session:
         except Exception:
             pass
 
-    def poison(self, bits: int = 0x7FC0) -> None:
-        """Fill the whole pool with a NaN pattern (bf16 0x7FC0 / fp16 0x7E00 are NaN)."""
+    def poison(self, bits: int | None = None) -> None:
+        """Fill the whole pool with a NaN pattern (0x7FC0 is NaN in bf16 and fp16, 0x7F in FP8 E4M3)."""
+        if bits is None:
+            bits = 0x7F7F if self.cfg.get("kv_dtype", "bf16") == "fp8" else 0x7FC0
         bw_kv_pool_fill(self.pool, bits)
         torch.cuda.synchronize()
 

@@ -33,4 +33,6 @@ def kv_values(synth_mod, seed: int, layer: int, seq: int, n: int, G: int, D: int
     bits = synth_mod.kv_fill(seed, layer, seq, 0, n, G, D, dtype)
     if dtype == synth_mod.KV_F16:
         return bits.view(np.float16).astype(np.float64)
+    if dtype == synth_mod.KV_FP8:
+        return torch.from_numpy(bits).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()

@@ -53,6 +53,12 @@ def test_null_and_shape_errors_are_reported_without_a_gpu():
     assert L.bw_model_free(None) == bw.BW_OK
     assert L.bw_kv_pool_free(None) == bw.BW_OK
     assert L.bw_check_device_error(None, None, None) == bw.BW_EINVAL
+    assert L.bw_debug_kv_round(3, None, 1, None, None, None) == bw.BW_EINVAL
+    cfg = bw.make_config(dict(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=1024,
+                              vocab=1024), 64, 1)
+    cfg.kv_dtype = 4
+    assert L.bw_model_load_synthetic(ctypes.byref(cfg), 1, ctypes.byref(out)) == bw.BW_EINVAL
+    assert "kv_dtype" in bw.bw_last_error()
 
 
 def test_binding_raises_when_library_is_missing(monkeypatch, tmp_path):

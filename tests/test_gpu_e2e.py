@@ -30,7 +30,11 @@ MOE_2K = dict(n_layers=2, d_model=2048, n_q_heads=16, n_kv_heads=4, head_dim=128
 # the 27B shape (d 5120, F 17408, five query heads per KV head) at two layers and a small vocabulary
 DENSE_27B_2L = dict(configs.DENSE_27B, n_layers=2, vocab=512, name="dense-27b-2l", prompt=12, steps=20)
 DENSE_27B_2L.pop("context", None)
-SINGLE_LAUNCH_SHAPES = ("tiny", "moe-2k", "dense-27b-2l")  # shapes with a single-launch instantiation
+TINY_FP8 = dict(configs.TINY, kv_dtype="fp8", name="tiny-fp8")
+DENSE_9B_2L_FP8 = dict(configs.DENSE_9B, n_layers=2, vocab=512, kv_dtype="fp8", name="dense-9b-2l-fp8",
+                       prompt=12, steps=20)
+# shapes with a single-launch instantiation
+SINGLE_LAUNCH_SHAPES = ("tiny", "moe-2k", "dense-27b-2l", "tiny-fp8", "dense-9b-2l-fp8")
 ROUTER_TAU = 1e-4
 
 
@@ -92,9 +96,12 @@ def _compare(g, gam, o, where):
                                                   (MOE_SMALL, 1011, None, 1), (configs.TINY, 1002, 1, 0),
                                                   (MOE_SMALL, 1012, 1, 0), (MOE_2K, 1013, None, 1),
                                                   (MOE_2K, 1014, None, 2), (MOE_2K, 1015, None, 0),
-                                                  (DENSE_27B_2L, 1016, None, 1)],
+                                                  (DENSE_27B_2L, 1016, None, 1), (TINY_FP8, 1041, None, 1),
+                                                  (TINY_FP8, 1042, None, 0), (TINY_FP8, 1043, 1, 0),
+                                                  (DENSE_9B_2L_FP8, 1044, None, 1)],
                          ids=["tiny", "tiny-cooperative", "tiny-chain", "moe-small", "tiny-gemm", "moe-small-gemm",
-                              "moe-2k", "moe-2k-cooperative", "moe-2k-chain", "dense-27b-2l"])
+                              "moe-2k", "moe-2k-cooperative", "moe-2k-chain", "dense-27b-2l", "tiny-fp8",
+                              "tiny-fp8-chain", "tiny-fp8-gemm", "dense-9b-2l-fp8"])
 def test_prompt_then_greedy_decode(cfg, seed, gemm, single):
     """single: batch-1 steps as one launch (1: ordinary, 2: cooperative; shapes with an instantiation), 0: the
     kernel chain.
@@ -153,9 +160,10 @@ def test_verify_step_equals_sequential_greedy(gemm):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("single", [True, False], ids=["single-launch", "chain"])
-def test_dense_9b_synthesized_context(single):
-    cfg = configs.DENSE_9B
+@pytest.mark.parametrize("single,kv", [(True, "bf16"), (False, "bf16"), (True, "fp8")],
+                         ids=["single-launch", "chain", "single-launch-fp8"])
+def test_dense_9b_synthesized_context(single, kv):
+    cfg = dict(configs.DENSE_9B, kv_dtype=kv)
     ctx, steps, seed = 2048, 3, cfg["seed"]
     p = Pair(cfg, seed, ctx + steps + 1, ctx0=ctx, synth_seed=seed + 7, single=single)
     assert p.single or not single
@@ -166,7 +174,7 @@ def test_dense_9b_synthesized_context(single):
             g, gam, o = p.step([nxt])
             worst = max(worst, _compare(g, gam, o, f"9b step {i}"))
             nxt = int(np.argmax(o[0]))
-        print(f"[result] dense-9b ({'single launch' if single else 'chain'}) max |logit diff| = {worst:.3e}")
+        print(f"[result] dense-9b {kv} cache ({'single launch' if single else 'chain'}) max |logit diff| = {worst:.3e}")
     finally:
         p.close()
 
@@ -177,11 +185,13 @@ VERIFY_SMALL = dict(configs.VERIFY_9B, n_layers=2, vocab=4096, name="verify-9b-2
 
 
 @pytest.mark.timeout(600)
-def test_batched_verify_ragged_contexts():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_batched_verify_ragged_contexts(kv):
     """Speculative verify over a ragged batch: 8 sequences with synthesised contexts of different
     lengths (U[40, 1200], ragged final pages), 4 tokens each, one step (32 rows on the matrix-core
-    GEMM path). Every row against the oracle, which decodes each sequence on its own."""
-    cfg, seed = VERIFY_SMALL, 1031
+    GEMM path). Every row against the oracle, which decodes each sequence on its own. An FP8 cache
+    is widened to bf16 for the matrix-core attention."""
+    cfg, seed = dict(VERIFY_SMALL, kv_dtype=kv), 1031
     B, t = 8, 4
     rng = np.random.default_rng(seed)
     lens = [int(v) for v in rng.integers(40, 1201, B)]

@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
 TINY = configs.TINY
 # one layer of the 9B shape (every matrix at its real size), small vocabulary
 LAYER9B = dict(configs.DENSE_9B, n_layers=1, vocab=4096)
+LAYER9B_FP8 = dict(LAYER9B, kv_dtype="fp8")
+TINY_FP8 = dict(configs.TINY, kv_dtype="fp8")
+KV_CODE = {"f16": synth.KV_F16, "bf16": synth.KV_BF16, "fp8": synth.KV_FP8}
 # one layer of the 27B shape
 LAYER27B = dict(configs.DENSE_27B, n_layers=1, vocab=2048)
 # a small MoE with the 35B-A3B layer structure (router, top-k, shared expert)
@@ -169,12 +172,13 @@ def _attention_case(cfg, seed, lens, t, pool_seed, poison=False):
 @pytest.mark.parametrize("cfg,lens,t", [
     (TINY, [1, 37, 300], 1), (TINY, [5, 64, 200], 4),
     (LAYER9B, [2048], 1), (LAYER9B, [1, 17, 999], 4), (LAYER27B, [700], 1),
-], ids=["tiny-t1", "tiny-t4", "9b-2048", "9b-t4-ragged", "27b-t1"])
+    (TINY_FP8, [1, 37, 300], 1), (LAYER9B_FP8, [2048], 1), (LAYER9B_FP8, [1, 17, 999], 4),
+], ids=["tiny-t1", "tiny-t4", "9b-2048", "9b-t4-ragged", "27b-t1", "tiny-fp8-t1", "9b-fp8-2048", "9b-fp8-t4-ragged"])
 def test_attention_matches_oracle(cfg, lens, t):
     seed = 31
     H, G, D = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     rep = H // G
-    dtype = synth.KV_F16 if cfg["kv_dtype"] == "f16" else synth.KV_BF16
+    dtype = KV_CODE[cfg["kv_dtype"]]
     print(f"[case] attention {cfg.get('name')} lens={lens} t={t}", flush=True)
     q, got, s = _attention_case(cfg, seed, lens, t, pool_seed=5)
     try:
@@ -205,11 +209,13 @@ def test_attention_invariant_to_pool_permutation_and_poison():
     assert np.isfinite(c).all()
 
 
-def test_kv_append_lands_at_page_table_slot():
+@pytest.mark.parametrize("cfg", [TINY, TINY_FP8], ids=["f16", "fp8"])
+def test_kv_append_lands_at_page_table_slot(cfg):
     """One step at position p writes k, v (RoPE'd, rounded) to page table[p // 16], slot p % 16 and
     nothing else; the values match the oracle's cached k, v to within one unit of the cache format."""
-    cfg = TINY
     seed, ctx = 51, 37
+    fp8 = cfg["kv_dtype"] == "fp8"
+    edt = np.uint8 if fp8 else np.uint16
     G, D = cfg["n_kv_heads"], cfg["head_dim"]
     s = Session(cfg, seed=seed, max_len=[ctx + 1], max_tokens=1, pool_seed=9)
     try:
@@ -217,7 +223,7 @@ def test_kv_append_lands_at_page_table_slot():
         before = {}
         for l in range(cfg["n_layers"]):
             for p in range(s.n_pages):
-                buf = np.empty(G * 2 * 16 * D, dtype=np.uint16)
+                buf = np.empty(G * 2 * 16 * D, dtype=edt)
                 bw.bw_kv_pool_read(s.pool, l, p, buf)
                 before[(l, p)] = buf
         tok = 123
@@ -231,7 +237,7 @@ def test_kv_append_lands_at_page_table_slot():
         slot = ctx % 16
         for l in range(cfg["n_layers"]):
             for p in range(s.n_pages):
-                buf = np.empty(G * 2 * 16 * D, dtype=np.uint16)
+                buf = np.empty(G * 2 * 16 * D, dtype=edt)
                 bw.bw_kv_pool_read(s.pool, l, p, buf)
                 v = buf.reshape(G, 2, 16, D)
                 w = before[(l, p)].reshape(G, 2, 16, D)
@@ -241,12 +247,62 @@ def test_kv_append_lands_at_page_table_slot():
                 mask = np.ones_like(v, dtype=bool)
                 mask[:, :, slot, :] = False
                 assert np.array_equal(v[mask], w[mask]), (l, p)
-                got = v[:, :, slot, :].view(np.float16).astype(np.float64)  # fp16 cache (tiny)
                 ref = np.array([[[okv.read(0, l, ctx, kv, g, d) for d in range(D)] for kv in range(2)] for g in range(G)])
-                ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+                if fp8:
+                    got = torch.from_numpy(np.ascontiguousarray(v[:, :, slot, :])).view(torch.float8_e4m3fn)
+                    got = got.to(torch.float64).numpy()
+                    # one E4M3 step at |ref|: 2^(e - 3), e = max(floor(log2 |ref|), -6)
+                    e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -9)))
+                    ulp = 2.0 ** (np.maximum(e, -6) - 3)
+                else:
+                    got = v[:, :, slot, :].view(np.float16).astype(np.float64)  # fp16 cache (tiny)
+                    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
                 assert np.all(np.abs(got - ref) <= ulp + 1e-12), (l, np.max(np.abs(got - ref)))
     finally:
         s.close()
+
+
+def _round_inputs(kv_dtype):
+    """fp32 values spanning the format: normals, subnormals, exact ties, values beyond the range"""
+    rng = np.random.default_rng(71 + kv_dtype)
+    lo, hi = {bw.BW_KV_F16: (-26, 17), bw.BW_KV_BF16: (-135, 128), bw.BW_KV_FP8: (-11, 10)}[kv_dtype]
+    v = rng.uniform(-1, 1, 40000) * 2.0 ** rng.uniform(lo, hi, 40000)
+    if kv_dtype == bw.BW_KV_FP8:
+        rep_vals = np.array([oracle.fp8_to_f64(b) for b in range(256) if b & 0x7F != 0x7F])
+        dec = oracle.fp8_to_f64
+    elif kv_dtype == bw.BW_KV_F16:
+        rep_vals = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float64)
+        dec = oracle.f16_to_f64
+    else:
+        rep_vals = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).to(torch.float64).numpy()
+        dec = oracle.bf16_to_f64
+    rep_vals = np.unique(rep_vals[np.isfinite(rep_vals)])
+    mids = (rep_vals[:-1] + rep_vals[1:]) / 2
+    sel = rng.choice(len(mids), min(len(mids), 20000), replace=False)
+    x = np.concatenate([v, rep_vals[rng.choice(len(rep_vals), min(len(rep_vals), 5000), replace=False)], mids[sel],
+                        [0.0, -0.0, 1e30, -1e30, np.inf, -np.inf, 460.0, 464.0, 470.0, -500.0]]).astype(np.float32)
+    return x[np.isfinite(x) | np.isinf(x)], dec
+
+
+@pytest.mark.parametrize("kv_dtype", [bw.BW_KV_F16, bw.BW_KV_BF16, bw.BW_KV_FP8], ids=["f16", "bf16", "fp8"])
+def test_kv_rounding_is_bit_exact(kv_dtype):
+    """The conversion that stores every key and value rounds exactly as the oracle does (nearest,
+    ties to even; FP8 saturating at +-448) on the same fp32 inputs, and reads back the oracle's value."""
+    x, dec = _round_inputs(kv_dtype)
+    enc = {bw.BW_KV_F16: oracle.f64_to_f16, bw.BW_KV_BF16: oracle.f64_to_bf16, bw.BW_KV_FP8: oracle.f64_to_fp8}[kv_dtype]
+    xd = torch.from_numpy(x).cuda()
+    bits = torch.empty(x.size, dtype=torch.int16, device="cuda")
+    back = torch.empty(x.size, dtype=torch.float32, device="cuda")
+    print(f"[case] kv rounding dtype {kv_dtype}, {x.size} values", flush=True)
+    bw.bw_debug_kv_round(kv_dtype, xd, bits, back)
+    torch.cuda.synchronize()
+    gb = bits.cpu().numpy().view(np.uint16)
+    gv = back.cpu().numpy().astype(np.float64)
+    ref = np.array([enc(float(v)) for v in x], dtype=np.uint16)
+    bad = np.nonzero(gb != ref)[0]
+    assert bad.size == 0, [(float(x[i]), int(gb[i]), int(ref[i])) for i in bad[:8]]
+    rv = np.array([dec(int(b)) for b in ref])
+    assert np.array_equal(gv, rv)
 
 
 def test_device_errors_are_flagged_not_faults():
