@@ -38,6 +38,11 @@ HBM_PEAK_GBPS = 8000.0
 INT4_BYTES_PER_WEIGHT = 18.0 / 32.0  # 16 bytes of codes + one fp16 scale per 32 weights
 
 
+def kv_bytes(cfg: dict) -> int:
+    """bytes per cached element: 2 (bf16, fp16) or 1 (FP8 E4M3)"""
+    return 1 if cfg.get("kv_dtype", "bf16") == "fp8" else 2
+
+
 def algorithmic_bytes(cfg: dict, ctx_mean: float) -> dict:
     """Bytes the step must move: active int4 weights, the KV read at the mean context, the new
     K/V written, one embedding row (router matrices for MoE)."""
@@ -52,8 +57,9 @@ def algorithmic_bytes(cfg: dict, ctx_mean: float) -> dict:
         router = 0
     w_lm = cfg["vocab"] * d
     weights = (w_attn + w_ffn + w_lm) * INT4_BYTES_PER_WEIGHT
-    kv_read = ctx_mean * 2 * G * D * 2 * L
-    kv_write = 2 * G * D * 2 * L
+    es = kv_bytes(cfg)
+    kv_read = ctx_mean * 2 * G * D * es * L
+    kv_write = 2 * G * D * es * L
     embed = d * 2
     return {"weights": weights, "kv_read": kv_read, "kv_write": kv_write, "router": router,
             "embed": embed, "total": weights + kv_read + kv_write + router + embed}
@@ -164,9 +170,11 @@ def run_workload(args) -> int:
     from memory_bound_autoregressive_amd import configs
     from memory_bound_autoregressive_amd.session import Session
 
-    cfg = configs.ALL[args.workload]
+    cfg = dict(configs.ALL[args.workload])
+    if args.kv:
+        cfg["kv_dtype"] = args.kv
     seed, V = cfg["seed"], cfg["vocab"]
-    K = args.steps if args.steps_set else cfg["steps"]
+    K = args.steps if args.steps_set else cfg.get("steps", 512)
     W = args.warmup if args.warmup_set else 4
     dev = "cuda"
     torch.cuda.set_device(0)
@@ -180,7 +188,7 @@ def run_workload(args) -> int:
         s.synthesize(seed + 7, lens)
     else:
         B, t = 1, 1
-        lens = [cfg["context"]]
+        lens = [cfg.get("context", cfg.get("prompt"))]
         s = Session(cfg, seed=seed, max_len=[lens[0] + W + K + 2], max_tokens=1, pool_seed=seed + 1)
         s.synthesize(seed + 7, lens)
     single = bool(bw.bw_set_single_launch(s.model, 0 if args.chain else 1)) and not args.chain and B * t == 1
@@ -228,15 +236,16 @@ def run_workload(args) -> int:
     # step k reads seq_lens_k + t positions; seq_lens grows by about one per step (drafts drawn at
     # random are almost never accepted; at t = 1 exactly one)
     ctx_mean = (ctx0 + ctx1) / 2.0 + t - 0.5
-    kv_per_pos = 2 * cfg["n_kv_heads"] * cfg["head_dim"] * 2 * cfg["n_layers"]
+    kv_per_pos = 2 * cfg["n_kv_heads"] * cfg["head_dim"] * kv_bytes(cfg) * cfg["n_layers"]
     kv_read = float(ctx_mean.sum()) * kv_per_pos
     per_step = ab1["weights"] + ab1["router"] + kv_read + B * t * (kv_per_pos + ab1["embed"]) + \
         (B * t * V * 4 if t > 1 else 0)
     gbps = per_step / (ms_per_step * 1e-3) / 1e9
+    kv_note = ", fp8 KV" if cfg.get("kv_dtype") == "fp8" else ""
     if t > 1:
-        metric, value, unit = "verified positions/s (verify-9b, 32 x 4 per step)", B * t * 1000.0 / ms_per_step, "positions/s"
+        metric, value, unit = f"verified positions/s (verify-9b, 32 x 4 per step{kv_note})", B * t * 1000.0 / ms_per_step, "positions/s"
     else:
-        metric, value, unit = f"decode tok/s at batch 1 ({args.workload} int4)", 1000.0 / ms_per_step, "tok/s"
+        metric, value, unit = f"decode tok/s at batch 1 ({args.workload} int4{kv_note})", 1000.0 / ms_per_step, "tok/s"
     print(f"[bench] {args.workload}: {K} steps, {ms_per_step * 1e3:.1f} us/step, {value:.1f} {unit}, "
           f"{gbps:.0f} GB/s algorithmic ({gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s)", file=sys.stderr, flush=True)
     out = {
@@ -244,7 +253,7 @@ def run_workload(args) -> int:
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "step": "single launch" if single else "kernel chain (hipGraph replay)",
-                   "batch": B, "t": t,
+                   "batch": B, "t": t, "kv": cfg.get("kv_dtype", "bf16"),
                    "context": "synthesised", "context_range": [int(ctx0.min()), int(ctx1.max())],
                    "context_sum_start": int(ctx0.sum()), "seed": seed},
         "achieved_hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
@@ -276,6 +285,9 @@ def main() -> int:
                     choices=("dense-9b", "dense-27b", "moe-35b-a3b", "verify-9b", "prefill-9b"),
                     help="dense-9b (default): the headline line; the others time their own workload")
     ap.add_argument("--chunk", type=int, default=256, help="prefill-9b: tokens per prefill step")
+    ap.add_argument("--kv", choices=("bf16", "fp8"), default=None,
+                    help="cache dtype of a decode or verify workload (default: the workload's own, bf16); "
+                         "an FP8 E4M3 cache runs dense-9b on a synthesised context")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -298,7 +310,7 @@ def main() -> int:
         return 2
     if args.workload == "prefill-9b":
         return run_prefill(args)
-    if args.workload != "dense-9b":
+    if args.workload != "dense-9b" or args.kv not in (None, "bf16"):
         return run_workload(args)
 
     import numpy as np
