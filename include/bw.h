@@ -63,6 +63,7 @@ extern "C" {
 
 typedef struct bw_model bw_model;
 typedef struct bw_kv_pool bw_kv_pool;
+typedef struct bw_kv_tier bw_kv_tier;
 
 /* Model shape. Dense models set n_experts = 0; MoE models set ffn_dim = 0 and the expert
  * fields. All layers share one shape. */
@@ -127,6 +128,57 @@ int bw_kv_pool_synthesize(bw_kv_pool* pool, uint64_t seed, const int32_t* seq_id
  * FP8, in the pool layout above) to host memory. Synchronous. Errors: BW_EINVAL, BW_ERANGE. */
 int bw_kv_pool_read(const bw_kv_pool* pool, int32_t layer, int32_t page, void* host_dst,
                     size_t bytes);
+
+/* ---- host tier of the pool (L2 residency) ----
+ * The deep-dive page ("Deep dive: bw24", section 6 item 3, Hy3 overflow) keeps hot KV pages in
+ * VRAM and moves cold ones to locked host memory over PCIe, choosing them by their access time
+ * stamps (least recently used first); a read of a page under migration waits for the copy. Here
+ * a page is one physical page id across all layers (n_layers page-layers). The tier owns pinned
+ * host memory (hipHostMalloc) for `host_pages` such pages and a copy stream of the default
+ * priority. The caller owns the page tables: it decides where a restored page goes and maps it.
+ *
+ * Ordering: evict and restore queue their copies on the tier's stream after the work already
+ * queued on the caller's `stream` (the steps that wrote or still read those pages). Before the
+ * caller's stream reads a restored page, or writes a device page whose contents were just
+ * evicted, it must call bw_kv_tier_wait (the dirty-page wait). Not thread-safe. */
+
+/* Create the host tier. Synchronous. Errors: BW_EINVAL, BW_ENOMEM (pinned allocation), BW_EHIP. */
+int bw_kv_tier_create(bw_kv_pool* pool, int32_t host_pages, bw_kv_tier** out);
+
+/* Wait for the tier's copies and release it. NULL is accepted. */
+int bw_kv_tier_free(bw_kv_tier* tier);
+
+/* Record that a step reads the pages mapped for positions [0, seq_lens[b] + tokens) of each of
+ * `batch` sequences (host arrays; page_table [batch][max_pages]): their access time becomes the
+ * tier's clock, which then advances by one. Touched pages are resident (evictable). Errors:
+ * BW_EINVAL (a needed page id out of range). */
+int bw_kv_tier_touch(bw_kv_tier* tier, const int32_t* page_table_host, const int32_t* seq_lens_host,
+                     int32_t batch, int32_t tokens, int32_t max_pages);
+
+/* Evict up to n resident pages, least recently touched first (ties: lower page id), limited by
+ * the free host slots: dev_pages_out[i] was copied to host slot host_slots_out[i], i < *n_out.
+ * The pages are no longer resident; their device memory may be reused after bw_kv_tier_wait.
+ * Asynchronous. Errors: BW_EINVAL, BW_EHIP. */
+int bw_kv_tier_evict_lru(bw_kv_tier* tier, int32_t n, int32_t* dev_pages_out, int32_t* host_slots_out,
+                         int32_t* n_out, void* stream);
+
+/* Copy host slot host_slots[i] back to device page dev_pages[i] (any page id; the caller maps it
+ * in its page table) for i < n, and free the slots. The pages become resident, touched now.
+ * Asynchronous; bw_kv_tier_wait before a step reads them. Errors: BW_EINVAL (a slot holding no
+ * page, a page out of range, a repeated slot or page), BW_EHIP. */
+int bw_kv_tier_restore(bw_kv_tier* tier, const int32_t* host_slots, const int32_t* dev_pages, int32_t n,
+                       void* stream);
+
+/* Make `stream` wait for every copy the tier has queued so far. Errors: BW_EINVAL, BW_EHIP. */
+int bw_kv_tier_wait(bw_kv_tier* tier, void* stream);
+
+/* Resident device pages and occupied host slots. */
+int bw_kv_tier_stats(const bw_kv_tier* tier, int32_t* resident_pages, int32_t* host_pages_used);
+
+/* The eviction order alone (host arrays, no device): the up-to-n entries p with resident[p] != 0
+ * of smallest stamps[p], ties to the lower p, in that order. Errors: BW_EINVAL. */
+int bw_kv_lru_select(const uint64_t* stamps, const uint8_t* resident, int32_t n_pages, int32_t n,
+                     int32_t* out, int32_t* n_out);
 
 /* One decode step for `batch` sequences of `t` new tokens each (t = 1: plain decode; t > 1:
  * the verify step of speculative decoding, the t tokens laid out along the sequence).

@@ -10,6 +10,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 from . import configs  # noqa: F401  (workload shapes)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +31,8 @@ EXPORTS = (
     "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden", "bw_set_trace", "bw_set_graphs",
     "bw_set_gemm_min_rows", "bw_set_single_launch", "bw_debug_single_launch_deadline",
     "bw_debug_single_launch_stamps", "bw_spec_accept", "bw_debug_kv_round",
+    "bw_kv_tier_create", "bw_kv_tier_free", "bw_kv_tier_touch", "bw_kv_tier_evict_lru", "bw_kv_tier_restore",
+    "bw_kv_tier_wait", "bw_kv_tier_stats", "bw_kv_lru_select",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -80,6 +84,14 @@ def lib() -> ctypes.CDLL:
         L.bw_debug_matvec.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp]
         L.bw_debug_attention.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
         L.bw_debug_kv_round.argtypes = [i32, vp, ctypes.c_int64, vp, vp, vp]
+        L.bw_kv_tier_create.argtypes = [vp, i32, ctypes.POINTER(vp)]
+        L.bw_kv_tier_free.argtypes = [vp]
+        L.bw_kv_tier_touch.argtypes = [vp, vp, vp, i32, i32, i32]
+        L.bw_kv_tier_evict_lru.argtypes = [vp, i32, vp, vp, vp, vp]
+        L.bw_kv_tier_restore.argtypes = [vp, vp, vp, i32, vp]
+        L.bw_kv_tier_wait.argtypes = [vp, vp]
+        L.bw_kv_tier_stats.argtypes = [vp, vp, vp]
+        L.bw_kv_lru_select.argtypes = [vp, vp, i32, i32, vp, vp]
         L.bw_debug_read_experts.argtypes = [vp, i32, vp, vp]
         L.bw_debug_read_hidden.argtypes = [vp, i32, vp, vp]
         L.bw_set_trace.argtypes = [vp, i32, vp, i32]
@@ -210,6 +222,60 @@ def bw_debug_kv_round(kv_dtype: int, x, bits, back, stream=None) -> None:
     """x: device float32 [n]; bits: device int16/uint16 [n]; back: device float32 [n]."""
     _check(lib().bw_debug_kv_round(kv_dtype, _ptr(x), x.numel(), _ptr(bits), _ptr(back), _stream(stream)),
            "bw_debug_kv_round")
+
+
+def bw_kv_tier_create(pool: int, host_pages: int) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().bw_kv_tier_create(pool, host_pages, ctypes.byref(out)), "bw_kv_tier_create")
+    return out.value
+
+
+def bw_kv_tier_free(tier: int) -> None:
+    _check(lib().bw_kv_tier_free(tier), "bw_kv_tier_free")
+
+
+def bw_kv_tier_touch(tier: int, page_table, seq_lens, batch: int, tokens: int, max_pages: int) -> None:
+    """page_table, seq_lens: host int32 numpy arrays."""
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    _check(lib().bw_kv_tier_touch(tier, _ptr(pt), _ptr(sl), batch, tokens, max_pages), "bw_kv_tier_touch")
+
+
+def bw_kv_tier_evict_lru(tier: int, n: int, stream=None):
+    """Returns (device pages, host slots) as int32 numpy arrays."""
+    pages = np.empty(max(n, 1), dtype=np.int32)
+    slots = np.empty(max(n, 1), dtype=np.int32)
+    got = ctypes.c_int32()
+    _check(lib().bw_kv_tier_evict_lru(tier, n, _ptr(pages), _ptr(slots), ctypes.byref(got), _stream(stream)),
+           "bw_kv_tier_evict_lru")
+    return pages[:got.value].copy(), slots[:got.value].copy()
+
+
+def bw_kv_tier_restore(tier: int, host_slots, dev_pages, stream=None) -> None:
+    hs = np.ascontiguousarray(host_slots, dtype=np.int32)
+    dp = np.ascontiguousarray(dev_pages, dtype=np.int32)
+    assert hs.size == dp.size
+    _check(lib().bw_kv_tier_restore(tier, _ptr(hs), _ptr(dp), hs.size, _stream(stream)), "bw_kv_tier_restore")
+
+
+def bw_kv_tier_wait(tier: int, stream=None) -> None:
+    _check(lib().bw_kv_tier_wait(tier, _stream(stream)), "bw_kv_tier_wait")
+
+
+def bw_kv_tier_stats(tier: int) -> tuple[int, int]:
+    r, h = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().bw_kv_tier_stats(tier, ctypes.byref(r), ctypes.byref(h)), "bw_kv_tier_stats")
+    return r.value, h.value
+
+
+def bw_kv_lru_select(stamps, resident, n: int):
+    """Host-only eviction order: stamps uint64 [n_pages], resident uint8 [n_pages]."""
+    st = np.ascontiguousarray(stamps, dtype=np.uint64)
+    rs = np.ascontiguousarray(resident, dtype=np.uint8)
+    out = np.empty(max(n, 1), dtype=np.int32)
+    got = ctypes.c_int32()
+    _check(lib().bw_kv_lru_select(_ptr(st), _ptr(rs), st.size, n, _ptr(out), ctypes.byref(got)), "bw_kv_lru_select")
+    return out[:got.value].copy()
 
 
 def bw_debug_read_experts(model: int, n_rows: int, out, stream=None) -> None:

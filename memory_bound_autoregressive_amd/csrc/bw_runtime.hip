@@ -777,6 +777,183 @@ extern "C" int bw_kv_pool_read(const bw_kv_pool* p, int32_t layer, int32_t page,
 }
 
 // ---------------------------------------------------------------------------------------------
+// host tier of the pool: pinned host page slots, least recently used pages evicted first
+// ---------------------------------------------------------------------------------------------
+// The deep-dive page's Hy3 overflow (section 6 item 3) keeps hot KV pages in VRAM and moves cold
+// ones to locked host memory over PCIe, evicting by the pages' access time stamps; a read of a
+// page under migration waits until the copy is done. Here a page is one physical page id across
+// all layers; its L slices are one strided (2-D) DMA copy on the tier's own stream.
+
+struct bw_kv_tier {
+  bw_kv_pool* pool = nullptr;
+  int32_t host_pages = 0;
+  uint8_t* host = nullptr;          // [host_pages][n_layers][page_bytes], pinned
+  std::vector<uint64_t> stamp;      // per device page: tier clock at its last touch
+  std::vector<uint8_t> resident;    // per device page: holds cached positions the tier may evict
+  std::vector<uint8_t> slot_used;   // per host slot
+  std::vector<int32_t> free_slots;  // host slots not holding a page (the last one is used first)
+  uint64_t clock = 1;
+  hipStream_t copy = nullptr;       // copy stream (default priority)
+  hipEvent_t after = nullptr;       // caller's stream position before a batch of copies
+  hipEvent_t done = nullptr;        // copy stream position after the latest batch of copies
+};
+
+extern "C" int bw_kv_lru_select(const uint64_t* stamps, const uint8_t* resident, int32_t n_pages, int32_t n,
+                                int32_t* out, int32_t* n_out) {
+  if (!stamps || !resident || !out || !n_out) return fail(BW_EINVAL, "null argument");
+  if (n_pages < 0 || n < 0) return fail(BW_EINVAL, "negative size");
+  std::vector<int32_t> cand;
+  for (int32_t p = 0; p < n_pages; ++p)
+    if (resident[p]) cand.push_back(p);
+  const size_t k = std::min<size_t>((size_t)n, cand.size());
+  std::partial_sort(cand.begin(), cand.begin() + k, cand.end(), [&](int32_t a, int32_t b) {
+    return stamps[a] != stamps[b] ? stamps[a] < stamps[b] : a < b;
+  });
+  for (size_t i = 0; i < k; ++i) out[i] = cand[i];
+  *n_out = (int32_t)k;
+  return BW_OK;
+}
+
+extern "C" int bw_kv_tier_free(bw_kv_tier* t) {
+  if (!t) return BW_OK;
+  if (t->copy) (void)hipStreamSynchronize(t->copy);
+  if (t->after) (void)hipEventDestroy(t->after);
+  if (t->done) (void)hipEventDestroy(t->done);
+  if (t->copy) (void)hipStreamDestroy(t->copy);
+  if (t->host) (void)hipHostFree(t->host);
+  delete t;
+  return BW_OK;
+}
+
+extern "C" int bw_kv_tier_create(bw_kv_pool* pool, int32_t host_pages, bw_kv_tier** out) {
+  if (!pool || !out) return fail(BW_EINVAL, "null argument");
+  *out = nullptr;
+  if (host_pages < 1) return fail(BW_EINVAL, "host_pages must be positive");
+  const size_t page_bytes = (size_t)pool->page_elems * pool->es;
+  const size_t bytes = (size_t)host_pages * pool->m->c.n_layers * page_bytes;
+  bw_kv_tier* t = new bw_kv_tier();
+  t->pool = pool;
+  t->host_pages = host_pages;
+  if (hipHostMalloc((void**)&t->host, bytes, hipHostMallocDefault) != hipSuccess) {
+    t->host = nullptr;
+    bw_kv_tier_free(t);
+    return fail(BW_ENOMEM, "hipHostMalloc(%zu) for the host tier failed", bytes);
+  }
+  if (hipStreamCreateWithFlags(&t->copy, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&t->after, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&t->done, hipEventDisableTiming) != hipSuccess) {
+    bw_kv_tier_free(t);
+    return fail(BW_EHIP, "tier stream or event creation failed");
+  }
+  t->stamp.assign(pool->n_pages, 0);
+  t->resident.assign(pool->n_pages, 0);
+  t->slot_used.assign(host_pages, 0);
+  for (int32_t s = host_pages - 1; s >= 0; --s) t->free_slots.push_back(s);
+  *out = t;
+  return BW_OK;
+}
+
+extern "C" int bw_kv_tier_touch(bw_kv_tier* t, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
+                                int32_t tokens, int32_t max_pages) {
+  if (!t || !page_table || !seq_lens) return fail(BW_EINVAL, "null argument");
+  if (batch < 1 || tokens < 0 || max_pages < 1) return fail(BW_EINVAL, "bad batch, tokens or max_pages");
+  for (int32_t b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 0) return fail(BW_EINVAL, "negative seq_len");
+    const int64_t np = ((int64_t)seq_lens[b] + tokens + kPageTokens - 1) / kPageTokens;
+    if (np > max_pages) return fail(BW_EINVAL, "sequence %d needs more than max_pages pages", b);
+    for (int64_t j = 0; j < np; ++j) {
+      const int32_t pg = page_table[(int64_t)b * max_pages + j];
+      if (pg < 0 || pg >= t->pool->n_pages) return fail(BW_EINVAL, "page id %d out of range", pg);
+      t->stamp[pg] = t->clock;
+      t->resident[pg] = 1;
+    }
+  }
+  ++t->clock;
+  return BW_OK;
+}
+
+// one page across all layers: device slice l of page p <-> host slot s, row l
+static hipError_t tier_copy(bw_kv_tier* t, int32_t page, int32_t slot, bool to_host) {
+  const bw_kv_pool* p = t->pool;
+  const size_t pb = (size_t)p->page_elems * p->es, lb = (size_t)p->layer_elems * p->es;
+  uint8_t* dev = (uint8_t*)p->data + (size_t)page * pb;
+  uint8_t* host = t->host + (size_t)slot * p->m->c.n_layers * pb;
+  if (to_host)
+    return hipMemcpy2DAsync(host, pb, dev, lb, pb, p->m->c.n_layers, hipMemcpyDeviceToHost, t->copy);
+  return hipMemcpy2DAsync(dev, lb, host, pb, pb, p->m->c.n_layers, hipMemcpyHostToDevice, t->copy);
+}
+
+extern "C" int bw_kv_tier_evict_lru(bw_kv_tier* t, int32_t n, int32_t* dev_pages, int32_t* host_slots,
+                                    int32_t* n_out, void* stream) {
+  if (!t || !dev_pages || !host_slots || !n_out) return fail(BW_EINVAL, "null argument");
+  if (n < 0) return fail(BW_EINVAL, "negative n");
+  const int32_t k = std::min<int32_t>(n, (int32_t)t->free_slots.size());
+  int32_t got = 0;
+  int rc = bw_kv_lru_select(t->stamp.data(), t->resident.data(), t->pool->n_pages, k, dev_pages, &got);
+  if (rc != BW_OK) return rc;
+  *n_out = got;
+  if (got == 0) return BW_OK;
+  // the copies start after the work already queued on the caller's stream (the steps that wrote
+  // these pages)
+  HIP_OK(hipEventRecord(t->after, (hipStream_t)stream));
+  HIP_OK(hipStreamWaitEvent(t->copy, t->after, 0));
+  for (int32_t i = 0; i < got; ++i) {
+    const int32_t slot = t->free_slots.back();
+    t->free_slots.pop_back();
+    t->slot_used[slot] = 1;
+    host_slots[i] = slot;
+    t->resident[dev_pages[i]] = 0;
+    t->stamp[dev_pages[i]] = 0;
+    HIP_OK(tier_copy(t, dev_pages[i], slot, true));
+  }
+  HIP_OK(hipEventRecord(t->done, t->copy));
+  return BW_OK;
+}
+
+extern "C" int bw_kv_tier_restore(bw_kv_tier* t, const int32_t* host_slots, const int32_t* dev_pages, int32_t n,
+                                  void* stream) {
+  if (!t || (n > 0 && (!host_slots || !dev_pages))) return fail(BW_EINVAL, "null argument");
+  if (n < 0) return fail(BW_EINVAL, "negative n");
+  for (int32_t i = 0; i < n; ++i) {
+    if (host_slots[i] < 0 || host_slots[i] >= t->host_pages || !t->slot_used[host_slots[i]])
+      return fail(BW_EINVAL, "host slot %d holds no page", host_slots[i]);
+    if (dev_pages[i] < 0 || dev_pages[i] >= t->pool->n_pages) return fail(BW_EINVAL, "page id %d out of range", dev_pages[i]);
+    for (int32_t j = 0; j < i; ++j)
+      if (host_slots[j] == host_slots[i] || dev_pages[j] == dev_pages[i])
+        return fail(BW_EINVAL, "slot or page repeated");
+  }
+  if (n == 0) return BW_OK;
+  // after the work queued on the caller's stream (a step that still reads a target page)
+  HIP_OK(hipEventRecord(t->after, (hipStream_t)stream));
+  HIP_OK(hipStreamWaitEvent(t->copy, t->after, 0));
+  for (int32_t i = 0; i < n; ++i) {
+    HIP_OK(tier_copy(t, dev_pages[i], host_slots[i], false));
+    t->resident[dev_pages[i]] = 1;
+    t->stamp[dev_pages[i]] = t->clock;
+    // the slot is free again; a later eviction into it runs after this copy on the same stream
+    t->slot_used[host_slots[i]] = 0;
+    t->free_slots.push_back(host_slots[i]);
+  }
+  HIP_OK(hipEventRecord(t->done, t->copy));
+  return BW_OK;
+}
+
+extern "C" int bw_kv_tier_wait(bw_kv_tier* t, void* stream) {
+  if (!t) return fail(BW_EINVAL, "null tier");
+  HIP_OK(hipStreamWaitEvent((hipStream_t)stream, t->done, 0));
+  return BW_OK;
+}
+
+extern "C" int bw_kv_tier_stats(const bw_kv_tier* t, int32_t* resident_pages, int32_t* host_pages_used) {
+  if (!t || !resident_pages || !host_pages_used) return fail(BW_EINVAL, "null argument");
+  int32_t r = 0;
+  for (uint8_t v : t->resident) r += v;
+  *resident_pages = r;
+  *host_pages_used = t->host_pages - (int32_t)t->free_slots.size();
+  return BW_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
 // the step
 // ---------------------------------------------------------------------------------------------
 
