@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tok/s at batch 1 (9B-shape int4) + achieved HBM GB/s vs ~8 TB/s peak"
 HBM_PEAK_GBPS = 8000.0
+PCIE_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
 INT4_BYTES_PER_WEIGHT = 18.0 / 32.0  # 16 bytes of codes + one fp16 scale per 32 weights
 
 
@@ -153,6 +154,86 @@ def run_prefill(args) -> int:
         "vs_baseline": None, "dtype": "f32 (fp16 hi/lo and bf16 parts on the matrix cores)", "data": "synthetic",
         "config": {"workload": "prefill-9b", "prompt": P, "chunk": C, "chunks": len(chunks), "seed": cfg["seed"]},
         "useful_tflops": round(tflops, 2),
+    }
+    print(json.dumps(out))
+    return 0
+
+
+def run_tier(args) -> int:
+    """kv-tier-9b: one dense-9b sequence's cache (context 16384: 1024 pages of 32 layers x 64 KiB)
+    evicted to the pinned host tier and restored, timed with events on the caller's stream around
+    each direction (each ends with the tier's dirty-page wait)."""
+    import numpy as np
+    import torch
+
+    import memory_bound_autoregressive_amd as bw
+    from memory_bound_autoregressive_amd import configs
+    from memory_bound_autoregressive_amd.session import Session
+
+    cfg = dict(configs.DENSE_9B)
+    if args.kv:
+        cfg["kv_dtype"] = args.kv
+    ctx = 16384
+    K = args.steps if args.steps_set else 5
+    W = args.warmup if args.warmup_set else 1
+    torch.cuda.set_device(0)
+    s = Session(cfg, seed=cfg["seed"], max_len=[ctx + 1], max_tokens=1, pool_seed=cfg["seed"] + 1, spare_pages=0)
+    s.synthesize(cfg["seed"] + 7, [ctx])
+    tier = bw.bw_kv_tier_create(s.pool, s.n_pages)
+    n_pg = (ctx + 15) // 16
+    page_bytes = cfg["n_layers"] * 2 * cfg["n_kv_heads"] * 16 * cfg["head_dim"] * kv_bytes(cfg)
+    moved = n_pg * page_bytes
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    d2h, h2d = [], []
+    for it in range(W + K):
+        bw.bw_kv_tier_touch(tier, s.page_table_host, np.array([ctx - 1], dtype=np.int32), 1, 1, s.max_pages)
+        torch.cuda.synchronize()
+        evs[0].record()
+        pages, slots = bw.bw_kv_tier_evict_lru(tier, n_pg)
+        bw.bw_kv_tier_wait(tier)
+        evs[1].record()
+        bw.bw_kv_tier_restore(tier, slots, pages)
+        bw.bw_kv_tier_wait(tier)
+        evs[2].record()
+        torch.cuda.synchronize()
+        assert len(pages) == n_pg
+        if it >= W:
+            d2h.append(evs[0].elapsed_time(evs[1]))
+            h2d.append(evs[1].elapsed_time(evs[2]))
+    bw.bw_kv_tier_free(tier)
+    s.close()
+    # the link as one contiguous copy of the same size each way (pinned host memory)
+    dev_buf = torch.empty(moved, dtype=torch.uint8, device="cuda")
+    host_buf = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+    cp = []
+    for it in range(2):
+        evs[0].record()
+        host_buf.copy_(dev_buf, non_blocking=True)
+        evs[1].record()
+        dev_buf.copy_(host_buf, non_blocking=True)
+        evs[2].record()
+        torch.cuda.synchronize()
+        cp = [evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[2])]
+    del dev_buf, host_buf
+    link = [moved / (t * 1e-3) / 1e9 for t in cp]
+    t_out, t_in = sum(d2h) / K, sum(h2d) / K
+    gb_out, gb_in = moved / (t_out * 1e-3) / 1e9, moved / (t_in * 1e-3) / 1e9
+    rt = 2 * moved / ((t_out + t_in) * 1e-3) / 1e9
+    print(f"[bench] kv-tier-9b: {n_pg} pages ({moved / 2**30:.2f} GiB) out {t_out:.1f} ms ({gb_out:.1f} GB/s), "
+          f"in {t_in:.1f} ms ({gb_in:.1f} GB/s); one contiguous copy: {link[0]:.1f} / {link[1]:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    out = {
+        "metric": "KV host-tier page migration GB/s (evict + restore, dense-9b pages)", "value": round(rt, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(t_out + t_in, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bytes", "data": "synthetic",
+        "config": {"workload": "kv-tier-9b", "context": ctx, "pages": n_pg, "page_bytes_all_layers": page_bytes,
+                   "kv": cfg.get("kv_dtype", "bf16"), "host_memory": "pinned (hipHostMalloc)",
+                   "copies": "one 2-D DMA copy per page (32 layer slices) on the tier's stream"},
+        "evict_gbps": round(gb_out, 2), "restore_gbps": round(gb_in, 2),
+        "contiguous_copy_gbps": {"to_host": round(link[0], 2), "to_device": round(link[1], 2)},
+        "roofline": {"bound": "pcie", "achieved": round(rt, 2), "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(rt / PCIE_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "DMA copies of the host tier (no kernel)"},
     }
     print(json.dumps(out))
     return 0
@@ -282,7 +363,7 @@ def main() -> int:
     ap.add_argument("--cooperative", action="store_true",
                     help="single-launch step through the cooperative launch API")
     ap.add_argument("--workload", default="dense-9b",
-                    choices=("dense-9b", "dense-27b", "moe-35b-a3b", "verify-9b", "prefill-9b"),
+                    choices=("dense-9b", "dense-27b", "moe-35b-a3b", "verify-9b", "prefill-9b", "kv-tier-9b"),
                     help="dense-9b (default): the headline line; the others time their own workload")
     ap.add_argument("--chunk", type=int, default=256, help="prefill-9b: tokens per prefill step")
     ap.add_argument("--kv", choices=("bf16", "fp8"), default=None,
@@ -310,6 +391,8 @@ def main() -> int:
         return 2
     if args.workload == "prefill-9b":
         return run_prefill(args)
+    if args.workload == "kv-tier-9b":
+        return run_tier(args)
     if args.workload != "dense-9b" or args.kv not in (None, "bf16"):
         return run_workload(args)
 

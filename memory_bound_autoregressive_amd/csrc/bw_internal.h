@@ -171,6 +171,13 @@ int launch_topk(const float* logits, int E, int k, int M, int32_t* sel, float* g
 int launch_dequant(const Mat& w, const int32_t* row_map, int map_lo, int map_n, float* dst, hipStream_t s);
 int launch_fill16(uint16_t* dst, size_t n, uint16_t bits, hipStream_t s);
 int launch_kv_round(int kv_dtype, const float* x, int64_t n, uint16_t* bits, float* back, hipStream_t s);
+// KV host tier: page ids of one packing launch, passed by value
+struct PageList {
+  static constexpr int kMax = 128;
+  int32_t id[kMax];
+};
+int launch_page_pack(uint8_t* pool, int64_t layer_bytes, int64_t page_bytes, int L, const PageList& ids, int n,
+                     uint8_t* stage, bool to_stage, hipStream_t s);
 
 // batched path (bw_gemm.hip): matrix-core GEMM over all rows of a step. IN_PLAIN / IN_RMSNORM
 // (rms = per-row RMSNorm factors from launch_rowrms); epilogues STORE_CANON, RESID, SWIGLU, LOGITS,

@@ -226,4 +226,28 @@ int launch_kv_round(int kv_dtype, const float* x, int64_t n, uint16_t* bits, flo
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// KV host tier: pages (every layer's slice of a physical page id) packed into / unpacked from a
+// contiguous staging buffer [i][layer][page_bytes], so that the PCIe transfer is one DMA copy.
+// Block (i, l) moves the slice of page ids.id[i] in layer l with 16-byte loads and stores.
+__global__ __launch_bounds__(256) void k_page_pack(uint8_t* __restrict__ pool, int64_t layer_bytes, int64_t page_bytes,
+                                                   PageList ids, uint8_t* __restrict__ stage, int to_stage) {
+  const int i = blockIdx.x, l = blockIdx.y, L = gridDim.y;
+  u32x4* dev = (u32x4*)(pool + l * layer_bytes + (int64_t)ids.id[i] * page_bytes);
+  u32x4* st = (u32x4*)(stage + ((int64_t)i * L + l) * page_bytes);
+  const int64_t n = page_bytes / 16;
+  if (to_stage) {
+    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) st[e] = dev[e];
+  } else {
+    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) dev[e] = st[e];
+  }
+}
+
+int launch_page_pack(uint8_t* pool, int64_t layer_bytes, int64_t page_bytes, int L, const PageList& ids, int n,
+                     uint8_t* stage, bool to_stage, hipStream_t s) {
+  if (n < 1 || n > PageList::kMax || page_bytes % 16) return -2;
+  hipLaunchKernelGGL(k_page_pack, dim3(n, L), dim3(256), 0, s, pool, layer_bytes, page_bytes, ids, stage,
+                     to_stage ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace bw

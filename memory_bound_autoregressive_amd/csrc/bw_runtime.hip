@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <map>
 #include <string>
 #include <thread>
@@ -782,7 +783,10 @@ extern "C" int bw_kv_pool_read(const bw_kv_pool* p, int32_t layer, int32_t page,
 // The deep-dive page's Hy3 overflow (section 6 item 3) keeps hot KV pages in VRAM and moves cold
 // ones to locked host memory over PCIe, evicting by the pages' access time stamps; a read of a
 // page under migration waits until the copy is done. Here a page is one physical page id across
-// all layers; its L slices are one strided (2-D) DMA copy on the tier's own stream.
+// all layers. A kernel packs up to 128 pages into a contiguous device staging buffer (or unpacks
+// them), and each run of consecutive host slots is one DMA copy, all on the tier's own stream: a
+// strided copy per page (L rows of one page-layer) reached 45 GB/s for 64 KiB rows and 37 GB/s
+// for 32 KiB rows, against 57 GB/s for one contiguous copy.
 
 struct bw_kv_tier {
   bw_kv_pool* pool = nullptr;
@@ -796,6 +800,8 @@ struct bw_kv_tier {
   hipStream_t copy = nullptr;       // copy stream (default priority)
   hipEvent_t after = nullptr;       // caller's stream position before a batch of copies
   hipEvent_t done = nullptr;        // copy stream position after the latest batch of copies
+  uint8_t* stage = nullptr;         // device staging buffer [stage_pages][n_layers][page_bytes]
+  int32_t stage_pages = 0;
 };
 
 extern "C" int bw_kv_lru_select(const uint64_t* stamps, const uint8_t* resident, int32_t n_pages, int32_t n,
@@ -821,6 +827,7 @@ extern "C" int bw_kv_tier_free(bw_kv_tier* t) {
   if (t->done) (void)hipEventDestroy(t->done);
   if (t->copy) (void)hipStreamDestroy(t->copy);
   if (t->host) (void)hipHostFree(t->host);
+  if (t->stage) (void)hipFree(t->stage);
   delete t;
   return BW_OK;
 }
@@ -844,6 +851,14 @@ extern "C" int bw_kv_tier_create(bw_kv_pool* pool, int32_t host_pages, bw_kv_tie
       hipEventCreateWithFlags(&t->done, hipEventDisableTiming) != hipSuccess) {
     bw_kv_tier_free(t);
     return fail(BW_EHIP, "tier stream or event creation failed");
+  }
+  const size_t per_page = (size_t)pool->m->c.n_layers * page_bytes;
+  t->stage_pages = (int32_t)std::max<size_t>(1, std::min<size_t>({(size_t)host_pages, (size_t)PageList::kMax,
+                                                                   ((size_t)256 << 20) / per_page}));
+  if (hipMalloc((void**)&t->stage, t->stage_pages * per_page) != hipSuccess) {
+    t->stage = nullptr;
+    bw_kv_tier_free(t);
+    return fail(BW_ENOMEM, "hipMalloc for the tier's staging buffer failed");
   }
   t->stamp.assign(pool->n_pages, 0);
   t->resident.assign(pool->n_pages, 0);
@@ -872,15 +887,31 @@ extern "C" int bw_kv_tier_touch(bw_kv_tier* t, const int32_t* page_table, const 
   return BW_OK;
 }
 
-// one page across all layers: device slice l of page p <-> host slot s, row l
-static hipError_t tier_copy(bw_kv_tier* t, int32_t page, int32_t slot, bool to_host) {
+// pages[i] <-> host slots[i], i < n, in chunks through the staging buffer; one DMA copy per run of
+// consecutive host slots within a chunk
+static int tier_move(bw_kv_tier* t, const int32_t* pages, const int32_t* slots, int32_t n, bool to_host) {
   const bw_kv_pool* p = t->pool;
-  const size_t pb = (size_t)p->page_elems * p->es, lb = (size_t)p->layer_elems * p->es;
-  uint8_t* dev = (uint8_t*)p->data + (size_t)page * pb;
-  uint8_t* host = t->host + (size_t)slot * p->m->c.n_layers * pb;
-  if (to_host)
-    return hipMemcpy2DAsync(host, pb, dev, lb, pb, p->m->c.n_layers, hipMemcpyDeviceToHost, t->copy);
-  return hipMemcpy2DAsync(dev, lb, host, pb, pb, p->m->c.n_layers, hipMemcpyHostToDevice, t->copy);
+  const int L = p->m->c.n_layers;
+  const int64_t pb = p->page_elems * p->es, lb = p->layer_elems * p->es, per = (int64_t)L * pb;
+  for (int32_t c0 = 0; c0 < n; c0 += t->stage_pages) {
+    const int32_t m = std::min(t->stage_pages, n - c0);
+    PageList ids;
+    for (int32_t i = 0; i < m; ++i) ids.id[i] = pages[c0 + i];
+    if (to_host && launch_page_pack((uint8_t*)p->data, lb, pb, L, ids, m, t->stage, true, t->copy))
+      return fail(BW_EHIP, "page packing launch failed");
+    for (int32_t i = 0; i < m;) {
+      int32_t j = i + 1;
+      while (j < m && slots[c0 + j] == slots[c0 + j - 1] + 1) ++j;
+      uint8_t* h = t->host + (int64_t)slots[c0 + i] * per;
+      uint8_t* d = t->stage + (int64_t)i * per;
+      HIP_OK(hipMemcpyAsync(to_host ? (void*)h : (void*)d, to_host ? (const void*)d : (const void*)h, (size_t)((j - i) * per),
+                            to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice, t->copy));
+      i = j;
+    }
+    if (!to_host && launch_page_pack((uint8_t*)p->data, lb, pb, L, ids, m, t->stage, false, t->copy))
+      return fail(BW_EHIP, "page unpacking launch failed");
+  }
+  return BW_OK;
 }
 
 extern "C" int bw_kv_tier_evict_lru(bw_kv_tier* t, int32_t n, int32_t* dev_pages, int32_t* host_slots,
@@ -897,15 +928,16 @@ extern "C" int bw_kv_tier_evict_lru(bw_kv_tier* t, int32_t n, int32_t* dev_pages
   // these pages)
   HIP_OK(hipEventRecord(t->after, (hipStream_t)stream));
   HIP_OK(hipStreamWaitEvent(t->copy, t->after, 0));
-  for (int32_t i = 0; i < got; ++i) {
+  for (int32_t i = 0; i < got; ++i) {  // the free list is kept descending: lowest slots first
     const int32_t slot = t->free_slots.back();
     t->free_slots.pop_back();
     t->slot_used[slot] = 1;
     host_slots[i] = slot;
     t->resident[dev_pages[i]] = 0;
     t->stamp[dev_pages[i]] = 0;
-    HIP_OK(tier_copy(t, dev_pages[i], slot, true));
   }
+  const int rc2 = tier_move(t, dev_pages, host_slots, got, true);
+  if (rc2 != BW_OK) return rc2;
   HIP_OK(hipEventRecord(t->done, t->copy));
   return BW_OK;
 }
@@ -926,14 +958,16 @@ extern "C" int bw_kv_tier_restore(bw_kv_tier* t, const int32_t* host_slots, cons
   // after the work queued on the caller's stream (a step that still reads a target page)
   HIP_OK(hipEventRecord(t->after, (hipStream_t)stream));
   HIP_OK(hipStreamWaitEvent(t->copy, t->after, 0));
+  const int rc2 = tier_move(t, dev_pages, host_slots, n, false);
+  if (rc2 != BW_OK) return rc2;
   for (int32_t i = 0; i < n; ++i) {
-    HIP_OK(tier_copy(t, dev_pages[i], host_slots[i], false));
     t->resident[dev_pages[i]] = 1;
     t->stamp[dev_pages[i]] = t->clock;
     // the slot is free again; a later eviction into it runs after this copy on the same stream
     t->slot_used[host_slots[i]] = 0;
     t->free_slots.push_back(host_slots[i]);
   }
+  std::sort(t->free_slots.begin(), t->free_slots.end(), std::greater<int32_t>());
   HIP_OK(hipEventRecord(t->done, t->copy));
   return BW_OK;
 }
