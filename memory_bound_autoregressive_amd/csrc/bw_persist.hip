@@ -1501,11 +1501,12 @@ static int launch_persist_t(const PersistParams& p, int nwg, hipStream_t s, bool
 // per wave group sized for 256 workgroups
 int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                    bool query_only) {
-  // FP8 E4M3 caches: the 9B and tiny shapes
+  // FP8 E4M3 caches
 #define BW_P8(DM, FF, LD, ND, LF, NF, DD, QR, RQ, RO, RG, RF)                        \
   if (kv_dtype == 3 && d == DM && F == FF && D == DD && rep == QR)                  \
     return launch_persist_t<LD, ND, LF, NF, 3, DD, QR, RQ, RO, RG, RF>(p, nwg, s, query_only);
   BW_P8(4096, 12288, 64, 2, 64, 6, 128, 4, 3, 2, 2, 1)
+  BW_P8(5120, 17408, 32, 5, 32, 17, 128, 5, 1, 1, 1, 1)
   BW_P8(256, 1024, 8, 1, 32, 1, 64, 2, 1, 1, 1, 1)
 #undef BW_P8
   if (kv_dtype == 3) return -2;
@@ -1527,10 +1528,10 @@ int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, in
 int launch_persist_moe(const PersistParams& p, int d, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                        bool query_only) {
   const int slots = p.top_k + p.n_shared;
-  if (kv_dtype == 3) return -2;  // no FP8 form: the kernel chain runs the step
 #define BW_PM(DM, FE, SL, LD, ND, LF, DD, QR, RQ, RO, RG, RF)                                                    \
   if (d == DM && p.Fe == FE && slots == SL && D == DD && rep == QR) {                                           \
     static_assert(DM == LD * ND * 32 && FE == LF * 32, "d and Fe match the lane split");                        \
+    if (kv_dtype == 3) return launch_persist_t<LD, ND, LF, SL, 3, DD, QR, RQ, RO, RG, RF, true>(p, nwg, s, query_only); \
     return kv_dtype == 1 ? launch_persist_t<LD, ND, LF, SL, 1, DD, QR, RQ, RO, RG, RF, true>(p, nwg, s, query_only) \
                          : launch_persist_t<LD, ND, LF, SL, 2, DD, QR, RQ, RO, RG, RF, true>(p, nwg, s, query_only); \
   }

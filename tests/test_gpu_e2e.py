@@ -33,8 +33,11 @@ DENSE_27B_2L.pop("context", None)
 TINY_FP8 = dict(configs.TINY, kv_dtype="fp8", name="tiny-fp8")
 DENSE_9B_2L_FP8 = dict(configs.DENSE_9B, n_layers=2, vocab=512, kv_dtype="fp8", name="dense-9b-2l-fp8",
                        prompt=12, steps=20)
+MOE_2K_FP8 = dict(MOE_2K, kv_dtype="fp8", name="moe-2k-fp8")
+DENSE_27B_2L_FP8 = dict(DENSE_27B_2L, kv_dtype="fp8", name="dense-27b-2l-fp8")
 # shapes with a single-launch instantiation
-SINGLE_LAUNCH_SHAPES = ("tiny", "moe-2k", "dense-27b-2l", "tiny-fp8", "dense-9b-2l-fp8")
+SINGLE_LAUNCH_SHAPES = ("tiny", "moe-2k", "dense-27b-2l", "tiny-fp8", "dense-9b-2l-fp8", "moe-2k-fp8",
+                        "dense-27b-2l-fp8")
 ROUTER_TAU = 1e-4
 
 
@@ -98,10 +101,11 @@ def _compare(g, gam, o, where):
                                                   (MOE_2K, 1014, None, 2), (MOE_2K, 1015, None, 0),
                                                   (DENSE_27B_2L, 1016, None, 1), (TINY_FP8, 1041, None, 1),
                                                   (TINY_FP8, 1042, None, 0), (TINY_FP8, 1043, 1, 0),
-                                                  (DENSE_9B_2L_FP8, 1044, None, 1)],
+                                                  (DENSE_9B_2L_FP8, 1044, None, 1), (MOE_2K_FP8, 1045, None, 1),
+                                                  (DENSE_27B_2L_FP8, 1046, None, 1)],
                          ids=["tiny", "tiny-cooperative", "tiny-chain", "moe-small", "tiny-gemm", "moe-small-gemm",
                               "moe-2k", "moe-2k-cooperative", "moe-2k-chain", "dense-27b-2l", "tiny-fp8",
-                              "tiny-fp8-chain", "tiny-fp8-gemm", "dense-9b-2l-fp8"])
+                              "tiny-fp8-chain", "tiny-fp8-gemm", "dense-9b-2l-fp8", "moe-2k-fp8", "dense-27b-2l-fp8"])
 def test_prompt_then_greedy_decode(cfg, seed, gemm, single):
     """single: batch-1 steps as one launch (1: ordinary, 2: cooperative; shapes with an instantiation), 0: the
     kernel chain.
