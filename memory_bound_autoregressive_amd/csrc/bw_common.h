@@ -99,17 +99,14 @@ __device__ __forceinline__ void kv_unpack8(typename KvT<KVDT>::C8 v, float* out)
 }
 
 // 8 FP8 E4M3 elements -> 8 bf16 (exact: every E4M3 value is a bf16 value), as the matrix-core
-// operand of a bf16 product
+// operand of a bf16 product: gfx950's scaled conversion with scale 1, two elements per instruction
 __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 v) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
-    r[2 * i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo[0]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo[1]) << 16);
-    r[2 * i + 1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi[0]) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi[1]) << 16);
+    r[2 * i] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[i], 1.0f, false));
+    r[2 * i + 1] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[i], 1.0f, true));
   }
   return r;
 }
