@@ -26,8 +26,8 @@
 // them in split order and applies the step's epilogue (RoPE + KV append, residual, SwiGLU, logits).
 //
 // Products of more than 64 rows (verify steps, prefill chunks) take k_gemm_w32 instead: 32x32
-// tiles, 256 weight rows per workgroup, and the block scales folded into the weights as exact fp16
-// pairs (described at the kernel). The two forms write the same partials.
+// tiles, 256 weight rows per workgroup, and the block scales applied once per block to exact block
+// sums (described at the kernel). The two forms write the same partials.
 #include <algorithm>
 
 #include "bw_common.h"
@@ -240,18 +240,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 }
 
-// ---- the wide form: 32x32 tiles with the scales folded into the weights --------------------------
+// ---- the wide form: 32x32 tiles, block sums scaled once per block --------------------------------
 // For products of more than 64 rows. A workgroup of 8 waves covers 256 weight rows x 128 X rows:
 // wave w owns weight rows [32 w, +32) against all 128 X rows as 4 tiles of
 // v_mfma_f32_32x32x16_f16 (lane l gives A row / B column l % 32 with K slots 8 (l / 32) .. +7; the
 // result's slot r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32), so each
-// dequantised weight fragment feeds 12 matrix instructions.
+// unpacked weight fragment feeds 8 matrix instructions.
 // Weights: lane l reads bytes 8h..8h+7 of a block (h = l / 32); its 4-byte group g = 2h + s feeds
-// K-step s of the block, in the staged X order. The block scale folds into the weight exactly as an
-// fp16 pair, w_hi = fp16(s (q - 8)) and w_lo = s (q - 8) - w_hi (a fused multiply-add whose exact
-// result is representable), so there is no per-block fp32 work and the accumulators run over the
-// whole K range: y += x_hi w_hi + x_hi w_lo + x_lo w_hi (the dropped x_lo w_lo is below 2^-22 of a
-// product). Rows past N or M read clamped addresses; their results are never stored.
+// K-step s of the block, in the staged X order. The codes enter the products as q - 8, exact in
+// fp16, against x_hi and x_lo (x = x_hi + x_lo in fp16, so every product is exact in fp32): each
+// block's sums d = sum (q - 8)(x_hi + x_lo) over its 32 columns start from zero, and the block
+// scale is applied once, acc += s d (one fused multiply-add per output per block, with the fp16
+// scale read by v_fma_mix_f32). Rows past N or M read clamped addresses; their results are never
+// stored.
 // Pipelining: a chunk's X (from L2) is loaded one chunk ahead and staged into the other LDS buffer
 // after the current chunk's products; its codes and scales (from HBM) are loaded two chunks ahead
 // into one of three register sets.
@@ -353,23 +354,26 @@ __global__ __launch_bounds__(kW32Threads, 2) void k_gemm_w32(GemvParams p, int M
   auto compute = [&](const WChunk& c, int buf) {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)c.sc[bb]);
-      const h8_t s8 = {sv, sv, sv, sv, sv, sv, sv, sv};
+      // the block's sums of (q - 8) x over its 32 columns (q - 8 exact in fp16, x as hi + lo), then
+      // scaled once: acc += s * sum
+      f16x_t d[4];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const h8_t q = codes_to_h8_perm(c.cw[bb][st]);
-        const h8_t wh = q * s8;
-        const h8_t wl = __builtin_elementwise_fma(q, s8, -wh);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int at = (32 * i + l32) * kW32XP + 32 * bb + 8 * (2 * h + st);
           const h8_t ah = *(const h8_t*)(xs[buf][0] + at);
           const h8_t al = *(const h8_t*)(xs[buf][1] + at);
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, wh, acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, wl, acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, wh, acc[i], 0, 0, 0);
+          d[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, q, st == 0 ? f16x_t{} : d[i], 0, 0, 0);
+          d[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, q, d[i], 0, 0, 0);
         }
       }
+      const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)c.sc[bb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(sv, d[i][r], acc[i][r]);
     }
   };
 
