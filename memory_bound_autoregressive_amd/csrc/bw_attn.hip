@@ -329,6 +329,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int ti = real ? qr / rep : 0, hr = real ? qr - ti * rep : 0;
   const int qpos = real ? base_pos + ti : 0x7fffffff;
   constexpr int NQ = MT == 2 ? 3 : 2;  // parts of the query
+  // head dims of the 8 K slots of lane group grp in 32-dim chunk c of the score product. A score
+  // sums over all dims, so any order that K and Q share is the same sum: 16-bit caches take dims
+  // 32 c + 8 grp ..+7 (one 16-byte load each); an FP8 cache takes 64 (c / 2) + 16 grp + 8 (c % 2)
+  // ..+7, so that one 16-byte load brings a lane the dims of two chunks
+  auto kdim = [&](int c) { return KVDT == 3 ? 64 * (c >> 1) + 16 * grp + 8 * (c & 1) : 32 * c + 8 * grp; };
   typedef typename std::remove_reference<decltype(e8{}[0])>::type el8;
   typedef typename std::remove_reference<decltype(e4{}[0])>::type el4;
   e8 qp[NQ][NC];
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) qv[c][h] = qsrc[(32 * c + 8 * grp) / 4 + h];
+      for (int h = 0; h < 2; ++h) qv[c][h] = qsrc[kdim(c) / 4 + h];
     const float qs = real ? p.scale : 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -379,17 +384,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         (ok ? (int64_t)page * p.pool_page_stride + (int64_t)(g * 2) * kPageTokens * D : 0);
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, ok ? 2 * kPageTokens * D * ES : 0, 0x00020000);
-    if constexpr (KVDT == 3) {  // 8-byte loads, widened to bf16 when the page is used
+    if constexpr (KVDT == 3) {
+      // 16-byte loads of 16 FP8 elements, widened to bf16 when the page is used: K in kr[0 .. NC/2)
+      // (kr[u] holds dims 64 u + 16 grp ..+15 of token c16: chunks 2u and 2u + 1), V in
+      // vr[0 .. D/64) (16-byte piece k = lane + 64 u: token k / (D/16), dims 16 (k % (D/16)) ..+15)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, c16 * D + 32 * c + 8 * grp, 0, 0);
-        kr[c] = u32x4{w[0], w[1], 0u, 0u};
-      }
+      for (int u = 0; u < NC / 2; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(r, c16 * D + 64 * u + 16 * grp, 0, 0);
 #pragma unroll
-      for (int q4 = 0; q4 < D / 32; ++q4) {
-        const int k = lane + 64 * q4;
-        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, kPageTokens * D + (k / (D / 8)) * D + 8 * (k % (D / 8)), 0, 0);
-        vr[q4] = u32x4{w[0], w[1], 0u, 0u};
+      for (int u = 0; u < D / 64; ++u) {
+        const int k = lane + 64 * u;
+        vr[u] = __builtin_amdgcn_raw_buffer_load_b128(r, kPageTokens * D + (k / (D / 16)) * D + 16 * (k % (D / 16)), 0, 0);
       }
     } else {
 #pragma unroll
@@ -408,25 +412,32 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       if (lane == 0) atomicOr(p.err, 1);
       return;
     }
-    u32x4 kraw[NC], vraw[D / 32];  // bf16 / fp16 operands
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if constexpr (KVDT == 3) kraw[c] = fp8x8_to_bf16x8(u32x2{kin[c][0], kin[c][1]});
-      else kraw[c] = kin[c];
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < D / 32; ++q4) {
-      if constexpr (KVDT == 3) vraw[q4] = fp8x8_to_bf16x8(u32x2{vin[q4][0], vin[q4][1]});
-      else vraw[q4] = vin[q4];
-    }
+    u32x4 kraw[NC];  // bf16 / fp16 operands
+    const u32x4 z = {0u, 0u, 0u, 0u};
     // stage V (this wave's buffer; the LDS operations of one wave run in order); slots past the
     // sequence end are written as zeros, so stale or NaN contents never meet a zero probability
+    if constexpr (KVDT == 3) {
 #pragma unroll
-    for (int q4 = 0; q4 < D / 32; ++q4) {
-      const int k = lane + 64 * q4;
-      const int tk = k / (D / 8);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *(u32x4*)(vl + tk * kVStride + 8 * (k % (D / 8))) = pg * kPageTokens + tk < kv_len ? vraw[q4] : z;
+      for (int c = 0; c < NC; ++c)
+        kraw[c] = fp8x8_to_bf16x8((c & 1) ? u32x2{kin[c >> 1][2], kin[c >> 1][3]} : u32x2{kin[c >> 1][0], kin[c >> 1][1]});
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) {
+        const int k = lane + 64 * u;
+        const int tk = k / (D / 16);
+        const bool live = pg * kPageTokens + tk < kv_len;
+        uint16_t* dst = vl + tk * kVStride + 16 * (k % (D / 16));
+        *(u32x4*)dst = live ? fp8x8_to_bf16x8(u32x2{vin[u][0], vin[u][1]}) : z;
+        *(u32x4*)(dst + 8) = live ? fp8x8_to_bf16x8(u32x2{vin[u][2], vin[u][3]}) : z;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kraw[c] = kin[c];
+#pragma unroll
+      for (int q4 = 0; q4 < D / 32; ++q4) {
+        const int k = lane + 64 * q4;
+        const int tk = k / (D / 8);
+        *(u32x4*)(vl + tk * kVStride + 8 * (k % (D / 8))) = pg * kPageTokens + tk < kv_len ? vin[q4] : z;
+      }
     }
     // scores^T: lane holds tokens 4 grp + i of row c16
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
