@@ -386,7 +386,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs the decode step on one GPU; --gpus {args.gpus} "
+        print(f"bench.py: the decode step runs on one GPU; --gpus {args.gpus} "
               f"(WORLD_SIZE {world}) is not supported. Run with --gpus 1.", file=sys.stderr)
         return 2
     if args.workload == "prefill-9b":
