@@ -183,6 +183,25 @@ def test_dense_9b_synthesized_context(single, kv):
         p.close()
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("single,kv", [(True, "bf16"), (False, "bf16"), (True, "fp8")],
+                         ids=["single-launch", "chain", "single-launch-fp8"])
+def test_last_position_of_the_longest_context(single, kv):
+    """The largest size a model allows (max_positions 65536): one step at position 65535 over a
+    synthesised context of 65535 positions (4096 pages per layer), 9B layer shape, two layers."""
+    cfg = dict(configs.DENSE_9B, n_layers=2, vocab=512, kv_dtype=kv, name="dense-9b-2l-longest")
+    ctx, seed = 65535, 1051
+    print(f"[case] longest context {ctx}, {kv} cache, {'single launch' if single else 'chain'}", flush=True)
+    p = Pair(cfg, seed, ctx + 1, ctx0=ctx, synth_seed=seed + 7, single=single)
+    assert p.single or not single
+    try:
+        g, gam, o = p.step([int(np.random.default_rng(seed).integers(0, cfg["vocab"]))])
+        err = _compare(g, gam, o, "position 65535")
+        print(f"[result] position 65535 ({kv}, {'single launch' if single else 'chain'}): max |logit diff| = {err:.3e}")
+    finally:
+        p.close()
+
+
 # the verify workload's layer shape (9B dimensions), two layers and a small vocabulary so that
 # the oracle checks every row of the batch
 VERIFY_SMALL = dict(configs.VERIFY_9B, n_layers=2, vocab=4096, name="verify-9b-2l")
