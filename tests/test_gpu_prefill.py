@@ -18,9 +18,11 @@ from test_gpu_e2e import VERIFY_SMALL, _compare, _cuda_i32
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("cfg,prompt_len,chunk", [(configs.TINY, 50, 16), (configs.TINY, 45, 40),
-                                                  (VERIFY_SMALL, 300, 128), (VERIFY_SMALL, 77, 77)],
-                         ids=["tiny-16", "tiny-40", "9b-layers-128", "9b-layers-one-chunk"])
+                                                  (VERIFY_SMALL, 300, 128), (VERIFY_SMALL, 77, 77),
+                                                  (VERIFY_SMALL, 700, 640)],
+                         ids=["tiny-16", "tiny-40", "9b-layers-128", "9b-layers-one-chunk", "9b-layers-640"])
 def test_chunked_prefill_matches_oracle(cfg, prompt_len, chunk):
     seed, steps = 1061, 6
     rng = np.random.default_rng(seed)
