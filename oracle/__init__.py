@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.or_model_router_logits.argtypes = [vp, i32, vp, vp]
         L.or_model_moe_ffn.restype = i32
         L.or_model_moe_ffn.argtypes = [vp, i32, vp, vp, vp]
+        L.or_model_moe_ffn_sel.restype = i32
+        L.or_model_moe_ffn_sel.argtypes = [vp, i32, vp, vp, vp, vp, dbl, vp]
         L.or_kv_create.restype = vp
         L.or_kv_create.argtypes = [vp, i32, i64]
         L.or_kv_free.argtypes = [vp]
@@ -287,6 +289,19 @@ class Model:
         sel = np.empty(self.cfg["top_k"], dtype=np.int32)
         lib().or_model_moe_ffn(self.h, layer, _p(h), _p(out), _p(sel))
         return out, sel
+
+    def moe_ffn_sel(self, layer: int, h, sel_in, tau: float):
+        """MoE FFN with a proposed expert set (the near-tie rule): (rc, out, set used, adopted)."""
+        h = _f64(h)
+        k = self.cfg["top_k"]
+        sin = np.ascontiguousarray(sel_in, dtype=np.int32)
+        assert sin.shape == (k,)
+        out = np.empty(self.cfg["d_model"], dtype=np.float64)
+        sel = np.empty(k, dtype=np.int32)
+        adopted = ctypes.c_int32(0)
+        rc = lib().or_model_moe_ffn_sel(self.h, layer, _p(h), _p(out), _p(sin), _p(sel), tau,
+                                        ctypes.byref(adopted))
+        return rc, out, sel, adopted.value
 
 
 class KV:

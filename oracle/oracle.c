@@ -716,6 +716,13 @@ int or_model_moe_ffn(const or_model* m, int layer, const double* h, double* out,
   return or_moe_ffn(m, layer, h, out, NULL, sel_out, 0.0, NULL);
 }
 
+/* exported for tests: the MoE FFN of one layer with a proposed expert set sel_in (the near-tie
+ * rule above); returns 0 (sel_in adopted, or equal to the oracle's set) or -1 (rejected) */
+int or_model_moe_ffn_sel(const or_model* m, int layer, const double* h, double* out,
+                         const int32_t* sel_in, int32_t* sel_out, double tau, int32_t* adopted) {
+  return or_moe_ffn(m, layer, h, out, sel_in, sel_out, tau, adopted);
+}
+
 /* Decode T new tokens of sequence s at positions pos0 .. pos0+T-1. The keys and values of all
  * T tokens are cached before any of them attends; token t attends to positions 0..pos0+t.
  *   logits      [T][vocab] (optional)

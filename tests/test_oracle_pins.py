@@ -463,6 +463,63 @@ def test_moe_full_topk_is_softmax_mixture_and_single_expert_is_dense():
     assert sel3.tolist() == np.argsort(-r8, kind="stable")[:3].tolist()
 
 
+def _gated_mixture(m, layer, h, experts):
+    """The MoE layer's definition written out for a given expert set: renormalised softmax gates
+    of the router logits over the set, times each expert's SwiGLU FFN, plus the ungated shared
+    expert (workload contract: softmax top-k routing, renormalised gates, one shared expert)."""
+    P = scipy.special.softmax(m.router_logits(layer, h))
+    z = sum(P[e] for e in experts)
+    out = sum((P[e] / z) * m.ffn(layer, h, expert=int(e)) for e in experts)
+    for s_ in range(m.cfg["n_shared"]):
+        out = out + m.ffn(layer, h, expert=s_, shared=True)
+    return out
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_moe_near_tie_adoption(seed):
+    """The router's several-correct-answers rule: a proposed top-k set is adopted only when it
+    differs from the oracle's by experts whose logits lie within tau of the k-th / (k+1)-th
+    boundary; duplicates, ids outside [0, E) and any other difference are rejected (rc -1)."""
+    m = oracle.Model(TINY_MOE, seed)
+    E, k = TINY_MOE["n_experts"], TINY_MOE["top_k"]
+    h = np.random.default_rng(seed).standard_normal(TINY_MOE["d_model"])
+    r = m.router_logits(1, h)
+    order = np.argsort(-r, kind="stable")
+    kth, nxt = int(order[k - 1]), int(order[k])
+    gap = r[kth] - r[nxt]
+    assert gap > 0
+    own = [int(e) for e in order[:k]]
+    ref_own = _gated_mixture(m, 1, h, own)
+    tol = dict(rtol=1e-12, atol=1e-12 * np.abs(ref_own).max())
+    # the oracle's own set in another order: nothing to adopt, same output
+    rc, out, used, adopted = m.moe_ffn_sel(1, h, own[::-1], 0.0)
+    assert (rc, adopted) == (0, 0) and sorted(used.tolist()) == sorted(own)
+    assert np.allclose(out, ref_own, **tol)
+    # k-th expert swapped for the (k+1)-th: adopted when the gap is within tau ...
+    swapped = own[:-1] + [nxt]
+    rc, out, used, adopted = m.moe_ffn_sel(1, h, swapped, gap * 1.01)
+    assert (rc, adopted) == (0, 1) and used.tolist() == swapped
+    ref_sw = _gated_mixture(m, 1, h, swapped)
+    assert np.allclose(out, ref_sw, **tol)
+    assert not np.allclose(out, ref_own, **tol)  # adoption changes the layer's output
+    # ... and rejected when it is not
+    rc, _, _, adopted = m.moe_ffn_sel(1, h, swapped, gap * 0.99)
+    assert (rc, adopted) == (-1, 0)
+    # duplicates and out-of-range ids are never valid, whatever tau
+    for bad in ([own[0], own[0]] + own[1:k - 1], own[:-1] + [E], own[:-1] + [-1]):
+        rc, _, _, adopted = m.moe_ffn_sel(1, h, bad, 1e9)
+        assert (rc, adopted) == (-1, 0), bad
+    # an expert far below the boundary may not come in ...
+    low = int(order[-1])
+    assert r[nxt] - r[low] > gap * 1.01
+    rc, _, _, _ = m.moe_ffn_sel(1, h, own[:-1] + [low], gap * 1.01)
+    assert rc == -1
+    # ... nor may an expert far above it go out (the top-1 dropped for the (k+1)-th)
+    assert r[int(order[0])] - r[kth] > gap * 1.01
+    rc, _, _, _ = m.moe_ffn_sel(1, h, own[1:] + [nxt], gap * 1.01)
+    assert rc == -1
+
+
 def test_oracle_reads_synthetic_context():
     m = oracle.Model(TINY, 3)
     kv = oracle.KV(m, 2, 8)
