@@ -66,6 +66,30 @@ def algorithmic_bytes(cfg: dict, ctx_mean: float) -> dict:
             "embed": embed, "total": weights + kv_read + kv_write + router + embed}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def traced_launch_us(step_fn, n: int) -> float:
+    """Mean duration of one bw_decode_step launch: HIP events recorded on the step's stream right
+    before and after the decode call only (bookkeeping kernels run outside the events)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a_, b_ in evs:
+        step_fn(a_, b_)
+    torch.cuda.synchronize()
+    return sum(a_.elapsed_time(b_) for a_, b_ in evs) * 1000.0 / n
+
+
 def cpu_baseline(cfg: dict, ctx: int, seconds: float) -> dict:
     """The oracle as it stands: fp64 decode steps at context `ctx` (synthesised), timed."""
     import numpy as np
@@ -86,9 +110,60 @@ def cpu_baseline(cfg: dict, ctx: int, seconds: float) -> dict:
         if el >= seconds or n >= 60:
             break
     om.close()
-    return {"value": n / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": n / el, "unit": "tok/s", "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} fp64 decode steps of the same model at context {ctx}..{ctx + n} "
                       f"(context synthesised, not prefilled), {el:.1f} s"}
+
+
+def cpu_baseline_verify(cfg: dict, lens: list, t: int, seconds: float) -> dict:
+    """The oracle on verify steps: sequences of the batch in order (shortest first), t positions
+    each at its own synthesised context, until the time budget is spent."""
+    import numpy as np
+    import oracle
+
+    keys = ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab", "rms_eps",
+            "rope_base", "kv_dtype")
+    om = oracle.Model({k: cfg[k] for k in keys if k in cfg}, cfg["seed"])
+    order = np.argsort(lens)
+    kv = oracle.KV(om, len(lens), t + 1)
+    rng = np.random.default_rng(cfg["seed"])
+    n, pos, t0 = 0, 0, time.perf_counter()
+    done = []
+    for b in order:
+        kv.set_synth(int(b), cfg["seed"] + 7, int(b), lens[b])
+        oracle.forward(om, kv, int(b), [int(v) for v in rng.integers(0, cfg["vocab"], t)], lens[b])
+        n += 1
+        pos += t
+        done.append(lens[b])
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    kv.close()
+    om.close()
+    return {"value": pos / el, "unit": "positions/s", "cores": oracle.num_threads(), "cpu_model": cpu_model(),
+            "kind": "oracle", "sample": f"{n} fp64 verify steps of single sequences ({t} positions each, contexts "
+                                        f"{done}, synthesised), {el:.1f} s"}
+
+
+def committed_traffic(workload: str, cfg: dict, ctx: float):
+    """Counted HBM bytes per launch of the single-launch step from the committed FETCH_SIZE /
+    WRITE_SIZE profile of this workload, when its kernel sources are unchanged and its contexts lie
+    within 64 positions of ctx; else None."""
+    name = {"dense-9b": "step_dense9b_traffic.json", "dense-27b": "step_dense27b_traffic.json",
+            "moe-35b-a3b": "step_moe35b_traffic.json"}.get(workload)
+    kv = cfg.get("kv_dtype", "bf16")
+    if name is None or kv != "bf16":
+        return None
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    from memory_bound_autoregressive_amd.build import source_digest
+    lo, hi = tr.get("contexts", (0, -1))
+    if lo - 64 <= ctx <= hi + 64 and tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ()))):
+        return round(tr["hbm_bytes_per_launch"])
+    return None
 
 
 def run_prefill(args) -> int:
@@ -264,13 +339,13 @@ def run_workload(args) -> int:
     if args.workload == "verify-9b":
         B, t = cfg["batch"], cfg["t"]
         lens = [int(v) for v in rng.integers(cfg["ctx_lo"], cfg["ctx_hi"] + 1, B)]
-        s = Session(cfg, seed=seed, max_len=[n + (W + K + 2) * t for n in lens], max_tokens=B * t,
-                    pool_seed=seed + 1)
+        s = Session(cfg, seed=seed, max_len=[n + (W + K + 2 + 8) * t for n in lens], max_tokens=B * t,
+                    pool_seed=seed + 1)  # 8 more steps for the traced passes
         s.synthesize(seed + 7, lens)
     else:
         B, t = 1, 1
         lens = [cfg.get("context", cfg.get("prompt"))]
-        s = Session(cfg, seed=seed, max_len=[lens[0] + W + K + 2], max_tokens=1, pool_seed=seed + 1)
+        s = Session(cfg, seed=seed, max_len=[lens[0] + W + K + 2 + 32], max_tokens=1, pool_seed=seed + 1)
         s.synthesize(seed + 7, lens)
     single = bool(bw.bw_set_single_launch(s.model, 0 if args.chain else 1)) and not args.chain and B * t == 1
     torch.cuda.synchronize()
@@ -286,10 +361,14 @@ def run_workload(args) -> int:
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
 
-    def step():
+    def step(ev=None):
         if t > 1:  # fresh drafts after each sequence's next input token
             tokens.view(B, t)[:, 1:] = torch.randint(0, V, (B, t - 1), generator=gen, device=dev, dtype=torch.int32)
+        if ev is not None:
+            ev[0].record()
         bw.bw_decode_step(s.model, s.pool, tokens, seq_lens, s.page_table, B, t, s.max_pages, logits, argmax)
+        if ev is not None:
+            ev[1].record()
         bw.bw_spec_accept(s.model, tokens, argmax, logits, seq_lens, ring, count, cap, None, B, t)
 
     for _ in range(W):
@@ -309,6 +388,62 @@ def run_workload(args) -> int:
     ms_per_step = e0.elapsed_time(e1) / K
     committed = int(count.sum().item()) - c0
     ctx1 = seq_lens.cpu().numpy().astype(np.float64)
+    kv_pos_layer = 2 * cfg["n_kv_heads"] * cfg["head_dim"] * kv_bytes(cfg)  # bytes per cached position and layer
+    roofline, roofline_mfma, kernel_us = None, None, {}
+    if single and not args.no_trace:
+        # the step is one kernel launch: events around the decode call only
+        n_tr = 32
+        launch_us = traced_launch_us(lambda a_, b_: step((a_, b_)), n_tr)
+        ctx_tr = float(ctx1[0]) + (n_tr - 1) / 2.0
+        bytes_tr = algorithmic_bytes(cfg, ctx_tr)["total"]
+        achieved = bytes_tr / (launch_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": committed_traffic(args.workload, cfg, ctx_tr),
+                    "kernel": f"k_persist: the whole batch-1 {args.workload} step in one launch",
+                    "bytes_per_launch": round(bytes_tr), "avg_launch_us": round(launch_us, 2),
+                    "context_mean": ctx_tr}
+        kernel_us["k_persist"] = round(launch_us, 2)
+    elif t > 1 and not args.no_trace:
+        # per-layer launch time of the attention (matrix-core split + merge) and the gate/up GEMM
+        L = cfg["n_layers"]
+        for cls in ("attn", "gate_up"):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+            for e in evs:  # torch creates its events lazily, at the first record
+                e.record()
+            torch.cuda.synchronize()
+            arr = (ctypes.c_void_p * (2 * L))(*[ctypes.c_void_p(e.cuda_event) for e in evs])
+            bw.bw_set_trace(s.model, cls, arr, L)
+            tot, cnt = 0.0, 0
+            sl_tr = []
+            for _ in range(4):
+                sl_tr.append(seq_lens.cpu().numpy().astype(np.float64))
+                step()
+                torch.cuda.synchronize()
+                for l in range(L):
+                    tot += evs[2 * l].elapsed_time(evs[2 * l + 1])
+                    cnt += 1
+            bw.bw_set_trace(s.model, cls, None, 0)
+            kernel_us[cls] = round(1000.0 * tot / cnt, 2)
+        # attention: every sequence's cached positions plus its t new ones, once per layer
+        kv_layer = float(np.mean([(x + t).sum() for x in sl_tr])) * kv_pos_layer
+        achieved = kv_layer / (kernel_us["attn"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "kernel": "verify attention per layer: k_attn_split_mfma (16 query rows per KV head, matrix "
+                              "cores) + k_attn_merge", "bytes_per_launch": round(kv_layer),
+                    "avg_launch_us": kernel_us["attn"]}
+        d, F = cfg["d_model"], cfg["ffn_dim"]
+        gu_flop = 2.0 * B * t * 2 * F * d
+        tf = gu_flop / (kernel_us["gate_up"] * 1e-6) / 1e12
+        roofline_mfma = {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                         "frac": round(tf / 2500.0, 4), "traffic": None,
+                         "kernel": f"gate/up int4 GEMM per layer ({B * t} x {2 * F} x {d}, fp16 matrix cores, "
+                                   "k_gemm_w32 + epilogue); useful products only",
+                         "flop_per_launch": gu_flop, "avg_launch_us": kernel_us["gate_up"]}
+    if bw.bw_check_device_error(s.model) != 0:
+        print("[bench] device error flag set in the traced passes", file=sys.stderr)
+        return 1
     s.close()
     # algorithmic bytes per step: the weights once, each sequence's KV read at its mean context
     # over the timed steps (t positions attend, the later ones to the earlier: counted once),
@@ -339,7 +474,16 @@ def run_workload(args) -> int:
                    "context_sum_start": int(ctx0.sum()), "seed": seed},
         "achieved_hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_step": round(per_step), "committed_tokens_per_s": round(committed * 1000.0 / (ms_per_step * K), 1),
+        "kernel_us": kernel_us, "roofline": roofline,
     }
+    if roofline_mfma is not None:
+        out["roofline_mfma"] = roofline_mfma
+    if not args.no_cpu_baseline:
+        if t > 1:
+            out["cpu_baseline"] = cpu_baseline_verify(cfg, lens, t, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(cfg, lens[0], args.cpu_seconds)
+        print(f"[bench] cpu baseline: {out['cpu_baseline']}", file=sys.stderr, flush=True)
     print(json.dumps(out))
     return 0
 
@@ -406,7 +550,8 @@ def main() -> int:
 
     cfg = configs.DENSE_9B
     P, W, K = args.prompt, args.warmup, args.steps
-    total = P + W + K + 1
+    n_traced = 64 + 8  # launches of the traced pass and of the phase-stamp pass after the timed steps
+    total = P + W + K + n_traced + 1
     torch.cuda.set_device(0)
     t_load = time.perf_counter()
     s = Session(cfg, seed=cfg["seed"], max_len=[total], max_tokens=1, pool_seed=cfg["seed"] + 1)
@@ -419,10 +564,17 @@ def main() -> int:
     tok = torch.zeros(1, dtype=torch.int32, device=dev)
     sl = torch.zeros(1, dtype=torch.int32, device=dev)
     am = torch.zeros(1, dtype=torch.int32, device=dev)
+    am_sink = torch.zeros(1, dtype=torch.int32, device=dev)  # prefill: the argmax is not fed back
 
-    def step(feed_back: bool):
-        bw.bw_decode_step(s.model, s.pool, tok, sl, s.page_table, 1, 1, s.max_pages, None, tok if feed_back else am)
-        sl.add_(1)
+    def step(feed_back: bool, ev=None):
+        # the decode step, then the library's greedy bookkeeping (t = 1): seq_lens += 1 and, when
+        # feeding back, the argmax becomes the next input token; all on the device
+        if ev is not None:
+            ev[0].record()
+        bw.bw_decode_step(s.model, s.pool, tok, sl, s.page_table, 1, 1, s.max_pages, None, am)
+        if ev is not None:
+            ev[1].record()
+        bw.bw_spec_accept(s.model, tok if feed_back else am_sink, am, None, sl, None, None, 0, None, 1, 1)
 
     t_pf = time.perf_counter()
     if args.synth_context:
@@ -467,28 +619,12 @@ def main() -> int:
         # traced pass: each step is one kernel launch; HIP events on the step's stream around each
         # launch give the kernel's duration (the events sit outside the kernel, between launches)
         n_tr = 64
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_tr)]
-        torch.cuda.synchronize()
-        for a_, b_ in evs:
-            a_.record()
-            step(feed_back=True)
-            b_.record()
-        torch.cuda.synchronize()
-        launch_us = sum(a_.elapsed_time(b_) for a_, b_ in evs) * 1000.0 / n_tr
+        launch_us = traced_launch_us(lambda a_, b_: step(feed_back=True, ev=(a_, b_)), n_tr)
         ctx_tr = P + W + K + (n_tr - 1) / 2.0
         bytes_tr = algorithmic_bytes(cfg, ctx_tr)["total"]
         achieved = bytes_tr / (launch_us * 1e-6) / 1e9
-        traffic = None
-        tr_path = os.path.join(ROOT, "profiles", "step_dense9b_traffic.json")
-        if os.path.exists(tr_path):
-            with open(tr_path) as f:
-                tr = json.load(f)
-            from memory_bound_autoregressive_amd.build import source_digest
-            # counted bytes per launch, measured at (about) this pass's context with unchanged sources
-            lo, hi = tr.get("contexts", (0, -1))
-            if (lo - 64 <= ctx_tr <= hi + 64 and
-                    tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ())))):
-                traffic = round(tr["hbm_bytes_per_launch"])
+        # counted bytes per launch, measured at (about) this pass's context with unchanged sources
+        traffic = committed_traffic("dense-9b", cfg, ctx_tr)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                     "kernel": "k_persist: the whole batch-1 step in one launch (32 layers + lm_head + argmax)",
@@ -519,6 +655,9 @@ def main() -> int:
         phases = {k: {"wait_us": round(float(acc[:, i, 0].mean()), 2), "work_us": round(float(acc[:, i, 1].mean()), 2)}
                   for i, k in enumerate(names)}
         phases["lm_head"] = {"wait_us": round(float(lm[0]), 2), "work_us": round(float(lm[1]), 2)}
+        if bw.bw_check_device_error(s.model) != 0:
+            print("[bench] device error flag set in the traced passes", file=sys.stderr)
+            return 1
         print(f"[bench] k_persist {launch_us:.1f} us per launch, {achieved:.0f} GB/s algorithmic; phases {phases}",
               file=sys.stderr, flush=True)
     elif not args.no_trace:

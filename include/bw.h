@@ -98,6 +98,26 @@ int bw_model_load_synthetic(const bw_model_config* cfg, uint64_t seed, bw_model*
 /* Release a model and all device memory it owns. NULL is accepted. */
 int bw_model_free(bw_model* model);
 
+/* Copy one of the model's tensors to host memory in the canonical layout, so that a checker can
+ * compare the library's weights with its own copy of the generated ones ("Deep dive: bw24",
+ * section 4: one Engine owns the loaded weights that every session shares). Names:
+ *   "embed" fp16 [vocab][d_model], "final_norm" fp16 [d_model],
+ *   "lm_head.codes", "lm_head.scales",
+ *   "layers.L.attn_norm", "layers.L.ffn_norm" fp16 [d_model],
+ *   "layers.L.M.codes", "layers.L.M.scales" with M = qkv, o, gate, up, down (dense models),
+ *   "layers.L.router" fp16 [n_experts][d_model] and "layers.L.experts.E.M.codes|scales",
+ *   "layers.L.shared.S.M.codes|scales" with M = gate, up, down (MoE models).
+ * An int4 matrix [N][K] exports as codes u8 [N][K/2] (canonical row order; block b of a row is
+ * bytes 16b..16b+15, byte i holds element i in bits 0-3 and element i+16 in bits 4-7) and scales
+ * fp16 [N][K/32] (one per block, canonical order), whatever its device tiling; QKV rows are q
+ * heads, then k, then v. `bytes` must equal the tensor's size (bw_model_tensor_bytes).
+ * Synchronous (waits for the device). Errors: BW_EINVAL (null argument, unknown name),
+ * BW_ERANGE (wrong size), BW_EHIP. */
+int bw_model_export_tensor(const bw_model* model, const char* name, void* host_dst, size_t bytes);
+
+/* Size in bytes of a tensor bw_model_export_tensor writes. Errors: BW_EINVAL. */
+int bw_model_tensor_bytes(const bw_model* model, const char* name, size_t* bytes);
+
 /* Create a physical KV page pool of n_pages pages for `model`. One page holds page_tokens
  * positions of every layer; its device layout is
  *   pool[layer][page][kv_head][0 = K, 1 = V][slot 0..page_tokens-1][head_dim]
@@ -282,9 +302,10 @@ int bw_check_device_error(bw_model* model, void* stream, int32_t* flags_host);
 #define BW_MAT_SUP 7
 #define BW_MAT_SDOWN 8
 
-/* Dequantise one int4 matrix on the device with the step's in-register dequantisation and
- * write it as fp32 [N][K] in canonical row and column order (dst_dev must hold N*K floats).
- * Asynchronous. Errors: BW_EINVAL. */
+/* Dequantise one int4 matrix on the device with a plain kernel (w = s * (q - 8) per element)
+ * and write it as fp32 [N][K] in canonical row and column order (dst_dev must hold N*K floats).
+ * The step's own in-register unpacks (GEMV, batched GEMM) are checked bit for bit through
+ * bw_debug_matvec with one-hot inputs, whose products are exact. Asynchronous. Errors: BW_EINVAL. */
 int bw_debug_dequant(const bw_model* model, int32_t which, int32_t layer, int32_t expert,
                      float* dst_dev, void* stream);
 
@@ -314,6 +335,12 @@ int bw_debug_read_experts(bw_model* model, int32_t n_rows, int32_t* host_dst, vo
 /* Residual stream after the last layer of the last bw_decode_step: float [batch * t][d_model],
  * copied to host. Synchronises `stream`. */
 int bw_debug_read_hidden(bw_model* model, int32_t n_rows, float* host_dst, void* stream);
+
+/* Copy row src of the lm_head (codes and scale) onto row dst, for tests that need two vocabulary
+ * rows with bitwise equal logits (the greedy argmax must then take the lower index: "Deep dive:
+ * bw24", section 1, output equal to token-by-token argmax decoding). Changes the model's weights.
+ * Synchronous. Errors: BW_EINVAL (null model, row out of range), BW_EHIP. */
+int bw_debug_copy_lm_head_row(bw_model* model, int32_t src, int32_t dst);
 
 /* Timeout of each wait inside the single-launch step, in ticks of the GPU's 100 MHz real-time
  * counter (default 50,000,000 = 0.5 s). A wait that passes it raises BW_DERR_PERSIST and ends the

@@ -32,7 +32,8 @@ EXPORTS = (
     "bw_set_gemm_min_rows", "bw_set_single_launch", "bw_debug_single_launch_deadline",
     "bw_debug_single_launch_stamps", "bw_spec_accept", "bw_debug_kv_round",
     "bw_kv_tier_create", "bw_kv_tier_free", "bw_kv_tier_touch", "bw_kv_tier_evict_lru", "bw_kv_tier_restore",
-    "bw_kv_tier_wait", "bw_kv_tier_stats", "bw_kv_lru_select",
+    "bw_kv_tier_wait", "bw_kv_tier_stats", "bw_kv_lru_select", "bw_model_export_tensor", "bw_model_tensor_bytes",
+    "bw_debug_copy_lm_head_row",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -78,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.bw_kv_pool_fill.argtypes = [vp, ctypes.c_uint16, vp]
         L.bw_kv_pool_synthesize.argtypes = [vp, u64, vp, vp, vp, i32, i32]
         L.bw_kv_pool_read.argtypes = [vp, i32, i32, vp, sz]
+        L.bw_model_export_tensor.argtypes = [vp, ctypes.c_char_p, vp, sz]
+        L.bw_model_tensor_bytes.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(sz)]
+        L.bw_debug_copy_lm_head_row.argtypes = [vp, i32, i32]
         L.bw_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
         L.bw_check_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.bw_debug_dequant.argtypes = [vp, i32, i32, i32, vp, vp]
@@ -174,6 +178,21 @@ def bw_kv_pool_synthesize(pool: int, seed: int, seq_ids, seq_lens, page_table, b
     """Host int32 numpy arrays."""
     _check(lib().bw_kv_pool_synthesize(pool, seed, _ptr(seq_ids), _ptr(seq_lens), _ptr(page_table), batch, max_pages),
            "bw_kv_pool_synthesize")
+
+
+def bw_model_tensor_bytes(model: int, name: str) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().bw_model_tensor_bytes(model, name.encode(), ctypes.byref(n)), "bw_model_tensor_bytes")
+    return n.value
+
+
+def bw_model_export_tensor(model: int, name: str, out: np.ndarray) -> None:
+    """out: host numpy array of exactly the tensor's size (uint8 codes, uint16 fp16 bits)."""
+    _check(lib().bw_model_export_tensor(model, name.encode(), _ptr(out), out.nbytes), "bw_model_export_tensor")
+
+
+def bw_debug_copy_lm_head_row(model: int, src: int, dst: int) -> None:
+    _check(lib().bw_debug_copy_lm_head_row(model, src, dst), "bw_debug_copy_lm_head_row")
 
 
 def bw_kv_pool_read(pool: int, layer: int, page: int, out) -> None:

@@ -51,6 +51,9 @@ constexpr uint32_t kRsrc3 = 0x00020000u;
 constexpr int kCohSC1 = 16;        // cache policy: coherent across the XCD L2s
 constexpr float kNoScore = -1.0e30f;               // running max of a split without positions
 constexpr int kOOB = 0x7FFFFFF0;  // buffer offset past every buffer: the load returns zero, touches nothing
+// argmax index of a workgroup with no candidate (every logit NaN): the largest index the 30-bit
+// field of an argmax partial holds, so it survives the packing and loses every tie to a real row
+constexpr int kNoIdx = 0x3FFFFFFF;
 
 // ---- exchange words ---------------------------------------------------------------------------
 
@@ -1356,7 +1359,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     if (bail) return;
     stamp(p, L * 16 + 1);
     float best_v = -INFINITY;
-    int best_i = 0x7fffffff;
+    int best_i = kNoIdx;
     const Mat lm = p.lm;
     for (int c0 = v0; c0 < v1; c0 += kMaxRows) {
       const int c1 = min(v1, c0 + kMaxRows);
@@ -1404,7 +1407,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     (void)lane;
     (void)wave;
     float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    int bi = kNoIdx;
     for (int k = tid; k < nwg; k += kPT) {
       uint64_t word = __hip_atomic_load(p.xarg + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ctl.t0 = __builtin_amdgcn_s_memrealtime();
@@ -1438,7 +1441,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         if (ov > b2 || (ov == b2 && oi < i2)) { b2 = ov; i2 = oi; }
       }
       if (!bail) {
-        if (p.argmax) p.argmax[0] = i2 == 0x7fffffff ? 0 : i2;
+        if (p.argmax) p.argmax[0] = i2 == kNoIdx ? 0 : i2;  // every logit NaN: token 0, as the chain
         p.epoch[0] = epoch + 1;  // every workgroup has read it: all have reached the final phase
       }
       if (p.stamps != nullptr) p.stamps[L * 16 + 3] = __builtin_amdgcn_s_memrealtime();

@@ -1380,6 +1380,132 @@ static int find_mat(const bw_model* m, int which, int layer, int expert, Mat* w,
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// tensor export in the canonical layout
+// ---------------------------------------------------------------------------------------------
+
+// A named tensor of the model: an fp16 vector or matrix (plain), or one part of an int4 matrix.
+struct TensorRef {
+  const void* fp16 = nullptr;  // plain fp16 tensor
+  int64_t elems = 0;
+  Mat w;                       // int4 matrix (codes or scales part)
+  bool is_mat = false, scales = false;
+  const int32_t* map = nullptr;// device -> canonical row (device memory), or null
+  int half = -1;               // interleaved gate/up: 0 = gate rows, 1 = up rows
+  int n_canon = 0;             // canonical rows
+};
+
+static int parse_tensor(const bw_model* m, const char* name, TensorRef* t) {
+  const auto& c = m->c;
+  const std::string s(name);
+  auto part = [&](const std::string& rest, int which, int layer, int expert) -> int {
+    // rest: ".codes" or ".scales"
+    if (rest != ".codes" && rest != ".scales") return fail(BW_EINVAL, "tensor %s: expected .codes or .scales", name);
+    if (int rc = find_mat(m, which, layer, expert, &t->w, &t->map, &t->n_canon, &t->half)) return rc;
+    t->is_mat = true;
+    t->scales = rest == ".scales";
+    return BW_OK;
+  };
+  if (s == "embed") { t->fp16 = m->embed; t->elems = (int64_t)c.vocab * c.d_model; return BW_OK; }
+  if (s == "final_norm") { t->fp16 = m->final_norm; t->elems = c.d_model; return BW_OK; }
+  if (s.rfind("lm_head", 0) == 0) return part(s.substr(7), BW_MAT_LM_HEAD, 0, 0);
+  int l = -1, e = -1, n = 0;
+  char kind[32] = {0}, mat[16] = {0}, tail[16] = {0};
+  if (sscanf(name, "layers.%d.%31[a-z_]%n", &l, kind, &n) < 2 || l < 0 || l >= c.n_layers)
+    return fail(BW_EINVAL, "unknown tensor %s", name);
+  const std::string k(kind), rest = s.substr(n);
+  if (k == "attn_norm" && rest.empty()) { t->fp16 = m->L[l].attn_norm; t->elems = c.d_model; return BW_OK; }
+  if (k == "ffn_norm" && rest.empty()) { t->fp16 = m->L[l].ffn_norm; t->elems = c.d_model; return BW_OK; }
+  if (k == "router" && rest.empty() && is_moe(c)) {
+    t->fp16 = m->L[l].router;
+    t->elems = (int64_t)c.n_experts * c.d_model;
+    return BW_OK;
+  }
+  if (k == "experts" || k == "shared") {
+    if (!is_moe(c) || sscanf(rest.c_str(), ".%d.%15[a-z]%15s", &e, mat, tail) != 3)
+      return fail(BW_EINVAL, "unknown tensor %s", name);
+    const std::string mm(mat);
+    const bool sh = k == "shared";
+    const int which = mm == "gate" ? (sh ? BW_MAT_SGATE : BW_MAT_GATE)
+                    : mm == "up"   ? (sh ? BW_MAT_SUP : BW_MAT_UP)
+                    : mm == "down" ? (sh ? BW_MAT_SDOWN : BW_MAT_DOWN) : -1;
+    if (which < 0) return fail(BW_EINVAL, "unknown tensor %s", name);
+    return part(tail, which, l, e);
+  }
+  const int which = k == "qkv" ? BW_MAT_QKV : k == "o" ? BW_MAT_O : k == "gate" ? BW_MAT_GATE
+                  : k == "up" ? BW_MAT_UP : k == "down" ? BW_MAT_DOWN : -1;
+  if (which < 0 || (is_moe(c) && (which == BW_MAT_GATE || which == BW_MAT_UP || which == BW_MAT_DOWN)))
+    return fail(BW_EINVAL, "unknown tensor %s", name);
+  return part(rest, which, l, 0);
+}
+
+static size_t tensor_bytes(const TensorRef& t) {
+  if (!t.is_mat) return (size_t)t.elems * 2;
+  return t.scales ? (size_t)t.n_canon * (t.w.K / 32) * 2 : (size_t)t.n_canon * (t.w.K / 2);
+}
+
+extern "C" int bw_model_tensor_bytes(const bw_model* m, const char* name, size_t* bytes) {
+  if (!m || !name || !bytes) return fail(BW_EINVAL, "null argument");
+  TensorRef t;
+  if (int rc = parse_tensor(m, name, &t)) return rc;
+  *bytes = tensor_bytes(t);
+  return BW_OK;
+}
+
+extern "C" int bw_model_export_tensor(const bw_model* m, const char* name, void* host_dst, size_t bytes) {
+  if (!m || !name || !host_dst) return fail(BW_EINVAL, "null argument");
+  TensorRef t;
+  if (int rc = parse_tensor(m, name, &t)) return rc;
+  const size_t want = tensor_bytes(t);
+  if (bytes != want) return fail(BW_ERANGE, "tensor %s holds %zu bytes, not %zu", name, want, bytes);
+  HIP_OK(hipDeviceSynchronize());
+  if (!t.is_mat) {
+    HIP_OK(hipMemcpy(host_dst, t.fp16, want, hipMemcpyDeviceToHost));
+    return BW_OK;
+  }
+  const Mat& w = t.w;
+  const int64_t rb = w.K / 2, nblk = w.K / 32;
+  // device rows and their canonical rows (gate/up: the requested half of the interleave)
+  std::vector<int32_t> map;
+  if (t.map) {
+    map.resize(w.N);
+    HIP_OK(hipMemcpy(map.data(), t.map, sizeof(int32_t) * w.N, hipMemcpyDeviceToHost));
+  }
+  const int64_t lo = t.half < 0 ? 0 : (int64_t)t.half * t.n_canon;
+  auto canon_of = [&](int64_t r) -> int64_t {
+    const int64_t cr = t.map ? (int64_t)map[r] - lo : r;
+    return cr >= 0 && cr < t.n_canon ? cr : -1;
+  };
+  if (!t.scales) {
+    std::vector<uint8_t> dev((size_t)w.N * rb);
+    HIP_OK(hipMemcpy(dev.data(), w.codes, dev.size(), hipMemcpyDeviceToHost));
+    uint8_t* dst = (uint8_t*)host_dst;
+    for (int64_t r = 0; r < w.N; ++r)
+      if (const int64_t cr = canon_of(r); cr >= 0) memcpy(dst + cr * rb, dev.data() + r * rb, rb);
+  } else {
+    std::vector<uint16_t> dev((size_t)w.N * nblk);
+    HIP_OK(hipMemcpy(dev.data(), w.scales, dev.size() * 2, hipMemcpyDeviceToHost));
+    uint16_t* dst = (uint16_t*)host_dst;
+    // device scales are tiled per row as [lpr][nb]: block b sits at (b % lpr) * nb + b / lpr
+    for (int64_t r = 0; r < w.N; ++r)
+      if (const int64_t cr = canon_of(r); cr >= 0)
+        for (int64_t b = 0; b < nblk; ++b) dst[cr * nblk + b] = dev[r * nblk + (b % w.lpr) * w.nb + b / w.lpr];
+  }
+  return BW_OK;
+}
+
+extern "C" int bw_debug_copy_lm_head_row(bw_model* m, int32_t src, int32_t dst) {
+  if (!m) return fail(BW_EINVAL, "null model");
+  const Mat& w = m->lm;
+  if (src < 0 || src >= w.N || dst < 0 || dst >= w.N) return fail(BW_EINVAL, "row out of range");
+  const int64_t rb = w.K / 2, sb = (w.K / 32) * 2;
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy((uint8_t*)w.codes + dst * rb, w.codes + src * rb, rb, hipMemcpyDeviceToDevice));
+  HIP_OK(hipMemcpy((uint8_t*)w.scales + dst * sb, (const uint8_t*)w.scales + src * sb, sb, hipMemcpyDeviceToDevice));
+  HIP_OK(hipDeviceSynchronize());
+  return BW_OK;
+}
+
 extern "C" int bw_debug_dequant(const bw_model* m, int32_t which, int32_t layer, int32_t expert,
                                 float* dst, void* stream) {
   if (!m || !dst) return fail(BW_EINVAL, "null argument");

@@ -1,5 +1,9 @@
 """Summaries of rocprofv3 CSV output for the decode-step kernels.
 
+Every profile is taken with `--output-format csv` (for example `rocprofv3 --kernel-trace --stats
+--output-format csv -d DIR -o run -- python3 bench.py ...`): the profiler's default output format
+has ended a finished run with a segmentation fault in its own exit path.
+
   python -m memory_bound_autoregressive_amd.profiling stats    <kernel_stats.csv> <out.md> --command "..."
   python -m memory_bound_autoregressive_amd.profiling counters <counter_collection.csv> <out.md> --command "..."
   python -m memory_bound_autoregressive_amd.profiling traffic  --fetch F.csv --write W.csv \

@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.or_kv_create.argtypes = [vp, i32, i64]
         L.or_kv_free.argtypes = [vp]
         L.or_kv_set_synth.argtypes = [vp, i32, u64, ctypes.c_uint32, i64]
+        L.or_kv_set.restype = i32
+        L.or_kv_set.argtypes = [vp, i32, i32, i64, vp]
         L.or_kv_read.restype = dbl
         L.or_kv_read.argtypes = [vp, i32, i32, i64, i32, i32, i32]
         L.or_forward.restype = i32
@@ -327,6 +329,13 @@ class KV:
 
     def read(self, seq: int, layer: int, pos: int, which: int, g: int, d: int) -> float:
         return float(lib().or_kv_read(self.h, seq, layer, pos, which, g, d))
+
+    def set(self, seq: int, layer: int, pos: int, vals) -> None:
+        """Store given keys and values [2][G][D] of one position (values already in the cache dtype)."""
+        v = _f64(vals)
+        assert v.shape == (2, self.model.cfg["n_kv_heads"], self.model.cfg["head_dim"])
+        if lib().or_kv_set(self.h, seq, layer, pos, _p(v)) != 0:
+            raise IndexError((seq, layer, pos))
 
 
 def forward(model: Model, kv: KV, seq: int, tokens, pos0: int, *, want_logits=True,

@@ -589,6 +589,19 @@ static inline double* or_kv_slot(or_kv* kv, or_seq* sq, int l, int64_t pos, int 
   return &sq->app[((((int64_t)l * sq->cap + a) * 2 + which) * kv->G + g) * kv->D];
 }
 
+/* store given (already rounded) keys and values of one position: vals [2][G][D] (for tests that
+ * take a cached context from elsewhere; pos must lie in the appendable range) */
+int or_kv_set(or_kv* kv, int s, int l, int64_t pos, const double* vals) {
+  or_seq* sq = &kv->seqs[s];
+  if (pos < sq->ctx0 || pos >= sq->ctx0 + sq->cap || l < 0 || l >= kv->L) return -1;
+  for (int w = 0; w < 2; ++w)
+    for (int g = 0; g < kv->G; ++g) {
+      double* dst = or_kv_slot(kv, sq, l, pos, w, g);
+      for (int d = 0; d < kv->D; ++d) dst[d] = vals[((int64_t)w * kv->G + g) * kv->D + d];
+    }
+  return 0;
+}
+
 /* read one cached element (for tests) */
 double or_kv_read(const or_kv* kv, int s, int l, int64_t pos, int which, int g, int d) {
   return or_kv_get(kv, &kv->seqs[s], l, pos, which, g, d);

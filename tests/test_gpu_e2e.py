@@ -131,6 +131,49 @@ def test_prompt_then_greedy_decode(cfg, seed, gemm, single):
         p.close()
 
 
+DENSE_9B_2L = dict(configs.DENSE_9B, n_layers=2, vocab=4096, name="dense-9b-2l")
+
+
+@pytest.mark.parametrize("cfg,single", [(configs.TINY, 1), (configs.TINY, 0), (DENSE_9B_2L, 1), (DENSE_9B_2L, 0)],
+                         ids=["tiny-single", "tiny-chain", "9b-2l-single", "9b-2l-chain"])
+def test_argmax_takes_the_lowest_index_on_planted_ties(cfg, single):
+    """Greedy argmax with exact ties: an lm_head row copied onto another gives both vocabulary
+    rows bitwise equal logits, and the step must then return the lower index (single launch,
+    kernel chain and, with 8 rows, the batched GEMM path). Every row is also checked against a
+    brute-force argmax of the step's own logits (first index of the maximum)."""
+    seed, V = 1061, cfg["vocab"]
+    s = Session(cfg, seed=seed, max_len=[16], max_tokens=8, pool_seed=seed + 1)
+    try:
+        got = bw.bw_set_single_launch(s.model, single)
+        assert got or not single
+        tok = _cuda_i32([7])
+
+        def run():
+            lg, am = s.step(tok, _cuda_i32([0]))
+            return lg.cpu().numpy()[0], int(am.cpu()[0])
+
+        lg0, a0 = run()
+        assert a0 == int(np.argmax(lg0))
+        # the winning row copied onto a lower row in another workgroup's range (or, if the winner is
+        # row 0, onto a higher one): the tie must go to the lower index
+        b = a0 // 2 if a0 >= 64 else a0 + V // 2
+        bw.bw_debug_copy_lm_head_row(s.model, a0, b)
+        lg1, a1 = run()
+        assert lg1[a0].view(np.uint32) == lg1[b].view(np.uint32) and lg1[a0] == lg1.max()
+        assert a1 == min(a0, b), (a0, b, a1)
+        assert a1 == int(np.flatnonzero(lg1 == lg1.max())[0])
+        # eight rows at once (verify shape, matrix-core GEMM and row-wise argmax)
+        toks = [7, 7, 3, 100 % V, 7, 5, 9, 7]
+        lg8, am8 = s.step(_cuda_i32(toks), _cuda_i32([0]), t=8)
+        lg8, am8 = lg8.cpu().numpy(), am8.cpu().numpy()
+        for i in range(8):
+            assert int(am8[i]) == int(np.flatnonzero(lg8[i] == lg8[i].max())[0]), i
+        assert bw.bw_check_device_error(s.model) == 0
+        print(f"[result] planted tie ({'single launch' if got else 'chain'}) rows {a0} and {b}: argmax {a1}")
+    finally:
+        s.close()
+
+
 @pytest.mark.parametrize("gemm", [None, 1], ids=["gemv", "gemm"])
 def test_verify_step_equals_sequential_greedy(gemm):
     """Four tokens verified in one call (the accepted token plus three drafts equal to the greedy

@@ -4,11 +4,17 @@
 - moe-35b-a3b: 40 layers, 256 experts (top-8 + 1 shared), a synthesised 4096-token context,
   two decode steps; a router selection that differs from the oracle's only inside the 1e-4
   near-tie band is adopted by the oracle (any other difference fails).
-- verify-9b: 32 sequences with contexts drawn from U{1024..32768}, 4 tokens each (the accepted
-  token and three drafts), one verify step on the batched path (128 rows, matrix-core GEMMs,
-  16 query rows per KV head); every row's logits are finite and in range, and three sequences
-  (the shortest and longest contexts and one in between) are checked row by row against the
-  oracle, which decodes each of them on its own.
+- verify-9b: 32 sequences with contexts drawn from U{1024..32768} (one rounded down to a whole
+  number of pages), 4 tokens each (the accepted token and three drafts), one verify step on the
+  batched path (128 rows, matrix-core GEMMs, 16 query rows per KV head); every row's logits are
+  finite and in range, and eight sequences (the shortest and longest contexts, the page-aligned
+  one and five spread over the rest) are checked row by row against the oracle, which decodes
+  each of them on its own.
+- dense-9b at full depth (32 layers, full vocabulary) with a real prompt: an 80-token prompt
+  prefilled in chunks of 32, 32 and 16 rows, then eight greedy decode steps. The oracle takes the
+  GPU's cached keys and values of the first 64 prompt positions (read back from the pool; an fp64
+  prefill of the whole prompt at this size would take minutes), computes the last chunk's 16
+  positions itself and is compared on all 16 rows, then on every decode step.
 Tolerances as everywhere: logits within 2e-2 max-abs, greedy tokens equal wherever the oracle's
 top-2 margin exceeds 1e-2.
 """
@@ -55,6 +61,9 @@ def test_verify_9b_full_batch_sampled():
     seed, B, t = cfg["seed"], cfg["batch"], cfg["t"]
     rng = np.random.default_rng(seed)
     lens = [int(v) for v in rng.integers(cfg["ctx_lo"], cfg["ctx_hi"] + 1, B)]
+    # one context a whole number of pages: the new tokens then start a fresh page
+    aligned = int(np.argsort(lens)[B // 3])
+    lens[aligned] -= lens[aligned] % 16
     print(f"[case] verify-9b: {B} sequences x {t} tokens, contexts {min(lens)}..{max(lens)} "
           f"(sum {sum(lens)})", flush=True)
     s = Session(cfg, seed=seed, max_len=[n + t for n in lens], max_tokens=B * t, pool_seed=seed + 1)
@@ -72,7 +81,9 @@ def test_verify_9b_full_batch_sampled():
         assert np.all(np.isfinite(g)), "non-finite logits"
         assert np.all((gam >= 0) & (gam < cfg["vocab"]))
         order = np.argsort(lens)
-        sample = [int(order[0]), int(order[B // 2]), int(order[-1])]
+        spread = [int(order[k]) for k in np.linspace(0, B - 1, 7).round().astype(int)]
+        sample = list(dict.fromkeys([int(order[0]), int(order[-1]), aligned] + spread))[:8]
+        assert len(sample) == 8 and lens[aligned] % 16 == 0
         worst = 0.0
         for b in sample:
             okv.set_synth(b, seed + 7, b, lens[b])
@@ -81,6 +92,66 @@ def test_verify_9b_full_batch_sampled():
                                         f"seq {b} ctx {lens[b]}"))
             print(f"[case] verify-9b: sequence {b} (context {lens[b]}) checked", flush=True)
         print(f"[result] verify-9b full batch: sampled sequences {sample}, max |logit diff| = {worst:.3e}")
+    finally:
+        okv.close()
+        om.close()
+        s.close()
+
+
+def _gpu_kv(s, cfg, layer, positions):
+    """Keys and values the GPU cached for positions of sequence 0: {pos: [2][G][D] fp64}."""
+    G, D = cfg["n_kv_heads"], cfg["head_dim"]
+    fp8 = cfg.get("kv_dtype") == "fp8"
+    pages, out = {}, {}
+    for p in positions:
+        pg = int(s.page_table_host[0, p // 16])
+        if pg not in pages:
+            buf = np.empty(G * 2 * 16 * D, dtype=np.uint8 if fp8 else np.uint16)
+            bw.bw_kv_pool_read(s.pool, layer, pg, buf)
+            pages[pg] = buf.reshape(G, 2, 16, D)
+        raw = np.ascontiguousarray(pages[pg][:, :, p % 16, :].transpose(1, 0, 2))
+        if fp8:
+            vals = torch.from_numpy(raw).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        else:
+            vals = torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+        out[p] = vals
+    return out
+
+
+@pytest.mark.timeout(900)
+def test_dense_9b_real_prompt_full_depth():
+    cfg = configs.DENSE_9B
+    seed, P, chunk, adopt, steps = cfg["seed"], 80, 32, 64, 8
+    V, L = cfg["vocab"], cfg["n_layers"]
+    rng = np.random.default_rng(seed + 11)
+    prompt = [int(v) for v in rng.integers(0, V, P)]
+    print(f"[case] dense-9b full depth: {P}-token prompt in chunks of {chunk}, {steps} decode steps", flush=True)
+    s = Session(cfg, seed=seed, max_len=[P + steps + 1], max_tokens=chunk, pool_seed=seed + 3)
+    om = oracle.Model(oracle_cfg(cfg), seed)
+    okv = oracle.KV(om, 1, P + steps + 1)
+    try:
+        s.poison()
+        for c0 in range(0, adopt, chunk):  # chunks before the last: no logits, no lm_head
+            bw.bw_decode_step(s.model, s.pool, _cuda_i32(prompt[c0:c0 + chunk]), _cuda_i32([c0]), s.page_table, 1,
+                              chunk, s.max_pages, None, None)
+        g_last, am_last = s.step(_cuda_i32(prompt[adopt:]), _cuda_i32([adopt]), t=P - adopt)
+        torch.cuda.synchronize()
+        assert bw.bw_check_device_error(s.model) == 0
+        for l in range(L):
+            for p, v in _gpu_kv(s, cfg, l, range(adopt)).items():
+                okv.set(0, l, p, v)
+        print("[case] dense-9b full depth: prompt prefilled, cached context handed to the oracle", flush=True)
+        r = oracle.forward(om, okv, 0, prompt[adopt:], adopt)
+        worst = _compare(g_last.cpu().numpy().astype(np.float64), am_last.cpu().numpy(), r["logits"],
+                         "last prompt chunk")
+        print(f"[case] dense-9b full depth: last chunk ({P - adopt} rows) max |logit diff| {worst:.3e}", flush=True)
+        nxt = int(np.argmax(r["logits"][-1]))
+        for i in range(steps):
+            g, gam = s.step(_cuda_i32([nxt]), _cuda_i32([P + i]))
+            o = oracle.forward(om, okv, 0, [nxt], P + i)["logits"]
+            worst = max(worst, _compare(g.cpu().numpy().astype(np.float64), gam.cpu().numpy(), o, f"decode {i}"))
+            nxt = int(np.argmax(o[0]))  # teacher forcing on the oracle's token
+        print(f"[result] dense-9b full depth, real prompt: max |logit diff| = {worst:.3e}")
     finally:
         okv.close()
         om.close()

@@ -71,6 +71,118 @@ def test_dequant_bit_exact(cfg, seed):
         bw.bw_model_free(m)
 
 
+def _one_hot_columns(K: int, n: int, rng) -> np.ndarray:
+    """n column indices of a K-wide matrix: the first and last column, then pairs in sampled
+    blocks, one on a low nibble (element i of the block) and one on a high nibble (element
+    16 + i), so both unpack forms of every sampled block are exercised."""
+    nblk = K // 32
+    cols = [0, K - 1]
+    blocks = rng.choice(nblk, size=min(nblk, max(1, (n - 2) // 2)), replace=False)
+    for b in blocks:
+        cols += [32 * b + int(rng.integers(16)), 32 * b + 16 + int(rng.integers(16))]
+    return np.array(cols[:n], dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg,seed", [(TINY, 14), (LAYER9B, 15), (MOE_SMALL, 16)], ids=["tiny", "9b-layer", "moe"])
+def test_hot_path_dequant_bit_exact(cfg, seed):
+    """Dequantisation inside the step's own products, bit for bit. With x = e_k every product but
+    one is zero and the one is s (q - 8) * 1, so y[n] = W[n][k] holds exactly in fp32 (fp16 s
+    times a 4-bit integer) whatever the summation order. Run through the batch-1 GEMV (one
+    column per call), the matrix-core GEMM at 37 rows (16x16 tiles) and at 128 rows (the wide
+    32x32 form), and compared bitwise with the oracle's dequantised columns."""
+    m = _model(cfg, seed, max_tokens=128)
+    bw.bw_set_gemm_min_rows(m, 2)
+    om = oracle.Model(oracle_cfg(cfg), seed)
+    rng = np.random.default_rng(seed)
+    try:
+        for name in _matrices(cfg):
+            routed = cfg.get("n_experts", 0) and name in ("gate", "up", "down")
+            expert = 5 if routed else 0
+            codes, scales = _canonical(om, name, expert)
+            N, K = codes.shape[0], codes.shape[1] * 2
+            W = oracle.dequant(codes, scales).astype(np.float32)
+            # rows: 1 (GEMV), 37 (16x16 GEMM), 128 (wide GEMM); routed experts take the GEMV only
+            for M in ((1,) if routed else (1, 37, 128)):
+                ncol = 8 if M == 1 else M
+                cols = _one_hot_columns(K, ncol, rng)
+                print(f"[case] one-hot dequant {name} expert={expert} [{N}x{K}] rows={M}", flush=True)
+                if M == 1:
+                    got = np.empty((len(cols), N), dtype=np.float32)
+                    for i, k in enumerate(cols):
+                        x = torch.zeros((1, K), dtype=torch.float32, device="cuda")
+                        x[0, int(k)] = 1.0
+                        y = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda")
+                        bw.bw_debug_matvec(m, name, 0, expert, x, y)
+                        torch.cuda.synchronize()
+                        got[i] = y.cpu().numpy()[0]
+                else:
+                    x = torch.zeros((len(cols), K), dtype=torch.float32, device="cuda")
+                    x[torch.arange(len(cols)), torch.from_numpy(cols).cuda()] = 1.0
+                    y = torch.full((len(cols), N), float("nan"), dtype=torch.float32, device="cuda")
+                    bw.bw_debug_matvec(m, name, 0, expert, x, y)
+                    torch.cuda.synchronize()
+                    got = y.cpu().numpy()
+                ref = np.ascontiguousarray(W[:, cols].T)
+                bad = np.argwhere(got.view(np.uint32) != ref.view(np.uint32))
+                assert bad.size == 0, (name, M, bad[:4].tolist(), got[tuple(bad[0])], ref[tuple(bad[0])])
+    finally:
+        bw.bw_model_free(m)
+
+
+LAYER9B_3L = dict(configs.DENSE_9B, n_layers=3, vocab=4096)
+
+
+@pytest.mark.parametrize("cfg,seed", [(LAYER9B_3L, 41), (MOE_SMALL, 42)], ids=["9b-3l", "moe"])
+def test_export_tensor_matches_generator(cfg, seed):
+    """The library's weights, exported in the canonical layout, equal the generator's tensors byte
+    for byte: the last layer's matrices and norms, the lm_head, sampled embedding rows and, for
+    MoE, the router, the last routed expert and the shared expert."""
+    m = _model(cfg, seed)
+    try:
+        L, d, V = cfg["n_layers"], cfg["d_model"], cfg["vocab"]
+        H, G, D = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+        l = L - 1
+
+        def export(name, dtype):
+            n = bw.bw_model_tensor_bytes(m, name)
+            out = np.empty(n // np.dtype(dtype).itemsize, dtype=dtype)
+            bw.bw_model_export_tensor(m, name, out)
+            return out
+
+        print(f"[case] export {cfg.get('name', 'custom')} layer {l}", flush=True)
+        assert np.array_equal(export("final_norm", np.uint16), synth.norm_gain(seed, synth.FINAL_NORM, 0, d))
+        assert np.array_equal(export(f"layers.{l}.attn_norm", np.uint16), synth.norm_gain(seed, synth.ATTN_NORM, l, d))
+        assert np.array_equal(export(f"layers.{l}.ffn_norm", np.uint16), synth.norm_gain(seed, synth.FFN_NORM, l, d))
+        emb = export("embed", np.uint16).reshape(V, d)
+        for r0 in (0, V // 2, V - 3):
+            assert np.array_equal(emb[r0:r0 + 3], synth.embed_rows(seed, d, r0, 3))
+        mats = [("lm_head", synth.LM_HEAD, 0, 0, V, d), (f"layers.{l}.qkv", synth.QKV, l, 0, (H + 2 * G) * D, d),
+                (f"layers.{l}.o", synth.O, l, 0, d, H * D)]
+        if cfg.get("n_experts", 0):
+            E, Fe, Fs = cfg["n_experts"], cfg["expert_ffn"], cfg["shared_ffn"]
+            assert np.array_equal(export(f"layers.{l}.router", np.uint16).reshape(E, d), synth.router(seed, l, E, d))
+            mats += [(f"layers.{l}.experts.{E - 1}.gate", synth.GATE, l, E, Fe, d),
+                     (f"layers.{l}.experts.{E - 1}.up", synth.UP, l, E, Fe, d),
+                     (f"layers.{l}.experts.{E - 1}.down", synth.DOWN, l, E, d, Fe),
+                     (f"layers.{l}.shared.0.gate", synth.GATE, l, synth.SHARED_EXPERT, Fs, d),
+                     (f"layers.{l}.shared.0.up", synth.UP, l, synth.SHARED_EXPERT, Fs, d),
+                     (f"layers.{l}.shared.0.down", synth.DOWN, l, synth.SHARED_EXPERT, d, Fs)]
+        else:
+            F = cfg["ffn_dim"]
+            mats += [(f"layers.{l}.gate", synth.GATE, l, 0, F, d), (f"layers.{l}.up", synth.UP, l, 0, F, d),
+                     (f"layers.{l}.down", synth.DOWN, l, 0, d, F)]
+        for name, kind, layer, ex, N, K in mats:
+            codes, scales = synth.int4_matrix(seed, kind, layer, ex, N, K)
+            assert np.array_equal(export(name + ".codes", np.uint8).reshape(N, K // 2), codes), name
+            assert np.array_equal(export(name + ".scales", np.uint16).reshape(N, K // 32), scales), name
+        with pytest.raises(bw.BWError):
+            bw.bw_model_export_tensor(m, "final_norm", np.empty(d + 1, dtype=np.uint16))  # wrong size
+        with pytest.raises(bw.BWError):
+            bw.bw_model_tensor_bytes(m, f"layers.{L}.o.codes")  # no such layer
+    finally:
+        bw.bw_model_free(m)
+
+
 @pytest.mark.parametrize("cfg,seed", [(TINY, 21), (LAYER9B, 22), (LAYER27B, 24), (MOE_SMALL, 23)],
                          ids=["tiny", "9b-layer", "27b-layer", "moe"])
 def test_gemv_matches_oracle(cfg, seed):

@@ -48,17 +48,30 @@ def _oracle_greedy(cfg, seed, prompts, n_new):
     return out
 
 
-@pytest.mark.parametrize("gemm", [None, 1000], ids=["gemm", "gemv"])
-def test_speculative_loop_commits_the_greedy_stream(gemm):
-    cfg, seed = configs.TINY, 1051
-    B, t, P, N = 3, 4, 12, 40
+# the verify workload's layer shape (9B dimensions) at two layers and a small vocabulary
+VERIFY_2L = dict(configs.VERIFY_9B, n_layers=2, vocab=4096, name="verify-9b-2l")
+
+
+@pytest.mark.parametrize("cfg,B,N,gemm", [(configs.TINY, 3, 40, None), (configs.TINY, 3, 40, 1000),
+                                          (VERIFY_2L, 32, 12, None)],
+                         ids=["gemm", "gemv", "verify-9b-2l-batch32"])
+def test_speculative_loop_commits_the_greedy_stream(cfg, B, N, gemm):
+    """B sequences; the first three follow the draft policies above and are checked against the
+    oracle's greedy stream. At the verify shape the other 29 sequences draft random tokens: their
+    bookkeeping is checked every step, and the batch has 32 x 4 = 128 rows, so each step runs the
+    wide matrix-core GEMM form and 16 query rows per KV head, as the verify workload does."""
+    seed = 1051
+    t, P = 4, 12
     V = cfg["vocab"]
+    NC = 3  # sequences checked against the oracle
     rng = np.random.default_rng(seed)
     prompts = [rng.integers(0, V, P) for _ in range(B)]
     L_max = 2 * N + 2 * t  # the most tokens any sequence commits (sequence 0 after N: one per step)
-    ref = _oracle_greedy(cfg, seed, prompts, L_max + t)
+    ref = _oracle_greedy(cfg, seed, prompts[:NC], L_max + t)
     cap = 64
-    s = Session(cfg, seed=seed, max_len=[P + L_max + 2 * t] * B, max_tokens=B * t, pool_seed=seed + 1)
+    # room for every step's t tokens over the most steps the loop may take
+    s = Session(cfg, seed=seed, max_len=[P + max(L_max, (N + 2) * t) + 2 * t] * B, max_tokens=B * t,
+                pool_seed=seed + 1)
     try:
         if gemm is not None:
             bw.bw_set_gemm_min_rows(s.model, gemm)  # above B * t: the verify rows take the GEMV path
@@ -80,10 +93,14 @@ def test_speculative_loop_commits_the_greedy_stream(gemm):
         n_hist = [[] for _ in range(B)]
         keep_hist = [[] for _ in range(B)]
         steps = 0
-        while min(len(c) for c in committed) < N:
+        while min(len(c) for c in committed[:NC]) < N:
             # drafts from the reference continuation of what each sequence has committed
             tk_host = tokens.cpu().numpy()
             for b in range(B):
+                if b >= NC:  # unchecked sequences of the batch: random drafts
+                    tk_host[b * t + 1:(b + 1) * t] = rng.integers(0, V, t - 1)
+                    keep_hist[b].append(0)
+                    continue
                 c = len(committed[b])
                 truth = ref[b][0][c:c + t - 1]
                 keep = {0: t - 1, 1: 0, 2: int(rng.integers(0, t))}[b] if c < N else 0
@@ -119,9 +136,9 @@ def test_speculative_loop_commits_the_greedy_stream(gemm):
                 n_hist[b].append(n)
             steps += 1
             assert steps <= N + 2
-            assert max(len(c) for c in committed) <= L_max
+            assert max(len(c) for c in committed[:NC]) <= L_max
         worst_stop = {}
-        for b in range(B):
+        for b in range(NC):
             toks, margins = ref[b]
             for k in range(N):
                 if committed[b][k] != toks[k]:
@@ -129,7 +146,7 @@ def test_speculative_loop_commits_the_greedy_stream(gemm):
                     worst_stop[b] = k
                     break
         # with the streams in agreement, the draft policies give their acceptance counts
-        for b in range(B):
+        for b in range(NC):
             if b not in worst_stop:
                 if b == 0:
                     assert all(n == t - 1 for n in n_hist[0][:N // t - 1])
@@ -140,7 +157,8 @@ def test_speculative_loop_commits_the_greedy_stream(gemm):
                     for k, (n, kp) in enumerate(zip(n_hist[2], keep_hist[2])):
                         if lens[k] + t <= N:
                             assert n == kp, (k, n, kp)
-        print(f"[result] speculative loop: {steps} verify steps, committed {[len(c) for c in committed]}, "
-              f"accepted per step {[round(float(np.mean(h)), 2) for h in n_hist]}, near-tie stops {worst_stop}")
+        print(f"[result] speculative loop {cfg['name']} batch {B}: {steps} verify steps, committed "
+              f"{[len(c) for c in committed[:NC]]}, accepted per step {[round(float(np.mean(h)), 2) for h in n_hist[:NC]]}, "
+              f"near-tie stops {worst_stop}")
     finally:
         s.close()

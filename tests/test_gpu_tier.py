@@ -1,14 +1,23 @@
 """The host tier of the KV pool on the GPU (bw24 deep-dive page, section 6 item 3: cold pages go
 to locked host memory, least recently used first, and come back before a read). Pages evicted to
-pinned host memory and restored to other device pages give back every byte, and a decode step
-over the restored pages equals, bit for bit, one over pages that never moved."""
+pinned host memory and restored to other device pages give back every byte (the synthesised
+context equals the generator's keys and values, the rest equals a pool that never moved), and a
+decode step over the restored pages equals, bit for bit, one over pages that never moved, and
+the oracle's step over the same context within the logits tolerance."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
+import synth
 import memory_bound_autoregressive_amd as bw
 from memory_bound_autoregressive_amd import configs
 from memory_bound_autoregressive_amd.session import Session, pages_needed
+
+from helpers import oracle_cfg
+from test_gpu_e2e import _compare
+
+KV_CODE = {"f16": synth.KV_F16, "bf16": synth.KV_BF16, "fp8": synth.KV_FP8}
 
 pytestmark = pytest.mark.gpu
 
@@ -72,9 +81,18 @@ def test_evict_restore_round_trip_and_decode(cfg):
         s.page_table = torch.from_numpy(table).cuda()
         torch.cuda.synchronize()
         assert bw.bw_kv_tier_stats(tier) == (len(pages), 0)
+        G, D = cfg["n_kv_heads"], cfg["head_dim"]
+        dt = np.uint8 if cfg.get("kv_dtype") == "fp8" else np.uint16
         for l in range(cfg["n_layers"]):
             for o, n in remap.items():
                 assert np.array_equal(_read_page(s, l, n), _read_page(ref, l, o)), (l, o, n)
+            # the synthesised context, restored, is the generator's: [tok][kv][g][d] -> page [g][kv][slot][d]
+            for b in range(B):
+                want = synth.kv_fill(seed + 7, l, b, 0, lens[b], G, D, KV_CODE[cfg.get("kv_dtype", "bf16")])
+                for j in range(pages_needed(lens[b])):
+                    page = _read_page(s, l, int(table[b, j])).view(dt).reshape(G, 2, 16, D)
+                    n = min(16, lens[b] - 16 * j)
+                    assert np.array_equal(page[:, :, :n, :], want[16 * j:16 * j + n].transpose(2, 1, 0, 3)), (l, b, j)
         sl = torch.from_numpy(np.array(n_tok, dtype=np.int32)).cuda()
         lr, ar = ref.step(torch.from_numpy(toks[steps]).cuda(), sl)
         ls, as_ = s.step(torch.from_numpy(toks[steps]).cuda(), sl.clone())
@@ -82,6 +100,19 @@ def test_evict_restore_round_trip_and_decode(cfg):
         assert torch.equal(lr.view(torch.int32), ls.view(torch.int32))
         assert torch.equal(ar, as_)
         assert bw.bw_check_device_error(s.model) == 0
+        # the same three steps in the oracle, over the same synthesised context
+        om = oracle.Model(oracle_cfg(cfg), seed)
+        okv = oracle.KV(om, B, steps + 2)
+        try:
+            g, gam = ls.cpu().numpy().astype(np.float64), as_.cpu().numpy()
+            for b in range(B):
+                okv.set_synth(b, seed + 7, b, lens[b])
+                for k in range(steps + 1):
+                    o = oracle.forward(om, okv, b, [int(toks[k][b])], lens[b] + k)["logits"]
+                _compare(g[b:b + 1], gam[b:b + 1], o, f"after restore, sequence {b}")
+        finally:
+            okv.close()
+            om.close()
     finally:
         if tier:
             bw.bw_kv_tier_free(tier)
