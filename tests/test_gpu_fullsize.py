@@ -81,9 +81,9 @@ def test_verify_9b_full_batch_sampled():
         assert np.all(np.isfinite(g)), "non-finite logits"
         assert np.all((gam >= 0) & (gam < cfg["vocab"]))
         order = np.argsort(lens)
-        spread = [int(order[k]) for k in np.linspace(0, B - 1, 7).round().astype(int)]
-        sample = list(dict.fromkeys([int(order[0]), int(order[-1]), aligned] + spread))[:8]
-        assert len(sample) == 8 and lens[aligned] % 16 == 0
+        spread = [int(order[k]) for k in np.linspace(0, B - 1, 16).round().astype(int)]
+        sample = list(dict.fromkeys([int(order[0]), int(order[-1]), aligned] + spread[1::2]))[:8]
+        assert len(sample) == 8 and lens[aligned] % 16 == 0 and len(set(sample)) == 8
         worst = 0.0
         for b in sample:
             okv.set_synth(b, seed + 7, b, lens[b])
