@@ -322,6 +322,21 @@ int bw_debug_attention(bw_model* model, bw_kv_pool* pool, int32_t layer, const f
                        const int32_t* seq_lens_dev, const int32_t* page_table_dev,
                        int32_t batch, int32_t t, int32_t max_pages, float* out_dev, void* stream);
 
+/* bw_debug_attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels, with the
+ * split-K partials [batch * t][n_q_heads][splits][head_dim + 2] (splits = ceil(max_pages / 4))
+ * in a static device array of the library, 16 MiB per GPU, held until the process ends, instead
+ * of the model's workspace. Calls no hipMalloc, hipFree or other allocating routine; the array's
+ * device address is looked up once per device (hipGetSymbolAddress) on the first call there.
+ * Every call on one GPU shares the array, so calls that overlap on one GPU (other streams or
+ * threads) race; a call's partials are all written before they are read, so nothing needs
+ * clearing between calls. Asynchronous on stream. Errors: BW_EINVAL (null or non-positive
+ * argument), BW_ESTATE (pool of another model), BW_ERANGE (the partials would exceed 16 MiB, or
+ * batch or t above 65535), BW_EHIP. */
+int bw_attention_noalloc(bw_model* model, bw_kv_pool* pool, int32_t layer, const float* q_dev,
+                         const int32_t* seq_lens_dev, const int32_t* page_table_dev, int32_t batch,
+                         int32_t t, int32_t max_pages, float* out_dev, void* stream);
+
 /* Round n fp32 values x_dev to the cache dtype kv_dtype with the conversion every kernel uses to
  * store a key or value: bits_dev[i] (uint16; an FP8 code in the low byte) and back_dev[i], the
  * stored value read back as fp32 the way the attention reads it. Asynchronous. Errors: BW_EINVAL. */

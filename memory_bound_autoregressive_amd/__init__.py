@@ -33,7 +33,7 @@ EXPORTS = (
     "bw_debug_single_launch_stamps", "bw_spec_accept", "bw_debug_kv_round",
     "bw_kv_tier_create", "bw_kv_tier_free", "bw_kv_tier_touch", "bw_kv_tier_evict_lru", "bw_kv_tier_restore",
     "bw_kv_tier_wait", "bw_kv_tier_stats", "bw_kv_lru_select", "bw_model_export_tensor", "bw_model_tensor_bytes",
-    "bw_debug_copy_lm_head_row",
+    "bw_debug_copy_lm_head_row", "bw_attention_noalloc",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.bw_model_export_tensor.argtypes = [vp, ctypes.c_char_p, vp, sz]
         L.bw_model_tensor_bytes.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(sz)]
         L.bw_debug_copy_lm_head_row.argtypes = [vp, i32, i32]
+        L.bw_attention_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
         L.bw_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
         L.bw_check_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.bw_debug_dequant.argtypes = [vp, i32, i32, i32, vp, vp]
@@ -235,6 +236,14 @@ def bw_debug_attention(model: int, pool: int, layer: int, q, seq_lens, page_tabl
                        max_pages: int, out, stream=None) -> None:
     _check(lib().bw_debug_attention(model, pool, layer, _ptr(q), _ptr(seq_lens), _ptr(page_table), batch, t,
                                     max_pages, _ptr(out), _stream(stream)), "bw_debug_attention")
+
+
+def bw_attention_noalloc(model: int, pool: int, layer: int, q, seq_lens, page_table, batch: int, t: int,
+                         max_pages: int, out, stream=None) -> None:
+    """bw_debug_attention with its split partials in the library's static device scratch (allocates
+    nothing; calls on one GPU must not overlap). See include/bw.h."""
+    _check(lib().bw_attention_noalloc(model, pool, layer, _ptr(q), _ptr(seq_lens), _ptr(page_table), batch, t,
+                                      max_pages, _ptr(out), _stream(stream)), "bw_attention_noalloc")
 
 
 def bw_debug_kv_round(kv_dtype: int, x, bits, back, stream=None) -> None:

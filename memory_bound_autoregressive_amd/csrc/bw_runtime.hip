@@ -18,6 +18,7 @@
 #include <cstring>
 #include <functional>
 #include <map>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -1550,6 +1551,58 @@ extern "C" int bw_debug_attention(bw_model* m, bw_kv_pool* pool, int32_t layer, 
   if (layer < 0 || layer >= m->c.n_layers) return fail(BW_EINVAL, "layer out of range");
   if (batch < 1 || t < 1 || batch * t > m->c.max_tokens) return fail(BW_ERANGE, "batch * t out of range");
   AttnParams a = attn_params(m, pool, layer, q, seq_lens, page_table, t, max_pages, out);
+  if (launch_attention(a, m->c.kv_dtype, batch, (hipStream_t)stream)) return fail(BW_EHIP, "attention launch failed");
+  return BW_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// attention that allocates nothing: split partials in a static device array
+// ---------------------------------------------------------------------------------------------
+
+// The split-K partials [rows][heads][splits][head_dim + 2] of bw_attention_noalloc live here, one
+// copy per GPU for the life of the process. In host code the name is only a stand-in: the device
+// address comes from hipGetSymbolAddress, once per device (noalloc_scratch below).
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64] = {};  // per device id
+
+static int noalloc_scratch(void** out) {
+  int dev = 0;
+  HIP_OK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(BW_EINVAL, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail(BW_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BW_OK;
+}
+
+extern "C" int bw_attention_noalloc(bw_model* m, bw_kv_pool* pool, int32_t layer, const float* q,
+                                    const int32_t* seq_lens, const int32_t* page_table, int32_t batch,
+                                    int32_t t, int32_t max_pages, float* out, void* stream) {
+  if (!m || !pool || !q || !seq_lens || !page_table || !out) return fail(BW_EINVAL, "null argument");
+  if (pool->m != m) return fail(BW_ESTATE, "pool belongs to another model");
+  if (layer < 0 || layer >= m->c.n_layers) return fail(BW_EINVAL, "layer out of range");
+  if (batch < 1 || t < 1 || max_pages < 1) return fail(BW_EINVAL, "batch, t and max_pages must be positive");
+  if (batch > 65535 || t > 65535) return fail(BW_ERANGE, "batch and t are at most 65535");
+  AttnParams a = attn_params(m, pool, layer, q, seq_lens, page_table, t, max_pages, out);
+  // splits of this call: enough for max_pages at the vector-unit kernel's split length (the
+  // matrix-core kernel takes longer splits, so fewer)
+  a.max_splits = (max_pages + a.pages_per_split - 1) / a.pages_per_split;
+  const double need = (double)batch * t * a.H * a.max_splits * (a.D + 2) * sizeof(float);
+  if (need > (double)kNoallocScratchBytes)
+    return fail(BW_ERANGE, "attention partials need %.0f bytes, more than the %zu-byte static scratch", need,
+                kNoallocScratchBytes);
+  void* ptr = nullptr;
+  if (int rc = noalloc_scratch(&ptr)) return rc;
+  a.part = (float*)ptr;
+  a.counters = nullptr;  // the attention kernels keep no arrival counters
   if (launch_attention(a, m->c.kv_dtype, batch, (hipStream_t)stream)) return fail(BW_EHIP, "attention launch failed");
   return BW_OK;
 }
