@@ -71,6 +71,12 @@ def lib() -> ctypes.CDLL:
         L.or_quantize.argtypes = [vp, vp, i64, i64, vp]
         L.or_gemv.argtypes = [vp, vp, i64, i64, vp, vp]
         L.or_gemv_f16.argtypes = [vp, i64, i64, vp, vp]
+        L.or_e2m1_to_f64.restype = dbl
+        L.or_e2m1_to_f64.argtypes = [i32]
+        L.or_e8m0_to_f64.restype = dbl
+        L.or_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+        L.or_mx_dequant.argtypes = [vp, vp, i64, i64, vp]
+        L.or_mx_matmul.argtypes = [vp, vp, i64, i64, vp, i64, vp]
         L.or_rmsnorm.argtypes = [vp, vp, i64, dbl, vp]
         L.or_rope.argtypes = [vp, i32, i64, dbl]
         L.or_silu.restype = dbl
@@ -173,6 +179,37 @@ def gemv_f16(W: np.ndarray, x) -> np.ndarray:
     y = np.empty(N, dtype=np.float64)
     lib().or_gemv_f16(_p(np.ascontiguousarray(W, dtype=np.uint16)), N, K, _p(x), _p(y))
     return y
+
+
+def e2m1_to_f64(code: int) -> float:
+    """OCP MX E2M1 code (4 bits) -> value"""
+    return float(lib().or_e2m1_to_f64(int(code)))
+
+
+def e8m0_to_f64(bits: int) -> float:
+    """OCP MX E8M0 scale byte -> 2^(bits - 127) (NaN for 255)"""
+    return float(lib().or_e8m0_to_f64(int(bits)))
+
+
+def mx_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 matrix (codes uint8 [N][K/2], E8M0 scales uint8 [N][K/32]) -> fp64 [N][K]"""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    W = np.empty((N, K), dtype=np.float64)
+    lib().or_mx_dequant(_p(np.ascontiguousarray(codes)), _p(np.ascontiguousarray(scales, dtype=np.uint8)), N, K,
+                        _p(W))
+    return W
+
+
+def mx_matmul(codes: np.ndarray, scales: np.ndarray, X) -> np.ndarray:
+    """Y = X W^T for X [M][K] (or a vector [K]) against an MXFP4 matrix W [N][K], in fp64"""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    X = _f64(X)
+    vec = X.ndim == 1
+    X2 = X.reshape(-1, K)
+    Y = np.empty((X2.shape[0], N), dtype=np.float64)
+    lib().or_mx_matmul(_p(np.ascontiguousarray(codes)), _p(np.ascontiguousarray(scales, dtype=np.uint8)), N, K,
+                       _p(np.ascontiguousarray(X2)), X2.shape[0], _p(Y))
+    return Y[0] if vec else Y
 
 
 def rmsnorm(x, gamma_bits: np.ndarray, eps: float) -> np.ndarray:

@@ -225,6 +225,59 @@ void or_gemv_f16(const uint16_t* W, int64_t N, int64_t K, const double* x, doubl
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* MXFP4 blocks: 32 E2M1 elements sharing one E8M0 scale                                       */
+/* ------------------------------------------------------------------------------------------ */
+
+/* The pages' engine keeps weights in a native 4-bit floating-point format beside FP16/BF16
+ * ("Deep dive: bw24 ...", section 1, quantisation formats; the performance-strategy row of the
+ * section 7 table). That format is NVIDIA's; the 4-bit float that CDNA4's matrix cores take is
+ * the OCP Microscaling (MX) MXFP4 format, which is what this section defines: blocks of 32 E2M1
+ * elements along K with one E8M0 scale each, w = scale * element.
+ *
+ * Canonical layout of an MXFP4 matrix [N][K] (K a multiple of 32):
+ *   codes : N * K/2 bytes; row n occupies K/2 bytes; byte i of a row holds element 2i in bits
+ *           0-3 and element 2i+1 in bits 4-7.
+ *   scales: N * K/32 bytes, one E8M0 byte per block, row-major. */
+
+/* E2M1: bit 3 sign, bits 2-1 exponent (bias 1), bit 0 fraction; exponent 0 is subnormal
+ * (f * 0.5). No infinity or NaN: the eight magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double or_e2m1_to_f64(int c) {
+  int sign = (c >> 3) & 1;
+  int e = (c >> 1) & 3;
+  int f = c & 1;
+  double v = e == 0 ? 0.5 * (double)f : ldexp(1.0 + 0.5 * (double)f, e - 1);
+  return sign ? -v : v;
+}
+
+/* E8M0: an unsigned exponent, 2^(e - 127); the byte 255 is NaN. */
+double or_e8m0_to_f64(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* element k of row n */
+double or_mx_weight(const uint8_t* codes, const uint8_t* scales, int64_t K, int64_t n, int64_t k) {
+  uint8_t byte = codes[n * (K / 2) + k / 2];
+  int c = (k % 2) ? (byte >> 4) : (byte & 0xF);
+  return or_e8m0_to_f64(scales[n * (K / 32) + k / 32]) * or_e2m1_to_f64(c);
+}
+
+void or_mx_dequant(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, double* W) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) W[n * K + k] = or_mx_weight(codes, scales, K, n, k);
+}
+
+/* Y[m][n] = sum_k X[m][k] W[n][k] for M input rows (the GEMV is M = 1), k ascending, every
+ * weight formed exactly in fp64. */
+void or_mx_matmul(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                  const double* X, int64_t M, double* Y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t m = 0; m < M; ++m) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += or_mx_weight(codes, scales, K, n, k) * X[m * K + k];
+      Y[m * N + n] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* elementwise pieces                                                                          */
 /* ------------------------------------------------------------------------------------------ */
 

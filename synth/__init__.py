@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.bws_norm_gain.argtypes = [u64, u32, u32, i64, vp]
         L.bws_embed_rows.argtypes = [u64, i64, i64, i64, vp]
         L.bws_router.argtypes = [u64, u32, i64, i64, vp]
+        L.bws_mx_matrix.argtypes = [u64, u32, u32, u32, i64, i64, i64, i32, i32, vp, vp]
         L.bws_kv_value.restype = ctypes.c_double
         L.bws_kv_value.argtypes = [u64, u32, u32, i64, i32, i32, i32, i32, i32]
         L.bws_kv_value_dt.restype = ctypes.c_double
@@ -74,6 +75,14 @@ def int4_matrix(seed: int, kind: int, layer: int, expert: int, N: int, K: int):
     codes = np.empty((N, K // 2), dtype=np.uint8)
     scales = np.empty((N, K // 32), dtype=np.uint16)
     lib().bws_int4_matrix(seed, kind, layer, expert, N, K, 0, N, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def mx_matrix(seed: int, kind: int, layer: int, expert: int, N: int, K: int, e_lo: int = 117, e_hi: int = 121):
+    """MXFP4 (codes uint8 [N][K/2], E8M0 scales uint8 [N][K/32]); scales uniform on [e_lo, e_hi]."""
+    codes = np.empty((N, K // 2), dtype=np.uint8)
+    scales = np.empty((N, K // 32), dtype=np.uint8)
+    lib().bws_mx_matrix(seed, kind, layer, expert, K, 0, N, e_lo, e_hi, codes.ctypes.data, scales.ctypes.data)
     return codes, scales
 
 

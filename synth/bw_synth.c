@@ -95,6 +95,22 @@ void bws_int4_matrix(uint64_t seed, uint32_t kind, uint32_t layer, uint32_t expe
                  1);
 }
 
+void bws_mx_matrix(uint64_t seed, uint32_t kind, uint32_t layer, uint32_t expert, int64_t K,
+                   int64_t row0, int64_t nrows, int e_lo, int e_hi, uint8_t* codes,
+                   uint8_t* scales) {
+  int64_t row_bytes = K / 2;
+  int64_t row_blocks = K / 32;
+  if (codes)
+    bws_fill_bytes(bws_key(seed, kind, layer, expert, BWS_SUB_MX_CODES),
+                   (uint64_t)(row0 * row_bytes), codes, (size_t)(nrows * row_bytes));
+  if (scales) {
+    uint64_t key = bws_key(seed, kind, layer, expert, BWS_SUB_MX_SCALES);
+    uint64_t span = (uint64_t)(e_hi - e_lo + 1);
+    for (int64_t i = 0; i < nrows * row_blocks; ++i)
+      scales[i] = (uint8_t)(e_lo + (int)(bws_hash(key, (uint64_t)(row0 * row_blocks + i)) % span));
+  }
+}
+
 void bws_norm_gain(uint64_t seed, uint32_t kind, uint32_t layer, int64_t n, uint16_t* dst) {
   bws_fill_f16(bws_key(seed, kind, layer, 0, 0), 0, dst, (size_t)n, 1.0, 0.1, 0);
 }

@@ -21,6 +21,8 @@
  *   embeddings        : fp16(z)
  *   RMSNorm gains     : fp16(1 + 0.1 z)
  *   MoE router matrix : fp16(0.02 z)
+ *   MXFP4 codes       : uniform on 0..15 (uniform random bytes, two E2M1 codes each)
+ *   MXFP4 scales      : E8M0 byte uniform on [e_lo, e_hi]
  *   synthetic KV      : c / 64 with c = (h & 0xFF) - 128, exact in bf16 and fp16; for an fp8
  *                       (OCP E4M3) cache (c >> 3) / 8, in [-2, 1.875], exact in E4M3
  */
@@ -54,9 +56,11 @@ enum {
  * BWS_SHARED_EXPERT + s for shared expert s. */
 #define BWS_SHARED_EXPERT 0x100000u
 
-/* sub-streams of an int4 matrix */
+/* sub-streams of an int4 matrix, and of an MXFP4 matrix */
 #define BWS_SUB_CODES 0u
 #define BWS_SUB_SCALES 1u
+#define BWS_SUB_MX_CODES 2u
+#define BWS_SUB_MX_SCALES 3u
 
 /* KV element dtype codes */
 #define BWS_KV_F16 1
@@ -103,6 +107,16 @@ void bws_fill_f16(uint64_t key, uint64_t off, uint16_t* dst, size_t n, double me
  * Either output pointer may be NULL. K must be a multiple of 32. */
 void bws_int4_matrix(uint64_t seed, uint32_t kind, uint32_t layer, uint32_t expert, int64_t N,
                      int64_t K, int64_t row0, int64_t nrows, uint8_t* codes, uint16_t* scales);
+
+/* One MXFP4 matrix [N][K] (OCP MX: E2M1 elements, one E8M0 scale per 32), rows
+ * [row0, row0+nrows):
+ *   codes : nrows * K/2 bytes; byte i of a row holds element 2i in bits 0-3 and element 2i+1
+ *           in bits 4-7 (uniform random bytes).
+ *   scales: nrows * K/32 bytes, one per block, row-major, each uniform on [e_lo, e_hi].
+ * Either output pointer may be NULL. K must be a multiple of 32; 0 <= e_lo <= e_hi <= 255. */
+void bws_mx_matrix(uint64_t seed, uint32_t kind, uint32_t layer, uint32_t expert, int64_t K,
+                   int64_t row0, int64_t nrows, int e_lo, int e_hi, uint8_t* codes,
+                   uint8_t* scales);
 
 /* Norm gains [n] for (kind in {BWS_ATTN_NORM, BWS_FFN_NORM, BWS_FINAL_NORM}, layer). */
 void bws_norm_gain(uint64_t seed, uint32_t kind, uint32_t layer, int64_t n, uint16_t* dst);

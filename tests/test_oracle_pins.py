@@ -167,6 +167,108 @@ def test_dequant_exhaustive_codes_and_finite_scales_exact_in_fp32():
         assert np.array_equal(f32.astype(np.float64), ref)
 
 
+def _golden_mx():
+    with open(os.path.join(GOLDEN, "mxfp4_blocks.json")) as f:
+        g = json.load(f)
+    codes = np.frombuffer(bytes.fromhex("".join(g["codes_hex"])), dtype=np.uint8).reshape(1, -1)
+    scales = np.array(g["scales_e8m0"], dtype=np.uint8).reshape(1, -1)
+    return g, codes, scales
+
+
+def _torch_e8m0(e: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(e, dtype=np.uint8)).view(torch.float8_e8m0fnu).to(
+        torch.float64).numpy()
+
+
+def test_e2m1_codes_match_hand_written_fixture():
+    g, _, _ = _golden_mx()
+    got = [oracle.e2m1_to_f64(c) for c in range(16)]
+    assert got == g["e2m1_values"]
+    assert [np.signbit(v) for v in got] == [c >= 8 for c in range(16)]  # -0.0 is code 8
+    # every magnitude is exact in E4M3 (the fp8 operand type of the scaled matrix cores)
+    for v in got:
+        assert oracle.fp8_to_f64(oracle.f64_to_fp8(v)) == v
+
+
+def test_e8m0_every_byte_matches_torch():
+    e = np.arange(256, dtype=np.uint8)
+    ref = _torch_e8m0(e)
+    got = np.array([oracle.e8m0_to_f64(int(b)) for b in e])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_mx_dequant_matches_hand_written_fixture():
+    g, codes, scales = _golden_mx()
+    W = oracle.mx_dequant(codes, scales)
+    assert W.shape == (1, g["K"])
+    assert W[0].tolist() == g["expected_weights"]
+    assert [np.signbit(v) for v in W[0, :16]] == [c >= 8 for c in range(16)]
+
+
+def test_mx_dequant_exhaustive_codes_and_scales():
+    # all 16 codes x all 256 scale bytes, each code in both nibble positions: the weight is the
+    # fixture's E2M1 value times torch's E8M0 value (NaN for the NaN scale)
+    g, _, _ = _golden_mx()
+    vals = np.array(g["e2m1_values"])
+    sc = _torch_e8m0(np.arange(256))
+    for c in range(16):
+        codes = np.full((256, 16), c | (c << 4), dtype=np.uint8)
+        W = oracle.mx_dequant(codes, np.arange(256, dtype=np.uint8).reshape(256, 1))
+        ref = sc * vals[c]
+        for col in (0, 1, 30, 31):
+            assert np.array_equal(W[:, col], ref, equal_nan=True), (c, col)
+        # and the low / high nibble positions hold different elements
+        codes = np.full((1, 16), c, dtype=np.uint8)  # high nibbles zero
+        W = oracle.mx_dequant(codes, np.array([[127]], dtype=np.uint8))
+        assert np.array_equal(W[0, 0::2], np.full(16, vals[c])) and not np.any(W[0, 1::2])
+
+
+def test_mx_matmul_matches_library_matmul_on_independent_decode():
+    # W decoded here from the fixture's value table, torch's E8M0 and the layout statement
+    # (element 2i low nibble, 2i+1 high nibble; block k // 32), then numpy's matmul
+    g, _, _ = _golden_mx()
+    vals = np.array(g["e2m1_values"])
+    rng = np.random.default_rng(77)
+    N, K, M = 5, 96, 3
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    W = np.empty((N, K))
+    for n in range(N):
+        for k in range(K):
+            byte = int(codes[n, k // 2])
+            c = (byte >> 4) if k % 2 else (byte & 0xF)
+            W[n, k] = vals[c] * 2.0 ** (int(scales[n, k // 32]) - 127)
+    assert np.array_equal(oracle.mx_dequant(codes, scales), W)
+    X = rng.standard_normal((M, K))
+    Y = oracle.mx_matmul(codes, scales, X)
+    assert Y.shape == (M, N)
+    np.testing.assert_allclose(Y, X @ W.T, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.mx_matmul(codes, scales, X[1]), X[1] @ W.T, rtol=1e-13, atol=1e-15)
+    # one-hot inputs read single weights exactly; a NaN scale poisons only its own row
+    for k in (0, 33, 95):
+        e = np.zeros(K)
+        e[k] = 1.0
+        assert np.array_equal(oracle.mx_matmul(codes, scales, e), W[:, k])
+    scales2 = scales.copy()
+    scales2[2, 1] = 255
+    y = oracle.mx_matmul(codes, scales2, X[0])
+    assert np.isnan(y[2]) and np.all(np.isfinite(np.delete(y, 2)))
+
+
+def test_generator_mx_matrix_layout_and_scale_range():
+    c, s = synth.mx_matrix(9, synth.QKV, 2, 0, 6, 128, 117, 121)
+    assert c.shape == (6, 64) and s.shape == (6, 4) and c.dtype == np.uint8 and s.dtype == np.uint8
+    assert s.min() >= 117 and s.max() <= 121
+    c2, s2 = synth.mx_matrix(9, synth.QKV, 2, 0, 6, 128, 117, 121)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+    c3, _ = synth.mx_matrix(9, synth.QKV, 3, 0, 6, 128)
+    assert not np.array_equal(c, c3)
+    cb, sb = synth.mx_matrix(9, synth.UP, 0, 0, 512, 512, 0, 255)
+    assert len(np.unique(sb)) > 200 and len(np.unique(cb & 0xF)) == 16 and len(np.unique(cb >> 4)) == 16
+
+
 def test_quant_round_trip():
     rng = np.random.default_rng(4)
     N, K = 16, 256
