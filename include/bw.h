@@ -64,6 +64,7 @@ extern "C" {
 typedef struct bw_model bw_model;
 typedef struct bw_kv_pool bw_kv_pool;
 typedef struct bw_kv_tier bw_kv_tier;
+typedef struct bw_expert_tier bw_expert_tier;
 
 /* Model shape. Dense models set n_experts = 0; MoE models set ffn_dim = 0 and the expert
  * fields. All layers share one shape. */
@@ -199,6 +200,49 @@ int bw_kv_tier_stats(const bw_kv_tier* tier, int32_t* resident_pages, int32_t* h
  * of smallest stamps[p], ties to the lower p, in that order. Errors: BW_EINVAL. */
 int bw_kv_lru_select(const uint64_t* stamps, const uint8_t* resident, int32_t n_pages, int32_t n,
                      int32_t* out, int32_t* n_out);
+
+/* ---- host tier of the routed expert weights (MoE) ----
+ * The deep-dive page ("Deep dive: bw24", section 6 item 3, the VRAM tier of Hy3; the comparison
+ * table of section 7, memory and model management) keeps the weights of the currently active
+ * experts in VRAM and moves cold ones to locked host memory by access time. Here a routed expert
+ * (gate/up and down matrices, codes and scales) sits either in a device region or in a pinned
+ * host slot, and the step's kernels read it wherever it is, through the model's per-layer expert
+ * pointer tables: an expert on the host is read over PCIe by the kernels themselves, so every
+ * step stays complete, only slower. Evicting an expert copies it to a host slot and repoints the
+ * tables; its device region joins a free list. Restoring takes any free region (routed experts
+ * all have one size) and copies the expert back. Copies and table updates are queued on the
+ * caller's stream after the work already queued there. Shared experts always stay on the device.
+ * Not thread-safe; free the tier before its model. */
+
+/* Create the tier with `host_slots` pinned host slots (hipHostMalloc, one routed expert each).
+ * Synchronous. Errors: BW_EINVAL, BW_ESTATE (a dense model), BW_ENOMEM, BW_EHIP. */
+int bw_expert_tier_create(bw_model* model, int32_t host_slots, bw_expert_tier** out);
+
+/* Restore every evicted expert (queued on `stream`), wait for the stream and release the tier.
+ * NULL is accepted. Errors: BW_EHIP (the tier is then kept). */
+int bw_expert_tier_free(bw_expert_tier* tier, void* stream);
+
+/* Record the experts that the last bw_decode_step routed rows [0, n_rows) to: their access time
+ * becomes the tier's clock, which then advances. Experts routed while on the host are marked for
+ * bw_expert_tier_restore_routed. Synchronises `stream`. Errors: BW_EINVAL, BW_ERANGE, BW_EHIP. */
+int bw_expert_tier_touch(bw_expert_tier* tier, int32_t n_rows, void* stream);
+
+/* Evict up to n device-resident routed experts, least recently routed first (ties: lower layer,
+ * then lower expert index), limited by the free host slots: (layers_out[i], experts_out[i]) for
+ * i < *n_out. Asynchronous on `stream`. Errors: BW_EINVAL, BW_EHIP. */
+int bw_expert_tier_evict_lru(bw_expert_tier* tier, int32_t n, int32_t* layers_out, int32_t* experts_out,
+                             int32_t* n_out, void* stream);
+
+/* Bring one evicted expert back into a free device region. Asynchronous on `stream`.
+ * Errors: BW_EINVAL (out of range, or the expert is on the device), BW_EHIP. */
+int bw_expert_tier_restore(bw_expert_tier* tier, int32_t layer, int32_t expert, void* stream);
+
+/* Restore every expert that the last touched step routed to while it was on the host (hot
+ * experts come back); *n_out receives their number. Asynchronous on `stream`. */
+int bw_expert_tier_restore_routed(bw_expert_tier* tier, int32_t* n_out, void* stream);
+
+/* Routed experts on the device and on the host. */
+int bw_expert_tier_stats(const bw_expert_tier* tier, int32_t* resident, int32_t* on_host);
 
 /* One decode step for `batch` sequences of `t` new tokens each (t = 1: plain decode; t > 1:
  * the verify step of speculative decoding, the t tokens laid out along the sequence).

@@ -33,7 +33,9 @@ EXPORTS = (
     "bw_debug_single_launch_stamps", "bw_spec_accept", "bw_debug_kv_round",
     "bw_kv_tier_create", "bw_kv_tier_free", "bw_kv_tier_touch", "bw_kv_tier_evict_lru", "bw_kv_tier_restore",
     "bw_kv_tier_wait", "bw_kv_tier_stats", "bw_kv_lru_select", "bw_model_export_tensor", "bw_model_tensor_bytes",
-    "bw_debug_copy_lm_head_row", "bw_attention_noalloc",
+    "bw_debug_copy_lm_head_row", "bw_attention_noalloc", "bw_expert_tier_create", "bw_expert_tier_free",
+    "bw_expert_tier_touch", "bw_expert_tier_evict_lru", "bw_expert_tier_restore", "bw_expert_tier_restore_routed",
+    "bw_expert_tier_stats",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -83,6 +85,13 @@ def lib() -> ctypes.CDLL:
         L.bw_model_tensor_bytes.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(sz)]
         L.bw_debug_copy_lm_head_row.argtypes = [vp, i32, i32]
         L.bw_attention_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
+        L.bw_expert_tier_create.argtypes = [vp, i32, ctypes.POINTER(vp)]
+        L.bw_expert_tier_free.argtypes = [vp, vp]
+        L.bw_expert_tier_touch.argtypes = [vp, i32, vp]
+        L.bw_expert_tier_evict_lru.argtypes = [vp, i32, vp, vp, ctypes.POINTER(i32), vp]
+        L.bw_expert_tier_restore.argtypes = [vp, i32, i32, vp]
+        L.bw_expert_tier_restore_routed.argtypes = [vp, ctypes.POINTER(i32), vp]
+        L.bw_expert_tier_stats.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.bw_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
         L.bw_check_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
         L.bw_debug_dequant.argtypes = [vp, i32, i32, i32, vp, vp]
@@ -190,6 +199,46 @@ def bw_model_tensor_bytes(model: int, name: str) -> int:
 def bw_model_export_tensor(model: int, name: str, out: np.ndarray) -> None:
     """out: host numpy array of exactly the tensor's size (uint8 codes, uint16 fp16 bits)."""
     _check(lib().bw_model_export_tensor(model, name.encode(), _ptr(out), out.nbytes), "bw_model_export_tensor")
+
+
+def bw_expert_tier_create(model: int, host_slots: int) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().bw_expert_tier_create(model, host_slots, ctypes.byref(h)), "bw_expert_tier_create")
+    return h.value
+
+
+def bw_expert_tier_free(tier: int, stream=None) -> None:
+    _check(lib().bw_expert_tier_free(tier, _stream(stream)), "bw_expert_tier_free")
+
+
+def bw_expert_tier_touch(tier: int, n_rows: int, stream=None) -> None:
+    _check(lib().bw_expert_tier_touch(tier, n_rows, _stream(stream)), "bw_expert_tier_touch")
+
+
+def bw_expert_tier_evict_lru(tier: int, n: int, stream=None):
+    """Returns (layers, experts) of the evicted experts, least recently routed first."""
+    ls = np.empty(max(n, 1), dtype=np.int32)
+    es = np.empty(max(n, 1), dtype=np.int32)
+    got = ctypes.c_int32()
+    _check(lib().bw_expert_tier_evict_lru(tier, n, _ptr(ls), _ptr(es), ctypes.byref(got), _stream(stream)),
+           "bw_expert_tier_evict_lru")
+    return ls[:got.value].copy(), es[:got.value].copy()
+
+
+def bw_expert_tier_restore(tier: int, layer: int, expert: int, stream=None) -> None:
+    _check(lib().bw_expert_tier_restore(tier, layer, expert, _stream(stream)), "bw_expert_tier_restore")
+
+
+def bw_expert_tier_restore_routed(tier: int, stream=None) -> int:
+    n = ctypes.c_int32()
+    _check(lib().bw_expert_tier_restore_routed(tier, ctypes.byref(n), _stream(stream)), "bw_expert_tier_restore_routed")
+    return n.value
+
+
+def bw_expert_tier_stats(tier: int):
+    r, h = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().bw_expert_tier_stats(tier, ctypes.byref(r), ctypes.byref(h)), "bw_expert_tier_stats")
+    return r.value, h.value
 
 
 def bw_debug_copy_lm_head_row(model: int, src: int, dst: int) -> None:

@@ -176,6 +176,8 @@ struct PageList {
   static constexpr int kMax = 128;
   int32_t id[kMax];
 };
+int launch_set_expert(const ExpertTab& tab, int e, const void* gc, const void* gs, const void* dc, const void* ds,
+                      hipStream_t s);
 int launch_page_pack(uint8_t* pool, int64_t layer_bytes, int64_t page_bytes, int L, const PageList& ids, int n,
                      uint8_t* stage, bool to_stage, hipStream_t s);
 

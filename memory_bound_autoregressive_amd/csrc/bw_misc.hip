@@ -250,4 +250,21 @@ int launch_page_pack(uint8_t* pool, int64_t layer_bytes, int64_t page_bytes, int
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// Expert host tier: repoint routed expert e of one layer's tables at new (gate/up codes, gate/up
+// scales, down codes, down scales) addresses, in stream order after the copies that moved it.
+__global__ void k_set_expert(ExpertTab tab, int e, const void* gc, const void* gs, const void* dc, const void* ds) {
+  if (threadIdx.x == 0) {
+    const_cast<const uint8_t**>(tab.gu_codes)[e] = (const uint8_t*)gc;
+    const_cast<const uint16_t**>(tab.gu_scales)[e] = (const uint16_t*)gs;
+    const_cast<const uint8_t**>(tab.dn_codes)[e] = (const uint8_t*)dc;
+    const_cast<const uint16_t**>(tab.dn_scales)[e] = (const uint16_t*)ds;
+  }
+}
+
+int launch_set_expert(const ExpertTab& tab, int e, const void* gc, const void* gs, const void* dc, const void* ds,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(k_set_expert, dim3(1), dim3(64), 0, s, tab, e, gc, gs, dc, ds);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace bw

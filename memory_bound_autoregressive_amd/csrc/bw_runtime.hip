@@ -989,6 +989,218 @@ extern "C" int bw_kv_tier_stats(const bw_kv_tier* t, int32_t* resident_pages, in
 }
 
 // ---------------------------------------------------------------------------------------------
+// host tier of the routed expert weights (MoE)
+// ---------------------------------------------------------------------------------------------
+
+// The device addresses of one routed expert's four parts.
+struct ExpertRegion {
+  const uint8_t* gc = nullptr;   // gate/up codes [2 Fe][d / 2]
+  const uint16_t* gs = nullptr;  // gate/up scales
+  const uint8_t* dc = nullptr;   // down codes [d][Fe / 2]
+  const uint16_t* ds = nullptr;  // down scales
+};
+
+struct bw_expert_tier {
+  bw_model* m = nullptr;
+  int32_t host_slots = 0;
+  size_t part[4] = {0, 0, 0, 0};  // bytes of each part (gate/up codes, scales, down codes, scales)
+  size_t off[4] = {0, 0, 0, 0};   // offset of each part inside a host slot (256-byte aligned)
+  size_t slot_bytes = 0;
+  uint8_t* host = nullptr;        // pinned [host_slots][slot_bytes] (hipHostMalloc)
+  uint8_t* host_dev = nullptr;    // the same memory as kernels address it
+  std::vector<uint64_t> stamp;    // [L * E]: tier clock when a touched step last routed the expert
+  std::vector<int32_t> slot_of;   // [L * E]: host slot of an evicted expert, -1 on the device
+  std::vector<ExpertRegion> dev_of;   // [L * E]: device region of a resident expert
+  std::vector<ExpertRegion> free_dev; // device regions holding no expert (one per evicted expert)
+  std::vector<int32_t> free_slots;    // host slots holding no expert (kept descending)
+  std::vector<uint8_t> routed_on_host;// [L * E]: routed by the last touched step while on the host
+  uint64_t clock = 1;
+};
+
+static ExpertRegion region_of(const LayerDev& Ld, int e) {
+  return {Ld.ex_gu[e].codes, Ld.ex_gu[e].scales, Ld.ex_dn[e].codes, Ld.ex_dn[e].scales};
+}
+
+// point expert e of layer l (tables on the device, descriptors on the host) at region r
+static int expert_point(bw_expert_tier* t, int l, int e, const ExpertRegion& r, hipStream_t s) {
+  LayerDev& Ld = t->m->L[l];
+  if (launch_set_expert(Ld.ex, e, r.gc, r.gs, r.dc, r.ds, s)) return fail(BW_EHIP, "expert table update failed");
+  Ld.ex_gu[e].codes = r.gc;
+  Ld.ex_gu[e].scales = r.gs;
+  Ld.ex_dn[e].codes = r.dc;
+  Ld.ex_dn[e].scales = r.ds;
+  return BW_OK;
+}
+
+static ExpertRegion slot_region(const bw_expert_tier* t, int32_t slot) {
+  uint8_t* b = t->host_dev + (size_t)slot * t->slot_bytes;
+  return {b + t->off[0], (const uint16_t*)(b + t->off[1]), b + t->off[2], (const uint16_t*)(b + t->off[3])};
+}
+
+// copy the four parts of an expert between two regions, in stream order
+static int expert_copy(const bw_expert_tier* t, const ExpertRegion& dst, const ExpertRegion& src, hipStream_t s) {
+  const void* sp[4] = {src.gc, src.gs, src.dc, src.ds};
+  void* dp[4] = {(void*)dst.gc, (void*)dst.gs, (void*)dst.dc, (void*)dst.ds};
+  for (int i = 0; i < 4; ++i) HIP_OK(hipMemcpyAsync(dp[i], sp[i], t->part[i], hipMemcpyDefault, s));
+  return BW_OK;
+}
+
+static int expert_evict(bw_expert_tier* t, int l, int e, hipStream_t s) {
+  const int E = t->m->c.n_experts;
+  const int32_t slot = t->free_slots.back();
+  t->free_slots.pop_back();
+  const ExpertRegion host = slot_region(t, slot), dev = t->dev_of[l * E + e];
+  if (int rc = expert_copy(t, host, dev, s)) return rc;
+  if (int rc = expert_point(t, l, e, host, s)) return rc;
+  t->free_dev.push_back(dev);
+  t->slot_of[l * E + e] = slot;
+  t->dev_of[l * E + e] = ExpertRegion{};
+  return BW_OK;
+}
+
+static int expert_restore(bw_expert_tier* t, int l, int e, hipStream_t s) {
+  const int E = t->m->c.n_experts;
+  const int32_t slot = t->slot_of[l * E + e];
+  const ExpertRegion dev = t->free_dev.back();
+  t->free_dev.pop_back();
+  if (int rc = expert_copy(t, dev, slot_region(t, slot), s)) return rc;
+  if (int rc = expert_point(t, l, e, dev, s)) return rc;
+  t->dev_of[l * E + e] = dev;
+  t->slot_of[l * E + e] = -1;
+  t->routed_on_host[l * E + e] = 0;
+  t->stamp[l * E + e] = t->clock;
+  // the slot is free again; a later eviction into it is queued after this copy on the same stream
+  t->free_slots.push_back(slot);
+  std::sort(t->free_slots.begin(), t->free_slots.end(), std::greater<int32_t>());
+  return BW_OK;
+}
+
+extern "C" int bw_expert_tier_create(bw_model* m, int32_t host_slots, bw_expert_tier** out) {
+  if (!m || !out) return fail(BW_EINVAL, "null argument");
+  *out = nullptr;
+  if (!is_moe(m->c)) return fail(BW_ESTATE, "the model has no routed experts");
+  if (host_slots < 1) return fail(BW_EINVAL, "host_slots must be positive");
+  const auto& c = m->c;
+  const int L = c.n_layers, E = c.n_experts, d = c.d_model, F = c.expert_ffn;
+  bw_expert_tier* t = new bw_expert_tier();
+  t->m = m;
+  t->host_slots = host_slots;
+  t->part[0] = (size_t)2 * F * d / 2;
+  t->part[1] = (size_t)2 * F * d / 32 * 2;
+  t->part[2] = (size_t)d * F / 2;
+  t->part[3] = (size_t)d * F / 32 * 2;
+  size_t o = 0;
+  for (int i = 0; i < 4; ++i) {
+    t->off[i] = o;
+    o += (t->part[i] + 255) & ~(size_t)255;
+  }
+  t->slot_bytes = o;
+  if (hipHostMalloc((void**)&t->host, (size_t)host_slots * o, hipHostMallocDefault) != hipSuccess) {
+    delete t;
+    return fail(BW_ENOMEM, "hipHostMalloc(%zu) for the expert tier failed", (size_t)host_slots * o);
+  }
+  if (hipHostGetDevicePointer((void**)&t->host_dev, t->host, 0) != hipSuccess || !t->host_dev) {
+    (void)hipHostFree(t->host);
+    delete t;
+    return fail(BW_EHIP, "no device address for the expert tier's host memory");
+  }
+  t->stamp.assign((size_t)L * E, 0);
+  t->slot_of.assign((size_t)L * E, -1);
+  t->routed_on_host.assign((size_t)L * E, 0);
+  t->dev_of.resize((size_t)L * E);
+  for (int l = 0; l < L; ++l)
+    for (int e = 0; e < E; ++e) t->dev_of[(size_t)l * E + e] = region_of(m->L[l], e);
+  for (int32_t sl = host_slots - 1; sl >= 0; --sl) t->free_slots.push_back(sl);
+  *out = t;
+  return BW_OK;
+}
+
+extern "C" int bw_expert_tier_free(bw_expert_tier* t, void* stream) {
+  if (!t) return BW_OK;
+  const int E = t->m->c.n_experts, L = t->m->c.n_layers;
+  int rc = BW_OK;
+  for (int l = 0; l < L && rc == BW_OK; ++l)
+    for (int e = 0; e < E && rc == BW_OK; ++e)
+      if (t->slot_of[l * E + e] >= 0) rc = expert_restore(t, l, e, (hipStream_t)stream);
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess && rc == BW_OK) rc = fail(BW_EHIP, "stream synchronisation failed");
+  if (rc != BW_OK) return rc;  // an expert may still point at the host memory: keep it
+  (void)hipHostFree(t->host);
+  delete t;
+  return BW_OK;
+}
+
+extern "C" int bw_expert_tier_touch(bw_expert_tier* t, int32_t n_rows, void* stream) {
+  if (!t) return fail(BW_EINVAL, "null tier");
+  const auto& c = t->m->c;
+  if (n_rows < 1 || n_rows > c.max_tokens) return fail(BW_ERANGE, "n_rows out of range");
+  const int L = c.n_layers, E = c.n_experts, k = c.top_k;
+  std::vector<int32_t> sel((size_t)L * c.max_tokens * k);
+  HIP_OK(hipStreamSynchronize((hipStream_t)stream));
+  HIP_OK(hipMemcpy(sel.data(), t->m->sel, sel.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+  std::fill(t->routed_on_host.begin(), t->routed_on_host.end(), 0);
+  for (int l = 0; l < L; ++l)
+    for (int r = 0; r < n_rows; ++r)
+      for (int j = 0; j < k; ++j) {
+        const int e = sel[((size_t)l * c.max_tokens + r) * k + j];
+        if (e < 0 || e >= E) continue;
+        t->stamp[(size_t)l * E + e] = t->clock;
+        if (t->slot_of[(size_t)l * E + e] >= 0) t->routed_on_host[(size_t)l * E + e] = 1;
+      }
+  ++t->clock;
+  return BW_OK;
+}
+
+extern "C" int bw_expert_tier_evict_lru(bw_expert_tier* t, int32_t n, int32_t* layers_out, int32_t* experts_out,
+                                        int32_t* n_out, void* stream) {
+  if (!t || !layers_out || !experts_out || !n_out) return fail(BW_EINVAL, "null argument");
+  if (n < 0) return fail(BW_EINVAL, "negative n");
+  const int E = t->m->c.n_experts, LE = t->m->c.n_layers * E;
+  std::vector<uint8_t> resident(LE);
+  for (int i = 0; i < LE; ++i) resident[i] = t->slot_of[i] < 0 ? 1 : 0;
+  const int32_t k = std::min<int32_t>(n, (int32_t)t->free_slots.size());
+  std::vector<int32_t> pick(std::max(k, 1));
+  int32_t got = 0;
+  if (int rc = bw_kv_lru_select(t->stamp.data(), resident.data(), LE, k, pick.data(), &got)) return rc;
+  for (int32_t i = 0; i < got; ++i) {
+    if (int rc = expert_evict(t, pick[i] / E, pick[i] % E, (hipStream_t)stream)) return rc;
+    layers_out[i] = pick[i] / E;
+    experts_out[i] = pick[i] % E;
+  }
+  *n_out = got;
+  return BW_OK;
+}
+
+extern "C" int bw_expert_tier_restore(bw_expert_tier* t, int32_t layer, int32_t expert, void* stream) {
+  if (!t) return fail(BW_EINVAL, "null tier");
+  const int E = t->m->c.n_experts;
+  if (layer < 0 || layer >= t->m->c.n_layers || expert < 0 || expert >= E) return fail(BW_EINVAL, "expert out of range");
+  if (t->slot_of[layer * E + expert] < 0) return fail(BW_EINVAL, "expert %d of layer %d is on the device", expert, layer);
+  return expert_restore(t, layer, expert, (hipStream_t)stream);
+}
+
+extern "C" int bw_expert_tier_restore_routed(bw_expert_tier* t, int32_t* n_out, void* stream) {
+  if (!t || !n_out) return fail(BW_EINVAL, "null argument");
+  const int E = t->m->c.n_experts, LE = t->m->c.n_layers * E;
+  int32_t n = 0;
+  for (int i = 0; i < LE; ++i)
+    if (t->routed_on_host[i] && t->slot_of[i] >= 0) {
+      if (int rc = expert_restore(t, i / E, i % E, (hipStream_t)stream)) return rc;
+      ++n;
+    }
+  *n_out = n;
+  return BW_OK;
+}
+
+extern "C" int bw_expert_tier_stats(const bw_expert_tier* t, int32_t* resident, int32_t* on_host) {
+  if (!t || !resident || !on_host) return fail(BW_EINVAL, "null argument");
+  int32_t h = 0;
+  for (int32_t v : t->slot_of) h += v >= 0 ? 1 : 0;
+  *on_host = h;
+  *resident = (int32_t)t->slot_of.size() - h;
+  return BW_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
 // the step
 // ---------------------------------------------------------------------------------------------
 
