@@ -488,6 +488,138 @@ def run_workload(args) -> int:
     return 0
 
 
+def run_mx(args) -> int:
+    """mx-gemv-9b / mx-gemm-9b: the dense-9b model's weight matrices (32 layers of QKV, O, gate/up and
+    down, then lm_head) in MXFP4, every matrix its own bytes in HBM. One step is one pass over all
+    of them: batch 1 on the vector-unit GEMV (bw_mx_gemv) or M = 128 rows (the verify shape, 32
+    sequences x 4 tokens) on the scaled matrix cores (bw_mx_gemm). Codes are uniform random bytes
+    and E8M0 scales uniform on 117..121 (the generator's MXFP4 distribution), drawn on the device
+    from a seeded generator; inputs are standard normal."""
+    import numpy as np
+    import torch
+
+    import memory_bound_autoregressive_amd as bw
+    from memory_bound_autoregressive_amd import configs
+
+    gemm = args.workload == "mx-gemm-9b"
+    cfg = configs.DENSE_9B
+    d, L, V = cfg["d_model"], cfg["n_layers"], cfg["vocab"]
+    H, G, D, F = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["ffn_dim"]
+    shapes = [((H + 2 * G) * D, d), (d, H * D), (2 * F, d), (d, F)] * L + [(V, d)]
+    M = 128 if gemm else 1
+    K = args.steps if args.steps_set else (20 if gemm else 100)
+    W = args.warmup if args.warmup_set else 3
+    torch.cuda.set_device(0)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg["seed"])
+    t0 = time.perf_counter()
+    mats = []
+    for N, Kd in shapes:
+        c = torch.randint(0, 256, (N, Kd // 2), dtype=torch.uint8, device="cuda", generator=gen)
+        sc = torch.randint(117, 122, (N, Kd // 32), dtype=torch.uint8, device="cuda", generator=gen)
+        mats.append((c, sc))
+    xin = {k: torch.randn((M, k), device="cuda", generator=gen) for k in {Kd for _, Kd in shapes}}
+    yout = {n: torch.empty((M, n), device="cuda") for n in {N for N, _ in shapes}}
+    ws = None
+    if gemm:
+        ws = torch.empty(max(bw.bw_mx_gemm_workspace_bytes(M, N, Kd) for N, Kd in shapes), dtype=torch.uint8,
+                         device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: {len(shapes)} MXFP4 matrices ready in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+
+    def one(i):
+        (c, sc), (N, Kd) = mats[i], shapes[i]
+        if gemm:
+            bw.bw_mx_gemm(c, sc, xin[Kd], yout[N], ws)
+        else:
+            bw.bw_mx_gemv(c, sc, xin[Kd][0], yout[N][0])
+
+    def step():
+        for i in range(len(mats)):
+            one(i)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    # per-launch kernel time: events around every launch of one extra pass
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in mats]
+    for i in range(len(mats)):
+        evs[i][0].record()
+        one(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    launch_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    wbytes = [N * Kd // 2 + N * Kd // 32 for N, Kd in shapes]
+    xbytes = [M * Kd * 4 + M * N * 4 for N, Kd in shapes]
+    step_bytes = sum(wbytes) + sum(xbytes)
+    flops = sum(2.0 * M * N * Kd for N, Kd in shapes)
+    kname = "k_mx_gemm" if gemm else "k_mx_gemv"
+    if gemm:
+        ach = flops / (sum(launch_us) * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": 5000.0, "unit": "TFLOP/s",
+                "frac": round(ach / 5000.0, 4), "traffic": None,
+                "kernel": "k_mx_gemm (with its X expansion and split-K reduction): E4M3 x E2M1 scaled products; "
+                          "achieved counts useful products, the matrix cores issue three per weight (one per X term)",
+                "flops_per_launch": round(flops / len(shapes)), "avg_launch_us": round(float(np.mean(launch_us)), 2),
+                "issued_tflops": round(3 * ach, 1)}
+        metric, value, unit = "MXFP4 GEMM useful TFLOP/s (dense-9b matrices, M = 128)", flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+    else:
+        ach = step_bytes / (sum(launch_us) * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0, "unit": "GB/s",
+                "frac": round(ach / 8000.0, 4), "traffic": None,
+                "kernel": "k_mx_gemv: one MXFP4 matrix times one fp32 vector",
+                "bytes_per_launch": round(step_bytes / len(shapes)), "avg_launch_us": round(float(np.mean(launch_us)), 2),
+                "lm_head_launch": {"bytes": wbytes[-1] + xbytes[-1], "us": round(launch_us[-1], 2),
+                                   "gbps": round((wbytes[-1] + xbytes[-1]) / (launch_us[-1] * 1e-6) / 1e9, 1)}}
+        metric, value, unit = "MXFP4 GEMV weight pass GB/s (dense-9b matrices, batch 1)", step_bytes / (ms * 1e-3) / 1e9, "GB/s"
+    print(f"[bench] {args.workload}: {ms * 1e3:.1f} us per pass, {value:.1f} {unit}; roofline {roof['frac']}",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        import synth
+        # the oracle's fp64 product on a bounded sample: 64 rows of a gate/up-shaped matrix
+        rows, Kd = 64, d
+        codes, scales = synth.mx_matrix(cfg["seed"], synth.UP, 0, 0, rows, Kd)
+        X = np.random.default_rng(0).standard_normal((M, Kd))
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.mx_matmul(codes, scales, X)
+            n += 1
+        dt = time.perf_counter() - t0
+        if gemm:
+            cv = 2.0 * M * rows * Kd * n / dt / 1e12
+            cpu = {"value": cv, "unit": "TFLOP/s", "cores": oracle.num_threads(), "cpu_model": cpu_model(),
+                   "kind": "oracle", "sample": f"{n} fp64 products of {M} x {Kd} by a {rows} x {Kd} MXFP4 matrix, {dt:.1f} s"}
+        else:
+            cv = (rows * Kd // 2 + rows * Kd // 32) * n / dt / 1e9
+            cpu = {"value": cv, "unit": "GB/s", "cores": oracle.num_threads(), "cpu_model": cpu_model(),
+                   "kind": "oracle", "sample": f"{n} fp64 GEMVs of a {rows} x {Kd} MXFP4 matrix, {dt:.1f} s"}
+        print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
+    out = {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "E4M3 x E2M1 products (X in three scaled E4M3 terms), f32 accumulation" if gemm else
+                 "f32 (E2M1 weights decoded exactly)",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": M, "matrices": len(shapes),
+                   "weights": "MXFP4: E2M1 codes, one E8M0 scale per 32 (uniform 117..121)", "seed": cfg["seed"]},
+        "weight_bytes_per_step": sum(wbytes), "bytes_per_step": step_bytes,
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -507,7 +639,8 @@ def main() -> int:
     ap.add_argument("--cooperative", action="store_true",
                     help="single-launch step through the cooperative launch API")
     ap.add_argument("--workload", default="dense-9b",
-                    choices=("dense-9b", "dense-27b", "moe-35b-a3b", "verify-9b", "prefill-9b", "kv-tier-9b"),
+                    choices=("dense-9b", "dense-27b", "moe-35b-a3b", "verify-9b", "prefill-9b", "kv-tier-9b",
+                             "mx-gemv-9b", "mx-gemm-9b"),
                     help="dense-9b (default): the headline line; the others time their own workload")
     ap.add_argument("--chunk", type=int, default=1024,
                     help="prefill-9b: tokens per prefill step (1024: 24.3 k tok/s against 18.7 k at 256)")
@@ -538,6 +671,8 @@ def main() -> int:
         return run_prefill(args)
     if args.workload == "kv-tier-9b":
         return run_tier(args)
+    if args.workload in ("mx-gemv-9b", "mx-gemm-9b"):
+        return run_mx(args)
     if args.workload != "dense-9b" or args.kv not in (None, "bf16"):
         return run_workload(args)
 
@@ -636,6 +771,7 @@ def main() -> int:
         st = torch.zeros(L * 16 + 8, dtype=torch.int64, device=dev)
         bw.bw_debug_single_launch_stamps(s.model, st, L * 16 + 8)
         acc = np.zeros((L, 6, 2))
+        att = np.zeros(3)  # attention work: page loop, wave reductions + barrier, cross-wave merge + stores
         lm = np.zeros(2)
         n_ph = 8
         for _ in range(n_ph):
@@ -648,6 +784,8 @@ def main() -> int:
             acc[:, :, 0] += ph[:, :, 1] - ph[:, :, 0]
             acc[:, :, 1] += nxt - ph[:, :, 1]
             lm += [v[L * 16 + 1] - v[L * 16], v[L * 16 + 3] - v[L * 16 + 1]]
+            a3, a12, a13, a4 = v[:L * 16].reshape(L, 16)[:, [3, 12, 13, 4]].T
+            att += [np.mean(a12 - a3), np.mean(a13 - a12), np.mean(a4 - a13)]
         bw.bw_debug_single_launch_stamps(s.model, None)
         acc /= n_ph
         lm /= n_ph
@@ -655,6 +793,10 @@ def main() -> int:
         phases = {k: {"wait_us": round(float(acc[:, i, 0].mean()), 2), "work_us": round(float(acc[:, i, 1].mean()), 2)}
                   for i, k in enumerate(names)}
         phases["lm_head"] = {"wait_us": round(float(lm[0]), 2), "work_us": round(float(lm[1]), 2)}
+        att /= n_ph
+        phases["attention"]["work_split_us"] = {"page_loop": round(float(att[0]), 2),
+                                                "wave_reduce": round(float(att[1]), 2),
+                                                "merge_store": round(float(att[2]), 2)}
         if bw.bw_check_device_error(s.model) != 0:
             print("[bench] device error flag set in the traced passes", file=sys.stderr)
             return 1

@@ -333,6 +333,42 @@ int bw_spec_accept(bw_model* model, int32_t* tokens_dev, const int32_t* argmax_d
  * and clear it. */
 int bw_check_device_error(bw_model* model, void* stream, int32_t* flags_host);
 
+/* ---- MXFP4 weights on the matrix cores ----------------------------------------------------
+ * A 4-bit floating-point weight format (bw24 deep-dive page, section 1, quantisation formats,
+ * and the performance-strategy row of the section 7 table). The pages' engine uses NVIDIA's
+ * NVFP4; the 4-bit float the CDNA4 matrix cores consume is OCP MX MXFP4, defined here: an
+ * [N][K] matrix (K a multiple of 32) in blocks of 32 E2M1 elements along K, one E8M0 scale byte
+ * per block, w = 2^(e - 127) * element (e = 255 is NaN).
+ *   codes : [N][K/2] bytes, row-major; byte i of a row holds element 2i in bits 0-3 and element
+ *           2i+1 in bits 4-7.
+ *   scales: [N][K/32] E8M0 bytes, row-major.
+ * These entry points take device pointers owned by the caller and run asynchronously on
+ * `stream`. Products too large for fp32 come out as +-inf. */
+
+/* y = W x for one input vector: x float32 [K], y float32 [N] (vector units; each weight is
+ * decoded exactly to fp32 in registers, products and sums in fp32; a block with scale byte 255
+ * makes its row NaN). K <= 16384; x 16-byte aligned.
+ * Errors: BW_EINVAL (null pointer, N < 1, K not a multiple of 32 in [32, 16384]), BW_EHIP. */
+int bw_mx_gemv(const uint8_t* codes_dev, const uint8_t* scales_dev, const float* x_dev, float* y_dev,
+               int64_t N, int64_t K, void* stream);
+
+/* Device workspace bytes bw_mx_gemm needs for these sizes on the current device.
+ * Errors: BW_EINVAL (null bytes_out, M, N or K out of range). */
+int bw_mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t* bytes_out);
+
+/* Y = X W^T for M input rows on the scaled matrix cores (bw24 deep-dive page, section 5, stage
+ * 4: the rows of a verify or batched step share one pass over the weights): X float32 [M][K]
+ * (finite, 16-byte aligned), Y float32 [M][N]. The weights enter the products as stored (E2M1 with their E8M0
+ * scales). X is first expanded into three MXFP8 terms (E4M3, one E8M0 scale per 32 along K), each
+ * quantising the exact residual of the ones before it, which leaves at most 2^-12 of each
+ * 32-element block's largest magnitude; each weight fragment feeds the three scaled products.
+ * `workspace` (device, 256-byte aligned, at least bw_mx_gemm_workspace_bytes) holds the terms and
+ * any split-K partials; calls sharing a workspace must not overlap. 1 <= M <= 2^22, K <= 2^20.
+ * Errors: BW_EINVAL (null pointer, size out of range, misaligned workspace), BW_ERANGE
+ * (workspace too small), BW_EHIP. */
+int bw_mx_gemm(const uint8_t* codes_dev, const uint8_t* scales_dev, const float* X_dev, float* Y_dev, int64_t M,
+               int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* ---- parity-test entry points (same kernels as the step, exposed one at a time) ---------- */
 
 /* Matrix selectors */

@@ -35,7 +35,7 @@ EXPORTS = (
     "bw_kv_tier_wait", "bw_kv_tier_stats", "bw_kv_lru_select", "bw_model_export_tensor", "bw_model_tensor_bytes",
     "bw_debug_copy_lm_head_row", "bw_attention_noalloc", "bw_expert_tier_create", "bw_expert_tier_free",
     "bw_expert_tier_touch", "bw_expert_tier_evict_lru", "bw_expert_tier_restore", "bw_expert_tier_restore_routed",
-    "bw_expert_tier_stats",
+    "bw_expert_tier_stats", "bw_mx_gemv", "bw_mx_gemm_workspace_bytes", "bw_mx_gemm",
 )
 KERNEL_CLASS = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4, "lm_head": 5, "router": 6,
                 "moe_gate_up": 7, "moe_down": 8}
@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
-        vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+        vp, i32, u64, sz, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_int64
         for name in EXPORTS:
             getattr(L, name).restype = i32
         L.bw_last_error.restype = ctypes.c_char_p
@@ -85,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.bw_model_tensor_bytes.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(sz)]
         L.bw_debug_copy_lm_head_row.argtypes = [vp, i32, i32]
         L.bw_attention_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
+        L.bw_mx_gemv.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+        L.bw_mx_gemm_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
+        L.bw_mx_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, vp]
         L.bw_expert_tier_create.argtypes = [vp, i32, ctypes.POINTER(vp)]
         L.bw_expert_tier_free.argtypes = [vp, vp]
         L.bw_expert_tier_touch.argtypes = [vp, i32, vp]
@@ -293,6 +296,28 @@ def bw_attention_noalloc(model: int, pool: int, layer: int, q, seq_lens, page_ta
     nothing; calls on one GPU must not overlap). See include/bw.h."""
     _check(lib().bw_attention_noalloc(model, pool, layer, _ptr(q), _ptr(seq_lens), _ptr(page_table), batch, t,
                                       max_pages, _ptr(out), _stream(stream)), "bw_attention_noalloc")
+
+
+def bw_mx_gemv(codes, scales, x, y, stream=None) -> None:
+    """MXFP4 y = W x. codes: device uint8 [N][K/2]; scales: device uint8 E8M0 [N][K/32]; x: device
+    float32 [K]; y: device float32 [N]."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    _check(lib().bw_mx_gemv(_ptr(codes), _ptr(scales), _ptr(x), _ptr(y), N, K, _stream(stream)), "bw_mx_gemv")
+
+
+def bw_mx_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    n = ctypes.c_int64()
+    _check(lib().bw_mx_gemm_workspace_bytes(M, N, K, ctypes.byref(n)), "bw_mx_gemm_workspace_bytes")
+    return n.value
+
+
+def bw_mx_gemm(codes, scales, X, Y, workspace, stream=None) -> None:
+    """MXFP4 Y = X W^T. X: device float32 [M][K]; Y: device float32 [M][N]; workspace: device buffer of
+    at least bw_mx_gemm_workspace_bytes(M, N, K) bytes."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    M = X.shape[0]
+    _check(lib().bw_mx_gemm(_ptr(codes), _ptr(scales), _ptr(X), _ptr(Y), M, N, K, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)), "bw_mx_gemm")
 
 
 def bw_debug_kv_round(kv_dtype: int, x, bits, back, stream=None) -> None:

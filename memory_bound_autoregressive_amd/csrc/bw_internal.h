@@ -176,6 +176,16 @@ struct PageList {
   static constexpr int kMax = 128;
   int32_t id[kMax];
 };
+// MXFP4 weights (bw_mx.hip)
+constexpr int kMxGemvMaxK = 16384;
+int launch_mx_gemv(const uint8_t* codes, const uint8_t* scales, const float* x, float* y, int64_t N, int K,
+                   hipStream_t st);
+int launch_mx_quant(const float* X, uint8_t* xq, uint32_t* xs, int64_t M, int K, int Kp, float* Y_zero,
+                    int64_t y_elems, hipStream_t st);
+int mx_gemm_splits(int64_t M, int64_t N, int K);
+int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int K, int splits);
+int launch_mx_gemm(const uint8_t* codes, const uint8_t* scales, const float* X, float* Y, int64_t M, int64_t N,
+                   int K, void* ws, int splits, hipStream_t st);
 int launch_set_expert(const ExpertTab& tab, int e, const void* gc, const void* gs, const void* dc, const void* ds,
                       hipStream_t s);
 int launch_page_pack(uint8_t* pool, int64_t layer_bytes, int64_t page_bytes, int L, const PageList& ids, int n,

@@ -373,14 +373,14 @@ static int persist_setup(bw_model* m) {
     if (!moe_fits) return BW_OK;
   }
   const int S = nwg / G;
-  const int Rm = (H * D + nwg - 1) / nwg;
   const int Rd = (d + nwg - 1) / nwg;
   const int Rq = ((((H + 2 * G) * D + nwg - 1) / nwg) + 1) & ~1;
   const int Rg = (((2 * F + nwg - 1) / nwg) + 1) & ~1;
   int lpr, nb;
   gemv_lane_split(d, &lpr, &nb);
-  const bool fits = H * D == d && S >= 1 && S <= 128 && Rm * S <= 2048 && Rm <= D && Rd <= 64 && Rq <= 1024 &&
-                    Rg <= 1024 && (H / G) * D <= 4096;
+  // one merger workgroup per query head among the splits of its KV head (S >= H / G)
+  const bool fits = H * D == d && S >= H / G && S <= 128 && Rd <= 64 && Rq <= 1024 && Rg <= 1024 &&
+                    (H / G) * D <= 4096;
   if (!fits) return BW_OK;
   PersistParams& p = m->pp;
   if (moe) {
@@ -1816,6 +1816,49 @@ extern "C" int bw_attention_noalloc(bw_model* m, bw_kv_pool* pool, int32_t layer
   a.part = (float*)ptr;
   a.counters = nullptr;  // the attention kernels keep no arrival counters
   if (launch_attention(a, m->c.kv_dtype, batch, (hipStream_t)stream)) return fail(BW_EHIP, "attention launch failed");
+  return BW_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// MXFP4 weights
+// ---------------------------------------------------------------------------------------------
+
+extern "C" int bw_mx_gemv(const uint8_t* codes, const uint8_t* scales, const float* x, float* y, int64_t N,
+                          int64_t K, void* stream) {
+  if (!codes || !scales || !x || !y) return fail(BW_EINVAL, "null argument");
+  if (N < 1 || N > ((int64_t)1 << 40)) return fail(BW_EINVAL, "N out of range");
+  if (K < 32 || K % 32 || K > kMxGemvMaxK) return fail(BW_EINVAL, "K must be a multiple of 32 in [32, %d]", kMxGemvMaxK);
+  if ((uintptr_t)x % 16) return fail(BW_EINVAL, "x must be 16-byte aligned");
+  if (launch_mx_gemv(codes, scales, x, y, N, (int)K, (hipStream_t)stream)) return fail(BW_EHIP, "MXFP4 GEMV launch failed");
+  return BW_OK;
+}
+
+static int mx_gemm_check(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > ((int64_t)1 << 22)) return fail(BW_EINVAL, "M out of range");
+  if (N < 1 || N > ((int64_t)1 << 36)) return fail(BW_EINVAL, "N out of range");
+  if (K < 32 || K % 32 || K > ((int64_t)1 << 20)) return fail(BW_EINVAL, "K must be a multiple of 32 in [32, 2^20]");
+  return BW_OK;
+}
+
+extern "C" int bw_mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t* bytes_out) {
+  if (!bytes_out) return fail(BW_EINVAL, "null argument");
+  if (int rc = mx_gemm_check(M, N, K)) return rc;
+  *bytes_out = mx_gemm_workspace_bytes(M, N, (int)K, mx_gemm_splits(M, N, (int)K));
+  return BW_OK;
+}
+
+extern "C" int bw_mx_gemm(const uint8_t* codes, const uint8_t* scales, const float* X, float* Y, int64_t M, int64_t N,
+                          int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!codes || !scales || !X || !Y || !workspace) return fail(BW_EINVAL, "null argument");
+  if (int rc = mx_gemm_check(M, N, K)) return rc;
+  const int splits = mx_gemm_splits(M, N, (int)K);
+  const int64_t need = mx_gemm_workspace_bytes(M, N, (int)K, splits);
+  if (workspace_bytes < need) return fail(BW_ERANGE, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                                          (long long)need);
+  if ((uintptr_t)workspace % 256) return fail(BW_EINVAL, "workspace must be 256-byte aligned");
+  if ((uintptr_t)X % 16) return fail(BW_EINVAL, "X must be 16-byte aligned");
+  if (launch_mx_gemm(codes, scales, X, Y, M, N, (int)K, workspace, splits, (hipStream_t)stream))
+    return fail(BW_EHIP, "MXFP4 GEMM launch failed");
   return BW_OK;
 }
 
