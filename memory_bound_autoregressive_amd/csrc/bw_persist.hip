@@ -195,8 +195,7 @@ constexpr int kLmRW = BW_LM_RW;  // row steps per group of the lm_head pass
 constexpr int kMaxOwn = 64;     // residual rows per workgroup
 constexpr int kMaxSplitPages = 256;  // pages of one attention split (workgroup)
 constexpr int kMaxSplit = kPT / 4;  // attention splits per KV head (workgroups / KV heads)
-constexpr int kMrgProd = 2048;      // (attention output, split) products per workgroup
-// merge scratch: (m, l) of [2 heads][splits], factors [2][splits], denominators [2], products
+// merge scratch: (m, l) of [splits], factors [splits], partial sums [kPT], the denominator
 // MoE scratch inside mrg (free outside the merge phase), in floats: top-k candidates [kMoeMaxE]
 // (uint64 keys), maxima of 16-key rows [32] (uint64), the threshold (uint64) and candidate count,
 // chosen experts [64] and their keys [64] (uint64), slot gates, slot matrix pointers [slots][4],
@@ -207,7 +206,7 @@ constexpr int kMoeGate = kMoeChosenKey + 128, kMoePtr = kMoeGate + 64;
 constexpr int kMoeMaxSlots = 32;
 constexpr int kMoeAll = kMoePtr + 2 * 4 * kMoeMaxSlots;
 constexpr int kMoeMaxEx = 480;  // routed + shared experts
-constexpr int kMrgMerge = 4 * kMaxSplit + 2 * kMaxSplit + 8 + kMrgProd;
+constexpr int kMrgMerge = 3 * kMaxSplit + kPT + 8;
 constexpr int kMrgMoe = kMoeAll + 2 * 2 * kMoeMaxEx;
 constexpr int kMrg = kMrgMerge > kMrgMoe ? kMrgMerge : kMrgMoe;
 static_assert(kMoeGmax % 4 == 0 && kMoeThr % 2 == 0 && kMoeChosenKey % 2 == 0 && kMoePtr % 4 == 0 && kMoeAll % 4 == 0,
@@ -657,8 +656,6 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   const int g0 = min(w * Rg, 2 * KF), g1 = min(g0 + Rg, 2 * KF);
   const int Rv = (p.V + nwg - 1) / nwg;
   const int v0 = min(w * Rv, p.V), v1 = min(v0 + Rv, p.V);
-  const int Rm = (HD + nwg - 1) / nwg;
-  const int m0 = min(w * Rm, HD), m1 = min(m0 + Rm, HD);
   const int S = nwg / G;  // attention splits per KV head
   const int ag = w / S, as = w - ag * S;  // this workgroup's (KV head, split); ag >= G: idle
 
@@ -983,7 +980,11 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       }
     }
 
-    // ================= MERGE (outputs [m0, m1) of the H*D attention vector) =================
+    // ================= MERGE (one workgroup per query head) =================
+    // Split q < QR of KV head g combines the S split partials of query head g * QR + q and stores
+    // that head's D outputs; every other workgroup goes on to the O phase at once (its O weights
+    // go out here), so the attention output takes one exchange from the splits to the mergers
+    // (S producers each) and one all-gather into O.
     stamp(p, l * 16 + 4);
     PGroup<LPR_D, NB_D, RWO> o_pre;
     {
@@ -991,89 +992,79 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int lane = tid & 63, wave = wave_of(tid);
       (void)lane;
       (void)wave;
-      // The range covers at most two heads (m1 - m0 <= D). Thread t first waits for one (m, l)
-      // word and for the acc words of (output, split) pairs t, t + kPT, ... (at most kMrgProd).
-      const __amdgpu_buffer_rsrc_t r = xrsrc(p.xp, (int64_t)H * S * (D + 2) * 4);
-      float* ml = s.mrg;                       // [2][S][2]
-      float* fm = s.mrg + 4 * kMaxSplit;       // [2][S]
-      float* den = fm + 2 * kMaxSplit;         // [2]
-      float* prod = den + 8;                   // [m1 - m0][S]
-      const int n_out = m1 - m0;
-      const int hA = m0 / D, hB = n_out > 0 ? (m1 - 1) / D : hA;
-      constexpr int NW = 1 + kMrgProd / kPT;
-      int idx[NW];
-      uint32_t word[NW];
-      {
-        const int e = tid;  // (head slot, split, m|l)
-        const int hh = e / (2 * S), rest = e - hh * 2 * S;
-        const bool use = n_out > 0 && hh < 2 && !(hh == 1 && hB == hA);
-        idx[0] = use ? ((hh == 0 ? hA : hB) * S + (rest >> 1)) * (D + 2) + D + (rest & 1) : -1;
-      }
+      if (ag < G && as < QR) {
+        const int h = ag * QR + as;
+        const __amdgpu_buffer_rsrc_t r = xrsrc(p.xp, (int64_t)H * S * (D + 2) * 4);
+        constexpr int SG = kPT / D;  // split groups: thread t takes output t % D of splits t / D + SG i
+        constexpr int NA = 8;        // partial words per thread per round
+        static_assert(kPT % D == 0 && 3 * kMaxSplit + kPT + 1 <= kMrg, "merge scratch");
+        const int dd = tid % D, sg = tid / D;
+        float* ml = s.mrg;                  // [S][2]: running max, denominator
+        float* fm = s.mrg + 2 * kMaxSplit;  // [S]: exp(m - M)
+        float* part = fm + kMaxSplit;       // [SG][D]
+        float* den = part + kPT;            // [1]
+        int idx[1 + NA];
+        uint32_t word[1 + NA];
+        idx[0] = tid < 2 * S ? (h * S + (tid >> 1)) * (D + 2) + D + (tid & 1) : -1;
 #pragma unroll
-      for (int i = 1; i < NW; ++i) {
-        const int t = tid + (i - 1) * kPT;  // (output, split)
-        const int eo = t / S, sp = t - eo * S;
-        if (eo < n_out) {
-          const int e = m0 + eo, h = e / D, dd = e - h * D;
-          idx[i] = (h * S + sp) * (D + 2) + dd;
-        } else {
-          idx[i] = -1;
+        for (int i = 0; i < NA; ++i) {
+          const int sp = sg + SG * i;
+          idx[1 + i] = sp < S ? (h * S + sp) * (D + 2) + dd : -1;
         }
-      }
-      poll_words_issue<NW>(r, idx, word);
-      gemv_first<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, o_pre);
-      poll_words_wait<NW>(r, idx, tout, word, ctl);
-      if (idx[0] >= 0) ml[tid] = xdec(word[0]);
-      __syncthreads();
-      stamp(p, l * 16 + 5);
-      if (bail) return;
-      // per head: max over splits, factors, denominator (fixed-order reductions: deterministic)
-      const bool fast = S <= kWave && (S & (S - 1)) == 0;
-      if (n_out > 0 && wave < 2 && !(wave == 1 && hB == hA)) {
-        float M = kNoScore;
-        for (int sp = lane; sp < S; sp += kWave) M = fmaxf(M, ml[(wave * S + sp) * 2]);
-        M = wmax(M);
-        float dpart = 0.f;
-        for (int sp = lane; sp < S; sp += kWave) {
-          const float f = __expf(ml[(wave * S + sp) * 2] - M);
-          fm[wave * kMaxSplit + sp] = f;
-          dpart = fmaf(ml[(wave * S + sp) * 2 + 1], f, dpart);
-        }
-        dpart = wsum(dpart);
-        if (lane == 0) den[wave] = dpart;
-      }
-      __syncthreads();
-      if (fast) {
-        // the S splits of one output sit in S consecutive lanes: butterfly sum within the group
-#pragma unroll
-        for (int i = 1; i < NW; ++i) {
-          const int t = tid + (i - 1) * kPT;
-          const int eo = t / S, sp = t - eo * S;
-          const int hh = (m0 + eo) / D == hA ? 0 : 1;
-          float v = idx[i] >= 0 ? xdec(word[i]) * fm[hh * kMaxSplit + sp] : 0.f;
-          v = sum_lanes(v, S);
-          if (idx[i] >= 0 && sp == 0) {
-            const float dd = den[hh];
-            xstore(p.xa, m0 + eo, dd > 0.f ? v / dd : 0.f, tout);
+        poll_words_issue<1 + NA>(r, idx, word);
+        gemv_first<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, o_pre);
+        poll_words_wait<1 + NA>(r, idx, tout, word, ctl);
+        if (idx[0] >= 0) ml[tid] = xdec(word[0]);
+        __syncthreads();
+        stamp(p, l * 16 + 5);
+        if (bail) return;
+        // max over the splits, factors, denominator (fixed-order reductions: deterministic)
+        if (wave == 0) {
+          float M = kNoScore;
+          for (int sp = lane; sp < S; sp += kWave) M = fmaxf(M, ml[2 * sp]);
+          M = wmax(M);
+          float dpart = 0.f;
+          for (int sp = lane; sp < S; sp += kWave) {
+            const float f = __expf(ml[2 * sp] - M);
+            fm[sp] = f;
+            dpart = fmaf(ml[2 * sp + 1], f, dpart);
           }
-        }
-      } else {
-#pragma unroll
-        for (int i = 1; i < NW; ++i) {
-          if (idx[i] < 0) continue;
-          const int t = tid + (i - 1) * kPT;
-          const int eo = t / S, sp = t - eo * S;
-          const int hh = (m0 + eo) / D == hA ? 0 : 1;
-          prod[eo * S + sp] = xdec(word[i]) * fm[hh * kMaxSplit + sp];
+          dpart = wsum(dpart);
+          if (lane == 0) den[0] = dpart;
         }
         __syncthreads();
-        for (int eo = tid; eo < n_out; eo += kPT) {
-          const int hh = (m0 + eo) / D == hA ? 0 : 1;
-          float a = 0.f;
-          for (int sp = 0; sp < S; ++sp) a += prod[eo * S + sp];
-          const float dd = den[hh];
-          xstore(p.xa, m0 + eo, dd > 0.f ? a / dd : 0.f, tout);
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+          if (idx[1 + i] >= 0) a = fmaf(xdec(word[1 + i]), fm[sg + SG * i], a);
+        // more splits than SG * NA (small models with many splits per KV head)
+        for (int base = SG * NA; base < S; base += SG * NA) {
+          int idx2[NA];
+          uint32_t w2[NA];
+#pragma unroll
+          for (int i = 0; i < NA; ++i) {
+            const int sp = base + sg + SG * i;
+            idx2[i] = sp < S ? (h * S + sp) * (D + 2) + dd : -1;
+          }
+          poll_words_issue<NA>(r, idx2, w2);
+          poll_words_wait<NA>(r, idx2, tout, w2, ctl);
+#pragma unroll
+          for (int i = 0; i < NA; ++i)
+            if (idx2[i] >= 0) a = fmaf(xdec(w2[i]), fm[base + sg + SG * i], a);
         }
+        part[sg * D + dd] = a;
+        __syncthreads();
+        if (bail) return;
+        if (tid < D) {
+          float o = 0.f;
+#pragma unroll
+          for (int g2 = 0; g2 < SG; ++g2) o += part[g2 * D + tid];
+          const float dn = den[0];
+          xstore(p.xa, h * D + tid, dn > 0.f ? o / dn : 0.f, tout);
+        }
+      } else {
+        gemv_first<LPR_D, NB_D, RWO>(tid, Ly.o, d0, d1, o_pre);
+        stamp(p, l * 16 + 5);
       }
     }
 
