@@ -11,8 +11,8 @@
 // the row, one 16-byte load each, so the 16 lanes of a row read 256 contiguous bytes per load
 // instruction. Each wave handles 4 rows at a time. The input vector is staged once per workgroup
 // in LDS (fp32). Each 32-element block is decoded in registers by v_cvt_scalef32_pk_f32_fp4 (two
-// elements per instruction, exact), multiplied into fp32 FMAs, and the block sum is scaled by the
-// exact power of two of its E8M0 byte.
+// elements per instruction, the block's E8M0 scale applied by the conversion, exact) and
+// multiplied into fp32 FMAs.
 //
 // GEMM (Y = X W^T, X fp32 [M][K]). The matrix cores take the weights as they are stored: E2M1
 // codes with their E8M0 block scales are the fp4 operand of v_mfma_scale_f32_32x32x64_f8f6f4.
@@ -41,17 +41,20 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // sum over the 32 elements of one block (codes in q, element 2i+h in nibble h of byte i) of
-// element * x, with x in LDS (fp32, 8 chunks of 4 at xs_chunk(xs, b, c))
-__device__ __forceinline__ float mx_block_dot(u32x4 q, const float* xs, int b) {
+// scale * element * x. The conversion applies the block's E8M0 scale itself (it reads only the
+// exponent field of its fp32 scale operand: field e means 2^(e - 127), 255 is NaN), so each
+// weight comes out exact in fp32. x sits in LDS chunk-major: chunk c (elements 4c..4c+3) of
+// block b at xc + c * cstride, with xc the block's first chunk.
+__device__ __forceinline__ float mx_block_dot(u32x4 q, float scale, const float* xc, int cstride) {
   float d0 = 0.f, d1 = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float4 xa = *(const float4*)xs_chunk(xs, b, 2 * w);
-    const float4 xb = *(const float4*)xs_chunk(xs, b, 2 * w + 1);
-    const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], 1.0f, 0);
-    const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], 1.0f, 1);
-    const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], 1.0f, 2);
-    const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], 1.0f, 3);
+    const float4 xa = *(const float4*)(xc + (2 * w) * cstride);
+    const float4 xb = *(const float4*)(xc + (2 * w + 1) * cstride);
+    const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], scale, 0);
+    const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], scale, 1);
+    const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], scale, 2);
+    const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], scale, 3);
     d0 = fmaf(e0[0], xa.x, d0);
     d1 = fmaf(e0[1], xa.y, d1);
     d0 = fmaf(e1[0], xa.z, d0);
@@ -89,12 +92,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p, int64_t
 // the current one is computed.
 __global__ __launch_bounds__(kBlock) void k_mx_gemv(MxGemvParams p) {
   extern __shared__ __align__(16) float xs[];  // K floats
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: descriptors built from it stay scalar
   const int K = p.K, nb = K / 32;
-  // stage x: chunk c of block b at its swizzled slot
+  // stage x chunk-major: chunk c of block b at float (c * nb + b) * 4, so the 16 lanes of a row,
+  // reading chunk c of 16 consecutive blocks, touch 256 consecutive bytes (every bank once), and
+  // a lane's addresses differ only by constants
   for (int i = tid; i < K / 4; i += kBlock) {
     const int b = i >> 3, c = i & 7;
-    *(float4*)xs_chunk(xs, b, c) = ((const float4*)p.x)[i];
+    *(float4*)(xs + (c * nb + b) * 4) = ((const float4*)p.x)[i];
   }
   __syncthreads();
   const int j = lane % kMxLpr, rsub = lane / kMxLpr;
@@ -112,16 +118,19 @@ __global__ __launch_bounds__(kBlock) void k_mx_gemv(MxGemvParams p) {
   auto load = [&](int64_t u, Unit& f) {
     const int64_t rs = gw + (u / nch) * nw;
     const int ch = (int)(u % nch);
-    const int64_t n = rs * kMxRpw + rsub;
-    const bool ok = n < p.N;
-    const __amdgpu_buffer_rsrc_t rc = mx_rsrc(p.codes + (ok ? n : 0) * (int64_t)(K / 2), ok ? K / 2 : 0);
-    const __amdgpu_buffer_rsrc_t rsc = mx_rsrc(p.scales + (ok ? n : 0) * (int64_t)nb, ok ? nb : 0);
+    // descriptors on the row step's first row (wave-uniform), covering its rows below N; this
+    // lane's row is an offset, and rows past N read zeros
+    const int64_t n0 = rs * kMxRpw;
+    const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(kMxRpw, p.N - n0));
+    const int64_t nbase = rows ? n0 : 0;
+    const __amdgpu_buffer_rsrc_t rc = mx_rsrc(p.codes + nbase * (int64_t)(K / 2), rows * (K / 2));
+    const __amdgpu_buffer_rsrc_t rsc = mx_rsrc(p.scales + nbase * (int64_t)nb, rows * nb);
 #pragma unroll
     for (int i = 0; i < kMxNbc; ++i) {
-      const int b = j + kMxLpr * (ch * kMxNbc + i);
-      // blocks past the row end read zeros (the descriptor holds exactly one row)
-      f.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, b * 16, 0, 2);
-      f.sc[i] = __builtin_amdgcn_raw_buffer_load_b8(rsc, b, 0, 2);
+      // blocks past the row end are skipped by compute (their loads read the next row or zeros)
+      const int b = min(j + kMxLpr * (ch * kMxNbc + i), nb - 1);
+      f.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, rsub * (K / 2) + b * 16, 0, 2);
+      f.sc[i] = __builtin_amdgcn_raw_buffer_load_b8(rsc, rsub * nb + b, 0, 2);
     }
   };
   float acc = 0.f;
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(kBlock) void k_mx_gemv(MxGemvParams p) {
 #pragma unroll
     for (int i = 0; i < kMxNbc; ++i) {
       const int b = j + kMxLpr * (ch * kMxNbc + i);
-      if (b < nb) acc = fmaf(e8m0_to_f32(f.sc[i]), mx_block_dot(f.q[i], xs, b), acc);
+      if (b < nb) acc += mx_block_dot(f.q[i], __uint_as_float(f.sc[i] << 23), xs + b * 4, nb * 4);
     }
     if (ch == nch - 1) {
       // the 16 lanes of a row
@@ -145,13 +154,18 @@ __global__ __launch_bounds__(kBlock) void k_mx_gemv(MxGemvParams p) {
     }
   };
   // two register sets, each unit's loads issued one unit ahead (static indexing: no scratch)
+  // every load is issued unconditionally (past the last unit it re-reads that unit), so the wait
+  // before each unit's products counts exactly the next unit's loads
   Unit fa, fb;
+  const int64_t ul = units > 0 ? units - 1 : 0;
   if (units > 0) load(0, fa);
   for (int64_t u = 0; u < units; u += 2) {
-    if (u + 1 < units) load(u + 1, fb);
+    load(std::min(u + 1, ul), fb);
+    __builtin_amdgcn_sched_barrier(0);
     compute(u, fa);
     if (u + 1 >= units) break;
-    if (u + 2 < units) load(u + 2, fa);
+    load(std::min(u + 2, ul), fa);
+    __builtin_amdgcn_sched_barrier(0);
     compute(u + 1, fb);
   }
 }
@@ -279,10 +293,11 @@ struct MxGemmParams {
 
 // One k-step's operands of one lane: three E4M3 terms of its X row (32 bytes each) with their
 // scale word, and the fp4 codes and scale of its column in each of the four column tiles.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 struct MxFrag {
-  u32x4 a[3][2];
+  i32x8 a[3];  // the two 16-byte halves of each term, already in operand order
   uint32_t as;
-  u32x4 b[4];
+  i32x4 b[4];
   uint32_t bs[4];
 };
 
@@ -293,17 +308,21 @@ struct MxFrag {
 // The scale of block h, for A and for B, is the scale byte of lane half h. The 32 x 32 result has
 // column l % 32 in lane l and rows (r % 4) + 8 (r / 4) + 4h in accumulator r.
 __global__ __launch_bounds__(kBlock, 2) void k_mx_gemm(MxGemmParams p) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: descriptors built from it stay scalar
   const int l32 = lane & 31, kh = lane >> 5;
   const int nbp = p.Kp / 32, nb = p.K / 32;
   const int64_t n0 = (int64_t)blockIdx.x * kMxTn;
   const int64_t m0 = (int64_t)blockIdx.y * kMxTm + 32 * wave;
   const int s0 = blockIdx.z * p.steps_per_split;
   const int s1 = min(p.Kp / 64, s0 + p.steps_per_split);
-  // A: this lane's X row; rows at or past M read zeros (the descriptor ends at row M)
-  const int64_t m = m0 + l32;
-  const __amdgpu_buffer_rsrc_t ra = mx_rsrc(p.xq + (m < p.M ? m : 0) * (int64_t)nbp * 96, m < p.M ? nbp * 96 : 0);
-  const __amdgpu_buffer_rsrc_t ras = mx_rsrc(p.xs + (m < p.M ? m : 0) * (int64_t)nbp, m < p.M ? nbp * 4 : 0);
+  // A: descriptors on the wave's first X row (wave-uniform) covering its rows below M; this
+  // lane's row is an offset, and rows at or past M read zeros
+  const int arows = (int)std::max<int64_t>(0, std::min<int64_t>(32, p.M - m0));
+  const int64_t abase = arows ? m0 : 0;
+  const __amdgpu_buffer_rsrc_t ra = mx_rsrc(p.xq + abase * (int64_t)nbp * 96, arows * nbp * 96);
+  const __amdgpu_buffer_rsrc_t ras = mx_rsrc(p.xs + abase * (int64_t)nbp, arows * nbp * 4);
+  const int arow_q = l32 * nbp * 96, arow_s = l32 * nbp * 4;
   // B: one descriptor per column tile covering its valid rows
   __amdgpu_buffer_rsrc_t rb[4], rbs[4];
 #pragma unroll
@@ -317,21 +336,15 @@ __global__ __launch_bounds__(kBlock, 2) void k_mx_gemm(MxGemmParams p) {
     const int kb = 2 * s + kh;
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      f.a[t][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, ((2 * s) * 3 + t) * 32 + 16 * kh, 0, 0);
-      f.a[t][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, ((2 * s + 1) * 3 + t) * 32 + 16 * kh, 0, 0);
+      const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, arow_q + ((2 * s) * 3 + t) * 32 + 16 * kh, 0, 0));
+      const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, arow_q + ((2 * s + 1) * 3 + t) * 32 + 16 * kh, 0, 0));
+      f.a[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    f.as = __builtin_amdgcn_raw_buffer_load_b32(ras, kb * 4, 0, 0);
+    f.as = __builtin_amdgcn_raw_buffer_load_b32(ras, arow_s + kb * 4, 0, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rb[j], l32 * (p.K / 2) + kb * 16, 0, 2);
+      f.b[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rb[j], l32 * (p.K / 2) + kb * 16, 0, 2));
       f.bs[j] = __builtin_amdgcn_raw_buffer_load_b8(rbs[j], l32 * nb + kb, 0, 2);
-    }
-    if (kb >= nb) {  // the zero half block past an odd number of blocks: weights zero, unit scale
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f.b[j] = u32x4{0u, 0u, 0u, 0u};
-        f.bs[j] = 127u;
-      }
     }
   };
   f32x16 acc[4];
@@ -339,36 +352,46 @@ __global__ __launch_bounds__(kBlock, 2) void k_mx_gemm(MxGemmParams p) {
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-  auto compute = [&](const MxFrag& f) {
-    i32x8 a[3];
-#pragma unroll
-    for (int t = 0; t < 3; ++t)
-      a[t] = i32x8{(int)f.a[t][0][0], (int)f.a[t][0][1], (int)f.a[t][0][2], (int)f.a[t][0][3],
-                   (int)f.a[t][1][0], (int)f.a[t][1][1], (int)f.a[t][1][2], (int)f.a[t][1][3]};
+  auto compute = [&](int s, const MxFrag& f) {
+    // the E2M1 operand uses the first four registers of the eight
     i32x8 bv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = i32x8{(int)f.b[j][0], (int)f.b[j][1], (int)f.b[j][2], (int)f.b[j][3], 0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) bv[j] = __builtin_shufflevector(f.b[j], f.b[j], 0, 1, 2, 3, -1, -1, -1, -1);
+    const i32x8* a = f.a;
+    // past an odd number of blocks, X is zero (every term) and the weights read there are finite
+    // codes of the next row; their scale is replaced by 1 so that a NaN scale byte there cannot
+    // reach the sum
+    const bool pad = 2 * s + kh >= nb;
+    uint32_t bs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bs[j] = pad ? 127u : f.bs[j];
     // A format 0 = E4M3, B format 4 = E2M1; the A scale of term t is byte t of the scale word.
     // Term-major order: four independent accumulators between two products into the same one.
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0], bv[j], acc[j], 0, 4, 0, (int)f.as, 0, (int)f.bs[j]);
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0], bv[j], acc[j], 0, 4, 0, (int)f.as, 0, (int)bs[j]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1], bv[j], acc[j], 0, 4, 1, (int)f.as, 0, (int)f.bs[j]);
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1], bv[j], acc[j], 0, 4, 1, (int)f.as, 0, (int)bs[j]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[2], bv[j], acc[j], 0, 4, 2, (int)f.as, 0, (int)f.bs[j]);
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[2], bv[j], acc[j], 0, 4, 2, (int)f.as, 0, (int)bs[j]);
   };
-  // two register sets, each k-step's loads issued one step ahead (static indexing: no scratch)
+  // two register sets, each k-step's loads issued one step ahead (static indexing: no scratch);
+  // every load is issued unconditionally (past the split it re-reads the split's last step), so
+  // the wait before each step's products counts exactly the next step's loads
   MxFrag f0, f1;
-  if (s0 < s1) load(s0, f0);
+  const int sl = max(s0, s1 - 1);
+  load(min(s0, sl), f0);
+  // (a scheduling barrier after each step's loads keeps them ahead of the products)
   for (int s = s0; s < s1; s += 2) {
-    if (s + 1 < s1) load(s + 1, f1);
-    compute(f0);
+    load(min(s + 1, sl), f1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s, f0);
     if (s + 1 >= s1) break;
-    if (s + 2 < s1) load(s + 2, f0);
-    compute(f1);
+    load(min(s + 2, sl), f0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s + 1, f1);
   }
   float* dst = p.out + (int64_t)blockIdx.z * p.M * p.N;
 #pragma unroll
