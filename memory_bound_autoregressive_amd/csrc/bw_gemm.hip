@@ -512,12 +512,18 @@ __global__ __launch_bounds__(kBlock) void k_gemm_epilogue(GemvParams p, int M, i
 }
 
 // argmax of each row of logits [M][N] (lowest index on ties; NaN never wins)
+// Per-row argmax of the batched logits in two passes: workgroup (c, m) scans chunk c of row m
+// (coalesced, ascending, so the first maximum of a thread is its lowest index) and writes its
+// (value, index) partial to val / idx [m][chunks]; k_argmax_final then reduces each row's partials
+// (lowest index on ties). NaN never wins; a row without a winner gives index 0.
 __global__ __launch_bounds__(kBlock) void k_argmax_rows(const float* __restrict__ logits, int64_t ld, int N,
-                                                       int32_t* __restrict__ out) {
-  const float* row = logits + (int64_t)blockIdx.x * ld;
+                                                       int chunk, float* __restrict__ val, int32_t* __restrict__ idx) {
+  const int m = blockIdx.y, c = blockIdx.x, chunks = gridDim.x;
+  const float* row = logits + (int64_t)m * ld;
+  const int i0 = c * chunk, i1 = min(N, i0 + chunk);
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < N; i += kBlock) {
+  for (int i = i0 + (int)threadIdx.x; i < i1; i += kBlock) {
     const float v = row[i];
     if (v > bv) { bv = v; bi = i; }
   }
@@ -534,7 +540,8 @@ __global__ __launch_bounds__(kBlock) void k_argmax_rows(const float* __restrict_
   if (threadIdx.x == 0) {
     for (int w = 1; w < 4; ++w)
       if (wv[w] > wv[0] || (wv[w] == wv[0] && wi[w] < wi[0])) { wv[0] = wv[w]; wi[0] = wi[w]; }
-    out[blockIdx.x] = wi[0] == 0x7fffffff ? 0 : wi[0];
+    val[(int64_t)m * chunks + c] = wv[0];
+    idx[(int64_t)m * chunks + c] = wi[0];
   }
 }
 
@@ -613,9 +620,15 @@ int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* r
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, int32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax_rows, dim3(M), dim3(kBlock), 0, s, logits, ld, N, out);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, float* val, int32_t* idx, int max_parts,
+                       int32_t* out, hipStream_t s) {
+  // about 2048 workgroups over all rows, chunks of at least 2048 columns
+  int chunks = std::max(1, std::min((2048 + M - 1) / M, (N + 2047) / 2048));
+  chunks = std::min(chunks, max_parts);
+  const int chunk = (N + chunks - 1) / chunks;
+  hipLaunchKernelGGL(k_argmax_rows, dim3(chunks, M), dim3(kBlock), 0, s, logits, ld, N, chunk, val, idx);
+  if (hipGetLastError() != hipSuccess) return -1;
+  return launch_argmax_final(val, idx, chunks, M, out, s);
 }
 
 }  // namespace bw

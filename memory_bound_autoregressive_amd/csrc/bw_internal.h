@@ -200,7 +200,9 @@ int64_t gemm_part_elems(int N, int K, int M);
 int launch_gemm(int in_mode, int epi, const GemvParams& p, int M, const float* rms, float* part, uint16_t* xs,
                 hipStream_t s);  // xs: [2][M][K] fp16 staging of X
 int launch_rowrms(const float* x, int64_t stride, int K, float eps, int M, float* r, hipStream_t s);
-int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, int32_t* out, hipStream_t s);
+// val / idx: at least M * max_parts partials (the lm_head's argmax workspace)
+int launch_argmax_rows(const float* logits, int64_t ld, int N, int M, float* val, int32_t* idx, int max_parts,
+                       int32_t* out, hipStream_t s);
 
 // greedy acceptance after a verify step (bw_spec.hip)
 int launch_spec_accept(int32_t* tokens, const int32_t* argmax, float* logits, int64_t V, int32_t* seq_lens,

@@ -1410,7 +1410,8 @@ static int enqueue_step(bw_model* m, bw_kv_pool* pool, const int32_t* tokens, co
   if (run_dense(m, IN_RMSNORM, EPI_LOGITS, lm, M, s, &lm_grid)) return fail(BW_EHIP, "lm_head launch failed");
   trace_mark(m, BW_K_LM_HEAD, 0, 1, s);
   if (batched(m, lm.w, M)) {
-    if (argmax_out && launch_argmax_rows(lm.y, lm.y_stride, c.vocab, M, argmax_out, s))
+    if (argmax_out && launch_argmax_rows(lm.y, lm.y_stride, c.vocab, M, m->amax_val, m->amax_idx, m->lm_parts,
+                                         argmax_out, s))
       return fail(BW_EHIP, "argmax launch failed");
     return BW_OK;
   }
