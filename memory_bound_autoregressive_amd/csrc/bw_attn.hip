@@ -25,6 +25,7 @@
 #include "bw_common.h"
 #include "bw_internal.h"
 #include "bw_lanes.h"
+#include "bw_mfma.h"
 
 #include <type_traits>
 
@@ -247,41 +248,6 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
 // so each product term is exact in fp32 and only the summation order differs from the VALU
 // kernel: Q in three bf16 parts (residual below 2^-26 of |q|; a score scales q by up to a few
 // hundred) or two fp16 parts (2^-22), P in two parts (2^-17 for bf16). Rows past QR are padding.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <int KVDT>
-struct MfmaT;
-template <>
-struct MfmaT<1> {  // fp16 cache
-  typedef _Float16 e8 __attribute__((ext_vector_type(8)));
-  typedef _Float16 e4 __attribute__((ext_vector_type(4)));
-  static __device__ __forceinline__ f32x4 mm32(e8 a, e8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 mm16(e4 a, e4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct MfmaT<2> {  // bf16 cache
-  typedef __bf16 e8 __attribute__((ext_vector_type(8)));
-  typedef short e4 __attribute__((ext_vector_type(4)));
-  static __device__ __forceinline__ f32x4 mm32(e8 a, e8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 mm16(e4 a, e4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-  }
-};
-
-// Round to the cache dtype, nearest even, with the hardware conversion (v_cvt_pk_bf16_f32 for
-// bf16); used for the query and probability parts, which no stored value depends on.
-template <int KVDT>
-__device__ __forceinline__ uint16_t part_bits(float x) {
-  if constexpr (KVDT == 1) return f32_to_f16(x);
-  else return __builtin_bit_cast(uint16_t, (__bf16)x);
-}
-
 constexpr int kVStride = 136;  // LDS row of a staged V page, in 16-bit elements (272 B: conflict-free reads)
 constexpr int kMfmaMaxPps = 128;  // most pages of one split of the matrix-core kernel
 

@@ -20,6 +20,17 @@ __device__ __forceinline__ float sum8(float v) {
 }
 // the value of lane ^ 8 (rotation by 8 within the row of 16)
 __device__ __forceinline__ float xor8(float v) { return dpp_mov<0x128>(v); }
+// rotations within each row of 16 lanes (DPP row_ror: lane i receives lane (i - n) mod 16)
+template <int N>
+__device__ __forceinline__ float row_to(float v) {  // lane i gets lane i - N (mod 16)
+  static_assert(N > 0 && N < 16, "rotation by 1..15");
+  return dpp_mov<0x120 + N>(v);
+}
+template <int N>
+__device__ __forceinline__ float row_from(float v) {  // lane i gets lane i + N (mod 16)
+  static_assert(N > 0 && N < 16, "rotation by 1..15");
+  return dpp_mov<0x120 + 16 - N>(v);
+}
 // (v of the even row, v of the odd row) of each pair of 16-lane rows (0, 1), (2, 3)
 __device__ __forceinline__ float2 pair16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -37,10 +37,12 @@
 // (xx across a step boundary) or 3 (the others across a step boundary). The argmax partials are
 // written once per step and carry the epoch itself (difference 1).
 #include <algorithm>
+#include <type_traits>
 
 #include "bw_common.h"
 #include "bw_dot.h"
 #include "bw_lanes.h"
+#include "bw_mfma.h"
 #include "bw_internal.h"
 
 namespace bw {
@@ -546,21 +548,33 @@ __device__ __forceinline__ void pload_moe_dn(int tid, const uint64_t* mp, int d,
 // ---- attention over the paged cache -----------------------------------------------------------
 
 // K and V of one page for KV head g, as buffer loads on the layer's pool slice (an invalid page id
-// reads zeros without touching memory). Lane layout as in the chain's attention kernel: scores use
-// 8 tokens x 8 lanes per pass (2 passes), values 4 token groups x 16 lanes.
+// reads zeros without touching memory). K is loaded as the A operand of the score products: lane
+// l holds token l % 16 and, per 32-dim chunk c, the 8 dims kdim(c, l / 16) ..+7 (16-bit caches:
+// one 16-byte load per chunk; FP8: one 16-byte load per two chunks, dims 64 u + 16 (l / 16) ..+15).
+// V is loaded as 16-byte pieces for staging in LDS: piece k = l + 64 u holds token k / (D / 8),
+// dims 8 (k % (D / 8)) ..+7 (FP8: token k / (D / 16), dims 16 (k % (D / 16)) ..+15).
 template <int D, int KVDT>
 struct PageRegs {
-  static constexpr int DL = D / 8, NV = D / 8, TG = kWave / NV, TPL = kPageTokens / TG, NCH = DL / 8;
-  typename KvT<KVDT>::C8 k[2][NCH];
-  typename KvT<KVDT>::C8 v[TPL];
+  static constexpr int NC = D / 32;                          // 32-dim chunks of the scores
+  static constexpr int NK = KVDT == 3 ? NC / 2 : NC;         // K loads per lane
+  static constexpr int NVL = KVDT == 3 ? D / 64 : D / 32;    // V loads per lane
+  u32x4 k[NK];
+  u32x4 v[NVL];
 };
+
+// head dims of the 8 K elements a lane holds in chunk c (lane group grp = lane / 16); a score sums
+// over all dims, so any order that K and the query parts share gives the same sum
+template <int KVDT>
+__device__ __forceinline__ int kdim(int c, int grp) {
+  return KVDT == 3 ? 64 * (c >> 1) + 16 * grp + 8 * (c & 1) : 32 * c + 8 * grp;
+}
 
 template <int D, int KVDT>
 __device__ __forceinline__ void load_page(int lane, const typename KvT<KVDT>::E* pool, int64_t page_elems,
                                           int n_pages, int page, int g, PageRegs<D, KVDT>& pr) {
   using PR = PageRegs<D, KVDT>;
   constexpr int ES = KvT<KVDT>::ES;
-  const int sc_tok = lane >> 3, sc_c = lane & 7, v_c = lane % PR::NV, v_tg = lane / PR::NV;
+  const int c16 = lane & 15, grp = lane >> 4;
   // the descriptor covers this KV head's K and V of the page, or no bytes for an invalid page id
   // (every load then reads zeros): the offsets need no selection, which the compiler would turn
   // into a branch around each load and a wait for every load in flight at the join
@@ -568,16 +582,24 @@ __device__ __forceinline__ void load_page(int lane, const typename KvT<KVDT>::E*
   const __amdgpu_buffer_rsrc_t r =
       uniform_rsrc(pool + (ok ? (int64_t)page * page_elems + (int64_t)(g * 2) * kPageTokens * D : 0),
                    ok ? 2 * kPageTokens * D * ES : 0);
-  auto ld = [&](int elem) {  // 8 elements: 16 bytes, or 8 for FP8
-    if constexpr (KVDT == 3) return __builtin_amdgcn_raw_buffer_load_b64(r, elem, 0, 0);
-    else return __builtin_amdgcn_raw_buffer_load_b128(r, elem * 2, 0, 0);
-  };
+  if constexpr (KVDT == 3) {
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps)
+    for (int u = 0; u < PR::NK; ++u) pr.k[u] = __builtin_amdgcn_raw_buffer_load_b128(r, c16 * D + 64 * u + 16 * grp, 0, 0);
 #pragma unroll
-    for (int ch = 0; ch < PR::NCH; ++ch) pr.k[ps][ch] = ld((ps * 8 + sc_tok) * D + sc_c * PR::DL + ch * 8);
+    for (int u = 0; u < PR::NVL; ++u) {
+      const int k = lane + 64 * u;
+      pr.v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, kPageTokens * D + (k / (D / 16)) * D + 16 * (k % (D / 16)), 0, 0);
+    }
+  } else {
 #pragma unroll
-  for (int u = 0; u < PR::TPL; ++u) pr.v[u] = ld(kPageTokens * D + (v_tg + u * PR::TG) * D + v_c * 8);
+    for (int c = 0; c < PR::NK; ++c)
+      pr.k[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c16 * D + 32 * c + 8 * grp) * 2, 0, 0);
+#pragma unroll
+    for (int u = 0; u < PR::NVL; ++u) {
+      const int k = lane + 64 * u;
+      pr.v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (kPageTokens * D + (k / (D / 8)) * D + 8 * (k % (D / 8))) * 2, 0, 0);
+    }
+  }
 }
 
 // 8 elements of the new token's key or value (cache dtype bits staged in LDS)
@@ -588,14 +610,16 @@ __device__ __forceinline__ typename KvT<KVDT>::C8 lds_chunk8(const uint16_t* bit
 
 // ---- parameters -------------------------------------------------------------------------------
 
+constexpr int kVPitch = 8;  // LDS row of a staged V page: D + 8 16-bit elements (conflict-free transpose reads)
+
 template <int D, int QR>
 struct alignas(16) AttnLds {
   float q[QR * D];
-  float p[kPW][QR][kPageTokens];
   float m[kPW][QR], l[kPW][QR];
   float acc[kPW][QR * D];
   alignas(16) uint16_t knew[D];  // cache dtype bits (the first D bytes for FP8)
   alignas(16) uint16_t vnew[D];
+  alignas(16) uint16_t vst[kPW][kPageTokens * (D + kVPitch)];  // each wave's staged V page (16-bit)
 };
 
 // ---- the kernel -------------------------------------------------------------------------------
@@ -785,22 +809,33 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     }
 
     // ================= ATTENTION (KV head ag, split as) =================
+    // Both products of a page on the matrix cores (16 x 16 tiles):
+    // - scores^T = K Q^T: K (16 tokens x 32 dims per product) as the A operand; the B operand's
+    //   columns 2h and 2h + 1 hold the hi and lo parts of query head h (16 significant bits), so
+    //   head h's scores are the sum of result columns 2h and 2h + 1 (adjacent lanes);
+    // - O += P V: P (rows 2h and 2h + 1: the hi and lo parts of head h's probabilities) as the A
+    //   operand, V (16 tokens x 16 dims) as the B operand, read from the wave's staged page with
+    //   transposing LDS reads; rows 2h and 2h + 1 of the result sit in one lane and add up there.
+    // Lane l of a 16 x 16 result holds column l % 16, rows 4 (l / 16) ..+3.
     stamp(p, l * 16 + 2);
     {
       const int tid = phase_tid();
       const int lane = tid & 63, wave = wave_of(tid);
-      (void)lane;
-      (void)wave;
-      constexpr int DL = D / 8, NV = D / 8, TG = kWave / NV, TPL = kPageTokens / TG, NCH = DL / 8;
-      const int rep = H / G;
+      constexpr int MT = KVDT == 3 ? 2 : KVDT;  // an FP8 cache is widened to bf16 (exact)
+      using MM = MfmaT<MT>;
+      typedef typename MM::e8 e8;
+      typedef typename MM::e4 e4;
+      typedef typename std::remove_reference<decltype(e8{}[0])>::type el8;
+      typedef typename std::remove_reference<decltype(e4{}[0])>::type el4;
+      using PR = PageRegs<D, KVDT>;
+      constexpr int NC = D / 32, NV16 = D / 16, VP = D + kVPitch;
+      static_assert(2 * QR <= 16, "two parts per query head fit one 16-wide tile");
+      const int c16 = lane & 15, grp = lane >> 4;
       const bool active = ag < G;
       const int pg0 = apg0, pg1 = apg1;
       const int pg_new = pos / kPageTokens, slot_new = pos % kPageTokens;
-      const int sc_tok = lane >> 3, sc_c = lane & 7, v_c = lane % NV, v_tg = lane / NV;
       int pg = pg0 + wave;
       int page = first_page;
-      typename KvT<KVDT>::C8 (&kraw)[2][NCH] = kv_first.k;
-      typename KvT<KVDT>::C8 (&vraw)[TPL] = kv_first.v;
       // q rows of this KV head and the new key / value
       if (active) {
         const __amdgpu_buffer_rsrc_t r = xrsrc(p.xq, (int64_t)Nq * 4);
@@ -812,7 +847,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           const int e = tid + i * kPT;
           if (e < QR * D) {
             const int qr = e / D, dd = e - qr * D;
-            idx[i] = (ag * rep + qr) * D + dd;
+            idx[i] = (ag * QR + qr) * D + dd;
           } else if (e < QR * D + 2 * D) {
             const int e2 = e - QR * D, which = e2 / D, dd = e2 - which * D;
             idx[i] = HD + which * GD + ag * D + dd;
@@ -838,119 +873,149 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       __syncthreads();
       stamp(p, l * 16 + 3);
       if (bail) return;
-      float mrun[QR], lrun[QR], acc[QR][8];
+      // the query parts as the B operand: column c16 = 2h + part, dims kdim(c, grp) ..+7
+      e8 qp[NC];
+      {
+        const int qh = c16 >> 1, lo_part = c16 & 1;
+        const bool qcol = qh < QR;
 #pragma unroll
-      for (int qr = 0; qr < QR; ++qr) {
-        mrun[qr] = -INFINITY;
-        lrun[qr] = 0.f;
+        for (int c = 0; c < NC; ++c) {
+          const float* qs = al.q + (qcol ? qh : 0) * D + kdim<KVDT>(c, grp);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[qr][e] = 0.f;
+          for (int e = 0; e < 8; ++e) {
+            const float x = qcol ? qs[e] : 0.f;
+            const uint16_t hb = part_bits<MT>(x);
+            const uint16_t lb = part_bits<MT>(x - kv_to_f32<MT>(hb));
+            qp[c][e] = __builtin_bit_cast(el8, qcol ? (lo_part ? lb : hb) : (uint16_t)0);
+          }
+        }
       }
+      float mrun = -INFINITY, lrun = 0.f;  // of head c16 / 2 (even lanes with c16 < 2 QR)
+      bool first = true;                   // no page computed yet: the accumulators are zero
+      f32x4 o[NV16];
+#pragma unroll
+      for (int c = 0; c < NV16; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      uint16_t* vl = al.vst[wave];
+      const uint16_t* vrow = vl + (4 * grp + (c16 >> 2)) * VP + 4 * (c16 & 3);
+      // the rows of the probability operand: row c16 = part c16 & 1 of head c16 / 2; zero beyond 2 QR
+      const int prow_part = c16 < 2 * QR ? (c16 & 1) : 2;
       for (; active && pg < pg1; pg += kPW) {
         const bool valid = page >= 0 && page < p.n_pages;
         if (!valid && lane == 0) atomicOr(p.err, 1);
         const int pgn = pg + kPW;
         const int page_n = pgn < pg1 ? s.pgid[pgn - pg0] : -1;
         if (pg == pg_new) {  // the new token's slot comes from the exchange
+          if (c16 == slot_new) {
 #pragma unroll
-          for (int ps = 0; ps < 2; ++ps)
-            if (ps * 8 + sc_tok == slot_new)
+            for (int u = 0; u < PR::NK; ++u)
+              kv_first.k[u] = *(const u32x4*)((const KE*)al.knew + (KVDT == 3 ? 64 * u + 16 * grp : 32 * u + 8 * grp));
+          }
 #pragma unroll
-              for (int ch = 0; ch < NCH; ++ch) kraw[ps][ch] = lds_chunk8<KVDT>(al.knew, sc_c * DL + ch * 8);
-#pragma unroll
-          for (int u = 0; u < TPL; ++u)
-            if (v_tg + u * TG == slot_new) vraw[u] = lds_chunk8<KVDT>(al.vnew, v_c * 8);
+          for (int u = 0; u < PR::NVL; ++u) {
+            const int k = lane + 64 * u;
+            const int tk = KVDT == 3 ? k / (D / 16) : k / (D / 8);
+            const int d0 = KVDT == 3 ? 16 * (k % (D / 16)) : 8 * (k % (D / 8));
+            if (tk == slot_new) kv_first.v[u] = *(const u32x4*)((const KE*)al.vnew + d0);
+          }
         }
         if (valid) {
-          float sc[2][QR];
+          // stage V (this wave's buffer; a wave's LDS operations run in order); slots past the
+          // sequence end are zeros, so stale contents never meet a zero probability
+          const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int ps = 0; ps < 2; ++ps) {
-            const int j = pg * kPageTokens + ps * 8 + sc_tok;
-            float kf[DL];
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) kv_unpack8<KVDT>(kraw[ps][ch], kf + ch * 8);
-#pragma unroll
-            for (int qr = 0; qr < QR; ++qr) {
-              float dot = 0.f;
-#pragma unroll
-              for (int e = 0; e < DL; ++e) dot = fmaf(al.q[qr * D + sc_c * DL + e], kf[e], dot);
-              dot = sum8(dot);  // the 8 lanes of token sc_tok
-              sc[ps][qr] = j < kv_len ? dot : -INFINITY;
+          for (int u = 0; u < PR::NVL; ++u) {
+            const int k = lane + 64 * u;
+            if constexpr (KVDT == 3) {
+              const int tk = k / (D / 16);
+              const bool live = pg * kPageTokens + tk < kv_len;
+              uint16_t* dst = vl + tk * VP + 16 * (k % (D / 16));
+              *(u32x4*)dst = live ? fp8x8_to_bf16x8(u32x2{kv_first.v[u][0], kv_first.v[u][1]}) : z;
+              *(u32x4*)(dst + 8) = live ? fp8x8_to_bf16x8(u32x2{kv_first.v[u][2], kv_first.v[u][3]}) : z;
+            } else {
+              const int tk = k / (D / 8);
+              *(u32x4*)(vl + tk * VP + 8 * (k % (D / 8))) = pg * kPageTokens + tk < kv_len ? kv_first.v[u] : z;
             }
           }
+          // scores^T
+          f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int qr = 0; qr < QR; ++qr) {
-            float pm = fmaxf(sc[0][qr], sc[1][qr]);
-            pm = fmaxf(pm, xor8(pm));
-            pm = max_xor16(pm);
-            pm = max_xor32(pm);
-            const float mnew = fmaxf(mrun[qr], pm);
-            float p0 = 0.f, p1 = 0.f, alpha = 1.f;
-            if (mnew != -INFINITY) {
-              p0 = __expf(sc[0][qr] - mnew);
-              p1 = __expf(sc[1][qr] - mnew);
-              alpha = __expf(mrun[qr] - mnew);
-            }
-            float ps_ = p0 + p1;
-            ps_ += xor8(ps_);
-            ps_ = sum_xor16(ps_);
-            ps_ = sum_xor32(ps_);
-            lrun[qr] = lrun[qr] * alpha + ps_;
-            mrun[qr] = mnew;
+          for (int c = 0; c < NC; ++c) {
+            u32x4 kr;
+            if constexpr (KVDT == 3)
+              kr = fp8x8_to_bf16x8((c & 1) ? u32x2{kv_first.k[c >> 1][2], kv_first.k[c >> 1][3]}
+                                           : u32x2{kv_first.k[c >> 1][0], kv_first.k[c >> 1][1]});
+            else
+              kr = kv_first.k[c];
+            sc = MM::mm32(__builtin_bit_cast(e8, kr), qp[c], sc);
+          }
+          // even lane c16 = 2h: head h's scores are its column plus the next lane's
+          float sv[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[qr][e] *= alpha;
-            if (sc_c == 0) {
-              al.p[wave][qr][sc_tok] = p0;
-              al.p[wave][qr][8 + sc_tok] = p1;
+          for (int i = 0; i < 4; ++i) {
+            const float t = sc[i] + row_from<1>(sc[i]);
+            const int j = pg * kPageTokens + 4 * grp + i;
+            sv[i] = j < kv_len ? t : -INFINITY;
+          }
+          float pm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          pm = max_xor32(max_xor16(pm));
+          const float mnew = fmaxf(mrun, pm);
+          float pv[4], psum = 0.f, alpha = 1.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pv[i] = mnew == -INFINITY ? 0.f : __expf(sv[i] - mnew);
+            psum += pv[i];
+          }
+          if (mnew != -INFINITY) alpha = __expf(mrun - mnew);
+          psum = sum_xor32(sum_xor16(psum));
+          lrun = lrun * alpha + psum;
+          mrun = mnew;
+          // the probability operand: odd lane 2h + 1 takes head h's values from lane 2h
+          e4 pa;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float ph = pv[i], pl = row_to<1>(pv[i]);  // pl: the even neighbour's value
+            const float x = prow_part == 0 ? ph : pl;
+            const uint16_t hb = part_bits<MT>(x);
+            const uint16_t lb = part_bits<MT>(x - kv_to_f32<MT>(hb));
+            pa[i] = __builtin_bit_cast(el4, prow_part == 0 ? hb : (prow_part == 1 ? lb : (uint16_t)0));
+          }
+          // rescale the accumulators when a running max moved (never on the first page, whose
+          // accumulators are zero): rows 2h and 2h + 1 take head h's factor from lane 2h
+          if (!first && __ballot(c16 < 2 * QR && alpha != 1.f) != 0) {
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              const float a = __shfl(alpha, (lane & ~15) | (4 * grp + i));
+#pragma unroll
+              for (int c = 0; c < NV16; ++c) {
+                o[c][i] *= a;
+                o[c][i + 1] *= a;
+              }
             }
           }
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          first = false;
+          typedef short s4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-          for (int u = 0; u < TPL; ++u) {
-            const int tok = v_tg + u * TG;
-            const int j = pg * kPageTokens + tok;
-            float vf[8];
-            kv_unpack8<KVDT>(vraw[u], vf);
-            const bool live = j < kv_len;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vf[e] = live ? vf[e] : 0.f;
-#pragma unroll
-            for (int qr = 0; qr < QR; ++qr) {
-              const float pw = al.p[wave][qr][tok];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[qr][e] = fmaf(pw, vf[e], acc[qr][e]);
-            }
+          for (int c = 0; c < NV16; ++c) {
+            const s4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vrow + 16 * c));
+            o[c] = MM::mm16(pa, __builtin_bit_cast(e4, t), o[c]);
           }
-          __builtin_amdgcn_wave_barrier();
         }
         page = page_n;
         load_page<D, KVDT>(lane, pool, p.page_elems, p.n_pages, pgn < pg1 ? page : -1, ag, kv_first);
       }
       if constexpr (!MOE) stamp(p, l * 16 + 12);  // MoE: the down phase's slot
-      // reduce the value partials over the token groups, then merge the waves
-      static_assert(NV == 8 || NV == 16, "value lanes per token group: 8 or 16");
+      // rows 2h (hi) and 2h + 1 (lo) of head h add up in the lane; then the waves merge in LDS
 #pragma unroll
-      for (int qr = 0; qr < QR; ++qr)
+      for (int i = 0; i < 4; i += 2) {
+        const int h = 2 * grp + (i >> 1);
+        if (h < QR) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float a = acc[qr][e];
-          if constexpr (NV == 8) a += xor8(a);
-          acc[qr][e] = sum_xor32(sum_xor16(a));
+          for (int c = 0; c < NV16; ++c) al.acc[wave][h * D + 16 * c + c16] = o[c][i] + o[c][i + 1];
         }
-      if (v_tg == 0) {
-#pragma unroll
-        for (int qr = 0; qr < QR; ++qr)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) al.acc[wave][qr * D + v_c * 8 + e] = acc[qr][e];
       }
-      if (lane == 0) {
-#pragma unroll
-        for (int qr = 0; qr < QR; ++qr) {
-          al.m[wave][qr] = mrun[qr];
-          al.l[wave][qr] = lrun[qr];
-        }
+      if (grp == 0 && c16 < 2 * QR && (c16 & 1) == 0) {
+        al.m[wave][c16 >> 1] = mrun;
+        al.l[wave][c16 >> 1] = lrun;
       }
       __syncthreads();
       if constexpr (!MOE) stamp(p, l * 16 + 13);
@@ -969,7 +1034,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
               lsum = fmaf(al.l[v][qr], f, lsum);
             }
           }
-          const int h = ag * rep + qr;
+          const int h = ag * QR + qr;
           uint32_t* dst = p.xp + ((int64_t)h * S + as) * (D + 2);
           xstore(dst, dd, a, tout);
           if (dd == 0) {
