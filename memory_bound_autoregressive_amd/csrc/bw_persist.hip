@@ -614,7 +614,7 @@ constexpr int kVPitch = 8;  // LDS row of a staged V page: D + 8 16-bit elements
 
 template <int D, int QR>
 struct alignas(16) AttnLds {
-  float q[QR * D];
+  alignas(16) uint16_t qpart[2][QR * D];  // the scaled query rows as hi and lo parts (16-bit operand type)
   float m[kPW][QR], l[kPW][QR];
   float acc[kPW][QR * D];
   alignas(16) uint16_t knew[D];  // cache dtype bits (the first D bytes for FP8)
@@ -861,7 +861,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         for (int i = 0; i < NQW; ++i) {
           const int e = tid + i * kPT;
           if (e < QR * D) {
-            al.q[e] = xdec(word[i]) * p.attn_scale;
+            const float x = xdec(word[i]) * p.attn_scale;
+            const uint16_t hb = part_bits<MT>(x);
+            al.qpart[0][e] = hb;
+            al.qpart[1][e] = part_bits<MT>(x - kv_to_f32<MT>(hb));
           } else if (e < QR * D + 2 * D) {
             const int e2 = e - QR * D, which = e2 / D, dd = e2 - which * D;
             const uint16_t bits = f32_to_kv<KVDT>(xdec(word[i]));
@@ -876,18 +879,13 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       // the query parts as the B operand: column c16 = 2h + part, dims kdim(c, grp) ..+7
       e8 qp[NC];
       {
-        const int qh = c16 >> 1, lo_part = c16 & 1;
+        const int qh = c16 >> 1;
         const bool qcol = qh < QR;
+        const uint16_t* qs = al.qpart[c16 & 1] + (qcol ? qh : 0) * D;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const float* qs = al.q + (qcol ? qh : 0) * D + kdim<KVDT>(c, grp);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = qcol ? qs[e] : 0.f;
-            const uint16_t hb = part_bits<MT>(x);
-            const uint16_t lb = part_bits<MT>(x - kv_to_f32<MT>(hb));
-            qp[c][e] = __builtin_bit_cast(el8, qcol ? (lo_part ? lb : hb) : (uint16_t)0);
-          }
+          const u32x4 v = *(const u32x4*)(qs + kdim<KVDT>(c, grp));
+          qp[c] = __builtin_bit_cast(e8, qcol ? v : u32x4{0u, 0u, 0u, 0u});
         }
       }
       float mrun = -INFINITY, lrun = 0.f;  // of head c16 / 2 (even lanes with c16 < 2 QR)

@@ -70,7 +70,7 @@ def _one(path: str, kernel: str, counter: str) -> float:
 
 # sources of the GEMV kernels of the kernel chain, and of the single-launch step
 GEMV_SOURCES = ("bw_gemv.hip", "bw_common.h", "bw_dot.h", "bw_internal.h")
-STEP_SOURCES = ("bw_persist.hip", "bw_common.h", "bw_dot.h", "bw_lanes.h", "bw_internal.h")
+STEP_SOURCES = ("bw_persist.hip", "bw_common.h", "bw_dot.h", "bw_lanes.h", "bw_mfma.h", "bw_internal.h")
 
 
 def _copy(path: str, kernel: str, counter: str) -> float:
