@@ -66,6 +66,49 @@ def algorithmic_bytes(cfg: dict, ctx_mean: float) -> dict:
             "embed": embed, "total": weights + kv_read + kv_write + router + embed}
 
 
+# phase start / input-ready stamp slots of one layer in the single-launch step's record (16 per layer)
+DENSE_PHASES = [("qkv", 0, 1), ("attention", 2, 3), ("merge", 4, 5), ("o", 6, 7), ("gate_up", 8, 9), ("down", 10, 11)]
+MOE_PHASES = [("qkv", 0, 1), ("attention", 2, 3), ("merge", 4, 5), ("o", 6, 7), ("router", 8, 9),
+              ("topk_gate_up", 10, 11), ("down", 12, 13)]
+
+
+def stamp_phases(run_once, L: int, moe: bool, n: int = 8) -> dict:
+    """Per-layer wait ("wait_us": phase start until its input is in LDS) and work ("work_us": the
+    rest, until the next phase starts) of each phase of the single-launch step, averaged over the
+    layers of n steps, from workgroup 0's GPU real-time-counter stamps. run_once(stamps) runs one
+    step with the stamp record `stamps` (int64 device tensor of L * 16 + 8) attached."""
+    import numpy as np
+    import torch
+    slots = MOE_PHASES if moe else DENSE_PHASES
+    st = torch.zeros(L * 16 + 8, dtype=torch.int64, device="cuda")
+    acc = np.zeros((len(slots), 2))
+    lm = np.zeros(2)
+    att = np.zeros(3)
+    for _ in range(n):
+        run_once(st)
+        torch.cuda.synchronize()
+        v = st.cpu().numpy().astype(np.float64) / 100.0  # us (100 MHz counter)
+        per = v[:L * 16].reshape(L, 16)
+        for i, (_, a, b) in enumerate(slots):
+            if i + 1 < len(slots):
+                end = per[:, slots[i + 1][1]]
+            else:  # the next layer's first phase, or the lm_head after the last layer
+                end = np.concatenate([per[1:, slots[0][1]], [v[L * 16]]])
+            acc[i, 0] += np.mean(per[:, b] - per[:, a])
+            acc[i, 1] += np.mean(end - per[:, b])
+        lm += [v[L * 16 + 1] - v[L * 16], v[L * 16 + 3] - v[L * 16 + 1]]
+        if not moe:  # attention work: page loop, wave reductions + barrier, cross-wave merge + stores
+            att += [np.mean(per[:, 12] - per[:, 3]), np.mean(per[:, 13] - per[:, 12]), np.mean(per[:, 4] - per[:, 13])]
+    out = {k: {"wait_us": round(float(acc[i, 0] / n), 2), "work_us": round(float(acc[i, 1] / n), 2)}
+           for i, (k, _, _) in enumerate(slots)}
+    out["lm_head"] = {"wait_us": round(float(lm[0] / n), 2), "work_us": round(float(lm[1] / n), 2)}
+    if not moe:
+        out["attention"]["work_split_us"] = {"page_loop": round(float(att[0] / n), 2),
+                                             "wave_reduce": round(float(att[1] / n), 2),
+                                             "merge_store": round(float(att[2] / n), 2)}
+    return out
+
+
 def cpu_model() -> str:
     """The host CPU's model name (first processor in /proc/cpuinfo)."""
     try:
@@ -345,7 +388,8 @@ def run_workload(args) -> int:
     else:
         B, t = 1, 1
         lens = [cfg.get("context", cfg.get("prompt"))]
-        s = Session(cfg, seed=seed, max_len=[lens[0] + W + K + 2 + 32], max_tokens=1, pool_seed=seed + 1)
+        # + 32 + 8: the traced pass and the phase-stamp pass after the timed steps
+        s = Session(cfg, seed=seed, max_len=[lens[0] + W + K + 2 + 32 + 8], max_tokens=1, pool_seed=seed + 1)
         s.synthesize(seed + 7, lens)
     single = bool(bw.bw_set_single_launch(s.model, 0 if args.chain else 1)) and not args.chain and B * t == 1
     torch.cuda.synchronize()
@@ -389,7 +433,7 @@ def run_workload(args) -> int:
     committed = int(count.sum().item()) - c0
     ctx1 = seq_lens.cpu().numpy().astype(np.float64)
     kv_pos_layer = 2 * cfg["n_kv_heads"] * cfg["head_dim"] * kv_bytes(cfg)  # bytes per cached position and layer
-    roofline, roofline_mfma, kernel_us = None, None, {}
+    roofline, roofline_mfma, kernel_us, phases = None, None, {}, None
     if single and not args.no_trace:
         # the step is one kernel launch: events around the decode call only
         n_tr = 32
@@ -404,6 +448,19 @@ def run_workload(args) -> int:
                     "bytes_per_launch": round(bytes_tr), "avg_launch_us": round(launch_us, 2),
                     "context_mean": ctx_tr}
         kernel_us["k_persist"] = round(launch_us, 2)
+        L = cfg["n_layers"]
+
+        def run_stamped(st):
+            bw.bw_debug_single_launch_stamps(s.model, st, L * 16 + 8)
+            step()
+
+        phases = stamp_phases(run_stamped, L, moe=cfg.get("n_experts", 0) > 0)
+        bw.bw_debug_single_launch_stamps(s.model, None)
+        if bw.bw_check_device_error(s.model) != 0:
+            print("[bench] device error flag set in the traced passes", file=sys.stderr)
+            return 1
+        print(f"[bench] {args.workload}: k_persist {launch_us:.1f} us per launch; phases {phases}", file=sys.stderr,
+              flush=True)
     elif t > 1 and not args.no_trace:
         # per-layer launch time of the attention (matrix-core split + merge) and the gate/up GEMM
         L = cfg["n_layers"]
@@ -474,7 +531,7 @@ def run_workload(args) -> int:
                    "context_sum_start": int(ctx0.sum()), "seed": seed},
         "achieved_hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_step": round(per_step), "committed_tokens_per_s": round(committed * 1000.0 / (ms_per_step * K), 1),
-        "kernel_us": kernel_us, "roofline": roofline,
+        "kernel_us": kernel_us, "phases": phases, "roofline": roofline,
     }
     if roofline_mfma is not None:
         out["roofline_mfma"] = roofline_mfma
@@ -768,35 +825,13 @@ def main() -> int:
         kernel_us["k_persist"] = round(launch_us, 2)
         # per-phase timeline of one workgroup (GPU real-time counter stamps)
         L = cfg["n_layers"]
-        st = torch.zeros(L * 16 + 8, dtype=torch.int64, device=dev)
-        bw.bw_debug_single_launch_stamps(s.model, st, L * 16 + 8)
-        acc = np.zeros((L, 6, 2))
-        att = np.zeros(3)  # attention work: page loop, wave reductions + barrier, cross-wave merge + stores
-        lm = np.zeros(2)
-        n_ph = 8
-        for _ in range(n_ph):
+
+        def run_stamped(st):
+            bw.bw_debug_single_launch_stamps(s.model, st, L * 16 + 8)
             step(feed_back=True)
-            torch.cuda.synchronize()
-            v = st.cpu().numpy().astype(np.float64) / 100.0  # us
-            ph = v[:L * 16].reshape(L, 8, 2)[:, :6, :]
-            starts = ph[:, :, 0]
-            nxt = np.concatenate([starts[:, 1:], np.concatenate([starts[1:, :1], [[v[L * 16]]]])], axis=1)
-            acc[:, :, 0] += ph[:, :, 1] - ph[:, :, 0]
-            acc[:, :, 1] += nxt - ph[:, :, 1]
-            lm += [v[L * 16 + 1] - v[L * 16], v[L * 16 + 3] - v[L * 16 + 1]]
-            a3, a12, a13, a4 = v[:L * 16].reshape(L, 16)[:, [3, 12, 13, 4]].T
-            att += [np.mean(a12 - a3), np.mean(a13 - a12), np.mean(a4 - a13)]
+
+        phases = stamp_phases(run_stamped, L, moe=False)
         bw.bw_debug_single_launch_stamps(s.model, None)
-        acc /= n_ph
-        lm /= n_ph
-        names = ["qkv", "attention", "merge", "o", "gate_up", "down"]
-        phases = {k: {"wait_us": round(float(acc[:, i, 0].mean()), 2), "work_us": round(float(acc[:, i, 1].mean()), 2)}
-                  for i, k in enumerate(names)}
-        phases["lm_head"] = {"wait_us": round(float(lm[0]), 2), "work_us": round(float(lm[1]), 2)}
-        att /= n_ph
-        phases["attention"]["work_split_us"] = {"page_loop": round(float(att[0]), 2),
-                                                "wave_reduce": round(float(att[1]), 2),
-                                                "merge_store": round(float(att[2]), 2)}
         if bw.bw_check_device_error(s.model) != 0:
             print("[bench] device error flag set in the traced passes", file=sys.stderr)
             return 1
