@@ -189,23 +189,24 @@ def cpu_baseline_verify(cfg: dict, lens: list, t: int, seconds: float) -> dict:
 
 
 def committed_traffic(workload: str, cfg: dict, ctx: float):
-    """Counted HBM bytes per launch of the single-launch step from the committed FETCH_SIZE /
-    WRITE_SIZE profile of this workload, when its kernel sources are unchanged and its contexts lie
-    within 64 positions of ctx; else None."""
-    name = {"dense-9b": "step_dense9b_traffic.json", "dense-27b": "step_dense27b_traffic.json",
-            "moe-35b-a3b": "step_moe35b_traffic.json"}.get(workload)
+    """Counted HBM bytes per launch of the single-launch step from a committed FETCH_SIZE /
+    WRITE_SIZE profile of this workload whose kernel sources are unchanged and whose contexts lie
+    within 64 positions of ctx (a workload may have profiles at several contexts); else None."""
+    names = {"dense-9b": ["step_dense9b_traffic.json", "step_dense9b_traffic_ctx2600.json"],
+             "dense-27b": ["step_dense27b_traffic.json"], "moe-35b-a3b": ["step_moe35b_traffic.json"]}.get(workload)
     kv = cfg.get("kv_dtype", "bf16")
-    if name is None or kv != "bf16":
+    if names is None or kv != "bf16":
         return None
-    path = os.path.join(ROOT, "profiles", name)
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        tr = json.load(f)
     from memory_bound_autoregressive_amd.build import source_digest
-    lo, hi = tr.get("contexts", (0, -1))
-    if lo - 64 <= ctx <= hi + 64 and tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ()))):
-        return round(tr["hbm_bytes_per_launch"])
+    for name in names:
+        path = os.path.join(ROOT, "profiles", name)
+        if not os.path.exists(path):
+            continue
+        with open(path) as f:
+            tr = json.load(f)
+        lo, hi = tr.get("contexts", (0, -1))
+        if lo - 64 <= ctx <= hi + 64 and tr.get("kernel_source_digest") == source_digest(tuple(tr.get("kernel_sources", ()))):
+            return round(tr["hbm_bytes_per_launch"])
     return None
 
 
