@@ -193,7 +193,8 @@ def committed_traffic(workload: str, cfg: dict, ctx: float):
     WRITE_SIZE profile of this workload whose kernel sources are unchanged and whose contexts lie
     within 64 positions of ctx (a workload may have profiles at several contexts); else None."""
     names = {"dense-9b": ["step_dense9b_traffic.json", "step_dense9b_traffic_ctx2600.json"],
-             "dense-27b": ["step_dense27b_traffic.json"], "moe-35b-a3b": ["step_moe35b_traffic.json"]}.get(workload)
+             "dense-27b": ["step_dense27b_traffic.json", "step_dense27b_traffic_ctx8452.json"],
+             "moe-35b-a3b": ["step_moe35b_traffic.json", "step_moe35b_traffic_ctx4612.json"]}.get(workload)
     kv = cfg.get("kv_dtype", "bf16")
     if names is None or kv != "bf16":
         return None
@@ -388,7 +389,7 @@ def run_workload(args) -> int:
         s.synthesize(seed + 7, lens)
     else:
         B, t = 1, 1
-        lens = [cfg.get("context", cfg.get("prompt"))]
+        lens = [args.context if args.context else cfg.get("context", cfg.get("prompt"))]
         # + 32 + 8: the traced pass and the phase-stamp pass after the timed steps
         s = Session(cfg, seed=seed, max_len=[lens[0] + W + K + 2 + 32 + 8], max_tokens=1, pool_seed=seed + 1)
         s.synthesize(seed + 7, lens)
@@ -705,6 +706,9 @@ def main() -> int:
     ap.add_argument("--kv", choices=("bf16", "fp8"), default=None,
                     help="cache dtype of a decode or verify workload (default: the workload's own, bf16); "
                          "an FP8 E4M3 cache runs dense-9b on a synthesised context")
+    ap.add_argument("--context", type=int, default=None,
+                    help="dense-27b / moe-35b-a3b: synthesised context before the warm-up steps (default: "
+                         "the workload's); a counter profile at the timed run's traced context uses it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
