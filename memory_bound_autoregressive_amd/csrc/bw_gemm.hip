@@ -552,13 +552,17 @@ int launch_rowrms(const float* x, int64_t stride, int K, float eps, int M, float
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// k-splits: enough workgroups for 256 CUs while each split keeps >= 4 rounds of 64 columns
+// k-splits: enough workgroups for 256 CUs while each split keeps >= 4 rounds of 64 columns. A
+// wide-form workgroup (one per CU) carries a large fixed cost next to its per-chunk cost (about
+// 16 us and 2 us at the 9B shapes), so where the doubling overshoots one round of workgroups the
+// last doubling is undone: one round of longer splits beats two rounds of shorter ones.
 int gemm_ksplit(int N, int K, int M) {
   const bool wide = M >= kW32MinRows;
   const int tiles = (N + (wide ? kW32N : kNT) - 1) / (wide ? kW32N : kNT);
   const int mg = (M + kMaxRowsWG - 1) / kMaxRowsWG;
   int ks = 1;
   while (tiles * ks * mg < 256 && K % (ks * 2 * kKC) == 0 && K / (ks * 2) >= 4 * kKC) ks *= 2;
+  if (wide && ks > 1 && tiles * ks * mg > 256) ks /= 2;
   return ks;
 }
 
