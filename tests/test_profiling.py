@@ -47,3 +47,31 @@ def test_traffic_scales_by_the_copy_and_fits_context(tmp_path):
     assert fit["contexts"] == [1, n] and fit["rms_residual_bytes"] < 1.0
     assert res["contexts"] == [1, n]
     json.dumps(res)
+
+
+def test_bench_takes_counted_traffic_only_at_its_context_and_sources(tmp_path, monkeypatch):
+    """bench.py's `traffic` field: the committed profile whose contexts lie within 64 positions of
+    the traced pass and whose kernel-source digest matches the current sources; else null."""
+    import bench
+    from memory_bound_autoregressive_amd.build import source_digest
+
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    digest = source_digest(profiling.STEP_SOURCES)
+
+    def put(name, lo, hi, bytes_, dig=digest):
+        with open(prof / name, "w") as f:
+            json.dump({"contexts": [lo, hi], "hbm_bytes_per_launch": bytes_, "kernel_sources": list(profiling.STEP_SOURCES),
+                       "kernel_source_digest": dig}, f)
+
+    put("step_dense9b_traffic.json", 2049, 2058, 4.19e9)
+    put("step_dense9b_traffic_ctx2600.json", 2601, 2610, 4.27e9)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    cfg = {"kv_dtype": "bf16"}
+    assert bench.committed_traffic("dense-9b", cfg, 2104.5) == round(4.19e9)
+    assert bench.committed_traffic("dense-9b", cfg, 2607.5) == round(4.27e9)
+    assert bench.committed_traffic("dense-9b", cfg, 2674.5) is None  # 64.5 past the profile's contexts
+    assert bench.committed_traffic("dense-9b", {"kv_dtype": "fp8"}, 2607.5) is None  # another cache dtype
+    assert bench.committed_traffic("verify-9b", cfg, 2607.5) is None  # no single-launch profile
+    put("step_dense9b_traffic_ctx2600.json", 2601, 2610, 4.27e9, dig="0" * 16)  # sources changed since
+    assert bench.committed_traffic("dense-9b", cfg, 2607.5) is None
