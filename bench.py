@@ -68,18 +68,29 @@ def algorithmic_bytes(cfg: dict, ctx_mean: float) -> dict:
 
 # phase start / input-ready stamp slots of one layer in the single-launch step's record (16 per layer)
 DENSE_PHASES = [("qkv", 0, 1), ("attention", 2, 3), ("merge", 4, 5), ("o", 6, 7), ("gate_up", 8, 9), ("down", 10, 11)]
+# the 9B shape on 256 workgroups runs its FFN by columns: gate/up and the matching W_down columns in
+# one pass, then each owner of residual rows adds the workgroups' partial sums
+DENSE_PHASES_COLF = DENSE_PHASES[:4] + [("gate_up_down", 8, 9), ("down_reduce", 10, 11)]
 MOE_PHASES = [("qkv", 0, 1), ("attention", 2, 3), ("merge", 4, 5), ("o", 6, 7), ("router", 8, 9),
               ("topk_gate_up", 10, 11), ("down", 12, 13)]
 
 
-def stamp_phases(run_once, L: int, moe: bool, n: int = 8) -> dict:
+def ffn_by_columns(cfg) -> bool:
+    """The single launch runs the dense FFN by columns for the 9B shape (d 4096, ffn 12288) on a
+    GPU of 256 compute units (one workgroup per CU)."""
+    import torch
+    return (cfg.get("n_experts", 0) == 0 and cfg["d_model"] == 4096 and cfg["ffn_dim"] == 12288
+            and torch.cuda.get_device_properties(0).multi_processor_count == 256)
+
+
+def stamp_phases(run_once, L: int, moe: bool, n: int = 8, colf: bool = False) -> dict:
     """Per-layer wait ("wait_us": phase start until its input is in LDS) and work ("work_us": the
     rest, until the next phase starts) of each phase of the single-launch step, averaged over the
     layers of n steps, from workgroup 0's GPU real-time-counter stamps. run_once(stamps) runs one
     step with the stamp record `stamps` (int64 device tensor of L * 16 + 8) attached."""
     import numpy as np
     import torch
-    slots = MOE_PHASES if moe else DENSE_PHASES
+    slots = MOE_PHASES if moe else (DENSE_PHASES_COLF if colf else DENSE_PHASES)
     st = torch.zeros(L * 16 + 8, dtype=torch.int64, device="cuda")
     acc = np.zeros((len(slots), 2))
     lm = np.zeros(2)
@@ -456,7 +467,7 @@ def run_workload(args) -> int:
             bw.bw_debug_single_launch_stamps(s.model, st, L * 16 + 8)
             step()
 
-        phases = stamp_phases(run_stamped, L, moe=cfg.get("n_experts", 0) > 0)
+        phases = stamp_phases(run_stamped, L, moe=cfg.get("n_experts", 0) > 0, colf=ffn_by_columns(cfg))
         bw.bw_debug_single_launch_stamps(s.model, None)
         if bw.bw_check_device_error(s.model) != 0:
             print("[bench] device error flag set in the traced passes", file=sys.stderr)
@@ -835,7 +846,7 @@ def main() -> int:
             bw.bw_debug_single_launch_stamps(s.model, st, L * 16 + 8)
             step(feed_back=True)
 
-        phases = stamp_phases(run_stamped, L, moe=False)
+        phases = stamp_phases(run_stamped, L, moe=False, colf=ffn_by_columns(cfg))
         bw.bw_debug_single_launch_stamps(s.model, None)
         if bw.bw_check_device_error(s.model) != 0:
             print("[bench] device error flag set in the traced passes", file=sys.stderr)

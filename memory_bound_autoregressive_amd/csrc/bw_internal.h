@@ -112,6 +112,7 @@ struct PLayer {
   const uint16_t* ffn_norm = nullptr;
   const uint16_t* router = nullptr; // MoE: fp16 [E][d]
   ExpertTab ex;                     // MoE: expert matrices (routed, then shared)
+  const uint8_t* dnc = nullptr;     // dense FFN by columns: W_down as per-workgroup column slices
 };
 
 constexpr int BW_DERR_PERSIST_BIT = 8;
@@ -139,6 +140,8 @@ struct PersistParams {
   uint32_t* xm = nullptr;           // [d]: residual after attention
   uint32_t* xf = nullptr;           // [F]: SwiGLU output
   uint32_t* xx = nullptr;           // [d]: residual after the FFN (layer input)
+  uint32_t* xdp = nullptr;          // FFN by columns: [d / 16 owners][workgroups][16] down partials
+  int32_t n_xdp = 0;                // words of xdp
   uint64_t* xarg = nullptr;         // [workgroups]: argmax partial (value, index | tag << 30)
   float* logits = nullptr;          // [V] or null
   int32_t* argmax = nullptr;        // [1] or null
@@ -213,6 +216,11 @@ int launch_spec_accept(int32_t* tokens, const int32_t* argmax, float* logits, in
 int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                    bool query_only);
 int launch_persist_reset(const PersistParams& p, int n_q, int n_p, int n_a, int n_d, int n_f, int n_arg, hipStream_t s);
+// FFN by columns in the single launch: bytes of one layer's W_down column-slice copy for this
+// shape and grid (0: the shape keeps the FFN by rows), and the kernel that writes that copy from
+// the device matrix
+int64_t persist_colffn_bytes(int d, int F, int nwg);
+int launch_down_slices(const Mat& dn, int nwg, uint8_t* out, hipStream_t s);
 // MoE form (router, top-k and expert phases): -2 when the shape has no instantiation
 int launch_persist_moe(const PersistParams& p, int d, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                        bool query_only);

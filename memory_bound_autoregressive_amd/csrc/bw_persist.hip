@@ -484,6 +484,74 @@ __device__ __forceinline__ void gemv_rest_f(int tid, int r0, int r1, PGroup<LPR,
   }
 }
 
+// ---- dense FFN by columns ---------------------------------------------------------------------
+// Workgroup w computes its gate/up rows (the SwiGLU outputs of ffn columns [Fw w, Fw w + Fw)),
+// keeps those Fw values in LDS and multiplies them at once by the same Fw columns of W_down, for
+// every one of the d rows. The d partial sums go to the owners of the rows, which add the nwg
+// partials of each row to their residual rows. So the FFN streams its gate/up and down weights
+// in one pass with no exchange between them; the F-long SwiGLU vector is never gathered.
+// Shape: d = 4096 (8 rows per thread), F = 12288 over 256 workgroups (Fw = 48 = three 16-column
+// half-blocks; a half-block takes the scale of its 32-column block).
+//
+// W_down column-slice copy (written once at load from the device matrix): for slice w and thread
+// t, 14 chunks of 16 bytes at ((w 14 + c) 512 + t) 16, so chunk c of all threads is contiguous:
+//   chunks 0..11: 48 code dwords, dword 6 i + k for row 8 t + i, slice columns 8k..8k+7; nibble n
+//                 (bits 4n..4n+3) holds column 8k + 2n for n < 4 and 8k + 2(n - 4) + 1 otherwise,
+//                 so (dword >> 4m) & 0x000F000F is the fp16-subnormal pair of columns (2m, 2m + 1);
+//   chunks 12, 13: one dword per row i (rows 0..3, then 4..7): the scale of the block of the
+//                 slice's first column (low half) and of its last column (high half).
+constexpr int kCfD = 4096, kCfF = 12288, kCfWG = 256;
+constexpr int kCfW = kCfF / kCfWG;   // ffn columns per workgroup
+constexpr int kCfRT = kCfD / kPT;    // W_down rows per thread
+constexpr int kCfChunks = 14;        // 16-byte chunks per thread
+constexpr int kCfOwn = kCfD / kCfWG; // residual rows per owner
+static_assert(kCfW == 48 && kCfRT == 8 && kCfOwn == 16 && 6 * kCfRT == 4 * 12 && kCfRT == 2 * 4,
+              "FFN-by-columns geometry");
+
+struct CfSlice {
+  u32x4 q[kCfChunks];
+};
+
+// this thread's chunks of slice w (every load unconditional, non-temporal)
+__device__ __forceinline__ void cf_issue(int tid, const uint8_t* dnc, int w, CfSlice& d) {
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc(dnc + (int64_t)w * kCfChunks * kPT * 16, kCfChunks * kPT * 16);
+#pragma unroll
+  for (int c = 0; c < kCfChunks; ++c) d.q[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c * kPT + tid) * 16, 0, kNT);
+}
+
+// the 8 partial sums sum_j s_j sum_{c in half-block j} (q_c - 8) x_c of this thread's rows;
+// xc: the slice's 48 SwiGLU values, then the sums of its three half-blocks (LDS)
+__device__ __forceinline__ void cf_partials(const CfSlice& d, const float* xc, bool odd_w, float (&out)[kCfRT]) {
+  float4 xv[12];
+#pragma unroll
+  for (int k = 0; k < 12; ++k) xv[k] = *(const float4*)(xc + 4 * k);
+  const float hs[3] = {xc[48], xc[49], xc[50]};
+#pragma unroll
+  for (int i = 0; i < kCfRT; ++i) {
+    float dj[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k = 2 * j + kk, li = 6 * i + k;
+        const uint32_t q = d.q[li >> 2][li & 3];
+        const float4 a = xv[2 * k], b = xv[2 * k + 1];  // columns 8k..8k+3, 8k+4..8k+7
+        acc = mix2(q & 0x000F000Fu, a.x, a.y, acc);
+        acc = mix2((q >> 4) & 0x000F000Fu, a.z, a.w, acc);
+        acc = mix2((q >> 8) & 0x000F000Fu, b.x, b.y, acc);
+        acc = mix2((q >> 12) & 0x000F000Fu, b.z, b.w, acc);
+      }
+      dj[j] = fmaf(16777216.0f, acc, -8.0f * hs[j]);
+    }
+    const uint32_t sw = d.q[12 + (i >> 2)][i & 3];
+    const float s_first = f16_to_f32((uint16_t)(sw & 0xFFFFu)), s_last = f16_to_f32((uint16_t)(sw >> 16));
+    // half-block 1 lies in the first column's block for an even slice, in the last one's for an odd one
+    const float s_mid = odd_w ? s_last : s_first;
+    out[i] = fmaf(s_last, dj[2], fmaf(s_mid, dj[1], s_first * dj[0]));
+  }
+}
+
 // ---- MoE expert matrices ----------------------------------------------------------------------
 // mp: per slot (top_k routed experts in rank order, then the shared ones) the device pointers of
 // its gate/up codes and scales and its down codes and scales, staged in LDS after the top-k.
@@ -626,8 +694,9 @@ struct alignas(16) AttnLds {
 
 // RWQ, RWO, RWG, RWF: row steps per register group of the QKV, O, gate/up and down passes; a
 // group that covers a wave's whole share of a phase is loaded in full before the phase's wait.
+// COLF: the dense FFN by columns (see cf_issue), for the shape and grid it is laid out for.
 template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF,
-          bool MOE>
+          bool MOE, bool COLF>
 __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   constexpr int KD = LPR_D * NB_D * 32;  // d_model (= Hq * D)
@@ -1153,7 +1222,122 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       }
     }
 
-    if constexpr (!MOE) {
+    if constexpr (COLF) {
+    static_assert(!MOE && KD == kCfD && KF == kCfF && LPR_D == 64 && NB_D == 2, "FFN by columns: 9B shape");
+    // ================= gate/up + SwiGLU + down by columns =================
+    // The W_down slice goes out in place of the gate/up pass's last next-group load, so the two
+    // matrices stream back to back; the SwiGLU values stay in LDS.
+    stamp(p, l * 16 + 8);
+    {
+      const int tid = phase_tid();
+      constexpr int GROUP = (kWave / LPR_D) * RWG;
+      constexpr int NG = 2 * kCfW / GROUP / kPW;  // groups per wave
+      static_assert(NG * GROUP * kPW == 2 * kCfW, "gate/up rows split evenly over the waves");
+      const int wave = wave_of(tid);
+      XStage<KD> xin;
+      stage_issue<KD, true>(tid, p.xm, Ly.ffn_norm, xin);
+      PGroup<LPR_D, NB_D, RWG> ga[2];
+      pload<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, wave, ga[0]);
+      __syncthreads();
+      stage_finish<KD, true>(tid, p.xm, tout, p.eps, xin, s, ctl);
+      if (bail) return;
+      stamp(p, l * 16 + 9);
+      CfSlice dq;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        if (i + 1 < NG) pload<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, wave + (i + 1) * kPW, ga[(i + 1) & 1]);
+        else cf_issue(tid, Ly.dnc, w, dq);
+        pcompute<LPR_D, NB_D, RWG>(tid, ga[i & 1], g0, g1, s);
+      }
+      __syncthreads();
+      // the slice's SwiGLU values and the sums of its three half-blocks (lanes 0..47 of wave 0)
+      if (tid < kWave) {
+        float v = 0.f;
+        if (tid < kCfW) {
+          v = silu(s.ydot[2 * tid]) * s.ydot[2 * tid + 1];
+          s.xs[tid] = v;
+        }
+        v = sum8(v);
+        v += xor8(v);
+        if (tid < kCfW && (tid & 15) == 0) s.xs[kCfW + (tid >> 4)] = v;
+      }
+      __syncthreads();
+      float part[kCfRT];
+      cf_partials(dq, s.xs, (w & 1) != 0, part);
+      // rows 8 t .. 8 t + 7 belong to owner t / 2, at 8 (t % 2) of this producer's 16 words
+      const __amdgpu_buffer_rsrc_t rp = xrsrc(p.xdp, (int64_t)p.n_xdp * 4);
+      const int off = (((tid >> 1) * kCfWG + w) * kCfOwn + (tid & 1) * 8) * 4;
+      u32x4 a, b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = xenc(part[i], tout);
+        b[i] = xenc(part[4 + i], tout);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(a, rp, off, 0, kCohSC1);
+      __builtin_amdgcn_raw_buffer_store_b128(b, rp, off + 16, 0, kCohSC1);
+    }
+
+    // ================= down partials -> owned residual rows =================
+    // Thread t reads producer t / 2's partials of rows 8 (t % 2) .. + 7; the 32 producers of a
+    // wave are summed across lanes of equal parity, the 8 waves in LDS (fixed order).
+    stamp(p, l * 16 + 10);
+    {
+      const int tid = phase_tid();
+      const int lane = tid & 63, wave = wave_of(tid);
+      const __amdgpu_buffer_rsrc_t rp = xrsrc(p.xdp, (int64_t)p.n_xdp * 4);
+      const int off = ((w * kCfWG + (tid >> 1)) * kCfOwn + (tid & 1) * 8) * 4;
+      u32x4 v[2];
+      v[0] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCohSC1);
+      v[1] = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16, 0, kCohSC1);
+      {
+        ctl.t0 = __builtin_amdgcn_s_memrealtime();
+        bool all = true;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) all &= xok(v[c][k], tout);
+        uint32_t flag = 0u;
+        while (!all && !give_up(ctl, flag)) {
+          __builtin_amdgcn_s_sleep(1);
+          flag = load_abort(ctl);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {  // branch-free reloads, as in stage_finish
+            bool ok = true;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ok &= xok(v[c][k], tout);
+            const u32x4 nv = __builtin_amdgcn_raw_buffer_load_b128(rp, ok ? kOOB : off + 16 * c, 0, kCohSC1);
+            v[c] = ok ? v[c] : nv;
+          }
+          all = true;
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) all &= xok(v[c][k], tout);
+        }
+      }
+      stamp(p, l * 16 + 11);
+      float* red = s.mrg;  // [kPW][16]
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float x = xdec(v[i >> 2][i & 3]);
+        x += dpp_mov<0x4E>(x);   // lane ^ 2 (same parity)
+        x += row_to<4>(x);       // the quad 4 lanes below, then 8 below: the row's 8 lanes of this parity
+        x += row_to<8>(x);
+        x = sum_xor32(sum_xor16(x));
+        if (lane < 2) red[wave * kCfOwn + lane * 8 + i] = x;
+      }
+      __syncthreads();
+      if (bail) return;
+      if (tid < kCfOwn) {
+        float dsum = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < kPW; ++wv) dsum += red[wv * kCfOwn + tid];
+        const float r = s.resid[tid] + dsum;
+        s.resid[tid] = r;
+        xstore(p.xx, d0 + tid, r, tout);
+      }
+    }
+    } else if constexpr (!MOE) {
     // ================= gate/up + SwiGLU =================
     stamp(p, l * 16 + 8);
     {
@@ -1519,6 +1703,7 @@ __global__ void k_persist_reset(PersistParams p, int n_q, int n_p, int n_a, int 
   }
   if (i < n_f) p.xf[i] = xenc(0.f, bad);
   if (p.xr != nullptr && i < p.E) p.xr[i] = xenc(0.f, bad);
+  if (p.xdp != nullptr && i < p.n_xdp) p.xdp[i] = xenc(0.f, bad);
   if (i < n_arg) p.xarg[i] = (uint64_t)((epoch + 2) & 3u) << 62;
   if (i == 0) p.abort_flag[0] = 0u;
 }
@@ -1534,9 +1719,9 @@ static size_t persist_lds_bytes() {
 }
 
 template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF,
-          bool MOE = false>
+          bool MOE = false, bool COLF = false>
 static int launch_persist_t(const PersistParams& p, int nwg, hipStream_t s, bool query_only) {
-  auto kern = k_persist<LPR_D, NB_D, LPR_F, NB_F, KVDT, D, QR, RWQ, RWO, RWG, RWF, MOE>;
+  auto kern = k_persist<LPR_D, NB_D, LPR_F, NB_F, KVDT, D, QR, RWQ, RWO, RWG, RWF, MOE, COLF>;
   const size_t lds = persist_lds_bytes<LPR_D, NB_D, LPR_F, NB_F, KVDT, D, QR>();
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return -1;
   if (query_only) {
@@ -1556,8 +1741,57 @@ static int launch_persist_t(const PersistParams& p, int nwg, hipStream_t s, bool
 
 // Shapes with an instantiation: (d, ffn, head dim, query heads per KV head) with the row steps
 // per wave group sized for 256 workgroups
+int64_t persist_colffn_bytes(int d, int F, int nwg) {
+  return d == kCfD && F == kCfF && nwg == kCfWG ? (int64_t)kCfWG * kCfChunks * kPT * 16 : 0;
+}
+
+// One 16-byte chunk (slice w, chunk c, thread t) of the W_down column-slice copy per thread (see
+// cf_issue for the layout), from the device matrix (codes [d][F/2], scales tiled [d][lpr][nb]).
+__global__ void k_down_slices(Mat dn, uint8_t* out) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= (int64_t)kCfWG * kCfChunks * kPT) return;
+  const int t = (int)(g % kPT), c = (int)((g / kPT) % kCfChunks), w = (int)(g / ((int64_t)kPT * kCfChunks));
+  const int nblk = dn.K / 32, col0 = w * kCfW;
+  auto scale = [&](int row, int col) {
+    const int b = col / 32;
+    return dn.scales[(int64_t)row * nblk + (b % dn.lpr) * dn.nb + b / dn.lpr];
+  };
+  u32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t word = 0u;
+    if (c < 12) {
+      const int li = 4 * c + e, i = li / 6, k = li % 6, row = kCfRT * t + i;
+      for (int n = 0; n < 8; ++n) {
+        const int col = col0 + 8 * k + (n < 4 ? 2 * n : 2 * (n - 4) + 1), in = col % 32;
+        const uint8_t byte = dn.codes[(int64_t)row * (dn.K / 2) + (col / 32) * 16 + (in % 16)];
+        const uint32_t q = in < 16 ? (byte & 15u) : (byte >> 4);
+        word |= q << (4 * n);
+      }
+    } else {
+      const int row = kCfRT * t + 4 * (c - 12) + e;
+      word = (uint32_t)scale(row, col0) | ((uint32_t)scale(row, col0 + kCfW - 1) << 16);
+    }
+    v[e] = word;
+  }
+  *(u32x4*)(out + g * 16) = v;
+}
+
+int launch_down_slices(const Mat& dn, int nwg, uint8_t* out, hipStream_t s) {
+  if (persist_colffn_bytes(dn.N, dn.K, nwg) == 0) return -2;
+  const int64_t n = (int64_t)kCfWG * kCfChunks * kPT;
+  hipLaunchKernelGGL(k_down_slices, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dn, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                    bool query_only) {
+  // the 9B shape on 256 workgroups: the FFN by columns
+  if (persist_colffn_bytes(d, F, nwg) > 0 && D == 128 && rep == 4) {
+    if (kv_dtype == 1) return launch_persist_t<64, 2, 64, 6, 1, 128, 4, 3, 2, 2, 1, false, true>(p, nwg, s, query_only);
+    if (kv_dtype == 2) return launch_persist_t<64, 2, 64, 6, 2, 128, 4, 3, 2, 2, 1, false, true>(p, nwg, s, query_only);
+    if (kv_dtype == 3) return launch_persist_t<64, 2, 64, 6, 3, 128, 4, 3, 2, 2, 1, false, true>(p, nwg, s, query_only);
+  }
   // FP8 E4M3 caches
 #define BW_P8(DM, FF, LD, ND, LF, NF, DD, QR, RQ, RO, RG, RF)                        \
   if (kv_dtype == 3 && d == DM && F == FF && D == DD && rep == QR)                  \
@@ -1598,7 +1832,7 @@ int launch_persist_moe(const PersistParams& p, int d, int kv_dtype, int D, int r
 }
 
 int launch_persist_reset(const PersistParams& p, int n_q, int n_p, int n_a, int n_d, int n_f, int n_arg, hipStream_t s) {
-  const int n = std::max({n_q, n_p, n_a, n_d, n_f, n_arg, p.xr != nullptr ? p.E : 0});
+  const int n = std::max({n_q, n_p, n_a, n_d, n_f, n_arg, p.xr != nullptr ? p.E : 0, p.xdp != nullptr ? p.n_xdp : 0});
   hipLaunchKernelGGL(k_persist_reset, dim3((n + 255) / 256), dim3(256), 0, s, p, n_q, n_p, n_a, n_d, n_f, n_arg);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

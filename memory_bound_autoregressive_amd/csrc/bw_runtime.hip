@@ -395,11 +395,25 @@ static int persist_setup(bw_model* m) {
     return BW_OK;
   }
   std::vector<PLayer> layers(c.n_layers);
+  // the FFN by columns (9B shape on 256 workgroups) reads W_down as per-workgroup column slices:
+  // one copy per layer, written on the device from the uploaded matrix
+  const int64_t dnc_bytes = moe ? 0 : persist_colffn_bytes(d, F, nwg);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerDev& Ld = m->L[l];
     layers[l] = PLayer{Ld.qkv, Ld.o, Ld.gu, Ld.dn, Ld.attn_norm, Ld.ffn_norm, Ld.router, Ld.ex};
+    if (dnc_bytes > 0) {
+      void* q;
+      if (int rc = m->arena.alloc((size_t)dnc_bytes, &q)) return rc;
+      if (launch_down_slices(Ld.dn, nwg, (uint8_t*)q, nullptr)) return fail(BW_EHIP, "W_down slice copy failed");
+      layers[l].dnc = (const uint8_t*)q;
+    }
   }
   void* ptr;
+  if (dnc_bytes > 0) {
+    p.n_xdp = d * nwg;  // d / 16 owners x nwg producers x 16 rows
+    if (int rc = ws_alloc(m, sizeof(uint32_t) * (size_t)p.n_xdp, &ptr)) return rc;
+    p.xdp = (uint32_t*)ptr;
+  }
   if (int rc = ws_alloc(m, sizeof(PLayer) * layers.size(), &ptr)) return rc;
   HIP_OK(hipMemcpy(ptr, layers.data(), sizeof(PLayer) * layers.size(), hipMemcpyHostToDevice));
   p.layers = (const PLayer*)ptr;
