@@ -188,6 +188,7 @@ struct Lds {
   float* mrg;    // merge scratch [kMrg]
   int* pgid;     // page ids of this workgroup's attention split [kMaxSplitPages]
   float* att;    // attention scratch
+  uint32_t* ltab;  // two slots of the layer table (this layer's and the next one's PLayer)
 };
 constexpr int kMaxRows = 1024;  // rows per workgroup per phase held in ydot
 #ifndef BW_LM_RW
@@ -197,6 +198,8 @@ constexpr int kLmRW = BW_LM_RW;  // row steps per group of the lm_head pass
 constexpr int kMaxOwn = 64;     // residual rows per workgroup
 constexpr int kMaxSplitPages = 256;  // pages of one attention split (workgroup)
 constexpr int kMaxSplit = kPT / 4;  // attention splits per KV head (workgroups / KV heads)
+constexpr int kLW = (int)(sizeof(PLayer) / 4);  // words of one layer's table entry
+static_assert(sizeof(PLayer) % 16 == 0 && kLW <= kWave, "layer table entry in whole 16-byte words");
 // merge scratch: (m, l) of [splits], factors [splits], partial sums [kPT], the denominator
 // MoE scratch inside mrg (free outside the merge phase), in floats: top-k candidates [kMoeMaxE]
 // (uint64 keys), maxima of 16-key rows [32] (uint64), the threshold (uint64) and candidate count,
@@ -690,6 +693,13 @@ struct alignas(16) AttnLds {
   alignas(16) uint16_t vst[kPW][kPageTokens * (D + kVPitch)];  // each wave's staged V page (16-bit)
 };
 
+// The next layer's table entry, issued by the first kLW threads ahead of the last phase's input
+// polls (the polls' first check waits for it anyway) and stored to its LDS slot after them.
+__device__ __forceinline__ uint32_t ltab_issue(const PersistParams& p, int l1, int tid) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)p.layers, 0, p.L * kLW * 4, kRsrc3);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, tid < kLW && l1 < p.L ? (l1 * kLW + tid) * 4 : kOOB, 0, 0);
+}
+
 // ---- the kernel -------------------------------------------------------------------------------
 
 // RWQ, RWO, RWG, RWF: row steps per register group of the QKV, O, gate/up and down passes; a
@@ -718,6 +728,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   s.mrg = s.red + 32;
   s.pgid = reinterpret_cast<int*>(s.mrg + kMrg);
   s.att = s.mrg + kMrg + kMaxSplitPages;
+  s.ltab = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(s.att) + sizeof(AttnLds<D, QR>));
   AttnLds<D, QR>& al = *reinterpret_cast<AttnLds<D, QR>*>(s.att);
 
   const int nwg = gridDim.x, w = blockIdx.x;
@@ -732,6 +743,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
 
   const int L = p.L, H = p.H, G = p.G;
   stamp(p, L * 16 + 4);
+  // layer 0's table entry into slot 0; later entries are loaded one layer ahead (ltab_issue)
+  if (threadIdx.x < kLW) s.ltab[threadIdx.x] = reinterpret_cast<const uint32_t*>(p.layers)[threadIdx.x];
   const uint32_t epoch = p.epoch[0];
   const uint32_t base_tag = epoch * (uint32_t)(L + 2);
   const int pos = p.seq_lens[0];
@@ -808,7 +821,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   for (int l = 0; l < L; ++l) {
     // this layer's descriptors, read once with scalar loads (the table is constant for the step),
     // so the matrix pointers are uniform registers and the loops below never re-read them
-    const PLayer Ly = load_uniform(p.layers + l);
+    const PLayer Ly = load_uniform(reinterpret_cast<const PLayer*>(s.ltab + (l & 1) * kLW));
     const uint32_t tin = base_tag + (uint32_t)l;       // T(l - 1)
     const uint32_t tout = base_tag + (uint32_t)l + 1;  // T(l)
     typedef typename KvT<KVDT>::E KE;
@@ -1286,6 +1299,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int lane = tid & 63, wave = wave_of(tid);
       const __amdgpu_buffer_rsrc_t rp = xrsrc(p.xdp, (int64_t)p.n_xdp * 4);
       const int off = ((w * kCfWG + (tid >> 1)) * kCfOwn + (tid & 1) * 8) * 4;
+      const uint32_t nxt = ltab_issue(p, l + 1, tid);
       u32x4 v[2];
       v[0] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCohSC1);
       v[1] = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16, 0, kCohSC1);
@@ -1316,18 +1330,25 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         }
       }
       stamp(p, l * 16 + 11);
-      float* red = s.mrg;  // [kPW][16]
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = xdec(v[i >> 2][i & 3]);
-        x += dpp_mov<0x4E>(x);   // lane ^ 2 (same parity)
-        x += row_to<4>(x);       // the quad 4 lanes below, then 8 below: the row's 8 lanes of this parity
-        x += row_to<8>(x);
-        x = sum_xor32(sum_xor16(x));
-        if (lane < 2) red[wave * kCfOwn + lane * 8 + i] = x;
-      }
+      if (tid < kLW) s.ltab[((l + 1) & 1) * kLW + tid] = nxt;
+      // transpose through LDS: [producer][16 rows] (past the 51 words the FFN phase may still read)
+      float* tp = s.xs + 64;
+      *(float4*)(tp + 8 * tid) = make_float4(xdec(v[0][0]), xdec(v[0][1]), xdec(v[0][2]), xdec(v[0][3]));
+      *(float4*)(tp + 8 * tid + 4) = make_float4(xdec(v[1][0]), xdec(v[1][1]), xdec(v[1][2]), xdec(v[1][3]));
       __syncthreads();
       if (bail) return;
+      // thread t: row t % 16 over producers t / 16 + 32 j; then the wave's four producer groups
+      // (lanes of equal t % 16) and the 8 waves (fixed order)
+      float* red = s.mrg;  // [kPW][16]
+      {
+        const int r = tid & 15, pg = tid >> 4;
+        float x = 0.f;
+#pragma unroll
+        for (int j = 0; j < kCfWG / 32; ++j) x += tp[(pg + 32 * j) * kCfOwn + r];
+        x = sum_xor32(sum_xor16(x));
+        if (lane < kCfOwn) red[wave * kCfOwn + lane] = x;
+      }
+      __syncthreads();
       if (tid < kCfOwn) {
         float dsum = 0.f;
 #pragma unroll
@@ -1369,6 +1390,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       (void)lane;
       (void)wave;
       XStage<KF> xin;
+      const uint32_t nxt = ltab_issue(p, l + 1, tid);
       stage_issue<KF, false>(tid, p.xf, nullptr, xin);
       PGroup<LPR_F, NB_F, RWF> cur;
       gemv_first<LPR_F, NB_F, RWF>(tid, Ly.dn, d0, d1, cur);
@@ -1376,6 +1398,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       stage_finish<KF, false>(tid, p.xf, tout, 0.f, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 11);
+      if (tid < kLW) s.ltab[((l + 1) & 1) * kLW + tid] = nxt;
       gemv_rest<LPR_F, NB_F, RWF, DBF>(tid, Ly.dn, d0, d1, cur, s);
       __syncthreads();
       for (int r = d0 + tid; r < d1; r += kPT) {
@@ -1561,6 +1584,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       const int tid = phase_tid();
       const uint64_t* mp = reinterpret_cast<const uint64_t*>(s.mrg + kMoePtr);
       XStage<KF> xin;
+      const uint32_t nxt = ltab_issue(p, l + 1, tid);
       stage_issue<KF, false>(tid, p.xf, nullptr, xin);
       PGroup<LPR_F, NB_F, RWF> cur;
       pload_moe_dn<LPR_F, NB_F, RWF>(tid, mp, KD, d0, d1, wave_of(tid), cur);
@@ -1568,6 +1592,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       stage_finish<KF, false>(tid, p.xf, tout, 0.f, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 13);
+      if (tid < kLW) s.ltab[((l + 1) & 1) * kLW + tid] = nxt;
       gemv_rest_f<LPR_F, NB_F, RWF, DBF>(tid, d0, d1, cur, s, [&](int gi, PGroup<LPR_F, NB_F, RWF>& gg) {
         pload_moe_dn<LPR_F, NB_F, RWF>(tid, mp, KD, d0, d1, gi, gg);
       });
@@ -1715,7 +1740,7 @@ static size_t persist_lds_bytes() {
   constexpr int KD = LPR_D * NB_D * 32, KF = LPR_F * NB_F * 32;
   constexpr int KMAX = KD > KF ? KD : KF;
   return sizeof(float) * ((size_t)KMAX + KMAX / 32 + kMaxRows + kMaxOwn + 32 + kMrg + kMaxSplitPages) +
-         sizeof(AttnLds<D, QR>);
+         sizeof(AttnLds<D, QR>) + 2 * sizeof(PLayer);
 }
 
 template <int LPR_D, int NB_D, int LPR_F, int NB_F, int KVDT, int D, int QR, int RWQ, int RWO, int RWG, int RWF,
