@@ -145,6 +145,21 @@ int bw_kv_pool_synthesize(bw_kv_pool* pool, uint64_t seed, const int32_t* seq_id
                           const int32_t* seq_lens_host, const int32_t* page_table_host,
                           int32_t batch, int32_t max_pages);
 
+/* The same synthetic context from device arrays, queued on `stream` (no host round trip, nothing
+ * allocated): seq_ids_dev [batch] (NULL: sequence b has id b), seq_lens_dev [batch] and
+ * page_table_dev [batch * max_pages] are read by the kernel, which writes exactly the bits of
+ * bw_kv_pool_synthesize (the generator is implemented on the device from the same definition).
+ * The caller keeps the three arrays alive until the work on `stream` completes. The paged cache
+ * that maps logical positions to fixed-size physical pages is the deep-dive page's (section 6
+ * item 2). Errors: BW_EINVAL (null pool or array, batch outside [1, 65535], max_pages < 1),
+ * BW_EHIP (launch). Range errors found on the device set bits in the device error word
+ * (bw_check_device_error): BW_DERR_PAGE for a needed page id outside [0, n_pages) (that page is
+ * skipped), BW_DERR_POS for a negative length or one needing more than max_pages pages (the
+ * first max_pages pages are written). */
+int bw_kv_pool_synthesize_async(bw_kv_pool* pool, uint64_t seed, const int32_t* seq_ids_dev,
+                                const int32_t* seq_lens_dev, const int32_t* page_table_dev,
+                                int32_t batch, int32_t max_pages, void* stream);
+
 /* Copy one page-layer (n_kv_heads * 2 * page_tokens * head_dim elements, 2 bytes each or 1 for
  * FP8, in the pool layout above) to host memory. Synchronous. Errors: BW_EINVAL, BW_ERANGE. */
 int bw_kv_pool_read(const bw_kv_pool* pool, int32_t layer, int32_t page, void* host_dst,

@@ -26,7 +26,7 @@ MAT = {"qkv": 0, "o": 1, "gate": 2, "up": 3, "down": 4, "lm_head": 5,
 
 EXPORTS = (
     "bw_model_load_synthetic", "bw_model_free", "bw_kv_pool_create", "bw_kv_pool_free",
-    "bw_kv_pool_fill", "bw_kv_pool_synthesize", "bw_kv_pool_read", "bw_decode_step",
+    "bw_kv_pool_fill", "bw_kv_pool_synthesize", "bw_kv_pool_synthesize_async", "bw_kv_pool_read", "bw_decode_step",
     "bw_last_error", "bw_check_device_error", "bw_debug_dequant", "bw_debug_matvec",
     "bw_debug_attention", "bw_debug_read_experts", "bw_debug_read_hidden", "bw_set_trace", "bw_set_graphs",
     "bw_set_gemm_min_rows", "bw_set_single_launch", "bw_debug_single_launch_deadline",
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.bw_kv_pool_free.argtypes = [vp]
         L.bw_kv_pool_fill.argtypes = [vp, ctypes.c_uint16, vp]
         L.bw_kv_pool_synthesize.argtypes = [vp, u64, vp, vp, vp, i32, i32]
+        L.bw_kv_pool_synthesize_async.argtypes = [vp, u64, vp, vp, vp, i32, i32, vp]
         L.bw_kv_pool_read.argtypes = [vp, i32, i32, vp, sz]
         L.bw_model_export_tensor.argtypes = [vp, ctypes.c_char_p, vp, sz]
         L.bw_model_tensor_bytes.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(sz)]
@@ -191,6 +192,13 @@ def bw_kv_pool_synthesize(pool: int, seed: int, seq_ids, seq_lens, page_table, b
     """Host int32 numpy arrays."""
     _check(lib().bw_kv_pool_synthesize(pool, seed, _ptr(seq_ids), _ptr(seq_lens), _ptr(page_table), batch, max_pages),
            "bw_kv_pool_synthesize")
+
+
+def bw_kv_pool_synthesize_async(pool: int, seed: int, seq_ids, seq_lens, page_table, batch: int, max_pages: int,
+                                stream=None) -> None:
+    """seq_ids (or None: sequence b has id b), seq_lens, page_table: int32 device tensors."""
+    _check(lib().bw_kv_pool_synthesize_async(pool, seed, _ptr(seq_ids), _ptr(seq_lens), _ptr(page_table), batch,
+                                             max_pages, _stream(stream)), "bw_kv_pool_synthesize_async")
 
 
 def bw_model_tensor_bytes(model: int, name: str) -> int:

@@ -711,6 +711,80 @@ __global__ void k_scatter_pages(const uint8_t* __restrict__ staged, const int32_
   }
 }
 
+// Device form of the synthetic context. The generator is implemented again here from its
+// published definition (splitmix64 of Steele, Lea and Flood, OOPSLA 2014, used as a counter
+// hash; finaliser constants as in Vigna's public splitmix64.c) with the stream-key derivation of
+// the shared input generator, so both forms write the same bits.
+__device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+__device__ __forceinline__ uint64_t sm64_key(uint64_t seed, uint32_t kind, uint32_t layer, uint32_t expert) {
+  uint64_t k = sm64_mix(seed ^ 0x5851F42D4C957F2DULL);
+  k = sm64_mix(k ^ ((uint64_t)kind << 40) ^ (uint64_t)layer);
+  return sm64_mix(k ^ ((uint64_t)expert * 0xD1B54A32D192ED03ULL));
+}
+
+// One workgroup per (logical page lp, sequence b, layer l): the page's first min(16, len - 16 lp)
+// slots of every KV head, K and V, in the pool layout [g][kv][slot][d].
+template <int DT>
+__global__ void k_kv_synth(uint8_t* pool, int64_t layer_bytes, int64_t page_elems, int n_pages, uint64_t seed,
+                           const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ seq_lens,
+                           const int32_t* __restrict__ page_table, int max_pages, int G, int D, int32_t* err) {
+  const int lp = blockIdx.x, b = blockIdx.y, l = blockIdx.z;
+  const int len = seq_lens[b];
+  const int np = len < 0 ? 0 : (len + kPageTokens - 1) / kPageTokens;
+  if (lp == 0 && l == 0 && threadIdx.x == 0 && (len < 0 || np > max_pages)) atomicOr(err, BW_DERR_POS);
+  if (lp >= np || lp >= max_pages) return;
+  const int page = page_table[(int64_t)b * max_pages + lp];
+  if (page < 0 || page >= n_pages) {
+    if (threadIdx.x == 0) atomicOr(err, BW_DERR_PAGE);
+    return;
+  }
+  const int nslot = min(kPageTokens, len - lp * kPageTokens);
+  const uint32_t seq = seq_ids ? (uint32_t)seq_ids[b] : (uint32_t)b;
+  const uint64_t key = sm64_key(seed, BWS_KV, (uint32_t)l, seq);
+  uint8_t* base = pool + (int64_t)l * layer_bytes + (int64_t)page * page_elems * (DT == 3 ? 1 : 2);
+  for (int64_t e = threadIdx.x; e < page_elems; e += blockDim.x) {
+    const int d = (int)(e % D), slot = (int)((e / D) % kPageTokens);
+    const int kv = (int)((e / ((int64_t)D * kPageTokens)) & 1), g = (int)(e / ((int64_t)D * kPageTokens * 2));
+    if (slot >= nslot) continue;
+    const int64_t pos = (int64_t)lp * kPageTokens + slot;
+    const uint64_t idx = (((uint64_t)pos * 2u + (uint64_t)kv) * (uint64_t)G + (uint64_t)g) * (uint64_t)D + (uint64_t)d;
+    const int c = (int)(sm64_mix(key + (idx + 1ull) * 0x9E3779B97F4A7C15ULL) & 0xFFu) - 128;
+    if constexpr (DT == 3) {
+      base[e] = (uint8_t)f32_to_fp8((float)(c >> 3) * 0.125f);  // at most 4 significant bits: exact
+    } else if constexpr (DT == 1) {
+      ((uint16_t*)base)[e] = f32_to_f16((float)c * 0.015625f);  // at most 8 significant bits: exact
+    } else {
+      ((uint16_t*)base)[e] = (uint16_t)(__float_as_uint((float)c * 0.015625f) >> 16);
+    }
+  }
+}
+
+extern "C" int bw_kv_pool_synthesize_async(bw_kv_pool* p, uint64_t seed, const int32_t* seq_ids_dev,
+                                           const int32_t* seq_lens_dev, const int32_t* page_table_dev,
+                                           int32_t batch, int32_t max_pages, void* stream) {
+  if (!p || !seq_lens_dev || !page_table_dev) return fail(BW_EINVAL, "null argument");
+  if (batch < 1 || max_pages < 1) return fail(BW_EINVAL, "batch and max_pages must be positive");
+  if (batch > 65535) return fail(BW_EINVAL, "batch must be <= 65535");
+  const auto& c = p->m->c;
+  const dim3 grid((unsigned)max_pages, (unsigned)batch, (unsigned)c.n_layers);
+  const int64_t layer_bytes = p->layer_elems * p->es;
+  hipStream_t s = (hipStream_t)stream;
+#define BW_SYNTH_LAUNCH(DT)                                                                                \
+  hipLaunchKernelGGL(k_kv_synth<DT>, grid, dim3(256), 0, s, (uint8_t*)p->data, layer_bytes, p->page_elems,   \
+                     p->n_pages, seed, seq_ids_dev, seq_lens_dev, page_table_dev, max_pages, c.n_kv_heads, \
+                     c.head_dim, p->m->err)
+  if (c.kv_dtype == BW_KV_FP8) BW_SYNTH_LAUNCH(3);
+  else if (c.kv_dtype == BW_KV_F16) BW_SYNTH_LAUNCH(1);
+  else BW_SYNTH_LAUNCH(2);
+#undef BW_SYNTH_LAUNCH
+  if (hipGetLastError() != hipSuccess) return fail(BW_EHIP, "synthesis launch failed");
+  return BW_OK;
+}
+
 extern "C" int bw_kv_pool_synthesize(bw_kv_pool* p, uint64_t seed, const int32_t* seq_ids,
                                      const int32_t* seq_lens, const int32_t* page_table,
                                      int32_t batch, int32_t max_pages) {

@@ -442,3 +442,64 @@ def test_device_errors_are_flagged_not_faults():
         assert e.value.code == bw.BW_ERANGE
     finally:
         s.close()
+
+
+LAYER9B_2L = dict(configs.DENSE_9B, n_layers=2, vocab=512)
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_FP8, LAYER9B_2L], ids=["f16", "fp8", "bf16-9b"])
+def test_pool_synthesis_on_device_matches_host_form(cfg):
+    """bw_kv_pool_synthesize_async (device arrays, caller's stream) writes exactly the bits of the
+    host form on a ragged batch with a permuted page table (lengths 0, 1, 16, 17, 100; sequence ids
+    other than b), slots it does not own stay as they were, and its pages hold the generator's
+    values; a page id out of range and a negative length are flagged, not faulted."""
+    seed, syn_seed = 61, 9001
+    lens = [0, 1, 16, 17, 100]
+    ids = [5, 0, 3, 7, 2]
+    fp8 = cfg["kv_dtype"] == "fp8"
+    edt = np.uint8 if fp8 else np.uint16
+    G, D, L = cfg["n_kv_heads"], cfg["head_dim"], cfg["n_layers"]
+    print(f"[case] device pool synthesis {cfg.get('name', cfg['kv_dtype'])} lens={lens}", flush=True)
+    host = Session(cfg, seed=seed, max_len=[max(n, 1) for n in lens], max_tokens=1, pool_seed=4)
+    dev = Session(cfg, seed=seed, max_len=[max(n, 1) for n in lens], max_tokens=1, pool_seed=4, model=host.model)
+    try:
+        host.poison()
+        dev.poison()
+        host.synthesize(syn_seed, lens, ids)
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        sid = torch.tensor(ids, dtype=torch.int32, device="cuda")
+        bw.bw_kv_pool_synthesize_async(dev.pool, syn_seed, sid, sl, dev.page_table, len(lens), dev.max_pages)
+        torch.cuda.synchronize()
+        assert bw.bw_check_device_error(dev.model) == 0
+        for l in range(L):
+            for p in range(host.n_pages):
+                a = np.empty(G * 2 * 16 * D, dtype=edt)
+                b = np.empty_like(a)
+                bw.bw_kv_pool_read(host.pool, l, p, a)
+                bw.bw_kv_pool_read(dev.pool, l, p, b)
+                assert np.array_equal(a, b), (l, p)
+        # the last sequence's pages against the generator itself
+        bl, n = len(lens) - 1, lens[-1]
+        for l in range(L):
+            want = synth.kv_fill(syn_seed, l, ids[bl], 0, n, G, D, KV_CODE[cfg["kv_dtype"]]).reshape(n, 2, G, D)
+            for lp in range((n + 15) // 16):
+                buf = np.empty(G * 2 * 16 * D, dtype=edt)
+                bw.bw_kv_pool_read(dev.pool, l, int(dev.page_table_host[bl, lp]), buf)
+                got = buf.reshape(G, 2, 16, D)
+                ns = min(16, n - 16 * lp)
+                assert np.array_equal(got[:, :, :ns, :], want[16 * lp:16 * lp + ns].transpose(2, 1, 0, 3)), (l, lp)
+        # range errors from the device: a page id past the pool, then a negative length
+        bad = dev.page_table.clone()
+        bad[4, 0] = dev.n_pages
+        bw.bw_kv_pool_synthesize_async(dev.pool, syn_seed, None, sl, bad, len(lens), dev.max_pages)
+        torch.cuda.synchronize()
+        assert bw.bw_check_device_error(dev.model) & bw.BW_DERR_PAGE
+        neg = torch.tensor([-3, 1, 1, 1, 1], dtype=torch.int32, device="cuda")
+        bw.bw_kv_pool_synthesize_async(dev.pool, syn_seed, None, neg, dev.page_table, len(lens), dev.max_pages)
+        torch.cuda.synchronize()
+        assert bw.bw_check_device_error(dev.model) & bw.BW_DERR_POS
+        assert bw.bw_check_device_error(dev.model) == 0
+        print(f"[result] device pool synthesis bit-identical to the host form over {L} layers x {host.n_pages} pages")
+    finally:
+        dev.close()
+        host.close()
