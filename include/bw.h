@@ -261,6 +261,11 @@ int bw_expert_tier_stats(const bw_expert_tier* tier, int32_t* resident, int32_t*
 
 /* One decode step for `batch` sequences of `t` new tokens each (t = 1: plain decode; t > 1:
  * the verify step of speculative decoding, the t tokens laid out along the sequence).
+ * Defined by the deep-dive page ("Deep dive: bw24", 10100.com): section 5 stage 4 (the verify
+ * kernel takes the drafted tokens along the sequence dimension in one pass), section 6 item 2 (the
+ * paged cache maps logical positions to fixed-size physical pages), and section 1 with the section 7
+ * comparison table (the output equals token-by-token greedy argmax decoding); the bw24 vs
+ * llama.cpp page (devpress.csdn.net) section 2.1 (each new token reads the whole cache).
  *   tokens_dev     int32 [batch * t]   token ids, row b*t + i is token i of sequence b
  *   seq_lens_dev   int32 [batch]       positions already cached BEFORE this call; token i of
  *                                      sequence b is at position seq_lens[b] + i
