@@ -52,8 +52,6 @@ constexpr int kPW = kPT / kWave;   // waves per workgroup
 constexpr uint32_t kRsrc3 = 0x00020000u;
 constexpr int kCohSC1 = 16;        // cache policy: coherent across the XCD L2s
 constexpr float kNoScore = -1.0e30f;               // running max of a split without positions
-// s_sleep between two polls of an exchange, in units of 64 cycles (0 and 8 timed no better)
-constexpr int kPollSleep = 1;
 constexpr int kOOB = 0x7FFFFFF0;  // buffer offset past every buffer: the load returns zero, touches nothing
 // argmax index of a workgroup with no candidate (every logit NaN): the largest index the 30-bit
 // field of an argmax partial holds, so it survives the packing and loses every tie to a real row
@@ -132,7 +130,7 @@ __device__ __forceinline__ void poll_words_wait(__amdgpu_buffer_rsrc_t r, const 
   for (int i = 0; i < N; ++i) all &= idx[i] < 0 || xok(w[i], tag);
   uint32_t flag = 0u;
   while (!all && !give_up(c, flag)) {
-    __builtin_amdgcn_s_sleep(kPollSleep);
+    __builtin_amdgcn_s_sleep(1);
     flag = load_abort(c);
     // branch-free reloads (a word already seen reads past the buffer), so they all go out
     // before the one wait below
@@ -281,7 +279,7 @@ __device__ __forceinline__ void stage_finish(int tid, const uint32_t* xin, uint3
       for (int k = 0; k < 4; ++k) all &= tid + i * kPT >= N4 || xok(v[i][k], tag);
     uint32_t flag = 0u;
     while (!all && !give_up(c, flag)) {
-      __builtin_amdgcn_s_sleep(kPollSleep);
+      __builtin_amdgcn_s_sleep(1);
       flag = load_abort(c);
       all = true;
 #pragma unroll
@@ -1314,7 +1312,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
           for (int k = 0; k < 4; ++k) all &= xok(v[c][k], tout);
         uint32_t flag = 0u;
         while (!all && !give_up(ctl, flag)) {
-          __builtin_amdgcn_s_sleep(kPollSleep);
+          __builtin_amdgcn_s_sleep(1);
           flag = load_abort(ctl);
 #pragma unroll
           for (int c = 0; c < 2; ++c) {  // branch-free reloads, as in stage_finish
@@ -1678,7 +1676,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       ctl.t0 = __builtin_amdgcn_s_memrealtime();
       while ((uint32_t)(word >> 62) != (epoch & 3u)) {
         if (give_up(ctl, __hip_atomic_load(ctl.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) break;
-        __builtin_amdgcn_s_sleep(kPollSleep);
+        __builtin_amdgcn_s_sleep(1);
         word = __hip_atomic_load(p.xarg + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       const float v = __uint_as_float((uint32_t)word);
