@@ -140,7 +140,7 @@ struct PersistParams {
   uint32_t* xm = nullptr;           // [d]: residual after attention
   uint32_t* xf = nullptr;           // [F]: SwiGLU output
   uint32_t* xx = nullptr;           // [d]: residual after the FFN (layer input)
-  uint32_t* xdp = nullptr;          // FFN by columns: [d / 16 owners][workgroups][16] down partials
+  uint32_t* xdp = nullptr;          // FFN by columns: [owners][workgroups][2 x 16-byte-aligned halves] down partials
   int32_t n_xdp = 0;                // words of xdp
   uint64_t* xarg = nullptr;         // [workgroups]: argmax partial (value, index | tag << 30)
   float* logits = nullptr;          // [V] or null
@@ -220,6 +220,7 @@ int launch_persist_reset(const PersistParams& p, int n_q, int n_p, int n_a, int 
 // shape and grid (0: the shape keeps the FFN by rows), and the kernel that writes that copy from
 // the device matrix
 int64_t persist_colffn_bytes(int d, int F, int nwg);
+int64_t persist_colffn_xdp_words(int d, int F, int nwg);  // words of the partial-sum exchange
 int launch_down_slices(const Mat& dn, int nwg, uint8_t* out, hipStream_t s);
 // MoE form (router, top-k and expert phases): -2 when the shape has no instantiation
 int launch_persist_moe(const PersistParams& p, int d, int kv_dtype, int D, int rep, int nwg, hipStream_t s,

@@ -488,70 +488,101 @@ __device__ __forceinline__ void gemv_rest_f(int tid, int r0, int r1, PGroup<LPR,
 }
 
 // ---- dense FFN by columns ---------------------------------------------------------------------
-// Workgroup w computes its gate/up rows (the SwiGLU outputs of ffn columns [Fw w, Fw w + Fw)),
-// keeps those Fw values in LDS and multiplies them at once by the same Fw columns of W_down, for
-// every one of the d rows. The d partial sums go to the owners of the rows, which add the nwg
-// partials of each row to their residual rows. So the FFN streams its gate/up and down weights
-// in one pass with no exchange between them; the F-long SwiGLU vector is never gathered.
-// Shape: d = 4096 (8 rows per thread), F = 12288 over 256 workgroups (Fw = 48 = three 16-column
-// half-blocks; a half-block takes the scale of its 32-column block).
+// Workgroup w computes its gate/up rows (the SwiGLU outputs of ffn columns [C w, C w + C), C =
+// F / 256), keeps those C values in LDS and multiplies them at once by the same C columns of
+// W_down, for every one of the d rows. The d partial sums go to the owners of the rows, which add
+// the 256 partials of each row to their residual rows. So the FFN streams its gate/up and down
+// weights in one pass with no exchange between them; the F-long SwiGLU vector is never gathered.
+// The slice's columns form units of U columns (16 when C is a multiple of 16, else 4); a unit
+// lies inside one 32-column block and takes that block's scale.
+//   9B  (d 4096, F 12288): C 48 = 3 units of 16, 8 rows per thread, 2 blocks per slice at most;
+//   27B (d 5120, F 17408) would take C 68 = 17 units of 4, 10 rows per thread, 3 blocks per slice
+//   at most (laid out and tested, not used: see with_colffn).
 //
 // W_down column-slice copy (written once at load from the device matrix): for slice w and thread
-// t, 14 chunks of 16 bytes at ((w 14 + c) 512 + t) 16, so chunk c of all threads is contiguous:
-//   chunks 0..11: 48 code dwords, dword 6 i + k for row 8 t + i, slice columns 8k..8k+7; nibble n
-//                 (bits 4n..4n+3) holds column 8k + 2n for n < 4 and 8k + 2(n - 4) + 1 otherwise,
-//                 so (dword >> 4m) & 0x000F000F is the fp16-subnormal pair of columns (2m, 2m + 1);
-//   chunks 12, 13: one dword per row i (rows 0..3, then 4..7): the scale of the block of the
-//                 slice's first column (low half) and of its last column (high half).
-constexpr int kCfD = 4096, kCfF = 12288, kCfWG = 256;
-constexpr int kCfW = kCfF / kCfWG;   // ffn columns per workgroup
-constexpr int kCfRT = kCfD / kPT;    // W_down rows per thread
-constexpr int kCfChunks = 14;        // 16-byte chunks per thread
-constexpr int kCfOwn = kCfD / kCfWG; // residual rows per owner
-static_assert(kCfW == 48 && kCfRT == 8 && kCfOwn == 16 && 6 * kCfRT == 4 * 12 && kCfRT == 2 * 4,
-              "FFN-by-columns geometry");
+// t, CH chunks of 16 bytes at ((w CH + c) 512 + t) 16, so chunk c of all threads is contiguous.
+// The thread's words, in order:
+//   code words: the RT rows' C codes each, flat code f = i C + c (row RT t + i, slice column c)
+//               in word f / 8; nibble n (bits 4n..4n+3) of a word holds flat code 8 (f / 8) + 2n
+//               for n < 4 and 8 (f / 8) + 2 (n - 4) + 1 otherwise, so (word >> 4m) & 0x000F000F
+//               is the fp16-subnormal pair of flat codes (2m, 2m + 1), which C even keeps in one row;
+//   scale words: fp16 e = i S + b (row i, b-th block the slice touches, S blocks at most per
+//               slice) in word e / 2, half e % 2 (zero past the slice's last block);
+//   zero words up to the chunk boundary.
+constexpr int kCfWG = 256;  // workgroups of the layout (one slice each)
 
-struct CfSlice {
-  u32x4 q[kCfChunks];
+template <int KD_, int KF_>
+struct CfGeo {
+  static constexpr int COLS = KF_ / kCfWG;               // ffn columns per workgroup
+  static constexpr int UW = COLS % 16 == 0 ? 16 : 4;     // columns per unit
+  static constexpr int NU = COLS / UW;
+  static constexpr int RT = KD_ / kPT;                   // W_down rows per thread
+  static constexpr int OWN = KD_ / kCfWG;                // residual rows per owner (= 2 RT)
+  static constexpr int RTP = (RT + 3) & ~3;              // words of half a partial record (16-byte aligned)
+  static constexpr int span() {                          // blocks one slice touches, at most
+    int m = 0;
+    for (int w = 0; w < kCfWG; ++w) {
+      const int b = ((w * COLS + COLS - 1) >> 5) - ((w * COLS) >> 5) + 1;
+      m = b > m ? b : m;
+    }
+    return m;
+  }
+  static constexpr int NSB = span();
+  static constexpr int CDW = RT * COLS / 8;              // code words per thread
+  static constexpr int SDW = (RT * NSB + 1) / 2;         // scale words per thread
+  static constexpr int CH = (CDW + SDW + 3) / 4;         // 16-byte chunks per thread
+  static constexpr int XS = 96;                          // LDS offset of the unit sums after the C values
+  static_assert(KF_ % kCfWG == 0 && COLS % 4 == 0 && (RT * COLS) % 8 == 0 && OWN == 2 * RT && RT % 2 == 0 &&
+                    COLS <= XS && XS + NU <= 128 && NSB <= 4,
+                "FFN-by-columns geometry");
 };
 
 // this thread's chunks of slice w (every load unconditional, non-temporal)
-__device__ __forceinline__ void cf_issue(int tid, const uint8_t* dnc, int w, CfSlice& d) {
-  const __amdgpu_buffer_rsrc_t r = uniform_rsrc(dnc + (int64_t)w * kCfChunks * kPT * 16, kCfChunks * kPT * 16);
+template <class G>
+__device__ __forceinline__ void cf_issue(int tid, const uint8_t* dnc, int w, u32x4 (&q)[G::CH]) {
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc(dnc + (int64_t)w * G::CH * kPT * 16, G::CH * kPT * 16);
 #pragma unroll
-  for (int c = 0; c < kCfChunks; ++c) d.q[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c * kPT + tid) * 16, 0, kNT);
+  for (int c = 0; c < G::CH; ++c) q[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c * kPT + tid) * 16, 0, kNT);
 }
 
-// the 8 partial sums sum_j s_j sum_{c in half-block j} (q_c - 8) x_c of this thread's rows;
-// xc: the slice's 48 SwiGLU values, then the sums of its three half-blocks (LDS)
-__device__ __forceinline__ void cf_partials(const CfSlice& d, const float* xc, bool odd_w, float (&out)[kCfRT]) {
-  float4 xv[12];
+// the RT partial sums sum_u s_b(u) sum_{c in unit u} (q_c - 8) x_c of this thread's rows, units in
+// order; xc: the slice's C SwiGLU values, then (at XS) the sums of its units (LDS); col0 = C w
+template <class G>
+__device__ __forceinline__ void cf_partials(const u32x4 (&q)[G::CH], const float* xc, int col0, float (&out)[G::RT]) {
 #pragma unroll
-  for (int k = 0; k < 12; ++k) xv[k] = *(const float4*)(xc + 4 * k);
-  const float hs[3] = {xc[48], xc[49], xc[50]};
+  for (int i = 0; i < G::RT; ++i) out[i] = 0.f;
 #pragma unroll
-  for (int i = 0; i < kCfRT; ++i) {
-    float dj[3];
+  for (int u = 0; u < G::NU; ++u) {
+    const int rb = ((col0 + G::UW * u) >> 5) - (col0 >> 5);  // the unit's block among the slice's (uniform)
+    float xv[G::UW];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int c = 0; c < G::UW; c += 4) {
+      const float4 v = *(const float4*)(xc + G::UW * u + c);
+      xv[c] = v.x;
+      xv[c + 1] = v.y;
+      xv[c + 2] = v.z;
+      xv[c + 3] = v.w;
+    }
+    const float su = xc[G::XS + u];
+#pragma unroll
+    for (int i = 0; i < G::RT; ++i) {
       float acc = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int k = 2 * j + kk, li = 6 * i + k;
-        const uint32_t q = d.q[li >> 2][li & 3];
-        const float4 a = xv[2 * k], b = xv[2 * k + 1];  // columns 8k..8k+3, 8k+4..8k+7
-        acc = mix2(q & 0x000F000Fu, a.x, a.y, acc);
-        acc = mix2((q >> 4) & 0x000F000Fu, a.z, a.w, acc);
-        acc = mix2((q >> 8) & 0x000F000Fu, b.x, b.y, acc);
-        acc = mix2((q >> 12) & 0x000F000Fu, b.z, b.w, acc);
+      for (int pr = 0; pr < G::UW / 2; ++pr) {
+        const int f = i * G::COLS + G::UW * u + 2 * pr, k = f >> 3, m = (f & 7) >> 1;
+        acc = mix2((q[k >> 2][k & 3] >> (4 * m)) & 0x000F000Fu, xv[2 * pr], xv[2 * pr + 1], acc);
       }
-      dj[j] = fmaf(16777216.0f, acc, -8.0f * hs[j]);
+      const float d = fmaf(16777216.0f, acc, -8.0f * su);
+      float sv = 0.f;
+#pragma unroll
+      for (int b = 0; b < G::NSB; ++b) {
+        const int e = i * G::NSB + b, k = G::CDW + (e >> 1);
+        const uint32_t sw = q[k >> 2][k & 3];
+        const float sb = f16_to_f32((uint16_t)((e & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+        sv = b == 0 ? sb : (rb == b ? sb : sv);
+      }
+      out[i] = fmaf(sv, d, out[i]);
     }
-    const uint32_t sw = d.q[12 + (i >> 2)][i & 3];
-    const float s_first = f16_to_f32((uint16_t)(sw & 0xFFFFu)), s_last = f16_to_f32((uint16_t)(sw >> 16));
-    // half-block 1 lies in the first column's block for an even slice, in the last one's for an odd one
-    const float s_mid = odd_w ? s_last : s_first;
-    out[i] = fmaf(s_last, dj[2], fmaf(s_mid, dj[1], s_first * dj[0]));
   }
 }
 
@@ -1236,7 +1267,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     }
 
     if constexpr (COLF) {
-    static_assert(!MOE && KD == kCfD && KF == kCfF && LPR_D == 64 && NB_D == 2, "FFN by columns: 9B shape");
+    using CG = CfGeo<KD, KF>;
+    static_assert(!MOE, "FFN by columns: dense models");
     // ================= gate/up + SwiGLU + down by columns =================
     // The W_down slice goes out in place of the gate/up pass's last next-group load, so the two
     // matrices stream back to back; the SwiGLU values stay in LDS.
@@ -1244,8 +1276,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
     {
       const int tid = phase_tid();
       constexpr int GROUP = (kWave / LPR_D) * RWG;
-      constexpr int NG = 2 * kCfW / GROUP / kPW;  // groups per wave
-      static_assert(NG * GROUP * kPW == 2 * kCfW, "gate/up rows split evenly over the waves");
+      constexpr int NG = (2 * CG::COLS + GROUP * kPW - 1) / (GROUP * kPW);  // groups per wave (the last may be empty)
       const int wave = wave_of(tid);
       XStage<KD> xin;
       stage_issue<KD, true>(tid, p.xm, Ly.ffn_norm, xin);
@@ -1255,104 +1286,114 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
       stage_finish<KD, true>(tid, p.xm, tout, p.eps, xin, s, ctl);
       if (bail) return;
       stamp(p, l * 16 + 9);
-      CfSlice dq;
+      u32x4 dq[CG::CH];
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         if (i + 1 < NG) pload<LPR_D, NB_D, RWG>(tid, Ly.gu, g0, g1, wave + (i + 1) * kPW, ga[(i + 1) & 1]);
-        else cf_issue(tid, Ly.dnc, w, dq);
+        else cf_issue<CG>(tid, Ly.dnc, w, dq);
         pcompute<LPR_D, NB_D, RWG>(tid, ga[i & 1], g0, g1, s);
       }
       __syncthreads();
-      // the slice's SwiGLU values and the sums of its three half-blocks (lanes 0..47 of wave 0)
-      if (tid < kWave) {
+      // the slice's SwiGLU values and the sums of its units (waves 0 and 1)
+      if (tid < 2 * kWave) {
         float v = 0.f;
-        if (tid < kCfW) {
+        if (tid < CG::COLS) {
           v = silu(s.ydot[2 * tid]) * s.ydot[2 * tid + 1];
           s.xs[tid] = v;
         }
-        v = sum8(v);
-        v += xor8(v);
-        if (tid < kCfW && (tid & 15) == 0) s.xs[kCfW + (tid >> 4)] = v;
+        v = sum_lanes(v, CG::UW);
+        if (tid < CG::COLS && tid % CG::UW == 0) s.xs[CG::XS + tid / CG::UW] = v;
       }
       __syncthreads();
-      float part[kCfRT];
-      cf_partials(dq, s.xs, (w & 1) != 0, part);
-      // rows 8 t .. 8 t + 7 belong to owner t / 2, at 8 (t % 2) of this producer's 16 words
+      float part[CG::RT];
+      cf_partials<CG>(dq, s.xs, w * CG::COLS, part);
+      // rows RT t .. RT t + RT - 1 belong to owner t / 2, at RTP (t % 2) of this producer's record
       const __amdgpu_buffer_rsrc_t rp = xrsrc(p.xdp, (int64_t)p.n_xdp * 4);
-      const int off = (((tid >> 1) * kCfWG + w) * kCfOwn + (tid & 1) * 8) * 4;
-      u32x4 a, b;
+      const int off = (((tid >> 1) * kCfWG + w) * (2 * CG::RTP) + (tid & 1) * CG::RTP) * 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = xenc(part[i], tout);
-        b[i] = xenc(part[4 + i], tout);
+      for (int c = 0; c < CG::RT / 4; ++c) {
+        u32x4 a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = xenc(part[4 * c + i], tout);
+        __builtin_amdgcn_raw_buffer_store_b128(a, rp, off + 16 * c, 0, kCohSC1);
       }
-      __builtin_amdgcn_raw_buffer_store_b128(a, rp, off, 0, kCohSC1);
-      __builtin_amdgcn_raw_buffer_store_b128(b, rp, off + 16, 0, kCohSC1);
+      if constexpr (CG::RT % 4 != 0) {
+        u32x2 a;
+        a[0] = xenc(part[CG::RT - 2], tout);
+        a[1] = xenc(part[CG::RT - 1], tout);
+        __builtin_amdgcn_raw_buffer_store_b64(a, rp, off + 16 * (CG::RT / 4), 0, kCohSC1);
+      }
     }
 
     // ================= down partials -> owned residual rows =================
-    // Thread t reads producer t / 2's partials of rows 8 (t % 2) .. + 7; the 32 producers of a
-    // wave are summed across lanes of equal parity, the 8 waves in LDS (fixed order).
+    // Thread t reads producer t / 2's partials of its RT rows; the 256 producers of each of the OWN
+    // rows are summed through LDS in a fixed order.
     stamp(p, l * 16 + 10);
     {
       const int tid = phase_tid();
-      const int lane = tid & 63, wave = wave_of(tid);
+      constexpr int N4 = CG::RT / 4, N2 = (CG::RT % 4) / 2;
       const __amdgpu_buffer_rsrc_t rp = xrsrc(p.xdp, (int64_t)p.n_xdp * 4);
-      const int off = ((w * kCfWG + (tid >> 1)) * kCfOwn + (tid & 1) * 8) * 4;
+      const int off = ((w * kCfWG + (tid >> 1)) * (2 * CG::RTP) + (tid & 1) * CG::RTP) * 4;
       const uint32_t nxt = ltab_issue(p, l + 1, tid);
-      u32x4 v[2];
-      v[0] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCohSC1);
-      v[1] = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16, 0, kCohSC1);
+      u32x4 v[N4 > 0 ? N4 : 1];
+      u32x2 v2 = {0u, 0u};
+#pragma unroll
+      for (int c = 0; c < N4; ++c) v[c] = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16 * c, 0, kCohSC1);
+      if constexpr (N2) v2 = __builtin_amdgcn_raw_buffer_load_b64(rp, off + 16 * N4, 0, kCohSC1);
       {
+        auto ok4 = [&](const u32x4& a) { return xok(a[0], tout) && xok(a[1], tout) && xok(a[2], tout) && xok(a[3], tout); };
+        auto ok2 = [&](const u32x2& a) { return !N2 || (xok(a[0], tout) && xok(a[1], tout)); };
+        auto all_ok = [&]() {
+          bool all = ok2(v2);
+#pragma unroll
+          for (int c = 0; c < N4; ++c) all &= ok4(v[c]);
+          return all;
+        };
         ctl.t0 = __builtin_amdgcn_s_memrealtime();
-        bool all = true;
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) all &= xok(v[c][k], tout);
+        bool all = all_ok();
         uint32_t flag = 0u;
         while (!all && !give_up(ctl, flag)) {
           __builtin_amdgcn_s_sleep(1);
           flag = load_abort(ctl);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {  // branch-free reloads, as in stage_finish
-            bool ok = true;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) ok &= xok(v[c][k], tout);
+          for (int c = 0; c < N4; ++c) {  // branch-free reloads, as in stage_finish
+            const bool ok = ok4(v[c]);
             const u32x4 nv = __builtin_amdgcn_raw_buffer_load_b128(rp, ok ? kOOB : off + 16 * c, 0, kCohSC1);
             v[c] = ok ? v[c] : nv;
           }
-          all = true;
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) all &= xok(v[c][k], tout);
+          if constexpr (N2) {
+            const bool ok = ok2(v2);
+            const u32x2 nv = __builtin_amdgcn_raw_buffer_load_b64(rp, ok ? kOOB : off + 16 * N4, 0, kCohSC1);
+            v2 = ok ? v2 : nv;
+          }
+          all = all_ok();
         }
       }
       stamp(p, l * 16 + 11);
       if (tid < kLW) s.ltab[((l + 1) & 1) * kLW + tid] = nxt;
-      // transpose through LDS: [producer][16 rows] (past the 51 words the FFN phase may still read)
-      float* tp = s.xs + 64;
-      *(float4*)(tp + 8 * tid) = make_float4(xdec(v[0][0]), xdec(v[0][1]), xdec(v[0][2]), xdec(v[0][3]));
-      *(float4*)(tp + 8 * tid + 4) = make_float4(xdec(v[1][0]), xdec(v[1][1]), xdec(v[1][2]), xdec(v[1][3]));
+      // transpose through LDS: [producer][OWN rows] (past the unit sums the FFN phase may still read)
+      float* tp = s.xs + 128;
+#pragma unroll
+      for (int c = 0; c < N4; ++c) {
+        *(float2*)(tp + CG::RT * tid + 4 * c) = make_float2(xdec(v[c][0]), xdec(v[c][1]));
+        *(float2*)(tp + CG::RT * tid + 4 * c + 2) = make_float2(xdec(v[c][2]), xdec(v[c][3]));
+      }
+      if constexpr (N2) *(float2*)(tp + CG::RT * tid + 4 * N4) = make_float2(xdec(v2[0]), xdec(v2[1]));
       __syncthreads();
       if (bail) return;
-      // thread t: row t % 16 over producers t / 16 + 32 j; then the wave's four producer groups
-      // (lanes of equal t % 16) and the 8 waves (fixed order)
-      float* red = s.mrg;  // [kPW][16]
-      {
-        const int r = tid & 15, pg = tid >> 4;
+      // thread t < 16 OWN: row t % OWN over producers t / OWN + 16 j; then the 16 groups (fixed order)
+      float* red = s.mrg;  // [16][OWN]
+      if (tid < 16 * CG::OWN) {
         float x = 0.f;
 #pragma unroll
-        for (int j = 0; j < kCfWG / 32; ++j) x += tp[(pg + 32 * j) * kCfOwn + r];
-        x = sum_xor32(sum_xor16(x));
-        if (lane < kCfOwn) red[wave * kCfOwn + lane] = x;
+        for (int j = 0; j < kCfWG / 16; ++j) x += tp[tid + 16 * j * CG::OWN];
+        red[tid] = x;
       }
       __syncthreads();
-      if (tid < kCfOwn) {
+      if (tid < CG::OWN) {
         float dsum = 0.f;
 #pragma unroll
-        for (int wv = 0; wv < kPW; ++wv) dsum += red[wv * kCfOwn + tid];
+        for (int g = 0; g < 16; ++g) dsum += red[g * CG::OWN + tid];
         const float r = s.resid[tid] + dsum;
         s.resid[tid] = r;
         xstore(p.xx, d0 + tid, r, tout);
@@ -1766,36 +1807,53 @@ static int launch_persist_t(const PersistParams& p, int nwg, hipStream_t s, bool
 
 // Shapes with an instantiation: (d, ffn, head dim, query heads per KV head) with the row steps
 // per wave group sized for 256 workgroups
-int64_t persist_colffn_bytes(int d, int F, int nwg) {
-  return d == kCfD && F == kCfF && nwg == kCfWG ? (int64_t)kCfWG * kCfChunks * kPT * 16 : 0;
+// shapes laid out for the FFN by columns (on 256 workgroups). The 27B shape (68 columns, units of
+// 4) passes the same tests but timed no faster than its FFN by rows (4109 against 4089 us per
+// step): its longer slice arithmetic is exposed at the end of the fused pass, so it keeps the rows.
+template <class F>
+static int64_t with_colffn(int d, int ffn, int nwg, F&& f) {
+  if (nwg != kCfWG) return 0;
+  if (d == 4096 && ffn == 12288) return f(CfGeo<4096, 12288>{});
+  return 0;
 }
 
-// One 16-byte chunk (slice w, chunk c, thread t) of the W_down column-slice copy per thread (see
-// cf_issue for the layout), from the device matrix (codes [d][F/2], scales tiled [d][lpr][nb]).
+int64_t persist_colffn_bytes(int d, int F, int nwg) {
+  return with_colffn(d, F, nwg, [](auto g) { return (int64_t)kCfWG * decltype(g)::CH * kPT * 16; });
+}
+
+int64_t persist_colffn_xdp_words(int d, int F, int nwg) {
+  return with_colffn(d, F, nwg, [](auto g) { return (int64_t)kCfWG * kCfWG * 2 * decltype(g)::RTP; });
+}
+
+// One 16-byte chunk (slice w, chunk c, thread t) of the W_down column-slice copy (see the layout
+// above cf_issue), from the device matrix (codes [d][F/2], scales tiled [d][lpr][nb]).
+template <class G>
 __global__ void k_down_slices(Mat dn, uint8_t* out) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= (int64_t)kCfWG * kCfChunks * kPT) return;
-  const int t = (int)(g % kPT), c = (int)((g / kPT) % kCfChunks), w = (int)(g / ((int64_t)kPT * kCfChunks));
-  const int nblk = dn.K / 32, col0 = w * kCfW;
-  auto scale = [&](int row, int col) {
-    const int b = col / 32;
-    return dn.scales[(int64_t)row * nblk + (b % dn.lpr) * dn.nb + b / dn.lpr];
+  if (g >= (int64_t)kCfWG * G::CH * kPT) return;
+  const int t = (int)(g % kPT), c = (int)((g / kPT) % G::CH), w = (int)(g / ((int64_t)kPT * G::CH));
+  const int nblk = dn.K / 32, col0 = w * G::COLS, b0 = col0 >> 5, b_last = (col0 + G::COLS - 1) >> 5;
+  auto scale = [&](int row, int b) {
+    return b > b_last ? (uint16_t)0 : dn.scales[(int64_t)row * nblk + (b % dn.lpr) * dn.nb + b / dn.lpr];
   };
   u32x4 v;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
+    const int k = 4 * c + e;
     uint32_t word = 0u;
-    if (c < 12) {
-      const int li = 4 * c + e, i = li / 6, k = li % 6, row = kCfRT * t + i;
+    if (k < G::CDW) {
       for (int n = 0; n < 8; ++n) {
-        const int col = col0 + 8 * k + (n < 4 ? 2 * n : 2 * (n - 4) + 1), in = col % 32;
+        const int f = 8 * k + (n < 4 ? 2 * n : 2 * (n - 4) + 1);
+        const int row = G::RT * t + f / G::COLS, col = col0 + f % G::COLS, in = col % 32;
         const uint8_t byte = dn.codes[(int64_t)row * (dn.K / 2) + (col / 32) * 16 + (in % 16)];
         const uint32_t q = in < 16 ? (byte & 15u) : (byte >> 4);
         word |= q << (4 * n);
       }
-    } else {
-      const int row = kCfRT * t + 4 * (c - 12) + e;
-      word = (uint32_t)scale(row, col0) | ((uint32_t)scale(row, col0 + kCfW - 1) << 16);
+    } else if (k < G::CDW + G::SDW) {
+      for (int h = 0; h < 2; ++h) {
+        const int sidx = 2 * (k - G::CDW) + h, i = sidx / G::NSB, b = sidx % G::NSB;
+        if (i < G::RT) word |= (uint32_t)scale(G::RT * t + i, b0 + b) << (16 * h);
+      }
     }
     v[e] = word;
   }
@@ -1803,16 +1861,21 @@ __global__ void k_down_slices(Mat dn, uint8_t* out) {
 }
 
 int launch_down_slices(const Mat& dn, int nwg, uint8_t* out, hipStream_t s) {
-  if (persist_colffn_bytes(dn.N, dn.K, nwg) == 0) return -2;
-  const int64_t n = (int64_t)kCfWG * kCfChunks * kPT;
-  hipLaunchKernelGGL(k_down_slices, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dn, out);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  int rc = -2;  // no layout for this shape
+  with_colffn(dn.N, dn.K, nwg, [&](auto g) -> int64_t {
+    using G = decltype(g);
+    const int64_t n = (int64_t)kCfWG * G::CH * kPT;
+    hipLaunchKernelGGL(k_down_slices<G>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dn, out);
+    rc = hipGetLastError() == hipSuccess ? 0 : -1;
+    return 1;
+  });
+  return rc;
 }
 
 int launch_persist(const PersistParams& p, int d, int F, int kv_dtype, int D, int rep, int nwg, hipStream_t s,
                    bool query_only) {
   // the 9B shape on 256 workgroups: the FFN by columns
-  if (persist_colffn_bytes(d, F, nwg) > 0 && D == 128 && rep == 4) {
+  if (persist_colffn_bytes(d, F, nwg) > 0 && D == 128 && d == 4096 && rep == 4) {
     if (kv_dtype == 1) return launch_persist_t<64, 2, 64, 6, 1, 128, 4, 3, 2, 2, 1, false, true>(p, nwg, s, query_only);
     if (kv_dtype == 2) return launch_persist_t<64, 2, 64, 6, 2, 128, 4, 3, 2, 2, 1, false, true>(p, nwg, s, query_only);
     if (kv_dtype == 3) return launch_persist_t<64, 2, 64, 6, 3, 128, 4, 3, 2, 2, 1, false, true>(p, nwg, s, query_only);

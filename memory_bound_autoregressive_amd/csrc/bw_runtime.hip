@@ -410,7 +410,7 @@ static int persist_setup(bw_model* m) {
   }
   void* ptr;
   if (dnc_bytes > 0) {
-    p.n_xdp = d * nwg;  // d / 16 owners x nwg producers x 16 rows
+    p.n_xdp = (int32_t)persist_colffn_xdp_words(d, F, nwg);  // owners x producers x one record each
     if (int rc = ws_alloc(m, sizeof(uint32_t) * (size_t)p.n_xdp, &ptr)) return rc;
     p.xdp = (uint32_t*)ptr;
   }

@@ -318,6 +318,28 @@ def test_single_launch_matches_chain_over_many_steps():
         b.close()
 
 
+def test_single_launch_9b_layers_against_the_oracle_over_many_steps():
+    """Two layers of the 9B shape (every matrix at its real size: the FFN by columns and its
+    partial-sum exchange) over 64 single-launch steps from an empty cache, teacher-forced with
+    seeded tokens, every step against the fp64 oracle at the contract tolerance (logits within
+    2e-2, tokens equal wherever the top-2 margin exceeds 1e-2): 64 epochs of the exchange tags,
+    every page and the ragged last one."""
+    seed = 1043
+    toks = np.random.default_rng(seed).integers(0, DENSE_9B_2L["vocab"], 64)
+    print(f"[case] 9b-2l single launch, 64 steps against the oracle", flush=True)
+    p = Pair(DENSE_9B_2L, seed, 65, single=True)
+    try:
+        assert p.single
+        worst = 0.0
+        for i, tok in enumerate(toks):
+            g, gam, o = p.step([int(tok)])
+            worst = max(worst, _compare(g, gam, o, f"9b-2l step {i}"))
+        assert bw.bw_check_device_error(p.s.model) == 0
+        print(f"[result] 9b-2l single launch, 64 steps: max |logit diff| against the oracle = {worst:.3e}")
+    finally:
+        p.close()
+
+
 def test_single_launch_timeout_is_reported_and_recovers():
     """A wait that passes its deadline ends the single-launch step on every workgroup with
     BW_DERR_PERSIST (forced here with a zero deadline); later steps return at once until the
