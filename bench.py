@@ -204,8 +204,8 @@ def committed_traffic(workload: str, cfg: dict, ctx: float):
     WRITE_SIZE profile of this workload whose kernel sources are unchanged and whose contexts lie
     within 64 positions of ctx (a workload may have profiles at several contexts); else None."""
     names = {"dense-9b": ["step_dense9b_traffic.json", "step_dense9b_traffic_ctx2600.json"],
-             "dense-27b": ["step_dense27b_traffic.json", "step_dense27b_traffic_ctx8452.json"],
-             "moe-35b-a3b": ["step_moe35b_traffic.json", "step_moe35b_traffic_ctx4612.json"]}.get(workload)
+             "dense-27b": ["step_dense27b_traffic_ctx8452.json"],
+             "moe-35b-a3b": ["step_moe35b_traffic_ctx4612.json"]}.get(workload)
     kv = cfg.get("kv_dtype", "bf16")
     if names is None or kv != "bf16":
         return None
