@@ -501,14 +501,15 @@ __device__ __forceinline__ void gemv_rest_f(int tid, int r0, int r1, PGroup<LPR,
 //
 // W_down column-slice copy (written once at load from the device matrix): for slice w and thread
 // t, CH chunks of 16 bytes at ((w CH + c) 512 + t) 16, so chunk c of all threads is contiguous.
-// The thread's words, in order:
-//   code words: the RT rows' C codes each, flat code f = i C + c (row RT t + i, slice column c)
-//               in word f / 8; nibble n (bits 4n..4n+3) of a word holds flat code 8 (f / 8) + 2n
+// The thread's RT rows go in pairs (rows RT t + 2j, RT t + 2j + 1), PW words per pair, so a pair
+// can be computed as soon as its words have arrived (loads complete in issue order):
+//   code words: the pair's 2 C codes, flat code f = r C + c (row 2j + r, slice column c) in word
+//               f / 8 of the pair; nibble n (bits 4n..4n+3) of a word holds flat code 8 (f / 8) + 2n
 //               for n < 4 and 8 (f / 8) + 2 (n - 4) + 1 otherwise, so (word >> 4m) & 0x000F000F
 //               is the fp16-subnormal pair of flat codes (2m, 2m + 1), which C even keeps in one row;
-//   scale words: fp16 e = i S + b (row i, b-th block the slice touches, S blocks at most per
-//               slice) in word e / 2, half e % 2 (zero past the slice's last block);
-//   zero words up to the chunk boundary.
+//   scale words: fp16 e = r S + b (row 2j + r, b-th block the slice touches, S blocks at most per
+//               slice) in word 2 C / 8 + e / 2 of the pair, half e % 2 (zero past the slice's last block);
+// and zero words up to the chunk boundary after the last pair.
 constexpr int kCfWG = 256;  // workgroups of the layout (one slice each)
 
 template <int KD_, int KF_>
@@ -528,11 +529,11 @@ struct CfGeo {
     return m;
   }
   static constexpr int NSB = span();
-  static constexpr int CDW = RT * COLS / 8;              // code words per thread
-  static constexpr int SDW = (RT * NSB + 1) / 2;         // scale words per thread
-  static constexpr int CH = (CDW + SDW + 3) / 4;         // 16-byte chunks per thread
+  static constexpr int PCW = 2 * COLS / 8;               // code words of a row pair
+  static constexpr int PW = PCW + NSB;                   // words of a row pair (2 NSB scales)
+  static constexpr int CH = (RT / 2 * PW + 3) / 4;       // 16-byte chunks per thread
   static constexpr int XS = 96;                          // LDS offset of the unit sums after the C values
-  static_assert(KF_ % kCfWG == 0 && COLS % 4 == 0 && (RT * COLS) % 8 == 0 && OWN == 2 * RT && RT % 2 == 0 &&
+  static_assert(KF_ % kCfWG == 0 && COLS % 4 == 0 && (2 * COLS) % 8 == 0 && OWN == 2 * RT && RT % 2 == 0 &&
                     COLS <= XS && XS + NU <= 128 && NSB <= 4,
                 "FFN-by-columns geometry");
 };
@@ -546,43 +547,46 @@ __device__ __forceinline__ void cf_issue(int tid, const uint8_t* dnc, int w, u32
 }
 
 // the RT partial sums sum_u s_b(u) sum_{c in unit u} (q_c - 8) x_c of this thread's rows, units in
-// order; xc: the slice's C SwiGLU values, then (at XS) the sums of its units (LDS); col0 = C w
+// order, row pairs in load order; xc: the slice's C SwiGLU values, then (at XS) the sums of its
+// units (LDS); col0 = C w
 template <class G>
 __device__ __forceinline__ void cf_partials(const u32x4 (&q)[G::CH], const float* xc, int col0, float (&out)[G::RT]) {
+  float xv[G::COLS], su[G::NU];
 #pragma unroll
-  for (int i = 0; i < G::RT; ++i) out[i] = 0.f;
+  for (int c = 0; c < G::COLS; c += 4) {
+    const float4 v = *(const float4*)(xc + c);
+    xv[c] = v.x;
+    xv[c + 1] = v.y;
+    xv[c + 2] = v.z;
+    xv[c + 3] = v.w;
+  }
 #pragma unroll
-  for (int u = 0; u < G::NU; ++u) {
-    const int rb = ((col0 + G::UW * u) >> 5) - (col0 >> 5);  // the unit's block among the slice's (uniform)
-    float xv[G::UW];
+  for (int u = 0; u < G::NU; ++u) su[u] = xc[G::XS + u];
 #pragma unroll
-    for (int c = 0; c < G::UW; c += 4) {
-      const float4 v = *(const float4*)(xc + G::UW * u + c);
-      xv[c] = v.x;
-      xv[c + 1] = v.y;
-      xv[c + 2] = v.z;
-      xv[c + 3] = v.w;
-    }
-    const float su = xc[G::XS + u];
+  for (int i = 0; i < G::RT; ++i) {
+    const int base = (i >> 1) * G::PW, r = i & 1;  // the row's pair and its place in the pair
+    float o = 0.f;
 #pragma unroll
-    for (int i = 0; i < G::RT; ++i) {
+    for (int u = 0; u < G::NU; ++u) {
+      const int rb = ((col0 + G::UW * u) >> 5) - (col0 >> 5);  // the unit's block among the slice's (uniform)
       float acc = 0.f;
 #pragma unroll
       for (int pr = 0; pr < G::UW / 2; ++pr) {
-        const int f = i * G::COLS + G::UW * u + 2 * pr, k = f >> 3, m = (f & 7) >> 1;
-        acc = mix2((q[k >> 2][k & 3] >> (4 * m)) & 0x000F000Fu, xv[2 * pr], xv[2 * pr + 1], acc);
+        const int f = r * G::COLS + G::UW * u + 2 * pr, k = base + (f >> 3), m = (f & 7) >> 1;
+        acc = mix2((q[k >> 2][k & 3] >> (4 * m)) & 0x000F000Fu, xv[G::UW * u + 2 * pr], xv[G::UW * u + 2 * pr + 1], acc);
       }
-      const float d = fmaf(16777216.0f, acc, -8.0f * su);
+      const float d = fmaf(16777216.0f, acc, -8.0f * su[u]);
       float sv = 0.f;
 #pragma unroll
       for (int b = 0; b < G::NSB; ++b) {
-        const int e = i * G::NSB + b, k = G::CDW + (e >> 1);
+        const int e = r * G::NSB + b, k = base + G::PCW + (e >> 1);
         const uint32_t sw = q[k >> 2][k & 3];
         const float sb = f16_to_f32((uint16_t)((e & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
         sv = b == 0 ? sb : (rb == b ? sb : sv);
       }
-      out[i] = fmaf(sv, d, out[i]);
+      o = fmaf(sv, d, o);
     }
+    out[i] = o;
   }
 }
 
@@ -1839,20 +1843,20 @@ __global__ void k_down_slices(Mat dn, uint8_t* out) {
   u32x4 v;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int k = 4 * c + e;
+    const int kw = 4 * c + e, j = kw / G::PW, k = kw % G::PW;  // row pair j, word k of the pair
     uint32_t word = 0u;
-    if (k < G::CDW) {
+    if (j < G::RT / 2 && k < G::PCW) {
       for (int n = 0; n < 8; ++n) {
         const int f = 8 * k + (n < 4 ? 2 * n : 2 * (n - 4) + 1);
-        const int row = G::RT * t + f / G::COLS, col = col0 + f % G::COLS, in = col % 32;
+        const int row = G::RT * t + 2 * j + f / G::COLS, col = col0 + f % G::COLS, in = col % 32;
         const uint8_t byte = dn.codes[(int64_t)row * (dn.K / 2) + (col / 32) * 16 + (in % 16)];
         const uint32_t q = in < 16 ? (byte & 15u) : (byte >> 4);
         word |= q << (4 * n);
       }
-    } else if (k < G::CDW + G::SDW) {
+    } else if (j < G::RT / 2) {
       for (int h = 0; h < 2; ++h) {
-        const int sidx = 2 * (k - G::CDW) + h, i = sidx / G::NSB, b = sidx % G::NSB;
-        if (i < G::RT) word |= (uint32_t)scale(G::RT * t + i, b0 + b) << (16 * h);
+        const int sidx = 2 * (k - G::PCW) + h, r = sidx / G::NSB, b = sidx % G::NSB;
+        if (r < 2) word |= (uint32_t)scale(G::RT * t + 2 * j + r, b0 + b) << (16 * h);
       }
     }
     v[e] = word;
