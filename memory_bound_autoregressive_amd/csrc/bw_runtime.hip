@@ -734,7 +734,7 @@ __global__ void k_kv_synth(uint8_t* pool, int64_t layer_bytes, int64_t page_elem
                            const int32_t* __restrict__ page_table, int max_pages, int G, int D, int32_t* err) {
   const int lp = blockIdx.x, b = blockIdx.y, l = blockIdx.z;
   const int len = seq_lens[b];
-  const int np = len < 0 ? 0 : (len + kPageTokens - 1) / kPageTokens;
+  const int64_t np = len < 0 ? 0 : ((int64_t)len + kPageTokens - 1) / kPageTokens;  // no overflow near INT_MAX
   if (lp == 0 && l == 0 && threadIdx.x == 0 && (len < 0 || np > max_pages)) atomicOr(err, BW_DERR_POS);
   if (lp >= np || lp >= max_pages) return;
   const int page = page_table[(int64_t)b * max_pages + lp];
