@@ -54,6 +54,10 @@ def test_null_and_shape_errors_are_reported_without_a_gpu():
     assert L.bw_kv_pool_free(None) == bw.BW_OK
     assert L.bw_check_device_error(None, None, None) == bw.BW_EINVAL
     assert L.bw_debug_kv_round(3, None, 1, None, None, None) == bw.BW_EINVAL
+    # both pool-synthesis forms refuse a null pool or array before touching the GPU
+    assert L.bw_kv_pool_synthesize(None, 1, None, None, None, 1, 1) == bw.BW_EINVAL
+    assert L.bw_kv_pool_synthesize_async(None, 1, None, None, None, 1, 1, None) == bw.BW_EINVAL
+    assert "null" in bw.bw_last_error()
     cfg = bw.make_config(dict(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=1024,
                               vocab=1024), 64, 1)
     cfg.kv_dtype = 4
