@@ -198,6 +198,7 @@ constexpr int kLmRW = BW_LM_RW;  // row steps per group of the lm_head pass
 constexpr int kMaxOwn = 64;     // residual rows per workgroup
 constexpr int kMaxSplitPages = 256;  // pages of one attention split (workgroup)
 constexpr int kMaxSplit = kPT / 4;  // attention splits per KV head (workgroups / KV heads)
+constexpr int kMergeNA = 8;         // split partial words per thread in one poll round of a merger
 constexpr int kLW = (int)(sizeof(PLayer) / 4);  // words of one layer's table entry
 static_assert(sizeof(PLayer) % 16 == 0 && kLW <= kWave, "layer table entry in whole 16-byte words");
 // merge scratch: (m, l) of [splits], factors [splits], partial sums [kPT], the denominator
@@ -797,7 +798,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
   const int g0 = min(w * Rg, 2 * KF), g1 = min(g0 + Rg, 2 * KF);
   const int Rv = (p.V + nwg - 1) / nwg;
   const int v0 = min(w * Rv, p.V), v1 = min(v0 + Rv, p.V);
-  const int S = nwg / G;  // attention splits per KV head
+  // attention splits per KV head: all workgroups, but no more than one merge round of the
+  // mergers covers (kPT / D split groups x 8 words per thread), so that a merger polls once;
+  // workgroups past S G take no split
+  const int S = min(nwg / G, (kPT / D) * kMergeNA);
   const int ag = w / S, as = w - ag * S;  // this workgroup's (KV head, split); ag >= G: idle
 
   // ---- embedding: owned residual rows
@@ -1176,7 +1180,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PersistParams p) {
         const int h = ag * QR + as;
         const __amdgpu_buffer_rsrc_t r = xrsrc(p.xp, (int64_t)H * S * (D + 2) * 4);
         constexpr int SG = kPT / D;  // split groups: thread t takes output t % D of splits t / D + SG i
-        constexpr int NA = 8;        // partial words per thread per round
+        constexpr int NA = kMergeNA;  // partial words per thread per round
         static_assert(kPT % D == 0 && 3 * kMaxSplit + kPT + 1 <= kMrg, "merge scratch");
         const int dd = tid % D, sg = tid / D;
         float* ml = s.mrg;                  // [S][2]: running max, denominator
